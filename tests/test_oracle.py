@@ -1,0 +1,389 @@
+"""Pins for the CPU f64 oracle (no GPU).
+
+The oracle is the reference every GPU result is compared with, so it is itself
+checked here against things other than itself: values the pages print, hand
+worked examples, closed forms, an independent textbook computation with numpy,
+invariants of softmax attention, central finite differences and dual numbers.
+Each check is chosen so that a plausible slip in the oracle (a dropped scale, a
+wrong sign, an off-by-one mask, a transposed operand, a wrong head map) fails
+at least one of them; ``test_oracle_mutants.py`` plants such slips and checks
+that they are caught.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _qkv(B, Hq, Hkv, N, d, seed=0, Nk=None):
+    Nk = N if Nk is None else Nk
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    do = rng.standard_normal((B, Hq, N, d))
+    return q, k, v, do
+
+
+def _textbook(q, k, v, causal, scale):
+    """softmax(scale Q K^T + mask) V with numpy, one head at a time (G = 1)."""
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            if causal:
+                mask = np.arange(Nk)[None, :] > np.arange(N)[:, None] + (Nk - N)
+                s = np.where(mask, -np.inf, s)
+            lse[b, h] = logsumexp(s, axis=1)
+            p = np.exp(s - lse[b, h][:, None])
+            o[b, h] = p @ v[b, h]
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# values printed on the pages, and hand-worked examples
+# --------------------------------------------------------------------------
+
+def test_dual_xsinx_golden():
+    rows = np.loadtxt(os.path.join(GOLDEN, "dual_xsinx.txt"))
+    for x, val, der in rows:
+        got_v, got_d = oracle.dual_xsinx(x)
+        assert got_v == pytest.approx(val, abs=1e-15)
+        assert got_d == pytest.approx(der, abs=1e-15)
+
+
+def test_dual_xsinx_closed_form():
+    for x in np.linspace(-4, 4, 33):
+        v, d = oracle.dual_xsinx(x)
+        assert v == pytest.approx(x * math.sin(x), abs=1e-15)
+        assert d == pytest.approx(math.sin(x) + x * math.cos(x), abs=1e-14)
+
+
+def _golden_worked():
+    vals = {}
+    with open(os.path.join(GOLDEN, "two_key_worked_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, *nums = line.split()
+            vals[name] = np.array([float(x) for x in nums])
+    return vals
+
+
+def test_two_key_worked_example():
+    g = _golden_worked()
+    q = g["q"].reshape(1, 1, 2, 1)
+    k = g["k"].reshape(1, 1, 2, 1)
+    v = g["v"].reshape(1, 1, 2, 1)
+    o, lse = oracle.attn_fwd(q, k, v, True, 1.0)
+    np.testing.assert_allclose(o.ravel(), g["o"], atol=1e-14)
+    np.testing.assert_allclose(lse.ravel(), g["lse"], atol=1e-14)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, g["dout"].reshape(1, 1, 2, 1), True, 1.0)
+    np.testing.assert_allclose(dq.ravel(), g["dq"], atol=1e-14)
+    np.testing.assert_allclose(dk.ravel(), g["dk"], atol=1e-14)
+    np.testing.assert_allclose(dv.ravel(), g["dv"], atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_softmax_rows_sum_to_one(causal):
+    # With d = Nk and V = identity, O row i is the probability row P_i itself.
+    N = 24
+    q = _rand((1, 2, N, N), 1)
+    k = _rand((1, 1, N, N), 2)
+    v = np.eye(N).reshape(1, 1, N, N)
+    o, _ = oracle.attn_fwd(q, k, v, causal, 0.7)
+    P = o[0]
+    np.testing.assert_allclose(P.sum(axis=-1), 1.0, atol=1e-14)
+    assert (P >= 0).all()
+    if causal:
+        upper = np.triu(np.ones((N, N), bool), k=1)
+        assert (P[:, upper] == 0).all()
+        assert (P[:, ~upper] > 0).all()
+
+
+def test_causal_row0_closed_form():
+    q, k, v, _ = _qkv(2, 4, 2, 16, 8, seed=3)
+    scale = 0.3
+    o, lse = oracle.attn_fwd(q, k, v, True, scale)
+    for h in range(4):
+        g = h // 2
+        np.testing.assert_array_equal(o[:, h, 0], v[:, g, 0])
+        np.testing.assert_allclose(lse[:, h, 0], scale * np.einsum("bc,bc->b", q[:, h, 0], k[:, g, 0]),
+                                   rtol=1e-15, atol=1e-15)
+
+
+def test_constant_keys_closed_form():
+    N, d, scale = 20, 6, 0.45
+    q, _, v, _ = _qkv(1, 2, 1, N, d, seed=4)
+    kvec = _rand((d,), 5)
+    k = np.broadcast_to(kvec, (1, 1, N, d)).copy()
+    o, lse = oracle.attn_fwd(q, k, v, True, scale)
+    for i in range(N):
+        np.testing.assert_allclose(o[0, :, i], np.broadcast_to(v[0, 0, : i + 1].mean(axis=0), (2, d)),
+                                   rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], scale * q[0, :, i] @ kvec + math.log(i + 1),
+                                   rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 4), (2, 3, 3, 17, 8), (1, 2, 2, 33, 16)])
+def test_matches_numpy_textbook(causal, shape):
+    B, Hq, Hkv, N, d = shape
+    q, k, v, _ = _qkv(B, Hq, Hkv, N, d, seed=6)
+    o, lse = oracle.attn_fwd(q, k, v, causal, 1.0 / math.sqrt(d))
+    ot, lt = _textbook(q, k, v, causal, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(o, ot, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lt, rtol=1e-12, atol=1e-13)
+
+
+def test_cross_length_bottom_right_mask():
+    # Nq < Nk: query i sits at absolute position i + (Nk - Nq).
+    q, k, v, _ = _qkv(1, 1, 1, 5, 4, seed=7, Nk=9)
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.5)
+    ot, lt = _textbook(q, k, v, True, 0.5)
+    np.testing.assert_allclose(o, ot, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lt, rtol=1e-12, atol=1e-13)
+    # the last query sees every key: equals the non-causal result
+    on, ln = oracle.attn_fwd(q[:, :, -1:], k, v, False, 0.5)
+    np.testing.assert_allclose(o[:, :, -1], on[:, :, 0], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4])
+def test_gqa_equals_mha_with_repeated_kv(G):
+    Hkv = 2
+    q, k, v, _ = _qkv(2, Hkv * G, Hkv, 19, 8, seed=8)
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.35)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    om, lm = oracle.attn_fwd(q, kr, vr, True, 0.35)
+    np.testing.assert_array_equal(o, om)
+    np.testing.assert_array_equal(lse, lm)
+    # and the group map is contiguous: head h reads kv head h // G
+    ot, lt = _textbook(q, kr, vr, True, 0.35)
+    np.testing.assert_allclose(o, ot, rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_invariance():
+    q, k, v, _ = _qkv(1, 2, 1, 64, 8, seed=9)
+    o64, l64 = oracle.attn_fwd(q, k, v, True, 0.4)
+    o32, l32 = oracle.attn_fwd(q[:, :, :32], k[:, :, :32], v[:, :, :32], True, 0.4)
+    np.testing.assert_array_equal(o64[:, :, :32], o32)
+    np.testing.assert_array_equal(l64[:, :, :32], l32)
+
+
+def test_key_shift_invariance():
+    q, k, v, _ = _qkv(1, 2, 1, 21, 8, seed=10)
+    c = _rand((8,), 11)
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.4)
+    o2, lse2 = oracle.attn_fwd(q, k + c, v, True, 0.4)
+    np.testing.assert_allclose(o2, o, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + 0.4 * np.einsum("bhnc,c->bhn", q, c), rtol=1e-11, atol=1e-11)
+
+
+def test_value_linearity():
+    q, k, v, _ = _qkv(1, 2, 1, 13, 4, seed=12)
+    v2 = _rand(v.shape, 13)
+    o1, _ = oracle.attn_fwd(q, k, v, True, 0.5)
+    o2, _ = oracle.attn_fwd(q, k, v2, True, 0.5)
+    o3, _ = oracle.attn_fwd(q, k, 2.0 * v - 3.0 * v2, True, 0.5)
+    np.testing.assert_allclose(o3, 2.0 * o1 - 3.0 * o2, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = oracle.attn_fwd(q, k, v, causal, scale)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 5, 3), (1, 2, 2, 6, 4), (2, 3, 1, 4, 2)])
+def test_bwd_central_finite_differences(causal, shape):
+    B, Hq, Hkv, N, d = shape
+    q, k, v, do = _qkv(B, Hq, Hkv, N, d, seed=14)
+    scale = 0.6
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, causal, scale)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, causal, scale)
+            fd[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - g)) / max(1.0, np.max(np.abs(g)))
+        assert err <= 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 7, 4), (2, 4, 2, 11, 8), (1, 3, 1, 16, 16)])
+def test_bwd_dual_numbers(causal, shape):
+    B, Hq, Hkv, N, d = shape
+    q, k, v, do = _qkv(B, Hq, Hkv, N, d, seed=15)
+    tq, tk, tv = _rand(q.shape, 16), _rand(k.shape, 17), _rand(v.shape, 18)
+    scale = 0.37
+    o, to, lse, tlse = oracle.attn_fwd_dual(q, tq, k, tk, v, tv, causal, scale)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-13, atol=1e-14)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal, scale)
+    directional = float(np.sum(do * to))
+    inner = float(np.sum(dq * tq) + np.sum(dk * tk) + np.sum(dv * tv))
+    assert abs(directional - inner) <= 1e-12 * max(1.0, abs(directional))
+
+
+def test_bwd_invariants():
+    B, Hq, Hkv, N, d = 2, 6, 2, 23, 8
+    q, k, v, do = _qkv(B, Hq, Hkv, N, d, seed=19)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, True, 0.3)
+    G = Hq // Hkv
+    # causal row 0 has a single visible key: its dq is exactly zero
+    assert np.all(dq[:, :, 0] == 0.0)
+    # shift invariance in the keys: sum_j dk_j = 0 per kv head
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # rows of P sum to one: sum_j dv_j = sum over the group and rows of dO
+    for g in range(Hkv):
+        np.testing.assert_allclose(dv[:, g].sum(axis=1), do[:, g * G:(g + 1) * G].sum(axis=(1, 2)),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_gqa_is_group_sum_of_mha():
+    B, Hkv, G, N, d = 1, 2, 3, 12, 4
+    q, k, v, do = _qkv(B, Hkv * G, Hkv, N, d, seed=20)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, True, 0.5)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    dqm, dkm, dvm = oracle.attn_bwd(q, kr, vr, do, True, 0.5)
+    np.testing.assert_allclose(dq, dqm, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dk, dkm.reshape(B, Hkv, G, N, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dvm.reshape(B, Hkv, G, N, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# split-KV decode, the merge and the online-softmax monoid
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L", [1, 7, 64, 100])
+def test_decode_split_invariance(L):
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, Hkv, L, d))
+    vc = rng.standard_normal((B, Hkv, L, d))
+    # unsplit definition: the one-row forward against every cached key
+    o_ref, l_ref = oracle.attn_fwd(q[:, :, None], kc, vc, False, 0.35)
+    for S in sorted({1, 2, 3, 16, L, L + 3}):
+        po, pl = oracle.attn_decode(q, kc, vc, 0.35, S)
+        o, lse = oracle.lse_merge(po, pl)
+        np.testing.assert_allclose(o, o_ref[:, :, 0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse, l_ref[:, :, 0], rtol=1e-13, atol=1e-14)
+        C = -(-L // S)
+        for s in range(S):
+            if s * C >= L:            # empty chunk: the identity
+                assert np.all(pl[:, :, s] == -np.inf) and np.all(po[:, :, s] == 0.0)
+
+
+def test_decode_equals_last_causal_row():
+    B, Hq, Hkv, L, d = 1, 4, 1, 37, 8
+    rng = np.random.default_rng(22)
+    Q = rng.standard_normal((B, Hq, L, d))
+    kc = rng.standard_normal((B, Hkv, L, d))
+    vc = rng.standard_normal((B, Hkv, L, d))
+    o, lse = oracle.attn_fwd(Q, kc, vc, True, 0.4)
+    po, pl = oracle.attn_decode(Q[:, :, -1], kc, vc, 0.4, 5)
+    od, ld = oracle.lse_merge(po, pl)
+    np.testing.assert_allclose(od, o[:, :, -1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(ld, lse[:, :, -1], rtol=1e-13, atol=1e-14)
+
+
+def test_merge_order_independent_and_identity():
+    rng = np.random.default_rng(23)
+    B, Hq, S, d = 1, 3, 9, 5
+    po = rng.standard_normal((B, Hq, S, d))
+    pl = rng.standard_normal((B, Hq, S)) * 4
+    o, lse = oracle.lse_merge(po, pl)
+    for _ in range(5):
+        perm = rng.permutation(S)
+        o2, l2 = oracle.lse_merge(po[:, :, perm], pl[:, :, perm])
+        np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(l2, lse, rtol=1e-13, atol=1e-14)
+    # adding empty chunks changes nothing
+    po_e = np.concatenate([po, np.zeros((B, Hq, 2, d))], axis=2)
+    pl_e = np.concatenate([pl, np.full((B, Hq, 2), -np.inf)], axis=2)
+    o3, l3 = oracle.lse_merge(po_e, pl_e)
+    np.testing.assert_allclose(o3, o, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(l3, lse, rtol=1e-15, atol=0)
+    # all chunks empty
+    o4, l4 = oracle.lse_merge(np.zeros((1, 1, 3, d)), np.full((1, 1, 3), -np.inf))
+    assert np.all(o4 == 0) and np.all(l4 == -np.inf)
+
+
+def _fold_tree(states, rng):
+    """Combine a list of states in a random binary tree shape."""
+    states = list(states)
+    while len(states) > 1:
+        i = int(rng.integers(0, len(states) - 1))
+        merged = oracle.state_combine(states[i], states[i + 1])
+        states[i:i + 2] = [merged]
+    return states[0]
+
+
+def test_online_monoid_order_and_tree_independence():
+    rng = np.random.default_rng(24)
+    n, d = 40, 6
+    s = rng.standard_normal(n) * 3
+    v = rng.standard_normal((n, d))
+    # materialised softmax
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    o_ref = p @ v
+    lse_ref = logsumexp(s)
+    singles = [(s[j], 1.0, v[j]) for j in range(n)]
+    for trial in range(8):
+        perm = rng.permutation(n)
+        m, l, a = _fold_tree([singles[j] for j in perm], rng)
+        np.testing.assert_allclose(a / l, o_ref, rtol=1e-12, atol=1e-13)
+        assert m + math.log(l) == pytest.approx(lse_ref, rel=1e-13, abs=1e-13)
+
+
+def test_online_monoid_laws():
+    rng = np.random.default_rng(25)
+    d = 4
+    ident = (-np.inf, 0.0, np.zeros(d))
+    x = (1.5, 2.0, rng.standard_normal(d))
+    y = (-0.5, 0.7, rng.standard_normal(d))
+    z = (3.0, 1.1, rng.standard_normal(d))
+    for left in (oracle.state_combine(ident, x), oracle.state_combine(x, ident)):
+        assert left[0] == x[0] and left[1] == x[1]
+        np.testing.assert_array_equal(left[2], x[2])
+    a = oracle.state_combine(oracle.state_combine(x, y), z)
+    b = oracle.state_combine(x, oracle.state_combine(y, z))
+    assert a[0] == b[0]
+    assert a[1] == pytest.approx(b[1], rel=1e-14)
+    np.testing.assert_allclose(a[2], b[2], rtol=1e-14, atol=1e-15)
+    c = oracle.state_combine(y, x)
+    d_ = oracle.state_combine(x, y)
+    assert c[0] == d_[0] and c[1] == pytest.approx(d_[1], rel=1e-15)
