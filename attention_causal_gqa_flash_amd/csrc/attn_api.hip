@@ -1,0 +1,209 @@
+// attn_api.hip -- the C ABI of libattn.so (declared in include/attn.h).
+//
+// Every entry point validates all of its arguments on the host before the
+// first launch, so an invalid call enqueues nothing and leaves its outputs
+// untouched (the fail-closed convention of the RustingBrain docs, "Training on
+// a GPU": a device failure returns an error instead of silently continuing on
+// the CPU).  No exception crosses the boundary; there is no host fallback.
+#include "attn.h"
+#include "attn_launch.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+using attn::kBF16;
+using attn::kF32;
+
+constexpr long kMaxGridX = 2147483647L;
+constexpr long kMaxGridYZ = 65535L;
+
+bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+attn_status check_common(int dt, int B, int Hq, int Hkv, int N, int d, float scale)
+{
+    if (dt != ATTN_F32 && dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return ATTN_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (!head_dim_ok(d)) return ATTN_ERR_UNSUPPORTED;
+    // launch-shape limits of the kernels (grid x is linear, y/z are heads and batch)
+    if ((long)Hq > kMaxGridYZ || (long)B > kMaxGridYZ) return ATTN_ERR_UNSUPPORTED;
+    if ((long)((N + 63) / 64) * (long)B * (long)Hq > kMaxGridX) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// The matrix-core kernels run softmax in base 2 on |scale|*log2(e) and need a
+// nonzero scale; a zero scale (uniform attention) takes the generic kernels.
+bool use_mfma(int dt, int d, float scale) { return attn::mfma_supported(dt, d) && scale != 0.f; }
+
+attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+size_t workspace_bytes(int B, int Hq, int N)
+{
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)N;
+    return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+// Kernel launches of the three backward stages (arguments already validated).
+hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int N, int d, const float *o,
+                                 const void *dout, float *delta, hipStream_t st)
+{
+    return attn::bwd_preprocess(dt, (long)B * Hq * N, d, dout, o, delta, st);
+}
+
+hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, const float *lse,
+                           const void *dout, const float *delta, float *dk, float *dv,
+                           hipStream_t st)
+{
+    if (use_mfma(dt, d, scale))
+        return attn::bwd_dkdv_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
+                                   delta, dk, dv, st);
+    return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
+                                  delta, dk, dv, st);
+}
+
+hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         const void *q, const void *k, const void *v, const float *lse,
+                         const void *dout, const float *delta, float *dq, hipStream_t st)
+{
+    if (use_mfma(dt, d, scale))
+        return attn::bwd_dq_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout, delta,
+                                 dq, st);
+    return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
+                                delta, dq, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const void *q, const void *k, const void *v, float *o, float *lse,
+                     void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (use_mfma(dt, d, scale))
+        e = attn::fwd_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);
+    else
+        e = attn::fwd_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);
+    return hip_status(e);
+}
+
+size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, int d)
+{
+    if (check_common(dt, B, Hq, Hkv, N, d, 1.0f) != ATTN_OK) return 0;
+    return workspace_bytes(B, Hq, N);
+}
+
+attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const void *q, const void *k, const void *v, const float *o,
+                     const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                     void *workspace, size_t ws_bytes, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    float *delta = (float *)workspace;
+    if (launch_bwd_preprocess(dt, B, Hq, N, d, o, dout, delta, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
+                        st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return hip_status(
+        launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st));
+}
+
+attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,
+                                const void *dout, float *delta, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, 1, N, d, 1.0f);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_bwd_preprocess(dt, B, Hq, N, d, o, dout, delta, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v,
+                          const float *lse, const void *dout, const float *delta, float *dk,
+                          float *dv, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout) ||
+        !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
+                                      delta, dk, dv, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v, const float *lse,
+                        const void *dout, const float *delta, float *dq, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout) ||
+        !aligned16(delta) || !aligned16(dq))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
+                                    delta, dq, (hipStream_t)stream));
+}
+
+attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,
+                        int n_splits, const void *q, const void *k_cache, const void *v_cache,
+                        float *part_o, float *part_lse, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, L, d, scale);
+    if (s != ATTN_OK) return s;
+    if (n_splits < 1) return ATTN_ERR_INVALID_ARG;
+    if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+    if ((long)n_splits > kMaxGridX || (long)Hkv > kMaxGridYZ) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o) ||
+        !aligned16(part_lse))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(attn::decode_split(dt, B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
+                                         v_cache, part_o, part_lse, (hipStream_t)stream));
+}
+
+attn_status attn_lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
+                           const float *part_lse, float *o, float *lse, void *stream)
+{
+    if (B <= 0 || Hq <= 0 || n_splits < 1 || d <= 0) return ATTN_ERR_INVALID_ARG;
+    if (!head_dim_ok(d)) return ATTN_ERR_UNSUPPORTED;
+    if ((long)Hq > kMaxGridX || (long)B > kMaxGridYZ) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(
+        attn::lse_merge(B, Hq, n_splits, d, part_o, part_lse, o, lse, (hipStream_t)stream));
+}
+
+const char *attn_status_str(attn_status s)
+{
+    switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int attn_abi_version(void) { return 1; }
+
+}  // extern "C"

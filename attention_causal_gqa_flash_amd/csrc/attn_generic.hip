@@ -1,0 +1,481 @@
+// attn_generic.hip -- vector-ALU kernels for every supported (dtype, head dim):
+// the f32 path, small head dims, the backward preprocess, split-KV decode and
+// the log-sum-exp merge.
+//
+// The forward keeps, per query row, the three running values of the streaming
+// softmax -- running max m, running sum l, running weighted sum acc -- while the
+// keys stream past once ("tang -- differentiable computing in Rust", "How tang
+// works" part 3, equation (6)).  Arithmetic is f32 with accurate expf/logf.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+#include <math.h>
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// Forward, one thread per query row.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q,
+                                                         const T *__restrict__ k,
+                                                         const T *__restrict__ v,
+                                                         float *__restrict__ o,
+                                                         float *__restrict__ lse, int Hq, int Hkv,
+                                                         int N, float scale, int causal)
+{
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (Hq / Hkv);
+    const T *qh = q + ((size_t)b * Hq + h) * (size_t)N * D;
+    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const int row = i < N ? i : N - 1;
+
+    float qr[D], acc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        qr[c] = to_f32(qh[(size_t)row * D + c]);
+        acc[c] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int jend = causal ? row + 1 : N;
+    // keys are read in lock-step across the wave (broadcast loads)
+    const int wave_end = causal ? min(N, (int)(blockIdx.x * 64 + 64)) : N;
+    for (int j = 0; j < wave_end; ++j) {
+        if (j >= jend) continue;
+        const T *kj = kg + (size_t)j * D;
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) s = fmaf(qr[c], to_f32(kj[c]), s);
+        s *= scale;
+        if (s > m) {                    // new running max: rescale the state
+            const float a = expf(m - s);
+            l *= a;
+#pragma unroll
+            for (int c = 0; c < D; ++c) acc[c] *= a;
+            m = s;
+        }
+        const float p = expf(s - m);
+        l += p;
+        const T *vj = vg + (size_t)j * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(p, to_f32(vj[c]), acc[c]);
+    }
+    if (i < N) {
+        float *oh = o + (((size_t)b * Hq + h) * N + i) * D;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int c = 0; c < D; ++c) oh[c] = acc[c] * inv;
+        lse[((size_t)b * Hq + h) * N + i] = m + logf(l);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward preprocess: D_i = dout_i . o_i.  D/8 lanes per row, 8 elements each.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout,
+                                                      const float *__restrict__ o,
+                                                      float *__restrict__ Dws, long rows)
+{
+    constexpr int LPR = D / 8;              // lanes per row
+    constexpr int RPB = 256 / LPR;          // rows per block
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    float s = 0.f;
+    if (row < rows) {
+        const size_t base = (size_t)row * D + part * 8;
+        const float4 o0 = *(const float4 *)(o + base);
+        const float4 o1 = *(const float4 *)(o + base + 4);
+        float dv[8];
+        if constexpr (sizeof(T) == 2) {
+            const uint4 u = *(const uint4 *)((const uint16_t *)dout + base);
+            dv[0] = bf16lo(u.x); dv[1] = bf16hi(u.x); dv[2] = bf16lo(u.y); dv[3] = bf16hi(u.y);
+            dv[4] = bf16lo(u.z); dv[5] = bf16hi(u.z); dv[6] = bf16lo(u.w); dv[7] = bf16hi(u.w);
+        } else {
+            const float4 a = *(const float4 *)((const float *)dout + base);
+            const float4 c = *(const float4 *)((const float *)dout + base + 4);
+            dv[0] = a.x; dv[1] = a.y; dv[2] = a.z; dv[3] = a.w;
+            dv[4] = c.x; dv[5] = c.y; dv[6] = c.z; dv[7] = c.w;
+        }
+        s = dv[0] * o0.x + dv[1] * o0.y + dv[2] * o0.z + dv[3] * o0.w +
+            dv[4] * o1.x + dv[5] * o1.y + dv[6] * o1.z + dv[7] * o1.w;
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (row < rows && part == 0) Dws[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Backward, dq: one thread per query row.  P is recomputed from lse.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
+    float *__restrict__ dq, int Hq, int Hkv, int N, float scale, int causal)
+{
+    const int i = blockIdx.x * 64 + threadIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (Hq / Hkv);
+    const size_t qrow0 = ((size_t)b * Hq + h) * N;
+    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const int row = i < N ? i : N - 1;
+
+    float qr[D], dor[D], acc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        qr[c] = to_f32(q[(qrow0 + row) * D + c]);
+        dor[c] = to_f32(dout[(qrow0 + row) * D + c]);
+        acc[c] = 0.f;
+    }
+    const float L = lse[qrow0 + row], Di = Dws[qrow0 + row];
+    const int jend = causal ? row + 1 : N;
+    const int wave_end = causal ? min(N, (int)(blockIdx.x * 64 + 64)) : N;
+    for (int j = 0; j < wave_end; ++j) {
+        if (j >= jend) continue;
+        const T *kj = kg + (size_t)j * D;
+        const T *vj = vg + (size_t)j * D;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+            s = fmaf(qr[c], to_f32(kj[c]), s);
+            dp = fmaf(dor[c], to_f32(vj[c]), dp);
+        }
+        const float p = expf(s * scale - L);
+        const float ds = p * (dp - Di);
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, to_f32(kj[c]), acc[c]);
+    }
+    if (i < N) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) dq[(qrow0 + i) * D + c] = acc[c] * scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, dk and dv: one thread per key row of a key/value head; the loop
+// runs over the query heads of the group and over the queries that see the key.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
+    float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, float scale,
+    int causal)
+{
+    const int j = blockIdx.x * 64 + threadIdx.x;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const size_t krow0 = ((size_t)b * Hkv + g) * N;
+    const int row = j < N ? j : N - 1;
+
+    float kr[D], vr[D], dka[D], dva[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        kr[c] = to_f32(k[(krow0 + row) * D + c]);
+        vr[c] = to_f32(v[(krow0 + row) * D + c]);
+        dka[c] = 0.f;
+        dva[c] = 0.f;
+    }
+    const int istart = causal ? row : 0;
+    const int wave_start = causal ? (int)(blockIdx.x * 64) : 0;
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        const size_t qrow0 = ((size_t)b * Hq + h) * N;
+        for (int i = wave_start; i < N; ++i) {
+            if (i < istart) continue;
+            const T *qi = q + (qrow0 + i) * D;
+            const T *di = dout + (qrow0 + i) * D;
+            float s = 0.f, dp = 0.f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                s = fmaf(to_f32(qi[c]), kr[c], s);
+                dp = fmaf(to_f32(di[c]), vr[c], dp);
+            }
+            const float p = expf(s * scale - lse[qrow0 + i]);
+            const float ds = p * (dp - Dws[qrow0 + i]);
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                dva[c] = fmaf(p, to_f32(di[c]), dva[c]);
+                dka[c] = fmaf(ds, to_f32(qi[c]), dka[c]);
+            }
+        }
+    }
+    if (j < N) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+            dk[(krow0 + j) * D + c] = dka[c] * scale;
+            dv[(krow0 + j) * D + c] = dva[c];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV decode.  One workgroup per (split, key/value head, batch) handles
+// all G query heads of the group, so each cached key and value is read from
+// memory once.  Four waves share the chunk; within a wave, scores are computed
+// one key per lane and the value sum one column pair per lane; the waves'
+// running states are then combined with the associative softmax merge.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int GM>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
+    float *__restrict__ part_o, float *__restrict__ part_lse, int Hq, int Hkv, int L,
+    float scale, int n_splits)
+{
+    constexpr int CPL = D >= 64 ? D / 64 : 1;   // value columns per lane
+    constexpr int ACT = D / CPL;                 // lanes that own columns
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+
+    __shared__ float qs[GM][D];
+    __shared__ float ps[4][64][GM];
+    __shared__ float wm[4][GM], wl[4][GM];
+    __shared__ float wacc[4][GM][D];
+
+    for (int t = threadIdx.x; t < G * D; t += 256) {
+        const int hh = t / D, c = t % D;
+        qs[hh][c] = to_f32(q[((size_t)b * Hq + g * G + hh) * D + c]) * scale;
+    }
+    __syncthreads();
+
+    const long C = ((long)L + n_splits - 1) / n_splits;
+    const long j0 = (long)s * C;
+    const long j1 = min((long)L, j0 + C);
+    const T *kg = kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+    const T *vg = vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+
+    // G <= GM; loops run to the compile-time GM so the state stays in registers
+    float m[GM], l[GM], acc[GM][CPL];
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+        m[hh] = -INFINITY;
+        l[hh] = 0.f;
+        for (int c = 0; c < CPL; ++c) acc[hh][c] = 0.f;
+    }
+
+    // wave w takes rounds of 64 keys: [j0 + 64*(4r + w), +64)
+    for (long base = j0 + 64 * w; base < j1; base += 256) {
+        const long j = base + lane;
+        const bool valid = j < j1;
+        float sc[GM];
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) sc[hh] = 0.f;
+        if (valid) {
+            const T *kj = kg + (size_t)j * D;
+            for (int c = 0; c < D; ++c) {
+                const float kv = to_f32(kj[c]);
+#pragma unroll
+                for (int hh = 0; hh < GM; ++hh)
+                    if (hh < G) sc[hh] = fmaf(qs[hh][c], kv, sc[hh]);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) {
+            if (hh >= G) continue;
+            const float x = valid ? sc[hh] : -INFINITY;
+            const float mx = wave_max(x);            // lane 0 is always valid: finite
+            const float mnew = fmaxf(m[hh], mx);
+            const float a = m[hh] == -INFINITY ? 0.f : expf(m[hh] - mnew);
+            const float p = valid ? expf(x - mnew) : 0.f;
+            l[hh] = l[hh] * a + wave_sum(p);
+            for (int c = 0; c < CPL; ++c) acc[hh][c] *= a;
+            m[hh] = mnew;
+            ps[w][lane][hh] = p;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        const long nk = min((long)64, j1 - base);
+        if (lane < ACT) {
+            for (long t = 0; t < nk; ++t) {
+                const T *vj = vg + (size_t)(base + t) * D + lane * CPL;
+                float vv[CPL];
+                for (int c = 0; c < CPL; ++c) vv[c] = to_f32(vj[c]);
+#pragma unroll
+                for (int hh = 0; hh < GM; ++hh) {
+                    if (hh >= G) continue;
+                    const float p = ps[w][t][hh];
+                    for (int c = 0; c < CPL; ++c) acc[hh][c] = fmaf(p, vv[c], acc[hh][c]);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // combine the four waves
+    if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh) { wm[w][hh] = m[hh]; wl[w][hh] = l[hh]; }
+    }
+    if (lane < ACT) {
+#pragma unroll
+        for (int hh = 0; hh < GM; ++hh)
+            for (int c = 0; c < CPL; ++c) wacc[w][hh][lane * CPL + c] = acc[hh][c];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * D; t += 256) {
+        const int hh = t / D, c = t % D;
+        float M = -INFINITY;
+        for (int x = 0; x < 4; ++x) M = fmaxf(M, wm[x][hh]);
+        const size_t ob = ((size_t)b * Hq + g * G + hh) * n_splits + s;
+        if (M == -INFINITY) {                    // empty chunk: the identity
+            part_o[ob * D + c] = 0.f;
+            if (c == 0) part_lse[ob] = -INFINITY;
+            continue;
+        }
+        float lt = 0.f, at = 0.f;
+        for (int x = 0; x < 4; ++x) {
+            if (wm[x][hh] == -INFINITY) continue;
+            const float e = expf(wm[x][hh] - M);
+            lt = fmaf(wl[x][hh], e, lt);
+            at = fmaf(wacc[x][hh][c], e, at);
+        }
+        part_o[ob * D + c] = at / lt;
+        if (c == 0) part_lse[ob] = M + logf(lt);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the split partials: one workgroup per (query head, batch).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void lse_merge_kernel(const float *__restrict__ part_o,
+                                                        const float *__restrict__ part_lse,
+                                                        float *__restrict__ o,
+                                                        float *__restrict__ lse, int Hq,
+                                                        int n_splits, int d)
+{
+    const int h = blockIdx.x, b = blockIdx.y;
+    const size_t row = (size_t)b * Hq + h;
+    const float *pl = part_lse + row * n_splits;
+    const float *po = part_o + row * (size_t)n_splits * d;
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pl[s]);
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+        if (M == -INFINITY) {
+            o[row * d + c] = 0.f;
+            continue;
+        }
+        float W = 0.f, acc = 0.f;
+        for (int s = 0; s < n_splits; ++s) {
+            const float ls = pl[s];
+            if (ls == -INFINITY) continue;
+            const float w = expf(ls - M);
+            W += w;
+            acc = fmaf(w, po[(size_t)s * d + c], acc);
+        }
+        o[row * d + c] = acc / W;
+    }
+    if (threadIdx.x == 0) {
+        if (M == -INFINITY) {
+            lse[row] = -INFINITY;
+        } else {
+            float W = 0.f;
+            for (int s = 0; s < n_splits; ++s)
+                if (pl[s] != -INFINITY) W += expf(pl[s] - M);
+            lse[row] = M + logf(W);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+#define ATTN_DISPATCH_D(d, ...)                              \
+    switch (d) {                                             \
+    case 16: { constexpr int D = 16; __VA_ARGS__; break; }   \
+    case 32: { constexpr int D = 32; __VA_ARGS__; break; }   \
+    case 64: { constexpr int D = 64; __VA_ARGS__; break; }   \
+    case 128: { constexpr int D = 128; __VA_ARGS__; break; } \
+    default: return hipErrorInvalidValue;                    \
+    }
+
+#define ATTN_DISPATCH_T(dt, ...)                                   \
+    if (dt == kBF16) { typedef bf16_t T; __VA_ARGS__; }            \
+    else { typedef float T; __VA_ARGS__; }
+
+hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       const void *q, const void *k, const void *v, float *o, float *lse,
+                       hipStream_t st)
+{
+    dim3 grid((N + 63) / 64, Hq, B);
+    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D>), grid,
+                                                              dim3(64), 0, st, (const T *)q,
+                                                              (const T *)k, (const T *)v, o, lse,
+                                                              Hq, Hkv, N, scale, causal)));
+    return hipGetLastError();
+}
+
+hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
+                          hipStream_t st)
+{
+    const int rpb = 256 / (d / 8);
+    dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid,
+                                                              dim3(256), 0, st, (const T *)dout,
+                                                              o, Dws, rows)));
+    return hipGetLastError();
+}
+
+hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          const void *q, const void *k, const void *v, const float *lse,
+                          const void *dout, const float *Dws, float *dq, hipStream_t st)
+{
+    dim3 grid((N + 63) / 64, Hq, B);
+    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
+                                               (bwd_dq_rowwise_kernel<T, D>), grid, dim3(64), 0,
+                                               st, (const T *)q, (const T *)k, (const T *)v, lse,
+                                               (const T *)dout, Dws, dq, Hq, Hkv, N, scale,
+                                               causal)));
+    return hipGetLastError();
+}
+
+hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                            const void *q, const void *k, const void *v, const float *lse,
+                            const void *dout, const float *Dws, float *dk, float *dv,
+                            hipStream_t st)
+{
+    dim3 grid((N + 63) / 64, Hkv, B);
+    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
+                                               (bwd_dkdv_colwise_kernel<T, D>), grid, dim3(64), 0,
+                                               st, (const T *)q, (const T *)k, (const T *)v, lse,
+                                               (const T *)dout, Dws, dk, dv, Hq, Hkv, N, scale,
+                                               causal)));
+    return hipGetLastError();
+}
+
+hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
+                        const void *q, const void *kc, const void *vc, float *part_o,
+                        float *part_lse, hipStream_t st)
+{
+    dim3 grid(n_splits, Hkv, B);
+    const int G = Hq / Hkv;
+#define ATTN_DEC_LAUNCH(GMV)                                                                     \
+    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(                                  \
+                                               (decode_split_kernel<T, D, GMV>), grid,           \
+                                               dim3(256), 0, st, (const T *)q, (const T *)kc,   \
+                                               (const T *)vc, part_o, part_lse, Hq, Hkv, L,     \
+                                               scale, n_splits)))
+    if (G <= 4) {
+        ATTN_DEC_LAUNCH(4);
+    } else if (G <= 8) {
+        ATTN_DEC_LAUNCH(8);
+    } else {
+        ATTN_DEC_LAUNCH(16);
+    }
+#undef ATTN_DEC_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
+                     const float *part_lse, float *o, float *lse, hipStream_t st)
+{
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(Hq, B), dim3(128), 0, st, part_o, part_lse, o, lse,
+                       Hq, n_splits, d);
+    return hipGetLastError();
+}
+
+}  // namespace attn

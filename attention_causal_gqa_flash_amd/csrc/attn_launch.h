@@ -1,0 +1,49 @@
+// attn_launch.h -- host-side launchers of the gfx950 kernels (internal to libattn.so).
+//
+// Every launcher enqueues its kernels on `st` and returns hipGetLastError().
+// Arguments have already been validated by the C ABI layer (attn_api.hip):
+// shapes are positive, Hq % Hkv == 0, d is supported, pointers are non-null.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// Generic kernels: any supported (dtype, d); one thread per query row or key row.
+hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       const void *q, const void *k, const void *v, float *o, float *lse,
+                       hipStream_t st);
+hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          const void *q, const void *k, const void *v, const float *lse,
+                          const void *dout, const float *Dws, float *dq, hipStream_t st);
+hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                            const void *q, const void *k, const void *v, const float *lse,
+                            const void *dout, const float *Dws, float *dk, float *dv,
+                            hipStream_t st);
+
+// D_i = dout_i . o_i for every query row (rows = B*Hq*N).
+hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
+                          hipStream_t st);
+
+// Matrix-core kernels: bf16 inputs, d in {64, 128}.
+bool mfma_supported(int dt, int d);
+hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                    const void *q, const void *k, const void *v, float *o, float *lse,
+                    hipStream_t st);
+hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         const void *q, const void *k, const void *v, const float *lse,
+                         const void *dout, const float *Dws, float *dk, float *dv, hipStream_t st);
+hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       const void *q, const void *k, const void *v, const float *lse,
+                       const void *dout, const float *Dws, float *dq, hipStream_t st);
+
+// Split-KV decode and the log-sum-exp merge.
+hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
+                        const void *q, const void *kc, const void *vc, float *part_o,
+                        float *part_lse, hipStream_t st);
+hipError_t lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
+                     const float *part_lse, float *o, float *lse, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,180 @@
+/*
+ * attn.h -- C ABI of libattn.so: causal grouped-query flash attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes softmax attention without ever writing a score or
+ * probability matrix to device memory.  The softmax maximum and its two sums
+ * are folded into one streaming reduction over keys that carries three running
+ * values per query row (running max, running sum, running weighted sum of
+ * values) -- the rewrite described in "tang -- differentiable computing in
+ * Rust", section "How tang works", part 3 "Optimizations are derived, not
+ * written" (equations (5) and (6)); the combine is associative, which is what
+ * lets the keys be tiled and split.  The gradient is the gradient of the same
+ * reduction, recomputed tile by tile (same part 3, and the compiler article
+ * "A compiler that derives GPU kernels matches hand-tuned code", paragraph on
+ * views and comprehensions).  Shapes follow the grouped-query statement of the
+ * problem in the "RustingBrain" docs ("What is in the box"; "A language model
+ * in twenty lines": query heads, key/value heads, head dim).
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, owned by the caller.  The library
+ *    allocates nothing, frees nothing and keeps no state between calls.
+ *  - Layouts are contiguous row-major with the head dimension fastest:
+ *        q, dout, o, dq      [B][Hq][N][d]
+ *        k, v, dk, dv        [B][Hkv][N][d]
+ *        lse                 [B][Hq][N]
+ *  - Input dtype (q, k, v, dout, caches) is ATTN_F32 (IEEE float) or ATTN_BF16
+ *    (bfloat16, stored as 16-bit words).  Every output (o, lse, dq, dk, dv,
+ *    decode partials) is float32 for both input dtypes.
+ *  - Grouped-query head map: query head h reads key/value head h / (Hq/Hkv)
+ *    (contiguous groups).  Hq must be a multiple of Hkv.
+ *  - Causal mask: key j is visible to query i iff j <= i.
+ *  - lse is the natural-log log-sum-exp of the row's scaled scores.
+ *  - scale multiplies q.k (normally 1/sqrt(d)); it must be finite.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns at once.  ATTN_OK means the work was enqueued; results
+ *    are valid after the caller synchronises the stream.
+ *  - Errors are fail-closed: every argument is checked on the host before any
+ *    launch, and an invalid call launches nothing and leaves every output
+ *    untouched.  There is no host fallback: the work runs on the GPU or the call
+ *    returns an error.  No C++ exception crosses this boundary.
+ *  - Pointers must be non-null and 16-byte aligned.
+ *  - Supported head dims: 16, 32, 64, 128.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,  /* a dim <= 0, Hq % Hkv != 0, null or misaligned pointer,
+                                  non-finite scale, n_splits < 1, bad dtype code */
+    ATTN_ERR_UNSUPPORTED = 2,  /* head dim outside {16,32,64,128}, or a size beyond the
+                                  documented limits (see each entry point) */
+    ATTN_ERR_WORKSPACE = 3,    /* workspace null or smaller than attn_bwd_workspace_bytes */
+    ATTN_ERR_HIP = 4           /* a HIP launch reported an error */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,
+    ATTN_BF16 = 1
+} attn_dtype;
+
+/*
+ * attn_fwd -- causal (or full) grouped-query attention forward.
+ *   Per query row: o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the
+ *   visible keys, and lse_i = log sum_j exp(scale * q_i . k_j).
+ *   Source: "How tang works" part 3 (the streaming softmax reduction); the
+ *   causal fused kernel of the RustingBrain docs ("What is in the box").
+ *   q [B][Hq][N][d], k/v [B][Hkv][N][d] of dtype dt -> o [B][Hq][N][d] f32,
+ *   lse [B][Hq][N] f32.  causal: nonzero for the causal mask.
+ */
+attn_status attn_fwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const void *q, const void *k, const void *v,
+                     float *o, float *lse, void *stream);
+
+/*
+ * attn_bwd_workspace_bytes -- device workspace attn_bwd needs, in bytes:
+ *   one f32 per query row, D_i = dout_i . o_i, rounded up to 256 bytes.
+ *   Returns 0 for invalid shapes.
+ */
+size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * attn_bwd -- gradient of attn_fwd's o with respect to q, k and v, given the
+ *   upstream gradient dout of o (the upstream gradient of lse is taken as 0).
+ *   With P the softmax probabilities (recomputed tile by tile from q, k and
+ *   lse, never stored), D_i = dout_i . o_i, dP_ij = dout_i . v_j and
+ *   dS_ij = P_ij (dP_ij - D_i):
+ *     dq_i = scale sum_j dS_ij k_j
+ *     dk_j = scale sum_{h in group} sum_i dS_ij q_i
+ *     dv_j = sum_{h in group} sum_i P_ij dout_i
+ *   Source: "How tang works" part 3 (gradients of the reduction are
+ *   reductions too) and the compiler article's paragraph on comprehensions.
+ *   o and lse must be the outputs of attn_fwd for the same q, k, v, causal,
+ *   scale.  dq [B][Hq][N][d], dk/dv [B][Hkv][N][d] are f32 and overwritten.
+ *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
+ *   owned by the caller; its contents on entry do not matter.
+ */
+attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const void *q, const void *k, const void *v,
+                     const float *o, const float *lse, const void *dout,
+                     float *dq, float *dk, float *dv,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The three stages attn_bwd runs, callable one by one (for example to put the
+ * dK/dV stage and the dQ stage on two streams once delta is ready, or to time
+ * them).  Arguments mean the same as in attn_bwd; delta [B][Hq][N] f32 is
+ * caller-owned device memory holding D_i = dout_i . o_i.
+ *
+ * attn_bwd_preprocess -- writes delta from o (f32) and dout (dtype dt).
+ * attn_bwd_dkdv       -- writes dk and dv; reads q, k, v, lse, dout, delta.
+ * attn_bwd_dq         -- writes dq; reads q, k, v, lse, dout, delta.
+ * dkdv and dq do not depend on each other; both need the preprocess first.
+ */
+attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d,
+                                const float *o, const void *dout, float *delta, void *stream);
+attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v,
+                          const float *lse, const void *dout, const float *delta,
+                          float *dk, float *dv, void *stream);
+attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v,
+                        const float *lse, const void *dout, const float *delta,
+                        float *dq, void *stream);
+
+/*
+ * attn_decode -- split-KV attention of one new query token per (b, query head)
+ *   against a cache of L keys, all of which are visible to it (the token sits
+ *   after the cache).  Source: RustingBrain docs, "Generating text" (after the
+ *   prefill each token costs one row of attention against the cache); the
+ *   split is legal because the softmax combine is associative ("How tang
+ *   works" part 3).
+ *   The keys are cut into n_splits contiguous chunks of C = ceil(L / n_splits)
+ *   keys; chunk s covers [s*C, min((s+1)*C, L)).  For each chunk the call
+ *   writes the chunk's normalised output and log-sum-exp:
+ *     part_o[b][h][s][:]  = sum_{j in chunk} softmax_j(scale q . k_j) v_j
+ *     part_lse[b][h][s]   = log sum_{j in chunk} exp(scale q . k_j)
+ *   An empty chunk (possible when n_splits > L) gets part_o = 0 and
+ *   part_lse = -inf.
+ *   q [B][Hq][d], k_cache/v_cache [B][Hkv][L][d] of dtype dt;
+ *   part_o [B][Hq][n_splits][d] f32, part_lse [B][Hq][n_splits] f32.
+ *   Combine the partials with attn_lse_merge.
+ *   Limits: Hq/Hkv <= 16.
+ */
+attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,
+                        int n_splits, const void *q, const void *k_cache, const void *v_cache,
+                        float *part_o, float *part_lse, void *stream);
+
+/*
+ * attn_lse_merge -- associative merge of split partials by their log-sum-exp:
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),
+ *     o = sum_s w_s o_s / sum_s w_s,   lse = M + log sum_s w_s.
+ *   If every chunk is empty (M = -inf) the result is o = 0, lse = -inf.
+ *   Source: "How tang works" part 3 (the combine is associative, so it tiles
+ *   and parallelises like a sum).
+ *   part_o [B][Hq][n_splits][d], part_lse [B][Hq][n_splits] f32
+ *   -> o [B][Hq][d] f32, lse [B][Hq] f32.
+ */
+attn_status attn_lse_merge(int B, int Hq, int n_splits, int d,
+                           const float *part_o, const float *part_lse,
+                           float *o, float *lse, void *stream);
+
+/* Human-readable name of a status code (a static string). */
+const char *attn_status_str(attn_status s);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -222,6 +222,7 @@ int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
                 int c;
                 for (i = 0; i < Nq; ++i) {
                     double s = dS[i * Nk + j], p = P[i * Nk + j];
+                    if (p == 0.0 && s == 0.0) continue;                          /* masked */
                     for (c = 0; c < d; ++c) {
                         dkg[j * d + c] += scale * s * qh[i * d + c];              /* step 13 */
                         dvg[j * d + c] += p * doh[i * d + c];                      /* step 14 */

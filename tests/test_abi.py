@@ -1,0 +1,163 @@
+"""The C ABI of libattn.so, checked without a GPU.
+
+The library must load, export every function that include/attn.h declares, and
+refuse invalid calls with the documented status before touching the device.
+Only refusal paths are exercised here: each call fails host-side validation,
+so nothing is launched.  (Pointers used below are fake, aligned addresses; the
+library never dereferences them on these paths.)
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_causal_gqa_flash_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on refusal paths
+MIS = ctypes.c_void_p(0x10004)      # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(attn.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return attn.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+                     "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
+                     "attn_status_str", "attn_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), f"libattn.so does not export {name}"
+
+
+def test_status_strings_and_version(L):
+    assert attn.attn_abi_version() == 1
+    assert attn.attn_status_str(OK) == "ok"
+    assert "invalid" in attn.attn_status_str(INVALID)
+    assert "unsupported" in attn.attn_status_str(UNSUPPORTED)
+    assert "workspace" in attn.attn_status_str(WORKSPACE)
+    assert attn.attn_status_str(99) == "unknown status"
+
+
+def _fwd(L, dt=1, B=1, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125, ptrs=None):
+    ptrs = ptrs or [P] * 5
+    return L.attn_fwd(dt, B, Hq, Hkv, N, d, causal, scale, *ptrs, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=0), INVALID), (dict(N=0), INVALID),
+    (dict(d=0), INVALID), (dict(B=-1), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(dt=2), INVALID), (dict(dt=-1), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=8), UNSUPPORTED),
+    (dict(Hq=70000, Hkv=1), UNSUPPORTED),
+])
+def test_fwd_refusals(L, kw, status):
+    assert _fwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_fwd_refuses_null_or_misaligned(L, which):
+    for bad in (NUL, MIS):
+        ptrs = [P] * 5
+        ptrs[which] = bad
+        assert _fwd(L, ptrs=ptrs) == INVALID
+
+
+def test_workspace_size(L):
+    assert L.attn_bwd_workspace_bytes(1, 2, 12, 4, 1024, 64) == 2 * 12 * 1024 * 4
+    assert L.attn_bwd_workspace_bytes(0, 1, 2, 1, 3, 16) == 256
+    assert L.attn_bwd_workspace_bytes(1, 1, 6, 4, 64, 64) == 0     # Hq % Hkv != 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 4, 4, 64, 48) == 0     # unsupported d
+
+
+def _bwd(L, ws=P, ws_bytes=1 << 20, ptrs=None, **kw):
+    a = dict(dt=1, B=1, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125)
+    a.update(kw)
+    ptrs = ptrs or [P] * 9
+    return L.attn_bwd(a["dt"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"],
+                      *ptrs, ws, ws_bytes, NUL)
+
+
+def test_bwd_refusals(L):
+    assert _bwd(L, Hq=5, Hkv=2) == INVALID
+    assert _bwd(L, d=96) == UNSUPPORTED
+    assert _bwd(L, scale=float("-inf")) == INVALID
+    for which in range(9):
+        ptrs = [P] * 9
+        ptrs[which] = NUL
+        assert _bwd(L, ptrs=ptrs) == INVALID
+    need = L.attn_bwd_workspace_bytes(1, 1, 4, 2, 64, 64)
+    assert _bwd(L, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd(L, ws=NUL) == WORKSPACE
+    assert _bwd(L, ws=MIS) == WORKSPACE
+
+
+def _dec(lib_, ptrs=None, **kw):
+    a = dict(dt=1, B=1, Hq=32, Hkv=8, L=4096, d=128, scale=0.088, S=16)
+    a.update(kw)
+    ptrs = ptrs or [P] * 5
+    return lib_.attn_decode(a["dt"], a["B"], a["Hq"], a["Hkv"], a["L"], a["d"], a["scale"], a["S"],
+                            *ptrs, NUL)
+
+
+def test_decode_refusals(L):
+    assert _dec(L, S=0) == INVALID
+    assert _dec(L, S=-3) == INVALID
+    assert _dec(L, L=0) == INVALID
+    assert _dec(L, Hq=12, Hkv=8) == INVALID
+    assert _dec(L, Hq=34, Hkv=2) == UNSUPPORTED      # group of 17 query heads
+    assert _dec(L, d=80) == UNSUPPORTED
+    assert _dec(L, scale=float("nan")) == INVALID
+    for which in range(5):
+        ptrs = [P] * 5
+        ptrs[which] = MIS
+        assert _dec(L, ptrs=ptrs) == INVALID
+
+
+def test_merge_refusals(L):
+    assert L.attn_lse_merge(0, 4, 2, 64, P, P, P, P, NUL) == INVALID
+    assert L.attn_lse_merge(1, 4, 0, 64, P, P, P, P, NUL) == INVALID
+    assert L.attn_lse_merge(1, 4, 2, 12, P, P, P, P, NUL) == UNSUPPORTED
+    assert L.attn_lse_merge(1, 4, 2, 64, NUL, P, P, P, NUL) == INVALID
+    assert L.attn_lse_merge(1, 4, 2, 64, P, P, P, MIS, NUL) == INVALID
+
+
+def test_bwd_stage_refusals(L):
+    assert L.attn_bwd_preprocess(1, 0, 4, 64, 64, P, P, P, NUL) == INVALID
+    assert L.attn_bwd_preprocess(1, 1, 4, 64, 40, P, P, P, NUL) == UNSUPPORTED
+    assert L.attn_bwd_preprocess(1, 1, 4, 64, 64, P, P, MIS, NUL) == INVALID
+    args = [1, 1, 4, 2, 64, 64, 1, 0.125]
+    assert L.attn_bwd_dkdv(1, 1, 4, 3, 64, 64, 1, 0.125, *([P] * 8), NUL) == INVALID
+    assert L.attn_bwd_dkdv(*args, *([P] * 7), NUL, NUL) == INVALID
+    assert L.attn_bwd_dq(1, 1, 4, 2, 64, 64, 1, float("nan"), *([P] * 7), NUL) == INVALID
+    assert L.attn_bwd_dq(*args, *([P] * 6), MIS, NUL) == INVALID
+
+
+def test_no_unexpected_exports(L):
+    """Only the declared attn_* functions are exported with C linkage."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    c_names = {n for n in exported if n.startswith("attn_")}
+    assert c_names == set(_declared_functions())

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU f64 oracle.
+
+Tolerances (max abs = max over every element of |gpu - oracle|; relative
+Frobenius = ||gpu - oracle||_F / ||oracle||_F over the whole tensor):
+  f32 inputs : every output (o, lse, dq, dk, dv) max abs <= 1e-5 on the tiny
+               f32 workload; on the other f32 shapes 1e-5 * max(1, max|oracle|);
+  bf16 inputs: o max abs <= 1e-2, lse max abs <= 1e-3, dq/dk/dv relative
+               Frobenius <= 2e-2.
+Both sides see the same inputs: float32 draws rounded to bf16 where the
+workload is bf16, widened exactly for the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import attention_causal_gqa_flash_amd as attn
+from attention_causal_gqa_flash_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+
+
+def _gpu_fwd_bwd(x, dtype, causal, scale):
+    g = {n: _to_dev(a, dtype) for n, a in x.items()}
+    o, lse = attn.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=scale)
+    dq, dk, dv = attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+
+
+def _relF(got, ref):
+    n = np.linalg.norm(ref)
+    d = np.linalg.norm(got - ref)
+    return d / n if n > 0 else d
+
+
+def _check(got, ref, dtype, tiny_f32=False, label=""):
+    o, lse, dq, dk, dv = got
+    ro, rl, rdq, rdk, rdv = ref
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), label
+    if dtype == "f32":
+        for name, a, b in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rdq), ("dk", dk, rdk),
+                           ("dv", dv, rdv)):
+            tol = 1e-5 if tiny_f32 else 1e-5 * max(1.0, float(np.abs(b).max()))
+            err = float(np.abs(a - b).max())
+            assert err <= tol, f"{label} {name}: max abs {err:.3e} > {tol:.1e}"
+    else:
+        eo = float(np.abs(o - ro).max())
+        el = float(np.abs(lse - rl).max())
+        assert eo <= 1e-2, f"{label} o: max abs {eo:.3e}"
+        assert el <= 1e-3, f"{label} lse: max abs {el:.3e}"
+        for name, a, b in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            e = _relF(a, b)
+            assert e <= 2e-2 or np.linalg.norm(a - b) <= 1e-6, f"{label} {name}: relF {e:.3e}"
+
+
+def _oracle_fwd_bwd(x, causal, scale):
+    ro, rl = oracle.attn_fwd(x["q"], x["k"], x["v"], causal, scale)
+    rdq, rdk, rdv = oracle.attn_bwd(x["q"], x["k"], x["v"], x["dout"], causal, scale)
+    return ro, rl, rdq, rdk, rdv
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [W.C1, W.C2, W.C3_128, W.C3_512], ids=lambda c: c.name)
+def test_workload_full(cfg):
+    print(f"\n[case] {cfg.name} B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} N={cfg.N} d={cfg.d}", flush=True)
+    x = W.train_inputs(cfg)
+    got = _gpu_fwd_bwd(x, cfg.dtype, True, cfg.scale)
+    ref = _oracle_fwd_bwd(x, True, cfg.scale)
+    _check(got, ref, cfg.dtype, tiny_f32=(cfg is W.C1), label=cfg.name)
+
+
+def test_long_context_sampled_groups():
+    """N = 4096, d = 128, 32/8 heads: the whole problem on the GPU, the oracle on two
+    grouped-query groups (a key/value head and its 4 query heads), plus
+    properties that hold over the whole output."""
+    cfg = W.C4
+    print(f"\n[case] {cfg.name} sampled groups 0 and 7", flush=True)
+    x = W.train_inputs(cfg)
+    o, lse, dq, dk, dv = _gpu_fwd_bwd(x, cfg.dtype, True, cfg.scale)
+    G = cfg.Hq // cfg.Hkv
+    for g in (0, cfg.Hkv - 1):
+        hs = slice(g * G, (g + 1) * G)
+        xs = {"q": x["q"][:, hs], "k": x["k"][:, g:g + 1], "v": x["v"][:, g:g + 1],
+              "dout": x["dout"][:, hs]}
+        ref = _oracle_fwd_bwd(xs, True, cfg.scale)
+        got = (o[:, hs], lse[:, hs], dq[:, hs], dk[:, g:g + 1], dv[:, g:g + 1])
+        _check(got, ref, cfg.dtype, label=f"{cfg.name} group {g}")
+    # whole-output properties: sum_j dk_j = 0 (key-shift invariance) and
+    # sum_j dv_j = sum over the group's query heads and rows of dout
+    dk_sum = dk.sum(axis=2)
+    assert np.linalg.norm(dk_sum) <= 2e-2 * np.linalg.norm(dk) / math.sqrt(cfg.N) * 10
+    dsum = x["dout"].astype(np.float64).reshape(cfg.B, cfg.Hkv, G, cfg.N, cfg.d).sum(axis=(2, 3))
+    assert _relF(dv.sum(axis=2), dsum) <= 1e-2
+
+
+def test_decode_workload():
+    cfg = W.C5
+    print(f"\n[case] {cfg.name}", flush=True)
+    x = W.decode_inputs(cfg)
+    g = {n: _to_dev(a, cfg.dtype) for n, a in x.items()}
+    po, pl = attn.attn_decode(g["q"], g["k_cache"], g["v_cache"], cfg.n_splits, scale=cfg.scale)
+    o, lse = attn.attn_lse_merge(po, pl)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.attn_decode(x["q"], x["k_cache"], x["v_cache"], cfg.scale, cfg.n_splits)
+    ro, rl = oracle.lse_merge(rpo, rpl)
+    assert float(np.abs(po.cpu().numpy() - rpo).max()) <= 1e-2
+    assert float(np.abs(pl.cpu().numpy() - rpl).max()) <= 1e-3
+    assert float(np.abs(o.cpu().numpy() - ro).max()) <= 1e-2
+    assert float(np.abs(lse.cpu().numpy() - rl).max()) <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# further shapes: ragged lengths, every head dim, group sizes, non-causal,
+# other scales, both dtypes
+# ---------------------------------------------------------------------------
+
+EXTRA = [
+    # B, Hq, Hkv, N, d, dtype, causal, scale (None = 1/sqrt(d))
+    (1, 1, 1, 1, 64, "bf16", True, None),
+    (1, 2, 1, 1, 128, "bf16", True, None),
+    (2, 4, 2, 100, 64, "bf16", True, None),
+    (1, 6, 2, 333, 128, "bf16", True, None),
+    (1, 4, 4, 257, 128, "bf16", False, None),
+    (1, 8, 2, 190, 64, "bf16", False, None),
+    (3, 4, 1, 129, 128, "bf16", True, None),
+    (1, 4, 2, 300, 64, "bf16", True, -0.1),
+    (1, 2, 2, 150, 128, "bf16", True, 0.0),
+    (1, 2, 1, 200, 64, "bf16", True, 0.3),
+    (2, 2, 1, 77, 16, "bf16", True, None),
+    (1, 3, 1, 65, 32, "bf16", True, None),
+    (1, 2, 1, 130, 64, "f32", True, None),
+    (1, 2, 2, 50, 128, "f32", False, None),
+    (2, 4, 2, 33, 32, "f32", True, None),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dtype,causal,scale", EXTRA,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_N{c[3]}_d{c[4]}_{c[5]}_{'c' if c[6] else 'nc'}"
+                              f"_s{c[7]}" for c in EXTRA])
+def test_extra_shapes(B, Hq, Hkv, N, d, dtype, causal, scale):
+    print(f"\n[case] B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} {dtype} causal={causal} scale={scale}",
+          flush=True)
+    x = W.random_train(B, Hq, Hkv, N, d, dtype=dtype, seed=N * 7 + d)
+    s = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
+    got = _gpu_fwd_bwd(x, dtype, causal, s)
+    ref = _oracle_fwd_bwd(x, causal, s)
+    _check(got, ref, dtype, label=f"N{N} d{d} {dtype}")
+
+
+def test_deterministic_repeat():
+    """No atomics anywhere: two runs give bit-identical outputs."""
+    x = W.random_train(1, 8, 2, 300, 128, dtype="bf16", seed=5)
+    a = _gpu_fwd_bwd(x, "bf16", True, 0.088)
+    b = _gpu_fwd_bwd(x, "bf16", True, 0.088)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+DECODE = [
+    # B, Hq, Hkv, L, d, n_splits, dtype
+    (1, 32, 8, 4096, 128, 16, "bf16"),
+    (2, 8, 2, 1000, 128, 7, "bf16"),
+    (1, 4, 4, 5, 64, 8, "bf16"),        # more splits than keys: empty chunks
+    (1, 16, 1, 1, 128, 1, "bf16"),      # a one-key cache, G = 16
+    (1, 4, 2, 513, 64, 16, "f32"),
+    (3, 6, 3, 77, 32, 3, "bf16"),
+    (1, 2, 1, 300, 16, 5, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,S,dtype", DECODE,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_L{c[3]}_d{c[4]}_S{c[5]}_{c[6]}" for c in DECODE])
+def test_decode_shapes(B, Hq, Hkv, L, d, S, dtype):
+    print(f"\n[case] decode B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} S={S} {dtype}", flush=True)
+    cfg = W.DecodeConfig("adhoc", dtype, B, Hq, Hkv, L, d, S, seed=L + d)
+    x = W.decode_inputs(cfg)
+    g = {n: _to_dev(a, dtype) for n, a in x.items()}
+    po, pl = attn.attn_decode(g["q"], g["k_cache"], g["v_cache"], S, scale=cfg.scale)
+    o, lse = attn.attn_lse_merge(po, pl)
+    torch.cuda.synchronize()
+    rpo, rpl = oracle.attn_decode(x["q"], x["k_cache"], x["v_cache"], cfg.scale, S)
+    ro, rl = oracle.lse_merge(rpo, rpl)
+    tol_o, tol_l = (1e-5, 1e-5) if dtype == "f32" else (1e-2, 1e-3)
+    gpl = pl.cpu().numpy()
+    empty = np.isneginf(rpl)
+    assert np.array_equal(np.isneginf(gpl), empty)
+    assert float(np.abs(gpl[~empty] - rpl[~empty]).max()) <= tol_l
+    assert float(np.abs(po.cpu().numpy() - rpo).max()) <= tol_o
+    assert float(np.abs(o.cpu().numpy() - ro).max()) <= tol_o
+    assert float(np.abs(lse.cpu().numpy() - rl).max()) <= tol_l
+    # the decoded row equals the last row of a causal forward over the cache
+    full_o, full_l = oracle.attn_fwd(x["q"][:, :, None], x["k_cache"], x["v_cache"], False, cfg.scale)
+    assert float(np.abs(o.cpu().numpy() - full_o[:, :, 0]).max()) <= tol_o
+
+
+def test_merge_all_empty():
+    po = torch.zeros((1, 3, 4, 64), device="cuda")
+    pl = torch.full((1, 3, 4), float("-inf"), device="cuda")
+    o, lse = attn.attn_lse_merge(po, pl)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0).item()
+    assert torch.all(torch.isneginf(lse)).item()
+
+
+def test_invalid_call_leaves_outputs_untouched():
+    q = torch.zeros((1, 3, 8, 64), device="cuda", dtype=torch.bfloat16)
+    k = torch.zeros((1, 2, 8, 64), device="cuda", dtype=torch.bfloat16)
+    o = torch.full((1, 3, 8, 64), 7.0, device="cuda")
+    lse = torch.full((1, 3, 8), 7.0, device="cuda")
+    with pytest.raises(attn.AttnError):
+        attn.attn_fwd(q, k, k, o=o, lse=lse)          # Hq % Hkv != 0
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0).item() and torch.all(lse == 7.0).item()
