@@ -16,13 +16,14 @@
 //     query tiles of every query head of the group past them.  4 waves = 2 key
 //     blocks x 2 query halves, each wave a 32x32 (query x key) tile per step;
 //     scores are laid out S = Q K^T (lane = key column), so P and dS feed the
-//     dV and dK MFMAs straight from registers.  The two query-half partials are
-//     summed through LDS at the end.
+//     dV and dK MFMAs straight from registers, and Q^T, dO^T come from the
+//     row-major Q and dO tiles through the transposed LDS read.  The two query
+//     halves' partials are summed through LDS at the end.
 //   * dq: query-stationary, the forward's layout (lane = query row, S^T = K Q^T)
-//     with dQ^T = K^T dS^T accumulated in registers; P and dP are recomputed.
-// Staging: every tile is loaded as (4 rows x 8 columns) units, stored to LDS
-// row-major and, where an MFMA needs the other operand order, also transposed
-// (the 4x8 block is transposed in registers and written as 8-byte rows).
+//     with dQ^T = K^T dS^T accumulated in registers; P and dP are recomputed,
+//     K^T is read from the row-major K tile through the transposed LDS read.
+// Both double-buffer their LDS tiles with one barrier per step, the next
+// step's global loads in flight during the current step's MFMAs.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -31,46 +32,34 @@
 namespace attn {
 namespace {
 
-constexpr int kPad = 8;
+constexpr int kPad = 16;
 
-// Transpose a 4-row x 8-column bf16 block held as 4 rows of uint4 and write it
-// as 8 rows of 4 elements: dst(e, 0..3) = src(0..3, e); row stride in elements.
-__device__ __forceinline__ void store_transposed_4x8(uint16_t *dst, int stride, const uint4 (&r)[4])
+// Global -> registers for one tile of 64 rows of two row-major tensors (rows
+// past N clamped to N-1; the callers give such rows zero weight), and back to LDS.
+template <int D, int CH_T>
+__device__ __forceinline__ void load_tile2(uint4 (&a)[CH_T], uint4 (&b)[CH_T], const uint16_t *A,
+                                           const uint16_t *Bm, int r0, int N, int tid)
 {
-    const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-    const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
-    const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
-    const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint32_t lo, hi;
-        if (e & 1) {
-            lo = (w0[wd] >> 16) | (w1[wd] & 0xffff0000u);
-            hi = (w2[wd] >> 16) | (w3[wd] & 0xffff0000u);
-        } else {
-            lo = (w0[wd] & 0xffffu) | (w1[wd] << 16);
-            hi = (w2[wd] & 0xffffu) | (w3[wd] << 16);
-        }
-        *(uint2 *)(dst + (size_t)e * stride) = make_uint2(lo, hi);
+    for (int i = 0; i < CH_T; ++i) {
+        const int c = tid + 256 * i;
+        const int row = min(r0 + c / (D / 8), N - 1), col = (c % (D / 8)) * 8;
+        a[i] = *(const uint4 *)(A + (size_t)row * D + col);
+        b[i] = *(const uint4 *)(Bm + (size_t)row * D + col);
     }
 }
 
-// 8 bf16 of an MFMA operand read from a key- or query-contiguous LDS row in the
-// permuted order that matches the 32x32 accumulator layout: elements
-// 0..3 = row[16t + 4hf + 0..3], elements 4..7 = row[16t + 8 + 4hf + 0..3].
-__device__ __forceinline__ bf16x8 read_perm_operand(const uint16_t *row, int t, int hf)
+template <int D, int CH_T, int ROW>
+__device__ __forceinline__ void store_tile2(uint16_t (*sa)[ROW], uint16_t (*sb)[ROW],
+                                            const uint4 (&a)[CH_T], const uint4 (&b)[CH_T], int tid)
 {
-    const uint2 lo = *(const uint2 *)(row + 16 * t + 4 * hf);
-    const uint2 hi = *(const uint2 *)(row + 16 * t + 8 + 4 * hf);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
-// Accumulator registers r0..r0+7 packed to a bf16 MFMA operand.
-__device__ __forceinline__ bf16x8 pack_operand(const f32x16 &acc, int r0)
-{
-    return as_bf16x8(make_uint4(pack_bf16x2(acc[r0 + 0], acc[r0 + 1]), pack_bf16x2(acc[r0 + 2], acc[r0 + 3]),
-                                pack_bf16x2(acc[r0 + 4], acc[r0 + 5]), pack_bf16x2(acc[r0 + 6], acc[r0 + 7])));
+#pragma unroll
+    for (int i = 0; i < CH_T; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *(uint4 *)&sa[row][col] = a[i];
+        *(uint4 *)&sb[row][col] = b[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -87,31 +76,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal)
 {
     constexpr int KS = D / 16, DB = D / 32;
-    constexpr int ROW = D + kPad;            // row-major tiles [64][ROW]
-    constexpr int TROW = kKvBM + kPad;       // transposed tiles [D][TROW]
-    constexpr int UNITS = (kKvBM / 4) * (D / 8);
-    constexpr int UNITS_T = (UNITS + 255) / 256;
+    constexpr int ROW = D + kPad;
+    constexpr int CH_T = kKvBM * D / 8 / 256;      // 16-byte chunks per thread per tile
+    static_assert(kKvBM * D / 8 % 256 == 0, "tile must split evenly over the workgroup");
 
-    // One LDS block: the staging tiles during the loop, then the reduction
-    // buffer for the two query halves' partial dK^T and dV^T.
+    // One LDS block: double-buffered Q, dO, lse and D tiles during the loop,
+    // then the reduction buffer for the two query halves' dK^T and dV^T.
     struct Smem {
-        uint16_t q[kKvBM][ROW];
-        uint16_t dO[kKvBM][ROW];
-        uint16_t qt[D][TROW];
-        uint16_t dOt[D][TROW];
-        float lse[kKvBM];
-        float dd[kKvBM];
+        uint16_t q[2][kKvBM][ROW];
+        uint16_t dO[2][kKvBM][ROW];
+        float lse[2][kKvBM];
+        float dd[2][kKvBM];
     };
     constexpr int RED = DB * 16 * 64;        // floats per (key block, dK or dV) partial
     static_assert(4 * RED * sizeof(float) <= sizeof(Smem), "reduction must fit in the staging LDS");
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(Smem)];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
-    auto &sq = sm.q;
-    auto &sdo = sm.dO;
-    auto &sqt = sm.qt;
-    auto &sdot = sm.dOt;
-    auto &slse = sm.lse;
-    auto &sdd = sm.dd;
 
     const int BG = B * Hkv;
     const int kt = blockIdx.x / BG;          // causal: low key tiles see the most queries
@@ -131,18 +111,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
 
-    // K^T and V^T operands, resident: lane holds row kj, dims 16ks + 8hf .. +7.
+    // K^T and V^T operands, resident: lane holds row kj (clamped), dims 16ks + 8hf .. +7.
     bf16x8 kf[KS], vf[KS];
+    {
+        const int kr = min(kj, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
-        if (kj < N) {
-            uk = *(const uint4 *)(Kg + (size_t)kj * D + 16 * ks + 8 * hf);
-            uv = *(const uint4 *)(Vg + (size_t)kj * D + 16 * ks + 8 * hf);
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 uk = *(const uint4 *)(Kg + (size_t)kr * D + 16 * ks + 8 * hf);
+            const uint4 uv = *(const uint4 *)(Vg + (size_t)kr * D + 16 * ks + 8 * hf);
+            uk.x ^= ksign; uk.y ^= ksign; uk.z ^= ksign; uk.w ^= ksign;
+            kf[ks] = as_bf16x8(uk);
+            vf[ks] = as_bf16x8(uv);
         }
-        uk.x ^= ksign; uk.y ^= ksign; uk.z ^= ksign; uk.w ^= ksign;
-        kf[ks] = as_bf16x8(uk);
-        vf[ks] = as_bf16x8(uv);
     }
 
     f32x16 dva[DB], dka[DB];
@@ -153,114 +133,96 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 
     const int nqt = (N + kKvBM - 1) / kKvBM;
     const int qt0 = causal ? k0 / kKvBM : 0;
+    const int nq = nqt - qt0;
+    const int steps = G * nq;                // (query head, query tile) pairs
 
-    uint4 qst[UNITS_T][4], dst[UNITS_T][4];
+    uint4 qst[CH_T], dst[CH_T];     // staging registers for one step
     float lst = 0.f, dstv = 0.f;
 
-    for (int hh = 0; hh < G; ++hh) {
-        const int h = g * G + hh;
-        const uint16_t *Qh = Q + ((size_t)b * Hq + h) * (size_t)N * D;
-        const uint16_t *dOh = dO + ((size_t)b * Hq + h) * (size_t)N * D;
-        const float *Lh = LSE + ((size_t)b * Hq + h) * N;
-        const float *Dh = Dws + ((size_t)b * Hq + h) * N;
-        for (int qt = qt0; qt < nqt; ++qt) {
-            const int q0 = qt * kKvBM;
-            // global -> registers
+// step s covers query head g*G + s/nq, query tile qt0 + s%nq
+#define ATTN_LOAD_STEP(s_)                                                                      \
+    {                                                                                           \
+        const size_t hrow_ = ((size_t)b * Hq + g * G + (s_) / nq) * N;                          \
+        const int q0_ = (qt0 + (s_) % nq) * kKvBM;                                              \
+        load_tile2<D, CH_T>(qst, dst, Q + hrow_ * D, dO + hrow_ * D, q0_, N, tid);              \
+        if (tid < kKvBM) {                                                                      \
+            const int row_ = q0_ + tid;                                                         \
+            lst = row_ < N ? LSE[hrow_ + row_] * kLog2e : INFINITY; /* P = 0 on padded rows */  \
+            dstv = row_ < N ? Dws[hrow_ + row_] : 0.f;                                          \
+        }                                                                                       \
+    }
+#define ATTN_STORE_STEP(buf_)                                                                   \
+    {                                                                                           \
+        store_tile2<D, CH_T, ROW>(sm.q[buf_], sm.dO[buf_], qst, dst, tid);                      \
+        if (tid < kKvBM) {                                                                      \
+            sm.lse[buf_][tid] = lst;                                                            \
+            sm.dd[buf_][tid] = dstv;                                                            \
+        }                                                                                       \
+    }
+    if (steps > 0) {
+        ATTN_LOAD_STEP(0);
+        ATTN_STORE_STEP(0);
+    }
+    __syncthreads();
+    for (int s = 0; s < steps; ++s) {
+        const int buf = s & 1;
+        // unconditional prefetch (see the dq loop); the last step re-reads itself
+        ATTN_LOAD_STEP(min(s + 1, steps - 1));
+        const int q0 = (qt0 + s % nq) * kKvBM;
+        const int qb0 = q0 + 32 * qh;       // first query row of this wave's block
+        const bool active = qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb);
+        if (active) {
+            f32x16 sacc, pacc;
 #pragma unroll
-            for (int i = 0; i < UNITS_T; ++i) {
-                const int u = tid + 256 * i;
-                if (u < UNITS) {
-                    const int rq = u / (D / 8), dc = u % (D / 8);
+            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = q0 + 4 * rq + r;
-                        qst[i][r] = make_uint4(0, 0, 0, 0);
-                        dst[i][r] = make_uint4(0, 0, 0, 0);
-                        if (row < N) {
-                            qst[i][r] = *(const uint4 *)(Qh + (size_t)row * D + dc * 8);
-                            dst[i][r] = *(const uint4 *)(dOh + (size_t)row * D + dc * 8);
-                        }
-                    }
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 aq = as_bf16x8(*(const uint4 *)&sm.q[buf][32 * qh + l32][16 * ks + 8 * hf]);
+                const bf16x8 ad = as_bf16x8(*(const uint4 *)&sm.dO[buf][32 * qh + l32][16 * ks + 8 * hf]);
+                sacc = mfma32x32x16(aq, kf[ks], sacc);
+                pacc = mfma32x32x16(ad, vf[ks], pacc);
+            }
+            // P = exp(scale s - lse), dS = P (dP - D); rows are queries, lane = key.
+            const bool diag = causal && qb0 < k0 + 32 * kb + 32;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int rr = 32 * qh + 8 * a + 4 * hf;       // local query row of r = 4a
+                const float4 l4 = *(const float4 *)&sm.lse[buf][rr];
+                const float4 d4 = *(const float4 *)&sm.dd[buf][rr];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    float p = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
+                    if (diag && kj > q0 + rr + e) p = 0.f;
+                    sacc[r] = p;
+                    pacc[r] = p * (pacc[r] - dv[e]);
                 }
             }
-            if (tid < kKvBM) {
-                const int row = q0 + tid;
-                lst = row < N ? Lh[row] * kLog2e : INFINITY;   // P = 0 on padded rows
-                dstv = row < N ? Dh[row] : 0.f;
-            }
-            __syncthreads();   // previous step's readers are done with LDS
+            // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
 #pragma unroll
-            for (int i = 0; i < UNITS_T; ++i) {
-                const int u = tid + 256 * i;
-                if (u < UNITS) {
-                    const int rq = u / (D / 8), dc = u % (D / 8);
+            for (int tt = 0; tt < 2; ++tt) {
+                const bf16x8 pb = tt ? pack_operand<8>(sacc) : pack_operand<0>(sacc);
+                const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        *(uint4 *)&sq[4 * rq + r][dc * 8] = qst[i][r];
-                        *(uint4 *)&sdo[4 * rq + r][dc * 8] = dst[i][r];
-                    }
-                    store_transposed_4x8(&sqt[dc * 8][4 * rq], TROW, qst[i]);
-                    store_transposed_4x8(&sdot[dc * 8][4 * rq], TROW, dst[i]);
-                }
-            }
-            if (tid < kKvBM) {
-                slse[tid] = lst;
-                sdd[tid] = dstv;
-            }
-            __syncthreads();
-
-            const int qb0 = q0 + 32 * qh;    // first query row of this wave's block
-            const bool active = qb0 < N && kj - l32 < N && (!causal || qb0 + 31 >= k0 + 32 * kb);
-            if (active) {
-                f32x16 sacc, pacc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 aq = as_bf16x8(*(const uint4 *)&sq[32 * qh + l32][16 * ks + 8 * hf]);
-                    const bf16x8 ad = as_bf16x8(*(const uint4 *)&sdo[32 * qh + l32][16 * ks + 8 * hf]);
-                    sacc = mfma32x32x16(aq, kf[ks], sacc);
-                    pacc = mfma32x32x16(ad, vf[ks], pacc);
-                }
-                // P = exp(scale s - lse), dS = P (dP - D); rows are queries, lane = key.
-                const bool diag = causal && qb0 < k0 + 32 * kb + 32;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int rr = 32 * qh + 8 * a + 4 * hf;       // local query row of r = 4a
-                    const float4 l4 = *(const float4 *)&slse[rr];
-                    const float4 d4 = *(const float4 *)&sdd[rr];
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * a + e;
-                        float p = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
-                        if (diag && kj > q0 + rr + e) p = 0.f;
-                        sacc[r] = p;
-                        pacc[r] = p * (pacc[r] - dv[e]);
-                    }
-                }
-                // dV^T += dO^T P,  dK^T += Q^T dS   (k = the wave's 32 queries)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const bf16x8 pb = pack_operand(sacc, 8 * tt);
-                    const bf16x8 sb = pack_operand(pacc, 8 * tt);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 ado = read_perm_operand(&sdot[db * 32 + l32][32 * qh], tt, hf);
-                        const bf16x8 aqt = read_perm_operand(&sqt[db * 32 + l32][32 * qh], tt, hf);
-                        dva[db] = mfma32x32x16(ado, pb, dva[db]);
-                        dka[db] = mfma32x32x16(aqt, sb, dka[db]);
-                    }
+                for (int db = 0; db < DB; ++db) {
+                    const bf16x8 ado = tr_operand(&sm.dO[buf][0][0], ROW, 32 * qh + 16 * tt, db * 32, lane);
+                    const bf16x8 aqt = tr_operand(&sm.q[buf][0][0], ROW, 32 * qh + 16 * tt, db * 32, lane);
+                    dva[db] = mfma32x32x16(ado, pb, dva[db]);
+                    dka[db] = mfma32x32x16(aqt, sb, dka[db]);
                 }
             }
         }
+        ATTN_STORE_STEP(buf ^ 1);
+        __syncthreads();
     }
+#undef ATTN_LOAD_STEP
+#undef ATTN_STORE_STEP
 
-    // Sum the two query halves through LDS (reusing the staging buffers), then
-    // write dK = scale dK^T^T and dV.  Accumulator layout: lane = key column kj,
-    // register r = dim db*32 + 8(r/4) + 4hf + (r&3).
-    __syncthreads();
+    // Sum the two query halves through LDS, then write dK = scale (dK^T)^T and
+    // dV.  Accumulator layout: lane = key column kj, register r = dim
+    // db*32 + 8(r/4) + 4hf + (r&3).
     float *red = reinterpret_cast<float *>(smem_raw);   // [key block][dK, dV][DB*16][64]
     if (qh == 1) {
 #pragma unroll
@@ -275,21 +237,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     if (qh == 0 && kj < N) {
         float *dkrow = dK + (((size_t)b * Hkv + g) * N + kj) * D;
         float *dvrow = dV + (((size_t)b * Hkv + g) * N + kj) * D;
-        const float sgn_scale = scale;
+        const float *rk = red + (kb * 2 + 0) * RED + lane;
+        const float *rv = red + (kb * 2 + 1) * RED + lane;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int d0 = db * 32 + 8 * a + 4 * hf;
+                const int r0 = db * 16 + 4 * a;
                 float4 k4, v4;
-                k4.x = (dka[db][4 * a + 0] + red[(kb * 2) * RED + (db * 16 + 4 * a + 0) * 64 + lane]) * sgn_scale;
-                k4.y = (dka[db][4 * a + 1] + red[(kb * 2) * RED + (db * 16 + 4 * a + 1) * 64 + lane]) * sgn_scale;
-                k4.z = (dka[db][4 * a + 2] + red[(kb * 2) * RED + (db * 16 + 4 * a + 2) * 64 + lane]) * sgn_scale;
-                k4.w = (dka[db][4 * a + 3] + red[(kb * 2) * RED + (db * 16 + 4 * a + 3) * 64 + lane]) * sgn_scale;
-                v4.x = dva[db][4 * a + 0] + red[(kb * 2 + 1) * RED + (db * 16 + 4 * a + 0) * 64 + lane];
-                v4.y = dva[db][4 * a + 1] + red[(kb * 2 + 1) * RED + (db * 16 + 4 * a + 1) * 64 + lane];
-                v4.z = dva[db][4 * a + 2] + red[(kb * 2 + 1) * RED + (db * 16 + 4 * a + 2) * 64 + lane];
-                v4.w = dva[db][4 * a + 3] + red[(kb * 2 + 1) * RED + (db * 16 + 4 * a + 3) * 64 + lane];
+                k4.x = (dka[db][4 * a + 0] + rk[(r0 + 0) * 64]) * scale;
+                k4.y = (dka[db][4 * a + 1] + rk[(r0 + 1) * 64]) * scale;
+                k4.z = (dka[db][4 * a + 2] + rk[(r0 + 2) * 64]) * scale;
+                k4.w = (dka[db][4 * a + 3] + rk[(r0 + 3) * 64]) * scale;
+                v4.x = dva[db][4 * a + 0] + rv[(r0 + 0) * 64];
+                v4.y = dva[db][4 * a + 1] + rv[(r0 + 1) * 64];
+                v4.z = dva[db][4 * a + 2] + rv[(r0 + 2) * 64];
+                v4.w = dva[db][4 * a + 3] + rv[(r0 + 3) * 64];
                 *(float4 *)(dkrow + d0) = k4;
                 *(float4 *)(dvrow + d0) = v4;
             }
@@ -311,13 +275,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int ROW = D + kPad;
-    constexpr int TROW = kQBN + kPad;
-    constexpr int UNITS = (kQBN / 4) * (D / 8);
-    constexpr int UNITS_T = (UNITS + 255) / 256;
+    constexpr int CH_T = kQBN * D / 8 / 256;
+    static_assert(kQBN * D / 8 % 256 == 0, "tile must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sk[kQBN][ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[kQBN][ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t skt[D][TROW];
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kQBN][ROW];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kQBN][ROW];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -339,18 +301,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
 
     bf16x8 qf[KS], dof[KS];
+    {
+        const int qr = min(qi, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 uq = make_uint4(0, 0, 0, 0), ud = make_uint4(0, 0, 0, 0);
-        if (qi < N) {
-            uq = *(const uint4 *)(Q + (qrow0 + qi) * D + 16 * ks + 8 * hf);
-            ud = *(const uint4 *)(dO + (qrow0 + qi) * D + 16 * ks + 8 * hf);
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 uq = *(const uint4 *)(Q + (qrow0 + qr) * D + 16 * ks + 8 * hf);
+            const uint4 ud = *(const uint4 *)(dO + (qrow0 + qr) * D + 16 * ks + 8 * hf);
+            uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
+            qf[ks] = as_bf16x8(uq);
+            dof[ks] = as_bf16x8(ud);
         }
-        uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
-        qf[ks] = as_bf16x8(uq);
-        dof[ks] = as_bf16x8(ud);
     }
-    const float lse2 = qi < N ? LSE[qrow0 + qi] * kLog2e : 0.f;
+    const float lse2 = qi < N ? LSE[qrow0 + qi] * kLog2e : INFINITY;
     const float Di = qi < N ? Dws[qrow0 + qi] : 0.f;
 
     f32x16 dqa[DB];
@@ -361,43 +323,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
     const int kv_end = causal ? min(N, q0 + kQBM) : N;
     const int ntiles = (kv_end + kQBN - 1) / kQBN;
-    uint4 kst[UNITS_T][4], vst[UNITS_T][4];
 
+    uint4 kst[CH_T], vst[CH_T];     // staging registers for one tile
+
+    load_tile2<D, CH_T>(kst, vst, Kg, Vg, 0, N, tid);
+    store_tile2<D, CH_T, ROW>(sk[0], sv[0], kst, vst, tid);
+    __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        // Prefetch unconditionally (the last iteration re-reads its own tile into
+        // the idle buffer): a conditional prefetch makes the compiler keep the
+        // staging registers in scratch memory.
+        load_tile2<D, CH_T>(kst, vst, Kg, Vg, min(t + 1, ntiles - 1) * kQBN, N, tid);
         const int kv0 = t * kQBN;
-#pragma unroll
-        for (int i = 0; i < UNITS_T; ++i) {
-            const int u = tid + 256 * i;
-            if (u < UNITS) {
-                const int rk = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = kv0 + 4 * rk + r;
-                    kst[i][r] = make_uint4(0, 0, 0, 0);
-                    vst[i][r] = make_uint4(0, 0, 0, 0);
-                    if (key < N) {
-                        kst[i][r] = *(const uint4 *)(Kg + (size_t)key * D + dc * 8);
-                        vst[i][r] = *(const uint4 *)(Vg + (size_t)key * D + dc * 8);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < UNITS_T; ++i) {
-            const int u = tid + 256 * i;
-            if (u < UNITS) {
-                const int rk = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    *(uint4 *)&sk[4 * rk + r][dc * 8] = kst[i][r];
-                    *(uint4 *)&sv[4 * rk + r][dc * 8] = vst[i][r];
-                }
-                store_transposed_4x8(&skt[dc * 8][4 * rk], TROW, kst[i]);
-            }
-        }
-        __syncthreads();
-
         const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
         if (active) {
             const bool need_mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
@@ -408,8 +346,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
                 for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 ak = as_bf16x8(*(const uint4 *)&sk[kb * 32 + l32][16 * ks + 8 * hf]);
-                    const bf16x8 av = as_bf16x8(*(const uint4 *)&sv[kb * 32 + l32][16 * ks + 8 * hf]);
+                    const bf16x8 ak = as_bf16x8(*(const uint4 *)&sk[buf][kb * 32 + l32][16 * ks + 8 * hf]);
+                    const bf16x8 av = as_bf16x8(*(const uint4 *)&sv[buf][kb * 32 + l32][16 * ks + 8 * hf]);
                     sacc = mfma32x32x16(ak, qf[ks], sacc);
                     pacc = mfma32x32x16(av, dof[ks], pacc);
                 }
@@ -425,15 +363,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
                 // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const bf16x8 sb = pack_operand(pacc, 8 * tt);
+                    const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const bf16x8 a = read_perm_operand(&skt[db * 32 + l32][kb * 32], tt, hf);
+                        const bf16x8 a = tr_operand(&sk[buf][0][0], ROW, kb * 32 + 16 * tt, db * 32, lane);
                         dqa[db] = mfma32x32x16(a, sb, dqa[db]);
                     }
                 }
             }
         }
+        store_tile2<D, CH_T, ROW>(sk[buf ^ 1], sv[buf ^ 1], kst, vst, tid);
+        __syncthreads();
     }
 
     if (qi < N) {

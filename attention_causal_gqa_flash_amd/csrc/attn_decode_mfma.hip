@@ -1,0 +1,305 @@
+// attn_decode_mfma.hip -- split-KV decode on gfx950 matrix cores (bf16 caches).
+//
+// One new query token per query head attends to every cached key; the keys are
+// cut into contiguous chunks, each chunk yields a normalised partial output and
+// its log-sum-exp, and the partials combine associatively ("tang --
+// differentiable computing in Rust", "How tang works" part 3: the combine is
+// associative, so it tiles and parallelises like any sum; the decode workload
+// is one row of attention per new token, "RustingBrain" docs, "Generating
+// text").  Decoding reads every cached byte once, so the kernel is bound by HBM
+// bandwidth ("Generating text": a decode step reads every active weight once).
+//
+// Layout of the work:
+//   * one workgroup per (split, key/value head, batch) handles all G <= 16
+//     query heads of the group, so each cached K/V byte is read from HBM once;
+//   * 8 waves, each takes 32-key blocks of the chunk (block w, w+8, ...); for
+//     the 4096-key, 16-split decode every wave has exactly one block, and all
+//     of a workgroup's loads are in flight before any arithmetic;
+//   * scores S^T = K q^T on v_mfma_f32_16x16x32_bf16 with K rows loaded from
+//     HBM straight into operand registers (no LDS) and q^T resident;
+//   * O = P V on the same instruction: P comes from the score registers (each
+//     lane holds one head and 4+4 keys, exactly an A operand), V is staged in
+//     the wave's own LDS slice and read back key-contiguous with
+//     ds_read_b64_tr_b16;
+//   * the 8 waves' running states (max, sum, output) merge through LDS with the
+//     associative combine, and the workgroup writes (part_o, part_lse).
+#include "attn_device.h"
+#include "attn_launch.h"
+
+#include <math.h>
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kBlk = 32;        // keys per wave step
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool kFused>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, float *__restrict__ part_o, float *__restrict__ part_lse,
+    float *__restrict__ o, float *__restrict__ lse, unsigned int *__restrict__ counters, int Hq,
+    int Hkv, int L, float scale, int n_splits)
+{
+    constexpr int KS = D / 32;            // k-steps over the head dim (32 per MFMA)
+    constexpr int DB = D / 16;            // 16-column blocks of the output
+    constexpr int VROW = D + 8;           // padded LDS row of the V tile
+    constexpr int VCH = kBlk * D / 8 / 64;   // 16-byte V chunks per lane per block
+
+    // per-wave V tiles; reused afterwards for the cross-wave merge
+    constexpr int VBYTES = kWaves * kBlk * VROW * 2;
+    constexpr int MBYTES = kWaves * 16 * D * 4 + 2 * kWaves * 16 * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[VBYTES > MBYTES ? VBYTES : MBYTES];
+    uint16_t(*sv)[kBlk][VROW] = reinterpret_cast<uint16_t(*)[kBlk][VROW]>(smem);
+
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, grp = lane >> 4;
+
+    // scores are x = q.k; the softmax runs on x * c2 in base 2 (c2 may be negative)
+    const float c2 = scale * kLog2e;
+
+    const long C = ((long)L + n_splits - 1) / n_splits;
+    const long j0 = (long)s * C;
+    const long j1 = min((long)L, j0 + C);
+    const uint16_t *Kg = kc + ((size_t)b * Hkv + g) * (size_t)L * D;
+    const uint16_t *Vg = vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+
+    // q^T operand: lane holds head l16 (rows past G read head G-1 and are never
+    // written out), dims 32ks + 8grp .. +7.  Loaded without a branch and
+    // consumed only by the first MFMA, so its latency overlaps the K/V loads.
+    bf16x8 qf[KS];
+    {
+        const int hq = g * G + min(l16, G - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = as_bf16x8(*(const uint4 *)(q + ((size_t)b * Hq + hq) * D + 32 * ks + 8 * grp));
+    }
+
+    float m_run = -INFINITY;   // running max of x * c2 for head l16
+    float l_run = 0.f;         // this lane's share of the running sum
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (long kb0 = j0 + (long)kBlk * wave; kb0 < j1; kb0 += (long)kBlk * kWaves) {
+        // ---- issue every load of the block: K operands and the V tile ----
+        // Rows past the chunk end are clamped to its last key: their scores are
+        // masked to -inf below, so their (finite) values get zero weight.
+        uint4 kraw[2][KS];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const long key = min(kb0 + 16 * kb + l16, j1 - 1);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kraw[kb][ks] = *(const uint4 *)(Kg + (size_t)key * D + 32 * ks + 8 * grp);
+        }
+        uint4 vraw[VCH];
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = lane + 64 * i;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            const long key = min(kb0 + row, j1 - 1);
+            vraw[i] = *(const uint4 *)(Vg + (size_t)key * D + col);
+        }
+        // ---- scores: S^T (16 keys x 16 heads) for the two 16-key halves ----
+        f32x4 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sacc[kb] = mfma16x16x32(as_bf16x8(kraw[kb][ks]), qf[ks], sacc[kb]);
+        }
+        // lane: head l16, keys kb0 + 16kb + 4grp + r
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = sacc[kb][r] * c2;
+                if (kb0 + 16 * kb + 4 * grp + r >= j1) x = -INFINITY;
+                sacc[kb][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);            // finite: the block's first key is valid
+        const float alpha = m_run == -INFINITY ? 0.f : exp2_fast(m_run - m_new);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2_fast(sacc[kb][r] - m_new);
+                sacc[kb][r] = p;
+                rs += p;
+            }
+        l_run = fmaf(l_run, alpha, rs);
+        m_run = m_new;
+        // rescale the output rows (heads 4grp + r) by their heads' alpha
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][r] *= ar;
+        }
+        // P operand: head l16, keys 4grp + 0..3 then 16 + 4grp + 0..3
+        const bf16x8 pa = as_bf16x8(make_uint4(pack_bf16x2(sacc[0][0], sacc[0][1]), pack_bf16x2(sacc[0][2], sacc[0][3]),
+                                               pack_bf16x2(sacc[1][0], sacc[1][1]), pack_bf16x2(sacc[1][2], sacc[1][3])));
+        // ---- V tile to this wave's LDS slice, then O += P V ----
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = lane + 64 * i;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            *(uint4 *)&sv[wave][row][col] = vraw[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            // source lane l16 of group grp addresses key (4grp + l16/4), dims 16db + 4(l16%4)
+            const uint2 lo = lds_read_tr16(&sv[wave][4 * grp + (l16 >> 2)][16 * db + 4 * (l16 & 3)]);
+            const uint2 hi = lds_read_tr16(&sv[wave][16 + 4 * grp + (l16 >> 2)][16 * db + 4 * (l16 & 3)]);
+            const bf16x8 vb = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            oacc[db] = mfma16x16x32(pa, vb, oacc[db]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- per-wave state -> LDS, then combine the 8 waves ----
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();                                   // V slices are no longer read
+    float *wo = reinterpret_cast<float *>(smem);       // [wave][head 16][D]
+    float *wm = wo + kWaves * 16 * D;                  // [wave][16]
+    float *wl = wm + kWaves * 16;                      // [wave][16]
+    if (grp == 0) {
+        wm[wave * 16 + l16] = m_run;
+        wl[wave * 16 + l16] = l_run;
+    }
+    // output layout: lane holds column 16db + l16 of heads 4grp + r
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wo[(wave * 16 + 4 * grp + r) * D + 16 * db + l16] = oacc[db][r];
+    __syncthreads();
+    for (int t = tid; t < G * D; t += 512) {
+        const int hh = t / D, c = t % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + hh]);
+        const size_t ob = ((size_t)b * Hq + g * G + hh) * n_splits + s;
+        if (M == -INFINITY) {                          // empty chunk: the identity
+            part_o[ob * D + c] = 0.f;
+            if (c == 0) part_lse[ob] = -INFINITY;
+            continue;
+        }
+        float lt = 0.f, at = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = wm[w * 16 + hh];
+            if (mw == -INFINITY) continue;
+            const float e = exp2_fast(mw - M);
+            lt = fmaf(wl[w * 16 + hh], e, lt);
+            at = fmaf(wo[(w * 16 + hh) * D + c], e, at);
+        }
+        part_o[ob * D + c] = at / lt;
+        if (c == 0) part_lse[ob] = M * kLn2 + logf(lt);
+    }
+    if constexpr (kFused) {
+        // The last workgroup of this (batch, kv head) to finish merges the
+        // n_splits partials of its G query heads into o and lse, then resets
+        // the counter so the workspace is zero again for the next call.
+        // The barrier completes every wave's partial stores; one wave then
+        // releases them device-wide (one L2 writeback per workgroup, not one per
+        // wave) and bumps the counter.
+        __shared__ unsigned int s_last;
+        __syncthreads();
+        if (wave == 0) {
+            __threadfence();
+            if (lane == 0) {
+                const unsigned int done = atomicAdd(&counters[(size_t)b * Hkv + g], 1u);
+                s_last = done == (unsigned int)(n_splits - 1);
+            }
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (wave == 0) __threadfence();        // acquire the other workgroups' partials
+        __syncthreads();
+        // per head: M = max_s lse_s and W = sum_s exp(lse_s - M), one wave per head
+        float *sMW = reinterpret_cast<float *>(smem);     // [16][2]
+        for (int hh = wave; hh < G; hh += kWaves) {
+            const float *pl = part_lse + ((size_t)b * Hq + g * G + hh) * n_splits;
+            float M = -INFINITY;
+            for (int x = lane; x < n_splits; x += 64) M = fmaxf(M, pl[x]);
+            M = wave_max(M);
+            float W = 0.f;
+            if (M != -INFINITY)
+                for (int x = lane; x < n_splits; x += 64) {
+                    const float lx = pl[x];
+                    if (lx != -INFINITY) W += expf(lx - M);
+                }
+            W = wave_sum(W);
+            if (lane == 0) { sMW[2 * hh] = M; sMW[2 * hh + 1] = W; }
+        }
+        __syncthreads();
+        for (int t = tid; t < G * D; t += 512) {
+            const int hh = t / D, c = t % D;
+            const size_t row = (size_t)b * Hq + g * G + hh;
+            const float M = sMW[2 * hh], W = sMW[2 * hh + 1];
+            if (M == -INFINITY) {                 // every chunk empty
+                o[row * D + c] = 0.f;
+                if (c == 0) lse[row] = -INFINITY;
+                continue;
+            }
+            const float *pl = part_lse + row * n_splits;
+            const float *po = part_o + row * (size_t)n_splits * D + c;
+            float acc = 0.f;
+#pragma unroll 8
+            for (int x = 0; x < n_splits; ++x) {
+                const float lx = pl[x];
+                const float w = lx == -INFINITY ? 0.f : expf(lx - M);
+                acc = fmaf(w, po[(size_t)x * D], acc);
+            }
+            o[row * D + c] = acc / W;
+            if (c == 0) lse[row] = M + logf(W);
+        }
+        if (tid == 0) counters[(size_t)b * Hkv + g] = 0u;
+    }
+}
+
+}  // namespace
+
+bool decode_mfma_supported(int dt, int d, int G) { return dt == kBF16 && (d == 64 || d == 128) && G <= 16; }
+
+hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
+                             const void *q, const void *kc, const void *vc, float *part_o,
+                             float *part_lse, float *o, float *lse, unsigned int *counters,
+                             hipStream_t st)
+{
+    dim3 grid(n_splits, Hkv, B);
+    const bool fused = o != nullptr;
+#define ATTN_DEC(DV, F)                                                                           \
+    hipLaunchKernelGGL((decode_mfma_kernel<DV, F>), grid, dim3(512), 0, st, (const uint16_t *)q,  \
+                       (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, o, lse,      \
+                       counters, Hq, Hkv, L, scale, n_splits)
+    if (d == 128) {
+        if (fused) ATTN_DEC(128, true); else ATTN_DEC(128, false);
+    } else if (d == 64) {
+        if (fused) ATTN_DEC(64, true); else ATTN_DEC(64, false);
+    } else {
+        return hipErrorInvalidValue;
+    }
+#undef ATTN_DEC
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -10,24 +10,25 @@
 // RustingBrain docs ("What is in the box"); grouped-query head sharing as in
 // the same docs.
 //
-// Layout of the work (MI355X-first, not a translation of any other design):
+// Layout of the work:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //     each wave owns 32 query rows and every lane owns ONE query row, so the
 //     softmax state (m, l) of a row lives in a single lane pair (l, l^32);
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-//     the accumulator layout then gives each lane one query and 16 keys, the
-//     row max needs one cross-lane exchange and the row sum none until the end;
-//   * the output is accumulated transposed too, O^T = V^T P^T, so the per-row
-//     rescale by alpha is a per-lane scalar and P^T feeds the next MFMA
-//     straight from registers (the key order inside an MFMA step is permuted to
-//     match the accumulator layout; V^T is read with the same permutation);
-//   * K tiles are staged in LDS row-major, V tiles transposed (key-contiguous)
-//     by a register 4x8 transpose on the way in, double-buffered with one
-//     barrier per tile; the next tile's global loads are in flight during the
-//     current tile's MFMAs;
-//   * exponentials are base 2 with scale*log2(e) folded into one FMA;
-//   * the grid is ordered heaviest query tiles first (causal tiles near the end
-//     of the sequence see the most keys).
+//     the accumulator layout then gives each lane one query and 16 keys per
+//     32-key block, the row max needs one cross-lane exchange and the row sum
+//     none until the end;
+//   * the output is accumulated transposed too, O^T = V^T P^T: the per-row
+//     rescale is a per-lane scalar and P^T feeds the next MFMA straight from
+//     the score registers; V^T is read from the row-major V tile with the
+//     gfx950 transposed LDS read, in the key order of the score accumulator;
+//   * K and V tiles stay row-major in LDS, double-buffered, one barrier per
+//     tile, the next tile's global loads in flight during the current MFMAs;
+//   * exponentials are base 2 with scale*log2(e) folded into one FMA, and the
+//     running max is only raised when a row's tile max exceeds it by more than
+//     kLazy (log2 units), so most tiles skip the rescale of O entirely
+//     (probabilities then stay below 2^kLazy, well inside f32 and bf16 range);
+//   * the grid is ordered heaviest query tiles first.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -36,9 +37,40 @@
 namespace attn {
 namespace {
 
-constexpr int kBM = 128;   // query rows per workgroup
-constexpr int kBN = 64;    // keys per tile
-constexpr int kPad = 8;    // bf16 padding per LDS row (keeps 16-byte alignment, spreads banks)
+constexpr int kBM = 128;      // query rows per workgroup
+constexpr int kBN = 64;       // keys per tile
+constexpr int kPad = 16;      // bf16 padding per LDS row
+constexpr float kLazy = 8.f;  // max growth tolerated before rescaling (log2 units)
+
+// Global -> registers for one K/V tile of kBN rows (rows past N clamped to
+// N-1: their scores are masked, so their finite values carry zero weight).
+template <int D, int CH_T>
+__device__ __forceinline__ void load_kv_tile(uint4 (&kst)[CH_T], uint4 (&vst)[CH_T],
+                                             const uint16_t *Kg, const uint16_t *Vg, int kv0,
+                                             int N, int tid)
+{
+#pragma unroll
+    for (int i = 0; i < CH_T; ++i) {
+        const int c = tid + 256 * i;
+        const int row = min(kv0 + c / (D / 8), N - 1), col = (c % (D / 8)) * 8;
+        kst[i] = *(const uint4 *)(Kg + (size_t)row * D + col);
+        vst[i] = *(const uint4 *)(Vg + (size_t)row * D + col);
+    }
+}
+
+template <int D, int CH_T, int ROW>
+__device__ __forceinline__ void store_kv_tile(uint16_t (*sk)[ROW], uint16_t (*sv)[ROW],
+                                              const uint4 (&kst)[CH_T], const uint4 (&vst)[CH_T],
+                                              int tid)
+{
+#pragma unroll
+    for (int i = 0; i < CH_T; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *(uint4 *)&sk[row][col] = kst[i];
+        *(uint4 *)&sv[row][col] = vst[i];
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
@@ -48,16 +80,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 {
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int DB = D / 32;              // 32-row blocks of O^T
-    constexpr int KROW = D + kPad;          // LDS row length of the K tile
-    constexpr int VROW = kBN + kPad;        // LDS row length of the V^T tile
-    constexpr int KCH = kBN * D / 8;        // 16-byte chunks per K tile
-    constexpr int KCH_T = KCH / 256;
-    constexpr int VUN = (kBN / 4) * (D / 8);   // 4-key x 8-dim transpose units per V tile
-    constexpr int VUN_T = (VUN + 255) / 256;
-    static_assert(KCH % 256 == 0, "K tile must split evenly over the workgroup");
+    constexpr int ROW = D + kPad;           // LDS row length of the K and V tiles
+    constexpr int CH = kBN * D / 8;         // 16-byte chunks per tile
+    constexpr int CH_T = CH / 256;
+    static_assert(CH % 256 == 0, "tile must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN][KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t svt[2][D][VROW];
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN][ROW];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN][ROW];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -75,86 +104,30 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
 
-    // The softmax is computed on x = q.k scaled by c = |scale| log2(e) > 0; a
-    // negative scale is carried by negating q, which is exact in bf16.
+    // Softmax on x = q.k scaled by c2 = |scale| log2(e) > 0; a negative scale
+    // is carried by negating q, which is exact in bf16.
     const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
     const float cabs = fabsf(scale);
     const float c2 = cabs * kLog2e;
 
-    // Q^T operand, resident for the whole loop: lane holds q[qi][16ks + 8hf .. +7].
+    // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7] (rows past N read row N-1).
     bf16x8 qf[KS];
+    {
+        const int qr = min(qi, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (qi < N) u = *(const uint4 *)(Qh + (size_t)qi * D + 16 * ks + 8 * hf);
-        u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
-        qf[ks] = as_bf16x8(u);
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 u = *(const uint4 *)(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
+            u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
+            qf[ks] = as_bf16x8(u);
+        }
     }
 
     const int kv_end = causal ? min(N, q0 + kBM) : N;
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
-    uint4 kst[KCH_T];
-    uint4 vst[VUN_T][4];
+    uint4 kst[CH_T], vst[CH_T];     // staging registers for one tile
 
-    auto load_tile = [&](int t) {
-        const int kv0 = t * kBN;
-#pragma unroll
-        for (int i = 0; i < KCH_T; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            kst[i] = make_uint4(0, 0, 0, 0);
-            if (kv0 + row < N) kst[i] = *(const uint4 *)(Kg + (size_t)(kv0 + row) * D + col);
-        }
-#pragma unroll
-        for (int i = 0; i < VUN_T; ++i) {
-            const int u = tid + 256 * i;
-            if (u < VUN) {
-                const int kq = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = kv0 + 4 * kq + r;
-                    vst[i][r] = make_uint4(0, 0, 0, 0);
-                    if (key < N) vst[i][r] = *(const uint4 *)(Vg + (size_t)key * D + dc * 8);
-                }
-            }
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KCH_T; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            *(uint4 *)&sk[buf][row][col] = kst[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VUN_T; ++i) {
-            const int u = tid + 256 * i;
-            if (u < VUN) {
-                const int kq = u / (D / 8), dc = u % (D / 8);
-                const uint32_t w0[4] = {vst[i][0].x, vst[i][0].y, vst[i][0].z, vst[i][0].w};
-                const uint32_t w1[4] = {vst[i][1].x, vst[i][1].y, vst[i][1].z, vst[i][1].w};
-                const uint32_t w2[4] = {vst[i][2].x, vst[i][2].y, vst[i][2].z, vst[i][2].w};
-                const uint32_t w3[4] = {vst[i][3].x, vst[i][3].y, vst[i][3].z, vst[i][3].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wd = e >> 1;
-                    uint32_t lo, hi;
-                    if (e & 1) {
-                        lo = (w0[wd] >> 16) | (w1[wd] & 0xffff0000u);
-                        hi = (w2[wd] >> 16) | (w3[wd] & 0xffff0000u);
-                    } else {
-                        lo = (w0[wd] & 0xffffu) | (w1[wd] << 16);
-                        hi = (w2[wd] & 0xffffu) | (w3[wd] << 16);
-                    }
-                    *(uint2 *)&svt[buf][dc * 8 + e][4 * kq] = make_uint2(lo, hi);
-                }
-            }
-        }
-    };
-
-    float m_run = -INFINITY;   // running max of x for this lane's row
+    float m_run = -INFINITY;   // running max of x * c2 for this lane's row
     float l_run = 0.f;         // this lane's share of the running sum
     f32x16 oacc[DB];
 #pragma unroll
@@ -162,13 +135,16 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-    load_tile(0);
-    store_tile(0);
+    load_kv_tile<D>(kst, vst, Kg, Vg, 0, N, tid);
+    store_kv_tile<D, CH_T, ROW>(sk[0], sv[0], kst, vst, tid);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        if (t + 1 < ntiles) load_tile(t + 1);
+        // Prefetch unconditionally (the last iteration re-reads its own tile into
+        // the idle buffer): a conditional prefetch makes the compiler keep the
+        // staging registers in scratch memory.
+        load_kv_tile<D>(kst, vst, Kg, Vg, min(t + 1, ntiles - 1) * kBN, N, tid);
         const int kv0 = t * kBN;
         const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
         if (active) {
@@ -184,62 +160,59 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
                     sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
                 }
             }
-            // Mask keys after the query (causal) and past the end of the sequence.
-            if ((causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if ((causal && key > qi) || key >= N) sacc[kb][r] = -INFINITY;
-                    }
-            }
+            // scale to log2 units; mask keys after the query and past the sequence end
+            const bool need_mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+                for (int r = 0; r < 16; ++r) {
+                    float x = sacc[kb][r] * c2;
+                    if (need_mask) {
+                        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if ((causal && key > qi) || key >= N) x = -INFINITY;
+                    }
+                    sacc[kb][r] = x;
+                    mx = fmaxf(mx, x);
+                }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);          // finite: key 0 is seen first
-            const float alpha = m_run == -INFINITY ? 0.f : exp2_fast((m_run - m_new) * c2);
-            const float mc = m_new * c2;
+            // lazy rescale: raise the running max only when some row of the wave
+            // grew past it by more than kLazy; the first tile always sets it.
+            if (__any(mx > m_run + kLazy)) {
+                const float m_new = fmaxf(m_run, mx);      // finite: key 0 is in the first tile
+                const float alpha = m_run == -INFINITY ? 0.f : exp2_fast(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m_run = m_new;
+            }
             float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2_fast(fmaf(sacc[kb][r], c2, -mc));
+                    const float p = exp2_fast(sacc[kb][r] - m_run);
                     sacc[kb][r] = p;
                     rs += p;
                 }
-            l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
+            l_run += rs;
 
             // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
-            // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys
-            // 16tt + 8(e/4) + 4hf + (e&3) for element e; V^T is read likewise.
+            // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
+            // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const int kb = tt >> 1, r0 = (tt & 1) * 8;
-                const uint4 pu = make_uint4(pack_bf16x2(sacc[kb][r0 + 0], sacc[kb][r0 + 1]),
-                                            pack_bf16x2(sacc[kb][r0 + 2], sacc[kb][r0 + 3]),
-                                            pack_bf16x2(sacc[kb][r0 + 4], sacc[kb][r0 + 5]),
-                                            pack_bf16x2(sacc[kb][r0 + 6], sacc[kb][r0 + 7]));
-                const bf16x8 pb = as_bf16x8(pu);
+                const bf16x8 pb = (tt & 1) ? pack_operand<8>(sacc[tt >> 1]) : pack_operand<0>(sacc[tt >> 1]);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const uint2 lo = *(const uint2 *)&svt[buf][db * 32 + l32][16 * tt + 4 * hf];
-                    const uint2 hi = *(const uint2 *)&svt[buf][db * 32 + l32][16 * tt + 8 + 4 * hf];
-                    const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const bf16x8 a = tr_operand(&sv[buf][0][0], ROW, 16 * tt, db * 32, lane);
                     oacc[db] = mfma32x32x16(a, pb, oacc[db]);
                 }
             }
         }
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        store_kv_tile<D, CH_T, ROW>(sk[buf ^ 1], sv[buf ^ 1], kst, vst, tid);
         __syncthreads();
     }
 
@@ -255,7 +228,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
                 *(float4 *)(orow + d0) = make_float4(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv,
                                                      oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
             }
-        if (hf == 0) LSE[((size_t)b * Hq + h) * N + qi] = m_run * cabs + logf(l_tot);
+        // lse = ln(sum exp(scale q.k)) = (m + log2 l) * ln 2
+        if (hf == 0) LSE[((size_t)b * Hq + h) * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
     }
 }
 

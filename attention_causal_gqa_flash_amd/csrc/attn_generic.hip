@@ -340,45 +340,58 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials: one workgroup per (query head, batch).
+// Log-sum-exp merge of the split partials: one workgroup per (query head,
+// batch).  The split weights are computed once, in parallel, and staged in LDS;
+// each thread then sums one output column with its loads unrolled.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float block128_reduce(float v, float *red, bool is_max)
+{
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return is_max ? fmaxf(red[0], red[1]) : red[0] + red[1];
+}
+
 __global__ __launch_bounds__(128) void lse_merge_kernel(const float *__restrict__ part_o,
                                                         const float *__restrict__ part_lse,
                                                         float *__restrict__ o,
                                                         float *__restrict__ lse, int Hq,
                                                         int n_splits, int d)
 {
-    const int h = blockIdx.x, b = blockIdx.y;
-    const size_t row = (size_t)b * Hq + h;
+    __shared__ float sw[128];
+    __shared__ float red[2];
+    const int tid = threadIdx.x;
+    const size_t row = (size_t)blockIdx.y * Hq + blockIdx.x;
     const float *pl = part_lse + row * n_splits;
     const float *po = part_o + row * (size_t)n_splits * d;
+
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pl[s]);
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-        if (M == -INFINITY) {
-            o[row * d + c] = 0.f;
-            continue;
-        }
-        float W = 0.f, acc = 0.f;
-        for (int s = 0; s < n_splits; ++s) {
+    for (int s = tid; s < n_splits; s += 128) M = fmaxf(M, pl[s]);
+    M = block128_reduce(M, red, true);
+
+    float W = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += 128) {
+        const int s = s0 + tid;
+        float w = 0.f;
+        if (s < n_splits && M != -INFINITY) {
             const float ls = pl[s];
-            if (ls == -INFINITY) continue;
-            const float w = expf(ls - M);
-            W += w;
-            acc = fmaf(w, po[(size_t)s * d + c], acc);
+            if (ls != -INFINITY) w = expf(ls - M);
         }
-        o[row * d + c] = acc / W;
-    }
-    if (threadIdx.x == 0) {
-        if (M == -INFINITY) {
-            lse[row] = -INFINITY;
-        } else {
-            float W = 0.f;
-            for (int s = 0; s < n_splits; ++s)
-                if (pl[s] != -INFINITY) W += expf(pl[s] - M);
-            lse[row] = M + logf(W);
+        W += w;
+        __syncthreads();
+        sw[tid] = w;
+        __syncthreads();
+        if (tid < d) {
+            const int n = min(128, n_splits - s0);
+            const float *pc = po + (size_t)s0 * d + tid;
+#pragma unroll 8
+            for (int i = 0; i < n; ++i) acc = fmaf(sw[i], pc[(size_t)i * d], acc);
         }
     }
+    W = block128_reduce(W, red, false);
+    if (tid < d) o[row * d + tid] = M == -INFINITY ? 0.f : acc / W;
+    if (tid == 0) lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
 }
 
 // ---------------------------------------------------------------------------

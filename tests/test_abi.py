@@ -161,3 +161,13 @@ def test_no_unexpected_exports(L):
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     c_names = {n for n in exported if n.startswith("attn_")}
     assert c_names == set(_declared_functions())
+
+
+def test_decode_merged_refusals(L):
+    assert L.attn_decode_workspace_bytes(1, 8) == 256
+    assert L.attn_decode_workspace_bytes(0, 8) == 0
+    args = [1, 1, 32, 8, 4096, 128, 0.088, 16]
+    assert L.attn_decode_merged(1, 1, 32, 8, 4096, 128, 0.088, 0, *([P] * 7), P, 256, NUL) == INVALID
+    assert L.attn_decode_merged(*args, *([P] * 7), P, 255, NUL) == WORKSPACE
+    assert L.attn_decode_merged(*args, *([P] * 7), NUL, 256, NUL) == WORKSPACE
+    assert L.attn_decode_merged(*args, *([P] * 6), MIS, P, 256, NUL) == INVALID
