@@ -32,6 +32,10 @@ def hipcc() -> str:
 def compile_flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPR form: the default AGPR form made the
+            # backward kernels copy every accumulator between AGPRs and VGPRs
+            # around each MFMA
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

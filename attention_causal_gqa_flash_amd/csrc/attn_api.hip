@@ -50,20 +50,32 @@ size_t workspace_bytes(int B, int Hq, int N)
 }
 
 // Kernel launches of the three backward stages (arguments already validated).
-hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int N, int d, const float *o,
-                                 const void *dout, float *delta, hipStream_t st)
+// dk/dv zero-fill piggybacked on the preprocess launch when the dK/dV kernel
+// will accumulate into them (zero_dkdv), else plain preprocess.
+hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int N, int d, const float *o,
+                                 const void *dout, float *delta, float *dk, float *dv,
+                                 bool zero_dkdv, hipStream_t st)
 {
-    return attn::bwd_preprocess(dt, (long)B * Hq * N, d, dout, o, delta, st);
+    const long n = (long)B * Hkv * N * d;
+    return attn::bwd_preprocess(dt, (long)B * Hq * N, d, dout, o, delta, zero_dkdv ? dk : nullptr,
+                                zero_dkdv ? dv : nullptr, n, st);
 }
 
+// Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
+int dkdv_split(int dt, int B, int Hq, int Hkv, int N, int d, float scale)
+{
+    return use_mfma(dt, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, N) : 1;
+}
+
+// dk and dv must already be zero when hs > 1.
 hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, const float *lse,
-                           const void *dout, const float *delta, float *dk, float *dv,
+                           const void *dout, const float *delta, float *dk, float *dv, int hs,
                            hipStream_t st)
 {
     if (use_mfma(dt, d, scale))
         return attn::bwd_dkdv_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
-                                   delta, dk, dv, st);
+                                   delta, dk, dv, hs, st);
     return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
                                   delta, dk, dv, st);
 }
@@ -119,10 +131,12 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
     if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float *delta = (float *)workspace;
-    if (launch_bwd_preprocess(dt, B, Hq, N, d, o, dout, delta, st) != hipSuccess)
+    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
+    if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st) !=
+        hipSuccess)
         return ATTN_ERR_HIP;
     if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
-                        st) != hipSuccess)
+                        hs, st) != hipSuccess)
         return ATTN_ERR_HIP;
     return hip_status(
         launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st));
@@ -134,7 +148,8 @@ attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, cons
     attn_status s = check_common(dt, B, Hq, 1, N, d, 1.0f);
     if (s != ATTN_OK) return s;
     if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_ERR_INVALID_ARG;
-    return hip_status(launch_bwd_preprocess(dt, B, Hq, N, d, o, dout, delta, (hipStream_t)stream));
+    return hip_status(launch_bwd_preprocess(dt, B, Hq, 1, N, d, o, dout, delta, nullptr, nullptr,
+                                            false, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
@@ -147,8 +162,12 @@ attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout) ||
         !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
         return ATTN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
+    if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * N * d, st) != hipSuccess)
+        return ATTN_ERR_HIP;
     return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
-                                      delta, dk, dv, (hipStream_t)stream));
+                                      delta, dk, dv, hs, st));
 }
 
 attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,

@@ -10,7 +10,7 @@
 //     dV = P^T dO,        dK = scale dS^T Q,   dQ = scale dS K,
 // and no P or dS tile ever reaches device memory.
 //
-// Two kernels, both deterministic (no atomics):
+// Two kernels:
 //   * dkdv: key-stationary.  A workgroup owns 64 keys of one key/value head and
 //     keeps their dK^T and dV^T accumulators in registers while it streams the
 //     query tiles of every query head of the group past them.  4 waves = 2 key
@@ -18,12 +18,16 @@
 //     scores are laid out S = Q K^T (lane = key column), so P and dS feed the
 //     dV and dK MFMAs straight from registers, and Q^T, dO^T come from the
 //     row-major Q and dO tiles through the transposed LDS read.  The two query
-//     halves' partials are summed through LDS at the end.
-//   * dq: query-stationary, the forward's layout (lane = query row, S^T = K Q^T)
+//     halves' partials are summed through LDS at the end.  When the key tiles
+//     alone are too few to fill the GPU, the group's query heads are split
+//     over several workgroups whose partial dK/dV are added with f32 atomics
+//     (so dK/dV are then order-dependent in the last bits).
+//   * dq (deterministic): query-stationary, the forward's layout (lane = query row, S^T = K Q^T)
 //     with dQ^T = K^T dS^T accumulated in registers; P and dP are recomputed,
 //     K^T is read from the row-major K tile through the transposed LDS read.
-// Both double-buffer their LDS tiles with one barrier per step, the next
-// step's global loads in flight during the current step's MFMAs.
+// Both double-buffer their LDS tiles (row-major, 16-byte chunks XOR-swizzled by
+// row), filled by direct global->LDS loads with the next step's loads in
+// flight during the current step's MFMAs, one barrier per step.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -32,36 +36,6 @@
 namespace attn {
 namespace {
 
-constexpr int kPad = 16;
-
-// Global -> registers for one tile of 64 rows of two row-major tensors (rows
-// past N clamped to N-1; the callers give such rows zero weight), and back to LDS.
-template <int D, int CH_T>
-__device__ __forceinline__ void load_tile2(uint4 (&a)[CH_T], uint4 (&b)[CH_T], const uint16_t *A,
-                                           const uint16_t *Bm, int r0, int N, int tid)
-{
-#pragma unroll
-    for (int i = 0; i < CH_T; ++i) {
-        const int c = tid + 256 * i;
-        const int row = min(r0 + c / (D / 8), N - 1), col = (c % (D / 8)) * 8;
-        a[i] = *(const uint4 *)(A + (size_t)row * D + col);
-        b[i] = *(const uint4 *)(Bm + (size_t)row * D + col);
-    }
-}
-
-template <int D, int CH_T, int ROW>
-__device__ __forceinline__ void store_tile2(uint16_t (*sa)[ROW], uint16_t (*sb)[ROW],
-                                            const uint4 (&a)[CH_T], const uint4 (&b)[CH_T], int tid)
-{
-#pragma unroll
-    for (int i = 0; i < CH_T; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(uint4 *)&sa[row][col] = a[i];
-        *(uint4 *)&sb[row][col] = b[i];
-    }
-}
-
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
@@ -69,22 +43,19 @@ constexpr int kKvBN = 64;   // keys per workgroup
 constexpr int kKvBM = 64;   // queries per step
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
-    float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal)
+    float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal, int hs)
 {
     constexpr int KS = D / 16, DB = D / 32;
-    constexpr int ROW = D + kPad;
-    constexpr int CH_T = kKvBM * D / 8 / 256;      // 16-byte chunks per thread per tile
-    static_assert(kKvBM * D / 8 % 256 == 0, "tile must split evenly over the workgroup");
 
     // One LDS block: double-buffered Q, dO, lse and D tiles during the loop,
     // then the reduction buffer for the two query halves' dK^T and dV^T.
     struct Smem {
-        uint16_t q[2][kKvBM][ROW];
-        uint16_t dO[2][kKvBM][ROW];
+        uint16_t q[2][kKvBM * D];                  // row-major, swizzled chunks
+        uint16_t dO[2][kKvBM * D];
         float lse[2][kKvBM];
         float dd[2][kKvBM];
     };
@@ -93,14 +64,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(Smem)];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
 
-    const int BG = B * Hkv;
-    const int kt = blockIdx.x / BG;          // causal: low key tiles see the most queries
-    const int bg = blockIdx.x % BG;
-    const int b = bg / Hkv, g = bg % Hkv;
-    const int G = Hq / Hkv;
+    // Work item = (key tile, batch, kv head, head subset).  The G query heads of
+    // a group are split into hs subsets of Gs heads; with hs > 1 the subsets'
+    // partial dK/dV are summed with atomics into zero-filled outputs.
+    const int BGH = B * Hkv * hs;
+    const int kt = blockIdx.x / BGH;         // causal: low key tiles see the most queries
+    const int rem = blockIdx.x % BGH;
+    const int b = rem / (Hkv * hs), g = (rem / hs) % Hkv, hsub = rem % hs;
+    const int G = Hq / Hkv, Gs = G / hs;
     const int k0 = kt * kKvBN;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int l32 = lane & 31, hf = lane >> 5;
     const int kb = wave & 1, qh = wave >> 1;
     const int kj = k0 + 32 * kb + l32;       // this lane's key column
@@ -134,40 +109,31 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int nqt = (N + kKvBM - 1) / kKvBM;
     const int qt0 = causal ? k0 / kKvBM : 0;
     const int nq = nqt - qt0;
-    const int steps = G * nq;                // (query head, query tile) pairs
+    const int steps = Gs * nq;               // (query head, query tile) pairs
 
-    uint4 qst[CH_T], dst[CH_T];     // staging registers for one step
-    float lst = 0.f, dstv = 0.f;
-
-// step s covers query head g*G + s/nq, query tile qt0 + s%nq
-#define ATTN_LOAD_STEP(s_)                                                                      \
+// Step s covers query head g*G + hsub*Gs + s/nq, query tile qt0 + s%nq.  Its Q and dO
+// tiles and its lse and D rows move global -> LDS directly (rows past N are
+// clamped to N-1 and masked in the step's arithmetic).
+#define ATTN_LOAD_STEP(s_, buf_)                                                                \
     {                                                                                           \
-        const size_t hrow_ = ((size_t)b * Hq + g * G + (s_) / nq) * N;                          \
+        const size_t hrow_ = ((size_t)b * Hq + g * G + hsub * Gs + (s_) / nq) * N;              \
         const int q0_ = (qt0 + (s_) % nq) * kKvBM;                                              \
-        load_tile2<D, CH_T>(qst, dst, Q + hrow_ * D, dO + hrow_ * D, q0_, N, tid);              \
-        if (tid < kKvBM) {                                                                      \
-            const int row_ = q0_ + tid;                                                         \
-            lst = row_ < N ? LSE[hrow_ + row_] * kLog2e : INFINITY; /* P = 0 on padded rows */  \
-            dstv = row_ < N ? Dws[hrow_ + row_] : 0.f;                                          \
-        }                                                                                       \
+        tile_load_lds<D, kKvBM>(sm.q[buf_], Q + hrow_ * D, q0_, N, wave, 4, lane);              \
+        tile_load_lds<D, kKvBM>(sm.dO[buf_], dO + hrow_ * D, q0_, N, wave, 4, lane);            \
+        const int row_ = min(q0_ + lane, N - 1);                                                \
+        if (wave == 0)                                                                          \
+            __builtin_amdgcn_global_load_lds((const void *)(LSE + hrow_ + row_),                \
+                (__attribute__((address_space(3))) void *)&sm.lse[buf_][0], 4, 0, 0);           \
+        else if (wave == 1)                                                                     \
+            __builtin_amdgcn_global_load_lds((const void *)(Dws + hrow_ + row_),                \
+                (__attribute__((address_space(3))) void *)&sm.dd[buf_][0], 4, 0, 0);            \
     }
-#define ATTN_STORE_STEP(buf_)                                                                   \
-    {                                                                                           \
-        store_tile2<D, CH_T, ROW>(sm.q[buf_], sm.dO[buf_], qst, dst, tid);                      \
-        if (tid < kKvBM) {                                                                      \
-            sm.lse[buf_][tid] = lst;                                                            \
-            sm.dd[buf_][tid] = dstv;                                                            \
-        }                                                                                       \
-    }
-    if (steps > 0) {
-        ATTN_LOAD_STEP(0);
-        ATTN_STORE_STEP(0);
-    }
+    if (steps > 0) ATTN_LOAD_STEP(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 0; s < steps; ++s) {
         const int buf = s & 1;
-        // unconditional prefetch (see the dq loop); the last step re-reads itself
-        ATTN_LOAD_STEP(min(s + 1, steps - 1));
+        if (s + 1 < steps) ATTN_LOAD_STEP(s + 1, buf ^ 1);   // in flight during the MFMAs
         const int q0 = (qt0 + s % nq) * kKvBM;
         const int qb0 = q0 + 32 * qh;       // first query row of this wave's block
         const bool active = qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb);
@@ -175,50 +141,71 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+            bf16x8 aq[KS], ad[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 aq = as_bf16x8(*(const uint4 *)&sm.q[buf][32 * qh + l32][16 * ks + 8 * hf]);
-                const bf16x8 ad = as_bf16x8(*(const uint4 *)&sm.dO[buf][32 * qh + l32][16 * ks + 8 * hf]);
-                sacc = mfma32x32x16(aq, kf[ks], sacc);
-                pacc = mfma32x32x16(ad, vf[ks], pacc);
+                aq[ks] = tile_row_operand<D>(sm.q[buf], 32 * qh + l32, 2 * ks + hf);
+                ad[ks] = tile_row_operand<D>(sm.dO[buf], 32 * qh + l32, 2 * ks + hf);
             }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc = mfma32x32x16(aq[ks], kf[ks], sacc);
+                pacc = mfma32x32x16(ad[ks], vf[ks], pacc);
+            }
+            sched_pipeline<2 * KS, 2 * KS, 4, 1>();
             // P = exp(scale s - lse), dS = P (dP - D); rows are queries, lane = key.
-            const bool diag = causal && qb0 < k0 + 32 * kb + 32;
+            // Masked (only on diagonal and tail steps, a wave-uniform branch):
+            // keys after the query (causal) and query rows past N.
+            const bool masked = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int rr = 32 * qh + 8 * a + 4 * hf;       // local query row of r = 4a
                 const float4 l4 = *(const float4 *)&sm.lse[buf][rr];
                 const float4 d4 = *(const float4 *)&sm.dd[buf][rr];
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
                 const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * a + e;
-                    float p = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
-                    if (diag && kj > q0 + rr + e) p = 0.f;
-                    sacc[r] = p;
-                    pacc[r] = p * (pacc[r] - dv[e]);
+                    sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
+                    pacc[r] = pacc[r] - dv[e];
                 }
+                if (masked) {
+                    const int qrow = q0 + rr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool keep = (!causal || kj <= qrow + e) && qrow + e < N;
+                        sacc[4 * a + e] = keep ? sacc[4 * a + e] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pacc[4 * a + e] *= sacc[4 * a + e];
             }
             // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
+            bf16x8 ado[2][DB], aqt[2][DB];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    ado[tt][db] = tr_operand<D>(sm.dO[buf], 32 * qh + 16 * tt, db * 32, lane);
+                    aqt[tt][db] = tr_operand<D>(sm.q[buf], 32 * qh + 16 * tt, db * 32, lane);
+                }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const bf16x8 pb = tt ? pack_operand<8>(sacc) : pack_operand<0>(sacc);
                 const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const bf16x8 ado = tr_operand(&sm.dO[buf][0][0], ROW, 32 * qh + 16 * tt, db * 32, lane);
-                    const bf16x8 aqt = tr_operand(&sm.q[buf][0][0], ROW, 32 * qh + 16 * tt, db * 32, lane);
-                    dva[db] = mfma32x32x16(ado, pb, dva[db]);
-                    dka[db] = mfma32x32x16(aqt, sb, dka[db]);
+                    dva[db] = mfma32x32x16(ado[tt][db], pb, dva[db]);
+                    dka[db] = mfma32x32x16(aqt[tt][db], sb, dka[db]);
                 }
             }
+            sched_pipeline<8 * DB, 4 * DB, 4, 2>();
         }
-        ATTN_STORE_STEP(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);      // this wave's prefetch has landed
         __syncthreads();
     }
 #undef ATTN_LOAD_STEP
-#undef ATTN_STORE_STEP
 
     // Sum the two query halves through LDS, then write dK = scale (dK^T)^T and
     // dV.  Accumulator layout: lane = key column kj, register r = dim
@@ -254,8 +241,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                 v4.y = dva[db][4 * a + 1] + rv[(r0 + 1) * 64];
                 v4.z = dva[db][4 * a + 2] + rv[(r0 + 2) * 64];
                 v4.w = dva[db][4 * a + 3] + rv[(r0 + 3) * 64];
-                *(float4 *)(dkrow + d0) = k4;
-                *(float4 *)(dvrow + d0) = v4;
+                if (hs == 1) {
+                    *(float4 *)(dkrow + d0) = k4;
+                    *(float4 *)(dvrow + d0) = v4;
+                } else {
+                    atomicAdd(dkrow + d0 + 0, k4.x); atomicAdd(dkrow + d0 + 1, k4.y);
+                    atomicAdd(dkrow + d0 + 2, k4.z); atomicAdd(dkrow + d0 + 3, k4.w);
+                    atomicAdd(dvrow + d0 + 0, v4.x); atomicAdd(dvrow + d0 + 1, v4.y);
+                    atomicAdd(dvrow + d0 + 2, v4.z); atomicAdd(dvrow + d0 + 3, v4.w);
+                }
             }
     }
 }
@@ -267,19 +261,17 @@ constexpr int kQBM = 128;   // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;    // keys per tile
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
     int Hq, int Hkv, int N, float scale, int causal, int nqt)
 {
     constexpr int KS = D / 16, DB = D / 32;
-    constexpr int ROW = D + kPad;
-    constexpr int CH_T = kQBN * D / 8 / 256;
-    static_assert(kQBN * D / 8 % 256 == 0, "tile must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kQBN][ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kQBN][ROW];
+    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kQBN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kQBN * D];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -288,7 +280,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const int g = h / (Hq / Hkv);
     const int q0 = qt * kQBM;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int l32 = lane & 31, hf = lane >> 5;
     const int qw0 = q0 + wave * 32;
     const int qi = qw0 + l32;
@@ -324,17 +317,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const int kv_end = causal ? min(N, q0 + kQBM) : N;
     const int ntiles = (kv_end + kQBN - 1) / kQBN;
 
-    uint4 kst[CH_T], vst[CH_T];     // staging registers for one tile
-
-    load_tile2<D, CH_T>(kst, vst, Kg, Vg, 0, N, tid);
-    store_tile2<D, CH_T, ROW>(sk[0], sv[0], kst, vst, tid);
+    // Tiles move global -> LDS directly; rows past N are clamped and masked.
+    tile_load_lds<D, kQBN>(sk[0], Kg, 0, N, wave, 4, lane);
+    tile_load_lds<D, kQBN>(sv[0], Vg, 0, N, wave, 4, lane);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        // Prefetch unconditionally (the last iteration re-reads its own tile into
-        // the idle buffer): a conditional prefetch makes the compiler keep the
-        // staging registers in scratch memory.
-        load_tile2<D, CH_T>(kst, vst, Kg, Vg, min(t + 1, ntiles - 1) * kQBN, N, tid);
+        if (t + 1 < ntiles) {       // prefetch into the idle buffer, in flight during the MFMAs
+            tile_load_lds<D, kQBN>(sk[buf ^ 1], Kg, (t + 1) * kQBN, N, wave, 4, lane);
+            tile_load_lds<D, kQBN>(sv[buf ^ 1], Vg, (t + 1) * kQBN, N, wave, 4, lane);
+        }
         const int kv0 = t * kQBN;
         const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
         if (active) {
@@ -344,13 +337,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
                 f32x16 sacc, pacc;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+                bf16x8 ak[KS], av[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 ak = as_bf16x8(*(const uint4 *)&sk[buf][kb * 32 + l32][16 * ks + 8 * hf]);
-                    const bf16x8 av = as_bf16x8(*(const uint4 *)&sv[buf][kb * 32 + l32][16 * ks + 8 * hf]);
-                    sacc = mfma32x32x16(ak, qf[ks], sacc);
-                    pacc = mfma32x32x16(av, dof[ks], pacc);
+                    ak[ks] = tile_row_operand<D>(sk[buf], kb * 32 + l32, 2 * ks + hf);
+                    av[ks] = tile_row_operand<D>(sv[buf], kb * 32 + l32, 2 * ks + hf);
                 }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    sacc = mfma32x32x16(ak[ks], qf[ks], sacc);
+                    pacc = mfma32x32x16(av[ks], dof[ks], pacc);
+                }
+                sched_pipeline<2 * KS, 2 * KS, 4, 1>();
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float p = exp2_fast(fmaf(sacc[r], c2, -lse2));
@@ -361,18 +359,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
                     pacc[r] = p * (pacc[r] - Di);
                 }
                 // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
+                bf16x8 kt_[2][DB];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        kt_[tt][db] = tr_operand<D>(sk[buf], kb * 32 + 16 * tt, db * 32, lane);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const bf16x8 a = tr_operand(&sk[buf][0][0], ROW, kb * 32 + 16 * tt, db * 32, lane);
-                        dqa[db] = mfma32x32x16(a, sb, dqa[db]);
-                    }
+                    for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16(kt_[tt][db], sb, dqa[db]);
                 }
+                sched_pipeline<4 * DB, 2 * DB, 4, 2>();
             }
         }
-        store_tile2<D, CH_T, ROW>(sk[buf ^ 1], sv[buf ^ 1], kst, vst, tid);
+        __builtin_amdgcn_s_waitcnt(0);      // this wave's prefetch has landed
         __syncthreads();
     }
 
@@ -391,20 +393,49 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 }  // namespace
 
+int dkdv_head_split(int B, int Hq, int Hkv, int N)
+{
+    // Split each group's query heads over enough workgroups to give every
+    // workgroup slot (two per CU) about two causal-imbalanced work items.
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    // Measured on MI355X: f32 atomics into dK/dV cost far more than the load
+    // imbalance they remove (4 x 1024 x 64 grouped-query workload: 66 -> 171 us;
+    // 32/8 heads at N=4096: no gain), so the split is only taken when the key
+    // tiles leave most of the GPU idle.
+    const int G = Hq / Hkv;
+    const long base = (long)((N + kKvBN - 1) / kKvBN) * B * Hkv;
+    int hs = 1;
+    for (int c = 1; c <= G; ++c)
+        if (G % c == 0) {
+            hs = c;
+            if (base * c >= cus / 4) break;
+        }
+    return hs;
+}
+
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
-                         const void *dout, const float *Dws, float *dk, float *dv, hipStream_t st)
+                         const void *dout, const float *Dws, float *dk, float *dv, int hs,
+                         hipStream_t st)
 {
     const int nkt = (N + kKvBN - 1) / kKvBN;
-    dim3 grid((unsigned)(nkt * B * Hkv));
+    dim3 grid((unsigned)(nkt * B * Hkv * hs));
     if (d == 128)
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal);
+                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal, hs);
     else if (d == 64)
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal);
+                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal, hs);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = Hq / Hkv;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int l16 = lane & 15, grp = lane >> 4;
 
     // scores are x = q.k; the softmax runs on x * c2 in base 2 (c2 may be negative)

@@ -53,22 +53,107 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p)
     return __builtin_bit_cast(uint2, v);
 }
 
+// Row-major bf16 tiles [rows][D] in LDS with their 16-byte chunks XOR-swizzled
+// by row: logical chunk c of row r lives at chunk c ^ swz(r).  swz is chosen so
+// that the two read patterns of the kernels hit distinct banks:
+//   * 16 consecutive rows reading the same logical chunk (ds_read_b128 of an
+//     MFMA operand row): swz takes 16 (D = 128) or 8 (D = 64) distinct values
+//     over consecutive rows;
+//   * 4 aligned rows x 2 adjacent chunks (the transposed reads of tr_operand):
+//     swz(r) >> 1 differs between the 4 rows while its low bit is shared.
+template <int D>
+__device__ __forceinline__ int swz(int row)
+{
+    static_assert(D == 64 || D == 128, "swizzle defined for 8 or 16 chunks per row");
+    const int f = ((row & 3) << 1) | ((row >> 2) & 1);
+    return D == 128 ? (f | (row & 8)) : f;
+}
+
+template <int D>
+__device__ __forceinline__ uint16_t *tile_chunk(uint16_t *tile, int row, int c)
+{
+    return tile + row * D + 8 * (c ^ swz<D>(row));
+}
+
+template <int D>
+__device__ __forceinline__ const uint16_t *tile_chunk(const uint16_t *tile, int row, int c)
+{
+    return tile + row * D + 8 * (c ^ swz<D>(row));
+}
+
+// Direct global -> LDS copy (global_load_lds_dwordx4, no registers): one wave
+// instruction moves 64 x 16 bytes into 1 KiB of LDS, lane L landing at byte
+// 16 L.  The tile of `rows` rows is filled in 1 KiB blocks; lane L of block j
+// owns physical chunk 64 j + L and so fetches the logical chunk that the
+// swizzle maps there.  Rows at or past N are clamped to row N-1 (the callers
+// give such rows zero weight).  Waves 0..nwaves-1 share the blocks.  The copy
+// completes asynchronously: wait for vmcnt before the barrier that publishes it.
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_load_lds(uint16_t *tile, const uint16_t *src, int r0, int N,
+                                              int wave, int nwaves, int lane)
+{
+    constexpr int CPR = D / 8;                    // 16-byte chunks per row
+    constexpr int BLOCKS = ROWS * CPR / 64;
+    static_assert(ROWS * CPR % 64 == 0, "tile must be whole 1 KiB blocks");
+    for (int j = wave; j < BLOCKS; j += nwaves) {
+        const int p = 64 * j + lane;
+        const int row = p / CPR;
+        const int c = (p % CPR) ^ swz<D>(row);
+        const int grow = min(r0 + row, N - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)grow * D + 8 * c),
+                                         (__attribute__((address_space(3))) void *)(tile + 512 * j),
+                                         16, 0, 0);
+    }
+}
+
+// 8 bf16 (logical chunk c) of one row: an MFMA operand whose contraction runs
+// along the row.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row_operand(const uint16_t *tile, int row, int c)
+{
+    return as_bf16x8(*(const uint4 *)tile_chunk<D>(tile, row, c));
+}
+
 // Operand of v_mfma_f32_32x32x16_bf16 whose contraction runs down the rows of a
-// row-major bf16 LDS tile: lane l gets column cbase + l%32 at rows
-// kbase + 4*(l/32) + {0,1,2,3} (elements 0..3) and kbase + 8 + 4*(l/32) + {0..3}
-// (elements 4..7).  That is exactly the row order in which the 32x32
-// accumulator of the previous MFMA holds its rows (rows 8(r/4) + 4*(l/32) + r%4),
-// so an accumulator repacked to bf16 pairs with this operand.  Two transposed
-// LDS reads: lane i of each 16-lane group addresses row kbase + 4*(l/32) + i/4,
-// columns cbase + 16*((l%32)/16) + 4*(i%4) .. +3.
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int stride, int kbase, int cbase,
-                                             int lane)
+// swizzled tile: lane l gets column cbase + l%32 at rows kbase + 4*(l/32) +
+// {0,1,2,3} (elements 0..3) and kbase + 8 + 4*(l/32) + {0..3} (elements 4..7).
+// That is exactly the row order in which the 32x32 accumulator of the previous
+// MFMA holds its rows (rows 8(r/4) + 4*(l/32) + r%4), so an accumulator
+// repacked to bf16 pairs with this operand.  Two transposed LDS reads: lane i
+// of each 16-lane group addresses row kbase + 4*(l/32) + i/4, columns
+// cbase + 16*((l%32)/16) + 4*(i%4) .. +3.  cbase is a multiple of 16.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int kbase, int cbase, int lane)
 {
     const int hf = lane >> 5, i = lane & 15, g16 = (lane >> 4) & 1;
-    const uint16_t *p = tile + (kbase + 4 * hf + (i >> 2)) * stride + cbase + 16 * g16 + 4 * (i & 3);
-    const uint2 lo = lds_read_tr16(p);
-    const uint2 hi = lds_read_tr16(p + 8 * stride);
+    const int row = kbase + 4 * hf + (i >> 2);
+    const int c = (cbase >> 3) + 2 * g16 + ((i & 3) >> 1);     // logical 16-byte chunk
+    const int off = 4 * (i & 1);                                // element within the chunk
+    const uint2 lo = lds_read_tr16(tile_chunk<D>(tile, row, c) + off);
+    const uint2 hi = lds_read_tr16(tile_chunk<D>(tile, row + 8, c) + off);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Scheduling hint for the current basic block: NR LDS reads and NM MFMAs are
+// interleaved as AHEAD reads first, then (one MFMA, RPM reads) while reads
+// remain, then the remaining MFMAs -- the reads for later MFMAs are in flight
+// while earlier MFMAs execute.  (Masks: 0x008 = MFMA, 0x100 = LDS read.)
+template <int I, int NM, int REST, int RPM>
+struct SchedPipeStep {
+    static __device__ __forceinline__ void emit()
+    {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (I * RPM < REST) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        if constexpr (I + 1 < NM) SchedPipeStep<I + 1, NM, REST, RPM>::emit();
+    }
+};
+
+template <int NR, int NM, int AHEAD, int RPM>
+__device__ __forceinline__ void sched_pipeline()
+{
+    static_assert(AHEAD <= NR && (NR - AHEAD) % RPM == 0, "reads must split evenly");
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+    SchedPipeStep<0, NM, NR - AHEAD, RPM>::emit();
 }
 
 // Accumulator registers R0..R0+7 of a 32x32 MFMA packed to a bf16 operand.

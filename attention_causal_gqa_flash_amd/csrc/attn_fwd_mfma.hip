@@ -22,8 +22,11 @@
 //     rescale is a per-lane scalar and P^T feeds the next MFMA straight from
 //     the score registers; V^T is read from the row-major V tile with the
 //     gfx950 transposed LDS read, in the key order of the score accumulator;
-//   * K and V tiles stay row-major in LDS, double-buffered, one barrier per
-//     tile, the next tile's global loads in flight during the current MFMAs;
+//   * K and V tiles stay row-major in LDS (16-byte chunks XOR-swizzled by row,
+//     which keeps both the row reads and the transposed reads conflict-free),
+//     double-buffered, filled by direct global->LDS loads (no staging
+//     registers), one barrier per tile, the next tile's loads in flight during
+//     the current MFMAs;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA, and the
 //     running max is only raised when a row's tile max exceeds it by more than
 //     kLazy (log2 units), so most tiles skip the rescale of O entirely
@@ -39,38 +42,7 @@ namespace {
 
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
-constexpr int kPad = 16;      // bf16 padding per LDS row
 constexpr float kLazy = 8.f;  // max growth tolerated before rescaling (log2 units)
-
-// Global -> registers for one K/V tile of kBN rows (rows past N clamped to
-// N-1: their scores are masked, so their finite values carry zero weight).
-template <int D, int CH_T>
-__device__ __forceinline__ void load_kv_tile(uint4 (&kst)[CH_T], uint4 (&vst)[CH_T],
-                                             const uint16_t *Kg, const uint16_t *Vg, int kv0,
-                                             int N, int tid)
-{
-#pragma unroll
-    for (int i = 0; i < CH_T; ++i) {
-        const int c = tid + 256 * i;
-        const int row = min(kv0 + c / (D / 8), N - 1), col = (c % (D / 8)) * 8;
-        kst[i] = *(const uint4 *)(Kg + (size_t)row * D + col);
-        vst[i] = *(const uint4 *)(Vg + (size_t)row * D + col);
-    }
-}
-
-template <int D, int CH_T, int ROW>
-__device__ __forceinline__ void store_kv_tile(uint16_t (*sk)[ROW], uint16_t (*sv)[ROW],
-                                              const uint4 (&kst)[CH_T], const uint4 (&vst)[CH_T],
-                                              int tid)
-{
-#pragma unroll
-    for (int i = 0; i < CH_T; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(uint4 *)&sk[row][col] = kst[i];
-        *(uint4 *)&sv[row][col] = vst[i];
-    }
-}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
@@ -80,13 +52,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 {
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int DB = D / 32;              // 32-row blocks of O^T
-    constexpr int ROW = D + kPad;           // LDS row length of the K and V tiles
-    constexpr int CH = kBN * D / 8;         // 16-byte chunks per tile
-    constexpr int CH_T = CH / 256;
-    static_assert(CH % 256 == 0, "tile must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN][ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN][ROW];
+    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered
+    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -95,7 +64,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const int g = h / (Hq / Hkv);
     const int q0 = qt * kBM;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int l32 = lane & 31, hf = lane >> 5;
     const int qw0 = q0 + wave * 32;         // first query row of this wave
     const int qi = qw0 + l32;               // this lane's query row
@@ -125,8 +95,6 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const int kv_end = causal ? min(N, q0 + kBM) : N;
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
-    uint4 kst[CH_T], vst[CH_T];     // staging registers for one tile
-
     float m_run = -INFINITY;   // running max of x * c2 for this lane's row
     float l_run = 0.f;         // this lane's share of the running sum
     f32x16 oacc[DB];
@@ -135,31 +103,42 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-    load_kv_tile<D>(kst, vst, Kg, Vg, 0, N, tid);
-    store_kv_tile<D, CH_T, ROW>(sk[0], sv[0], kst, vst, tid);
+    // Tiles move global -> LDS directly (no staging registers); rows past N are
+    // clamped to N-1, their scores masked below.
+    tile_load_lds<D, kBN>(sk[0], Kg, 0, N, wave, 4, lane);
+    tile_load_lds<D, kBN>(sv[0], Vg, 0, N, wave, 4, lane);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        // Prefetch unconditionally (the last iteration re-reads its own tile into
-        // the idle buffer): a conditional prefetch makes the compiler keep the
-        // staging registers in scratch memory.
-        load_kv_tile<D>(kst, vst, Kg, Vg, min(t + 1, ntiles - 1) * kBN, N, tid);
+        if (t + 1 < ntiles) {       // prefetch into the idle buffer, in flight during the MFMAs
+            tile_load_lds<D, kBN>(sk[buf ^ 1], Kg, (t + 1) * kBN, N, wave, 4, lane);
+            tile_load_lds<D, kBN>(sv[buf ^ 1], Vg, (t + 1) * kBN, N, wave, 4, lane);
+        }
         const int kv0 = t * kBN;
         const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
         if (active) {
             // S^T = K Q^T for the 64 keys of the tile, two 32-key blocks.
+            // All of the tile's K operands are read before the MFMAs, so the
+            // LDS latency is paid once per tile rather than once per MFMA.
             f32x16 sacc[2];
+            bf16x8 ka[2][KS];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    ka[kb][ks] = tile_row_operand<D>(sk[buf], kb * 32 + l32, 2 * ks + hf);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = as_bf16x8(*(const uint4 *)&sk[buf][kb * 32 + l32][16 * ks + 8 * hf]);
-                    sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
-                }
-            }
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], qf[ks], sacc[kb]);
+            // Pipeline: 4 operand reads ahead, then one read per MFMA.
+            sched_pipeline<2 * KS, 2 * KS, 4, 1>();
             // scale to log2 units; mask keys after the query and past the sequence end
             const bool need_mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
             float mx = -INFINITY;
@@ -202,17 +181,22 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
             // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
             // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
             // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
+            // V^T operands for all four 16-key steps are read first, then the
+            // MFMAs run back to back (DB independent accumulators).
+            bf16x8 va[4][DB];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) va[tt][db] = tr_operand<D>(sv[buf], 16 * tt, db * 32, lane);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const bf16x8 pb = (tt & 1) ? pack_operand<8>(sacc[tt >> 1]) : pack_operand<0>(sacc[tt >> 1]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const bf16x8 a = tr_operand(&sv[buf][0][0], ROW, 16 * tt, db * 32, lane);
-                    oacc[db] = mfma32x32x16(a, pb, oacc[db]);
-                }
+                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(va[tt][db], pb, oacc[db]);
             }
+            sched_pipeline<8 * DB, 4 * DB, 4, 2>();
         }
-        store_kv_tile<D, CH_T, ROW>(sk[buf ^ 1], sv[buf ^ 1], kst, vst, tid);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's prefetch has landed
         __syncthreads();
     }
 

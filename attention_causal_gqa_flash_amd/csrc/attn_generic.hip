@@ -11,6 +11,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace attn {
 
 // ---------------------------------------------------------------------------
@@ -74,11 +76,31 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
 // ---------------------------------------------------------------------------
 // Backward preprocess: D_i = dout_i . o_i.  D/8 lanes per row, 8 elements each.
 // ---------------------------------------------------------------------------
+// Zero-fill n floats at a and at b (n a multiple of 4, 16-byte aligned).
+__device__ __forceinline__ void zero2_grid_stride(float *a, float *b, long n)
+{
+    const long stride = (long)gridDim.x * blockDim.x;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
+        ((float4 *)a)[i] = z;
+        ((float4 *)b)[i] = z;
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_fill2_kernel(float *__restrict__ a, float *__restrict__ b,
+                                                         long n)
+{
+    zero2_grid_stride(a, b, n);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout,
                                                       const float *__restrict__ o,
-                                                      float *__restrict__ Dws, long rows)
+                                                      float *__restrict__ Dws, long rows,
+                                                      float *__restrict__ zero,
+                                                      float *__restrict__ zero2, long zero_len)
 {
+    if (zero != nullptr) zero2_grid_stride(zero, zero2, zero_len);
     constexpr int LPR = D / 8;              // lanes per row
     constexpr int RPB = 256 / LPR;          // rows per block
     const long row = (long)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -423,13 +445,22 @@ hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal,
 }
 
 hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
-                          hipStream_t st)
+                          float *zero, float *zero2, long zero_len, hipStream_t st)
 {
     const int rpb = 256 / (d / 8);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid,
                                                               dim3(256), 0, st, (const T *)dout,
-                                                              o, Dws, rows)));
+                                                              o, Dws, rows, zero, zero2,
+                                                              zero_len)));
+    return hipGetLastError();
+}
+
+hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st)
+{
+    const long blocks = std::min<long>((n / 4 + 255) / 256, 4096L);
+    hipLaunchKernelGGL(zero_fill2_kernel, dim3((unsigned)std::max<long>(blocks, 1)), dim3(256), 0,
+                       st, a, b, n);
     return hipGetLastError();
 }
 

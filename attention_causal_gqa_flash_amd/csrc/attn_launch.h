@@ -23,18 +23,26 @@ hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int ca
                             const void *dout, const float *Dws, float *dk, float *dv,
                             hipStream_t st);
 
-// D_i = dout_i . o_i for every query row (rows = B*Hq*N).
+// D_i = dout_i . o_i for every query row (rows = B*Hq*N).  With zero != nullptr
+// the same launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
 hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
-                          hipStream_t st);
+                          float *zero, float *zero2, long zero_len, hipStream_t st);
+// Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
+hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 
 // Matrix-core kernels: bf16 inputs, d in {64, 128}.
 bool mfma_supported(int dt, int d);
 hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                     const void *q, const void *k, const void *v, float *o, float *lse,
                     hipStream_t st);
+// Number of workgroups each group's query heads are split over by the dK/dV
+// kernel; with more than one, dk and dv must be zero-filled before the launch
+// (the kernel adds into them).
+int dkdv_head_split(int B, int Hq, int Hkv, int N);
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
-                         const void *dout, const float *Dws, float *dk, float *dv, hipStream_t st);
+                         const void *dout, const float *Dws, float *dk, float *dv, int hs,
+                         hipStream_t st);
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st);

@@ -51,7 +51,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch eagerly instead of replaying graphs (for counter collection; "
+                         "short ops are then bound by host launch overhead)")
     return ap.parse_args()
+
+
+def eager_time_us(torch, fns, reps: int) -> float:
+    """Run `fns` eagerly between HIP events; microseconds divided by `reps`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for fn in fns:
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
 
 
 def graph_time_us(torch, fns, reps: int) -> float:
@@ -148,11 +162,12 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    timer = eager_time_us if args.eager else graph_time_us
     train_fns = [fn for _ in range(K) for fn in train_op]
     dec_fns = [decode(s) for s in range(K)]
     # the timed region: K steps = K training ops and K decode ops
-    train_us = graph_time_us(torch, train_fns, K)
-    dec_us = graph_time_us(torch, dec_fns, K)
+    train_us = timer(torch, train_fns, K)
+    dec_us = timer(torch, dec_fns, K)
     step_us = train_us + dec_us
 
     pairs = cfg.pairs
@@ -167,7 +182,7 @@ def main():
     kernels = {}
     if not args.no_kernel_breakdown:
         for name, fn in (("fwd", fwd), ("bwd_preprocess", pre), ("bwd_dkdv", dkdv), ("bwd_dq", dqk)):
-            kernels[name] = {"avg_us": round(graph_time_us(torch, [fn] * K, K), 3)}
+            kernels[name] = {"avg_us": round(timer(torch, [fn] * K, K), 3)}
         kernels["decode_merged"] = {"avg_us": round(dec_us, 3)}
         for n, f in flop.items():
             t = kernels[n]["avg_us"] * 1e-6
@@ -214,7 +229,8 @@ def main():
                    "launches_per_call": 1},
         "kernels": kernels,
         "roofline": roof,
-        "timing": "HIP graph replay of K back-to-back ops between HIP events",
+        "timing": ("eager launches between HIP events" if args.eager else
+                   "HIP graph replay of K back-to-back ops between HIP events"),
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:

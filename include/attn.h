@@ -99,6 +99,9 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
  *   reductions too) and the compiler article's paragraph on comprehensions.
  *   o and lse must be the outputs of attn_fwd for the same q, k, v, causal,
  *   scale.  dq [B][Hq][N][d], dk/dv [B][Hkv][N][d] are f32 and overwritten.
+ *   dq is bitwise deterministic.  When the key tiles alone are too few to fill
+ *   the GPU, dk and dv sum the query heads of a group with f32 atomics and may
+ *   then differ from run to run in the last bits.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry do not matter.
  */
