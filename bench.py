@@ -54,7 +54,110 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch eagerly instead of replaying graphs (for counter collection; "
                          "short ops are then bound by host launch overhead)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="only run a plain device-to-device copy of known size (the reference "
+                         "dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise four rocprofv3 counter_collection.csv files (the bench's and "
+                         "the calibration copy's FETCH_SIZE and WRITE_SIZE runs) as markdown")
     return ap.parse_args()
+
+
+# Size of the calibration copy: far beyond L2 and the last-level cache.
+CALIB_BYTES = 1 << 30
+
+# Kernel symbol fragment -> kernel name used in the bench output.
+KERNEL_NAMES = (("fwd_mfma_kernel", "fwd"), ("bwd_pre_kernel", "bwd_preprocess"),
+                ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
+                ("decode_mfma_kernel", "decode_merged"), ("lse_merge_kernel", "lse_merge"))
+
+TRAFFIC_TAG = "traffic-json: "
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the library's kernel sources: a counter summary taken from
+    other sources no longer describes these kernels."""
+    import hashlib
+    d = os.path.join(ROOT, "attention_causal_gqa_flash_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+
+
+def load_traffic(workload: str):
+    """Per-kernel HBM bytes per launch from the committed counter summary of this
+    workload, or None when there is none or the kernel sources changed since."""
+    try:
+        with open(traffic_file(workload)) as f:
+            for line in f:
+                if line.startswith(TRAFFIC_TAG):
+                    t = json.loads(line[len(TRAFFIC_TAG):])
+                    return t["kernels"] if t.get("source_sha") == kernel_source_sha() else None
+    except OSError:
+        pass
+    return None
+
+
+def read_counter_csv(path: str, counter: str) -> dict:
+    """{kernel symbol: [per-dispatch values]} of one counter in a rocprofv3
+    counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload) -> str:
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel,
+    scaled to bytes by the calibration copy (which reads and writes CALIB_BYTES)."""
+    fetch, write = read_counter_csv(fetch_csv, "FETCH_SIZE"), read_counter_csv(write_csv, "WRITE_SIZE")
+    cf = [v for vals in read_counter_csv(copy_fetch_csv, "FETCH_SIZE").values() for v in vals]
+    cw = [v for vals in read_counter_csv(copy_write_csv, "WRITE_SIZE").values() for v in vals]
+    if not cf or not cw:
+        raise SystemExit("no calibration dispatches in the copy runs")
+    # median over the copy dispatches: KiB the counter reports for CALIB_BYTES moved
+    kf, kw = sorted(cf)[len(cf) // 2], sorted(cw)[len(cw) // 2]
+    sf, sw = CALIB_BYTES / (kf * 1024), CALIB_BYTES / (kw * 1024)
+    lines = [f"calibration copy of {CALIB_BYTES} B: FETCH_SIZE {kf:.0f} KiB (scale {sf:.4f}), "
+             f"WRITE_SIZE {kw:.0f} KiB (scale {sw:.4f})", "",
+             "| kernel | dispatches | FETCH_SIZE KiB (mean) | WRITE_SIZE KiB (mean) | "
+             "HBM read B (scaled) | HBM write B (scaled) |", "|---|---|---|---|---|---|"]
+    kernels = {}
+    for frag, name in KERNEL_NAMES:
+        fv = [v for k, vals in fetch.items() if frag in k for v in vals]
+        wv = [v for k, vals in write.items() if frag in k for v in vals]
+        if not fv or not wv:
+            continue
+        mf, mw = sum(fv) / len(fv), sum(wv) / len(wv)
+        rb, wb = mf * 1024 * sf, mw * 1024 * sw
+        kernels[name] = {"read_bytes": round(rb), "write_bytes": round(wb), "bytes": round(rb + wb)}
+        lines.append(f"| {name} | {len(fv)} | {mf:.1f} | {mw:.1f} | {rb:.0f} | {wb:.0f} |")
+    lines += ["", TRAFFIC_TAG + json.dumps({"workload": workload, "source_sha": kernel_source_sha(),
+                                            "kernels": kernels})]
+    return "\n".join(lines)
+
+
+def calibration_copy():
+    import torch
+    n = CALIB_BYTES // 4
+    src = torch.empty(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": CALIB_BYTES, "dispatches": 5}), flush=True)
 
 
 def eager_time_us(torch, fns, reps: int) -> float:
@@ -94,8 +197,11 @@ def graph_time_us(torch, fns, reps: int) -> float:
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        print(traffic_summary(*args.traffic_summary, workload=args.workload))
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs on one GPU only; "
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only; "
                                    "multi-GPU runs are not supported"}))
         sys.exit(2)
 
@@ -105,6 +211,9 @@ def main():
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+    if args.calibration_copy:
+        calibration_copy()
+        return
     attn.lib()
     dev = torch.device("cuda:0")
 
@@ -192,6 +301,12 @@ def main():
         kernels["bwd_preprocess"]["GB_s"] = round(pre_bytes / (kernels["bwd_preprocess"]["avg_us"] * 1e-6) / 1e9, 1)
         kernels["decode_merged"]["GB_s"] = round(dec_gbs, 1)
 
+    traffic = load_traffic(cfg.name)
+    if traffic:
+        for n, t in traffic.items():
+            if n in kernels:
+                kernels[n]["hbm_bytes_measured"] = t["bytes"]
+
     roof = None
     if kernels:
         dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
@@ -199,12 +314,14 @@ def main():
         if dom in flop:
             ach = flop[dom] / (t * 1e-6) / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
                     "avg_launch_us": t}
         else:
             ach = kernels[dom]["GB_s"]
             roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
                     "avg_launch_us": t}
 
     result = {
@@ -246,7 +363,7 @@ def cpu_baseline(cfg, x, budget_s: float) -> dict:
     groups = [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
     done, flop = 0, 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < 4 * len(groups):
+    while time.perf_counter() - t0 < budget_s and done < 64 * len(groups):
         b, g = groups[done % len(groups)]
         hs = slice(g * G, (g + 1) * G)
         q, k, v, do = (x["q"][b:b + 1, hs], x["k"][b:b + 1, g:g + 1], x["v"][b:b + 1, g:g + 1],
