@@ -39,7 +39,13 @@ attn_status check_common(int dt, int B, int Hq, int Hkv, int N, int d, float sca
 
 // The matrix-core kernels run softmax in base 2 on |scale|*log2(e) and need a
 // nonzero scale; a zero scale (uniform attention) takes the generic kernels.
-bool use_mfma(int dt, int d, float scale) { return attn::mfma_supported(dt, d) && scale != 0.f; }
+// They address one head's [N][d] bf16 rows through a buffer resource with
+// 32-bit byte offsets, so heads of 2^31 bytes or more take the generic
+// kernels too.
+bool use_mfma(int dt, int N, int d, float scale)
+{
+    return attn::mfma_supported(dt, d) && scale != 0.f && (long)N * d * 2 < (1L << 31);
+}
 
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
@@ -64,7 +70,7 @@ hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int N, int d, c
 // Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
 int dkdv_split(int dt, int B, int Hq, int Hkv, int N, int d, float scale)
 {
-    return use_mfma(dt, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, N) : 1;
+    return use_mfma(dt, N, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, N) : 1;
 }
 
 // dk and dv must already be zero when hs > 1.
@@ -73,7 +79,7 @@ hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int N, int d, int cau
                            const void *dout, const float *delta, float *dk, float *dv, int hs,
                            hipStream_t st)
 {
-    if (use_mfma(dt, d, scale))
+    if (use_mfma(dt, N, d, scale))
         return attn::bwd_dkdv_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
                                    delta, dk, dv, hs, st);
     return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
@@ -84,7 +90,7 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causa
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *delta, float *dq, hipStream_t st)
 {
-    if (use_mfma(dt, d, scale))
+    if (use_mfma(dt, N, d, scale))
         return attn::bwd_dq_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout, delta,
                                  dq, st);
     return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
@@ -105,7 +111,7 @@ attn_status attn_fwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
         return ATTN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (use_mfma(dt, d, scale))
+    if (use_mfma(dt, N, d, scale))
         e = attn::fwd_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);
     else
         e = attn::fwd_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);

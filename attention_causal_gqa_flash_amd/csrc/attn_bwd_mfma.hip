@@ -42,8 +42,77 @@ namespace {
 constexpr int kKvBN = 64;   // keys per workgroup
 constexpr int kKvBM = 64;   // queries per step
 
+// One (64-query step, 32x32 block) of the dK/dV kernel for one wave: S = Q K^T
+// and dP = dO V^T (lane = key column), P = 2^(c2 s - lse log2 e),
+// dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS over the block's 32
+// queries.  With `mask` (wave-uniform) keys after the query and query rows
+// past N get P = 0.
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+__device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
+                                           const float *ddt, const bf16x8 (&kf)[D / 16],
+                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32],
+                                           f32x16 (&dva)[D / 32], float c2, int qh, int q0, int kj,
+                                           int N, int causal, bool mask, int lane)
+{
+    constexpr int KS = D / 16, DB = D / 32;
+    const int l32 = lane & 31, hf = lane >> 5;
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 aq = tile_row_operand<D>(qt, 32 * qh + l32, 2 * ks + hf);
+        const bf16x8 ad = tile_row_operand<D>(dt, 32 * qh + l32, 2 * ks + hf);
+        sacc = mfma32x32x16(aq, kf[ks], sacc);
+        pacc = mfma32x32x16(ad, vf[ks], pacc);
+    }
+    sched_pipeline<2 * KS, 2 * KS, 4, 1>();
+    // rows are queries (register r: local row 32qh + 8(r/4) + 4hf + r%4), lane = key
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int rr = 32 * qh + 8 * a + 4 * hf;
+        const float4 l4 = *(const float4 *)&lt[rr];
+        const float4 d4 = *(const float4 *)&ddt[rr];
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * a + e;
+            sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
+            pacc[r] = pacc[r] - dv[e];
+        }
+    }
+    if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + 32 * qh + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool keep = (!causal || kj <= qrow) && qrow < N;
+            sacc[r] = keep ? sacc[r] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] *= sacc[r];
+    // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const bf16x8 pb = tt ? pack_operand<8>(sacc) : pack_operand<0>(sacc);
+        const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const bf16x8 ado = tr_operand<D>(dt, 32 * qh + 16 * tt, db * 32, lane);
+            const bf16x8 aqt = tr_operand<D>(qt, 32 * qh + 16 * tt, db * 32, lane);
+            dva[db] = mfma32x32x16(ado, pb, dva[db]);
+            dka[db] = mfma32x32x16(aqt, sb, dka[db]);
+        }
+    }
+    sched_pipeline<8 * DB, 4 * DB, 4, 2>();
+}
+
+// d = 128 needs more than the 256 registers of two waves per SIMD (K, V
+// operands 64 + dK, dV accumulators 128 + scores 32 + operands in flight):
+// it runs one wave per SIMD with up to 512.
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
@@ -51,18 +120,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 {
     constexpr int KS = D / 16, DB = D / 32;
 
-    // One LDS block: double-buffered Q, dO, lse and D tiles during the loop,
-    // then the reduction buffer for the two query halves' dK^T and dV^T.
-    struct Smem {
-        uint16_t q[2][kKvBM * D];                  // row-major, swizzled chunks
-        uint16_t dO[2][kKvBM * D];
-        float lse[2][kKvBM];
-        float dd[2][kKvBM];
-    };
-    constexpr int RED = DB * 16 * 64;        // floats per (key block, dK or dV) partial
-    static_assert(4 * RED * sizeof(float) <= sizeof(Smem), "reduction must fit in the staging LDS");
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(Smem)];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    // Double-buffered Q, dO, lse and D tiles in separate arrays (see Buf); at
+    // the end the four tile arrays hold the dK^T / dV^T partials of the two
+    // query halves.
+    __shared__ __attribute__((aligned(16))) uint16_t q0s[kKvBM * D], q1s[kKvBM * D];
+    __shared__ __attribute__((aligned(16))) uint16_t d0s[kKvBM * D], d1s[kKvBM * D];
+    __shared__ __attribute__((aligned(16))) float l0s[kKvBM], l1s[kKvBM], e0s[kKvBM], e1s[kKvBM];
 
     // Work item = (key tile, batch, kv head, head subset).  The G query heads of
     // a group are split into hs subsets of Gs heads; with hs > 1 the subsets'
@@ -111,146 +174,109 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const int nq = nqt - qt0;
     const int steps = Gs * nq;               // (query head, query tile) pairs
 
-// Step s covers query head g*G + hsub*Gs + s/nq, query tile qt0 + s%nq.  Its Q and dO
-// tiles and its lse and D rows move global -> LDS directly (rows past N are
-// clamped to N-1 and masked in the step's arithmetic).
-#define ATTN_LOAD_STEP(s_, buf_)                                                                \
-    {                                                                                           \
-        const size_t hrow_ = ((size_t)b * Hq + g * G + hsub * Gs + (s_) / nq) * N;              \
-        const int q0_ = (qt0 + (s_) % nq) * kKvBM;                                              \
-        tile_load_lds<D, kKvBM>(sm.q[buf_], Q + hrow_ * D, q0_, N, wave, 4, lane);              \
-        tile_load_lds<D, kKvBM>(sm.dO[buf_], dO + hrow_ * D, q0_, N, wave, 4, lane);            \
-        const int row_ = min(q0_ + lane, N - 1);                                                \
-        if (wave == 0)                                                                          \
-            __builtin_amdgcn_global_load_lds((const void *)(LSE + hrow_ + row_),                \
-                (__attribute__((address_space(3))) void *)&sm.lse[buf_][0], 4, 0, 0);           \
-        else if (wave == 1)                                                                     \
-            __builtin_amdgcn_global_load_lds((const void *)(Dws + hrow_ + row_),                \
-                (__attribute__((address_space(3))) void *)&sm.dd[buf_][0], 4, 0, 0);            \
-    }
-    if (steps > 0) ATTN_LOAD_STEP(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < steps) ATTN_LOAD_STEP(s + 1, buf ^ 1);   // in flight during the MFMAs
+    // Step s covers query head g*G + hsub*Gs + s/nq, query tile qt0 + s%nq.  Its
+    // Q and dO tiles and its lse and D rows move global -> LDS directly; rows
+    // past N read as zero and are masked in the step's arithmetic.
+    const uint32_t tile_bytes = (uint32_t)N * D * 2, row_bytes = (uint32_t)N * 4;
+    auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd, float *ld, float *ed) {
+        const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * N;
+        const int q0_ = (qt0 + s_ % nq) * kKvBM;
+        tile_load_lds<D, kKvBM>(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave, 4, lane);
+        tile_load_lds<D, kKvBM>(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave, 4, lane);
+        if (wave == 0) row_load_lds(ld, make_rsrc(LSE + hrow, row_bytes), q0_, lane);
+        else if (wave == 1) row_load_lds(ed, make_rsrc(Dws + hrow, row_bytes), q0_, lane);
+    };
+    if (steps > 0) load_step(0, q0s, d0s, l0s, e0s);
+
+    auto run_step = [&](auto bufc, int s) {
+        constexpr int BI = decltype(bufc)::value;
+        const uint16_t *qc = BI ? q1s : q0s, *dc = BI ? d1s : d0s;
+        const float *lc = BI ? l1s : l0s, *ec = BI ? e1s : e0s;
+        wait_vmcnt<0>();                    // this wave's copies of step s have landed
+        __syncthreads();                    // ... and every wave's; buffer s+1 is free
+        if (s + 1 < steps) {
+            if (BI) load_step(s + 1, q0s, d0s, l0s, e0s);
+            else load_step(s + 1, q1s, d1s, l1s, e1s);
+        }
         const int q0 = (qt0 + s % nq) * kKvBM;
         const int qb0 = q0 + 32 * qh;       // first query row of this wave's block
-        const bool active = qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb);
-        if (active) {
-            f32x16 sacc, pacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-            bf16x8 aq[KS], ad[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                aq[ks] = tile_row_operand<D>(sm.q[buf], 32 * qh + l32, 2 * ks + hf);
-                ad[ks] = tile_row_operand<D>(sm.dO[buf], 32 * qh + l32, 2 * ks + hf);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sacc = mfma32x32x16(aq[ks], kf[ks], sacc);
-                pacc = mfma32x32x16(ad[ks], vf[ks], pacc);
-            }
-            sched_pipeline<2 * KS, 2 * KS, 4, 1>();
-            // P = exp(scale s - lse), dS = P (dP - D); rows are queries, lane = key.
-            // Masked (only on diagonal and tail steps, a wave-uniform branch):
-            // keys after the query (causal) and query rows past N.
-            const bool masked = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int rr = 32 * qh + 8 * a + 4 * hf;       // local query row of r = 4a
-                const float4 l4 = *(const float4 *)&sm.lse[buf][rr];
-                const float4 d4 = *(const float4 *)&sm.dd[buf][rr];
-                const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * a + e;
-                    sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
-                    pacc[r] = pacc[r] - dv[e];
-                }
-                if (masked) {
-                    const int qrow = q0 + rr;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool keep = (!causal || kj <= qrow + e) && qrow + e < N;
-                        sacc[4 * a + e] = keep ? sacc[4 * a + e] : 0.f;
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pacc[4 * a + e] *= sacc[4 * a + e];
-            }
-            // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
-            bf16x8 ado[2][DB], aqt[2][DB];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    ado[tt][db] = tr_operand<D>(sm.dO[buf], 32 * qh + 16 * tt, db * 32, lane);
-                    aqt[tt][db] = tr_operand<D>(sm.q[buf], 32 * qh + 16 * tt, db * 32, lane);
-                }
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const bf16x8 pb = tt ? pack_operand<8>(sacc) : pack_operand<0>(sacc);
-                const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dva[db] = mfma32x32x16(ado[tt][db], pb, dva[db]);
-                    dka[db] = mfma32x32x16(aqt[tt][db], sb, dka[db]);
-                }
-            }
-            sched_pipeline<8 * DB, 4 * DB, 4, 2>();
+        if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
+            const bool mask = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
+            dkdv_block<D>(qc, dc, lc, ec, kf, vf, dka, dva, c2, qh, q0, kj, N, causal, mask, lane);
         }
-        __builtin_amdgcn_s_waitcnt(0);      // this wave's prefetch has landed
-        __syncthreads();
+        sched_fence();
+    };
+    for (int s = 0; s < steps; s += 2) {
+        run_step(Buf<0>{}, s);
+        if (s + 1 < steps) run_step(Buf<1>{}, s + 1);
     }
-#undef ATTN_LOAD_STEP
 
-    // Sum the two query halves through LDS, then write dK = scale (dK^T)^T and
-    // dV.  Accumulator layout: lane = key column kj, register r = dim
-    // db*32 + 8(r/4) + 4hf + (r&3).
-    float *red = reinterpret_cast<float *>(smem_raw);   // [key block][dK, dV][DB*16][64]
+    // Sum the two query halves and write dK = scale (dK^T)^T and dV.
+    // Accumulator layout: lane = key column kj, register r of block db = dim
+    // db*32 + 8(r/4) + 4hf + (r&3).  The query-half-1 waves park their partials
+    // in the tile arrays (one array per (key block, dK or dV)), the half-0 waves
+    // add them and park the sums, transposed to [key][dim], so that the final
+    // stores (or atomics) run along the dim with consecutive lanes.
+    constexpr int RED = DB * 16 * 64;        // floats per (key block, dK or dV) partial
+    static_assert(RED * sizeof(float) == sizeof(q0s), "one partial per tile array");
+    float *redk = reinterpret_cast<float *>(kb ? q1s : q0s);
+    float *redv = reinterpret_cast<float *>(kb ? d1s : d0s);
+    __syncthreads();                         // the last step's reads are done
     if (qh == 1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                red[(kb * 2 + 0) * RED + (db * 16 + r) * 64 + lane] = dka[db][r];
-                red[(kb * 2 + 1) * RED + (db * 16 + r) * 64 + lane] = dva[db][r];
+                redk[(db * 16 + r) * 64 + lane] = dka[db][r];
+                redv[(db * 16 + r) * 64 + lane] = dva[db][r];
             }
     }
     __syncthreads();
-    if (qh == 0 && kj < N) {
-        float *dkrow = dK + (((size_t)b * Hkv + g) * N + kj) * D;
-        float *dvrow = dV + (((size_t)b * Hkv + g) * N + kj) * D;
-        const float *rk = red + (kb * 2 + 0) * RED + lane;
-        const float *rv = red + (kb * 2 + 1) * RED + lane;
+    if (qh == 0) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int d0 = db * 32 + 8 * a + 4 * hf;
-                const int r0 = db * 16 + 4 * a;
-                float4 k4, v4;
-                k4.x = (dka[db][4 * a + 0] + rk[(r0 + 0) * 64]) * scale;
-                k4.y = (dka[db][4 * a + 1] + rk[(r0 + 1) * 64]) * scale;
-                k4.z = (dka[db][4 * a + 2] + rk[(r0 + 2) * 64]) * scale;
-                k4.w = (dka[db][4 * a + 3] + rk[(r0 + 3) * 64]) * scale;
-                v4.x = dva[db][4 * a + 0] + rv[(r0 + 0) * 64];
-                v4.y = dva[db][4 * a + 1] + rv[(r0 + 1) * 64];
-                v4.z = dva[db][4 * a + 2] + rv[(r0 + 2) * 64];
-                v4.w = dva[db][4 * a + 3] + rv[(r0 + 3) * 64];
-                if (hs == 1) {
-                    *(float4 *)(dkrow + d0) = k4;
-                    *(float4 *)(dvrow + d0) = v4;
-                } else {
-                    atomicAdd(dkrow + d0 + 0, k4.x); atomicAdd(dkrow + d0 + 1, k4.y);
-                    atomicAdd(dkrow + d0 + 2, k4.z); atomicAdd(dkrow + d0 + 3, k4.w);
-                    atomicAdd(dvrow + d0 + 0, v4.x); atomicAdd(dvrow + d0 + 1, v4.y);
-                    atomicAdd(dvrow + d0 + 2, v4.z); atomicAdd(dvrow + d0 + 3, v4.w);
-                }
+            for (int r = 0; r < 16; ++r) {
+                dka[db][r] = (dka[db][r] + redk[(db * 16 + r) * 64 + lane]) * scale;
+                dva[db][r] += redv[(db * 16 + r) * 64 + lane];
             }
+    }
+    __syncthreads();
+    // transposed park: key row l32 (of this key block), dim d at
+    // [l32][d ^ l32] -- the XOR spreads the 32 rows written by one instruction
+    // over the banks and keeps each row a permutation of its dims
+    static_assert(32 * D * sizeof(float) == sizeof(q0s), "transposed partial fits");
+    if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dim = db * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                redk[l32 * D + (dim ^ l32)] = dka[db][r];
+                redv[l32 * D + (dim ^ l32)] = dva[db][r];
+            }
+    }
+    __syncthreads();
+    // all 4 waves write: wave w takes key rows w, w+4, ... of the 64-key tile;
+    // lanes run along the dim
+    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)N * D;
+    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)N * D;
+    for (int kr = wave; kr < kKvBN; kr += 4) {
+        const int key = k0 + kr;
+        if (key >= N) break;
+        const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s) + (kr & 31) * D;
+        const float *sv = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s) + (kr & 31) * D;
+#pragma unroll
+        for (int d0 = 0; d0 < D; d0 += 64) {
+            const int dim = d0 + lane, src = dim ^ (kr & 31);
+            if (hs == 1) {
+                dKg[(size_t)key * D + dim] = sk[src];
+                dVg[(size_t)key * D + dim] = sv[src];
+            } else {
+                atomicAdd(dKg + (size_t)key * D + dim, sk[src]);
+                atomicAdd(dVg + (size_t)key * D + dim, sv[src]);
+            }
+        }
     }
 }
 
@@ -259,6 +285,53 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kQBM = 128;   // queries per workgroup (32 per wave)
 constexpr int kQBN = 64;    // keys per tile
+
+// One 64-key tile of the dQ kernel for one wave (lane = query row): S^T = K Q^T
+// and dP^T = V dO^T per 32-key block, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+template <int D>
+__device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb, const bf16x8 (&qf)[D / 16],
+                                        const bf16x8 (&dof)[D / 16], f32x16 (&dqa)[D / 32], float c2,
+                                        float lse2, float Di, int kv0, int qi, int N, int causal,
+                                        bool mask, int lane)
+{
+    constexpr int KS = D / 16, DB = D / 32;
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 ak = tile_row_operand<D>(skb, kb * 32 + l32, 2 * ks + hf);
+            const bf16x8 av = tile_row_operand<D>(svb, kb * 32 + l32, 2 * ks + hf);
+            sacc = mfma32x32x16(ak, qf[ks], sacc);
+            pacc = mfma32x32x16(av, dof[ks], pacc);
+        }
+        sched_pipeline<2 * KS, 2 * KS, 4, 1>();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lse2));
+        if (mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                const bool hide = (causal && key > qi) || key >= N;
+                sacc[r] = hide ? 0.f : sacc[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - Di);
+        // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dqa[db] = mfma32x32x16(tr_operand<D>(skb, kb * 32 + 16 * tt, db * 32, lane), sb, dqa[db]);
+        }
+        sched_pipeline<4 * DB, 2 * DB, 4, 2>();
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
@@ -269,9 +342,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 {
     constexpr int KS = D / 16, DB = D / 32;
 
-    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kQBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kQBN * D];
+    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered in
+    // separate arrays (see Buf)
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -317,65 +391,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int kv_end = causal ? min(N, q0 + kQBM) : N;
     const int ntiles = (kv_end + kQBN - 1) / kQBN;
 
-    // Tiles move global -> LDS directly; rows past N are clamped and masked.
-    tile_load_lds<D, kQBN>(sk[0], Kg, 0, N, wave, 4, lane);
-    tile_load_lds<D, kQBN>(sv[0], Vg, 0, N, wave, 4, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) {       // prefetch into the idle buffer, in flight during the MFMAs
-            tile_load_lds<D, kQBN>(sk[buf ^ 1], Kg, (t + 1) * kQBN, N, wave, 4, lane);
-            tile_load_lds<D, kQBN>(sv[buf ^ 1], Vg, (t + 1) * kQBN, N, wave, 4, lane);
+    // Tiles move global -> LDS directly; rows past N read as zero and are masked.
+    const uint32_t kv_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, kv_bytes), rv = make_rsrc(Vg, kv_bytes);
+    tile_load_lds<D, kQBN>(sk0, rk, 0, wave, 4, lane);
+    tile_load_lds<D, kQBN>(sv0, rv, 0, wave, 4, lane);
+
+    auto run_tile = [&](auto bufc, int t) {
+        constexpr int BI = decltype(bufc)::value;
+        const uint16_t *skc = BI ? sk1 : sk0, *svc = BI ? sv1 : sv0;
+        uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
+        wait_vmcnt<0>();                    // this wave's copies of tile t have landed
+        __syncthreads();                    // ... and every wave's; buffer t+1 is free
+        if (t + 1 < ntiles) {
+            tile_load_lds<D, kQBN>(skn, rk, (t + 1) * kQBN, wave, 4, lane);
+            tile_load_lds<D, kQBN>(svn, rv, (t + 1) * kQBN, wave, 4, lane);
         }
         const int kv0 = t * kQBN;
-        const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
-        if (active) {
-            const bool need_mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x16 sacc, pacc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-                bf16x8 ak[KS], av[KS];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    ak[ks] = tile_row_operand<D>(sk[buf], kb * 32 + l32, 2 * ks + hf);
-                    av[ks] = tile_row_operand<D>(sv[buf], kb * 32 + l32, 2 * ks + hf);
-                }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    sacc = mfma32x32x16(ak[ks], qf[ks], sacc);
-                    pacc = mfma32x32x16(av[ks], dof[ks], pacc);
-                }
-                sched_pipeline<2 * KS, 2 * KS, 4, 1>();
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = exp2_fast(fmaf(sacc[r], c2, -lse2));
-                    if (need_mask) {
-                        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if ((causal && key > qi) || key >= N) p = 0.f;
-                    }
-                    pacc[r] = p * (pacc[r] - Di);
-                }
-                // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
-                bf16x8 kt_[2][DB];
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        kt_[tt][db] = tr_operand<D>(sk[buf], kb * 32 + 16 * tt, db * 32, lane);
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const bf16x8 sb = tt ? pack_operand<8>(pacc) : pack_operand<0>(pacc);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16(kt_[tt][db], sb, dqa[db]);
-                }
-                sched_pipeline<4 * DB, 2 * DB, 4, 2>();
-            }
+        if (qw0 < N && (!causal || kv0 <= qw0 + 31)) {
+            const bool mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
+            dq_tile<D>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi, N, causal, mask, lane);
         }
-        __builtin_amdgcn_s_waitcnt(0);      // this wave's prefetch has landed
-        __syncthreads();
+        sched_fence();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        run_tile(Buf<0>{}, t);
+        if (t + 1 < ntiles) run_tile(Buf<1>{}, t + 1);
     }
 
     if (qi < N) {

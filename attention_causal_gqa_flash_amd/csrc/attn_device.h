@@ -81,15 +81,28 @@ __device__ __forceinline__ const uint16_t *tile_chunk(const uint16_t *tile, int 
     return tile + row * D + 8 * (c ^ swz<D>(row));
 }
 
-// Direct global -> LDS copy (global_load_lds_dwordx4, no registers): one wave
-// instruction moves 64 x 16 bytes into 1 KiB of LDS, lane L landing at byte
-// 16 L.  The tile of `rows` rows is filled in 1 KiB blocks; lane L of block j
-// owns physical chunk 64 j + L and so fetches the logical chunk that the
-// swizzle maps there.  Rows at or past N are clamped to row N-1 (the callers
-// give such rows zero weight).  Waves 0..nwaves-1 share the blocks.  The copy
+// Buffer resource over `bytes` bytes at `base` (raw buffer, stride 0): loads
+// at byte offsets past `bytes` return zero.  Dword 3 = 0x00020000 is the
+// gfx9 untyped 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds, no registers): one
+// wave instruction moves 64 x 16 bytes into 1 KiB of LDS, lane L landing at
+// byte 16 L.  The LDS address is wave-uniform (M0).  The tile of `rows` rows
+// starting at row r0 of the [*][D] bf16 tensor behind `rs` is filled in 1 KiB
+// blocks; lane L of block j owns physical chunk 64 j + L and so fetches the
+// logical chunk that the swizzle maps there.  Rows past the end of the
+// resource read as zero.  Waves 0..nwaves-1 share the blocks.  The copy
 // completes asynchronously: wait for vmcnt before the barrier that publishes it.
+// (The buffer form, unlike global_load_lds, lets the compiler keep partial
+// LDS-read waits while a copy is in flight.)
 template <int D, int ROWS>
-__device__ __forceinline__ void tile_load_lds(uint16_t *tile, const uint16_t *src, int r0, int N,
+__device__ __forceinline__ void tile_load_lds(uint16_t *tile, __amdgpu_buffer_rsrc_t rs, int r0,
                                               int wave, int nwaves, int lane)
 {
     constexpr int CPR = D / 8;                    // 16-byte chunks per row
@@ -99,11 +112,16 @@ __device__ __forceinline__ void tile_load_lds(uint16_t *tile, const uint16_t *sr
         const int p = 64 * j + lane;
         const int row = p / CPR;
         const int c = (p % CPR) ^ swz<D>(row);
-        const int grow = min(r0 + row, N - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)grow * D + 8 * c),
-                                         (__attribute__((address_space(3))) void *)(tile + 512 * j),
-                                         16, 0, 0);
+        const int off = ((r0 + row) * D + 8 * c) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + 512 * j), 16, off, 0, 0, 0);
     }
+}
+
+// 64 consecutive floats (rows r0 .. r0+63 of a per-row vector) -> LDS, one
+// wave instruction; entries past the end of the resource read as zero.
+__device__ __forceinline__ void row_load_lds(float *dst, __amdgpu_buffer_rsrc_t rs, int r0, int lane)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, (r0 + lane) * 4, 0, 0, 0);
 }
 
 // 8 bf16 (logical chunk c) of one row: an MFMA operand whose contraction runs
@@ -133,6 +151,30 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int kbase, in
     const uint2 hi = lds_read_tr16(tile_chunk<D>(tile, row + 8, c) + off);
     return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
+
+// Wait until at most N of this wave's vector-memory operations (direct
+// global->LDS copies included) are outstanding; LDS and export counters are
+// not waited on.  gfx9 s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// No instruction is scheduled across this point (keeps MFMAs issued before a
+// wait instead of after it).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// LDS tile buffers are separate __shared__ arrays chosen at compile time: the
+// compiler then knows that a read of the current buffer does not alias the
+// direct global->LDS copy in flight into the other one, and does not wait for
+// that copy before the read.
+template <int I>
+struct Buf {
+    static constexpr int value = I;
+};
 
 // Scheduling hint for the current basic block: NR LDS reads and NM MFMAs are
 // interleaved as AHEAD reads first, then (one MFMA, RPM reads) while reads

@@ -44,18 +44,118 @@ constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
 constexpr float kLazy = 8.f;  // max growth tolerated before rescaling (log2 units)
 
+// Per-wave state of the streaming softmax: this lane's query row, its Q^T
+// operand, the O^T accumulator and the running max / partial sum.
+template <int D>
+struct FwdState {
+    static constexpr int KS = D / 16;       // MFMA k-steps over the head dim
+    static constexpr int DB = D / 32;       // 32-row blocks of O^T
+    bf16x8 qf[KS];
+    f32x16 oacc[DB];
+    float m_run;    // running max of c2 * q.k for this lane's row (log2 units)
+    float l_run;    // this lane's share of the running sum
+};
+
+// One 64-key tile for one wave: S^T = K Q^T, the online-softmax update and
+// O^T += V^T P^T.  With `mask` (wave-uniform: diagonal and tail tiles) keys
+// after the query row and past the sequence end are hidden.
+template <int D>
+__device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, const uint16_t *svb,
+                                         float c2, int kv0, int qi, int N, int causal, bool mask,
+                                         int lane)
+{
+    constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
+    const int l32 = lane & 31, hf = lane >> 5;
+
+    // S^T for the tile's two 32-key blocks; the K operands are read first and
+    // interleaved with the MFMAs (4 reads ahead, then one per MFMA).
+    f32x16 sacc[2];
+    bf16x8 ka[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = tile_row_operand<D>(skb, kb * 32 + l32, 2 * ks + hf);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], st.qf[ks], sacc[kb]);
+    sched_pipeline<2 * KS, 2 * KS, 4, 1>();
+
+    // Row max on the raw scores (c2 > 0 commutes with max); masked scores are -inf.
+    if (mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                const bool hide = (causal && key > qi) || key >= N;
+                sacc[kb][r] = hide ? -INFINITY : sacc[kb][r];
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    // Lazy rescale: raise the running max only when some row of the wave grew
+    // past it by more than kLazy.  A row's first tile always sets it, since
+    // every row sees key 0 in the first tile; a fully hidden row keeps -inf.
+    if (__any(mx > st.m_run + kLazy)) {
+        const float m_new = fmaxf(st.m_run, mx);
+        const float alpha = st.m_run == -INFINITY ? 0.f : exp2_fast(st.m_run - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
+        st.m_run = m_new;
+    }
+    // p = 2^(c2 s - m): one FMA and one exp per score (exp2(-inf) = 0)
+    float rs = 0.f;
+    const float nm = -st.m_run;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(fmaf(sacc[kb][r], c2, nm));
+            sacc[kb][r] = p;
+            rs += p;
+        }
+    st.l_run += rs;
+
+    // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
+    // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
+    // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
+    bf16x8 va[4][DB];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[tt][db] = tr_operand<D>(svb, 16 * tt, db * 32, lane);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const bf16x8 pb = (tt & 1) ? pack_operand<8>(sacc[tt >> 1]) : pack_operand<0>(sacc[tt >> 1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) st.oacc[db] = mfma32x32x16(va[tt][db], pb, st.oacc[db]);
+    }
+    sched_pipeline<8 * DB, 4 * DB, 4, 2>();
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
     int Hkv, int N, float scale, int causal, int nqt)
 {
-    constexpr int KS = D / 16;              // MFMA k-steps over the head dim
-    constexpr int DB = D / 32;              // 32-row blocks of O^T
-
-    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered
-    __shared__ __attribute__((aligned(16))) uint16_t sk[2][kBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sv[2][kBN * D];
+    constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
+    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered in
+    // four separate arrays (see Buf)
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[kBN * D], sk1[kBN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[kBN * D], sv1[kBN * D];
 
     const int BH = B * Hq;
     const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
@@ -74,133 +174,63 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
 
-    // Softmax on x = q.k scaled by c2 = |scale| log2(e) > 0; a negative scale
-    // is carried by negating q, which is exact in bf16.
+    // Softmax on c2 q.k with c2 = |scale| log2(e) > 0; a negative scale is
+    // carried by negating q, which is exact in bf16.
     const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-    const float cabs = fabsf(scale);
-    const float c2 = cabs * kLog2e;
+    const float c2 = fabsf(scale) * kLog2e;
 
-    // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7] (rows past N read row N-1).
-    bf16x8 qf[KS];
+    FwdState<D> st;
     {
+        // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7] (rows past N read row N-1)
         const int qr = min(qi, N - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 u = *(const uint4 *)(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
             u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
-            qf[ks] = as_bf16x8(u);
+            st.qf[ks] = as_bf16x8(u);
         }
     }
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
 
     const int kv_end = causal ? min(N, q0 + kBM) : N;
     const int ntiles = (kv_end + kBN - 1) / kBN;
 
-    float m_run = -INFINITY;   // running max of x * c2 for this lane's row
-    float l_run = 0.f;         // this lane's share of the running sum
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    // Tiles move global -> LDS directly (no staging registers); rows past N
+    // read as zero, their scores are masked.
+    const uint32_t kv_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, kv_bytes), rv = make_rsrc(Vg, kv_bytes);
+    tile_load_lds<D, kBN>(sk0, rk, 0, wave, 4, lane);
+    tile_load_lds<D, kBN>(sv0, rv, 0, wave, 4, lane);
 
-    // Tiles move global -> LDS directly (no staging registers); rows past N are
-    // clamped to N-1, their scores masked below.
-    tile_load_lds<D, kBN>(sk[0], Kg, 0, N, wave, 4, lane);
-    tile_load_lds<D, kBN>(sv[0], Vg, 0, N, wave, 4, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) {       // prefetch into the idle buffer, in flight during the MFMAs
-            tile_load_lds<D, kBN>(sk[buf ^ 1], Kg, (t + 1) * kBN, N, wave, 4, lane);
-            tile_load_lds<D, kBN>(sv[buf ^ 1], Vg, (t + 1) * kBN, N, wave, 4, lane);
+    // Tile t reads buffer t % 2 while tile t+1 is copied into the other one.
+    auto run_tile = [&](auto bufc, int t) {
+        constexpr int BI = decltype(bufc)::value;
+        uint16_t *skc = BI ? sk1 : sk0, *svc = BI ? sv1 : sv0;
+        uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
+        wait_vmcnt<0>();                    // this wave's copies of tile t have landed
+        __syncthreads();                    // ... and every wave's; buffer t+1 is free
+        if (t + 1 < ntiles) {
+            tile_load_lds<D, kBN>(skn, rk, (t + 1) * kBN, wave, 4, lane);
+            tile_load_lds<D, kBN>(svn, rv, (t + 1) * kBN, wave, 4, lane);
         }
         const int kv0 = t * kBN;
-        const bool active = qw0 < N && (!causal || kv0 <= qw0 + 31);
-        if (active) {
-            // S^T = K Q^T for the 64 keys of the tile, two 32-key blocks.
-            // All of the tile's K operands are read before the MFMAs, so the
-            // LDS latency is paid once per tile rather than once per MFMA.
-            f32x16 sacc[2];
-            bf16x8 ka[2][KS];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    ka[kb][ks] = tile_row_operand<D>(sk[buf], kb * 32 + l32, 2 * ks + hf);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], qf[ks], sacc[kb]);
-            // Pipeline: 4 operand reads ahead, then one read per MFMA.
-            sched_pipeline<2 * KS, 2 * KS, 4, 1>();
-            // scale to log2 units; mask keys after the query and past the sequence end
-            const bool need_mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = sacc[kb][r] * c2;
-                    if (need_mask) {
-                        const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        if ((causal && key > qi) || key >= N) x = -INFINITY;
-                    }
-                    sacc[kb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // lazy rescale: raise the running max only when some row of the wave
-            // grew past it by more than kLazy; the first tile always sets it.
-            if (__any(mx > m_run + kLazy)) {
-                const float m_new = fmaxf(m_run, mx);      // finite: key 0 is in the first tile
-                const float alpha = m_run == -INFINITY ? 0.f : exp2_fast(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                m_run = m_new;
-            }
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = exp2_fast(sacc[kb][r] - m_run);
-                    sacc[kb][r] = p;
-                    rs += p;
-                }
-            l_run += rs;
-
-            // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
-            // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
-            // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
-            // V^T operands for all four 16-key steps are read first, then the
-            // MFMAs run back to back (DB independent accumulators).
-            bf16x8 va[4][DB];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) va[tt][db] = tr_operand<D>(sv[buf], 16 * tt, db * 32, lane);
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const bf16x8 pb = (tt & 1) ? pack_operand<8>(sacc[tt >> 1]) : pack_operand<0>(sacc[tt >> 1]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] = mfma32x32x16(va[tt][db], pb, oacc[db]);
-            }
-            sched_pipeline<8 * DB, 4 * DB, 4, 2>();
+        if (qw0 < N && (!causal || kv0 <= qw0 + 31)) {
+            const bool mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
+            fwd_tile<D>(st, skc, svc, c2, kv0, qi, N, causal, mask, lane);
         }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's prefetch has landed
-        __syncthreads();
+        sched_fence();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        run_tile(Buf<0>{}, t);
+        if (t + 1 < ntiles) run_tile(Buf<1>{}, t + 1);
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (qi < N) {
         const float inv = 1.f / l_tot;
         float *orow = O + (((size_t)b * Hq + h) * N + qi) * D;
@@ -209,11 +239,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int d0 = db * 32 + 8 * a + 4 * hf;
-                *(float4 *)(orow + d0) = make_float4(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv,
-                                                     oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
+                *(float4 *)(orow + d0) = make_float4(st.oacc[db][4 * a + 0] * inv, st.oacc[db][4 * a + 1] * inv,
+                                                     st.oacc[db][4 * a + 2] * inv, st.oacc[db][4 * a + 3] * inv);
             }
         // lse = ln(sum exp(scale q.k)) = (m + log2 l) * ln 2
-        if (hf == 0) LSE[((size_t)b * Hq + h) * N + qi] = (m_run + __log2f(l_tot)) * kLn2;
+        if (hf == 0) LSE[((size_t)b * Hq + h) * N + qi] = (st.m_run + __log2f(l_tot)) * kLn2;
     }
 }
 
