@@ -40,7 +40,8 @@ namespace {
 // dK, dV
 // ---------------------------------------------------------------------------
 constexpr int kKvBN = 64;   // keys per workgroup
-constexpr int kKvBM = 64;   // queries per step
+constexpr int kKvBM = 64;   // queries per sub-step (the two query halves of the waves)
+constexpr int kKvSub = 2;   // sub-steps per step: one LDS buffer holds 128 query rows
 
 // One (64-query step, 32x32 block) of the dK/dV kernel for one wave: S = Q K^T
 // and dP = dO V^T (lane = key column), P = 2^(c2 s - lse log2 e),
@@ -120,12 +121,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
 {
     constexpr int KS = D / 16, DB = D / 32;
 
-    // Double-buffered Q, dO, lse and D tiles in separate arrays (see Buf); at
-    // the end the four tile arrays hold the dK^T / dV^T partials of the two
-    // query halves.
-    __shared__ __attribute__((aligned(16))) uint16_t q0s[kKvBM * D], q1s[kKvBM * D];
-    __shared__ __attribute__((aligned(16))) uint16_t d0s[kKvBM * D], d1s[kKvBM * D];
-    __shared__ __attribute__((aligned(16))) float l0s[kKvBM], l1s[kKvBM], e0s[kKvBM], e1s[kKvBM];
+    // Double-buffered Q, dO, lse and D tiles of kKvSub * kKvBM query rows in
+    // separate arrays (see Buf): the copy of step s+1 has the two sub-steps of
+    // step s to land.  At the end the four tile arrays hold the dK^T / dV^T
+    // partials of the two query halves.
+    constexpr int SR = kKvSub * kKvBM;       // query rows per step
+    __shared__ __attribute__((aligned(16))) uint16_t q0s[SR * D], q1s[SR * D];
+    __shared__ __attribute__((aligned(16))) uint16_t d0s[SR * D], d1s[SR * D];
+    __shared__ __attribute__((aligned(16))) float l0s[SR], l1s[SR], e0s[SR], e1s[SR];
 
     // Work item = (key tile, batch, kv head, head subset).  The G query heads of
     // a group are split into hs subsets of Gs heads; with hs > 1 the subsets'
@@ -169,22 +172,24 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dva[db][r] = 0.f; dka[db][r] = 0.f; }
 
-    const int nqt = (N + kKvBM - 1) / kKvBM;
-    const int qt0 = causal ? k0 / kKvBM : 0;
+    const int nqt = (N + SR - 1) / SR;
+    const int qt0 = causal ? k0 / SR : 0;
     const int nq = nqt - qt0;
     const int steps = Gs * nq;               // (query head, query tile) pairs
 
-    // Step s covers query head g*G + hsub*Gs + s/nq, query tile qt0 + s%nq.  Its
-    // Q and dO tiles and its lse and D rows move global -> LDS directly; rows
-    // past N read as zero and are masked in the step's arithmetic.
+    // Step s covers query head g*G + hsub*Gs + s/nq, query rows (qt0 + s%nq)*SR
+    // .. +SR-1.  Its Q and dO tiles and its lse and D rows move global -> LDS
+    // directly (waves 0/1 copy the two halves of lse, waves 2/3 those of D);
+    // rows past N read as zero and are masked in the step's arithmetic.
     const uint32_t tile_bytes = (uint32_t)N * D * 2, row_bytes = (uint32_t)N * 4;
     auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd, float *ld, float *ed) {
         const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * N;
-        const int q0_ = (qt0 + s_ % nq) * kKvBM;
-        tile_load_lds<D, kKvBM>(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave, 4, lane);
-        tile_load_lds<D, kKvBM>(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave, 4, lane);
-        if (wave == 0) row_load_lds(ld, make_rsrc(LSE + hrow, row_bytes), q0_, lane);
-        else if (wave == 1) row_load_lds(ed, make_rsrc(Dws + hrow, row_bytes), q0_, lane);
+        const int q0_ = (qt0 + s_ % nq) * SR;
+        tile_load_lds<D, SR>(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave, 4, lane);
+        tile_load_lds<D, SR>(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave, 4, lane);
+        const int half = wave & 1;
+        if (wave < 2) row_load_lds(ld + 64 * half, make_rsrc(LSE + hrow, row_bytes), q0_ + 64 * half, lane);
+        else row_load_lds(ed + 64 * half, make_rsrc(Dws + hrow, row_bytes), q0_ + 64 * half, lane);
     };
     if (steps > 0) load_step(0, q0s, d0s, l0s, e0s);
 
@@ -198,11 +203,15 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
             if (BI) load_step(s + 1, q0s, d0s, l0s, e0s);
             else load_step(s + 1, q1s, d1s, l1s, e1s);
         }
-        const int q0 = (qt0 + s % nq) * kKvBM;
-        const int qb0 = q0 + 32 * qh;       // first query row of this wave's block
-        if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
-            const bool mask = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
-            dkdv_block<D>(qc, dc, lc, ec, kf, vf, dka, dva, c2, qh, q0, kj, N, causal, mask, lane);
+#pragma unroll
+        for (int sub = 0; sub < kKvSub; ++sub) {
+            const int q0 = (qt0 + s % nq) * SR + sub * kKvBM;
+            const int qb0 = q0 + 32 * qh;   // first query row of this wave's block
+            if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
+                const bool mask = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
+                dkdv_block<D>(qc + sub * kKvBM * D, dc + sub * kKvBM * D, lc + sub * kKvBM,
+                              ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj, N, causal, mask, lane);
+            }
         }
         sched_fence();
     };
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     // add them and park the sums, transposed to [key][dim], so that the final
     // stores (or atomics) run along the dim with consecutive lanes.
     constexpr int RED = DB * 16 * 64;        // floats per (key block, dK or dV) partial
-    static_assert(RED * sizeof(float) == sizeof(q0s), "one partial per tile array");
+    static_assert(RED * sizeof(float) <= sizeof(q0s), "one partial per tile array");
     float *redk = reinterpret_cast<float *>(kb ? q1s : q0s);
     float *redv = reinterpret_cast<float *>(kb ? d1s : d0s);
     __syncthreads();                         // the last step's reads are done
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     // transposed park: key row l32 (of this key block), dim d at
     // [l32][d ^ l32] -- the XOR spreads the 32 rows written by one instruction
     // over the banks and keeps each row a permutation of its dims
-    static_assert(32 * D * sizeof(float) == sizeof(q0s), "transposed partial fits");
+    static_assert(32 * D * sizeof(float) <= sizeof(q0s), "transposed partial fits");
     if (qh == 0) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
