@@ -182,11 +182,12 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     // directly (waves 0/1 copy the two halves of lse, waves 2/3 those of D);
     // rows past N read as zero and are masked in the step's arithmetic.
     const uint32_t tile_bytes = (uint32_t)N * D * 2, row_bytes = (uint32_t)N * 4;
+    const TileCopy<D, SR, 4> copy(wave, lane);
     auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd, float *ld, float *ed) {
         const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * N;
         const int q0_ = (qt0 + s_ % nq) * SR;
-        tile_load_lds<D, SR>(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave, 4, lane);
-        tile_load_lds<D, SR>(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave, 4, lane);
+        copy(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave);
+        copy(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave);
         const int half = wave & 1;
         if (wave < 2) row_load_lds(ld + 64 * half, make_rsrc(LSE + hrow, row_bytes), q0_ + 64 * half, lane);
         else row_load_lds(ed + 64 * half, make_rsrc(Dws + hrow, row_bytes), q0_ + 64 * half, lane);
@@ -297,16 +298,19 @@ constexpr int kQBN = 64;    // keys per tile
 
 // One 64-key tile of the dQ kernel for one wave (lane = query row): S^T = K Q^T
 // and dP^T = V dO^T per 32-key block, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
-template <int D>
+// `prefetch` issues NV direct copies (the next tile), interleaved with the
+// first block's MFMAs.
+template <int D, int NV, class Prefetch>
 __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&dof)[D / 16], f32x16 (&dqa)[D / 32], float c2,
                                         float lse2, float Di, int kv0, int qi, int N, int causal,
-                                        bool mask, int lane)
+                                        bool mask, int lane, const Prefetch &prefetch)
 {
     constexpr int KS = D / 16, DB = D / 32;
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+        if (kb == 0) prefetch();
         f32x16 sacc, pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
@@ -317,7 +321,8 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
             sacc = mfma32x32x16(ak, qf[ks], sacc);
             pacc = mfma32x32x16(av, dof[ks], pacc);
         }
-        sched_pipeline<2 * KS, 2 * KS, 4, 1>();
+        if (kb == 0) sched_pipeline<2 * KS, 2 * KS, 4, 1, NV>();
+        else sched_pipeline<2 * KS, 2 * KS, 4, 1>();
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lse2));
         if (mask) {
@@ -356,11 +361,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
 
-    const int BH = B * Hq;
-    const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
-    const int bh = blockIdx.x % BH;
-    const int b = bh / Hq, h = bh % Hq;
-    const int g = h / (Hq / Hkv);
+    // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
+    const int G = Hq / Hkv;
+    WorkItem w;
+    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
+    const int qt = w.tile;
+    const int b = w.group / Hkv, g = w.group % Hkv;
+    const int h = g * G + w.head;
     const int q0 = qt * kQBM;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -402,9 +409,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     // Tiles move global -> LDS directly; rows past N read as zero and are masked.
     const uint32_t kv_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, kv_bytes), rv = make_rsrc(Vg, kv_bytes);
-    tile_load_lds<D, kQBN>(sk0, rk, 0, wave, 4, lane);
-    tile_load_lds<D, kQBN>(sv0, rv, 0, wave, 4, lane);
+    using Copy = TileCopy<D, kQBN, 4>;
+    const Copy copy(wave, lane);
+    copy(sk0, make_rsrc(Kg, kv_bytes), 0, wave);
+    copy(sv0, make_rsrc(Vg, kv_bytes), 0, wave);
 
     auto run_tile = [&](auto bufc, int t) {
         constexpr int BI = decltype(bufc)::value;
@@ -412,15 +420,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of tile t have landed
         __syncthreads();                    // ... and every wave's; buffer t+1 is free
-        if (t + 1 < ntiles) {
-            tile_load_lds<D, kQBN>(skn, rk, (t + 1) * kQBN, wave, 4, lane);
-            tile_load_lds<D, kQBN>(svn, rv, (t + 1) * kQBN, wave, 4, lane);
-        }
+        // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
+        // past the last tile they read nothing (zero-byte resources)
+        const uint32_t nb = t + 1 < ntiles ? kv_bytes : 0u;
+        const __amdgpu_buffer_rsrc_t rkn = make_rsrc(Kg, nb), rvn = make_rsrc(Vg, nb);
+        auto prefetch = [&] {
+            copy(skn, rkn, (t + 1) * kQBN, wave);
+            copy(svn, rvn, (t + 1) * kQBN, wave);
+        };
+        // No branch on whether the wave has work in this tile (a branch would
+        // duplicate the interleaved copies and spill registers): a wave whose
+        // rows all precede the tile runs it fully masked, and rows past N have
+        // lse = +inf, so both add exact zeros.
         const int kv0 = t * kQBN;
-        if (qw0 < N && (!causal || kv0 <= qw0 + 31)) {
-            const bool mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
-            dq_tile<D>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi, N, causal, mask, lane);
-        }
+        const bool mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
+        dq_tile<D, 2 * Copy::PER_WAVE>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi, N, causal, mask,
+                                       lane, prefetch);
         sched_fence();
     };
     for (int t = 0; t < ntiles; t += 2) {
@@ -445,8 +460,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 int dkdv_head_split(int B, int Hq, int Hkv, int N)
 {
-    // Split each group's query heads over enough workgroups to give every
-    // workgroup slot (two per CU) about two causal-imbalanced work items.
+    // Split each group's query heads over workgroups until there are about two
+    // work items per CU.  The split workgroups add their partial dK/dV with
+    // f32 atomics (coalesced along the head dim); measured on MI355X: 4 x 1024
+    // x 64 grouped-query workload 46.5 -> 39.6 us with the 3 heads split, while
+    // splitting further than two items per CU (32/8 heads at N = 4096) only
+    // adds atomic traffic.
     static int cus = 0;
     if (cus == 0) {
         int dev = 0, n = 0;
@@ -456,17 +475,13 @@ int dkdv_head_split(int B, int Hq, int Hkv, int N)
         else
             cus = 256;
     }
-    // Measured on MI355X: f32 atomics into dK/dV cost far more than the load
-    // imbalance they remove (4 x 1024 x 64 grouped-query workload: 66 -> 171 us;
-    // 32/8 heads at N=4096: no gain), so the split is only taken when the key
-    // tiles leave most of the GPU idle.
     const int G = Hq / Hkv;
     const long base = (long)((N + kKvBN - 1) / kKvBN) * B * Hkv;
     int hs = 1;
     for (int c = 1; c <= G; ++c)
         if (G % c == 0) {
             hs = c;
-            if (base * c >= cus / 4) break;
+            if (base * c >= 2L * cus) break;
         }
     return hs;
 }
@@ -496,7 +511,7 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float s
                        const void *dout, const float *Dws, float *dq, hipStream_t st)
 {
     const int nqt = (N + kQBM - 1) / kQBM;
-    dim3 grid((unsigned)(nqt * B * Hq));
+    dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
     if (d == 128)
         hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,

@@ -91,31 +91,44 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// Direct global -> LDS copy (buffer_load_dwordx4 ... lds, no registers): one
-// wave instruction moves 64 x 16 bytes into 1 KiB of LDS, lane L landing at
-// byte 16 L.  The LDS address is wave-uniform (M0).  The tile of `rows` rows
-// starting at row r0 of the [*][D] bf16 tensor behind `rs` is filled in 1 KiB
-// blocks; lane L of block j owns physical chunk 64 j + L and so fetches the
-// logical chunk that the swizzle maps there.  Rows past the end of the
-// resource read as zero.  Waves 0..nwaves-1 share the blocks.  The copy
-// completes asynchronously: wait for vmcnt before the barrier that publishes it.
-// (The buffer form, unlike global_load_lds, lets the compiler keep partial
-// LDS-read waits while a copy is in flight.)
-template <int D, int ROWS>
-__device__ __forceinline__ void tile_load_lds(uint16_t *tile, __amdgpu_buffer_rsrc_t rs, int r0,
-                                              int wave, int nwaves, int lane)
-{
-    constexpr int CPR = D / 8;                    // 16-byte chunks per row
-    constexpr int BLOCKS = ROWS * CPR / 64;
-    static_assert(ROWS * CPR % 64 == 0, "tile must be whole 1 KiB blocks");
-    for (int j = wave; j < BLOCKS; j += nwaves) {
-        const int p = 64 * j + lane;
+// Direct global -> LDS copy of a tile (buffer_load_dwordx4 ... lds, no
+// registers).  One wave instruction moves 64 x 16 bytes into 1 KiB of LDS,
+// lane L landing at byte 16 L of it; the LDS address is wave-uniform (M0).
+// The tile of ROWS rows starting at row r0 of the [*][D] bf16 tensor behind
+// the resource is filled in 1 KiB blocks, NW waves sharing them: wave w takes
+// blocks w, w + NW, w + 2 NW, ...  Lane L of block j owns physical chunk
+// 64 j + L and fetches the logical chunk the swizzle maps there.  Consecutive
+// blocks of a wave lie 64 NW / (D/8) rows apart -- a multiple of the swizzle
+// period -- so every block of a wave uses the same per-lane byte offset
+// (computed once) plus a wave-uniform one.  Rows past the end of the resource
+// read as zero.  The copy completes asynchronously: wait for vmcnt before the
+// barrier that publishes it.  (The buffer form, unlike global_load_lds, lets
+// the compiler keep partial LDS-read waits while a copy is in flight.)
+template <int D, int ROWS, int NW>
+struct TileCopy {
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int BLOCKS = ROWS * CPR / 64;
+    static constexpr int PER_WAVE = BLOCKS / NW;      // copy instructions per wave
+    static_assert(ROWS * CPR % 64 == 0 && BLOCKS % NW == 0, "whole 1 KiB blocks per wave");
+    static_assert((64 * NW / CPR) % (D == 128 ? 16 : 8) == 0, "block stride keeps the swizzle");
+    int voff;                                         // byte offset of this lane in block `wave`
+
+    __device__ __forceinline__ TileCopy(int wave, int lane)
+    {
+        const int p = 64 * wave + lane;
         const int row = p / CPR;
-        const int c = (p % CPR) ^ swz<D>(row);
-        const int off = ((r0 + row) * D + 8 * c) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + 512 * j), 16, off, 0, 0, 0);
+        voff = (row * D + 8 * ((p % CPR) ^ swz<D>(row))) * 2;
     }
-}
+
+    __device__ __forceinline__ void operator()(uint16_t *tile, __amdgpu_buffer_rsrc_t rs, int r0,
+                                               int wave) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + 512 * (wave + NW * i)), 16, voff,
+                                                     r0 * D * 2 + 1024 * NW * i, 0, 0);
+    }
+};
 
 // 64 consecutive floats (rows r0 .. r0+63 of a per-row vector) -> LDS, one
 // wave instruction; entries past the end of the resource read as zero.
@@ -176,26 +189,31 @@ struct Buf {
     static constexpr int value = I;
 };
 
-// Scheduling hint for the current basic block: NR LDS reads and NM MFMAs are
-// interleaved as AHEAD reads first, then (one MFMA, RPM reads) while reads
-// remain, then the remaining MFMAs -- the reads for later MFMAs are in flight
-// while earlier MFMAs execute.  (Masks: 0x008 = MFMA, 0x100 = LDS read.)
-template <int I, int NM, int REST, int RPM>
+// Scheduling hint for the current basic block: NR LDS reads, NM MFMAs and NV
+// vector-memory instructions (the next tile's direct copies) are interleaved as
+// AHEAD reads first, then per MFMA: the MFMA, RPM reads while reads remain, and
+// VPM copies while copies remain.  The reads for later MFMAs and the copies are
+// issued while earlier MFMAs execute -- a wave that issues many copies back to
+// back stalls until the memory pipeline accepts them, so they are spread out.
+// (Masks: 0x008 = MFMA, 0x010 = vector memory, 0x100 = LDS read.)
+template <int I, int NM, int REST, int RPM, int NV, int VPM>
 struct SchedPipeStep {
     static __device__ __forceinline__ void emit()
     {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if constexpr (I * RPM < REST) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-        if constexpr (I + 1 < NM) SchedPipeStep<I + 1, NM, REST, RPM>::emit();
+        if constexpr (I * VPM < NV) __builtin_amdgcn_sched_group_barrier(0x010, VPM, 0);
+        if constexpr (I + 1 < NM) SchedPipeStep<I + 1, NM, REST, RPM, NV, VPM>::emit();
     }
 };
 
-template <int NR, int NM, int AHEAD, int RPM>
+template <int NR, int NM, int AHEAD, int RPM, int NV = 0>
 __device__ __forceinline__ void sched_pipeline()
 {
     static_assert(AHEAD <= NR && (NR - AHEAD) % RPM == 0, "reads must split evenly");
+    constexpr int VPM = NV == 0 ? 1 : (NV + NM - 1) / NM;
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-    SchedPipeStep<0, NM, NR - AHEAD, RPM>::emit();
+    SchedPipeStep<0, NM, NR - AHEAD, RPM, NV, VPM>::emit();
 }
 
 // Accumulator registers R0..R0+7 of a 32x32 MFMA packed to a bf16 operand.
@@ -216,6 +234,42 @@ __device__ __forceinline__ float wave_sum(float v)
 {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip (block i
+// runs on XCD i % 8), and every XCD has its own L2.  For work items indexed by
+// (key/value group, heaviest-first tile index, head in group) this returns the
+// item of block i such that, when the group count is a multiple of 8, each XCD
+// owns whole groups (their K and V stay in one L2) and runs its items
+// heaviest tile first, the groups interleaved (so that the heavy items of all
+// its groups start first).  Otherwise blocks take items in plain
+// heaviest-first order.  Returns false for padding blocks (the grid is a
+// multiple of 8).
+struct WorkItem {
+    int group, tile, head;
+};
+
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool xcd_work_item(int block, int groups, int tiles, int heads, WorkItem &w)
+{
+    const int total = groups * tiles * heads;
+    if (groups % kXcds == 0) {
+        const int per_xcd = total / kXcds, gpx = groups / kXcds;
+        const int x = block % kXcds, k = block / kXcds;
+        if (k >= per_xcd) return false;
+        const int level = k / (gpx * heads), rem = k % (gpx * heads);
+        w.tile = tiles - 1 - level;
+        w.group = x * gpx + rem / heads;
+        w.head = rem % heads;
+    } else {
+        if (block >= total) return false;
+        const int level = block / (groups * heads), rem = block % (groups * heads);
+        w.tile = tiles - 1 - level;
+        w.group = rem / heads;
+        w.head = rem % heads;
+    }
+    return true;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -58,14 +58,17 @@ struct FwdState {
 
 // One 64-key tile for one wave: S^T = K Q^T, the online-softmax update and
 // O^T += V^T P^T.  With `mask` (wave-uniform: diagonal and tail tiles) keys
-// after the query row and past the sequence end are hidden.
-template <int D>
+// after the query row and past the sequence end are hidden.  `prefetch`
+// issues the wave's NV direct copies of the next tile; they are interleaved
+// with the S^T MFMAs.
+template <int D, int NV, class Prefetch>
 __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, const uint16_t *svb,
                                          float c2, int kv0, int qi, int N, int causal, bool mask,
-                                         int lane)
+                                         int lane, const Prefetch &prefetch)
 {
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
     const int l32 = lane & 31, hf = lane >> 5;
+    prefetch();
 
     // S^T for the tile's two 32-key blocks; the K operands are read first and
     // interleaved with the MFMAs (4 reads ahead, then one per MFMA).
@@ -83,7 +86,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], st.qf[ks], sacc[kb]);
-    sched_pipeline<2 * KS, 2 * KS, 4, 1>();
+    sched_pipeline<2 * KS, 2 * KS, 4, 1, NV>();
 
     // Row max on the raw scores (c2 > 0 commutes with max); masked scores are -inf.
     if (mask) {
@@ -157,11 +160,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kBN * D], sk1[kBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kBN * D], sv1[kBN * D];
 
-    const int BH = B * Hq;
-    const int qt = nqt - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
-    const int bh = blockIdx.x % BH;
-    const int b = bh / Hq, h = bh % Hq;
-    const int g = h / (Hq / Hkv);
+    // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
+    const int G = Hq / Hkv;
+    WorkItem w;
+    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
+    const int qt = w.tile;
+    const int b = w.group / Hkv, g = w.group % Hkv;
+    const int h = g * G + w.head;
     const int q0 = qt * kBM;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -203,9 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     // Tiles move global -> LDS directly (no staging registers); rows past N
     // read as zero, their scores are masked.
     const uint32_t kv_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, kv_bytes), rv = make_rsrc(Vg, kv_bytes);
-    tile_load_lds<D, kBN>(sk0, rk, 0, wave, 4, lane);
-    tile_load_lds<D, kBN>(sv0, rv, 0, wave, 4, lane);
+    using Copy = TileCopy<D, kBN, 4>;
+    const Copy copy(wave, lane);
+    copy(sk0, make_rsrc(Kg, kv_bytes), 0, wave);
+    copy(sv0, make_rsrc(Vg, kv_bytes), 0, wave);
 
     // Tile t reads buffer t % 2 while tile t+1 is copied into the other one.
     auto run_tile = [&](auto bufc, int t) {
@@ -214,14 +220,20 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of tile t have landed
         __syncthreads();                    // ... and every wave's; buffer t+1 is free
-        if (t + 1 < ntiles) {
-            tile_load_lds<D, kBN>(skn, rk, (t + 1) * kBN, wave, 4, lane);
-            tile_load_lds<D, kBN>(svn, rv, (t + 1) * kBN, wave, 4, lane);
-        }
+        // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
+        // past the last tile they read nothing (zero-byte resources)
+        const uint32_t nb = t + 1 < ntiles ? kv_bytes : 0u;
+        const __amdgpu_buffer_rsrc_t rkn = make_rsrc(Kg, nb), rvn = make_rsrc(Vg, nb);
+        auto prefetch = [&] {
+            copy(skn, rkn, (t + 1) * kBN, wave);
+            copy(svn, rvn, (t + 1) * kBN, wave);
+        };
         const int kv0 = t * kBN;
         if (qw0 < N && (!causal || kv0 <= qw0 + 31)) {
             const bool mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
-            fwd_tile<D>(st, skc, svc, c2, kv0, qi, N, causal, mask, lane);
+            fwd_tile<D, 2 * Copy::PER_WAVE>(st, skc, svc, c2, kv0, qi, N, causal, mask, lane, prefetch);
+        } else {
+            prefetch();
         }
         sched_fence();
     };
@@ -256,7 +268,7 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scal
                     hipStream_t st)
 {
     const int nqt = (N + kBM - 1) / kBM;
-    dim3 grid((unsigned)(nqt * B * Hq));
+    dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
     if (d == 128)
         hipLaunchKernelGGL(fwd_mfma_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, o, lse, B, Hq, Hkv, N, scale,
