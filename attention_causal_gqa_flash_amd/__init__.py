@@ -14,7 +14,7 @@ import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
-           "attn_decode_merged", "attn_decode_workspace_bytes",
+           "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
            "ATTN_F32", "ATTN_BF16"]
 
@@ -59,9 +59,7 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.restype = i
     L.attn_decode.argtypes = [i, i, i, i, i, i, f, i, p, p, p, p, p, p]
     L.attn_decode.restype = i
-    L.attn_decode_workspace_bytes.argtypes = [i, i]
-    L.attn_decode_workspace_bytes.restype = sz
-    L.attn_decode_merged.argtypes = [i, i, i, i, i, i, f, i] + [p] * 7 + [p, sz, p]
+    L.attn_decode_merged.argtypes = [i, i, i, i, i, i, f, i] + [p] * 7 + [p]
     L.attn_decode_merged.restype = i
     L.attn_lse_merge.argtypes = [i, i, i, i, p, p, p, p, p]
     L.attn_lse_merge.restype = i
@@ -249,20 +247,11 @@ def attn_decode(q, k_cache, v_cache, n_splits: int, scale: float | None = None,
     return part_o, part_lse
 
 
-_decode_ws = {}
-
-
-def attn_decode_workspace_bytes(B: int, Hkv: int) -> int:
-    return int(lib().attn_decode_workspace_bytes(B, Hkv))
-
-
 def attn_decode_merged(q, k_cache, v_cache, n_splits: int, scale: float | None = None,
-                       part_o=None, part_lse=None, o=None, lse=None, workspace=None, stream=None):
-    """Split-KV decode and the LSE merge in one call (one launch where supported).
+                       part_o=None, part_lse=None, o=None, lse=None, stream=None):
+    """Split-KV decode and the LSE merge in one call.
 
-    Returns (o [B,Hq,d], lse [B,Hq], part_o, part_lse).  The counter workspace
-    must start zero-filled; the library leaves it zero-filled, so the default
-    one (allocated zeroed once per device and size) is reused across calls.
+    Returns (o [B,Hq,d], lse [B,Hq], part_o, part_lse).
     """
     torch = _torch()
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -277,19 +266,10 @@ def attn_decode_merged(q, k_cache, v_cache, n_splits: int, scale: float | None =
     part_lse = torch.empty((B, Hq, n_splits), **f32) if part_lse is None else part_lse
     o = torch.empty((B, Hq, d), **f32) if o is None else o
     lse = torch.empty((B, Hq), **f32) if lse is None else lse
-    nbytes = attn_decode_workspace_bytes(B, Hkv)
-    if workspace is None:
-        key = (q.device.index, nbytes)
-        workspace = _decode_ws.get(key)
-        if workspace is None:
-            workspace = torch.zeros(nbytes, device=q.device, dtype=torch.uint8)
-            _decode_ws[key] = workspace
     rc = lib().attn_decode_merged(_dtype_code(q), B, Hq, Hkv, L, d, scale, int(n_splits),
                                   _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(_dev(part_o, "part_o")), _ptr(_dev(part_lse, "part_lse")),
-                                  _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")),
-                                  _ptr(_dev(workspace, "workspace")),
-                                  workspace.numel() * workspace.element_size(), _stream(stream))
+                                  _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
     _check("attn_decode_merged", rc)
     return o, lse, part_o, part_lse
 

@@ -204,22 +204,15 @@ attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, flo
     hipStream_t st = (hipStream_t)stream;
     if (attn::decode_mfma_supported(dt, d, Hq / Hkv) && scale != 0.f)
         return hip_status(attn::decode_split_mfma(B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
-                                                  v_cache, part_o, part_lse, nullptr, nullptr,
-                                                  nullptr, st));
+                                                  v_cache, part_o, part_lse, st));
     return hip_status(attn::decode_split(dt, B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
                                          v_cache, part_o, part_lse, st));
-}
-
-size_t attn_decode_workspace_bytes(int B, int Hkv)
-{
-    if (B <= 0 || Hkv <= 0) return 0;
-    return ((size_t)B * (size_t)Hkv * sizeof(unsigned int) + 255) & ~(size_t)255;
 }
 
 attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,
                                int n_splits, const void *q, const void *k_cache,
                                const void *v_cache, float *part_o, float *part_lse, float *o,
-                               float *lse, void *workspace, size_t ws_bytes, void *stream)
+                               float *lse, void *stream)
 {
     attn_status s = check_common(dt, B, Hq, Hkv, L, d, scale);
     if (s != ATTN_OK) return s;
@@ -229,16 +222,15 @@ attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(part_o) ||
         !aligned16(part_lse) || !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_INVALID_ARG;
-    if (!aligned16(workspace) || ws_bytes < attn_decode_workspace_bytes(B, Hkv))
-        return ATTN_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
     if (attn::decode_mfma_supported(dt, d, Hq / Hkv) && scale != 0.f)
-        return hip_status(attn::decode_split_mfma(B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
-                                                  v_cache, part_o, part_lse, o, lse,
-                                                  (unsigned int *)workspace, st));
-    if (attn::decode_split(dt, B, Hq, Hkv, L, d, scale, n_splits, q, k_cache, v_cache, part_o,
-                           part_lse, st) != hipSuccess)
-        return ATTN_ERR_HIP;
+        e = attn::decode_split_mfma(B, Hq, Hkv, L, d, scale, n_splits, q, k_cache, v_cache, part_o,
+                                    part_lse, st);
+    else
+        e = attn::decode_split(dt, B, Hq, Hkv, L, d, scale, n_splits, q, k_cache, v_cache, part_o,
+                               part_lse, st);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
     return hip_status(attn::lse_merge(B, Hq, n_splits, d, part_o, part_lse, o, lse, st));
 }
 
@@ -266,6 +258,6 @@ const char *attn_status_str(attn_status s)
     return "unknown status";
 }
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 }  // extern "C"

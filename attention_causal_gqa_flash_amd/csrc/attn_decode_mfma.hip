@@ -39,12 +39,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool kFused>
+template <int D>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, float *__restrict__ part_o, float *__restrict__ part_lse,
-    float *__restrict__ o, float *__restrict__ lse, unsigned int *__restrict__ counters, int Hq,
-    int Hkv, int L, float scale, int n_splits)
+    int Hq, int Hkv, int L, float scale, int n_splits)
 {
     constexpr int KS = D / 32;            // k-steps over the head dim (32 per MFMA)
     constexpr int DB = D / 16;            // 16-column blocks of the output
@@ -215,66 +214,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(
         part_o[ob * D + c] = at / lt;
         if (c == 0) part_lse[ob] = M * kLn2 + logf(lt);
     }
-    if constexpr (kFused) {
-        // The last workgroup of this (batch, kv head) to finish merges the
-        // n_splits partials of its G query heads into o and lse, then resets
-        // the counter so the workspace is zero again for the next call.
-        // The barrier completes every wave's partial stores; one wave then
-        // releases them device-wide (one L2 writeback per workgroup, not one per
-        // wave) and bumps the counter.
-        __shared__ unsigned int s_last;
-        __syncthreads();
-        if (wave == 0) {
-            __threadfence();
-            if (lane == 0) {
-                const unsigned int done = atomicAdd(&counters[(size_t)b * Hkv + g], 1u);
-                s_last = done == (unsigned int)(n_splits - 1);
-            }
-        }
-        __syncthreads();
-        if (!s_last) return;
-        if (wave == 0) __threadfence();        // acquire the other workgroups' partials
-        __syncthreads();
-        // per head: M = max_s lse_s and W = sum_s exp(lse_s - M), one wave per head
-        float *sMW = reinterpret_cast<float *>(smem);     // [16][2]
-        for (int hh = wave; hh < G; hh += kWaves) {
-            const float *pl = part_lse + ((size_t)b * Hq + g * G + hh) * n_splits;
-            float M = -INFINITY;
-            for (int x = lane; x < n_splits; x += 64) M = fmaxf(M, pl[x]);
-            M = wave_max(M);
-            float W = 0.f;
-            if (M != -INFINITY)
-                for (int x = lane; x < n_splits; x += 64) {
-                    const float lx = pl[x];
-                    if (lx != -INFINITY) W += expf(lx - M);
-                }
-            W = wave_sum(W);
-            if (lane == 0) { sMW[2 * hh] = M; sMW[2 * hh + 1] = W; }
-        }
-        __syncthreads();
-        for (int t = tid; t < G * D; t += 512) {
-            const int hh = t / D, c = t % D;
-            const size_t row = (size_t)b * Hq + g * G + hh;
-            const float M = sMW[2 * hh], W = sMW[2 * hh + 1];
-            if (M == -INFINITY) {                 // every chunk empty
-                o[row * D + c] = 0.f;
-                if (c == 0) lse[row] = -INFINITY;
-                continue;
-            }
-            const float *pl = part_lse + row * n_splits;
-            const float *po = part_o + row * (size_t)n_splits * D + c;
-            float acc = 0.f;
-#pragma unroll 8
-            for (int x = 0; x < n_splits; ++x) {
-                const float lx = pl[x];
-                const float w = lx == -INFINITY ? 0.f : expf(lx - M);
-                acc = fmaf(w, po[(size_t)x * D], acc);
-            }
-            o[row * D + c] = acc / W;
-            if (c == 0) lse[row] = M + logf(W);
-        }
-        if (tid == 0) counters[(size_t)b * Hkv + g] = 0u;
-    }
 }
 
 }  // namespace
@@ -283,23 +222,19 @@ bool decode_mfma_supported(int dt, int d, int G) { return dt == kBF16 && (d == 6
 
 hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
                              const void *q, const void *kc, const void *vc, float *part_o,
-                             float *part_lse, float *o, float *lse, unsigned int *counters,
-                             hipStream_t st)
+                             float *part_lse, hipStream_t st)
 {
     dim3 grid(n_splits, Hkv, B);
-    const bool fused = o != nullptr;
-#define ATTN_DEC(DV, F)                                                                           \
-    hipLaunchKernelGGL((decode_mfma_kernel<DV, F>), grid, dim3(512), 0, st, (const uint16_t *)q,  \
-                       (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, o, lse,      \
-                       counters, Hq, Hkv, L, scale, n_splits)
-    if (d == 128) {
-        if (fused) ATTN_DEC(128, true); else ATTN_DEC(128, false);
-    } else if (d == 64) {
-        if (fused) ATTN_DEC(64, true); else ATTN_DEC(64, false);
-    } else {
+    if (d == 128)
+        hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, dim3(512), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, Hq, Hkv, L,
+                           scale, n_splits);
+    else if (d == 64)
+        hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, dim3(512), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, Hq, Hkv, L,
+                           scale, n_splits);
+    else
         return hipErrorInvalidValue;
-    }
-#undef ATTN_DEC
     return hipGetLastError();
 }
 

@@ -52,13 +52,9 @@ hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scal
                         const void *q, const void *kc, const void *vc, float *part_o,
                         float *part_lse, hipStream_t st);
 bool decode_mfma_supported(int dt, int d, int G);
-// With o != nullptr the same launch also merges the partials into o and lse
-// (the last workgroup of each (batch, kv head) does it, counted in `counters`,
-// B*Hkv zero-initialised words that the launch leaves zero again).
 hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
                              const void *q, const void *kc, const void *vc, float *part_o,
-                             float *part_lse, float *o, float *lse, unsigned int *counters,
-                             hipStream_t st);
+                             float *part_lse, hipStream_t st);
 hipError_t lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
                      const float *part_lse, float *o, float *lse, hipStream_t st);
 

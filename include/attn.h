@@ -171,24 +171,18 @@ attn_status attn_lse_merge(int B, int Hq, int n_splits, int d,
                            float *o, float *lse, void *stream);
 
 /*
- * attn_decode_merged -- attn_decode followed by attn_lse_merge in ONE launch
- *   where the matrix-core decode applies (bf16, d in {64,128}, Hq/Hkv <= 16,
- *   scale != 0): the last workgroup to finish the chunks of a (batch, kv head)
- *   merges that group's partials.  Other configurations run the two steps as
- *   two launches.  Results are those of attn_decode + attn_lse_merge: part_o and
- *   part_lse are written as by attn_decode, o [B][Hq][d] and lse [B][Hq] as by
- *   attn_lse_merge.
- *   workspace: device memory of at least attn_decode_workspace_bytes(B, Hkv)
- *   bytes holding completion counters.  It must be zero-filled before its first
- *   use; every call leaves it zero-filled again when its work completes.  Calls
- *   that share a workspace must not run concurrently (stream order is enough).
+ * attn_decode_merged -- attn_decode followed by attn_lse_merge, enqueued by
+ *   one call (two launches on `stream`).  part_o and part_lse are written as by
+ *   attn_decode, o [B][Hq][d] and lse [B][Hq] as by attn_lse_merge; argument
+ *   checks are those of both calls and an invalid call launches nothing.
+ *   (A single-launch form, in which the last workgroup of each (batch, kv
+ *   head) merges after a device-scope release, measured slower on MI355X:
+ *   the release writes back and invalidates L2.)
  */
-size_t attn_decode_workspace_bytes(int B, int Hkv);
 attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,
                                int n_splits, const void *q, const void *k_cache,
                                const void *v_cache, float *part_o, float *part_lse, float *o,
-                               float *lse, void *workspace, size_t workspace_bytes,
-                               void *stream);
+                               float *lse, void *stream);
 
 /* Human-readable name of a status code (a static string). */
 const char *attn_status_str(attn_status s);

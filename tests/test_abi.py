@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert attn.attn_abi_version() == 1
+    assert attn.attn_abi_version() == 2
     assert attn.attn_status_str(OK) == "ok"
     assert "invalid" in attn.attn_status_str(INVALID)
     assert "unsupported" in attn.attn_status_str(UNSUPPORTED)
@@ -164,10 +164,9 @@ def test_no_unexpected_exports(L):
 
 
 def test_decode_merged_refusals(L):
-    assert L.attn_decode_workspace_bytes(1, 8) == 256
-    assert L.attn_decode_workspace_bytes(0, 8) == 0
     args = [1, 1, 32, 8, 4096, 128, 0.088, 16]
-    assert L.attn_decode_merged(1, 1, 32, 8, 4096, 128, 0.088, 0, *([P] * 7), P, 256, NUL) == INVALID
-    assert L.attn_decode_merged(*args, *([P] * 7), P, 255, NUL) == WORKSPACE
-    assert L.attn_decode_merged(*args, *([P] * 7), NUL, 256, NUL) == WORKSPACE
-    assert L.attn_decode_merged(*args, *([P] * 6), MIS, P, 256, NUL) == INVALID
+    assert L.attn_decode_merged(1, 1, 32, 8, 4096, 128, 0.088, 0, *([P] * 7), NUL) == INVALID
+    assert L.attn_decode_merged(1, 1, 32, 8, 4096, 96, 0.088, 16, *([P] * 7), NUL) == UNSUPPORTED
+    assert L.attn_decode_merged(1, 1, 34, 8, 4096, 128, 0.088, 16, *([P] * 7), NUL) == INVALID
+    assert L.attn_decode_merged(*args, *([P] * 6), MIS, NUL) == INVALID
+    assert L.attn_decode_merged(*args, NUL, *([P] * 6), NUL) == INVALID

@@ -235,16 +235,16 @@ MERGED = [
     (2, 8, 2, 1000, 64, 7, "bf16", 64),
     (1, 4, 4, 5, 128, 8, "bf16", 3),         # empty chunks
     (1, 16, 1, 300, 128, 3, "bf16", 299),
-    (1, 4, 2, 513, 64, 16, "f32", 100),      # two-launch fallback
-    (1, 6, 3, 77, 32, 3, "bf16", 40),        # two-launch fallback (d = 32)
+    (1, 4, 2, 513, 64, 16, "f32", 100),      # generic decode kernel
+    (1, 6, 3, 77, 32, 3, "bf16", 40),        # generic decode kernel (d = 32)
 ]
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,d,S,dtype,L2", MERGED,
                          ids=[f"B{c[0]}_H{c[1]}x{c[2]}_L{c[3]}_d{c[4]}_S{c[5]}_{c[6]}" for c in MERGED])
 def test_decode_merged_two_calls(B, Hq, Hkv, L, d, S, dtype, L2):
-    """The fused decode+merge equals the oracle on two calls in a row that share
-    the counter workspace (the second on a shorter cache)."""
+    """Decode + merge in one call equals the oracle on two calls in a row reusing
+    the outputs (the second on a shorter cache)."""
     for Lc in (L, L2):
         print(f"\n[case] decode_merged B={B} Hq={Hq} Hkv={Hkv} L={Lc} d={d} S={S} {dtype}", flush=True)
         cfg = W.DecodeConfig("adhoc", dtype, B, Hq, Hkv, Lc, d, S, seed=Lc * 3 + d)
@@ -258,8 +258,6 @@ def test_decode_merged_two_calls(B, Hq, Hkv, L, d, S, dtype, L2):
         assert float(np.abs(o.cpu().numpy() - ro).max()) <= tol_o
         assert float(np.abs(lse.cpu().numpy() - rl).max()) <= tol_l
         assert float(np.abs(po.cpu().numpy() - rpo).max()) <= tol_o
-    ws = attn._decode_ws[(0, attn.attn_decode_workspace_bytes(B, Hkv))]
-    assert int(ws.count_nonzero().item()) == 0          # counters left at zero
 
 
 def test_graph_replay_matches_eager():
