@@ -99,11 +99,14 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
                 sacc[kb][r] = hide ? -INFINITY : sacc[kb][r];
             }
     }
-    float mx = -INFINITY;
+    // Row max and row sum as four independent chains each (short dependency
+    // chains matter: a wave's tile is a latency chain at small head dims).
+    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
     // Lazy rescale: raise the running max only when some row of the wave grew
     // past it by more than kLazy.  A row's first tile always sets it, since
@@ -119,7 +122,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
         st.m_run = m_new;
     }
     // p = 2^(c2 s - m): one FMA and one exp per score (exp2(-inf) = 0)
-    float rs = 0.f;
+    float rq[4] = {0.f, 0.f, 0.f, 0.f};
     const float nm = -st.m_run;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -127,9 +130,9 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
         for (int r = 0; r < 16; ++r) {
             const float p = exp2_fast(fmaf(sacc[kb][r], c2, nm));
             sacc[kb][r] = p;
-            rs += p;
+            rq[r & 3] += p;
         }
-    st.l_run += rs;
+    st.l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
 
     // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
     // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
@@ -148,17 +151,26 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     sched_pipeline<8 * DB, 4 * DB, 4, 2>();
 }
 
-template <int D>
+// KSPLIT = 1: one workgroup = 4 waves = 128 query rows (32 per wave), every
+// wave streaming all the key tiles of its query tile.
+// KSPLIT = 2 (small grids, d = 64): one workgroup = 64 query rows; waves
+// (row half, key half) -- the two key halves stream disjoint halves of the
+// key tiles side by side and their softmax states combine through LDS at the
+// end with the associative merge, which halves the longest chain of tiles.
+template <int D, int KSPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
     int Hkv, int N, float scale, int causal, int nqt)
 {
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
-    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered in
-    // four separate arrays (see Buf)
-    __shared__ __attribute__((aligned(16))) uint16_t sk0[kBN * D], sk1[kBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sv0[kBN * D], sv1[kBN * D];
+    constexpr int RW = 4 / KSPLIT;           // row waves
+    constexpr int BMW = 32 * RW;             // query rows per workgroup
+    constexpr int TE = kBN * D;              // elements of one tile
+    // K and V tiles (one per key half), row-major with swizzled 16-byte
+    // chunks, double-buffered in four separate arrays (see Buf)
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[KSPLIT * TE], sk1[KSPLIT * TE];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[KSPLIT * TE], sv1[KSPLIT * TE];
 
     // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
     const int G = Hq / Hkv;
@@ -167,12 +179,13 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const int qt = w.tile;
     const int b = w.group / Hkv, g = w.group % Hkv;
     const int h = g * G + w.head;
-    const int q0 = qt * kBM;
+    const int q0 = qt * BMW;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int rw = wave % RW, kh = wave / RW;                     // row wave, key half
     const int l32 = lane & 31, hf = lane >> 5;
-    const int qw0 = q0 + wave * 32;         // first query row of this wave
+    const int qw0 = q0 + rw * 32;           // first query row of this wave
     const int qi = qw0 + l32;               // this lane's query row
 
     const uint16_t *Qh = Q + ((size_t)b * Hq + h) * (size_t)N * D;
@@ -202,44 +215,87 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
 
-    const int kv_end = causal ? min(N, q0 + kBM) : N;
+    const int kv_end = causal ? min(N, q0 + BMW) : N;
     const int ntiles = (kv_end + kBN - 1) / kBN;
+    // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles); both
+    // halves' first tiles hold a key every row of the query tile sees
+    const int ntA = KSPLIT == 2 ? ntiles / 2 : 0;
+    const int nsteps = ntiles - ntA;
+    auto tile_of = [&](int half, int s_) { return half == 0 && KSPLIT == 2 ? s_ : ntA + s_; };
+    auto valid = [&](int half, int s_) {
+        return (half == 0 && KSPLIT == 2) ? s_ < ntA : s_ < nsteps;
+    };
 
     // Tiles move global -> LDS directly (no staging registers); rows past N
-    // read as zero, their scores are masked.
+    // read as zero, their scores are masked; copies of tiles that do not
+    // exist read nothing (zero-byte resources).
     const uint32_t kv_bytes = (uint32_t)N * D * 2;
     using Copy = TileCopy<D, kBN, 4>;
     const Copy copy(wave, lane);
-    copy(sk0, make_rsrc(Kg, kv_bytes), 0, wave);
-    copy(sv0, make_rsrc(Vg, kv_bytes), 0, wave);
+    auto copy_step = [&](uint16_t *skd, uint16_t *svd, int s_) {
+#pragma unroll
+        for (int half = 0; half < KSPLIT; ++half) {
+            const uint32_t nb = valid(half, s_) ? kv_bytes : 0u;
+            const int t_ = tile_of(half, s_);
+            copy(skd + half * TE, make_rsrc(Kg, nb), t_ * kBN, wave);
+            copy(svd + half * TE, make_rsrc(Vg, nb), t_ * kBN, wave);
+        }
+    };
+    copy_step(sk0, sv0, 0);
 
-    // Tile t reads buffer t % 2 while tile t+1 is copied into the other one.
-    auto run_tile = [&](auto bufc, int t) {
+    // Step s reads buffer s % 2 while step s+1 is copied into the other one.
+    auto run_step = [&](auto bufc, int s_) {
         constexpr int BI = decltype(bufc)::value;
         uint16_t *skc = BI ? sk1 : sk0, *svc = BI ? sv1 : sv0;
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
-        wait_vmcnt<0>();                    // this wave's copies of tile t have landed
-        __syncthreads();                    // ... and every wave's; buffer t+1 is free
-        // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
-        // past the last tile they read nothing (zero-byte resources)
-        const uint32_t nb = t + 1 < ntiles ? kv_bytes : 0u;
-        const __amdgpu_buffer_rsrc_t rkn = make_rsrc(Kg, nb), rvn = make_rsrc(Vg, nb);
-        auto prefetch = [&] {
-            copy(skn, rkn, (t + 1) * kBN, wave);
-            copy(svn, rvn, (t + 1) * kBN, wave);
-        };
-        const int kv0 = t * kBN;
-        if (qw0 < N && (!causal || kv0 <= qw0 + 31)) {
+        wait_vmcnt<0>();                    // this wave's copies of step s have landed
+        __syncthreads();                    // ... and every wave's; buffer s+1 is free
+        // copies of step s+1 (branch-free, so they can interleave with MFMAs)
+        auto prefetch = [&] { copy_step(skn, svn, s_ + 1); };
+        const int kv0 = tile_of(kh, s_) * kBN;
+        if (valid(kh, s_) && qw0 < N && (!causal || kv0 <= qw0 + 31)) {
             const bool mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
-            fwd_tile<D, 2 * Copy::PER_WAVE>(st, skc, svc, c2, kv0, qi, N, causal, mask, lane, prefetch);
+            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi, N,
+                                                     causal, mask, lane, prefetch);
         } else {
             prefetch();
         }
         sched_fence();
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        run_tile(Buf<0>{}, t);
-        if (t + 1 < ntiles) run_tile(Buf<1>{}, t + 1);
+    for (int s_ = 0; s_ < nsteps; s_ += 2) {
+        run_step(Buf<0>{}, s_);
+        if (s_ + 1 < nsteps) run_step(Buf<1>{}, s_ + 1);
+    }
+
+    if constexpr (KSPLIT == 2) {
+        // Key half 1 parks (O^T, m, l) per lane in LDS; key half 0 merges:
+        // m = max(mA, mB), O = OA 2^(mA-m) + OB 2^(mB-m), l likewise.  Half 1
+        // always saw keys, so m is finite (an empty half 0 has mA = -inf).
+        float *po = reinterpret_cast<float *>(sk0);   // [rw][DB*16][64]
+        float *pm = reinterpret_cast<float *>(sv0);   // [rw][2][64]
+        static_assert(RW * DB * 16 * 64 * sizeof(float) <= sizeof(sk0), "partial O fits");
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kh == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) po[(rw * DB * 16 + db * 16 + r) * 64 + lane] = st.oacc[db][r];
+            pm[(rw * 2 + 0) * 64 + lane] = st.m_run;
+            pm[(rw * 2 + 1) * 64 + lane] = st.l_run;
+        }
+        __syncthreads();
+        if (kh == 1) return;
+        const float mB = pm[(rw * 2 + 0) * 64 + lane], lB = pm[(rw * 2 + 1) * 64 + lane];
+        const float m = fmaxf(st.m_run, mB);
+        const float ea = exp2_fast(st.m_run - m), eb = exp2_fast(mB - m);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                st.oacc[db][r] = st.oacc[db][r] * ea + po[(rw * DB * 16 + db * 16 + r) * 64 + lane] * eb;
+        st.l_run = st.l_run * ea + lB * eb;
+        st.m_run = m;
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
@@ -267,18 +323,37 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scal
                     const void *q, const void *k, const void *v, float *o, float *lse,
                     hipStream_t st)
 {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
     const int nqt = (N + kBM - 1) / kBM;
-    dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
-    if (d == 128)
-        hipLaunchKernelGGL(fwd_mfma_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, o, lse, B, Hq, Hkv, N, scale,
-                           causal, nqt);
-    else if (d == 64)
-        hipLaunchKernelGGL(fwd_mfma_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, o, lse, B, Hq, Hkv, N, scale,
-                           causal, nqt);
-    else
+    // Key split when the 128-row workgroups would not give every CU two
+    // (d = 64; measured on MI355X, B = 4, N = 1024, 12/4 heads: 22.6 us
+    // unsplit, 20.5 us split).
+    const bool split = d == 64 && (long)nqt * B * Hq < 2L * cus;
+    auto grid_of = [&](int n_tiles) {
+        return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
+    };
+    const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
+    if (d == 128) {
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+                           B, Hq, Hkv, N, scale, causal, nqt);
+    } else if (d == 64 && !split) {
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+                           B, Hq, Hkv, N, scale, causal, nqt);
+    } else if (d == 64) {
+        const int nqt64 = (N + 63) / 64;
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
+                           B, Hq, Hkv, N, scale, causal, nqt64);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

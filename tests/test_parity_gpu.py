@@ -144,6 +144,7 @@ EXTRA = [
     (1, 2, 1, 130, 64, "f32", True, None),
     (1, 2, 2, 50, 128, "f32", False, None),
     (2, 4, 2, 33, 32, "f32", True, None),
+    (4, 16, 4, 1024, 64, "bf16", True, None),   # d = 64 grid large enough for 128-row tiles
 ]
 
 
