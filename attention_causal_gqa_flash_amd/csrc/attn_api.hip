@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 using attn::kBF16;
@@ -97,6 +99,42 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causa
                                 delta, dq, st);
 }
 
+// attn_bwd runs the dK/dV and dQ kernels concurrently: dQ goes to an
+// auxiliary stream of the device, forked from and joined back into the
+// caller's stream with events (so a graph capture of the caller's stream
+// captures both branches).  Measured on MI355X (4 x 1024 x 12/4 heads, d = 64,
+// HIP-graph replay): 65.0 us one after the other, 59.4 us side by side; the
+// small grids leave CUs idle in each kernel's tail.  One auxiliary stream and
+// two events per device are created on first use (default priority); the
+// fork/join is serialised by a mutex so that concurrent callers do not
+// interleave their event records.
+struct BwdAux {
+    hipStream_t st = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;
+BwdAux g_aux[kMaxDevices];
+
+// The device's auxiliary stream and events (created on first use), or null
+// when they cannot be used: creation failed, or `st` is capturing and they do
+// not exist yet (nothing may be created during a capture).  Call with
+// g_aux_mu held.
+BwdAux *bwd_aux(hipStream_t st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    BwdAux &a = g_aux[dev];
+    if (a.st && a.fork && a.join) return &a;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    if (!a.st && hipStreamCreateWithFlags(&a.st, hipStreamNonBlocking) != hipSuccess) a.st = nullptr;
+    if (!a.fork && hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess) a.fork = nullptr;
+    if (!a.join && hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess) a.join = nullptr;
+    return (a.st && a.fork && a.join) ? &a : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -141,11 +179,25 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st) !=
         hipSuccess)
         return ATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    BwdAux *aux = bwd_aux(st);
+    hipStream_t st_dq = st;
+    if (aux) {
+        if (hipEventRecord(aux->fork, st) != hipSuccess ||
+            hipStreamWaitEvent(aux->st, aux->fork, 0) != hipSuccess)
+            return ATTN_ERR_HIP;
+        st_dq = aux->st;
+    }
+    if (launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st_dq) !=
+        hipSuccess)
+        return ATTN_ERR_HIP;
     if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
                         hs, st) != hipSuccess)
         return ATTN_ERR_HIP;
-    return hip_status(
-        launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st));
+    if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
+                hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,

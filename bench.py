@@ -3,12 +3,11 @@
 
 One step = one pass of the whole hot path on seeded synthetic inputs already
 resident in device memory:
-  * the training op: attn_fwd, then the backward's three stages (preprocess,
-    dK/dV, dQ) on the training workload (default: bf16, B=4, 12 query / 4
-    key-value heads, N=1024, d=64);
+  * the training op: attn_fwd, then attn_bwd (preprocess, then the dK/dV and
+    dQ kernels side by side) on the training workload (default: bf16, B=4,
+    12 query / 4 key-value heads, N=1024, d=64);
   * the decode op: split-KV decode + LSE merge (attn_decode_merged: the decode
-    kernel then the merge kernel)
-    on the decode workload (bf16, 32/8 heads, d=128, a 4096-key cache in 16
+    kernel then the merge kernel) on the decode workload (bf16, 32/8 heads, d=128, a 4096-key cache in 16
     splits), rotating over enough distinct caches (default 24 x 16 MiB) that
     every step reads its keys and values from HBM rather than from cache.
 
@@ -256,12 +255,21 @@ def main():
     def dqk():
         attn.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq)
 
+    bwd_ws = torch.empty(max(256, attn.attn_bwd_workspace_bytes(1 if cfg.dtype == "bf16" else 0,
+                                                                B, Hq, Hkv, N, d)),
+                         device=dev, dtype=torch.uint8)
+
+    def bwd():
+        # the whole backward as a caller runs it (dK/dV and dQ side by side)
+        attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], True, cfg.scale, dq=dq, dk=dk,
+                      dv=dv, workspace=bwd_ws)
+
     def decode(i):
         kc, vc = caches[i % ncache]
         return lambda: attn.attn_decode_merged(qd, kc, vc, S, dcfg.scale, part_o=part_o,
                                                part_lse=part_lse, o=dec_o, lse=dec_lse)
 
-    train_op = [fwd, pre, dkdv, dqk]
+    train_op = [fwd, bwd]
     for s in range(args.warmup):
         for fn in train_op:
             fn()

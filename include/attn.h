@@ -19,7 +19,9 @@
  * Conventions common to every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers, owned by the caller.  The library
- *    allocates nothing, frees nothing and keeps no state between calls.
+ *    allocates no device memory and keeps no data between calls.  Its only
+ *    state is, per device, one auxiliary stream and two events that attn_bwd
+ *    creates on first use (see attn_bwd).
  *  - Layouts are contiguous row-major with the head dimension fastest:
  *        q, dout, o, dq      [B][Hq][N][d]
  *        k, v, dk, dv        [B][Hkv][N][d]
@@ -104,6 +106,13 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
  *   then differ from run to run in the last bits.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry do not matter.
+ *   Streams: the dq kernel runs on an auxiliary stream of the current device,
+ *   forked from and joined back into `stream` with events, concurrently with
+ *   the dk/dv kernel; to the caller the call behaves as if all its work were
+ *   on `stream` (a graph capture of `stream` captures both branches).  The
+ *   auxiliary stream and events are created on the device's first attn_bwd
+ *   call; if that first call is made while `stream` is being captured, or
+ *   they cannot be created, the kernels run one after the other on `stream`.
  */
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      const void *q, const void *k, const void *v,

@@ -261,8 +261,11 @@ def test_decode_merged_two_calls(B, Hq, Hkv, L, d, S, dtype, L2):
         assert float(np.abs(po.cpu().numpy() - rpo).max()) <= tol_o
 
 
-def test_graph_replay_matches_eager():
-    """The whole path captured in a HIP graph: every replay equals the eager run."""
+@pytest.mark.parametrize("whole_bwd", [False, True], ids=["stages", "attn_bwd"])
+def test_graph_replay_matches_eager(whole_bwd):
+    """The whole path captured in a HIP graph: every replay equals the eager run.
+    With whole_bwd the backward is attn_bwd, whose dQ kernel runs on the
+    library's auxiliary stream (a fork/join inside the capture)."""
     cfg = W.TrainConfig("graph", "bf16", 1, 8, 2, 320, 128, seed=11)
     x = W.train_inputs(cfg)
     g = {n: _to_dev(a, "bf16") for n, a in x.items()}
@@ -277,12 +280,19 @@ def test_graph_replay_matches_eager():
                   torch.empty((B, Hkv, N, d), **f32))
     po, pl = torch.empty((1, 8, 5, 128), **f32), torch.empty((1, 8, 5), **f32)
     do_, dl = torch.empty((1, 8, 128), **f32), torch.empty((1, 8), **f32)
+    ws = torch.empty(max(256, attn.attn_bwd_workspace_bytes(1, B, Hq, Hkv, N, d)), device="cuda",
+                     dtype=torch.uint8)
 
     def step():
         attn.attn_fwd(g["q"], g["k"], g["v"], True, cfg.scale, o=o, lse=lse)
         attn.attn_bwd_preprocess(o, g["dout"], delta=delta)
-        attn.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dk=dk, dv=dv)
-        attn.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq)
+        if whole_bwd:
+            attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], True, cfg.scale, dq=dq, dk=dk,
+                          dv=dv, workspace=ws)
+        else:
+            attn.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale,
+                               dk=dk, dv=dv)
+            attn.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq)
         attn.attn_decode_merged(gd["q"], gd["k_cache"], gd["v_cache"], 5, dc.scale,
                                 part_o=po, part_lse=pl, o=do_, lse=dl)
 
