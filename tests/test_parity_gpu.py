@@ -145,6 +145,8 @@ EXTRA = [
     (1, 2, 2, 50, 128, "f32", False, None),
     (2, 4, 2, 33, 32, "f32", True, None),
     (4, 16, 4, 1024, 64, "bf16", True, None),   # d = 64 grid large enough for 128-row tiles
+    (2, 128, 32, 300, 128, "bf16", True, None),  # d = 128 grid large enough for 256-row tiles
+    (4, 128, 16, 256, 128, "bf16", False, None),
 ]
 
 
