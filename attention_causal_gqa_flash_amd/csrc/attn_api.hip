@@ -108,6 +108,11 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causa
 // two events per device are created on first use (default priority); the
 // fork/join is serialised by a mutex so that concurrent callers do not
 // interleave their event records.
+// The matrix-core gradients run as one launch (dK/dV and dQ workgroups in
+// one grid, ordered heaviest first over both kinds) where that beats the
+// two-stream form.
+bool fuse_bwd(int d) { return d == 64; }
+
 struct BwdAux {
     hipStream_t st = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
@@ -179,6 +184,9 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st) !=
         hipSuccess)
         return ATTN_ERR_HIP;
+    if (use_mfma(dt, N, d, scale) && fuse_bwd(d))
+        return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse,
+                                               dout, delta, dq, dk, dv, hs, st));
     std::lock_guard<std::mutex> lock(g_aux_mu);
     BwdAux *aux = bwd_aux(st);
     hipStream_t st_dq = st;

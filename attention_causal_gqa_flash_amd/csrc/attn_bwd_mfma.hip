@@ -33,7 +33,23 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <vector>
+
 namespace attn {
+
+// Block order of the one-launch backward: plan.n groups of blocks; group i
+// starts at block first[i] and holds consecutive levels of one kind (0: dK/dV
+// key tiles, lev0 first and ascending; 1: dQ query tiles, lev0 first and
+// descending), each level padded to a multiple of kXcds blocks.
+struct BwdPlan {
+    static constexpr int kMax = 48;
+    int n;
+    int first[kMax + 1];
+    int lev0[kMax];
+    int kind[kMax];
+};
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -46,8 +62,10 @@ constexpr int kKvSub = 2;   // sub-steps per step: one LDS buffer holds 128 quer
 // One (64-query step, 32x32 block) of the dK/dV kernel for one wave: S = Q K^T
 // and dP = dO V^T (lane = key column), P = 2^(c2 s - lse log2 e),
 // dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS over the block's 32
-// queries.  With `mask` (wave-uniform) keys after the query and query rows
-// past N get P = 0.
+// queries.  With `mask` (wave-uniform: causal diagonal blocks) keys after the
+// query get P = 0.  Query rows past N need no mask: their Q and dO rows and
+// their lse and D read as zero, so P = 1 there and every product they feed
+// (dV += P^T dO, dK += dS^T Q with dS = P (dP - D) = 0) adds exact zeros.
 template <int D>
 __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
                                            const float *ddt, const bf16x8 (&kf)[D / 16],
@@ -87,12 +105,15 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
             pacc[r] = pacc[r] - dv[e];
         }
     }
+    // Register r holds query row q0 + 32qh + 4hf + c, c = 8(r/4) + r%4 (a
+    // constant): the causal mask keeps c >= kj - (q0 + 32qh + 4hf), one compare
+    // and one select per score.
     if (mask) {
+        const int t = kj - (q0 + 32 * qh + 4 * hf);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int qrow = q0 + 32 * qh + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool keep = (!causal || kj <= qrow) && qrow < N;
-            sacc[r] = keep ? sacc[r] : 0.f;
+            const int c = 8 * (r >> 2) + (r & 3);
+            sacc[r] = c >= t ? sacc[r] : 0.f;
         }
     }
 #pragma unroll
@@ -113,34 +134,44 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
     sched_pipeline<8 * DB, 4 * DB, kAheadT, 2>();
 }
 
-// d = 128 needs more than the 256 registers of two waves per SIMD (K, V
-// operands 64 + dK, dV accumulators 128 + scores 32 + operands in flight):
-// it runs one wave per SIMD with up to 512.
+// The LDS of the dK/dV work: double-buffered Q, dO, lse and D tiles of
+// kKvSub * kKvBM query rows, each buffer an array of its own (see Buf).  The
+// dQ work uses the first kQBN rows of the Q and dO arrays as its
+// double-buffered K and V tiles.
 template <int D>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+struct BwdLds {
+    static constexpr int SR = kKvSub * kKvBM;   // query rows per dK/dV step
+    uint16_t *q0s, *q1s, *d0s, *d1s;
+    float *l0s, *l1s, *e0s, *e1s;
+};
+
+#define ATTN_BWD_LDS(D_, name)                                                                    \
+    __shared__ __attribute__((aligned(16))) uint16_t name##q0[BwdLds<D_>::SR * D_],                \
+        name##q1[BwdLds<D_>::SR * D_], name##d0[BwdLds<D_>::SR * D_], name##d1[BwdLds<D_>::SR * D_]; \
+    __shared__ __attribute__((aligned(16))) float name##l0[BwdLds<D_>::SR], name##l1[BwdLds<D_>::SR], \
+        name##e0[BwdLds<D_>::SR], name##e1[BwdLds<D_>::SR];                                       \
+    const BwdLds<D_> name{name##q0, name##q1, name##d0, name##d1, name##l0, name##l1, name##e0, name##e1}
+
+// dK/dV of key tile kt for work item `item` = (batch, kv head, head subset):
+// the G query heads of a group are split into hs subsets of Gs heads; with
+// hs > 1 the subsets' partial dK/dV are summed with atomics into zero-filled
+// outputs.  The copy of step s+1 has the two sub-steps of step s to land; at
+// the end the four tile arrays hold the dK^T / dV^T partials of the two query
+// halves.
+template <int D>
+__device__ __forceinline__ void dkdv_body(
+    int kt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
     float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal, int hs)
 {
     constexpr int KS = D / 16, DB = D / 32;
+    constexpr int SR = BwdLds<D>::SR;
+    uint16_t *const q0s = lds.q0s, *const q1s = lds.q1s, *const d0s = lds.d0s, *const d1s = lds.d1s;
+    float *const l0s = lds.l0s, *const l1s = lds.l1s, *const e0s = lds.e0s, *const e1s = lds.e1s;
 
-    // Double-buffered Q, dO, lse and D tiles of kKvSub * kKvBM query rows in
-    // separate arrays (see Buf): the copy of step s+1 has the two sub-steps of
-    // step s to land.  At the end the four tile arrays hold the dK^T / dV^T
-    // partials of the two query halves.
-    constexpr int SR = kKvSub * kKvBM;       // query rows per step
-    __shared__ __attribute__((aligned(16))) uint16_t q0s[SR * D], q1s[SR * D];
-    __shared__ __attribute__((aligned(16))) uint16_t d0s[SR * D], d1s[SR * D];
-    __shared__ __attribute__((aligned(16))) float l0s[SR], l1s[SR], e0s[SR], e1s[SR];
-
-    // Work item = (key tile, batch, kv head, head subset).  The G query heads of
-    // a group are split into hs subsets of Gs heads; with hs > 1 the subsets'
-    // partial dK/dV are summed with atomics into zero-filled outputs.
-    const int BGH = B * Hkv * hs;
-    const int kt = blockIdx.x / BGH;         // causal: low key tiles see the most queries
-    const int rem = blockIdx.x % BGH;
-    const int b = rem / (Hkv * hs), g = (rem / hs) % Hkv, hsub = rem % hs;
+    const int grp = item / hs, hsub = item % hs;
+    const int b = grp / Hkv, g = grp % Hkv;
     const int G = Hq / Hkv, Gs = G / hs;
     const int k0 = kt * kKvBN;
 
@@ -213,7 +244,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
             const int q0 = (qt0 + s % nq) * SR + sub * kKvBM;
             const int qb0 = q0 + 32 * qh;   // first query row of this wave's block
             if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
-                const bool mask = (causal && qb0 < k0 + 32 * kb + 32) || qb0 + 32 > N;
+                const bool mask = causal && qb0 < k0 + 32 * kb + 32;
                 dkdv_block<D>(qc + sub * kKvBM * D, dc + sub * kKvBM * D, lc + sub * kKvBM,
                               ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj, N, causal, mask, lane);
             }
@@ -228,39 +259,17 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     // Sum the two query halves and write dK = scale (dK^T)^T and dV.
     // Accumulator layout: lane = key column kj, register r of block db = dim
     // db*32 + 8(r/4) + 4hf + (r&3).  The query-half-1 waves park their partials
-    // in the tile arrays (one array per (key block, dK or dV)), the half-0 waves
-    // add them and park the sums, transposed to [key][dim], so that the final
-    // stores (or atomics) run along the dim with consecutive lanes.
-    constexpr int RED = DB * 16 * 64;        // floats per (key block, dK or dV) partial
-    static_assert(RED * sizeof(float) <= sizeof(q0s), "one partial per tile array");
+    // in the tile arrays (one array per (key block, dK or dV)) transposed to
+    // [key][dim], the half-0 waves add theirs in place, so that the final
+    // stores (or atomics) run along the dim with consecutive lanes.  Key row
+    // l32 of a key block keeps dim d at [l32][d ^ l32]: the XOR spreads the 32
+    // rows written by one instruction over the banks and keeps each row a
+    // permutation of its dims.
+    static_assert(32 * D * sizeof(float) <= SR * D * sizeof(uint16_t), "transposed partial fits");
     float *redk = reinterpret_cast<float *>(kb ? q1s : q0s);
     float *redv = reinterpret_cast<float *>(kb ? d1s : d0s);
     __syncthreads();                         // the last step's reads are done
     if (qh == 1) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                redk[(db * 16 + r) * 64 + lane] = dka[db][r];
-                redv[(db * 16 + r) * 64 + lane] = dva[db][r];
-            }
-    }
-    __syncthreads();
-    if (qh == 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dka[db][r] = (dka[db][r] + redk[(db * 16 + r) * 64 + lane]) * scale;
-                dva[db][r] += redv[(db * 16 + r) * 64 + lane];
-            }
-    }
-    __syncthreads();
-    // transposed park: key row l32 (of this key block), dim d at
-    // [l32][d ^ l32] -- the XOR spreads the 32 rows written by one instruction
-    // over the banks and keeps each row a permutation of its dims
-    static_assert(32 * D * sizeof(float) <= sizeof(q0s), "transposed partial fits");
-    if (qh == 0) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -271,27 +280,73 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
             }
     }
     __syncthreads();
-    // all 4 waves write: wave w takes key rows w, w+4, ... of the 64-key tile;
-    // lanes run along the dim
-    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)N * D;
-    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)N * D;
-    for (int kr = wave; kr < kKvBN; kr += 4) {
-        const int key = k0 + kr;
-        if (key >= N) break;
+    if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dim = db * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                const int at = l32 * D + (dim ^ l32);
+                redk[at] = (redk[at] + dka[db][r]) * scale;
+                redv[at] = redv[at] + dva[db][r];
+            }
+    }
+    __syncthreads();
+    // all 4 waves write: wave w takes key rows w, w+4, ... of the 64-key tile,
+    // lanes along the dim; every LDS read is issued before the first store
+    constexpr int RPW = kKvBN / 4, CPR = D / 64;   // rows per wave, 64-dim chunks per row
+    float vk[RPW * CPR], vv[RPW * CPR];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int kr = wave + 4 * i;
         const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s) + (kr & 31) * D;
         const float *sv = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s) + (kr & 31) * D;
 #pragma unroll
-        for (int d0 = 0; d0 < D; d0 += 64) {
-            const int dim = d0 + lane, src = dim ^ (kr & 31);
-            if (hs == 1) {
-                dKg[(size_t)key * D + dim] = sk[src];
-                dVg[(size_t)key * D + dim] = sv[src];
-            } else {
-                atomicAdd(dKg + (size_t)key * D + dim, sk[src]);
-                atomicAdd(dVg + (size_t)key * D + dim, sv[src]);
+        for (int c = 0; c < CPR; ++c) {
+            const int src = (64 * c + lane) ^ (kr & 31);
+            vk[i * CPR + c] = sk[src];
+            vv[i * CPR + c] = sv[src];
+        }
+    }
+    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)N * D;
+    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)N * D;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int key = k0 + wave + 4 * i;
+        if (key < N) {
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) {
+                const size_t at = (size_t)key * D + 64 * c + lane;
+                if (hs == 1) {
+                    dKg[at] = vk[i * CPR + c];
+                    dVg[at] = vv[i * CPR + c];
+                } else {
+                    atomicAdd(dKg + at, vk[i * CPR + c]);
+                    atomicAdd(dVg + at, vv[i * CPR + c]);
+                }
             }
         }
     }
+}
+
+// d = 128 needs more than the 256 registers of two waves per SIMD (K, V
+// operands 64 + dK, dV accumulators 128 + scores 32 + operands in flight):
+// it runs one wave per SIMD with up to 512.
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
+    float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal, int hs)
+{
+    ATTN_BWD_LDS(D, lds);
+    // XCD-aware (see xcd_work_item): a group's Q and dO rows stay in one L2,
+    // the heaviest key tiles (causal: the lowest) first.
+    const int nkt = (N + kKvBN - 1) / kKvBN;
+    WorkItem w;
+    if (!xcd_work_item(blockIdx.x, B * Hkv, nkt, hs, w)) return;
+    dkdv_body<D>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq,
+                 Hkv, N, scale, causal, hs);
 }
 
 // ---------------------------------------------------------------------------
@@ -329,12 +384,12 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
         else sched_pipeline<2 * KS, 2 * KS, 4, 1>();
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lse2));
-        if (mask) {
+        if (mask) {   // keys kv0 + 32kb + 4hf + c (c constant) kept iff c < lim
+            const int lim = (causal ? min(qi + 1, N) : N) - (kv0 + kb * 32 + 4 * hf);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                const bool hide = (causal && key > qi) || key >= N;
-                sacc[r] = hide ? 0.f : sacc[r];
+                const int c = 8 * (r >> 2) + (r & 3);
+                sacc[r] = c < lim ? sacc[r] : 0.f;
             }
         }
 #pragma unroll
@@ -351,27 +406,23 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
     }
 }
 
+// dQ of query tile qt for work item `item` = (batch, query head).  K and V
+// tiles, row-major with swizzled 16-byte chunks, double-buffered in the first
+// kQBN rows of the Q and dO arrays of `lds`.
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+__device__ __forceinline__ void dq_body(
+    int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int N, float scale, int causal, int nqt)
+    int Hq, int Hkv, int N, float scale, int causal)
 {
     constexpr int KS = D / 16, DB = D / 32;
+    uint16_t *const sk0 = lds.q0s, *const sk1 = lds.q1s, *const sv0 = lds.d0s, *const sv1 = lds.d1s;
 
-    // K and V tiles, row-major with swizzled 16-byte chunks, double-buffered in
-    // separate arrays (see Buf)
-    __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
-
-    // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
     const int G = Hq / Hkv;
-    WorkItem w;
-    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    const int qt = w.tile;
-    const int b = w.group / Hkv, g = w.group % Hkv;
-    const int h = g * G + w.head;
+    const int grp = item / G;
+    const int b = grp / Hkv, g = grp % Hkv;
+    const int h = g * G + item % G;
     const int q0 = qt * kQBM;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -460,6 +511,57 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
 }
 
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
+    int Hq, int Hkv, int N, float scale, int causal, int nqt)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
+    const BwdLds<D> lds{sk0, sk1, sv0, sv1, nullptr, nullptr, nullptr, nullptr};
+    // work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
+    const int G = Hq / Hkv;
+    WorkItem w;
+    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
+    dq_body<D>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, N, scale,
+               causal);
+}
+
+// Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
+// blocks, each group one or more levels of one kind -- dK/dV key tiles or dQ
+// query tiles -- with the heaviest levels first over both kinds, so that the
+// hardware's in-order dispatch of blocks to free CU slots packs the two kinds
+// together.  Within a level, the block's XCD picks a contiguous range of its
+// work items (a group's rows stay in one L2).
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ,
+    float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale,
+    int causal, int hs, BwdPlan plan)
+{
+    static_assert(kQBN <= BwdLds<D>::SR, "dQ's K/V tiles fit the Q/dO arrays");
+    ATTN_BWD_LDS(D, lds);
+    const int blk = blockIdx.x;
+    int i = 0;
+    while (i + 1 < plan.n && blk >= plan.first[i + 1]) ++i;
+    const int kind = plan.kind[i];
+    const int per_level = kind == 0 ? B * Hkv * hs : B * Hq;
+    const int per_xcd = (per_level + kXcds - 1) / kXcds;
+    const int rel = blk - plan.first[i];
+    const int k = rel / kXcds;
+    const int level = kind == 0 ? plan.lev0[i] + k / per_xcd : plan.lev0[i] - k / per_xcd;
+    const int item = (rel % kXcds) * per_xcd + k % per_xcd;
+    if (item >= per_level) return;
+    if (kind == 0)
+        dkdv_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, N, scale, causal, hs);
+    else
+        dq_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, N, scale, causal);
+}
+
 }  // namespace
 
 int dkdv_head_split(int B, int Hq, int Hkv, int N)
@@ -524,6 +626,99 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float s
         hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
                            Dws, dq, B, Hq, Hkv, N, scale, causal, nqt);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+namespace {
+
+// Estimated time of one work item of each kind (arbitrary units, fitted to
+// per-workgroup timelines measured on MI355X at d = 64: about 1.9 per 128-query
+// dK/dV step and 0.8 per 64-key dQ tile on top of a fixed part for loading the
+// item's resident operands and storing its result), for ordering only.
+double dkdv_cost(int steps, int d) { return 7.0 + 1.9 * steps * (d / 64); }
+double dq_cost(int tiles, int d) { return 6.0 + 0.8 * tiles * (d / 64); }
+
+struct PlanLevel {
+    int kind, lev, nlev;
+    double cost;
+};
+
+// Level groups of one kind, heaviest first, coarsened to at most `cap` groups.
+void plan_levels(int kind, int nlev, int cap, const double *cost, const int *lev,
+                 std::vector<PlanLevel> &out)
+{
+    const int chunk = (nlev + cap - 1) / cap;
+    for (int i = 0; i < nlev; i += chunk) {
+        const int n = std::min(chunk, nlev - i);
+        double c = 0;
+        for (int j = 0; j < n; ++j) c += cost[i + j];
+        out.push_back({kind, lev[i], n, c / n});
+    }
+}
+
+}  // namespace
+
+BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *grid)
+{
+    const int nkt = (N + kKvBN - 1) / kKvBN, nqkv = (N + kKvSub * kKvBM - 1) / (kKvSub * kKvBM);
+    const int nqt = (N + kQBM - 1) / kQBM;
+    const int G = Hq / Hkv, Gs = G / hs;
+    std::vector<double> ck(nkt), cq(nqt);
+    std::vector<int> lk(nkt), lq(nqt);
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int nq = nqkv - (causal ? kt * kKvBN / (kKvSub * kKvBM) : 0);
+        lk[kt] = kt;
+        ck[kt] = dkdv_cost(Gs * nq, d);
+    }
+    for (int j = 0; j < nqt; ++j) {
+        const int qt = nqt - 1 - j;
+        const int kv_end = causal ? std::min(N, (qt + 1) * kQBM) : N;
+        lq[j] = qt;
+        cq[j] = dq_cost((kv_end + kQBN - 1) / kQBN, d);
+    }
+    std::vector<PlanLevel> a, q, m;
+    plan_levels(0, nkt, BwdPlan::kMax / 2, ck.data(), lk.data(), a);
+    plan_levels(1, nqt, BwdPlan::kMax / 2, cq.data(), lq.data(), q);
+    // merge, heaviest first (ties: dK/dV first)
+    size_t ia = 0, iq = 0;
+    while (ia < a.size() || iq < q.size()) {
+        if (iq == q.size() || (ia < a.size() && a[ia].cost >= q[iq].cost)) m.push_back(a[ia++]);
+        else m.push_back(q[iq++]);
+    }
+    BwdPlan p{};
+    p.n = (int)m.size();
+    int blk = 0;
+    for (int i = 0; i < p.n; ++i) {
+        const int per_level = m[i].kind == 0 ? B * Hkv * hs : B * Hq;
+        const int per_xcd = (per_level + kXcds - 1) / kXcds;
+        p.first[i] = blk;
+        p.lev0[i] = m[i].lev;
+        p.kind[i] = m[i].kind;
+        blk += m[i].nlev * per_xcd * kXcds;
+    }
+    p.first[p.n] = blk;
+    *grid = blk;
+    return p;
+}
+
+hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          const void *q, const void *k, const void *v, const float *lse,
+                          const void *dout, const float *Dws, float *dq, float *dk, float *dv,
+                          int hs, hipStream_t st)
+{
+    int nblk = 0;
+    const BwdPlan plan = bwd_plan(B, Hq, Hkv, N, d, causal, hs, &nblk);
+    const dim3 grid((unsigned)nblk);
+    if (d == 128)
+        hipLaunchKernelGGL(bwd_fused_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
+                           Dws, dq, dk, dv, B, Hq, Hkv, N, scale, causal, hs, plan);
+    else if (d == 64)
+        hipLaunchKernelGGL(bwd_fused_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
+                           Dws, dq, dk, dv, B, Hq, Hkv, N, scale, causal, hs, plan);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

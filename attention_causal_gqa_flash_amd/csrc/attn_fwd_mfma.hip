@@ -89,14 +89,16 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     sched_pipeline<2 * KS, 2 * KS, 4, 1, NV>();
 
     // Row max on the raw scores (c2 > 0 commutes with max); masked scores are -inf.
+    // Register r of block kb holds key kv0 + 4hf + c, c = 32kb + 8(r/4) + r%4
+    // (a constant), kept iff c < lim: one compare and one select per score.
     if (mask) {
+        const int lim = (causal ? min(qi + 1, N) : N) - (kv0 + 4 * hf);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                const bool hide = (causal && key > qi) || key >= N;
-                sacc[kb][r] = hide ? -INFINITY : sacc[kb][r];
+                const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+                sacc[kb][r] = c < lim ? sacc[kb][r] : -INFINITY;
             }
     }
     // Row max and row sum as four independent chains each (short dependency

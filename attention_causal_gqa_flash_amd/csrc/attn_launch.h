@@ -18,6 +18,11 @@ hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal,
 hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, hipStream_t st);
+// dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
+hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          const void *q, const void *k, const void *v, const float *lse,
+                          const void *dout, const float *Dws, float *dq, float *dk, float *dv,
+                          int hs, hipStream_t st);
 hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                             const void *q, const void *k, const void *v, const float *lse,
                             const void *dout, const float *Dws, float *dk, float *dv,
@@ -46,6 +51,11 @@ hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st);
+// dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
+hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          const void *q, const void *k, const void *v, const float *lse,
+                          const void *dout, const float *Dws, float *dq, float *dk, float *dv,
+                          int hs, hipStream_t st);
 
 // Split-KV decode and the log-sum-exp merge.
 hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
