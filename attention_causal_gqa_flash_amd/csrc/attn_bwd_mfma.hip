@@ -59,24 +59,26 @@ constexpr int kKvBN = 64;   // keys per workgroup
 constexpr int kKvBM = 64;   // queries per sub-step (the two query halves of the waves)
 constexpr int kKvSub = 2;   // sub-steps per step: one LDS buffer holds 128 query rows
 
-// One (64-query step, 32x32 block) of the dK/dV kernel for one wave: S = Q K^T
-// and dP = dO V^T (lane = key column), P = 2^(c2 s - lse log2 e),
-// dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS over the block's 32
-// queries.  With `mask` (wave-uniform: causal diagonal blocks) keys after the
-// query get P = 0.  Query rows past N need no mask: their Q and dO rows and
-// their lse and D read as zero, so P = 1 there and every product they feed
-// (dV += P^T dO, dK += dS^T Q with dS = P (dP - D) = 0) adds exact zeros.
+// One (64-query sub-step, 32x32 block) of the dK/dV kernel for one wave, in
+// three phases: S = Q K^T and dP = dO V^T (lane = key column); P = 2^(c2 s -
+// lse log2 e) and dS = P (dP - D); then dV^T += dO^T P and dK^T += Q^T dS
+// over the block's 32 queries.  With `mask` (wave-uniform: causal diagonal
+// blocks) keys after the query get P = 0.  Query rows past N need no mask:
+// their Q and dO rows and their lse and D read as zero, so P = 1 there and
+// every product they feed (dV += P^T dO, dK += dS^T Q with dS = P (dP - D) =
+// 0) adds exact zeros.
+constexpr int kAhead = 8;    // operand reads issued ahead of the score MFMAs
+constexpr int kAheadT = 8;   // ... and of the dV/dK MFMAs
+// (measured on the 32/8-head N = 4096 dK/dV kernel: 4 ahead 374 us, 8 ahead
+// 354 us, 12 or 16 ahead slower again)
+
 template <int D>
-__device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
-                                           const float *ddt, const bf16x8 (&kf)[D / 16],
-                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32],
-                                           f32x16 (&dva)[D / 32], float c2, int qh, int q0, int kj,
-                                           int N, int causal, bool mask, int lane)
+__device__ __forceinline__ void dkdv_scores(const uint16_t *qt, const uint16_t *dt,
+                                            const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
+                                            f32x16 &sacc, f32x16 &pacc, int qh, int lane)
 {
-    constexpr int KS = D / 16, DB = D / 32;
-    constexpr int kAhead = 8, kAheadT = 8;
+    constexpr int KS = D / 16;
     const int l32 = lane & 31, hf = lane >> 5;
-    f32x16 sacc, pacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
 #pragma unroll
@@ -86,18 +88,32 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
         sacc = mfma32x32x16(aq, kf[ks], sacc);
         pacc = mfma32x32x16(ad, vf[ks], pacc);
     }
-    // Operand reads run kAhead ahead of their MFMAs (measured on the 32/8-head
-    // N = 4096 dK/dV kernel: 4 ahead 374 us, 8 ahead 354 us, 12 or 16 ahead
-    // slower again).
-    sched_pipeline<2 * KS, 2 * KS, kAhead, 1>();
-    // rows are queries (register r: local row 32qh + 8(r/4) + 4hf + r%4), lane = key
+}
+
+// lse and D of the block's rows (register r: local row 32qh + 8(r/4) + 4hf + r%4)
+struct RowStats {
+    float4 l[4], d[4];
+};
+
+__device__ __forceinline__ RowStats dkdv_rows(const float *lt, const float *ddt, int qh, int lane)
+{
+    RowStats rs;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        const int rr = 32 * qh + 8 * a + 4 * hf;
-        const float4 l4 = *(const float4 *)&lt[rr];
-        const float4 d4 = *(const float4 *)&ddt[rr];
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const int rr = 32 * qh + 8 * a + 4 * (lane >> 5);
+        rs.l[a] = *(const float4 *)&lt[rr];
+        rs.d[a] = *(const float4 *)&ddt[rr];
+    }
+    return rs;
+}
+
+__device__ __forceinline__ void dkdv_probs(const RowStats &rs, f32x16 &sacc, f32x16 &pacc, float c2,
+                                           bool mask, int t)
+{
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const float lv[4] = {rs.l[a].x * kLog2e, rs.l[a].y * kLog2e, rs.l[a].z * kLog2e, rs.l[a].w * kLog2e};
+        const float dv[4] = {rs.d[a].x, rs.d[a].y, rs.d[a].z, rs.d[a].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e;
@@ -106,10 +122,9 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
         }
     }
     // Register r holds query row q0 + 32qh + 4hf + c, c = 8(r/4) + r%4 (a
-    // constant): the causal mask keeps c >= kj - (q0 + 32qh + 4hf), one compare
-    // and one select per score.
+    // constant): the causal mask keeps c >= t = kj - (q0 + 32qh + 4hf), one
+    // compare and one select per score.
     if (mask) {
-        const int t = kj - (q0 + 32 * qh + 4 * hf);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = 8 * (r >> 2) + (r & 3);
@@ -118,7 +133,15 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) pacc[r] *= sacc[r];
-    // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
+}
+
+// dV^T += dO^T P,  dK^T += Q^T dS   (contraction over the wave's 32 queries)
+template <int D>
+__device__ __forceinline__ void dkdv_grads(const uint16_t *qt, const uint16_t *dt, const f32x16 &sacc,
+                                           const f32x16 &pacc, f32x16 (&dka)[D / 32],
+                                           f32x16 (&dva)[D / 32], int qh, int lane)
+{
+    constexpr int DB = D / 32;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         const bf16x8 pb = tt ? pack_operand<8>(sacc) : pack_operand<0>(sacc);
@@ -131,6 +154,24 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
             dka[db] = mfma32x32x16(aqt, sb, dka[db]);
         }
     }
+}
+
+// One sub-step, the three phases in sequence (the block's lse and D rows
+// are all read before its probabilities are computed).
+template <int D>
+__device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
+                                           const float *ddt, const bf16x8 (&kf)[D / 16],
+                                           const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32],
+                                           f32x16 (&dva)[D / 32], float c2, int qh, int q0, int kj,
+                                           bool mask, int lane)
+{
+    constexpr int KS = D / 16, DB = D / 32;
+    f32x16 sacc, pacc;
+    dkdv_scores<D>(qt, dt, kf, vf, sacc, pacc, qh, lane);
+    sched_pipeline<2 * KS, 2 * KS, kAhead, 1>();
+    const RowStats rs = dkdv_rows(lt, ddt, qh, lane);
+    dkdv_probs(rs, sacc, pacc, c2, mask, kj - (q0 + 32 * qh + 4 * (lane >> 5)));
+    dkdv_grads<D>(qt, dt, sacc, pacc, dka, dva, qh, lane);
     sched_pipeline<8 * DB, 4 * DB, kAheadT, 2>();
 }
 
@@ -239,14 +280,15 @@ __device__ __forceinline__ void dkdv_body(
             if (BI) load_step(s + 1, q0s, d0s, l0s, e0s);
             else load_step(s + 1, q1s, d1s, l1s, e1s);
         }
+        const int qs = (qt0 + s % nq) * SR;  // first query row of the step
 #pragma unroll
         for (int sub = 0; sub < kKvSub; ++sub) {
-            const int q0 = (qt0 + s % nq) * SR + sub * kKvBM;
+            const int q0 = qs + sub * kKvBM;
             const int qb0 = q0 + 32 * qh;   // first query row of this wave's block
             if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
                 const bool mask = causal && qb0 < k0 + 32 * kb + 32;
                 dkdv_block<D>(qc + sub * kKvBM * D, dc + sub * kKvBM * D, lc + sub * kKvBM,
-                              ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj, N, causal, mask, lane);
+                              ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj, mask, lane);
             }
         }
         sched_fence();
