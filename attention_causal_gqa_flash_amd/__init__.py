@@ -13,6 +13,7 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+           "attn_bwd_grads", "attn_bwd_grads_single_launch",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dkdv.argtypes = [i, i, i, i, i, i, i, f] + [p] * 9
     L.attn_bwd_dkdv.restype = i
     L.attn_bwd_dq.argtypes = [i, i, i, i, i, i, i, f] + [p] * 8
+    L.attn_bwd_grads.argtypes = [i, i, i, i, i, i, i, f] + [p] * 10
+    L.attn_bwd_grads.restype = i
+    L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
+    L.attn_bwd_grads_single_launch.restype = i
     L.attn_bwd_dq.restype = i
     L.attn_decode.argtypes = [i, i, i, i, i, i, f, i, p, p, p, p, p, p]
     L.attn_decode.restype = i
@@ -222,6 +227,33 @@ def attn_bwd_dq(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, str
                            _ptr(_dev(delta, "delta")), _ptr(_dev(dq, "dq")), _stream(stream))
     _check("attn_bwd_dq", rc)
     return dq
+
+
+def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, dk=None, dv=None,
+                   stream=None):
+    """Stages 2 and 3 of the backward as attn_bwd runs them: (dq, dk, dv) f32."""
+    torch = _torch()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if dq is None:
+        dq = torch.empty((B, Hq, N, d), device=q.device, dtype=torch.float32)
+    if dk is None:
+        dk = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
+    if dv is None:
+        dv = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
+    rc = lib().attn_bwd_grads(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), scale,
+                              _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
+                              _ptr(_dev(lse, "lse")), _ptr(_dev(dout, "dout")),
+                              _ptr(_dev(delta, "delta")), _ptr(_dev(dq, "dq")),
+                              _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _stream(stream))
+    _check("attn_bwd_grads", rc)
+    return dq, dk, dv
+
+
+def attn_bwd_grads_single_launch(dtype_code: int, N: int, d: int, scale: float) -> bool:
+    """Whether attn_bwd_grads runs as one kernel for this dtype code, N, d, scale."""
+    return bool(lib().attn_bwd_grads_single_launch(int(dtype_code), int(N), int(d), float(scale)))
 
 
 def attn_decode(q, k_cache, v_cache, n_splits: int, scale: float | None = None,

@@ -99,18 +99,20 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causa
                                 delta, dq, st);
 }
 
-// attn_bwd runs the dK/dV and dQ kernels concurrently: dQ goes to an
-// auxiliary stream of the device, forked from and joined back into the
-// caller's stream with events (so a graph capture of the caller's stream
-// captures both branches).  Measured on MI355X (4 x 1024 x 12/4 heads, d = 64,
-// HIP-graph replay): 65.0 us one after the other, 59.4 us side by side; the
-// small grids leave CUs idle in each kernel's tail.  One auxiliary stream and
-// two events per device are created on first use (default priority); the
+// The gradient stage after the preprocess.  At d = 64 on the matrix-core path
+// it is one launch whose grid holds both the dK/dV and the dQ work items,
+// ordered heaviest first over both kinds (measured on MI355X, 4 x 1024 x 12/4
+// heads, HIP-graph replay of the training step: 83.1 us with the two kernels
+// side by side on two streams, 79.8-80.0 us with the one launch).  Otherwise
+// -- d = 128, where the one launch would hold dQ to the dK/dV kernel's
+// one-wave-per-SIMD occupancy (694 us vs 713 us for the 32/8-head N = 4096
+// step), and the row-wise fallback -- the dK/dV and dQ kernels run
+// concurrently: dQ goes to an auxiliary stream of the device, forked from and
+// joined back into the caller's stream with events (so a graph capture of the
+// caller's stream captures both branches).  One auxiliary stream and two
+// events per device are created on first use (default priority); the
 // fork/join is serialised by a mutex so that concurrent callers do not
 // interleave their event records.
-// The matrix-core gradients run as one launch (dK/dV and dQ workgroups in
-// one grid, ordered heaviest first over both kinds) where that beats the
-// two-stream form.
 bool fuse_bwd(int d) { return d == 64; }
 
 struct BwdAux {
@@ -138,6 +140,36 @@ BwdAux *bwd_aux(hipStream_t st)
     if (!a.fork && hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess) a.fork = nullptr;
     if (!a.join && hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess) a.join = nullptr;
     return (a.st && a.fork && a.join) ? &a : nullptr;
+}
+
+// dQ, dK, dV from delta (dk/dv already zero when hs > 1).
+attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                             const void *q, const void *k, const void *v, const float *lse,
+                             const void *dout, const float *delta, float *dq, float *dk, float *dv,
+                             int hs, hipStream_t st)
+{
+    if (use_mfma(dt, N, d, scale) && fuse_bwd(d))
+        return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse,
+                                               dout, delta, dq, dk, dv, hs, st));
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    BwdAux *aux = bwd_aux(st);
+    hipStream_t st_dq = st;
+    if (aux) {
+        if (hipEventRecord(aux->fork, st) != hipSuccess ||
+            hipStreamWaitEvent(aux->st, aux->fork, 0) != hipSuccess)
+            return ATTN_ERR_HIP;
+        st_dq = aux->st;
+    }
+    if (launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st_dq) !=
+        hipSuccess)
+        return ATTN_ERR_HIP;
+    if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
+                        hs, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
+                hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 }  // namespace
@@ -184,28 +216,8 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st) !=
         hipSuccess)
         return ATTN_ERR_HIP;
-    if (use_mfma(dt, N, d, scale) && fuse_bwd(d))
-        return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse,
-                                               dout, delta, dq, dk, dv, hs, st));
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    BwdAux *aux = bwd_aux(st);
-    hipStream_t st_dq = st;
-    if (aux) {
-        if (hipEventRecord(aux->fork, st) != hipSuccess ||
-            hipStreamWaitEvent(aux->st, aux->fork, 0) != hipSuccess)
-            return ATTN_ERR_HIP;
-        st_dq = aux->st;
-    }
-    if (launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st_dq) !=
-        hipSuccess)
-        return ATTN_ERR_HIP;
-    if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
-                        hs, st) != hipSuccess)
-        return ATTN_ERR_HIP;
-    if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
-                hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
-        return ATTN_ERR_HIP;
-    return ATTN_OK;
+    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
+                            dv, hs, st);
 }
 
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,
@@ -247,6 +259,30 @@ attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int
         return ATTN_ERR_INVALID_ARG;
     return hip_status(launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
                                     delta, dq, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_grads(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                           float scale, const void *q, const void *k, const void *v,
+                           const float *lse, const void *dout, const float *delta, float *dq,
+                           float *dk, float *dv, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout) ||
+        !aligned16(delta) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
+    if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * N * d, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
+                            dv, hs, st);
+}
+
+int attn_bwd_grads_single_launch(attn_dtype dt, int N, int d, float scale)
+{
+    if (check_common(dt, 1, 1, 1, N, d, scale) != ATTN_OK) return 0;
+    return use_mfma(dt, N, d, scale) && fuse_bwd(d) ? 1 : 0;
 }
 
 attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,

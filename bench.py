@@ -3,9 +3,10 @@
 
 One step = one pass of the whole hot path on seeded synthetic inputs already
 resident in device memory:
-  * the training op: attn_fwd, then attn_bwd (preprocess, then the dK/dV and
-    dQ kernels side by side) on the training workload (default: bf16, B=4,
-    12 query / 4 key-value heads, N=1024, d=64);
+  * the training op: attn_fwd, then attn_bwd (preprocess, then the gradient
+    stage: at d=64 one kernel holding both the dK/dV and the dQ work, at
+    d=128 the dK/dV and dQ kernels side by side) on the training workload
+    (default: bf16, B=4, 12 query / 4 key-value heads, N=1024, d=64);
   * the decode op: split-KV decode + LSE merge (attn_decode_merged: the decode
     kernel then the merge kernel) on the decode workload (bf16, 32/8 heads, d=128, a 4096-key cache in 16
     splits), rotating over enough distinct caches (default 24 x 16 MiB) that
@@ -15,7 +16,9 @@ The K timed steps are captured into two HIP graphs (K training ops, K decode
 ops) and replayed once each between HIP events; the launches are the same
 C-ABI calls an eager caller makes, without the host-side launch overhead that
 would otherwise dominate the short decode op.  Each kernel's average duration
-is measured the same way (a graph of K launches of that kernel alone).
+is measured the same way (a graph of K launches of that kernel alone; the
+gradient stage `bwd_grads` is timed per attn_bwd_grads call, which includes a
+zero-fill launch of dk/dv when they are accumulated with atomics).
 
 Prints ONE JSON line.  `value` is the training workload's algorithmic fwd+bwd
 TFLOP/s (4*d flop per unmasked (query, key) pair forward, 10*d backward);
@@ -69,6 +72,7 @@ CALIB_BYTES = 1 << 30
 
 # Kernel symbol fragment -> kernel name used in the bench output.
 KERNEL_NAMES = (("fwd_mfma_kernel", "fwd"), ("bwd_pre_kernel", "bwd_preprocess"),
+                ("bwd_fused_kernel", "bwd_grads"),
                 ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
                 ("decode_mfma_kernel", "decode_merged"), ("lse_merge_kernel", "lse_merge"))
 
@@ -255,6 +259,13 @@ def main():
     def dqk():
         attn.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq)
 
+    def grads():
+        attn.attn_bwd_grads(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq,
+                            dk=dk, dv=dv)
+
+    dt_code = 1 if cfg.dtype == "bf16" else 0
+    grads_one_kernel = attn.attn_bwd_grads_single_launch(dt_code, N, d, cfg.scale)
+
     bwd_ws = torch.empty(max(256, attn.attn_bwd_workspace_bytes(1 if cfg.dtype == "bf16" else 0,
                                                                 B, Hq, Hkv, N, d)),
                          device=dev, dtype=torch.uint8)
@@ -292,12 +303,15 @@ def main():
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
 
     flop = {"fwd": 4 * d * pairs,
+            "bwd_grads": 10 * d * pairs,    # the whole gradient stage
             "bwd_dkdv": 8 * d * pairs,      # recomputed S, dP, dV, dK
             "bwd_dq": 2 * d * pairs}        # dQ (its S and dP recompute is not credited)
     kernels = {}
     if not args.no_kernel_breakdown:
-        for name, fn in (("fwd", fwd), ("bwd_preprocess", pre), ("bwd_dkdv", dkdv), ("bwd_dq", dqk)):
+        for name, fn in (("fwd", fwd), ("bwd_preprocess", pre), ("bwd_grads", grads),
+                         ("bwd_dkdv", dkdv), ("bwd_dq", dqk)):
             kernels[name] = {"avg_us": round(timer(torch, [fn] * K, K), 3)}
+        kernels["bwd_grads"]["one_kernel"] = grads_one_kernel
         kernels["decode_merged"] = {"avg_us": round(dec_us, 3)}
         for n, f in flop.items():
             t = kernels[n]["avg_us"] * 1e-6
@@ -315,7 +329,11 @@ def main():
 
     roof = None
     if kernels:
-        dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+        # the kernels the training step launches: the gradient stage is one
+        # kernel (bwd_grads) or the dK/dV and dQ kernels
+        in_step = ["fwd", "bwd_preprocess", "decode_merged"] + (
+            ["bwd_grads"] if grads_one_kernel else ["bwd_dkdv", "bwd_dq"])
+        dom = max(in_step, key=lambda n: kernels[n]["avg_us"])
         t = kernels[dom]["avg_us"]
         if dom in flop:
             ach = flop[dom] / (t * 1e-6) / 1e12

@@ -106,13 +106,15 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
  *   then differ from run to run in the last bits.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry do not matter.
- *   Streams: the dq kernel runs on an auxiliary stream of the current device,
- *   forked from and joined back into `stream` with events, concurrently with
- *   the dk/dv kernel; to the caller the call behaves as if all its work were
- *   on `stream` (a graph capture of `stream` captures both branches).  The
- *   auxiliary stream and events are created on the device's first attn_bwd
- *   call; if that first call is made while `stream` is being captured, or
- *   they cannot be created, the kernels run one after the other on `stream`.
+ *   Streams: the gradients run as described at attn_bwd_grads; when they are
+ *   two kernels, the dq kernel runs on an auxiliary stream of the current
+ *   device, forked from and joined back into `stream` with events,
+ *   concurrently with the dk/dv kernel; to the caller the call behaves as if
+ *   all its work were on `stream` (a graph capture of `stream` captures both
+ *   branches).  The auxiliary stream and events are created on the device's
+ *   first such call; if that first call is made while `stream` is being
+ *   captured, or they cannot be created, the kernels run one after the other
+ *   on `stream`.
  */
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      const void *q, const void *k, const void *v,
@@ -129,7 +131,13 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
  * attn_bwd_preprocess -- writes delta from o (f32) and dout (dtype dt).
  * attn_bwd_dkdv       -- writes dk and dv; reads q, k, v, lse, dout, delta.
  * attn_bwd_dq         -- writes dq; reads q, k, v, lse, dout, delta.
- * dkdv and dq do not depend on each other; both need the preprocess first.
+ * attn_bwd_grads      -- writes dq, dk and dv the way attn_bwd does after its
+ *                        preprocess: on the bf16 matrix-core path at d = 64
+ *                        ONE kernel launch whose grid holds both the dk/dv and
+ *                        the dq work items (after a zero-fill launch of dk and
+ *                        dv when they are accumulated with atomics); otherwise
+ *                        the dk/dv and dq kernels side by side (see attn_bwd).
+ * dkdv and dq do not depend on each other; all need the preprocess first.
  */
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d,
                                 const float *o, const void *dout, float *delta, void *stream);
@@ -141,6 +149,18 @@ attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int
                         float scale, const void *q, const void *k, const void *v,
                         const float *lse, const void *dout, const float *delta,
                         float *dq, void *stream);
+attn_status attn_bwd_grads(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                           float scale, const void *q, const void *k, const void *v,
+                           const float *lse, const void *dout, const float *delta,
+                           float *dq, float *dk, float *dv, void *stream);
+
+/*
+ * attn_bwd_grads_single_launch -- 1 when attn_bwd_grads (and the gradient part
+ *   of attn_bwd) runs dq, dk and dv as one kernel for this dtype, sequence
+ *   length, head dim and scale, else 0 (also 0 for arguments attn_bwd would
+ *   refuse).  No device work.
+ */
+int attn_bwd_grads_single_launch(attn_dtype dt, int N, int d, float scale);
 
 /*
  * attn_decode -- split-KV attention of one new query token per (b, query head)

@@ -39,7 +39,8 @@ def L():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-                     "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
+                     "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
+                     "attn_bwd_grads_single_launch", "attn_decode", "attn_lse_merge",
                      "attn_status_str", "attn_abi_version"):
         assert required in names
 
@@ -151,6 +152,25 @@ def test_bwd_stage_refusals(L):
     assert L.attn_bwd_dkdv(*args, *([P] * 7), NUL, NUL) == INVALID
     assert L.attn_bwd_dq(1, 1, 4, 2, 64, 64, 1, float("nan"), *([P] * 7), NUL) == INVALID
     assert L.attn_bwd_dq(*args, *([P] * 6), MIS, NUL) == INVALID
+    assert L.attn_bwd_grads(1, 1, 4, 3, 64, 64, 1, 0.125, *([P] * 9), NUL) == INVALID
+    assert L.attn_bwd_grads(1, 1, 4, 2, 64, 40, 1, 0.125, *([P] * 9), NUL) == UNSUPPORTED
+    for which in range(9):
+        ptrs = [P] * 9
+        ptrs[which] = MIS
+        assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
+        ptrs[which] = NUL
+        assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
+
+
+def test_bwd_grads_single_launch_query(L):
+    """One launch exactly for the bf16 matrix-core path at d = 64; no device work."""
+    assert L.attn_bwd_grads_single_launch(1, 1024, 64, 0.125) == 1
+    assert L.attn_bwd_grads_single_launch(1, 4096, 128, 0.088) == 0
+    assert L.attn_bwd_grads_single_launch(0, 1024, 64, 0.125) == 0     # f32: row-wise kernels
+    assert L.attn_bwd_grads_single_launch(1, 1024, 64, 0.0) == 0       # scale 0: row-wise
+    assert L.attn_bwd_grads_single_launch(1, 1024, 40, 0.125) == 0     # unsupported head dim
+    assert L.attn_bwd_grads_single_launch(1, 0, 64, 0.125) == 0
+    assert L.attn_bwd_grads_single_launch(1, 1024, 64, float("nan")) == 0
 
 
 def test_no_unexpected_exports(L):

@@ -263,12 +263,37 @@ def test_decode_merged_two_calls(B, Hq, Hkv, L, d, S, dtype, L2):
         assert float(np.abs(po.cpu().numpy() - rpo).max()) <= tol_o
 
 
-@pytest.mark.parametrize("whole_bwd", [False, True], ids=["stages", "attn_bwd"])
-def test_graph_replay_matches_eager(whole_bwd):
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [
+    (4, 12, 4, 1024, 64, True),     # the 4 x 1024 training shape: one launch, 3-way head split
+    (2, 8, 2, 333, 64, True),       # ragged tail, 4-way head split
+    (1, 6, 3, 200, 64, False),
+    (1, 8, 2, 300, 128, True),      # d = 128: two kernels side by side
+])
+def test_bwd_grads_stage(B, Hq, Hkv, N, d, causal):
+    """preprocess + attn_bwd_grads against the oracle (bf16 tolerances)."""
+    cfg = W.TrainConfig("grads", "bf16", B, Hq, Hkv, N, d, seed=21)
+    print(f"\n[case] grads B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}", flush=True)
+    x = W.train_inputs(cfg)
+    g = {n: _to_dev(a, "bf16") for n, a in x.items()}
+    o, lse = attn.attn_fwd(g["q"], g["k"], g["v"], causal=causal, scale=cfg.scale)
+    delta = attn.attn_bwd_preprocess(o, g["dout"])
+    dq, dk, dv = attn.attn_bwd_grads(g["q"], g["k"], g["v"], lse, g["dout"], delta, causal,
+                                     cfg.scale)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    ref = _oracle_fwd_bwd(x, causal, cfg.scale)
+    _check(got, ref, "bf16", label=f"grads B{B} H{Hq}x{Hkv} N{N} d{d} c{int(causal)}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", ["stages", "grads", "attn_bwd"])
+def test_graph_replay_matches_eager(mode, d):
     """The whole path captured in a HIP graph: every replay equals the eager run.
-    With whole_bwd the backward is attn_bwd, whose dQ kernel runs on the
-    library's auxiliary stream (a fork/join inside the capture)."""
-    cfg = W.TrainConfig("graph", "bf16", 1, 8, 2, 320, 128, seed=11)
+    The backward is the preprocess then the dK/dV and dQ stages ("stages"),
+    attn_bwd_grads ("grads") or attn_bwd; at d = 128 the latter two run the dQ
+    kernel on the library's auxiliary stream (a fork/join inside the capture),
+    at d = 64 they are one launch after a zero-fill launch of dk and dv."""
+    cfg = W.TrainConfig("graph", "bf16", 1, 8, 2, 320, d, seed=11)
     x = W.train_inputs(cfg)
     g = {n: _to_dev(a, "bf16") for n, a in x.items()}
     dc = W.DecodeConfig("graphdec", "bf16", 1, 8, 2, 700, 128, 5, seed=12)
@@ -288,9 +313,12 @@ def test_graph_replay_matches_eager(whole_bwd):
     def step():
         attn.attn_fwd(g["q"], g["k"], g["v"], True, cfg.scale, o=o, lse=lse)
         attn.attn_bwd_preprocess(o, g["dout"], delta=delta)
-        if whole_bwd:
+        if mode == "attn_bwd":
             attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], True, cfg.scale, dq=dq, dk=dk,
                           dv=dv, workspace=ws)
+        elif mode == "grads":
+            attn.attn_bwd_grads(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale,
+                                dq=dq, dk=dk, dv=dv)
         else:
             attn.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale,
                                dk=dk, dv=dv)
