@@ -70,9 +70,11 @@ class Oracle:
         lib.oracle_lse_merge.argtypes = [i, i, i, i, _D, _D, _D, _D]
         lib.oracle_state_combine.argtypes = [i, d, d, _D, d, d, _D, _D, _D, _D]
         lib.oracle_state_combine.restype = None
+        lib.oracle_attn_decode_append.argtypes = [i, i, i, i, i, d, _D, _D, _D, _D, _D,
+                                                  ctypes.POINTER(ctypes.c_int), _D, _D]
         for name in ("oracle_attn_fwd", "oracle_attn_bwd", "oracle_attn_fwd_dual",
                      "oracle_dual_xsinx", "oracle_attn_decode", "oracle_lse_merge",
-                     "oracle_abi_version", "oracle_num_threads"):
+                     "oracle_attn_decode_append", "oracle_abi_version", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -128,6 +130,24 @@ class Oracle:
         _check(self.lib.oracle_attn_decode(B, Hq, Hkv, L, d, float(scale), int(n_splits),
                                            _p(q), _p(kc), _p(vc), _p(po), _p(pl)), "attn_decode")
         return po, pl
+
+    def attn_decode_append(self, q, k_new, v_new, k_cache, v_cache, seq_lens, scale: float):
+        """One decode step with cache append: q [B,Hq,d], k_new/v_new [B,Hkv,d], caches
+        [B,Hkv,Lcap,d], seq_lens [B] -> (o [B,Hq,d], lse [B,Hq], k_cache', v_cache') with the
+        caches returned as updated copies (the inputs are not modified)."""
+        q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+        kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+        lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+        B, Hq, d = q.shape
+        _, Hkv, Lcap, _ = kc.shape
+        if kn.shape != (B, Hkv, d) or vn.shape != (B, Hkv, d) or lens.shape != (B,):
+            raise ValueError("k_new, v_new or seq_lens shape mismatch")
+        o = np.empty((B, Hq, d))
+        lse = np.empty((B, Hq))
+        _check(self.lib.oracle_attn_decode_append(
+            B, Hq, Hkv, Lcap, d, float(scale), _p(q), _p(kn), _p(vn), _p(kc), _p(vc),
+            lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _p(o), _p(lse)), "attn_decode_append")
+        return o, lse, kc, vc
 
     def lse_merge(self, part_o, part_lse):
         """part_o [B,Hq,S,d], part_lse [B,Hq,S] -> (o [B,Hq,d], lse [B,Hq])."""
@@ -185,6 +205,10 @@ def dual_xsinx(x):
 
 def attn_decode(q, k_cache, v_cache, scale, n_splits):
     return default().attn_decode(q, k_cache, v_cache, scale, n_splits)
+
+
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale):
+    return default().attn_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale)
 
 
 def lse_merge(part_o, part_lse):

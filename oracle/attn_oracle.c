@@ -469,6 +469,84 @@ void oracle_state_combine(int d, double m1, double l1, const double *a1,
     *m = mm;
 }
 
+/* ------------------------------------------------------------------------ */
+/* One decode step against a growing cache ("RustingBrain" docs, "Generating */
+/* text": after the prefill, each new token's key and value join the cache    */
+/* and the token costs one row of attention over it).  For sequence b with   */
+/* n = seq_lens[b] tokens already cached (0 <= n < Lcap):                    */
+/*   1. append: the new token's key and value are written at cache row n of */
+/*      every key/value head;                                                */
+/*   2. each query head h (kv head g = h / (Hq/Hkv)) attends over the n + 1  */
+/*      keys 0..n, all visible (the token sits after the cache):             */
+/*      s_j = scale <q, k_j>, m = max s_j, l = sum exp(s_j - m),             */
+/*      o = sum exp(s_j - m) v_j / l, lse = m + ln l.                        */
+/* A length outside [0, Lcap) is reported, not clamped (reading; the pages   */
+/* are silent): that sequence's cache is left untouched and its o and lse    */
+/* are NaN.                                                                  */
+/* q : [B][Hq][d]   k_new, v_new : [B][Hkv][d]   kc, vc : [B][Hkv][Lcap][d]  */
+/* seq_lens : [B]   o : [B][Hq][d]   lse : [B][Hq]                           */
+/* Parity: pinned (closed forms at n = 0 and for identical keys, equality    */
+/* with the last row of a causal forward, the cache rows after the append,   */
+/* rows past n without influence, invalid lengths).                          */
+/* ------------------------------------------------------------------------ */
+int oracle_attn_decode_append(int B, int Hq, int Hkv, int Lcap, int d, double scale,
+                              const double *q, const double *k_new, const double *v_new,
+                              double *kc, double *vc, const int *seq_lens, double *o,
+                              double *lse)
+{
+    if (bad_shape(B, Hq, Hkv, 1, Lcap, d)) return ORACLE_BAD_ARG;
+    int G = Hq / Hkv;
+    double *e = (double *)malloc(sizeof(double) * (size_t)Lcap);
+    if (!e) return ORACLE_NOMEM;
+    for (int b = 0; b < B; ++b) {
+        long n = seq_lens[b];
+        if (n < 0 || n >= Lcap) {
+            for (int h = 0; h < Hq; ++h) {
+                for (int c = 0; c < d; ++c) o[((size_t)b * Hq + h) * d + c] = NAN;
+                lse[(size_t)b * Hq + h] = NAN;
+            }
+            continue;
+        }
+        /* step 1: append */
+        for (int g = 0; g < Hkv; ++g) {
+            double *krow = kc + (((size_t)b * Hkv + g) * (size_t)Lcap + n) * d;
+            double *vrow = vc + (((size_t)b * Hkv + g) * (size_t)Lcap + n) * d;
+            for (int c = 0; c < d; ++c) {
+                krow[c] = k_new[((size_t)b * Hkv + g) * d + c];
+                vrow[c] = v_new[((size_t)b * Hkv + g) * d + c];
+            }
+        }
+        /* step 2: one row of attention over keys 0..n */
+        for (int h = 0; h < Hq; ++h) {
+            int g = h / G;
+            const double *qh = q + ((size_t)b * Hq + h) * d;
+            const double *kg = kc + ((size_t)b * Hkv + g) * (size_t)Lcap * d;
+            const double *vg = vc + ((size_t)b * Hkv + g) * (size_t)Lcap * d;
+            double m = -INFINITY;
+            for (long j = 0; j <= n; ++j) {
+                double sc = 0.0;
+                for (int c = 0; c < d; ++c) sc += qh[c] * kg[j * d + c];
+                e[j] = scale * sc;
+                if (e[j] > m) m = e[j];
+            }
+            double l = 0.0;
+            for (long j = 0; j <= n; ++j) {
+                e[j] = exp(e[j] - m);
+                l += e[j];
+            }
+            double *oh = o + ((size_t)b * Hq + h) * d;
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (long j = 0; j <= n; ++j) acc += e[j] * vg[j * d + c];
+                oh[c] = acc / l;
+            }
+            lse[(size_t)b * Hq + h] = m + log(l);
+        }
+    }
+    free(e);
+    return ORACLE_OK;
+}
+
 int oracle_abi_version(void) { return 1; }
 
 /* Number of host threads the parallel loops above use. */

@@ -319,6 +319,89 @@ def test_decode_equals_last_causal_row():
     np.testing.assert_allclose(ld, lse[:, :, -1], rtol=1e-13, atol=1e-14)
 
 
+# --------------------------------------------------------------------------
+# one decode step with cache append and per-sequence lengths
+# --------------------------------------------------------------------------
+
+def _append_inputs(B, Hq, Hkv, Lcap, d, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Hq, d)), rng.standard_normal((B, Hkv, d)),
+            rng.standard_normal((B, Hkv, d)), rng.standard_normal((B, Hkv, Lcap, d)),
+            rng.standard_normal((B, Hkv, Lcap, d)))
+
+
+def test_append_first_token_closed_form():
+    """n = 0: the token attends to itself only, so o = v_new and lse = scale q.k_new."""
+    B, Hq, Hkv, Lcap, d = 2, 6, 3, 5, 4
+    q, kn, vn, kc, vc = _append_inputs(B, Hq, Hkv, Lcap, d, 31)
+    o, lse, _, _ = oracle.attn_decode_append(q, kn, vn, kc, vc, [0, 0], 0.7)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(o[b, h], vn[b, h // G], rtol=1e-15, atol=1e-15)
+            assert abs(lse[b, h] - 0.7 * float(q[b, h] @ kn[b, h // G])) < 1e-14
+
+
+def test_append_identical_keys_closed_form():
+    """All n + 1 keys equal: uniform weights, o = mean of the values, lse = s + ln(n + 1)."""
+    B, Hq, Hkv, Lcap, d, n = 1, 2, 1, 9, 3, 6
+    q, kn, vn, kc, vc = _append_inputs(B, Hq, Hkv, Lcap, d, 32)
+    kc[:] = kn[:, :, None, :]
+    o, lse, kc2, vc2 = oracle.attn_decode_append(q, kn, vn, kc, vc, [n], 1.3)
+    mean_v = (vc[0, 0, :n].sum(axis=0) + vn[0, 0]) / (n + 1)
+    for h in range(Hq):
+        np.testing.assert_allclose(o[0, h], mean_v, rtol=1e-13, atol=1e-14)
+        assert abs(lse[0, h] - (1.3 * float(q[0, h] @ kn[0, 0]) + math.log(n + 1))) < 1e-13
+
+
+def test_append_equals_last_causal_row_per_sequence():
+    """Sequence b with n_b cached tokens: the step's output is the last row of a
+    causal forward over the n_b + 1 tokens (cache rows then the new token)."""
+    B, Hq, Hkv, Lcap, d = 3, 4, 2, 12, 8
+    q, kn, vn, kc, vc = _append_inputs(B, Hq, Hkv, Lcap, d, 33)
+    lens = [11, 0, 5]
+    o, lse, _, _ = oracle.attn_decode_append(q, kn, vn, kc, vc, lens, 0.45)
+    for b, n in enumerate(lens):
+        K = np.concatenate([kc[b:b + 1, :, :n], kn[b:b + 1, :, None]], axis=2)
+        V = np.concatenate([vc[b:b + 1, :, :n], vn[b:b + 1, :, None]], axis=2)
+        Q = np.zeros((1, Hq, n + 1, d))
+        Q[0, :, n] = q[b]
+        of, lf = oracle.attn_fwd(Q, K, V, True, 0.45)
+        np.testing.assert_allclose(o[b], of[0, :, n], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[b], lf[0, :, n], rtol=1e-13, atol=1e-14)
+        # and against numpy's own softmax, head by head
+        for h in range(Hq):
+            sc = 0.45 * (K[0, h // (Hq // Hkv)] @ q[b, h])
+            w = np.exp(sc - logsumexp(sc))
+            np.testing.assert_allclose(o[b, h], w @ V[0, h // (Hq // Hkv)], rtol=1e-12, atol=1e-13)
+
+
+def test_append_writes_row_n_only_and_rows_past_n_are_ignored():
+    B, Hq, Hkv, Lcap, d = 2, 2, 2, 10, 4
+    q, kn, vn, kc, vc = _append_inputs(B, Hq, Hkv, Lcap, d, 34)
+    lens = [3, 9]
+    o, lse, kc2, vc2 = oracle.attn_decode_append(q, kn, vn, kc, vc, lens, 0.5)
+    for b, n in enumerate(lens):
+        exp_k, exp_v = kc[b].copy(), vc[b].copy()
+        exp_k[:, n], exp_v[:, n] = kn[b], vn[b]
+        assert np.array_equal(kc2[b], exp_k) and np.array_equal(vc2[b], exp_v)
+    # rows past n (and the stale row n) have no influence
+    kp, vp = kc.copy(), vc.copy()
+    kp[0, :, 3:], vp[0, :, 3:] = np.nan, 1e300
+    o2, l2, _, _ = oracle.attn_decode_append(q, kn, vn, kp, vp, lens, 0.5)
+    np.testing.assert_array_equal(o2[0], o[0])
+    np.testing.assert_array_equal(l2[0], lse[0])
+
+
+def test_append_invalid_length_is_reported():
+    B, Hq, Hkv, Lcap, d = 3, 2, 1, 6, 4
+    q, kn, vn, kc, vc = _append_inputs(B, Hq, Hkv, Lcap, d, 35)
+    o, lse, kc2, vc2 = oracle.attn_decode_append(q, kn, vn, kc, vc, [-1, 6, 2], 0.5)
+    assert np.all(np.isnan(o[:2])) and np.all(np.isnan(lse[:2]))
+    assert np.array_equal(kc2[:2], kc[:2]) and np.array_equal(vc2[:2], vc[:2])
+    assert np.all(np.isfinite(o[2])) and np.all(np.isfinite(lse[2]))
+
+
 def test_merge_order_independent_and_identity():
     rng = np.random.default_rng(23)
     B, Hq, S, d = 1, 3, 9, 5

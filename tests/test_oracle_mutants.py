@@ -35,8 +35,14 @@ MUTANTS = [
     ("dv_transposed_P", "double s = dS[i * Nk + j], p = P[i * Nk + j];",
      "double s = dS[i * Nk + j], p = P[j * Nk + i];", 1),
     ("dq_wrong_operand", "dqh[i * d + c] += s * kg[j * d + c];", "dqh[i * d + c] += s * vg[j * d + c];", 1),
-    ("head_map_interleaved", "int g = h / G;", "int g = h % Hkv;", 4),
+    ("head_map_interleaved", "int g = h / G;", "int g = h % Hkv;", 5),
     ("decode_chunk_short", "long j0 = (long)s * C, j1 = j0 + C;", "long j0 = (long)s * C, j1 = j0 + C - 1;", 1),
+    ("append_drops_new_key", "for (long j = 0; j <= n; ++j) {\n                double sc = 0.0;",
+     "for (long j = 0; j < n; ++j) {\n                double sc = 0.0;", 1),
+    ("append_wrong_row", "double *krow = kc + (((size_t)b * Hkv + g) * (size_t)Lcap + n) * d;",
+     "double *krow = kc + (((size_t)b * Hkv + g) * (size_t)Lcap + (n + 1 < Lcap ? n + 1 : n)) * d;", 1),
+    ("append_value_from_key", "vrow[c] = v_new[((size_t)b * Hkv + g) * d + c];",
+     "vrow[c] = k_new[((size_t)b * Hkv + g) * d + c];", 1),
     ("merge_not_normalised", "for (int c = 0; c < d; ++c) oo[c] /= W;", "", 1),
     ("merge_lse_drops_max", "lse[(size_t)b * Hq + h] = M + log(W);", "lse[(size_t)b * Hq + h] = log(W);", 1),
     ("combine_wrong_weight", "*l = l1 * w1 + l2 * w2;", "*l = l1 * w1 + l2 * w1;", 1),
@@ -153,6 +159,23 @@ def battery(O) -> list:
         ok = ok and np.allclose(od, o_full[:, :, -1], rtol=1e-11, atol=1e-12) \
             and np.allclose(ld, l_full[:, :, -1], rtol=1e-11, atol=1e-12)
     check("decode", ok)
+
+    # decode step with append: n = 0 closed form, last causal row, cache rows
+    Bq, Hq2, Hkv2, Lc, d2 = 2, 4, 2, 8, 4
+    qa = rng.standard_normal((Bq, Hq2, d2))
+    kn, vn = rng.standard_normal((Bq, Hkv2, d2)), rng.standard_normal((Bq, Hkv2, d2))
+    kca, vca = rng.standard_normal((Bq, Hkv2, Lc, d2)), rng.standard_normal((Bq, Hkv2, Lc, d2))
+    oa, la, kc2, vc2 = O.attn_decode_append(qa, kn, vn, kca, vca, [0, 5], 0.6)
+    ok = np.allclose(oa[0], np.repeat(vn[0], 2, axis=0), rtol=1e-14, atol=1e-14)
+    K = np.concatenate([kca[1:2, :, :5], kn[1:2, :, None]], axis=2)
+    V = np.concatenate([vca[1:2, :, :5], vn[1:2, :, None]], axis=2)
+    for h in range(Hq2):
+        sc = 0.6 * (K[0, h // 2] @ qa[1, h])
+        ok = ok and np.allclose(oa[1, h], np.exp(sc - logsumexp(sc)) @ V[0, h // 2], rtol=1e-12)
+        ok = ok and abs(la[1, h] - logsumexp(sc)) < 1e-12
+    ok = ok and np.array_equal(kc2[1, :, 5], kn[1]) and np.array_equal(vc2[1, :, 5], vn[1]) \
+        and np.array_equal(kc2[1, :, 6:], kca[1, :, 6:]) and np.array_equal(kc2[0, :, 1:], kca[0, :, 1:])
+    check("decode_append", ok)
 
     # the online monoid: folds of singletons equal the materialised softmax
     s = rng.standard_normal(12) * 2
