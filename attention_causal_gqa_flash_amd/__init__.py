@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_grads", "attn_bwd_grads_single_launch",
+           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.argtypes = [i, i, i, i, i, i, i, f] + [p] * 8
     L.attn_bwd_grads.argtypes = [i, i, i, i, i, i, i, f] + [p] * 10
     L.attn_bwd_grads.restype = i
+    L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
+    L.attn_decode_append.restype = i
     L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
     L.attn_bwd_grads_single_launch.restype = i
     L.attn_bwd_dq.restype = i
@@ -254,6 +256,36 @@ def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, 
 def attn_bwd_grads_single_launch(dtype_code: int, N: int, d: int, scale: float) -> bool:
     """Whether attn_bwd_grads runs as one kernel for this dtype code, N, d, scale."""
     return bool(lib().attn_bwd_grads_single_launch(int(dtype_code), int(N), int(d), float(scale)))
+
+
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, n_splits: int,
+                       scale: float | None = None, part_o=None, part_lse=None, o=None, lse=None,
+                       stream=None):
+    """One decode step with cache append.  q [B,Hq,d], k_new/v_new [B,Hkv,d], caches
+    [B,Hkv,L_cap,d] (row seq_lens[b] is written), seq_lens int32 [B] on the device
+    -> (o [B,Hq,d], lse [B,Hq]) f32."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError(f"seq_lens must be int32 of shape ({B},)")
+    if part_o is None:
+        part_o = torch.empty((B, Hq, n_splits, d), device=q.device, dtype=torch.float32)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, n_splits), device=q.device, dtype=torch.float32)
+    if o is None:
+        o = torch.empty((B, Hq, d), device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
+    rc = lib().attn_decode_append(_dtype_code(q), B, Hq, Hkv, L_cap, d, scale, int(n_splits),
+                                  _ptr(_dev(q, "q")), _ptr(_dev(k_new, "k_new")),
+                                  _ptr(_dev(v_new, "v_new")), _ptr(_dev(k_cache, "k_cache")),
+                                  _ptr(_dev(v_cache, "v_cache")), _ptr(_dev(seq_lens, "seq_lens")),
+                                  _ptr(_dev(part_o, "part_o")), _ptr(_dev(part_lse, "part_lse")),
+                                  _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    _check("attn_decode_append", rc)
+    return o, lse
 
 
 def attn_decode(q, k_cache, v_cache, n_splits: int, scale: float | None = None,

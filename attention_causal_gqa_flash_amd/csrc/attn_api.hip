@@ -330,6 +330,29 @@ attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int
     return hip_status(attn::lse_merge(B, Hq, n_splits, d, part_o, part_lse, o, lse, st));
 }
 
+attn_status attn_decode_append(attn_dtype dt, int B, int Hq, int Hkv, int L_cap, int d,
+                               float scale, int n_splits, const void *q, const void *k_new,
+                               const void *v_new, void *k_cache, void *v_cache,
+                               const int *seq_lens, float *part_o, float *part_lse, float *o,
+                               float *lse, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, L_cap, d, scale);
+    if (s != ATTN_OK) return s;
+    if (n_splits < 1) return ATTN_ERR_INVALID_ARG;
+    if ((long)n_splits > kMaxGridX || (long)Hkv > kMaxGridYZ) return ATTN_ERR_UNSUPPORTED;
+    if (!attn::decode_mfma_supported(dt, d, Hq / Hkv) || scale == 0.f) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) ||
+        !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    if (seq_lens == nullptr || ((uintptr_t)seq_lens & 3) != 0) return ATTN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (attn::decode_append_mfma(B, Hq, Hkv, L_cap, d, scale, n_splits, q, k_new, v_new, k_cache,
+                                 v_cache, seq_lens, part_o, part_lse, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return hip_status(attn::lse_merge(B, Hq, n_splits, d, part_o, part_lse, o, lse, st));
+}
+
 attn_status attn_lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
                            const float *part_lse, float *o, float *lse, void *stream)
 {

@@ -23,6 +23,12 @@
 //     ds_read_b64_tr_b16;
 //   * the 8 waves' running states (max, sum, output) merge through LDS with the
 //     associative combine, and the workgroup writes (part_o, part_lse).
+// The append form (one decode step of a batch of sequences of their own
+// lengths, "Generating text": each new token's key and value join the cache)
+// reads sequence b's length n from device memory, attends over the n + 1 keys
+// 0..n -- key n is the new token's, taken straight from k_new / v_new -- and
+// the split-0 workgroup of each (kv head, sequence) writes the new row into the
+// cache; no workgroup reads cache row n, so the write races with no read.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -39,11 +45,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool APPEND>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, float *__restrict__ part_o, float *__restrict__ part_lse,
-    int Hq, int Hkv, int L, float scale, int n_splits)
+    const uint16_t *__restrict__ q, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
+    float *__restrict__ part_o, float *__restrict__ part_lse, int Hq, int Hkv, int L, float scale,
+    int n_splits, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    const int *__restrict__ seq_lens)
 {
     constexpr int KS = D / 32;            // k-steps over the head dim (32 per MFMA)
     constexpr int DB = D / 16;            // 16-column blocks of the output
@@ -65,11 +72,41 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(
     // scores are x = q.k; the softmax runs on x * c2 in base 2 (c2 may be negative)
     const float c2 = scale * kLog2e;
 
-    const long C = ((long)L + n_splits - 1) / n_splits;
+    // keys attended: all L cached ones, or (append) the n + 1 of sequence b
+    long Lk = L, nb = -1;
+    const uint16_t *Kn = nullptr, *Vn = nullptr;
+    if constexpr (APPEND) {
+        nb = seq_lens[b];
+        if (nb < 0 || nb >= L) {
+            // invalid length: nothing is written to the cache; partials that the
+            // merge turns into NaN (lse +inf makes every weight inf - inf)
+            for (int t = tid; t < G * D; t += 512) {
+                const size_t ob = ((size_t)b * Hq + g * G + t / D) * n_splits + s;
+                part_o[ob * D + t % D] = NAN;
+                if (t % D == 0) part_lse[ob] = INFINITY;
+            }
+            return;
+        }
+        Lk = nb + 1;
+        Kn = k_new + ((size_t)b * Hkv + g) * D;
+        Vn = v_new + ((size_t)b * Hkv + g) * D;
+        if (s == 0 && wave == 0 && lane < 2 * (D / 8)) {
+            // the new row into the cache, 16 bytes per lane (K: lanes 0..D/8-1)
+            const int c = 8 * (lane % (D / 8));
+            const uint16_t *src = lane < D / 8 ? Kn : Vn;
+            uint16_t *dst = (lane < D / 8 ? kc : vc) + (((size_t)b * Hkv + g) * (size_t)L + nb) * D;
+            *(uint4 *)(dst + c) = *(const uint4 *)(src + c);
+        }
+    }
+
+    const long C = (Lk + n_splits - 1) / n_splits;
     const long j0 = (long)s * C;
-    const long j1 = min((long)L, j0 + C);
+    const long j1 = min(Lk, j0 + C);
     const uint16_t *Kg = kc + ((size_t)b * Hkv + g) * (size_t)L * D;
     const uint16_t *Vg = vc + ((size_t)b * Hkv + g) * (size_t)L * D;
+    // row `key` of the keys attended (append: key n is the new token's)
+    auto krow = [&](long key) { return (APPEND && key == nb) ? Kn : Kg + (size_t)key * D; };
+    auto vrow = [&](long key) { return (APPEND && key == nb) ? Vn : Vg + (size_t)key * D; };
 
     // q^T operand: lane holds head l16 (rows past G read head G-1 and are never
     // written out), dims 32ks + 8grp .. +7.  Loaded without a branch and
@@ -95,18 +132,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(
         uint4 kraw[2][KS];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const long key = min(kb0 + 16 * kb + l16, j1 - 1);
+            const uint16_t *kr = krow(min(kb0 + 16 * kb + l16, j1 - 1));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kraw[kb][ks] = *(const uint4 *)(Kg + (size_t)key * D + 32 * ks + 8 * grp);
+            for (int ks = 0; ks < KS; ++ks) kraw[kb][ks] = *(const uint4 *)(kr + 32 * ks + 8 * grp);
         }
         uint4 vraw[VCH];
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = lane + 64 * i;
             const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            const long key = min(kb0 + row, j1 - 1);
-            vraw[i] = *(const uint4 *)(Vg + (size_t)key * D + col);
+            vraw[i] = *(const uint4 *)(vrow(min(kb0 + row, j1 - 1)) + col);
         }
         // ---- scores: S^T (16 keys x 16 heads) for the two 16-key halves ----
         f32x4 sacc[2];
@@ -224,15 +259,37 @@ hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, 
                              const void *q, const void *kc, const void *vc, float *part_o,
                              float *part_lse, hipStream_t st)
 {
+    // the plain form never writes the caches
+    uint16_t *k = const_cast<uint16_t *>((const uint16_t *)kc);
+    uint16_t *v = const_cast<uint16_t *>((const uint16_t *)vc);
     dim3 grid(n_splits, Hkv, B);
     if (d == 128)
-        hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, dim3(512), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, Hq, Hkv, L,
-                           scale, n_splits);
+        hipLaunchKernelGGL((decode_mfma_kernel<128, false>), grid, dim3(512), 0, st, (const uint16_t *)q,
+                           k, v, part_o, part_lse, Hq, Hkv, L, scale, n_splits, nullptr, nullptr,
+                           nullptr);
     else if (d == 64)
-        hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, dim3(512), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)kc, (const uint16_t *)vc, part_o, part_lse, Hq, Hkv, L,
-                           scale, n_splits);
+        hipLaunchKernelGGL((decode_mfma_kernel<64, false>), grid, dim3(512), 0, st, (const uint16_t *)q,
+                           k, v, part_o, part_lse, Hq, Hkv, L, scale, n_splits, nullptr, nullptr,
+                           nullptr);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t decode_append_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
+                              const void *q, const void *k_new, const void *v_new, void *kc,
+                              void *vc, const int *seq_lens, float *part_o, float *part_lse,
+                              hipStream_t st)
+{
+    dim3 grid(n_splits, Hkv, B);
+    if (d == 128)
+        hipLaunchKernelGGL((decode_mfma_kernel<128, true>), grid, dim3(512), 0, st, (const uint16_t *)q,
+                           (uint16_t *)kc, (uint16_t *)vc, part_o, part_lse, Hq, Hkv, L, scale,
+                           n_splits, (const uint16_t *)k_new, (const uint16_t *)v_new, seq_lens);
+    else if (d == 64)
+        hipLaunchKernelGGL((decode_mfma_kernel<64, true>), grid, dim3(512), 0, st, (const uint16_t *)q,
+                           (uint16_t *)kc, (uint16_t *)vc, part_o, part_lse, Hq, Hkv, L, scale,
+                           n_splits, (const uint16_t *)k_new, (const uint16_t *)v_new, seq_lens);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

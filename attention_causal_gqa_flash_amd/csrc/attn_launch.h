@@ -65,6 +65,11 @@ bool decode_mfma_supported(int dt, int d, int G);
 hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
                              const void *q, const void *kc, const void *vc, float *part_o,
                              float *part_lse, hipStream_t st);
+// One decode step of B sequences of their own lengths with cache append.
+hipError_t decode_append_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
+                              const void *q, const void *k_new, const void *v_new, void *kc,
+                              void *vc, const int *seq_lens, float *part_o, float *part_lse,
+                              hipStream_t st);
 hipError_t lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
                      const float *part_lse, float *o, float *lse, hipStream_t st);
 

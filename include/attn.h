@@ -213,6 +213,36 @@ attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int
                                const void *v_cache, float *part_o, float *part_lse, float *o,
                                float *lse, void *stream);
 
+/*
+ * attn_decode_append -- one decode step of B sequences of their own lengths
+ *   against caches that grow by one token per step.  Source: RustingBrain
+ *   docs, "Generating text" (after the prefill each new token's key and value
+ *   join the cache, and the token costs one row of attention over it); the
+ *   split and merge are those of attn_decode / attn_lse_merge.
+ *   For sequence b with n = seq_lens[b] tokens already cached:
+ *     1. k_new[b][g] and v_new[b][g] are written to cache row n of every kv
+ *        head g (the caller then counts the sequence as n + 1 long);
+ *     2. every query head h of the group attends over the n + 1 keys 0..n
+ *        (all visible: the token sits after the cache), split into n_splits
+ *        chunks of ceil((n + 1) / n_splits) keys, then merged:
+ *        o[b][h] = softmax(scale q.K^T) V, lse[b][h] = log-sum-exp.
+ *   q [B][Hq][d], k_new / v_new [B][Hkv][d]: dtype dt (bf16 only; d 64 or 128,
+ *   Hq/Hkv <= 16, scale != 0; anything else returns ATTN_ERR_UNSUPPORTED).
+ *   k_cache / v_cache [B][Hkv][L_cap][d] dt: read at rows < n, written at row
+ *   n only.  seq_lens [B] int32 device memory, read only (4-byte aligned).
+ *   part_o [B][Hq][n_splits][d], part_lse [B][Hq][n_splits] f32 scratch as in
+ *   attn_decode (chunks past n hold (0, -inf)); o [B][Hq][d], lse [B][Hq] f32.
+ *   All buffers caller-owned device memory; the call enqueues two launches on
+ *   `stream` (the decode kernel, then the merge) and allocates nothing.
+ *   A length outside [0, L_cap) is not an error the host can see: that
+ *   sequence's cache is left untouched and its o and lse come out NaN.
+ */
+attn_status attn_decode_append(attn_dtype dt, int B, int Hq, int Hkv, int L_cap, int d,
+                               float scale, int n_splits, const void *q, const void *k_new,
+                               const void *v_new, void *k_cache, void *v_cache,
+                               const int *seq_lens, float *part_o, float *part_lse, float *o,
+                               float *lse, void *stream);
+
 /* Human-readable name of a status code (a static string). */
 const char *attn_status_str(attn_status s);
 

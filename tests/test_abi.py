@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
-                     "attn_bwd_grads_single_launch", "attn_decode", "attn_lse_merge",
+                     "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
+                     "attn_lse_merge",
                      "attn_status_str", "attn_abi_version"):
         assert required in names
 
@@ -160,6 +161,27 @@ def test_bwd_stage_refusals(L):
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
         ptrs[which] = NUL
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
+
+
+def test_decode_append_refusals(L):
+    def call(dt=1, B=2, Hq=8, Hkv=2, Lc=64, d=128, scale=0.088, S=4, ptrs=None, lens=P):
+        ptrs = ptrs or [P] * 5
+        return L.attn_decode_append(dt, B, Hq, Hkv, Lc, d, scale, S, *ptrs, lens, P, P, P, P, NUL)
+    assert call(B=0) == INVALID
+    assert call(Hq=6, Hkv=4) == INVALID
+    assert call(S=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(dt=0) == UNSUPPORTED                 # f32: no append kernel
+    assert call(d=32) == UNSUPPORTED
+    assert call(scale=0.0) == UNSUPPORTED
+    assert call(Hq=34, Hkv=2) == UNSUPPORTED         # group of 17 heads
+    assert call(lens=NUL) == INVALID
+    assert call(lens=ctypes.c_void_p(0x10002)) == INVALID
+    for which in range(5):
+        ptrs = [P] * 5
+        ptrs[which] = MIS
+        assert call(ptrs=ptrs) == INVALID
+    assert L.attn_decode_append(1, 2, 8, 2, 64, 128, 0.088, 4, *([P] * 6), P, P, P, MIS, NUL) == INVALID
 
 
 def test_bwd_grads_single_launch_query(L):

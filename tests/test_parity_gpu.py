@@ -212,6 +212,91 @@ def test_decode_shapes(B, Hq, Hkv, L, d, S, dtype):
     assert float(np.abs(o.cpu().numpy() - full_o[:, :, 0]).max()) <= tol_o
 
 
+# ---------------------------------------------------------------------------
+# one decode step with cache append (per-sequence lengths)
+# ---------------------------------------------------------------------------
+
+def _append_inputs(B, Hq, Hkv, Lc, d, seed):
+    """bf16-representable draws (float64 arrays) for q, k_new, v_new and the caches."""
+    rng = np.random.default_rng(seed)
+    draw = lambda *sh: torch.from_numpy(rng.standard_normal(sh).astype(np.float32)).to(
+        torch.bfloat16).to(torch.float64).numpy()
+    return dict(q=draw(B, Hq, d), k_new=draw(B, Hkv, d), v_new=draw(B, Hkv, d),
+                k_cache=draw(B, Hkv, Lc, d), v_cache=draw(B, Hkv, Lc, d))
+
+
+def _run_append(x, lens, S, scale, dev=None):
+    dev = dev or {n: _to_dev(a, "bf16") for n, a in x.items()}
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    B, Hq, d = x["q"].shape
+    po = torch.empty((B, Hq, S, d), device="cuda")
+    pl = torch.empty((B, Hq, S), device="cuda")
+    o, lse = attn.attn_decode_append(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"],
+                                     dev["v_cache"], sl, S, scale, part_o=po, part_lse=pl)
+    torch.cuda.synchronize()
+    return dev, o.cpu().numpy(), lse.cpu().numpy(), po.cpu().numpy(), pl.cpu().numpy()
+
+
+APPEND = [
+    (4, 32, 8, 600, 128, 16, [0, 1, 299, 599]),
+    (3, 12, 4, 257, 64, 7, [256, 100, 31]),
+    (2, 16, 1, 40, 128, 16, [2, 39]),           # more splits than keys, G = 16
+    (1, 8, 8, 4096, 64, 16, [4095]),            # full cache, G = 1
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lc,d,S,lens", APPEND,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Lc{c[3]}_d{c[4]}_S{c[5]}" for c in APPEND])
+def test_decode_append(B, Hq, Hkv, Lc, d, S, lens):
+    print(f"\n[case] decode_append B={B} Hq={Hq} Hkv={Hkv} Lc={Lc} d={d} S={S} lens={lens}", flush=True)
+    x = _append_inputs(B, Hq, Hkv, Lc, d, seed=Lc + d)
+    scale = d ** -0.5
+    dev, o, lse, po, pl = _run_append(x, lens, S, scale)
+    ro, rl, rkc, rvc = oracle.attn_decode_append(x["q"], x["k_new"], x["v_new"], x["k_cache"],
+                                                 x["v_cache"], lens, scale)
+    assert float(np.abs(o - ro).max()) <= 1e-2
+    assert float(np.abs(lse - rl).max()) <= 1e-3
+    # the cache after the append, bit for bit: row n replaced, every other row untouched
+    assert np.array_equal(dev["k_cache"].double().cpu().numpy(), rkc)
+    assert np.array_equal(dev["v_cache"].double().cpu().numpy(), rvc)
+    # the split partials: the oracle's split decode over each sequence's n + 1 keys
+    for b, n in enumerate(lens):
+        rpo, rpl = oracle.attn_decode(x["q"][b:b + 1], rkc[b:b + 1, :, :n + 1], rvc[b:b + 1, :, :n + 1],
+                                      scale, S)
+        empty = np.isneginf(rpl[0])
+        assert np.array_equal(np.isneginf(pl[b]), empty)
+        assert float(np.abs(pl[b][~empty] - rpl[0][~empty]).max()) <= 1e-3
+        assert float(np.abs(po[b] - rpo[0]).max()) <= 1e-2
+
+
+def test_decode_append_invalid_lengths_and_two_steps():
+    """Lengths outside [0, L_cap) give NaN outputs and leave that cache alone; a
+    second step (lengths + 1, new tokens) continues from the first."""
+    B, Hq, Hkv, Lc, d, S = 4, 8, 2, 50, 128, 5
+    scale = d ** -0.5
+    x = _append_inputs(B, Hq, Hkv, Lc, d, seed=5)
+    lens = [-1, 50, 7, 49]
+    dev, o, lse, _, _ = _run_append(x, lens, S, scale)
+    assert np.all(np.isnan(o[:2])) and np.all(np.isnan(lse[:2]))
+    assert np.all(np.isfinite(o[2:])) and np.all(np.isfinite(lse[2:]))
+    ro, rl, rkc, rvc = oracle.attn_decode_append(x["q"], x["k_new"], x["v_new"], x["k_cache"],
+                                                 x["v_cache"], lens, scale)
+    assert np.array_equal(dev["k_cache"].double().cpu().numpy(), rkc)
+    assert np.array_equal(dev["v_cache"].double().cpu().numpy(), rvc)
+    assert float(np.abs(o[2:] - ro[2:]).max()) <= 1e-2
+    # step 2 on the updated caches, valid lengths only
+    x2 = _append_inputs(B, Hq, Hkv, Lc, d, seed=6)
+    x2["k_cache"], x2["v_cache"] = rkc, rvc
+    lens2 = [0, 10, 8, 48]
+    dev2 = {n: _to_dev(x2[n], "bf16") for n in ("q", "k_new", "v_new")}
+    dev2["k_cache"], dev2["v_cache"] = dev["k_cache"], dev["v_cache"]
+    _, o2, l2, _, _ = _run_append(x2, lens2, S, scale, dev=dev2)
+    ro2, rl2, rkc2, rvc2 = oracle.attn_decode_append(x2["q"], x2["k_new"], x2["v_new"], rkc, rvc,
+                                                     lens2, scale)
+    assert float(np.abs(o2 - ro2).max()) <= 1e-2 and float(np.abs(l2 - rl2).max()) <= 1e-3
+    assert np.array_equal(dev2["k_cache"].double().cpu().numpy(), rkc2)
+
+
 def test_merge_all_empty():
     po = torch.zeros((1, 3, 4, 64), device="cuda")
     pl = torch.full((1, 3, 4), float("-inf"), device="cuda")
