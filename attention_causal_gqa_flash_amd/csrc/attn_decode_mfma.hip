@@ -46,7 +46,7 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 }
 
 template <int D, bool APPEND>
-__global__ __launch_bounds__(512) void decode_mfma_kernel(
+__global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
     const uint16_t *__restrict__ q, uint16_t *__restrict__ kc, uint16_t *__restrict__ vc,
     float *__restrict__ part_o, float *__restrict__ part_lse, int Hq, int Hkv, int L, float scale,
     int n_splits, const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,

@@ -91,12 +91,48 @@ class DecodeConfig:
         return kv + q + out
 
 
+@dataclass(frozen=True)
+class DecodeAppendConfig:
+    """One decode step of B sequences of their own lengths against caches of
+    capacity L_cap, appending the new token (lengths: seq_lens)."""
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    L_cap: int
+    d: int
+    n_splits: int
+    seq_lens: tuple
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def algorithmic_bytes(self) -> int:
+        """Per sequence: its n cached K and V rows and the new k, v read, the new
+        row written to both caches, q read, O (f32) and LSE (f32) written."""
+        esz = 2 if self.dtype == "bf16" else 4
+        row = self.Hkv * self.d * esz                 # one token of one cache
+        kv = sum(2 * n * row for n in self.seq_lens)
+        new = self.B * 2 * row * 2                    # k_new, v_new read; cache rows written
+        q = self.B * self.Hq * self.d * esz
+        out = self.B * self.Hq * self.d * 4 + self.B * self.Hq * 4
+        return kv + new + q + out
+
+
 C1 = TrainConfig("tiny_f32_b1_h2x1_n64_d16", "f32", 1, 2, 1, 64, 16, seed=1001)
 C2 = TrainConfig("gqa12x4_b4_n1024_d64", "bf16", 4, 12, 4, 1024, 64, seed=1002, dout_scale=0.1)
 C3_128 = TrainConfig("gqa32x8_b1_n128_d128", "bf16", 1, 32, 8, 128, 128, seed=1003)
 C3_512 = TrainConfig("gqa32x8_b1_n512_d128", "bf16", 1, 32, 8, 512, 128, seed=1003)
 C4 = TrainConfig("gqa32x8_b1_n4096_d128", "bf16", 1, 32, 8, 4096, 128, seed=1004)
 C5 = DecodeConfig("decode_gqa32x8_l4096_d128_s16", "bf16", 1, 32, 8, 4096, 128, 16, seed=1005)
+
+# 8 sequences of 512, 1024, ..., 4096 tokens after the step (a length mix over
+# the 4k context of the decode workload)
+C6 = DecodeAppendConfig("decode_append_gqa32x8_b8_lc4096_d128_s16", "bf16", 8, 32, 8, 4096, 128, 16,
+                        tuple(512 * (b + 1) - 1 for b in range(8)), seed=1006)
 
 TRAIN_CONFIGS = {c.name: c for c in (C1, C2, C3_128, C3_512, C4)}
 DECODE_CONFIGS = {C5.name: C5}
@@ -137,6 +173,19 @@ def decode_inputs(cfg: DecodeConfig, seed: int | None = None) -> dict:
     kc = _draw(rng, (cfg.B, cfg.Hkv, cfg.L, cfg.d), cfg.dtype)
     vc = _draw(rng, (cfg.B, cfg.Hkv, cfg.L, cfg.d), cfg.dtype)
     return {"q": q, "k_cache": kc, "v_cache": vc}
+
+
+def decode_append_inputs(cfg: DecodeAppendConfig, seed: int | None = None) -> dict:
+    """q [B,Hq,d], k_new / v_new [B,Hkv,d], the caches [B,Hkv,L_cap,d] as float32
+    arrays and seq_lens [B] int32."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    q = _draw(rng, (cfg.B, cfg.Hq, cfg.d), cfg.dtype)
+    kn = _draw(rng, (cfg.B, cfg.Hkv, cfg.d), cfg.dtype)
+    vn = _draw(rng, (cfg.B, cfg.Hkv, cfg.d), cfg.dtype)
+    kc = _draw(rng, (cfg.B, cfg.Hkv, cfg.L_cap, cfg.d), cfg.dtype)
+    vc = _draw(rng, (cfg.B, cfg.Hkv, cfg.L_cap, cfg.d), cfg.dtype)
+    return {"q": q, "k_new": kn, "v_new": vn, "k_cache": kc, "v_cache": vc,
+            "seq_lens": np.asarray(cfg.seq_lens, dtype=np.int32)}
 
 
 def random_train(B, Hq, Hkv, N, d, dtype="bf16", seed=0, dout_scale=1.0) -> dict:

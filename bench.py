@@ -20,6 +20,10 @@ is measured the same way (a graph of K launches of that kernel alone; the
 gradient stage `bwd_grads` is timed per attn_bwd_grads call, which includes a
 zero-fill launch of dk/dv when they are accumulated with atomics).
 
+Outside the step, `decode_append` times one decode step with cache append over
+8 sequences of their own lengths (attn_decode_append, workload
+decode_append_gqa32x8_b8_lc4096_d128_s16), rotating over 4 distinct cache pairs.
+
 Prints ONE JSON line.  `value` is the training workload's algorithmic fwd+bwd
 TFLOP/s (4*d flop per unmasked (query, key) pair forward, 10*d backward);
 `decode` gives the decode workload's GB/s of algorithmic bytes (K and V caches
@@ -51,6 +55,8 @@ def parse():
                     help="training workload name (see workloads.TRAIN_CONFIGS)")
     ap.add_argument("--decode-caches", type=int, default=24,
                     help="distinct KV caches the decode op rotates over (cold-cache reads)")
+    ap.add_argument("--append-caches", type=int, default=4,
+                    help="distinct cache pairs the decode-append measurement rotates over")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
@@ -280,11 +286,33 @@ def main():
         return lambda: attn.attn_decode_merged(qd, kc, vc, S, dcfg.scale, part_o=part_o,
                                                part_lse=part_lse, o=dec_o, lse=dec_lse)
 
+    # decode step with cache append (per-sequence lengths), outside the step:
+    # rotates over distinct cache pairs so that its reads come from HBM
+    acfg = W.C6
+    xa = W.decode_append_inputs(acfg)
+    ga = {n: torch.from_numpy(xa[n]).to(dev).to(ddt) for n in ("q", "k_new", "v_new")}
+    a_lens = torch.from_numpy(xa["seq_lens"]).to(dev)
+    ka0 = torch.from_numpy(xa["k_cache"]).to(dev).to(ddt)
+    va0 = torch.from_numpy(xa["v_cache"]).to(dev).to(ddt)
+    a_ncache = max(1, args.append_caches)
+    a_caches = [(ka0.clone(), va0.clone()) for _ in range(a_ncache)]
+    del ka0, va0
+    a_po = torch.empty((acfg.B, acfg.Hq, acfg.n_splits, acfg.d), **f32)
+    a_pl = torch.empty((acfg.B, acfg.Hq, acfg.n_splits), **f32)
+    a_o, a_lse = torch.empty((acfg.B, acfg.Hq, acfg.d), **f32), torch.empty((acfg.B, acfg.Hq), **f32)
+
+    def decode_append(i):
+        kc, vc = a_caches[i % a_ncache]
+        return lambda: attn.attn_decode_append(ga["q"], ga["k_new"], ga["v_new"], kc, vc, a_lens,
+                                               acfg.n_splits, acfg.scale, part_o=a_po,
+                                               part_lse=a_pl, o=a_o, lse=a_lse)
+
     train_op = [fwd, bwd]
     for s in range(args.warmup):
         for fn in train_op:
             fn()
         decode(s)()
+        decode_append(s)()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -295,6 +323,9 @@ def main():
     train_us = timer(torch, train_fns, K)
     dec_us = timer(torch, dec_fns, K)
     step_us = train_us + dec_us
+    app_us = timer(torch, [decode_append(s) for s in range(K)], K)
+    app_bytes = acfg.algorithmic_bytes()
+    app_gbs = app_bytes / (app_us * 1e-6) / 1e9
 
     pairs = cfg.pairs
     train_flop = cfg.fwd_flop + cfg.bwd_flop
@@ -368,6 +399,11 @@ def main():
         "decode": {"GB_per_s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "us_per_call": round(dec_us, 3), "bytes": dec_bytes, "distinct_caches": ncache,
                    "launches_per_call": 2},
+        "decode_append": {"workload": acfg.name, "GB_per_s": round(app_gbs, 1),
+                          "frac_hbm_peak": round(app_gbs / PEAK_HBM_GBS, 4),
+                          "us_per_call": round(app_us, 3), "bytes": app_bytes,
+                          "distinct_caches": a_ncache, "launches_per_call": 2,
+                          "seq_lens": list(acfg.seq_lens)},
         "kernels": kernels,
         "roofline": roof,
         "timing": ("eager launches between HIP events" if args.eager else
