@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append",
+           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.argtypes = [i, i, i, i, i, i, i, f] + [p] * 8
     L.attn_bwd_grads.argtypes = [i, i, i, i, i, i, i, f] + [p] * 10
     L.attn_bwd_grads.restype = i
+    L.attn_fwd_kv.argtypes = [i, i, i, i, i, i, i, i, f, p, p, p, p, p, p]
+    L.attn_fwd_kv.restype = i
     L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
     L.attn_decode_append.restype = i
     L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
@@ -229,6 +231,25 @@ def attn_bwd_dq(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, str
                            _ptr(_dev(delta, "delta")), _ptr(_dev(dq, "dq")), _stream(stream))
     _check("attn_bwd_dq", rc)
     return dq
+
+
+def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None, o=None, lse=None,
+                stream=None):
+    """Forward of q [B,Hq,Nq,d] against k, v [B,Hkv,Nk,d] (Nk >= Nq, queries at the last Nq
+    positions) -> (o [B,Hq,Nq,d] f32, lse [B,Hq,Nq] f32)."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    rc = lib().attn_fwd_kv(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+                           _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
+                           _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    _check("attn_fwd_kv", rc)
+    return o, lse
 
 
 def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, dk=None, dv=None,

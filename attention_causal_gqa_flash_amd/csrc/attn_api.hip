@@ -69,6 +69,16 @@ hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int N, int d, c
                                 zero_dkdv ? dv : nullptr, n, st);
 }
 
+// Forward of Nq queries against Nk >= Nq keys (arguments already validated).
+hipError_t launch_fwd(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                      float scale, const void *q, const void *k, const void *v, float *o,
+                      float *lse, hipStream_t st)
+{
+    if (use_mfma(dt, Nk, d, scale))
+        return attn::fwd_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st);
+    return attn::fwd_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st);
+}
+
 // Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
 int dkdv_split(int dt, int B, int Hq, int Hkv, int N, int d, float scale)
 {
@@ -184,13 +194,21 @@ attn_status attn_fwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
     if (s != ATTN_OK) return s;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e;
-    if (use_mfma(dt, N, d, scale))
-        e = attn::fwd_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);
-    else
-        e = attn::fwd_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, o, lse, st);
-    return hip_status(e);
+    return hip_status(launch_fwd(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse,
+                                 (hipStream_t)stream));
+}
+
+attn_status attn_fwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v, float *o,
+                        float *lse, void *stream)
+{
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nq, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_fwd(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse,
+                                 (hipStream_t)stream));
 }
 
 size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, int d)

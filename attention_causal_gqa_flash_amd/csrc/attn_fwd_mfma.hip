@@ -58,12 +58,12 @@ struct FwdState {
 
 // One 64-key tile for one wave: S^T = K Q^T, the online-softmax update and
 // O^T += V^T P^T.  With `mask` (wave-uniform: diagonal and tail tiles) keys
-// after the query row and past the sequence end are hidden.  `prefetch`
+// after the query row's position qa and past the key count Nk are hidden.  `prefetch`
 // issues the wave's NV direct copies of the next tile; they are interleaved
 // with the S^T MFMAs.
 template <int D, int NV, class Prefetch>
 __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, const uint16_t *svb,
-                                         float c2, int kv0, int qi, int N, int causal, bool mask,
+                                         float c2, int kv0, int qa, int Nk, int causal, bool mask,
                                          int lane, const Prefetch &prefetch)
 {
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     // Register r of block kb holds key kv0 + 4hf + c, c = 32kb + 8(r/4) + r%4
     // (a constant), kept iff c < lim: one compare and one select per score.
     if (mask) {
-        const int lim = (causal ? min(qi + 1, N) : N) - (kv0 + 4 * hf);
+        const int lim = (causal ? min(qa + 1, Nk) : Nk) - (kv0 + 4 * hf);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -163,7 +163,7 @@ template <int D, int KSPLIT>
 __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
-    int Hkv, int N, float scale, int causal, int nqt)
+    int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
 {
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
     constexpr int RW = 4 / KSPLIT;           // row waves
@@ -190,9 +190,12 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const int qw0 = q0 + rw * 32;           // first query row of this wave
     const int qi = qw0 + l32;               // this lane's query row
 
-    const uint16_t *Qh = Q + ((size_t)b * Hq + h) * (size_t)N * D;
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
+    // Nq queries against Nk >= Nq keys: query row i sits at key position
+    // i + off (the queries are the last Nq positions; off = 0 for self-attention)
+    const int off = Nk - Nq;
+    const uint16_t *Qh = Q + ((size_t)b * Hq + h) * (size_t)Nq * D;
+    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
     // Softmax on c2 q.k with c2 = |scale| log2(e) > 0; a negative scale is
     // carried by negating q, which is exact in bf16.
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     FwdState<D> st;
     {
         // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7] (rows past N read row N-1)
-        const int qr = min(qi, N - 1);
+        const int qr = min(qi, Nq - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 u = *(const uint4 *)(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
@@ -217,10 +220,11 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
 
-    const int kv_end = causal ? min(N, q0 + BMW) : N;
+    const int kv_end = causal ? min(Nk, q0 + off + BMW) : Nk;
     const int ntiles = (kv_end + kBN - 1) / kBN;
     // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles); both
-    // halves' first tiles hold a key every row of the query tile sees
+    // halves' first tiles hold a key every row of the query tile sees (the
+    // launcher splits only self-attention, off = 0)
     const int ntA = KSPLIT == 2 ? ntiles / 2 : 0;
     const int nsteps = ntiles - ntA;
     auto tile_of = [&](int half, int s_) { return half == 0 && KSPLIT == 2 ? s_ : ntA + s_; };
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     // Tiles move global -> LDS directly (no staging registers); rows past N
     // read as zero, their scores are masked; copies of tiles that do not
     // exist read nothing (zero-byte resources).
-    const uint32_t kv_bytes = (uint32_t)N * D * 2;
+    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
     using Copy = TileCopy<D, kBN, 4>;
     const Copy copy(wave, lane);
     auto copy_step = [&](uint16_t *skd, uint16_t *svd, int s_) {
@@ -255,10 +259,10 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
         // copies of step s+1 (branch-free, so they can interleave with MFMAs)
         auto prefetch = [&] { copy_step(skn, svn, s_ + 1); };
         const int kv0 = tile_of(kh, s_) * kBN;
-        if (valid(kh, s_) && qw0 < N && (!causal || kv0 <= qw0 + 31)) {
-            const bool mask = (causal && kv0 + kBN - 1 > qw0) || kv0 + kBN > N;
-            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi, N,
-                                                     causal, mask, lane, prefetch);
+        if (valid(kh, s_) && qw0 < Nq && (!causal || kv0 <= qw0 + off + 31)) {
+            const bool mask = (causal && kv0 + kBN - 1 > qw0 + off) || kv0 + kBN > Nk;
+            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi + off,
+                                                     Nk, causal, mask, lane, prefetch);
         } else {
             prefetch();
         }
@@ -301,9 +305,9 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    if (qi < N) {
+    if (qi < Nq) {
         const float inv = 1.f / l_tot;
-        float *orow = O + (((size_t)b * Hq + h) * N + qi) * D;
+        float *orow = O + (((size_t)b * Hq + h) * Nq + qi) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
                                                      st.oacc[db][4 * a + 2] * inv, st.oacc[db][4 * a + 3] * inv);
             }
         // lse = ln(sum exp(scale q.k)) = (m + log2 l) * ln 2
-        if (hf == 0) LSE[((size_t)b * Hq + h) * N + qi] = (st.m_run + __log2f(l_tot)) * kLn2;
+        if (hf == 0) LSE[((size_t)b * Hq + h) * Nq + qi] = (st.m_run + __log2f(l_tot)) * kLn2;
     }
 }
 
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
 
 bool mfma_supported(int dt, int d) { return dt == kBF16 && (d == 64 || d == 128); }
 
-hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                     const void *q, const void *k, const void *v, float *o, float *lse,
                     hipStream_t st)
 {
@@ -334,25 +338,25 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scal
         else
             cus = 256;
     }
-    const int nqt = (N + kBM - 1) / kBM;
+    const int nqt = (Nq + kBM - 1) / kBM;
     // Key split when the 128-row workgroups would not give every CU two
     // (d = 64; measured on MI355X, B = 4, N = 1024, 12/4 heads: 22.6 us
     // unsplit, 20.5 us split).
-    const bool split = d == 64 && (long)nqt * B * Hq < 2L * cus;
+    const bool split = d == 64 && Nq == Nk && (long)nqt * B * Hq < 2L * cus;
     auto grid_of = [&](int n_tiles) {
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     if (d == 128) {
         hipLaunchKernelGGL((fwd_mfma_kernel<128, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, N, scale, causal, nqt);
+                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 64 && !split) {
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, N, scale, causal, nqt);
+                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 64) {
-        const int nqt64 = (N + 63) / 64;
+        const int nqt64 = (Nq + 63) / 64;
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, N, scale, causal, nqt64);
+                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else {
         return hipErrorInvalidValue;
     }

@@ -24,15 +24,17 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
                                                          const T *__restrict__ v,
                                                          float *__restrict__ o,
                                                          float *__restrict__ lse, int Hq, int Hkv,
-                                                         int N, float scale, int causal)
+                                                         int Nq, int Nk, float scale, int causal)
 {
+    // Nq queries against Nk >= Nq keys; query i sits at key position i + off
     const int i = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = h / (Hq / Hkv);
-    const T *qh = q + ((size_t)b * Hq + h) * (size_t)N * D;
-    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const int row = i < N ? i : N - 1;
+    const int off = Nk - Nq;
+    const T *qh = q + ((size_t)b * Hq + h) * (size_t)Nq * D;
+    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const int row = i < Nq ? i : Nq - 1;
 
     float qr[D], acc[D];
 #pragma unroll
@@ -41,9 +43,9 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
         acc[c] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    const int jend = causal ? row + 1 : N;
+    const int jend = causal ? row + off + 1 : Nk;
     // keys are read in lock-step across the wave (broadcast loads)
-    const int wave_end = causal ? min(N, (int)(blockIdx.x * 64 + 64)) : N;
+    const int wave_end = causal ? min(Nk, (int)(blockIdx.x * 64 + 64) + off) : Nk;
     for (int j = 0; j < wave_end; ++j) {
         if (j >= jend) continue;
         const T *kj = kg + (size_t)j * D;
@@ -64,12 +66,12 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
 #pragma unroll
         for (int c = 0; c < D; ++c) acc[c] = fmaf(p, to_f32(vj[c]), acc[c]);
     }
-    if (i < N) {
-        float *oh = o + (((size_t)b * Hq + h) * N + i) * D;
+    if (i < Nq) {
+        float *oh = o + (((size_t)b * Hq + h) * Nq + i) * D;
         const float inv = 1.f / l;
 #pragma unroll
         for (int c = 0; c < D; ++c) oh[c] = acc[c] * inv;
-        lse[((size_t)b * Hq + h) * N + i] = m + logf(l);
+        lse[((size_t)b * Hq + h) * Nq + i] = m + logf(l);
     }
 }
 
@@ -432,15 +434,15 @@ __global__ __launch_bounds__(128) void lse_merge_kernel(const float *__restrict_
     if (dt == kBF16) { typedef bf16_t T; __VA_ARGS__; }            \
     else { typedef float T; __VA_ARGS__; }
 
-hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                       const void *q, const void *k, const void *v, float *o, float *lse,
-                       hipStream_t st)
+hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                       float scale, const void *q, const void *k, const void *v, float *o,
+                       float *lse, hipStream_t st)
 {
-    dim3 grid((N + 63) / 64, Hq, B);
+    dim3 grid((Nq + 63) / 64, Hq, B);
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D>), grid,
                                                               dim3(64), 0, st, (const T *)q,
                                                               (const T *)k, (const T *)v, o, lse,
-                                                              Hq, Hkv, N, scale, causal)));
+                                                              Hq, Hkv, Nq, Nk, scale, causal)));
     return hipGetLastError();
 }
 

@@ -12,9 +12,10 @@ namespace attn {
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // Generic kernels: any supported (dtype, d); one thread per query row or key row.
-hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                       const void *q, const void *k, const void *v, float *o, float *lse,
-                       hipStream_t st);
+// Forward of Nq queries against Nk >= Nq keys (query i at key position i + Nk - Nq).
+hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                       float scale, const void *q, const void *k, const void *v, float *o,
+                       float *lse, hipStream_t st);
 hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, hipStream_t st);
@@ -37,7 +38,7 @@ hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 
 // Matrix-core kernels: bf16 inputs, d in {64, 128}.
 bool mfma_supported(int dt, int d);
-hipError_t fwd_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                     const void *q, const void *k, const void *v, float *o, float *lse,
                     hipStream_t st);
 // Number of workgroups each group's query heads are split over by the dK/dV

@@ -82,6 +82,22 @@ attn_status attn_fwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
                      float *o, float *lse, void *stream);
 
 /*
+ * attn_fwd_kv -- the forward for Nq queries against Nk >= Nq keys, the queries
+ *   being the last Nq positions: query row i sits at key position
+ *   i + (Nk - Nq), and with causal it sees keys 0 .. i + (Nk - Nq).  This is
+ *   a chunk of new tokens prefilled against a cache that already holds the
+ *   first Nk - Nq ("RustingBrain" docs, "Generating text": only the new tokens
+ *   are computed, the cache supplies the rest).  Nq = Nk is attn_fwd; Nq = 1
+ *   is one decode row.
+ *   q [B][Hq][Nq][d], k/v [B][Hkv][Nk][d] of dtype dt -> o [B][Hq][Nq][d] f32,
+ *   lse [B][Hq][Nq] f32.  Nq <= 0 or Nk < Nq: ATTN_ERR_INVALID_ARG; other
+ *   checks as attn_fwd.  Buffers caller-owned; one launch on `stream`.
+ */
+attn_status attn_fwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v, float *o,
+                        float *lse, void *stream);
+
+/*
  * attn_bwd_workspace_bytes -- device workspace attn_bwd needs, in bytes:
  *   one f32 per query row, D_i = dout_i . o_i, rounded up to 256 bytes.
  *   Returns 0 for invalid shapes.

@@ -38,7 +38,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+    for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
                      "attn_lse_merge",
@@ -161,6 +161,21 @@ def test_bwd_stage_refusals(L):
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
         ptrs[which] = NUL
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
+
+
+def test_fwd_kv_refusals(L):
+    def call(Nq=32, Nk=64, d=64, scale=0.125, ptrs=None):
+        ptrs = ptrs or [P] * 5
+        return L.attn_fwd_kv(1, 1, 4, 2, Nq, Nk, d, 1, scale, *ptrs, NUL)
+    assert call(Nq=0) == INVALID
+    assert call(Nq=65) == INVALID                   # more queries than keys
+    assert call(Nk=-1) == INVALID
+    assert call(d=48) == UNSUPPORTED
+    assert call(scale=float("inf")) == INVALID
+    for which in range(5):
+        ptrs = [P] * 5
+        ptrs[which] = MIS
+        assert call(ptrs=ptrs) == INVALID
 
 
 def test_decode_append_refusals(L):

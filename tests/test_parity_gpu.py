@@ -213,6 +213,47 @@ def test_decode_shapes(B, Hq, Hkv, L, d, S, dtype):
 
 
 # ---------------------------------------------------------------------------
+# Nq queries against Nk >= Nq keys (a prefill chunk against a cache)
+# ---------------------------------------------------------------------------
+
+FWD_KV = [
+    (2, 8, 2, 100, 1000, 128, True, "bf16"),
+    (1, 12, 4, 1, 777, 64, True, "bf16"),      # one decode row
+    (2, 6, 3, 64, 101, 64, True, "bf16"),
+    (1, 4, 2, 200, 300, 64, False, "bf16"),
+    (1, 8, 2, 512, 4096, 128, True, "bf16"),   # a 512-token chunk at the end of a 4k context
+    (1, 2, 1, 20, 50, 16, True, "f32"),        # generic kernels
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype", FWD_KV,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}_{c[7]}"
+                              for c in FWD_KV])
+def test_fwd_kv(B, Hq, Hkv, Nq, Nk, d, causal, dtype):
+    print(f"\n[case] fwd_kv B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype}",
+          flush=True)
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq + Nk)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])      # the last Nq query rows
+    scale = d ** -0.5
+    o, lse = attn.attn_fwd_kv(_to_dev(q, dtype), _to_dev(x["k"], dtype), _to_dev(x["v"], dtype),
+                              causal, scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd(q, x["k"], x["v"], causal, scale)
+    tol_o, tol_l = (1e-5, 1e-5) if dtype == "f32" else (1e-2, 1e-3)
+    assert float(np.abs(o.cpu().numpy() - ro).max()) <= tol_o
+    assert float(np.abs(lse.cpu().numpy() - rl).max()) <= tol_l
+
+
+def test_fwd_kv_square_equals_fwd():
+    x = W.random_train(2, 12, 4, 333, 64, seed=3)
+    g = {n: _to_dev(a, "bf16") for n, a in x.items()}
+    o1, l1 = attn.attn_fwd(g["q"], g["k"], g["v"], True, 0.125)
+    o2, l2 = attn.attn_fwd_kv(g["q"], g["k"], g["v"], True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
 # one decode step with cache append (per-sequence lengths)
 # ---------------------------------------------------------------------------
 
