@@ -122,6 +122,35 @@ class DecodeAppendConfig:
         return kv + new + q + out
 
 
+@dataclass(frozen=True)
+class ChunkConfig:
+    """A causal forward of Nq new tokens against Nk >= Nq keys (the queries are
+    the last Nq positions: a prefill chunk against a cache)."""
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def pairs(self) -> int:
+        """Visible (query, key) pairs: query i sees keys 0 .. i + Nk - Nq."""
+        off = self.Nk - self.Nq
+        return self.B * self.Hq * (self.Nq * (off + 1) + self.Nq * (self.Nq - 1) // 2)
+
+    @property
+    def fwd_flop(self) -> int:
+        return 4 * self.d * self.pairs
+
+
 C1 = TrainConfig("tiny_f32_b1_h2x1_n64_d16", "f32", 1, 2, 1, 64, 16, seed=1001)
 C2 = TrainConfig("gqa12x4_b4_n1024_d64", "bf16", 4, 12, 4, 1024, 64, seed=1002, dout_scale=0.1)
 C3_128 = TrainConfig("gqa32x8_b1_n128_d128", "bf16", 1, 32, 8, 128, 128, seed=1003)
@@ -133,6 +162,9 @@ C5 = DecodeConfig("decode_gqa32x8_l4096_d128_s16", "bf16", 1, 32, 8, 4096, 128, 
 # the 4k context of the decode workload)
 C6 = DecodeAppendConfig("decode_append_gqa32x8_b8_lc4096_d128_s16", "bf16", 8, 32, 8, 4096, 128, 16,
                         tuple(512 * (b + 1) - 1 for b in range(8)), seed=1006)
+
+# the last 512 tokens of the 4k context prefilled against the first 3584
+C7 = ChunkConfig("chunk_gqa32x8_nq512_nk4096_d128", "bf16", 1, 32, 8, 512, 4096, 128, seed=1007)
 
 TRAIN_CONFIGS = {c.name: c for c in (C1, C2, C3_128, C3_512, C4)}
 DECODE_CONFIGS = {C5.name: C5}
@@ -186,6 +218,15 @@ def decode_append_inputs(cfg: DecodeAppendConfig, seed: int | None = None) -> di
     vc = _draw(rng, (cfg.B, cfg.Hkv, cfg.L_cap, cfg.d), cfg.dtype)
     return {"q": q, "k_new": kn, "v_new": vn, "k_cache": kc, "v_cache": vc,
             "seq_lens": np.asarray(cfg.seq_lens, dtype=np.int32)}
+
+
+def chunk_inputs(cfg: ChunkConfig, seed: int | None = None) -> dict:
+    """q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d] as float32 arrays."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    q = _draw(rng, (cfg.B, cfg.Hq, cfg.Nq, cfg.d), cfg.dtype)
+    k = _draw(rng, (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), cfg.dtype)
+    v = _draw(rng, (cfg.B, cfg.Hkv, cfg.Nk, cfg.d), cfg.dtype)
+    return {"q": q, "k": k, "v": v}
 
 
 def random_train(B, Hq, Hkv, N, d, dtype="bf16", seed=0, dout_scale=1.0) -> dict:

@@ -20,7 +20,9 @@ is measured the same way (a graph of K launches of that kernel alone; the
 gradient stage `bwd_grads` is timed per attn_bwd_grads call, which includes a
 zero-fill launch of dk/dv when they are accumulated with atomics).
 
-Outside the step, `decode_append` times one decode step with cache append over
+Outside the step, `fwd_chunk` times attn_fwd_kv on a 512-token prefill chunk
+against a 4096-key context (workload chunk_gqa32x8_nq512_nk4096_d128, 4·d flop
+per visible pair), and `decode_append` times one decode step with cache append over
 8 sequences of their own lengths (attn_decode_append, workload
 decode_append_gqa32x8_b8_lc4096_d128_s16), rotating over 4 distinct cache pairs.
 
@@ -301,6 +303,16 @@ def main():
     a_pl = torch.empty((acfg.B, acfg.Hq, acfg.n_splits), **f32)
     a_o, a_lse = torch.empty((acfg.B, acfg.Hq, acfg.d), **f32), torch.empty((acfg.B, acfg.Hq), **f32)
 
+    # forward of a prefill chunk against a cache (attn_fwd_kv), outside the step
+    ccfg = W.C7
+    xc = W.chunk_inputs(ccfg)
+    gc = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in xc.items()}
+    c_o = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d), **f32)
+    c_lse = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq), **f32)
+
+    def fwd_chunk():
+        attn.attn_fwd_kv(gc["q"], gc["k"], gc["v"], True, ccfg.scale, o=c_o, lse=c_lse)
+
     def decode_append(i):
         kc, vc = a_caches[i % a_ncache]
         return lambda: attn.attn_decode_append(ga["q"], ga["k_new"], ga["v_new"], kc, vc, a_lens,
@@ -313,6 +325,7 @@ def main():
             fn()
         decode(s)()
         decode_append(s)()
+        fwd_chunk()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -326,6 +339,8 @@ def main():
     app_us = timer(torch, [decode_append(s) for s in range(K)], K)
     app_bytes = acfg.algorithmic_bytes()
     app_gbs = app_bytes / (app_us * 1e-6) / 1e9
+    chunk_us = timer(torch, [fwd_chunk] * K, K)
+    chunk_tflops = ccfg.fwd_flop / (chunk_us * 1e-6) / 1e12
 
     pairs = cfg.pairs
     train_flop = cfg.fwd_flop + cfg.bwd_flop
@@ -404,6 +419,9 @@ def main():
                           "us_per_call": round(app_us, 3), "bytes": app_bytes,
                           "distinct_caches": a_ncache, "launches_per_call": 2,
                           "seq_lens": list(acfg.seq_lens)},
+        "fwd_chunk": {"workload": ccfg.name, "TFLOP_s": round(chunk_tflops, 2),
+                      "frac_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),
+                      "us_per_call": round(chunk_us, 3), "flop": ccfg.fwd_flop},
         "kernels": kernels,
         "roofline": roof,
         "timing": ("eager launches between HIP events" if args.eager else
