@@ -41,13 +41,15 @@ namespace attn {
 // Block order of the one-launch backward: plan.n groups of blocks; group i
 // starts at block first[i] and holds consecutive levels of one kind (0: dK/dV
 // key tiles, lev0 first and ascending; 1: dQ query tiles, lev0 first and
-// descending), each level padded to a multiple of kXcds blocks.
+// descending), each level padded to a multiple of kXcds blocks.  A dK/dV
+// group's key tiles split each query-head group over hs[i] work items.
 struct BwdPlan {
     static constexpr int kMax = 48;
     int n;
     int first[kMax + 1];
     int lev0[kMax];
     int kind[kMax];
+    int hs[kMax];
 };
 
 namespace {
@@ -591,7 +593,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     int i = 0;
     while (i + 1 < plan.n && blk >= plan.first[i + 1]) ++i;
     const int kind = plan.kind[i];
-    const int per_level = kind == 0 ? B * Hkv * hs : B * Hq;
+    const int hsi = plan.hs[i];
+    const int per_level = kind == 0 ? B * Hkv * hsi : B * Hq;
     const int per_xcd = (per_level + kXcds - 1) / kXcds;
     const int rel = blk - plan.first[i];
     const int k = rel / kXcds;
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const int item = (rel % kXcds) * per_xcd + k % per_xcd;
     if (item >= per_level) return;
     if (kind == 0)
-        dkdv_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, N, scale, causal, hs);
+        dkdv_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, N, scale, causal, hsi);
     else
         dq_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, N, scale, causal);
 }
@@ -683,20 +686,23 @@ double dkdv_cost(int steps, int d) { return 7.0 + 1.9 * steps * (d / 64); }
 double dq_cost(int tiles, int d) { return 6.0 + 0.8 * tiles * (d / 64); }
 
 struct PlanLevel {
-    int kind, lev, nlev;
+    int kind, lev, nlev, hs;
     double cost;
 };
 
-// Level groups of one kind, heaviest first, coarsened to at most `cap` groups.
-void plan_levels(int kind, int nlev, int cap, const double *cost, const int *lev,
+// Level groups of one kind, heaviest first, coarsened to at most `cap` groups
+// (a group never mixes head splits).
+void plan_levels(int kind, int nlev, int cap, const double *cost, const int *lev, const int *hs,
                  std::vector<PlanLevel> &out)
 {
     const int chunk = (nlev + cap - 1) / cap;
-    for (int i = 0; i < nlev; i += chunk) {
-        const int n = std::min(chunk, nlev - i);
+    for (int i = 0; i < nlev;) {
+        int n = 1;
+        while (n < chunk && i + n < nlev && hs[i + n] == hs[i]) ++n;
         double c = 0;
         for (int j = 0; j < n; ++j) c += cost[i + j];
-        out.push_back({kind, lev[i], n, c / n});
+        out.push_back({kind, lev[i], n, hs[i], c / n});
+        i += n;
     }
 }
 
@@ -706,13 +712,22 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
 {
     const int nkt = (N + kKvBN - 1) / kKvBN, nqkv = (N + kKvSub * kKvBM - 1) / (kKvSub * kKvBM);
     const int nqt = (N + kQBM - 1) / kQBM;
-    const int G = Hq / Hkv, Gs = G / hs;
+    const int G = Hq / Hkv;
+    // Key tiles whose query range is short take fewer head subsets: the
+    // fewest (a divisor of G) whose chain of steps stays within the longest
+    // chain under the split hs (fewer work items and, at one subset, plain
+    // stores instead of atomics).
+    const int max_chain = (G / hs) * nqkv;
     std::vector<double> ck(nkt), cq(nqt);
-    std::vector<int> lk(nkt), lq(nqt);
+    std::vector<int> lk(nkt), lq(nqt), hk(nkt), hq(nqt, 1);
     for (int kt = 0; kt < nkt; ++kt) {
         const int nq = nqkv - (causal ? kt * kKvBN / (kKvSub * kKvBM) : 0);
+        int c = hs;
+        for (int e = 1; e <= hs; ++e)
+            if (G % e == 0 && hs % e == 0 && (G / e) * nq <= max_chain) { c = e; break; }
         lk[kt] = kt;
-        ck[kt] = dkdv_cost(Gs * nq, d);
+        hk[kt] = c;
+        ck[kt] = dkdv_cost((G / c) * nq, d);
     }
     for (int j = 0; j < nqt; ++j) {
         const int qt = nqt - 1 - j;
@@ -721,8 +736,8 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
         cq[j] = dq_cost((kv_end + kQBN - 1) / kQBN, d);
     }
     std::vector<PlanLevel> a, q, m;
-    plan_levels(0, nkt, BwdPlan::kMax / 2, ck.data(), lk.data(), a);
-    plan_levels(1, nqt, BwdPlan::kMax / 2, cq.data(), lq.data(), q);
+    plan_levels(0, nkt, BwdPlan::kMax / 2, ck.data(), lk.data(), hk.data(), a);
+    plan_levels(1, nqt, BwdPlan::kMax / 2, cq.data(), lq.data(), hq.data(), q);
     // merge, heaviest first (ties: dK/dV first)
     size_t ia = 0, iq = 0;
     while (ia < a.size() || iq < q.size()) {
@@ -733,11 +748,12 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
     p.n = (int)m.size();
     int blk = 0;
     for (int i = 0; i < p.n; ++i) {
-        const int per_level = m[i].kind == 0 ? B * Hkv * hs : B * Hq;
+        const int per_level = m[i].kind == 0 ? B * Hkv * m[i].hs : B * Hq;
         const int per_xcd = (per_level + kXcds - 1) / kXcds;
         p.first[i] = blk;
         p.lev0[i] = m[i].lev;
         p.kind[i] = m[i].kind;
+        p.hs[i] = m[i].hs;
         blk += m[i].nlev * per_xcd * kXcds;
     }
     p.first[p.n] = blk;
