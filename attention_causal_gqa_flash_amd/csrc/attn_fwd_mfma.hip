@@ -160,7 +160,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // key tiles side by side and their softmax states combine through LDS at the
 // end with the associative merge, which halves the longest chain of tiles.
 template <int D, int KSPLIT>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
+__global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
     int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(
     const int ntiles = (kv_end + kBN - 1) / kBN;
     // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles); both
     // halves' first tiles hold a key every row of the query tile sees (the
-    // launcher splits only self-attention, off = 0)
+    // launcher splits only where that holds: off = 0, off >= 64 or no mask)
     const int ntA = KSPLIT == 2 ? ntiles / 2 : 0;
     const int nsteps = ntiles - ntA;
     auto tile_of = [&](int half, int s_) { return half == 0 && KSPLIT == 2 ? s_ : ntA + s_; };
@@ -339,22 +339,32 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, f
             cus = 256;
     }
     const int nqt = (Nq + kBM - 1) / kBM;
-    // Key split when the 128-row workgroups would not give every CU two
-    // (d = 64; measured on MI355X, B = 4, N = 1024, 12/4 heads: 22.6 us
-    // unsplit, 20.5 us split).
-    const bool split = d == 64 && Nq == Nk && (long)nqt * B * Hq < 2L * cus;
+    // Key split of small grids.  Its second key half starts mid-range, so every
+    // row of a query tile must see that half's first key: true for
+    // self-attention, for queries at least 64 positions into the keys (a
+    // prefill chunk against a cache) and without the causal mask.
+    // d = 64: when the 128-row workgroups would not give every CU two
+    // (measured on MI355X, B = 4, N = 1024, 12/4 heads: 22.6 us unsplit, 20.5
+    // us split).  d = 128 (one split workgroup per CU: 128 KB of LDS): when
+    // the 128-row workgroups would leave CUs empty.
+    const bool split_ok = !causal || Nq == Nk || Nk - Nq >= 64;
+    const long items = (long)nqt * B * Hq;
+    const bool split = split_ok && (d == 64 ? items < 2L * cus : items < cus);
     auto grid_of = [&](int n_tiles) {
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
-    if (d == 128) {
+    const int nqt64 = (Nq + 63) / 64;
+    if (d == 128 && !split) {
         hipLaunchKernelGGL((fwd_mfma_kernel<128, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
+    } else if (d == 128) {
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
+                           lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else if (d == 64 && !split) {
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 64) {
-        const int nqt64 = (Nq + 63) / 64;
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else {
