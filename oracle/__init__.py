@@ -64,6 +64,7 @@ class Oracle:
         i, d = ctypes.c_int, ctypes.c_double
         lib.oracle_attn_fwd.argtypes = [i, i, i, i, i, i, i, d, _D, _D, _D, _D, _D]
         lib.oracle_attn_bwd.argtypes = [i, i, i, i, i, i, i, d, _D, _D, _D, _D, _D, _D, _D]
+        lib.oracle_attn_bwd_dlse.argtypes = [i, i, i, i, i, i, i, d] + [_D] * 8
         lib.oracle_attn_fwd_dual.argtypes = [i, i, i, i, i, i, i, d] + [_D] * 10
         lib.oracle_dual_xsinx.argtypes = [d, _D, _D]
         lib.oracle_attn_decode.argtypes = [i, i, i, i, i, d, i, _D, _D, _D, _D, _D]
@@ -72,7 +73,7 @@ class Oracle:
         lib.oracle_state_combine.restype = None
         lib.oracle_attn_decode_append.argtypes = [i, i, i, i, i, d, _D, _D, _D, _D, _D,
                                                   ctypes.POINTER(ctypes.c_int), _D, _D]
-        for name in ("oracle_attn_fwd", "oracle_attn_bwd", "oracle_attn_fwd_dual",
+        for name in ("oracle_attn_fwd", "oracle_attn_bwd", "oracle_attn_bwd_dlse", "oracle_attn_fwd_dual",
                      "oracle_dual_xsinx", "oracle_attn_decode", "oracle_lse_merge",
                      "oracle_attn_decode_append", "oracle_abi_version", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
@@ -100,6 +101,18 @@ class Oracle:
         _check(self.lib.oracle_attn_bwd(B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale),
                                         _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv)),
                "attn_bwd")
+        return dq, dk, dv
+
+    def attn_bwd_dlse(self, q, k, v, dout, dlse, causal: bool, scale: float):
+        """Returns (dq, dk, dv) for upstream gradients dout of o and dlse [B,Hq,Nq] of lse."""
+        q, k, v, dout, dlse = _f64(q), _f64(k), _f64(v), _f64(dout), _f64(dlse)
+        B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
+        if dlse.shape != (B, Hq, Nq):
+            raise ValueError("dlse shape mismatch")
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        _check(self.lib.oracle_attn_bwd_dlse(B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale),
+                                             _p(q), _p(k), _p(v), _p(dout), _p(dlse), _p(dq),
+                                             _p(dk), _p(dv)), "attn_bwd_dlse")
         return dq, dk, dv
 
     def attn_fwd_dual(self, q, tq, k, tk, v, tv, causal: bool, scale: float):
@@ -193,6 +206,10 @@ def attn_fwd(q, k, v, causal, scale):
 
 def attn_bwd(q, k, v, dout, causal, scale):
     return default().attn_bwd(q, k, v, dout, causal, scale)
+
+
+def attn_bwd_dlse(q, k, v, dout, dlse, causal, scale):
+    return default().attn_bwd_dlse(q, k, v, dout, dlse, causal, scale)
 
 
 def attn_fwd_dual(q, tq, k, tk, v, tv, causal, scale):

@@ -150,11 +150,11 @@ int oracle_attn_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
 }
 
 /* ------------------------------------------------------------------------ */
-/* Backward, the analytic gradient of the forward for an upstream dO (and a  */
-/* zero upstream gradient on lse):                                           */
+/* Backward, the analytic gradient of the forward for an upstream dO and an  */
+/* upstream gradient dlse of lse (oracle_attn_bwd: dlse = 0):                */
 /*    9. D_i   = <dO_i, o_i>                                                 */
 /*   10. dP_ij = <dO_i, v_j>                                                 */
-/*   11. dS_ij = P_ij (dP_ij - D_i)                                          */
+/*   11. dS_ij = P_ij (dP_ij - D_i + dlse_i)   (d lse_i / d s_ij = P_ij)     */
 /*   12. dq_i  = scale * sum_j dS_ij k_j                                     */
 /*   13. dk_j  = scale * sum_{h in group} sum_i dS_ij q_i                    */
 /*   14. dv_j  = sum_{h in group} sum_i P_ij dO_i                            */
@@ -163,9 +163,9 @@ int oracle_attn_fwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
 /* and comprehensions).  Written out from the chain rule through softmax.    */
 /* Parity: pinned (central finite differences, dual numbers, invariants).    */
 /* ------------------------------------------------------------------------ */
-int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, double scale,
-                    const double *q, const double *k, const double *v, const double *dout,
-                    double *dq, double *dk, double *dv)
+static int attn_bwd_impl(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, double scale,
+                         const double *q, const double *k, const double *v, const double *dout,
+                         const double *dlse, double *dq, double *dk, double *dv)
 {
     if (bad_shape(B, Hq, Hkv, Nq, Nk, d)) return ORACLE_BAD_ARG;
     int G = Hq / Hkv;
@@ -191,6 +191,7 @@ int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
             double *dqh = dq + ((size_t)b * Hq + h) * (size_t)Nq * d;
             double *dkg = dk + ((size_t)b * Hkv + g) * (size_t)Nk * d;
             double *dvg = dv + ((size_t)b * Hkv + g) * (size_t)Nk * d;
+            const double *dlh = dlse ? dlse + ((size_t)b * Hq + h) * (size_t)Nq : NULL;
             long i, j;
 
             head_probs(Nq, Nk, d, causal, scale, qh, kg, P, lh);
@@ -202,12 +203,13 @@ int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
                 double Di = 0.0;
                 for (c = 0; c < d; ++c) Di += doh[i * d + c] * oh[i * d + c];   /* step 9 */
                 Dv[i] = Di;
+                double gl = dlh ? dlh[i] : 0.0;
                 for (j = 0; j < Nk; ++j) {
                     double p = P[i * Nk + j];
                     if (p == 0.0) { dS[i * Nk + j] = 0.0; continue; }
                     double dp = 0.0;
                     for (c = 0; c < d; ++c) dp += doh[i * d + c] * vg[j * d + c]; /* step 10 */
-                    dS[i * Nk + j] = p * (dp - Di);                              /* step 11 */
+                    dS[i * Nk + j] = p * (dp - Di + gl);                         /* step 11 */
                 }
                 for (c = 0; c < d; ++c) dqh[i * d + c] = 0.0;
                 for (j = 0; j < Nk; ++j) {
@@ -232,6 +234,23 @@ int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, d
         }
     free(P); free(dS); free(oh); free(lh); free(Dv);
     return ORACLE_OK;
+}
+
+int oracle_attn_bwd(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, double scale,
+                    const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv)
+{
+    return attn_bwd_impl(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, dout, NULL, dq, dk, dv);
+}
+
+/* Backward with an upstream gradient dlse [B][Hq][Nq] of lse as well.        */
+/* Parity: pinned (central finite differences of <o, dO> + <lse, dlse>, and  */
+/* the dual-number directional derivative of o and lse).                     */
+int oracle_attn_bwd_dlse(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, double scale,
+                         const double *q, const double *k, const double *v, const double *dout,
+                         const double *dlse, double *dq, double *dk, double *dv)
+{
+    return attn_bwd_impl(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, dout, dlse, dq, dk, dv);
 }
 
 /* ------------------------------------------------------------------------ */

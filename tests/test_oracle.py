@@ -283,6 +283,56 @@ def test_bwd_gqa_is_group_sum_of_mha():
 
 
 # --------------------------------------------------------------------------
+# backward with an upstream gradient of lse
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Nq,Nk,causal", [(4, 4, True), (3, 7, True), (5, 5, False)])
+def test_bwd_dlse_finite_differences(Nq, Nk, causal):
+    """d/dx of <o, dO> + <lse, dlse> by central differences equals the backward."""
+    B, Hq, Hkv, d = 1, 2, 1, 3
+    rng = np.random.default_rng(41 + Nq + Nk)
+    q = rng.standard_normal((B, Hq, Nq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    do = rng.standard_normal((B, Hq, Nq, d))
+    dl = rng.standard_normal((B, Hq, Nq))
+    dq, dk, dv = oracle.attn_bwd_dlse(q, k, v, do, dl, causal, 0.7)
+
+    def loss(a):
+        o, lse = oracle.attn_fwd(a["q"], a["k"], a["v"], causal, 0.7)
+        return float(np.sum(o * do) + np.sum(lse * dl))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = {"q": q, "k": k, "v": v}
+            a[name] = xp
+            lp = loss(a)
+            a[name] = xm
+            lm = loss(a)
+            assert abs((lp - lm) / (2 * h) - g[idx]) <= 2e-6, (name, idx)
+
+
+def test_bwd_dlse_zero_equals_bwd_and_lse_only_leaves_dv_zero():
+    B, Hq, Hkv, N, d = 2, 4, 2, 9, 5
+    rng = np.random.default_rng(44)
+    q, k, v = rng.standard_normal((B, Hq, N, d)), rng.standard_normal((B, Hkv, N, d)), \
+        rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, Hq, N, d))
+    a = oracle.attn_bwd(q, k, v, do, True, 0.5)
+    b = oracle.attn_bwd_dlse(q, k, v, do, np.zeros((B, Hq, N)), True, 0.5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    # only lse has an upstream gradient: v does not reach lse
+    _, _, dv = oracle.attn_bwd_dlse(q, k, v, np.zeros_like(do), rng.standard_normal((B, Hq, N)),
+                                    True, 0.5)
+    assert np.all(dv == 0.0)
+
+
+# --------------------------------------------------------------------------
 # split-KV decode, the merge and the online-softmax monoid
 # --------------------------------------------------------------------------
 

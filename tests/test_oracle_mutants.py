@@ -26,8 +26,9 @@ MUTANTS = [
     ("mask_off_by_one", "return !causal || j <= i + (Nk - Nq);", "return !causal || j < i + (Nk - Nq);", 1),
     ("mask_wrong_alignment", "return !causal || j <= i + (Nk - Nq);", "return !causal || j <= i;", 1),
     ("max_not_subtracted_lse", "lse_h[i] = m + log(l);", "lse_h[i] = log(l);", 1),
-    ("ds_sign", "dS[i * Nk + j] = p * (dp - Di);", "dS[i * Nk + j] = p * (Di - dp);", 1),
-    ("ds_drops_D", "dS[i * Nk + j] = p * (dp - Di);", "dS[i * Nk + j] = p * dp;", 1),
+    ("ds_sign", "dS[i * Nk + j] = p * (dp - Di + gl);", "dS[i * Nk + j] = p * (Di - dp + gl);", 1),
+    ("ds_drops_D", "dS[i * Nk + j] = p * (dp - Di + gl);", "dS[i * Nk + j] = p * (dp + gl);", 1),
+    ("ds_dlse_sign", "dS[i * Nk + j] = p * (dp - Di + gl);", "dS[i * Nk + j] = p * (dp - Di - gl);", 1),
     ("dq_scale_dropped", "dqh[i * d + c] *= scale;", "dqh[i * d + c] *= 1.0;", 1),
     ("dk_scale_dropped", "dkg[j * d + c] += scale * s * qh[i * d + c];",
      "dkg[j * d + c] += s * qh[i * d + c];", 1),
@@ -142,6 +143,14 @@ def battery(O) -> list:
     lhs = float(np.sum(do * to))
     rhs = float(np.sum(dq * tq) + np.sum(dk * tk) + np.sum(dv * tv))
     check("dual_vs_bwd", abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs)))
+
+    # upstream gradient of lse: the dual directional derivative of <o, dO> + <lse, dlse>
+    dl = rng.standard_normal((B, Hkv * G, N))
+    _, to2, _, tl2 = O.attn_fwd_dual(q, tq, k, tk, v, tv, True, 0.45)
+    dq2, dk2, dv2 = O.attn_bwd_dlse(q, k, v, do, dl, True, 0.45)
+    lhs2 = float(np.sum(do * to2) + np.sum(dl * tl2))
+    rhs2 = float(np.sum(dq2 * tq) + np.sum(dk2 * tk) + np.sum(dv2 * tv))
+    check("dual_vs_bwd_dlse", abs(lhs2 - rhs2) <= 1e-10 * max(1.0, abs(lhs2)))
 
     # backward invariants
     check("bwd_invariants", np.allclose(dk.sum(axis=2), 0, atol=1e-10) and np.all(dq[:, :, 0] == 0))
