@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
+           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv", "attn_bwd_dlse",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.argtypes = [i, i, i, i, i, i, i, f] + [p] * 8
     L.attn_bwd_grads.argtypes = [i, i, i, i, i, i, i, f] + [p] * 10
     L.attn_bwd_grads.restype = i
+    L.attn_bwd_dlse.argtypes = [i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
+    L.attn_bwd_dlse.restype = i
     L.attn_fwd_kv.argtypes = [i, i, i, i, i, i, i, i, f, p, p, p, p, p, p]
     L.attn_fwd_kv.restype = i
     L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
@@ -152,8 +154,9 @@ def attn_bwd_workspace_bytes(dtype_code: int, B: int, Hq: int, Hkv: int, N: int,
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
-             dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward.  Returns (dq, dk, dv), all float32, for the upstream gradient dout of o."""
+             dq=None, dk=None, dv=None, workspace=None, stream=None, dlse=None):
+    """Backward.  Returns (dq, dk, dv), all float32, for the upstream gradient dout of o
+    (and, with dlse [B,Hq,N] float32, of lse: attn_bwd_dlse)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
         _dev(t, n)
@@ -174,6 +177,16 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     nbytes = attn_bwd_workspace_bytes(code, B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    if dlse is not None:
+        if dlse.dtype != torch.float32 or tuple(dlse.shape) != (B, Hq, N):
+            raise ValueError("dlse must be float32 of the shape of lse")
+        rc = lib().attn_bwd_dlse(code, B, Hq, Hkv, N, d, int(bool(causal)), scale,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(_dev(dlse, "dlse")), _ptr(_dev(dq, "dq")),
+                                 _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+        _check("attn_bwd_dlse", rc)
+        return dq, dk, dv
     rc = lib().attn_bwd(code, B, Hq, Hkv, N, d, int(bool(causal)), scale,
                         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                         _ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")),

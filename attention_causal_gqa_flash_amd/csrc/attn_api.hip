@@ -62,11 +62,11 @@ size_t workspace_bytes(int B, int Hq, int N)
 // will accumulate into them (zero_dkdv), else plain preprocess.
 hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int N, int d, const float *o,
                                  const void *dout, float *delta, float *dk, float *dv,
-                                 bool zero_dkdv, hipStream_t st)
+                                 bool zero_dkdv, hipStream_t st, const float *dlse = nullptr)
 {
     const long n = (long)B * Hkv * N * d;
     return attn::bwd_preprocess(dt, (long)B * Hq * N, d, dout, o, delta, zero_dkdv ? dk : nullptr,
-                                zero_dkdv ? dv : nullptr, n, st);
+                                zero_dkdv ? dv : nullptr, n, dlse, st);
 }
 
 // Forward of Nq queries against Nk >= Nq keys (arguments already validated).
@@ -182,6 +182,29 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int N, int d, int c
     return ATTN_OK;
 }
 
+// The whole backward: the preprocess (with the upstream lse gradient folded
+// into delta when dlse is given), then the gradient stage.
+attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      const void *q, const void *k, const void *v, const float *o,
+                      const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
+                      float *dv, void *workspace, size_t ws_bytes, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return ATTN_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    float *delta = (float *)workspace;
+    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
+    if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st, dlse) !=
+        hipSuccess)
+        return ATTN_ERR_HIP;
+    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
+                            dv, hs, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,25 +240,23 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
     return workspace_bytes(B, Hq, N);
 }
 
+attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v, const float *o,
+                          const float *lse, const void *dout, const float *dlse, float *dq,
+                          float *dk, float *dv, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    return bwd_whole(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk, dv,
+                     workspace, ws_bytes, stream);
+}
+
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      const void *q, const void *k, const void *v, const float *o,
                      const float *lse, const void *dout, float *dq, float *dk, float *dv,
                      void *workspace, size_t ws_bytes, void *stream)
 {
-    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
-    if (s != ATTN_OK) return s;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-        return ATTN_ERR_INVALID_ARG;
-    if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    float *delta = (float *)workspace;
-    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
-    if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st) !=
-        hipSuccess)
-        return ATTN_ERR_HIP;
-    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
-                            dv, hs, st);
+    return bwd_whole(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, o, lse, dout, nullptr, dq, dk,
+                     dv, workspace, ws_bytes, stream);
 }
 
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,
@@ -247,6 +268,7 @@ attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, cons
     return hip_status(launch_bwd_preprocess(dt, B, Hq, 1, N, d, o, dout, delta, nullptr, nullptr,
                                             false, (hipStream_t)stream));
 }
+
 
 attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
                           float scale, const void *q, const void *k, const void *v,

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
                                                       const float *__restrict__ o,
                                                       float *__restrict__ Dws, long rows,
                                                       float *__restrict__ zero,
-                                                      float *__restrict__ zero2, long zero_len)
+                                                      float *__restrict__ zero2, long zero_len,
+                                                      const float *__restrict__ dlse)
 {
     if (zero != nullptr) zero2_grid_stride(zero, zero2, zero_len);
     constexpr int LPR = D / 8;              // lanes per row
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (row < rows && part == 0) Dws[row] = s;
+    // an upstream gradient of lse enters as D - dlse (dS = P (dP - (D - dlse)))
+    if (row < rows && part == 0) Dws[row] = dlse ? s - dlse[row] : s;
 }
 
 // ---------------------------------------------------------------------------
@@ -447,14 +449,15 @@ hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, in
 }
 
 hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
-                          float *zero, float *zero2, long zero_len, hipStream_t st)
+                          float *zero, float *zero2, long zero_len, const float *dlse,
+                          hipStream_t st)
 {
     const int rpb = 256 / (d / 8);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid,
                                                               dim3(256), 0, st, (const T *)dout,
                                                               o, Dws, rows, zero, zero2,
-                                                              zero_len)));
+                                                              zero_len, dlse)));
     return hipGetLastError();
 }
 

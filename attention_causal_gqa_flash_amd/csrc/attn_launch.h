@@ -32,7 +32,8 @@ hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int ca
 // D_i = dout_i . o_i for every query row (rows = B*Hq*N).  With zero != nullptr
 // the same launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
 hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
-                          float *zero, float *zero2, long zero_len, hipStream_t st);
+                          float *zero, float *zero2, long zero_len, const float *dlse,
+                          hipStream_t st);
 // Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
 hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 

@@ -139,6 +139,22 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_bwd_dlse -- attn_bwd with an upstream gradient of lse as well:
+ *   dlse [B][Hq][N] f32 (device, 16-byte aligned, read only).  Since
+ *   d lse_i / d s_ij = P_ij, it enters as dS_ij = P_ij (dP_ij - D_i + dlse_i),
+ *   i.e. the preprocess writes D_i - dlse_i into the workspace and the
+ *   gradient stage is unchanged.  Needed wherever lse itself is consumed, e.g.
+ *   when partial attention outputs are merged by their log-sum-exp (split-KV,
+ *   ring attention: "How tang works" part 3, the associative combine).
+ *   Everything else as attn_bwd.
+ */
+attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v,
+                          const float *o, const float *lse, const void *dout, const float *dlse,
+                          float *dq, float *dk, float *dv, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * The three stages attn_bwd runs, callable one by one (for example to put the
  * dK/dV stage and the dQ stage on two streams once delta is ready, or to time
  * them).  Arguments mean the same as in attn_bwd; delta [B][Hq][N] f32 is

@@ -38,7 +38,7 @@ def L():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+    for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
                      "attn_lse_merge",
@@ -161,6 +161,18 @@ def test_bwd_stage_refusals(L):
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
         ptrs[which] = NUL
         assert L.attn_bwd_grads(*args, *ptrs, NUL) == INVALID
+
+
+def test_bwd_dlse_refusals(L):
+    args = [1, 1, 4, 2, 64, 64, 1, 0.125]
+    ws, nb = P, ctypes.c_size_t(1 << 20)
+    for which in range(10):
+        ptrs = [P] * 10
+        ptrs[which] = MIS
+        assert L.attn_bwd_dlse(*args, *ptrs, ws, nb, NUL) == INVALID
+    assert L.attn_bwd_dlse(*args, *([P] * 6), NUL, *([P] * 3), ws, nb, NUL) == INVALID   # no dlse
+    assert L.attn_bwd_dlse(*args, *([P] * 10), ws, ctypes.c_size_t(16), NUL) == WORKSPACE
+    assert L.attn_bwd_dlse(1, 1, 4, 3, 64, 64, 1, 0.125, *([P] * 10), ws, nb, NUL) == INVALID
 
 
 def test_fwd_kv_refusals(L):

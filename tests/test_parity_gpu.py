@@ -213,6 +213,38 @@ def test_decode_shapes(B, Hq, Hkv, L, d, S, dtype):
 
 
 # ---------------------------------------------------------------------------
+# backward with an upstream gradient of lse
+# ---------------------------------------------------------------------------
+
+DLSE = [
+    (4, 12, 4, 1024, 64, True, "bf16"),     # the one-launch gradient kernel, 3-way head split
+    (1, 8, 2, 300, 128, True, "bf16"),      # d = 128, two kernels side by side
+    (2, 6, 3, 200, 64, False, "bf16"),
+    (1, 2, 1, 64, 16, True, "f32"),         # generic kernels
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,dtype", DLSE,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_N{c[3]}_d{c[4]}_{'c' if c[5] else 'nc'}_{c[6]}" for c in DLSE])
+def test_bwd_dlse(B, Hq, Hkv, N, d, causal, dtype):
+    print(f"\n[case] bwd_dlse B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} {dtype}", flush=True)
+    x = W.random_train(B, Hq, Hkv, N, d, dtype=dtype, seed=N + d, dout_scale=0.1)
+    dl = np.random.default_rng(N).standard_normal((B, Hq, N)).astype(np.float32) * 0.3
+    g = {n: _to_dev(a, dtype) for n, a in x.items()}
+    scale = d ** -0.5
+    o, lse = attn.attn_fwd(g["q"], g["k"], g["v"], causal, scale)
+    dq, dk, dv = attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], causal, scale,
+                               dlse=torch.from_numpy(dl).cuda())
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    ro, rl = oracle.attn_fwd(x["q"], x["k"], x["v"], causal, scale)
+    rdq, rdk, rdv = oracle.attn_bwd_dlse(x["q"], x["k"], x["v"], x["dout"], dl.astype(np.float64),
+                                         causal, scale)
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, tiny_f32=(dtype == "f32"),
+           label=f"dlse N{N} d{d}")
+
+
+# ---------------------------------------------------------------------------
 # Nq queries against Nk >= Nq keys (a prefill chunk against a cache)
 # ---------------------------------------------------------------------------
 
