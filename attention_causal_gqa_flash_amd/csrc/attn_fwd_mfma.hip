@@ -41,7 +41,7 @@ namespace attn {
 namespace {
 
 constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kBN = 64;       // keys per tile
+constexpr int kBN = 64;       // keys per tile (the key-split d = 64 kernel: 32)
 constexpr float kLazy = 8.f;  // max growth tolerated before rescaling (log2 units)
 
 // Per-wave state of the streaming softmax: this lane's query row, its Q^T
@@ -61,7 +61,7 @@ struct FwdState {
 // after the query row's position qa and past the key count Nk are hidden.  `prefetch`
 // issues the wave's NV direct copies of the next tile; they are interleaved
 // with the S^T MFMAs.
-template <int D, int NV, class Prefetch>
+template <int D, int NV, int NKB, class Prefetch>
 __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, const uint16_t *svb,
                                          float c2, int kv0, int qa, int Nk, int causal, bool mask,
                                          int lane, const Prefetch &prefetch)
@@ -70,23 +70,23 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     const int l32 = lane & 31, hf = lane >> 5;
     prefetch();
 
-    // S^T for the tile's two 32-key blocks; the K operands are read first and
+    // S^T for the tile's NKB 32-key blocks; the K operands are read first and
     // interleaved with the MFMAs (4 reads ahead, then one per MFMA).
-    f32x16 sacc[2];
-    bf16x8 ka[2][KS];
+    f32x16 sacc[NKB];
+    bf16x8 ka[NKB][KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = tile_row_operand<D>(skb, kb * 32 + l32, 2 * ks + hf);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], st.qf[ks], sacc[kb]);
-    sched_pipeline<2 * KS, 2 * KS, 4, 1, NV>();
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], st.qf[ks], sacc[kb]);
+    sched_pipeline<NKB * KS, NKB * KS, 4, 1, NV>();
 
     // Row max on the raw scores (c2 > 0 commutes with max); masked scores are -inf.
     // Register r of block kb holds key kv0 + 4hf + c, c = 32kb + 8(r/4) + r%4
@@ -94,7 +94,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     if (mask) {
         const int lim = (causal ? min(qa + 1, Nk) : Nk) - (kv0 + 4 * hf);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
@@ -105,14 +105,14 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     // chains matter: a wave's tile is a latency chain at small head dims).
     float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
     float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
     // Lazy rescale: raise the running max only when some row of the wave grew
-    // past it by more than kLazy.  A row's first tile always sets it, since
-    // every row sees key 0 in the first tile; a fully hidden row keeps -inf.
+    // past it by more than kLazy.  A row that has seen no key yet keeps -inf
+    // (its probabilities are then exact zeros, see nm).
     if (__any(mx > st.m_run + kLazy)) {
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = st.m_run == -INFINITY ? 0.f : exp2_fast(st.m_run - m_new);
@@ -123,11 +123,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
             for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
         st.m_run = m_new;
     }
-    // p = 2^(c2 s - m): one FMA and one exp per score (exp2(-inf) = 0)
+    // p = 2^(c2 s - m): one FMA and one exp per score (exp2(-inf) = 0; a row
+    // with no key seen yet has only hidden scores, and m = -inf is taken as 0)
     float rq[4] = {0.f, 0.f, 0.f, 0.f};
-    const float nm = -st.m_run;
+    const float nm = st.m_run == -INFINITY ? 0.f : -st.m_run;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float p = exp2_fast(fmaf(sacc[kb][r], c2, nm));
@@ -136,21 +137,21 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
         }
     st.l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
 
-    // O^T += V^T P^T, four 16-key steps.  Step tt consumes accumulator
+    // O^T += V^T P^T, 2 NKB 16-key steps.  Step tt consumes accumulator
     // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
     // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
-    bf16x8 va[4][DB];
+    bf16x8 va[2 * NKB][DB];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 2 * NKB; ++tt)
 #pragma unroll
         for (int db = 0; db < DB; ++db) va[tt][db] = tr_operand<D>(svb, 16 * tt, db * 32, lane);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2 * NKB; ++tt) {
         const bf16x8 pb = (tt & 1) ? pack_operand<8>(sacc[tt >> 1]) : pack_operand<0>(sacc[tt >> 1]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) st.oacc[db] = mfma32x32x16(va[tt][db], pb, st.oacc[db]);
     }
-    sched_pipeline<8 * DB, 4 * DB, 4, 2>();
+    sched_pipeline<4 * NKB * DB, 2 * NKB * DB, 4, 2>();
 }
 
 // KSPLIT = 1: one workgroup = 4 waves = 128 query rows (32 per wave), every
@@ -159,7 +160,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // (row half, key half) -- the two key halves stream disjoint halves of the
 // key tiles side by side and their softmax states combine through LDS at the
 // end with the associative merge, which halves the longest chain of tiles.
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int TN>
 __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
     constexpr int RW = 4 / KSPLIT;           // row waves
     constexpr int BMW = 32 * RW;             // query rows per workgroup
-    constexpr int TE = kBN * D;              // elements of one tile
+    constexpr int TE = TN * D;               // elements of one tile (TN keys)
     // K and V tiles (one per key half), row-major with swizzled 16-byte
     // chunks, double-buffered in four separate arrays (see Buf)
     __shared__ __attribute__((aligned(16))) uint16_t sk0[KSPLIT * TE], sk1[KSPLIT * TE];
@@ -221,10 +222,10 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
 
     const int kv_end = causal ? min(Nk, q0 + off + BMW) : Nk;
-    const int ntiles = (kv_end + kBN - 1) / kBN;
-    // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles); both
-    // halves' first tiles hold a key every row of the query tile sees (the
-    // launcher splits only where that holds: off = 0, off >= 64 or no mask)
+    const int ntiles = (kv_end + TN - 1) / TN;
+    // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles).  A row
+    // may see no key of one half (its max stays -inf, its weights are zeros);
+    // the half holding tile 0 holds key 0, which every row sees.
     const int ntA = KSPLIT == 2 ? ntiles / 2 : 0;
     const int nsteps = ntiles - ntA;
     auto tile_of = [&](int half, int s_) { return half == 0 && KSPLIT == 2 ? s_ : ntA + s_; };
@@ -236,15 +237,15 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // read as zero, their scores are masked; copies of tiles that do not
     // exist read nothing (zero-byte resources).
     const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
-    using Copy = TileCopy<D, kBN, 4>;
+    using Copy = TileCopy<D, TN, 4>;
     const Copy copy(wave, lane);
     auto copy_step = [&](uint16_t *skd, uint16_t *svd, int s_) {
 #pragma unroll
         for (int half = 0; half < KSPLIT; ++half) {
             const uint32_t nb = valid(half, s_) ? kv_bytes : 0u;
             const int t_ = tile_of(half, s_);
-            copy(skd + half * TE, make_rsrc(Kg, nb), t_ * kBN, wave);
-            copy(svd + half * TE, make_rsrc(Vg, nb), t_ * kBN, wave);
+            copy(skd + half * TE, make_rsrc(Kg, nb), t_ * TN, wave);
+            copy(svd + half * TE, make_rsrc(Vg, nb), t_ * TN, wave);
         }
     };
     copy_step(sk0, sv0, 0);
@@ -258,10 +259,10 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
         // copies of step s+1 (branch-free, so they can interleave with MFMAs)
         auto prefetch = [&] { copy_step(skn, svn, s_ + 1); };
-        const int kv0 = tile_of(kh, s_) * kBN;
+        const int kv0 = tile_of(kh, s_) * TN;
         if (valid(kh, s_) && qw0 < Nq && (!causal || kv0 <= qw0 + off + 31)) {
-            const bool mask = (causal && kv0 + kBN - 1 > qw0 + off) || kv0 + kBN > Nk;
-            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi + off,
+            const bool mask = (causal && kv0 + TN - 1 > qw0 + off) || kv0 + TN > Nk;
+            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE, TN / 32>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi + off,
                                                      Nk, causal, mask, lane, prefetch);
         } else {
             prefetch();
@@ -275,18 +276,19 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
 
     if constexpr (KSPLIT == 2) {
         // Key half 1 parks (O^T, m, l) per lane in LDS; key half 0 merges:
-        // m = max(mA, mB), O = OA 2^(mA-m) + OB 2^(mB-m), l likewise.  Half 1
-        // always saw keys, so m is finite (an empty half 0 has mA = -inf).
-        float *po = reinterpret_cast<float *>(sk0);   // [rw][DB*16][64]
-        float *pm = reinterpret_cast<float *>(sv0);   // [rw][2][64]
-        static_assert(RW * DB * 16 * 64 * sizeof(float) <= sizeof(sk0), "partial O fits");
+        // m = max(mA, mB), O = OA 2^(mA-m) + OB 2^(mB-m), l likewise.  One half
+        // saw key 0, so m is finite (a half that saw no key has m = -inf).
+        float *po = reinterpret_cast<float *>(rw == 0 ? sk0 : sk1);   // [DB*16][64] per row wave
+        float *pm = reinterpret_cast<float *>(sv0);                   // [rw][2][64]
+        static_assert(RW == 2 && DB * 16 * 64 * sizeof(float) <= sizeof(sk0), "partial O fits");
+        static_assert(RW * 2 * 64 * sizeof(float) <= sizeof(sv0), "partial m, l fit");
         wait_vmcnt<0>();
         __syncthreads();
         if (kh == 1) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) po[(rw * DB * 16 + db * 16 + r) * 64 + lane] = st.oacc[db][r];
+                for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64 + lane] = st.oacc[db][r];
             pm[(rw * 2 + 0) * 64 + lane] = st.m_run;
             pm[(rw * 2 + 1) * 64 + lane] = st.l_run;
         }
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                st.oacc[db][r] = st.oacc[db][r] * ea + po[(rw * DB * 16 + db * 16 + r) * 64 + lane] * eb;
+                st.oacc[db][r] = st.oacc[db][r] * ea + po[(db * 16 + r) * 64 + lane] * eb;
         st.l_run = st.l_run * ea + lB * eb;
         st.m_run = m;
     }
@@ -339,33 +341,28 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, f
             cus = 256;
     }
     const int nqt = (Nq + kBM - 1) / kBM;
-    // Key split of small grids.  Its second key half starts mid-range, so every
-    // row of a query tile must see that half's first key: true for
-    // self-attention, for queries at least 64 positions into the keys (a
-    // prefill chunk against a cache) and without the causal mask.
-    // d = 64: when the 128-row workgroups would not give every CU two
-    // (measured on MI355X, B = 4, N = 1024, 12/4 heads: 22.6 us unsplit, 20.5
-    // us split).  d = 128 (one split workgroup per CU: 128 KB of LDS): when
+    // Key split of small grids.  d = 64 (32-key tiles, 32 KB of LDS, up to
+    // three workgroups per CU): when the 128-row workgroups would not give
+    // every CU two.  d = 128 (one split workgroup per CU: 128 KB of LDS): when
     // the 128-row workgroups would leave CUs empty.
-    const bool split_ok = !causal || Nq == Nk || Nk - Nq >= 64;
     const long items = (long)nqt * B * Hq;
-    const bool split = split_ok && (d == 64 ? items < 2L * cus : items < cus);
+    const bool split = d == 64 ? items < 2L * cus : items < cus;
     auto grid_of = [&](int n_tiles) {
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     const int nqt64 = (Nq + 63) / 64;
     if (d == 128 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 128) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2, kBN>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
                            lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else if (d == 64 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 64) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else {
         return hipErrorInvalidValue;
