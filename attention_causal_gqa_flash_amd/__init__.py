@@ -13,7 +13,8 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv", "attn_bwd_dlse",
+           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
+           "attn_bwd_dlse", "attn_bwd_kv",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dlse.restype = i
     L.attn_fwd_kv.argtypes = [i, i, i, i, i, i, i, i, f, p, p, p, p, p, p]
     L.attn_fwd_kv.restype = i
+    L.attn_bwd_kv.argtypes = [i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
+    L.attn_bwd_kv.restype = i
     L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
     L.attn_decode_append.restype = i
     L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
@@ -157,42 +160,66 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
              dq=None, dk=None, dv=None, workspace=None, stream=None, dlse=None):
     """Backward.  Returns (dq, dk, dv), all float32, for the upstream gradient dout of o
     (and, with dlse [B,Hq,N] float32, of lse: attn_bwd_dlse)."""
+    if dlse is not None:
+        return attn_bwd_dlse(q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, workspace,
+                             stream)
+    return _bwd_call("attn_bwd", q, k, v, o, lse, dout, None, causal, scale, dq, dk, dv, workspace,
+                     stream)
+
+
+def attn_bwd_dlse(q, k, v, o, lse, dout, dlse, causal: bool = True, scale: float | None = None,
+                  dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """attn_bwd with an upstream gradient dlse [B,Hq,N] float32 of lse as well."""
+    return _bwd_call("attn_bwd_dlse", q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv,
+                     workspace, stream)
+
+
+def attn_bwd_kv(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+                dq=None, dk=None, dv=None, workspace=None, stream=None, dlse=None):
+    """Backward of attn_fwd_kv: q, dout [B,Hq,Nq,d] against k, v [B,Hkv,Nk,d] (Nk >= Nq, the
+    queries at the last Nq positions), o, lse from attn_fwd_kv, dlse [B,Hq,Nq] float32 or None.
+    Returns (dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]), all float32."""
+    return _bwd_call("attn_bwd_kv", q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv,
+                     workspace, stream)
+
+
+def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, workspace, stream):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
         _dev(t, n)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if fn != "attn_bwd_kv" and Nk != Nq:
+        raise ValueError(f"{fn} needs as many keys as queries (attn_bwd_kv takes Nk > Nq)")
     if dout.shape != q.shape or dout.dtype != q.dtype:
         raise ValueError("dout must match q in shape and dtype")
     if o.dtype != torch.float32 or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be the float32 outputs of attn_fwd")
+        raise ValueError("o and lse must be the float32 outputs of the forward")
     scale = float(d) ** -0.5 if scale is None else float(scale)
     code = _dtype_code(q)
     if dq is None:
-        dq = torch.empty((B, Hq, N, d), device=q.device, dtype=torch.float32)
+        dq = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
     if dk is None:
-        dk = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
+        dk = torch.empty((B, Hkv, Nk, d), device=q.device, dtype=torch.float32)
     if dv is None:
-        dv = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
-    nbytes = attn_bwd_workspace_bytes(code, B, Hq, Hkv, N, d)
+        dv = torch.empty((B, Hkv, Nk, d), device=q.device, dtype=torch.float32)
+    nbytes = attn_bwd_workspace_bytes(code, B, Hq, Hkv, Nq, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
     if dlse is not None:
-        if dlse.dtype != torch.float32 or tuple(dlse.shape) != (B, Hq, N):
+        if dlse.dtype != torch.float32 or tuple(dlse.shape) != (B, Hq, Nq):
             raise ValueError("dlse must be float32 of the shape of lse")
-        rc = lib().attn_bwd_dlse(code, B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                                 _ptr(_dev(dlse, "dlse")), _ptr(_dev(dq, "dq")),
-                                 _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream))
-        _check("attn_bwd_dlse", rc)
-        return dq, dk, dv
-    rc = lib().attn_bwd(code, B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                        _ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")),
-                        _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream(stream))
-    _check("attn_bwd", rc)
+        dlse_p = _ptr(_dev(dlse, "dlse"))
+    elif fn == "attn_bwd_dlse":
+        raise ValueError("attn_bwd_dlse needs dlse")
+    else:
+        dlse_p = None
+    head = (code, B, Hq, Hkv) + ((Nq, Nk) if fn == "attn_bwd_kv" else (Nq,)) + \
+        (d, int(bool(causal)), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout))
+    tail = (_ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    rc = getattr(lib(), fn)(*head, *((dlse_p,) if fn != "attn_bwd" else ()), *tail)
+    _check(fn, rc)
     return dq, dk, dv
 
 

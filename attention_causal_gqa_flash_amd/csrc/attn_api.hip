@@ -57,15 +57,17 @@ size_t workspace_bytes(int B, int Hq, int N)
     return (rows * sizeof(float) + 255) & ~(size_t)255;
 }
 
-// Kernel launches of the three backward stages (arguments already validated).
+// Kernel launches of the three backward stages (arguments already validated;
+// Nq query rows against Nk >= Nq keys, Nq == Nk in the square entry points).
 // dk/dv zero-fill piggybacked on the preprocess launch when the dK/dV kernel
 // will accumulate into them (zero_dkdv), else plain preprocess.
-hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int N, int d, const float *o,
-                                 const void *dout, float *delta, float *dk, float *dv,
-                                 bool zero_dkdv, hipStream_t st, const float *dlse = nullptr)
+hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                 const float *o, const void *dout, float *delta, float *dk,
+                                 float *dv, bool zero_dkdv, hipStream_t st,
+                                 const float *dlse = nullptr)
 {
-    const long n = (long)B * Hkv * N * d;
-    return attn::bwd_preprocess(dt, (long)B * Hq * N, d, dout, o, delta, zero_dkdv ? dk : nullptr,
+    const long n = (long)B * Hkv * Nk * d;
+    return attn::bwd_preprocess(dt, (long)B * Hq * Nq, d, dout, o, delta, zero_dkdv ? dk : nullptr,
                                 zero_dkdv ? dv : nullptr, n, dlse, st);
 }
 
@@ -80,32 +82,34 @@ hipError_t launch_fwd(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int
 }
 
 // Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
-int dkdv_split(int dt, int B, int Hq, int Hkv, int N, int d, float scale)
+// (use_mfma on Nk covers the Nq <= Nk query rows as well.)
+int dkdv_split(int dt, int B, int Hq, int Hkv, int Nk, int d, float scale)
 {
-    return use_mfma(dt, N, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, N) : 1;
+    return use_mfma(dt, Nk, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, Nk) : 1;
 }
 
 // dk and dv must already be zero when hs > 1.
-hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                           const void *q, const void *k, const void *v, const float *lse,
-                           const void *dout, const float *delta, float *dk, float *dv, int hs,
-                           hipStream_t st)
+hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                           float scale, const void *q, const void *k, const void *v,
+                           const float *lse, const void *dout, const float *delta, float *dk,
+                           float *dv, int hs, hipStream_t st)
 {
-    if (use_mfma(dt, N, d, scale))
-        return attn::bwd_dkdv_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
+    if (use_mfma(dt, Nk, d, scale))
+        return attn::bwd_dkdv_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
                                    delta, dk, dv, hs, st);
-    return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
-                                  delta, dk, dv, st);
+    return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse,
+                                  dout, delta, dk, dv, st);
 }
 
-hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                         const void *q, const void *k, const void *v, const float *lse,
-                         const void *dout, const float *delta, float *dq, hipStream_t st)
+hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                         float scale, const void *q, const void *k, const void *v,
+                         const float *lse, const void *dout, const float *delta, float *dq,
+                         hipStream_t st)
 {
-    if (use_mfma(dt, N, d, scale))
-        return attn::bwd_dq_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout, delta,
-                                 dq, st);
-    return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse, dout,
+    if (use_mfma(dt, Nk, d, scale))
+        return attn::bwd_dq_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
+                                 delta, dq, st);
+    return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
                                 delta, dq, st);
 }
 
@@ -153,14 +157,14 @@ BwdAux *bwd_aux(hipStream_t st)
 }
 
 // dQ, dK, dV from delta (dk/dv already zero when hs > 1).
-attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                             const void *q, const void *k, const void *v, const float *lse,
-                             const void *dout, const float *delta, float *dq, float *dk, float *dv,
-                             int hs, hipStream_t st)
+attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                             float scale, const void *q, const void *k, const void *v,
+                             const float *lse, const void *dout, const float *delta, float *dq,
+                             float *dk, float *dv, int hs, hipStream_t st)
 {
-    if (use_mfma(dt, N, d, scale) && fuse_bwd(d))
-        return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, N, d, causal != 0, scale, q, k, v, lse,
-                                               dout, delta, dq, dk, dv, hs, st));
+    if (use_mfma(dt, Nk, d, scale) && fuse_bwd(d))
+        return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v,
+                                               lse, dout, delta, dq, dk, dv, hs, st));
     std::lock_guard<std::mutex> lock(g_aux_mu);
     BwdAux *aux = bwd_aux(st);
     hipStream_t st_dq = st;
@@ -170,11 +174,11 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int N, int d, int c
             return ATTN_ERR_HIP;
         st_dq = aux->st;
     }
-    if (launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, st_dq) !=
-        hipSuccess)
+    if (launch_bwd_dq(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dq,
+                      st_dq) != hipSuccess)
         return ATTN_ERR_HIP;
-    if (launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dk, dv,
-                        hs, st) != hipSuccess)
+    if (launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dk,
+                        dv, hs, st) != hipSuccess)
         return ATTN_ERR_HIP;
     if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
                 hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
@@ -182,27 +186,29 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int N, int d, int c
     return ATTN_OK;
 }
 
-// The whole backward: the preprocess (with the upstream lse gradient folded
-// into delta when dlse is given), then the gradient stage.
-attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                      const void *q, const void *k, const void *v, const float *o,
+// The whole backward of Nq query rows against Nk >= Nq keys: the preprocess
+// (with the upstream lse gradient folded into delta when dlse is given), then
+// the gradient stage.
+attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                      float scale, const void *q, const void *k, const void *v, const float *o,
                       const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
                       float *dv, void *workspace, size_t ws_bytes, void *stream)
 {
-    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
     if (s != ATTN_OK) return s;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
         !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return ATTN_ERR_INVALID_ARG;
-    if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float *delta = (float *)workspace;
-    const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
-    if (launch_bwd_preprocess(dt, B, Hq, Hkv, N, d, o, dout, delta, dk, dv, hs > 1, st, dlse) !=
-        hipSuccess)
+    const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale);
+    if (launch_bwd_preprocess(dt, B, Hq, Hkv, Nq, Nk, d, o, dout, delta, dk, dv, hs > 1, st,
+                              dlse) != hipSuccess)
         return ATTN_ERR_HIP;
-    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
-                            dv, hs, st);
+    return launch_bwd_grads(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta,
+                            dq, dk, dv, hs, st);
 }
 
 }  // namespace
@@ -246,8 +252,18 @@ attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
                           float *dk, float *dv, void *workspace, size_t ws_bytes, void *stream)
 {
     if (!aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
-    return bwd_whole(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk, dv,
-                     workspace, ws_bytes, stream);
+    return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
+                     dv, workspace, ws_bytes, stream);
+}
+
+attn_status attn_bwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v, const float *o,
+                        const float *lse, const void *dout, const float *dlse, float *dq,
+                        float *dk, float *dv, void *workspace, size_t ws_bytes, void *stream)
+{
+    if (dlse != nullptr && !aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    return bwd_whole(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
+                     dv, workspace, ws_bytes, stream);
 }
 
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -255,8 +271,8 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
                      const float *lse, const void *dout, float *dq, float *dk, float *dv,
                      void *workspace, size_t ws_bytes, void *stream)
 {
-    return bwd_whole(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, o, lse, dout, nullptr, dq, dk,
-                     dv, workspace, ws_bytes, stream);
+    return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, nullptr, dq,
+                     dk, dv, workspace, ws_bytes, stream);
 }
 
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,
@@ -265,8 +281,8 @@ attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, cons
     attn_status s = check_common(dt, B, Hq, 1, N, d, 1.0f);
     if (s != ATTN_OK) return s;
     if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_ERR_INVALID_ARG;
-    return hip_status(launch_bwd_preprocess(dt, B, Hq, 1, N, d, o, dout, delta, nullptr, nullptr,
-                                            false, (hipStream_t)stream));
+    return hip_status(launch_bwd_preprocess(dt, B, Hq, 1, N, N, d, o, dout, delta, nullptr,
+                                            nullptr, false, (hipStream_t)stream));
 }
 
 
@@ -284,7 +300,7 @@ attn_status attn_bwd_dkdv(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
     const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
     if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * N * d, st) != hipSuccess)
         return ATTN_ERR_HIP;
-    return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
+    return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, lse, dout,
                                       delta, dk, dv, hs, st));
 }
 
@@ -297,7 +313,7 @@ attn_status attn_bwd_dq(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout) ||
         !aligned16(delta) || !aligned16(dq))
         return ATTN_ERR_INVALID_ARG;
-    return hip_status(launch_bwd_dq(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout,
+    return hip_status(launch_bwd_dq(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, lse, dout,
                                     delta, dq, (hipStream_t)stream));
 }
 
@@ -315,8 +331,8 @@ attn_status attn_bwd_grads(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, 
     const int hs = dkdv_split(dt, B, Hq, Hkv, N, d, scale);
     if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * N * d, st) != hipSuccess)
         return ATTN_ERR_HIP;
-    return launch_bwd_grads(dt, B, Hq, Hkv, N, d, causal, scale, q, k, v, lse, dout, delta, dq, dk,
-                            dv, hs, st);
+    return launch_bwd_grads(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, lse, dout, delta, dq,
+                            dk, dv, hs, st);
 }
 
 int attn_bwd_grads_single_launch(attn_dtype dt, int N, int d, float scale)

@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 namespace attn {
@@ -65,7 +66,7 @@ constexpr int kKvSub = 2;   // sub-steps per step: one LDS buffer holds 128 quer
 // three phases: S = Q K^T and dP = dO V^T (lane = key column); P = 2^(c2 s -
 // lse log2 e) and dS = P (dP - D); then dV^T += dO^T P and dK^T += Q^T dS
 // over the block's 32 queries.  With `mask` (wave-uniform: causal diagonal
-// blocks) keys after the query get P = 0.  Query rows past N need no mask:
+// blocks) keys after the query get P = 0.  Query rows past Nq need no mask:
 // their Q and dO rows and their lse and D read as zero, so P = 1 there and
 // every product they feed (dV += P^T dO, dK += dS^T Q with dS = P (dP - D) =
 // 0) adds exact zeros.
@@ -124,8 +125,9 @@ __device__ __forceinline__ void dkdv_probs(const RowStats &rs, f32x16 &sacc, f32
         }
     }
     // Register r holds query row q0 + 32qh + 4hf + c, c = 8(r/4) + r%4 (a
-    // constant): the causal mask keeps c >= t = kj - (q0 + 32qh + 4hf), one
-    // compare and one select per score.
+    // constant): the causal mask keeps c >= t = kj - off - (q0 + 32qh + 4hf)
+    // (key kj is visible to query rows at or after kj - off), one compare and
+    // one select per score.
     if (mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -159,12 +161,13 @@ __device__ __forceinline__ void dkdv_grads(const uint16_t *qt, const uint16_t *d
 }
 
 // One sub-step, the three phases in sequence (the block's lse and D rows
-// are all read before its probabilities are computed).
+// are all read before its probabilities are computed).  kq = kj - off: the
+// first query row that sees this lane's key.
 template <int D>
 __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
                                            const float *ddt, const bf16x8 (&kf)[D / 16],
                                            const bf16x8 (&vf)[D / 16], f32x16 (&dka)[D / 32],
-                                           f32x16 (&dva)[D / 32], float c2, int qh, int q0, int kj,
+                                           f32x16 (&dva)[D / 32], float c2, int qh, int q0, int kq,
                                            bool mask, int lane)
 {
     constexpr int KS = D / 16, DB = D / 32;
@@ -172,7 +175,7 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
     dkdv_scores<D>(qt, dt, kf, vf, sacc, pacc, qh, lane);
     sched_pipeline<2 * KS, 2 * KS, kAhead, 1>();
     const RowStats rs = dkdv_rows(lt, ddt, qh, lane);
-    dkdv_probs(rs, sacc, pacc, c2, mask, kj - (q0 + 32 * qh + 4 * (lane >> 5)));
+    dkdv_probs(rs, sacc, pacc, c2, mask, kq - (q0 + 32 * qh + 4 * (lane >> 5)));
     dkdv_grads<D>(qt, dt, sacc, pacc, dka, dva, qh, lane);
     sched_pipeline<8 * DB, 4 * DB, kAheadT, 2>();
 }
@@ -195,21 +198,27 @@ struct BwdLds {
         name##e0[BwdLds<D_>::SR], name##e1[BwdLds<D_>::SR];                                       \
     const BwdLds<D_> name{name##q0, name##q1, name##d0, name##d1, name##l0, name##l1, name##e0, name##e1}
 
-// dK/dV of key tile kt for work item `item` = (batch, kv head, head subset):
+// dK/dV of key tile kt for work item `item` = (batch, kv head, head subset),
+// Nq query rows against Nk >= Nq keys, query row i at key position i + Nk - Nq
+// (so under the causal mask key j is seen by query rows i >= j - (Nk - Nq)):
 // the G query heads of a group are split into hs subsets of Gs heads; with
 // hs > 1 the subsets' partial dK/dV are summed with atomics into zero-filled
 // outputs.  The copy of step s+1 has the two sub-steps of step s to land; at
 // the end the four tile arrays hold the dK^T / dV^T partials of the two query
-// halves.
-template <int D>
+// halves.  XL = false compiles the square case (Nk taken equal to Nq).
+template <int D, bool XL>
 __device__ __forceinline__ void dkdv_body(
     int kt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
-    float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal, int hs)
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs)
 {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int SR = BwdLds<D>::SR;
+    if constexpr (!XL) Nk = Nq;
+    // XL = false: a literal 0, folded before the compiler shapes the loop's branches
+    // (Nk - Nq with Nk = Nq was folded too late and cost 2% in the loop)
+    const int off = XL ? Nk - Nq : 0;
     uint16_t *const q0s = lds.q0s, *const q1s = lds.q1s, *const d0s = lds.d0s, *const d1s = lds.d1s;
     float *const l0s = lds.l0s, *const l1s = lds.l1s, *const e0s = lds.e0s, *const e1s = lds.e1s;
 
@@ -227,13 +236,13 @@ __device__ __forceinline__ void dkdv_body(
     const uint32_t ksign = scale < 0.f ? 0x80008000u : 0u;
     const float c2 = fabsf(scale) * kLog2e;
 
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
     // K^T and V^T operands, resident: lane holds row kj (clamped), dims 16ks + 8hf .. +7.
     bf16x8 kf[KS], vf[KS];
     {
-        const int kr = min(kj, N - 1);
+        const int kr = min(kj, Nk - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 uk = *(const uint4 *)(Kg + (size_t)kr * D + 16 * ks + 8 * hf);
@@ -250,19 +259,19 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dva[db][r] = 0.f; dka[db][r] = 0.f; }
 
-    const int nqt = (N + SR - 1) / SR;
-    const int qt0 = causal ? k0 / SR : 0;
+    const int nqt = (Nq + SR - 1) / SR;
+    const int qt0 = causal ? (XL ? max(k0 - off, 0) : k0) / SR : 0;
     const int nq = nqt - qt0;
     const int steps = Gs * nq;               // (query head, query tile) pairs
 
     // Step s covers query head g*G + hsub*Gs + s/nq, query rows (qt0 + s%nq)*SR
     // .. +SR-1.  Its Q and dO tiles and its lse and D rows move global -> LDS
     // directly (waves 0/1 copy the two halves of lse, waves 2/3 those of D);
-    // rows past N read as zero and are masked in the step's arithmetic.
-    const uint32_t tile_bytes = (uint32_t)N * D * 2, row_bytes = (uint32_t)N * 4;
+    // rows past Nq read as zero and are masked in the step's arithmetic.
+    const uint32_t tile_bytes = (uint32_t)Nq * D * 2, row_bytes = (uint32_t)Nq * 4;
     const TileCopy<D, SR, 4> copy(wave, lane);
     auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd, float *ld, float *ed) {
-        const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * N;
+        const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * Nq;
         const int q0_ = (qt0 + s_ % nq) * SR;
         copy(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave);
         copy(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave);
@@ -287,10 +296,10 @@ __device__ __forceinline__ void dkdv_body(
         for (int sub = 0; sub < kKvSub; ++sub) {
             const int q0 = qs + sub * kKvBM;
             const int qb0 = q0 + 32 * qh;   // first query row of this wave's block
-            if (qb0 < N && k0 + 32 * kb < N && (!causal || qb0 + 31 >= k0 + 32 * kb)) {
-                const bool mask = causal && qb0 < k0 + 32 * kb + 32;
+            if (qb0 < Nq && k0 + 32 * kb < Nk && (!causal || qb0 + 31 + off >= k0 + 32 * kb)) {
+                const bool mask = causal && qb0 + off < k0 + 32 * kb + 32;
                 dkdv_block<D>(qc + sub * kKvBM * D, dc + sub * kKvBM * D, lc + sub * kKvBM,
-                              ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj, mask, lane);
+                              ec + sub * kKvBM, kf, vf, dka, dva, c2, qh, q0, kj - off, mask, lane);
             }
         }
         sched_fence();
@@ -352,12 +361,12 @@ __device__ __forceinline__ void dkdv_body(
             vv[i * CPR + c] = sv[src];
         }
     }
-    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)N * D;
-    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)N * D;
+    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int key = k0 + wave + 4 * i;
-        if (key < N) {
+        if (key < Nk) {
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
                 const size_t at = (size_t)key * D + 64 * c + lane;
@@ -376,21 +385,22 @@ __device__ __forceinline__ void dkdv_body(
 // d = 128 needs more than the 256 registers of two waves per SIMD (K, V
 // operands 64 + dK, dV accumulators 128 + scores 32 + operands in flight):
 // it runs one wave per SIMD with up to 512.
-template <int D>
+template <int D, bool XL>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
-    float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale, int causal, int hs)
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs)
 {
     ATTN_BWD_LDS(D, lds);
+    if constexpr (!XL) Nk = Nq;
     // XCD-aware (see xcd_work_item): a group's Q and dO rows stay in one L2,
     // the heaviest key tiles (causal: the lowest) first.
-    const int nkt = (N + kKvBN - 1) / kKvBN;
+    const int nkt = (Nk + kKvBN - 1) / kKvBN;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nkt, hs, w)) return;
-    dkdv_body<D>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq,
-                 Hkv, N, scale, causal, hs);
+    dkdv_body<D, XL>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq,
+                 Hkv, Nq, Nk, scale, causal, hs);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,11 +412,12 @@ constexpr int kQBN = 64;    // keys per tile
 // One 64-key tile of the dQ kernel for one wave (lane = query row): S^T = K Q^T
 // and dP^T = V dO^T per 32-key block, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 // `prefetch` issues NV direct copies (the next tile), interleaved with the
-// first block's MFMAs.
+// first block's MFMAs.  qk: the lane's query row as a key position (the last
+// key it sees under the causal mask).
 template <int D, int NV, class Prefetch>
 __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&dof)[D / 16], f32x16 (&dqa)[D / 32], float c2,
-                                        float lse2, float Di, int kv0, int qi, int N, int causal,
+                                        float lse2, float Di, int kv0, int qk, int Nk, int causal,
                                         bool mask, int lane, const Prefetch &prefetch)
 {
     constexpr int KS = D / 16, DB = D / 32;
@@ -429,7 +440,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lse2));
         if (mask) {   // keys kv0 + 32kb + 4hf + c (c constant) kept iff c < lim
-            const int lim = (causal ? min(qi + 1, N) : N) - (kv0 + kb * 32 + 4 * hf);
+            const int lim = (causal ? min(qk + 1, Nk) : Nk) - (kv0 + kb * 32 + 4 * hf);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int c = 8 * (r >> 2) + (r & 3);
@@ -450,17 +461,23 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
     }
 }
 
-// dQ of query tile qt for work item `item` = (batch, query head).  K and V
-// tiles, row-major with swizzled 16-byte chunks, double-buffered in the first
-// kQBN rows of the Q and dO arrays of `lds`.
-template <int D>
+// dQ of query tile qt for work item `item` = (batch, query head), Nq query
+// rows against Nk >= Nq keys (query row i at key position i + Nk - Nq; XL =
+// false compiles the square case).  K and V tiles, row-major with swizzled
+// 16-byte chunks, double-buffered in the first kQBN rows of the Q and dO
+// arrays of `lds`.
+template <int D, bool XL>
 __device__ __forceinline__ void dq_body(
     int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int N, float scale, int causal)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal)
 {
     constexpr int KS = D / 16, DB = D / 32;
+    if constexpr (!XL) Nk = Nq;
+    // XL = false: a literal 0, folded before the compiler shapes the loop's branches
+    // (Nk - Nq with Nk = Nq was folded too late and cost 2% in the loop)
+    const int off = XL ? Nk - Nq : 0;
     uint16_t *const sk0 = lds.q0s, *const sk1 = lds.q1s, *const sv0 = lds.d0s, *const sv1 = lds.d1s;
 
     const int G = Hq / Hkv;
@@ -478,13 +495,13 @@ __device__ __forceinline__ void dq_body(
     const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
     const float c2 = fabsf(scale) * kLog2e;
 
-    const size_t qrow0 = ((size_t)b * Hq + h) * N;
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)N * D;
+    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
+    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
     bf16x8 qf[KS], dof[KS];
     {
-        const int qr = min(qi, N - 1);
+        const int qr = min(qi, Nq - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 uq = *(const uint4 *)(Q + (qrow0 + qr) * D + 16 * ks + 8 * hf);
@@ -494,8 +511,8 @@ __device__ __forceinline__ void dq_body(
             dof[ks] = as_bf16x8(ud);
         }
     }
-    const float lse2 = qi < N ? LSE[qrow0 + qi] * kLog2e : INFINITY;
-    const float Di = qi < N ? Dws[qrow0 + qi] : 0.f;
+    const float lse2 = qi < Nq ? LSE[qrow0 + qi] * kLog2e : INFINITY;
+    const float Di = qi < Nq ? Dws[qrow0 + qi] : 0.f;
 
     f32x16 dqa[DB];
 #pragma unroll
@@ -503,11 +520,11 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
 
-    const int kv_end = causal ? min(N, q0 + kQBM) : N;
+    const int kv_end = causal ? min(Nk, q0 + kQBM + off) : Nk;
     const int ntiles = (kv_end + kQBN - 1) / kQBN;
 
-    // Tiles move global -> LDS directly; rows past N read as zero and are masked.
-    const uint32_t kv_bytes = (uint32_t)N * D * 2;
+    // Tiles move global -> LDS directly; rows past Nk read as zero and are masked.
+    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
     using Copy = TileCopy<D, kQBN, 4>;
     const Copy copy(wave, lane);
     copy(sk0, make_rsrc(Kg, kv_bytes), 0, wave);
@@ -529,12 +546,12 @@ __device__ __forceinline__ void dq_body(
         };
         // No branch on whether the wave has work in this tile (a branch would
         // duplicate the interleaved copies and spill registers): a wave whose
-        // rows all precede the tile runs it fully masked, and rows past N have
+        // rows all precede the tile runs it fully masked, and rows past Nq have
         // lse = +inf, so both add exact zeros.
         const int kv0 = t * kQBN;
-        const bool mask = (causal && kv0 + kQBN - 1 > qw0) || kv0 + kQBN > N;
-        dq_tile<D, 2 * Copy::PER_WAVE>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi, N, causal, mask,
-                                       lane, prefetch);
+        const bool mask = (causal && kv0 + kQBN - 1 > qw0 + off) || kv0 + kQBN > Nk;
+        dq_tile<D, 2 * Copy::PER_WAVE>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi + off, Nk, causal,
+                                       mask, lane, prefetch);
         sched_fence();
     };
     for (int t = 0; t < ntiles; t += 2) {
@@ -542,7 +559,7 @@ __device__ __forceinline__ void dq_body(
         if (t + 1 < ntiles) run_tile(Buf<1>{}, t + 1);
     }
 
-    if (qi < N) {
+    if (qi < Nq) {
         float *row = dQ + (qrow0 + qi) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -555,12 +572,12 @@ __device__ __forceinline__ void dq_body(
     }
 }
 
-template <int D>
+template <int D, bool XL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int N, float scale, int causal, int nqt)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
@@ -569,8 +586,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int G = Hq / Hkv;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    dq_body<D>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, N, scale,
-               causal);
+    dq_body<D, XL>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
+               scale, causal);
 }
 
 // Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
@@ -579,13 +596,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // hardware's in-order dispatch of blocks to free CU slots packs the two kinds
 // together.  Within a level, the block's XCD picks a contiguous range of its
 // work items (a group's rows stay in one L2).
-template <int D>
+template <int D, bool XL>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ,
-    float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int N, float scale,
-    int causal, int hs, BwdPlan plan)
+    float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk,
+    float scale, int causal, int hs, BwdPlan plan)
 {
     static_assert(kQBN <= BwdLds<D>::SR, "dQ's K/V tiles fit the Q/dO arrays");
     ATTN_BWD_LDS(D, lds);
@@ -602,14 +619,30 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const int item = (rel % kXcds) * per_xcd + k % per_xcd;
     if (item >= per_level) return;
     if (kind == 0)
-        dkdv_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, N, scale, causal, hsi);
+        dkdv_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale, causal,
+                     hsi);
     else
-        dq_body<D>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, N, scale, causal);
+        dq_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal);
+}
+
+// Runs f(D, XL) (as integral constants) for head dim d and the cross-length
+// flag xl; the square instantiations keep Nk == Nq known to the compiler.
+template <class F>
+hipError_t bwd_variant(int d, bool xl, F &&f)
+{
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using T = std::true_type;
+    using Fa = std::false_type;
+    if (d == 128) xl ? f(I128{}, T{}) : f(I128{}, Fa{});
+    else if (d == 64) xl ? f(I64{}, T{}) : f(I64{}, Fa{});
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace
 
-int dkdv_head_split(int B, int Hq, int Hkv, int N)
+int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
 {
     // Split each group's query heads over workgroups until there are about two
     // work items per CU.  The split workgroups add their partial dK/dV with
@@ -627,7 +660,7 @@ int dkdv_head_split(int B, int Hq, int Hkv, int N)
             cus = 256;
     }
     const int G = Hq / Hkv;
-    const long base = (long)((N + kKvBN - 1) / kKvBN) * B * Hkv;
+    const long base = (long)((Nk + kKvBN - 1) / kKvBN) * B * Hkv;
     int hs = 1;
     for (int c = 1; c <= G; ++c)
         if (G % c == 0) {
@@ -637,43 +670,33 @@ int dkdv_head_split(int B, int Hq, int Hkv, int N)
     return hs;
 }
 
-hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
                          hipStream_t st)
 {
-    const int nkt = (N + kKvBN - 1) / kKvBN;
-    dim3 grid((unsigned)(nkt * B * Hkv * hs));
-    if (d == 128)
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal, hs);
-    else if (d == 64)
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dk, dv, B, Hq, Hkv, N, scale, causal, hs);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    const int nkt = (Nk + kKvBN - 1) / kKvBN;
+    const dim3 grid((unsigned)(nkt * B * Hkv * hs));
+    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
+                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+                           (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dk, dv, B, Hq,
+                           Hkv, Nq, Nk, scale, causal, hs);
+    });
 }
 
-hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st)
 {
-    const int nqt = (N + kQBM - 1) / kQBM;
-    dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
-    if (d == 128)
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dq, B, Hq, Hkv, N, scale, causal, nqt);
-    else if (d == 64)
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dq, B, Hq, Hkv, N, scale, causal, nqt);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    const int nqt = (Nq + kQBM - 1) / kQBM;
+    const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
+    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
+        hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
+                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+                           (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, B, Hq, Hkv,
+                           Nq, Nk, scale, causal, nqt);
+    });
 }
 
 namespace {
@@ -708,10 +731,11 @@ void plan_levels(int kind, int nlev, int cap, const double *cost, const int *lev
 
 }  // namespace
 
-BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *grid)
+BwdPlan bwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *grid)
 {
-    const int nkt = (N + kKvBN - 1) / kKvBN, nqkv = (N + kKvSub * kKvBM - 1) / (kKvSub * kKvBM);
-    const int nqt = (N + kQBM - 1) / kQBM;
+    const int off = Nk - Nq;
+    const int nkt = (Nk + kKvBN - 1) / kKvBN, nqkv = (Nq + kKvSub * kKvBM - 1) / (kKvSub * kKvBM);
+    const int nqt = (Nq + kQBM - 1) / kQBM;
     const int G = Hq / Hkv;
     // Key tiles whose query range is short take fewer head subsets: the
     // fewest (a divisor of G) whose chain of steps stays within the longest
@@ -721,7 +745,7 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
     std::vector<double> ck(nkt), cq(nqt);
     std::vector<int> lk(nkt), lq(nqt), hk(nkt), hq(nqt, 1);
     for (int kt = 0; kt < nkt; ++kt) {
-        const int nq = nqkv - (causal ? kt * kKvBN / (kKvSub * kKvBM) : 0);
+        const int nq = nqkv - (causal ? std::max(kt * kKvBN - off, 0) / (kKvSub * kKvBM) : 0);
         int c = hs;
         for (int e = 1; e <= hs; ++e)
             if (G % e == 0 && hs % e == 0 && (G / e) * nq <= max_chain) { c = e; break; }
@@ -731,7 +755,7 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
     }
     for (int j = 0; j < nqt; ++j) {
         const int qt = nqt - 1 - j;
-        const int kv_end = causal ? std::min(N, (qt + 1) * kQBM) : N;
+        const int kv_end = causal ? std::min(Nk, (qt + 1) * kQBM + off) : Nk;
         lq[j] = qt;
         cq[j] = dq_cost((kv_end + kQBN - 1) / kQBN, d);
     }
@@ -761,25 +785,20 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int N, int d, int causal, int hs, int *
     return p;
 }
 
-hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
                           int hs, hipStream_t st)
 {
     int nblk = 0;
-    const BwdPlan plan = bwd_plan(B, Hq, Hkv, N, d, causal, hs, &nblk);
+    const BwdPlan plan = bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, &nblk);
     const dim3 grid((unsigned)nblk);
-    if (d == 128)
-        hipLaunchKernelGGL(bwd_fused_kernel<128>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dq, dk, dv, B, Hq, Hkv, N, scale, causal, hs, plan);
-    else if (d == 64)
-        hipLaunchKernelGGL(bwd_fused_kernel<64>, grid, dim3(256), 0, st, (const uint16_t *)q,
-                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout,
-                           Dws, dq, dk, dv, B, Hq, Hkv, N, scale, causal, hs, plan);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
+        hipLaunchKernelGGL((bwd_fused_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
+                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+                           (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, dk, dv, B,
+                           Hq, Hkv, Nq, Nk, scale, causal, hs, plan);
+    });
 }
 
 }  // namespace attn

@@ -134,21 +134,23 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
 }
 
 // ---------------------------------------------------------------------------
-// Backward, dq: one thread per query row.  P is recomputed from lse.
+// Backward, dq: one thread per query row.  P is recomputed from lse.  Nq
+// query rows against Nk >= Nq keys, query row i at key position i + Nk - Nq.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
-    float *__restrict__ dq, int Hq, int Hkv, int N, float scale, int causal)
+    float *__restrict__ dq, int Hq, int Hkv, int Nq, int Nk, float scale, int causal)
 {
     const int i = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = h / (Hq / Hkv);
-    const size_t qrow0 = ((size_t)b * Hq + h) * N;
-    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)N * D;
-    const int row = i < N ? i : N - 1;
+    const int off = Nk - Nq;
+    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
+    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const int row = i < Nq ? i : Nq - 1;
 
     float qr[D], dor[D], acc[D];
 #pragma unroll
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
         acc[c] = 0.f;
     }
     const float L = lse[qrow0 + row], Di = Dws[qrow0 + row];
-    const int jend = causal ? row + 1 : N;
-    const int wave_end = causal ? min(N, (int)(blockIdx.x * 64 + 64)) : N;
+    const int jend = causal ? min(row + 1 + off, Nk) : Nk;
+    const int wave_end = causal ? min(Nk, (int)(blockIdx.x * 64 + 64) + off) : Nk;
     for (int j = 0; j < wave_end; ++j) {
         if (j >= jend) continue;
         const T *kj = kg + (size_t)j * D;
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
 #pragma unroll
         for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, to_f32(kj[c]), acc[c]);
     }
-    if (i < N) {
+    if (i < Nq) {
 #pragma unroll
         for (int c = 0; c < D; ++c) dq[(qrow0 + i) * D + c] = acc[c] * scale;
     }
@@ -183,20 +185,22 @@ __global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
 
 // ---------------------------------------------------------------------------
 // Backward, dk and dv: one thread per key row of a key/value head; the loop
-// runs over the query heads of the group and over the queries that see the key.
+// runs over the query heads of the group and over the queries that see the key
+// (under the causal mask, query rows i >= j - (Nk - Nq)).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
-    float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int N, float scale,
+    float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int Nq, int Nk, float scale,
     int causal)
 {
     const int j = blockIdx.x * 64 + threadIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
     const int G = Hq / Hkv;
-    const size_t krow0 = ((size_t)b * Hkv + g) * N;
-    const int row = j < N ? j : N - 1;
+    const int off = Nk - Nq;
+    const size_t krow0 = ((size_t)b * Hkv + g) * Nk;
+    const int row = j < Nk ? j : Nk - 1;
 
     float kr[D], vr[D], dka[D], dva[D];
 #pragma unroll
@@ -206,12 +210,12 @@ __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
         dka[c] = 0.f;
         dva[c] = 0.f;
     }
-    const int istart = causal ? row : 0;
-    const int wave_start = causal ? (int)(blockIdx.x * 64) : 0;
+    const int istart = causal ? max(row - off, 0) : 0;
+    const int wave_start = causal ? max((int)(blockIdx.x * 64) - off, 0) : 0;
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
-        const size_t qrow0 = ((size_t)b * Hq + h) * N;
-        for (int i = wave_start; i < N; ++i) {
+        const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
+        for (int i = wave_start; i < Nq; ++i) {
             if (i < istart) continue;
             const T *qi = q + (qrow0 + i) * D;
             const T *di = dout + (qrow0 + i) * D;
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
             }
         }
     }
-    if (j < N) {
+    if (j < Nk) {
 #pragma unroll
         for (int c = 0; c < D; ++c) {
             dk[(krow0 + j) * D + c] = dka[c] * scale;
@@ -469,30 +473,31 @@ hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                          const void *q, const void *k, const void *v, const float *lse,
-                          const void *dout, const float *Dws, float *dq, hipStream_t st)
+hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v,
+                          const float *lse, const void *dout, const float *Dws, float *dq,
+                          hipStream_t st)
 {
-    dim3 grid((N + 63) / 64, Hq, B);
+    dim3 grid((Nq + 63) / 64, Hq, B);
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
                                                (bwd_dq_rowwise_kernel<T, D>), grid, dim3(64), 0,
                                                st, (const T *)q, (const T *)k, (const T *)v, lse,
-                                               (const T *)dout, Dws, dq, Hq, Hkv, N, scale,
-                                               causal)));
+                                               (const T *)dout, Dws, dq, Hq, Hkv, Nq, Nk,
+                                               scale, causal)));
     return hipGetLastError();
 }
 
-hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                            const void *q, const void *k, const void *v, const float *lse,
-                            const void *dout, const float *Dws, float *dk, float *dv,
-                            hipStream_t st)
+hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            float scale, const void *q, const void *k, const void *v,
+                            const float *lse, const void *dout, const float *Dws, float *dk,
+                            float *dv, hipStream_t st)
 {
-    dim3 grid((N + 63) / 64, Hkv, B);
+    dim3 grid((Nk + 63) / 64, Hkv, B);
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
                                                (bwd_dkdv_colwise_kernel<T, D>), grid, dim3(64), 0,
                                                st, (const T *)q, (const T *)k, (const T *)v, lse,
-                                               (const T *)dout, Dws, dk, dv, Hq, Hkv, N, scale,
-                                               causal)));
+                                               (const T *)dout, Dws, dk, dv, Hq, Hkv, Nq, Nk,
+                                               scale, causal)));
     return hipGetLastError();
 }
 

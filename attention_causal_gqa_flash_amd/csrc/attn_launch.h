@@ -16,18 +16,16 @@ enum Dtype { kF32 = 0, kBF16 = 1 };
 hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                        float scale, const void *q, const void *k, const void *v, float *o,
                        float *lse, hipStream_t st);
-hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                          const void *q, const void *k, const void *v, const float *lse,
-                          const void *dout, const float *Dws, float *dq, hipStream_t st);
-// dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
-hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                          const void *q, const void *k, const void *v, const float *lse,
-                          const void *dout, const float *Dws, float *dq, float *dk, float *dv,
-                          int hs, hipStream_t st);
-hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                            const void *q, const void *k, const void *v, const float *lse,
-                            const void *dout, const float *Dws, float *dk, float *dv,
-                            hipStream_t st);
+// The backward launchers take Nq query rows against Nk >= Nq keys in the same
+// alignment (Nq == Nk: the square case).
+hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, const void *q, const void *k, const void *v,
+                          const float *lse, const void *dout, const float *Dws, float *dq,
+                          hipStream_t st);
+hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            float scale, const void *q, const void *k, const void *v,
+                            const float *lse, const void *dout, const float *Dws, float *dk,
+                            float *dv, hipStream_t st);
 
 // D_i = dout_i . o_i for every query row (rows = B*Hq*N).  With zero != nullptr
 // the same launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
@@ -45,16 +43,16 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, f
 // Number of workgroups each group's query heads are split over by the dK/dV
 // kernel; with more than one, dk and dv must be zero-filled before the launch
 // (the kernel adds into them).
-int dkdv_head_split(int B, int Hq, int Hkv, int N);
-hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+int dkdv_head_split(int B, int Hq, int Hkv, int Nk);
+hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
                          hipStream_t st);
-hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st);
 // dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
-hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
                           int hs, hipStream_t st);

@@ -155,6 +155,28 @@ attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
                           size_t workspace_bytes, void *stream);
 
 /*
+ * attn_bwd_kv -- the backward of attn_fwd_kv: Nq query rows against Nk >= Nq
+ *   keys, query row i at key position i + (Nk - Nq) (under causal it sees keys
+ *   0 .. i + (Nk - Nq), so key j receives gradient from query rows
+ *   i >= j - (Nk - Nq)).  Same sums as attn_bwd over the visible pairs; this
+ *   is the gradient of a prefill chunk against a cache, and of one block pair
+ *   of ring attention ("How tang works" part 3: the reduction over keys and
+ *   its gradient do not depend on where the keys sit).
+ *   q, dout [B][Hq][Nq][d] and k, v [B][Hkv][Nk][d] of dtype dt; o, lse from
+ *   attn_fwd_kv with the same arguments; dlse [B][Hq][Nq] f32 or NULL (no
+ *   upstream gradient of lse; otherwise as attn_bwd_dlse).  dq [B][Hq][Nq][d],
+ *   dk/dv [B][Hkv][Nk][d] f32, overwritten.  workspace: at least
+ *   attn_bwd_workspace_bytes(dt, B, Hq, Hkv, Nq, d) bytes.  Nq <= 0 or
+ *   Nk < Nq: ATTN_ERR_INVALID_ARG; Nq = Nk is attn_bwd (or attn_bwd_dlse).
+ *   Streams, determinism and every other check as attn_bwd.
+ */
+attn_status attn_bwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, const void *q, const void *k, const void *v,
+                        const float *o, const float *lse, const void *dout, const float *dlse,
+                        float *dq, float *dk, float *dv, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
  * The three stages attn_bwd runs, callable one by one (for example to put the
  * dK/dV stage and the dQ stage on two streams once delta is ready, or to time
  * them).  Arguments mean the same as in attn_bwd; delta [B][Hq][N] f32 is

@@ -38,7 +38,8 @@ def L():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+    for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_kv",
+                     "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
                      "attn_lse_merge",
@@ -188,6 +189,26 @@ def test_fwd_kv_refusals(L):
         ptrs = [P] * 5
         ptrs[which] = MIS
         assert call(ptrs=ptrs) == INVALID
+
+
+def test_bwd_kv_refusals(L):
+    def call(Nq=32, Nk=64, d=64, scale=0.125, ptrs=None, nb=1 << 20, dt=1):
+        ptrs = ptrs or [P] * 10
+        return L.attn_bwd_kv(dt, 1, 4, 2, Nq, Nk, d, 1, scale, *ptrs, P, ctypes.c_size_t(nb), NUL)
+    assert call(Nq=0) == INVALID
+    assert call(Nq=65) == INVALID                   # more queries than keys
+    assert call(Nk=-1) == INVALID
+    assert call(d=48) == UNSUPPORTED
+    assert call(dt=2) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(nb=16) == WORKSPACE                 # below 4 heads x 32 rows x 4 bytes
+    for which in range(10):
+        ptrs = [P] * 10
+        ptrs[which] = MIS
+        assert call(ptrs=ptrs) == INVALID
+        if which != 6:                              # dlse may be null
+            ptrs[which] = NUL
+            assert call(ptrs=ptrs) == INVALID
 
 
 def test_decode_append_refusals(L):

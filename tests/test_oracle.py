@@ -282,6 +282,44 @@ def test_bwd_gqa_is_group_sum_of_mha():
     np.testing.assert_allclose(dv, dvm.reshape(B, Hkv, G, N, d).sum(axis=2), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("Nq,Nk,causal", [(3, 7, True), (2, 5, False), (1, 6, True)])
+def test_bwd_cross_length_finite_differences(Nq, Nk, causal):
+    """Nq queries at the last Nq of Nk key positions: central differences of <o, dO>."""
+    B, Hq, Hkv, d = 1, 2, 1, 3
+    q, k, v, do = _qkv(B, Hq, Hkv, Nq, d, seed=50 + Nq + Nk, Nk=Nk)
+    scale = 0.8
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal, scale)
+    assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = {"q": q, "k": k, "v": v}
+            a[name] = xp
+            lp = _loss(a["q"], a["k"], a["v"], do, causal, scale)
+            a[name] = xm
+            lm = _loss(a["q"], a["k"], a["v"], do, causal, scale)
+            assert abs((lp - lm) / (2 * h) - g[idx]) <= 2e-6, (name, idx)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_cross_length_is_square_with_silent_prefix(causal):
+    """The chunk's gradients equal those of the square problem over all Nk positions whose
+    first Nk - Nq query rows (any values) receive dO = 0: those rows add nothing."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 4, 2, 5, 12, 6
+    q, k, v, do = _qkv(B, Hq, Hkv, Nq, d, seed=60, Nk=Nk)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal, 0.4)
+    pre = _rand((B, Hq, Nk - Nq, d), 61)
+    qf = np.concatenate([pre, q], axis=2)
+    dof = np.concatenate([np.zeros_like(pre), do], axis=2)
+    dqf, dkf, dvf = oracle.attn_bwd(qf, k, v, dof, causal, 0.4)
+    np.testing.assert_allclose(dq, dqf[:, :, Nk - Nq:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dk, dkf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dvf, rtol=1e-12, atol=1e-13)
+
+
 # --------------------------------------------------------------------------
 # backward with an upstream gradient of lse
 # --------------------------------------------------------------------------

@@ -35,6 +35,8 @@ MUTANTS = [
     ("dv_wrong_operand", "dvg[j * d + c] += p * doh[i * d + c];", "dvg[j * d + c] += p * qh[i * d + c];", 1),
     ("dv_transposed_P", "double s = dS[i * Nk + j], p = P[i * Nk + j];",
      "double s = dS[i * Nk + j], p = P[j * Nk + i];", 1),
+    ("bwd_dk_stride_of_queries", "double *dkg = dk + ((size_t)b * Hkv + g) * (size_t)Nk * d;",
+     "double *dkg = dk + ((size_t)b * Hkv + g) * (size_t)Nq * d;", 1),
     ("dq_wrong_operand", "dqh[i * d + c] += s * kg[j * d + c];", "dqh[i * d + c] += s * vg[j * d + c];", 1),
     ("head_map_interleaved", "int g = h / G;", "int g = h % Hkv;", 5),
     ("decode_chunk_short", "long j0 = (long)s * C, j1 = j0 + C;", "long j0 = (long)s * C, j1 = j0 + C - 1;", 1),
@@ -151,6 +153,14 @@ def battery(O) -> list:
     lhs2 = float(np.sum(do * to2) + np.sum(dl * tl2))
     rhs2 = float(np.sum(dq2 * tq) + np.sum(dk2 * tk) + np.sum(dv2 * tv))
     check("dual_vs_bwd_dlse", abs(lhs2 - rhs2) <= 1e-10 * max(1.0, abs(lhs2)))
+
+    # cross-length backward: the square problem with dO = 0 on the first Nk - Nq rows
+    qc, doc = q[:, :, 6:], do[:, :, 6:]
+    dqc, dkc, dvc = O.attn_bwd(qc, k, v, doc, True, 0.45)
+    dof = np.concatenate([np.zeros_like(do[:, :, :6]), doc], axis=2)
+    dqf, dkf, dvf = O.attn_bwd(q, k, v, dof, True, 0.45)
+    check("bwd_cross_length", dkc.shape == k.shape and np.allclose(dqc, dqf[:, :, 6:], rtol=1e-11, atol=1e-12)
+          and np.allclose(dkc, dkf, rtol=1e-11, atol=1e-12) and np.allclose(dvc, dvf, rtol=1e-11, atol=1e-12))
 
     # backward invariants
     check("bwd_invariants", np.allclose(dk.sum(axis=2), 0, atol=1e-10) and np.all(dq[:, :, 0] == 0))

@@ -285,6 +285,62 @@ def test_fwd_kv_square_equals_fwd():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+BWD_KV = [
+    (4, 12, 4, 256, 1024, 64, True, "bf16", False),   # one-launch gradients, 3-way head split
+    (1, 8, 2, 300, 700, 128, True, "bf16", True),     # d = 128, two kernels, with dlse
+    (2, 6, 3, 64, 101, 64, True, "bf16", False),      # ragged tiles on both sides
+    (1, 4, 2, 200, 300, 64, False, "bf16", False),
+    (2, 6, 2, 1, 333, 64, True, "bf16", True),        # one row against a cache
+    (1, 4, 1, 512, 4096, 128, True, "bf16", False),   # a 512-token chunk at the end of 4k keys
+    (1, 2, 1, 20, 50, 16, True, "f32", True),         # generic kernels
+    (1, 4, 2, 37, 130, 32, False, "f32", False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype,with_dlse", BWD_KV,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}"
+                              f"_{c[7]}{'_dlse' if c[8] else ''}" for c in BWD_KV])
+def test_bwd_kv(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
+    print(f"\n[case] bwd_kv B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype} "
+          f"dlse={with_dlse}", flush=True)
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq + 3 * Nk, dout_scale=0.1)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    dl = (np.random.default_rng(Nq).standard_normal((B, Hq, Nq)).astype(np.float32) * 0.3
+          if with_dlse else None)
+    scale = d ** -0.5
+    gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
+    o, lse = attn.attn_fwd_kv(gq, gk, gv, causal, scale)
+    dq, dk, dv = attn.attn_bwd_kv(gq, gk, gv, o, lse, gdo, causal, scale,
+                                  dlse=None if dl is None else torch.from_numpy(dl).cuda())
+    torch.cuda.synchronize()
+    assert dq.shape == (B, Hq, Nq, d) and dk.shape == (B, Hkv, Nk, d)
+    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    ro, rl = oracle.attn_fwd(q, x["k"], x["v"], causal, scale)
+    if dl is None:
+        rdq, rdk, rdv = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
+    else:
+        rdq, rdk, rdv = oracle.attn_bwd_dlse(q, x["k"], x["v"], do, dl.astype(np.float64), causal,
+                                             scale)
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, tiny_f32=(dtype == "f32" and Nk <= 64),
+           label=f"bwd_kv Nq{Nq} Nk{Nk} d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_kv_square_equals_bwd(d):
+    """Nq = Nk through attn_bwd_kv runs the same kernels as attn_bwd: the same bits (dq is
+    deterministic; dk, dv too where the key tiles alone fill the GPU)."""
+    x = W.random_train(1, 8, 2, 2048, d, seed=5, dout_scale=0.1)
+    g = {n: _to_dev(a, "bf16") for n, a in x.items()}
+    o, lse = attn.attn_fwd(g["q"], g["k"], g["v"], True, 0.1)
+    r1 = attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], True, 0.1)
+    r2 = attn.attn_bwd_kv(g["q"], g["k"], g["v"], o, lse, g["dout"], True, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0])
+    rel = [float((a - b).norm() / b.norm()) for a, b in zip(r1[1:], r2[1:])]
+    assert max(rel) <= 1e-6, rel
+
+
 # ---------------------------------------------------------------------------
 # one decode step with cache append (per-sequence lengths)
 # ---------------------------------------------------------------------------
