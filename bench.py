@@ -230,6 +230,7 @@ def main():
 
     import torch
     import attention_causal_gqa_flash_amd as attn
+    from attention_causal_gqa_flash_amd import bounds as BD
     from attention_causal_gqa_flash_amd import workloads as W
 
     if not torch.cuda.is_available():
@@ -359,12 +360,18 @@ def main():
                                    "frac_hbm_peak": round(app_gbs / PEAK_HBM_GBS, 4),
                                    "us_per_call": round(app_us, 3), "bytes": app_bytes,
                                    "distinct_caches": a_ncache, "launches_per_call": 2,
-                                   "seq_lens": list(acfg.seq_lens)}
+                                   "seq_lens": list(acfg.seq_lens),
+                                   # the caches rotate through HBM: compulsory bytes at its peak
+                                   "floor_us": round(app_bytes / (BD.PEAK_HBM / 1e6), 3),
+                                   "of_floor": round(app_bytes / (BD.PEAK_HBM / 1e6) / app_us, 4)}
         chunk_us = timer(torch, [fwd_chunk] * K, K)
         chunk_tflops = ccfg.fwd_flop / (chunk_us * 1e-6) / 1e12
+        cf = BD.fwd(ccfg.B, ccfg.Hq, ccfg.Hkv, ccfg.Nq, ccfg.Nk, ccfg.d, True,
+                    **BD.fwd_tile(ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d))
         extras["fwd_chunk"] = {"workload": ccfg.name, "TFLOP_s": round(chunk_tflops, 2),
                                "frac_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),
-                               "us_per_call": round(chunk_us, 3), "flop": ccfg.fwd_flop}
+                               "us_per_call": round(chunk_us, 3), "flop": ccfg.fwd_flop,
+                               "floor_us": cf["floor_us"], "of_floor": round(cf["floor_us"] / chunk_us, 4)}
 
     pairs = cfg.pairs
     train_flop = cfg.fwd_flop + cfg.bwd_flop
@@ -391,6 +398,30 @@ def main():
         kernels["bwd_preprocess"]["GB_s"] = round(pre_bytes / (kernels["bwd_preprocess"]["avg_us"] * 1e-6) / 1e9, 1)
         kernels["decode_merged"]["GB_s"] = round(dec_gbs, 1)
 
+    # time floors from the tile sizes (bounds.py), next to each measured time
+    if kernels and cfg.dtype == "bf16":
+        ft = BD.fwd_tile(B, Hq, N, d)
+        hs = BD.head_split(B, Hq, Hkv, N)
+        kv = dict(BKV=64, SR=128, hs=hs)
+        floors = {
+            "fwd": (BD.fwd(B, Hq, Hkv, N, N, d, True, **ft), BD.best_fwd(B, Hq, Hkv, N, N, d)),
+            "bwd_preprocess": (BD.preprocess(B, Hq, Hkv, N, d, hs > 1), None),
+            "bwd_grads": (BD.bwd_grads(B, Hq, Hkv, N, N, d, True, BQ=128, BN=64, **kv),
+                          BD.best_bwd_grads(B, Hq, Hkv, N, N, d)),
+            "bwd_dkdv": (BD.bwd_dkdv(B, Hq, Hkv, N, N, d, True, **kv), BD.best_bwd_dkdv(B, Hq, Hkv, N, N, d)),
+            "bwd_dq": (BD.bwd_dq(B, Hq, Hkv, N, N, d, True, 128, 64), BD.best_bwd_dq(B, Hq, Hkv, N, N, d)),
+            "decode_merged": (BD.decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, dcfg.n_splits, resident=False),
+                              BD.best_decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, resident=False)),
+        }
+        for n, (fl, best) in floors.items():
+            k = kernels[n]
+            k["floor_us"] = fl["floor_us"]
+            k["floor_bound"] = max(fl["terms_us"], key=fl["terms_us"].get)
+            k["of_floor"] = round(fl["floor_us"] / k["avg_us"], 4)
+            k["tile"] = fl["tile"]
+            if best is not None:
+                k["best_tile"], k["best_floor_us"] = best["tile"], best["floor_us"]
+
     traffic = load_traffic(cfg.name)
     if traffic:
         for n, t in traffic.items():
@@ -411,6 +442,9 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
                     "avg_launch_us": t}
+            for key in ("floor_us", "floor_bound", "of_floor", "tile", "best_tile", "best_floor_us"):
+                if key in kernels[dom]:
+                    roof[key] = kernels[dom][key]
         else:
             ach = kernels[dom]["GB_s"]
             roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
@@ -435,6 +469,10 @@ def main():
                    "causal": True, "decode_workload": dcfg.name},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_bwd_us": round(train_us, 3),
+        # the step's kernels run one after another: their floors add (the two
+        # gradient kernels, side by side at d = 128, share the CUs: one floor)
+        "fwd_bwd_floor_us": (round(sum(kernels[n]["floor_us"] for n in ("fwd", "bwd_preprocess", "bwd_grads")), 3)
+                             if "floor_us" in kernels.get("fwd", {}) else None),
         "decode": {"GB_per_s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "us_per_call": round(dec_us, 3), "bytes": dec_bytes, "distinct_caches": ncache,
                    "launches_per_call": 2},
