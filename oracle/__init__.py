@@ -73,7 +73,9 @@ class Oracle:
         lib.oracle_state_combine.restype = None
         lib.oracle_attn_decode_append.argtypes = [i, i, i, i, i, d, _D, _D, _D, _D, _D,
                                                   ctypes.POINTER(ctypes.c_int), _D, _D]
+        lib.oracle_rope.argtypes = [i, i, i, i, ctypes.c_long, d, i, _D, _D]
         for name in ("oracle_attn_fwd", "oracle_attn_bwd", "oracle_attn_bwd_dlse", "oracle_attn_fwd_dual",
+                     "oracle_rope",
                      "oracle_dual_xsinx", "oracle_attn_decode", "oracle_lse_merge",
                      "oracle_attn_decode_append", "oracle_abi_version", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
@@ -82,6 +84,16 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def rope(self, x, pos0: int, base: float, inverse: bool = False):
+        """Rotary positions on x [B,H,N,d] (row n at position pos0 + n); inverse: the transposed
+        rotation."""
+        x = _f64(x)
+        B, H, N, d = x.shape
+        y = np.empty_like(x)
+        _check(self.lib.oracle_rope(B, H, N, d, int(pos0), float(base), int(inverse), _p(x), _p(y)),
+               "rope")
+        return y
 
     def attn_fwd(self, q, k, v, causal: bool, scale: float):
         """Returns (o [B,Hq,Nq,d], lse [B,Hq,Nq]) in float64."""
@@ -206,6 +218,28 @@ def attn_fwd(q, k, v, causal, scale):
 
 def attn_bwd(q, k, v, dout, causal, scale):
     return default().attn_bwd(q, k, v, dout, causal, scale)
+
+
+def rope(x, pos0, base, inverse=False):
+    return default().rope(x, pos0, base, inverse)
+
+
+def attn_fwd_rope(q, k, v, causal, scale, base):
+    """Attention of rotated q (positions Nk - Nq + i) and rotated k (positions j)."""
+    Nq, Nk = q.shape[2], k.shape[2]
+    return default().attn_fwd(rope(q, Nk - Nq, base), rope(k, 0, base), v, causal, scale)
+
+
+def attn_bwd_rope(q, k, v, dout, causal, scale, base, dlse=None):
+    """Gradients with respect to the unrotated q and k: the attention backward at the rotated
+    inputs, carried back through the rotations by their transposes."""
+    Nq, Nk = q.shape[2], k.shape[2]
+    qr, kr = rope(q, Nk - Nq, base), rope(k, 0, base)
+    if dlse is None:
+        dq, dk, dv = attn_bwd(qr, kr, v, dout, causal, scale)
+    else:
+        dq, dk, dv = attn_bwd_dlse(qr, kr, v, dout, dlse, causal, scale)
+    return rope(dq, Nk - Nq, base, inverse=True), rope(dk, 0, base, inverse=True), dv
 
 
 def attn_bwd_dlse(q, k, v, dout, dlse, causal, scale):

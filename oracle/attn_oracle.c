@@ -566,6 +566,45 @@ int oracle_attn_decode_append(int B, int Hq, int Hkv, int Lcap, int d, double sc
     return ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Rotary positions.  The pages name rotary position embeddings beside GQA   */
+/* attention among the derived ops ("tang -- differentiable computing in     */
+/* Rust", the "A transformer" panel; RustingBrain docs, "What is in the      */
+/* box") but print no formula.  Reading: the usual rotary embedding on       */
+/* paired halves of the head dimension.  For a row at position p and pair   */
+/* index i in [0, d/2):                                                      */
+/*   theta_i = base^(-2i/d),  a = p * theta_i,                               */
+/*   y_i       = x_i cos a - x_{i+d/2} sin a                                 */
+/*   y_{i+d/2} = x_i sin a + x_{i+d/2} cos a                                 */
+/* and with inverse != 0 the transposed rotation (angle -a), which is also   */
+/* the map that carries a gradient with respect to y back to x.  Row n of    */
+/* each [N][d] head sits at position pos0 + n.                               */
+/* Parity: pinned (identity at p = 0, pair norms kept, scores depend only on */
+/* the position difference, a d = 2 closed form, inverse after forward is    */
+/* the identity, finite differences through attention).                      */
+/* ------------------------------------------------------------------------ */
+int oracle_rope(int B, int H, int N, int d, long pos0, double base, int inverse,
+                const double *x, double *y)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || d % 2 != 0 || !(base > 0.0)) return ORACLE_BAD_ARG;
+    int half = d / 2;
+    double sgn = inverse ? -1.0 : 1.0;
+    for (long r = 0; r < (long)B * H * N; ++r) {
+        long p = pos0 + r % N;
+        const double *xr = x + r * d;
+        double *yr = y + r * d;
+        for (int i = 0; i < half; ++i) {
+            double theta = pow(base, -2.0 * i / d);
+            double a = (double)p * theta;
+            double c = cos(a), s = sgn * sin(a);
+            double x0 = xr[i], x1 = xr[i + half];
+            yr[i] = x0 * c - x1 * s;
+            yr[i + half] = x0 * s + x1 * c;
+        }
+    }
+    return ORACLE_OK;
+}
+
 int oracle_abi_version(void) { return 1; }
 
 /* Number of host threads the parallel loops above use. */

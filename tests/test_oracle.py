@@ -321,6 +321,79 @@ def test_bwd_cross_length_is_square_with_silent_prefix(causal):
 
 
 # --------------------------------------------------------------------------
+# rotary positions
+# --------------------------------------------------------------------------
+
+def _rope_complex(x, pos0, base):
+    """The rotation as complex multiplication: pair (x_i, x_{i+d/2}) is z = x_i + 1j x_{i+d/2},
+    turned by exp(1j p base^(-2i/d)) at position p."""
+    d = x.shape[-1]
+    h = d // 2
+    z = x[..., :h] + 1j * x[..., h:]
+    p = pos0 + np.arange(x.shape[-2])[:, None]
+    w = np.exp(1j * p * np.power(float(base), -2.0 * np.arange(h) / d)[None, :])
+    y = z * w
+    return np.concatenate([y.real, y.imag], axis=-1)
+
+
+@pytest.mark.parametrize("pos0,base,d", [(0, 10000.0, 8), (5, 10000.0, 16), (4093, 500000.0, 64),
+                                         (2, 3.0, 2)])
+def test_rope_is_a_complex_turn(pos0, base, d):
+    x = _rand((2, 3, 7, d), 70 + d)
+    np.testing.assert_allclose(oracle.rope(x, pos0, base), _rope_complex(x, pos0, base),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rope_identity_at_zero_and_norms_kept():
+    x = _rand((1, 2, 9, 12), 71)
+    y = oracle.rope(x, 0, 10000.0)
+    assert np.array_equal(y[:, :, 0], x[:, :, 0])          # position 0: no turn
+    h = 6
+    np.testing.assert_allclose(y[..., :h] ** 2 + y[..., h:] ** 2, x[..., :h] ** 2 + x[..., h:] ** 2,
+                               rtol=1e-12)
+
+
+def test_rope_scores_depend_on_position_difference():
+    q, k = _rand((1, 1, 1, 16), 72), _rand((1, 1, 1, 16), 73)
+    base = 10000.0
+    dots = [float(np.sum(oracle.rope(q, 7 + t, base) * oracle.rope(k, 3 + t, base))) for t in (0, 1, 50, 999)]
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-12)
+
+
+def test_rope_inverse_is_transpose():
+    x, y = _rand((2, 2, 5, 8), 74), _rand((2, 2, 5, 8), 75)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, 11, 1e4), 11, 1e4, inverse=True), x,
+                               rtol=1e-13, atol=1e-13)
+    lhs = float(np.sum(oracle.rope(x, 11, 1e4) * y))
+    rhs = float(np.sum(x * oracle.rope(y, 11, 1e4, inverse=True)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("Nq,Nk,causal", [(4, 4, True), (3, 6, True), (4, 5, False)])
+def test_attn_rope_gradient_finite_differences(Nq, Nk, causal):
+    """Attention of rotated q and k: the composite's gradient by central differences."""
+    B, Hq, Hkv, d, base = 1, 2, 1, 4, 100.0
+    q, k, v, do = _qkv(B, Hq, Hkv, Nq, d, seed=80 + Nq + Nk, Nk=Nk)
+    dq, dk, dv = oracle.attn_bwd_rope(q, k, v, do, causal, 0.6, base)
+
+    def loss(a):
+        return float(np.sum(oracle.attn_fwd_rope(a["q"], a["k"], a["v"], causal, 0.6, base)[0] * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = {"q": q, "k": k, "v": v}
+            a[name] = xp
+            lp = loss(a)
+            a[name] = xm
+            lm = loss(a)
+            assert abs((lp - lm) / (2 * h) - g[idx]) <= 2e-6, (name, idx)
+
+
+# --------------------------------------------------------------------------
 # backward with an upstream gradient of lse
 # --------------------------------------------------------------------------
 

@@ -46,6 +46,10 @@ MUTANTS = [
      "double *krow = kc + (((size_t)b * Hkv + g) * (size_t)Lcap + (n + 1 < Lcap ? n + 1 : n)) * d;", 1),
     ("append_value_from_key", "vrow[c] = v_new[((size_t)b * Hkv + g) * d + c];",
      "vrow[c] = k_new[((size_t)b * Hkv + g) * d + c];", 1),
+    ("rope_sine_sign", "double c = cos(a), s = sgn * sin(a);", "double c = cos(a), s = -sgn * sin(a);", 1),
+    ("rope_frequency", "double theta = pow(base, -2.0 * i / d);", "double theta = pow(base, -1.0 * i / d);", 1),
+    ("rope_position_offset_dropped", "long p = pos0 + r % N;", "long p = r % N;", 1),
+    ("rope_pairs_adjacent", "double x0 = xr[i], x1 = xr[i + half];", "double x0 = xr[i], x1 = xr[i ^ 1];", 1),
     ("merge_not_normalised", "for (int c = 0; c < d; ++c) oo[c] /= W;", "", 1),
     ("merge_lse_drops_max", "lse[(size_t)b * Hq + h] = M + log(W);", "lse[(size_t)b * Hq + h] = log(W);", 1),
     ("combine_wrong_weight", "*l = l1 * w1 + l2 * w2;", "*l = l1 * w1 + l2 * w1;", 1),
@@ -161,6 +165,15 @@ def battery(O) -> list:
     dqf, dkf, dvf = O.attn_bwd(q, k, v, dof, True, 0.45)
     check("bwd_cross_length", dkc.shape == k.shape and np.allclose(dqc, dqf[:, :, 6:], rtol=1e-11, atol=1e-12)
           and np.allclose(dkc, dkf, rtol=1e-11, atol=1e-12) and np.allclose(dvc, dvf, rtol=1e-11, atol=1e-12))
+
+    # rotary positions: a complex turn of each (x_i, x_{i+d/2}) pair by p base^(-2i/d)
+    xr = rng.standard_normal((1, 2, 5, 8))
+    z = xr[..., :4] + 1j * xr[..., 4:]
+    w = np.exp(1j * (3 + np.arange(5))[:, None] * np.power(500.0, -2.0 * np.arange(4) / 8)[None, :])
+    yz = z * w
+    yr = O.rope(xr, 3, 500.0)
+    check("rope", np.allclose(yr, np.concatenate([yz.real, yz.imag], axis=-1), rtol=1e-12, atol=1e-12)
+          and np.allclose(O.rope(yr, 3, 500.0, True), xr, rtol=1e-12, atol=1e-12))
 
     # backward invariants
     check("bwd_invariants", np.allclose(dk.sum(axis=2), 0, atol=1e-10) and np.all(dq[:, :, 0] == 0))
