@@ -14,7 +14,7 @@ import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
-           "attn_bwd_dlse", "attn_bwd_kv",
+           "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -66,6 +66,13 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_kv.restype = i
     L.attn_bwd_kv.argtypes = [i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
     L.attn_bwd_kv.restype = i
+    dbl, ll = ctypes.c_double, ctypes.c_longlong
+    L.attn_rope.argtypes = [i, i, i, i, i, ll, dbl, i, p, p, p]
+    L.attn_rope.restype = i
+    L.attn_fwd_rope.argtypes = [i, i, i, i, i, i, i, i, f, dbl] + [p] * 7 + [p]
+    L.attn_fwd_rope.restype = i
+    L.attn_bwd_rope.argtypes = [i, i, i, i, i, i, i, i, f, dbl] + [p] * 10 + [p, sz, p]
+    L.attn_bwd_rope.restype = i
     L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
     L.attn_decode_append.restype = i
     L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
@@ -183,13 +190,14 @@ def attn_bwd_kv(q, k, v, o, lse, dout, causal: bool = True, scale: float | None 
                      workspace, stream)
 
 
-def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, workspace, stream):
+def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, workspace, stream,
+              base=None):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
         _dev(t, n)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    if fn != "attn_bwd_kv" and Nk != Nq:
+    if fn not in ("attn_bwd_kv", "attn_bwd_rope") and Nk != Nq:
         raise ValueError(f"{fn} needs as many keys as queries (attn_bwd_kv takes Nk > Nq)")
     if dout.shape != q.shape or dout.dtype != q.dtype:
         raise ValueError("dout must match q in shape and dtype")
@@ -214,8 +222,9 @@ def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, worksp
         raise ValueError("attn_bwd_dlse needs dlse")
     else:
         dlse_p = None
-    head = (code, B, Hq, Hkv) + ((Nq, Nk) if fn == "attn_bwd_kv" else (Nq,)) + \
-        (d, int(bool(causal)), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout))
+    head = (code, B, Hq, Hkv) + ((Nq, Nk) if fn in ("attn_bwd_kv", "attn_bwd_rope") else (Nq,)) + \
+        (d, int(bool(causal)), scale) + ((float(base),) if fn == "attn_bwd_rope" else ()) + \
+        (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout))
     tail = (_ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     rc = getattr(lib(), fn)(*head, *((dlse_p,) if fn != "attn_bwd" else ()), *tail)
@@ -290,6 +299,51 @@ def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None, o=None
                            _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
     _check("attn_fwd_kv", rc)
     return o, lse
+
+
+def attn_rope(x, pos0: int, base: float, inverse: bool = False, y=None, stream=None):
+    """Rotary positions on x [B,H,N,d] (row n at position pos0 + n) into y (default: a new
+    tensor; y may be x).  inverse: the transposed rotation."""
+    torch = _torch()
+    B, H, N, d = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("y must match x in shape and dtype")
+    rc = lib().attn_rope(_dtype_code(x), B, H, N, d, int(pos0), float(base), int(bool(inverse)),
+                         _ptr(_dev(x, "x")), _ptr(_dev(y, "y")), _stream(stream))
+    _check("attn_rope", rc)
+    return y
+
+
+def attn_fwd_rope(q, k, v, causal: bool = True, scale: float | None = None, base: float = 10000.0,
+                  q_rot=None, k_rot=None, o=None, lse=None, stream=None):
+    """Forward over rotated q (row i at position Nk - Nq + i) and k (row j at j).
+    Returns (o, lse, q_rot, k_rot); attn_bwd_rope takes q_rot and k_rot."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    q_rot = torch.empty_like(q) if q_rot is None else q_rot
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    rc = lib().attn_fwd_rope(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+                             float(base), _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
+                             _ptr(_dev(q_rot, "q_rot")), _ptr(_dev(k_rot, "k_rot")),
+                             _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    _check("attn_fwd_rope", rc)
+    return o, lse, q_rot, k_rot
+
+
+def attn_bwd_rope(q_rot, k_rot, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+                  base: float = 10000.0, dq=None, dk=None, dv=None, workspace=None, stream=None,
+                  dlse=None):
+    """Backward of attn_fwd_rope: (dq, dk, dv) with respect to the unrotated q, k and v."""
+    return _bwd_call("attn_bwd_rope", q_rot, k_rot, v, o, lse, dout, dlse, causal, scale, dq, dk,
+                     dv, workspace, stream, base=base)
 
 
 def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, dk=None, dv=None,

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -92,11 +93,11 @@ int dkdv_split(int dt, int B, int Hq, int Hkv, int Nk, int d, float scale)
 hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                            float scale, const void *q, const void *k, const void *v,
                            const float *lse, const void *dout, const float *delta, float *dk,
-                           float *dv, int hs, hipStream_t st)
+                           float *dv, int hs, hipStream_t st, double rope_lb = 0.0)
 {
     if (use_mfma(dt, Nk, d, scale))
         return attn::bwd_dkdv_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                   delta, dk, dv, hs, st);
+                                   delta, dk, dv, hs, st, rope_lb);
     return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse,
                                   dout, delta, dk, dv, st);
 }
@@ -104,11 +105,11 @@ hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d
 hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                          float scale, const void *q, const void *k, const void *v,
                          const float *lse, const void *dout, const float *delta, float *dq,
-                         hipStream_t st)
+                         hipStream_t st, double rope_lb = 0.0)
 {
     if (use_mfma(dt, Nk, d, scale))
         return attn::bwd_dq_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                 delta, dq, st);
+                                 delta, dq, st, rope_lb);
     return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
                                 delta, dq, st);
 }
@@ -160,11 +161,11 @@ BwdAux *bwd_aux(hipStream_t st)
 attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                              float scale, const void *q, const void *k, const void *v,
                              const float *lse, const void *dout, const float *delta, float *dq,
-                             float *dk, float *dv, int hs, hipStream_t st)
+                             float *dk, float *dv, int hs, hipStream_t st, double rope_lb = 0.0)
 {
     if (use_mfma(dt, Nk, d, scale) && fuse_bwd(d))
         return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v,
-                                               lse, dout, delta, dq, dk, dv, hs, st));
+                                               lse, dout, delta, dq, dk, dv, hs, st, rope_lb));
     std::lock_guard<std::mutex> lock(g_aux_mu);
     BwdAux *aux = bwd_aux(st);
     hipStream_t st_dq = st;
@@ -175,10 +176,10 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int
         st_dq = aux->st;
     }
     if (launch_bwd_dq(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dq,
-                      st_dq) != hipSuccess)
+                      st_dq, rope_lb) != hipSuccess)
         return ATTN_ERR_HIP;
     if (launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dk,
-                        dv, hs, st) != hipSuccess)
+                        dv, hs, st, rope_lb) != hipSuccess)
         return ATTN_ERR_HIP;
     if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
                 hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
@@ -192,7 +193,7 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int
 attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                       float scale, const void *q, const void *k, const void *v, const float *o,
                       const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
-                      float *dv, void *workspace, size_t ws_bytes, void *stream)
+                      float *dv, void *workspace, size_t ws_bytes, void *stream, double rope_lb = 0.0)
 {
     if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
     attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
@@ -208,7 +209,7 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
                               dlse) != hipSuccess)
         return ATTN_ERR_HIP;
     return launch_bwd_grads(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta,
-                            dq, dk, dv, hs, st);
+                            dq, dk, dv, hs, st, rope_lb);
 }
 
 }  // namespace
@@ -254,6 +255,59 @@ attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
     if (!aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
     return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
                      dv, workspace, ws_bytes, stream);
+}
+
+attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0, double base,
+                      int inverse, const void *x, void *y, void *stream)
+{
+    attn_status s = check_common(dt, B, H, H, N, d, 1.0f);
+    if (s != ATTN_OK) return s;
+    if (!(base > 0.0) || !isfinite(base) || llabs(pos0) > (1LL << 40)) return ATTN_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y)) return ATTN_ERR_INVALID_ARG;
+    return hip_status(attn::rope(dt, (long)B * H * N, N, d, (long)pos0, base, inverse != 0, x, y,
+                                 (hipStream_t)stream));
+}
+
+attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, double base, const void *q, const void *k, const void *v,
+                          void *q_rot, void *k_rot, float *o, float *lse, void *stream)
+{
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!(base > 0.0) || !isfinite(base)) return ATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_rot) || !aligned16(k_rot) ||
+        !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (attn::rope(dt, (long)B * Hq * Nq, Nq, d, Nk - Nq, base, 0, q, q_rot, st) != hipSuccess ||
+        attn::rope(dt, (long)B * Hkv * Nk, Nk, d, 0, base, 0, k, k_rot, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return hip_status(launch_fwd(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q_rot, k_rot, v, o, lse, st));
+}
+
+attn_status attn_bwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, double base, const void *q_rot, const void *k_rot,
+                          const void *v, const float *o, const float *lse, const void *dout,
+                          const float *dlse, float *dq, float *dk, float *dv, void *workspace,
+                          size_t ws_bytes, void *stream)
+{
+    if (!(base > 0.0) || !isfinite(base)) return ATTN_ERR_INVALID_ARG;
+    if (dlse != nullptr && !aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    // gradients with respect to the unrotated q and k: the transposed rotations,
+    // in the gradient kernels' epilogues on the matrix-core path, else a pass
+    // over dq and dk afterwards
+    // (log2 base = 0 means "no rotation" to the kernels: a base of 1 takes the pass)
+    const bool in_epilogue = use_mfma(dt, Nk, d, scale) && log2(base) != 0.0;
+    attn_status s = bwd_whole(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q_rot, k_rot, v, o, lse,
+                              dout, dlse, dq, dk, dv, workspace, ws_bytes, stream,
+                              in_epilogue ? log2(base) : 0.0);
+    if (s != ATTN_OK || in_epilogue) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (attn::rope(kF32, (long)B * Hq * Nq, Nq, d, Nk - Nq, base, 1, dq, dq, st) != hipSuccess ||
+        attn::rope(kF32, (long)B * Hkv * Nk, Nk, d, 0, base, 1, dk, dk, st) != hipSuccess)
+        return ATTN_ERR_HIP;
+    return ATTN_OK;
 }
 
 attn_status attn_bwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,

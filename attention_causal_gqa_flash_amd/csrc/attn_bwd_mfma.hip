@@ -211,7 +211,8 @@ __device__ __forceinline__ void dkdv_body(
     int kt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
-    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs)
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
+    double rope_lb)
 {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int SR = BwdLds<D>::SR;
@@ -361,6 +362,25 @@ __device__ __forceinline__ void dkdv_body(
             vv[i * CPR + c] = sv[src];
         }
     }
+    // rope_lb != 0: dK was taken at rotated keys; the transposed rotation of
+    // key `key` carries it back (dim and its partner dim ^ D/2 of the same row)
+    if (rope_lb != 0.0) {
+        // every value of this lane is dim 64c + lane: one pair index, one frequency
+        const double th = rope_theta(lane & (D / 2 - 1), D, rope_lb);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int kr = wave + 4 * i;
+            const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s) + (kr & 31) * D;
+            float sn, cs;
+            rope_sincos_hw((double)(k0 + kr) * th, sn, cs);
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) {
+                const int dim = 64 * c + lane;
+                const float partner = sk[(dim ^ (D / 2)) ^ (kr & 31)];
+                vk[i * CPR + c] = vk[i * CPR + c] * cs + (dim < D / 2 ? sn : -sn) * partner;
+            }
+        }
+    }
     float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 #pragma unroll
@@ -390,7 +410,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
-    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs)
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
+    double rope_lb)
 {
     ATTN_BWD_LDS(D, lds);
     if constexpr (!XL) Nk = Nq;
@@ -400,7 +421,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nkt, hs, w)) return;
     dkdv_body<D, XL>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq,
-                 Hkv, Nq, Nk, scale, causal, hs);
+                 Hkv, Nq, Nk, scale, causal, hs, rope_lb);
 }
 
 // ---------------------------------------------------------------------------
@@ -471,7 +492,7 @@ __device__ __forceinline__ void dq_body(
     int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int Nq, int Nk, float scale, int causal)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, double rope_lb)
 {
     constexpr int KS = D / 16, DB = D / 32;
     if constexpr (!XL) Nk = Nq;
@@ -559,6 +580,35 @@ __device__ __forceinline__ void dq_body(
         if (t + 1 < ntiles) run_tile(Buf<1>{}, t + 1);
     }
 
+    // rope_lb != 0: dQ was taken at rotated queries; the transposed rotation of
+    // position qi + off carries it back (dims i and i + D/2 sit in blocks db
+    // and db + DB/2 of the same lane and register)
+    if (rope_lb != 0.0) {
+        // pair i = 32db + 8(r/4) + 4hf + r%4 has frequency q^i, q = base^(-2/D):
+        // q^(4hf + r%4) once, then steps of q^8 and q^32
+        const double pos = (double)(qi + off);
+        const double q1 = rope_theta(1, D, rope_lb), q8 = rope_theta(8, D, rope_lb);
+        const double q32 = rope_theta(32, D, rope_lb);
+        double t0[4];
+        t0[0] = rope_theta(4 * hf, D, rope_lb);
+        t0[1] = t0[0] * q1; t0[2] = t0[1] * q1; t0[3] = t0[2] * q1;
+        double tdb = 1.0;
+#pragma unroll
+        for (int db = 0; db < DB / 2; ++db, tdb *= q32) {
+            double ta = tdb;
+#pragma unroll
+            for (int a = 0; a < 4; ++a, ta *= q8)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * a + e;
+                    float sn, cs;
+                    rope_sincos_hw(pos * (t0[e] * ta), sn, cs);
+                    const float x0 = dqa[db][r], x1 = dqa[db + DB / 2][r];
+                    dqa[db][r] = x0 * cs + x1 * sn;
+                    dqa[db + DB / 2][r] = x1 * cs - x0 * sn;
+                }
+        }
+    }
     if (qi < Nq) {
         float *row = dQ + (qrow0 + qi) * D;
 #pragma unroll
@@ -577,7 +627,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt, double rope_lb)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
@@ -587,7 +637,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
     dq_body<D, XL>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
-               scale, causal);
+                   scale, causal, rope_lb);
 }
 
 // Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
@@ -602,7 +652,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ,
     float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk,
-    float scale, int causal, int hs, BwdPlan plan)
+    float scale, int causal, int hs, BwdPlan plan, double rope_lb)
 {
     static_assert(kQBN <= BwdLds<D>::SR, "dQ's K/V tiles fit the Q/dO arrays");
     ATTN_BWD_LDS(D, lds);
@@ -619,10 +669,11 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const int item = (rel % kXcds) * per_xcd + k % per_xcd;
     if (item >= per_level) return;
     if (kind == 0)
-        dkdv_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale, causal,
-                     hsi);
+        dkdv_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale,
+                         causal, hsi, rope_lb);
     else
-        dq_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal);
+        dq_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal,
+                       rope_lb);
 }
 
 // Runs f(D, XL) (as integral constants) for head dim d and the cross-length
@@ -673,7 +724,7 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
-                         hipStream_t st)
+                         hipStream_t st, double rope_lb)
 {
     const int nkt = (Nk + kKvBN - 1) / kKvBN;
     const dim3 grid((unsigned)(nkt * B * Hkv * hs));
@@ -681,13 +732,14 @@ hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int caus
         hipLaunchKernelGGL((bwd_dkdv_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
                            dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dk, dv, B, Hq,
-                           Hkv, Nq, Nk, scale, causal, hs);
+                           Hkv, Nq, Nk, scale, causal, hs, rope_lb);
     });
 }
 
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
-                       const void *dout, const float *Dws, float *dq, hipStream_t st)
+                       const void *dout, const float *Dws, float *dq, hipStream_t st,
+                       double rope_lb)
 {
     const int nqt = (Nq + kQBM - 1) / kQBM;
     const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
@@ -695,7 +747,7 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
         hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
                            dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, B, Hq, Hkv,
-                           Nq, Nk, scale, causal, nqt);
+                           Nq, Nk, scale, causal, nqt, rope_lb);
     });
 }
 
@@ -788,7 +840,7 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int 
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
-                          int hs, hipStream_t st)
+                          int hs, hipStream_t st, double rope_lb)
 {
     int nblk = 0;
     const BwdPlan plan = bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, &nblk);
@@ -797,7 +849,7 @@ hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
         hipLaunchKernelGGL((bwd_fused_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
                            dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, dk, dv, B,
-                           Hq, Hkv, Nq, Nk, scale, causal, hs, plan);
+                           Hq, Hkv, Nq, Nk, scale, causal, hs, plan, rope_lb);
     });
 }
 

@@ -42,6 +42,29 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotary positions: the frequency base^(-2i/d) of pair i (log2_base = log2 base),
+// and the sine and cosine of an angle of any size, reduced to [-pi, pi] in
+// double and then evaluated in f32.
+__device__ __forceinline__ double rope_theta(int i, int d, double log2_base)
+{
+    return exp2(-2.0 * i / d * log2_base);
+}
+__device__ __forceinline__ void rope_sincos(double a, float &s, float &c)
+{
+    const double turns = rint(a * 0.15915494309189535);   // a / (2 pi)
+    sincosf((float)fma(-6.283185307179586, turns, a), &s, &c);
+}
+// The same on the hardware sine and cosine (v_sin_f32 / v_cos_f32 take the
+// angle in turns), for the matrix-core path's epilogues: a few instructions
+// instead of the library's full-range code, accurate to about 1e-6.
+__device__ __forceinline__ void rope_sincos_hw(double a, float &s, float &c)
+{
+    const double t = a * 0.15915494309189535;             // turns
+    const float f = (float)(t - rint(t));                  // in [-1/2, 1/2]
+    s = __builtin_amdgcn_sinf(f);
+    c = __builtin_amdgcn_cosf(f);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // ds_read_b64_tr_b16: within each 16-lane group, result lane i, element k is

@@ -32,10 +32,17 @@ hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int 
 hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
                           float *zero, float *zero2, long zero_len, const float *dlse,
                           hipStream_t st);
+// Rotary positions on `rows` rows of d elements of dtype dt, row r at position
+// pos0 + r % N (inverse: the transposed rotation); x and y may alias.
+hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
+                void *y, hipStream_t st);
 // Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
 hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 
-// Matrix-core kernels: bf16 inputs, d in {64, 128}.
+// Matrix-core kernels: bf16 inputs, d in {64, 128}.  The gradient launchers'
+// rope_lb (log2 of the rotary base; 0: none, so a base of 1 is left to the
+// caller) carries dQ and dK, taken at rotated q and k, back through the
+// transposed rotations in their epilogues.
 bool mfma_supported(int dt, int d);
 hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                     const void *q, const void *k, const void *v, float *o, float *lse,
@@ -47,15 +54,16 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk);
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
-                         hipStream_t st);
+                         hipStream_t st, double rope_lb = 0.0);
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
-                       const void *dout, const float *Dws, float *dq, hipStream_t st);
+                       const void *dout, const float *Dws, float *dq, hipStream_t st,
+                       double rope_lb = 0.0);
 // dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
-                          int hs, hipStream_t st);
+                          int hs, hipStream_t st, double rope_lb = 0.0);
 
 // Split-KV decode and the log-sum-exp merge.
 hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,

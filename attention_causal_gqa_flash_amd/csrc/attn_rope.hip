@@ -1,0 +1,103 @@
+// attn_rope.hip -- rotary positions on the rows of q, k (and, transposed, on
+// the gradients with respect to them).
+//
+// The pages list rotary position embeddings beside grouped-query attention
+// among the derived ops ("tang -- differentiable computing in Rust", the "A
+// transformer" panel; RustingBrain docs, "What is in the box") without a
+// formula.  The rotation used (the usual one, on paired halves of the head
+// dimension): for a row at position p and pair i in [0, d/2), theta_i =
+// base^(-2i/d), a = p theta_i,
+//     y_i = x_i cos a - x_{i+d/2} sin a,   y_{i+d/2} = x_i sin a + x_{i+d/2} cos a,
+// and the transposed rotation (angle -a) for `inverse`.
+//
+// One elementwise pass, not a prologue inside the attention kernels: the
+// dK/dV kernel streams Q tiles into LDS by direct global->LDS copies, which
+// bypass the registers, so the backward needs the rotated Q in memory anyway;
+// once written for it, the forward reads the same bytes as it would read the
+// unrotated Q.  K is rotated once per key/value head here instead of once per
+// query tile that loads it.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace attn {
+namespace {
+
+constexpr int kPairs = 4;   // consecutive pairs per thread
+
+__device__ __forceinline__ void load4(const bf16_t *p, float (&v)[4])
+{
+    const uint2 u = *(const uint2 *)p;
+    v[0] = bf16lo(u.x); v[1] = bf16hi(u.x); v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+}
+__device__ __forceinline__ void load4(const float *p, float (&v)[4])
+{
+    const float4 u = *(const float4 *)p;
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
+__device__ __forceinline__ void store4(bf16_t *p, const float (&v)[4])
+{
+    *(uint2 *)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void store4(float *p, const float (&v)[4])
+{
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// Row r of `rows` rows of d elements sits at position pos0 + r % N.  A thread
+// owns pairs i0 .. i0+3 of its rows (the grid stride is a multiple of the
+// threads per row, so i0 is fixed and its frequencies are computed once, in
+// double).  The angle is reduced to [-pi, pi] in double before the f32
+// sine and cosine, so positions in the millions keep f32 accuracy.  x and y
+// may be the same buffer.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(const T *x, T *y, long rows, int N, int d, long pos0,
+                                                   double log2_base, int inverse)
+{
+    const int half = d / 2, tpr = half / kPairs;
+    const long t0 = (long)blockIdx.x * 256 + threadIdx.x;
+    const long stride = (long)gridDim.x * 256;
+    const int i0 = (int)(t0 % tpr) * kPairs;
+    double th[kPairs];
+#pragma unroll
+    for (int e = 0; e < kPairs; ++e) th[e] = rope_theta(i0 + e, d, log2_base);
+    for (long t = t0; t < rows * tpr; t += stride) {
+        const long r = t / tpr;
+        const double p = (double)(pos0 + r % N);
+        float x0[kPairs], x1[kPairs], y0[kPairs], y1[kPairs];
+        load4(x + r * d + i0, x0);
+        load4(x + r * d + half + i0, x1);
+#pragma unroll
+        for (int e = 0; e < kPairs; ++e) {
+            float s, c;
+            rope_sincos(p * th[e], s, c);
+            if (inverse) s = -s;
+            y0[e] = x0[e] * c - x1[e] * s;
+            y1[e] = x0[e] * s + x1[e] * c;
+        }
+        store4(y + r * d + i0, y0);
+        store4(y + r * d + half + i0, y1);
+    }
+}
+
+}  // namespace
+
+hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
+                void *y, hipStream_t st)
+{
+    const long threads = rows * (d / 2 / kPairs);
+    const unsigned blocks = (unsigned)std::min<long>((threads + 255) / 256, 2048L);
+    const double lb = log2(base);
+    if (dt == kBF16)
+        hipLaunchKernelGGL(rope_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t *)x,
+                           (bf16_t *)y, rows, N, d, pos0, lb, inverse);
+    else
+        hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float *)x,
+                           (float *)y, rows, N, d, pos0, lb, inverse);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -322,6 +322,17 @@ def main():
     c_o = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d), **f32)
     c_lse = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq), **f32)
 
+    # the training step over rotated q and k (attn_fwd_rope / attn_bwd_rope), outside the step
+    q_rot, k_rot = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+
+    def fwd_rope():
+        attn.attn_fwd_rope(g["q"], g["k"], g["v"], True, cfg.scale, 10000.0, q_rot=q_rot, k_rot=k_rot,
+                           o=o, lse=lse)
+
+    def bwd_rope():
+        attn.attn_bwd_rope(q_rot, k_rot, g["v"], o, lse, g["dout"], True, cfg.scale, 10000.0, dq=dq,
+                           dk=dk, dv=dv, workspace=bwd_ws)
+
     def fwd_chunk():
         attn.attn_fwd_kv(gc["q"], gc["k"], gc["v"], True, ccfg.scale, o=c_o, lse=c_lse)
 
@@ -351,7 +362,7 @@ def main():
     step_us = train_us + dec_us
     # the measurements beside the step (skipped in the eager counter-collection
     # runs, whose per-kernel counters must describe the step's kernels alone)
-    extras = {"decode_append": None, "fwd_chunk": None}
+    extras = {"decode_append": None, "fwd_chunk": None, "fwd_bwd_rope": None}
     if not args.eager:
         app_us = timer(torch, [decode_append(s) for s in range(K)], K)
         app_bytes = acfg.algorithmic_bytes()
@@ -364,6 +375,10 @@ def main():
                                    # the caches rotate through HBM: compulsory bytes at its peak
                                    "floor_us": round(app_bytes / (BD.PEAK_HBM / 1e6), 3),
                                    "of_floor": round(app_bytes / (BD.PEAK_HBM / 1e6) / app_us, 4)}
+        rope_us = timer(torch, [f for _ in range(K) for f in (fwd_rope, bwd_rope)], K)
+        extras["fwd_bwd_rope"] = {"us_per_step": round(rope_us, 3),
+                                  "TFLOP_s": round((cfg.fwd_flop + cfg.bwd_flop) / (rope_us * 1e-6) / 1e12, 2),
+                                  "rotary_cost_us": round(rope_us - train_us, 3)}
         chunk_us = timer(torch, [fwd_chunk] * K, K)
         chunk_tflops = ccfg.fwd_flop / (chunk_us * 1e-6) / 1e12
         cf = BD.fwd(ccfg.B, ccfg.Hq, ccfg.Hkv, ccfg.Nq, ccfg.Nk, ccfg.d, True,
@@ -478,6 +493,7 @@ def main():
                    "launches_per_call": 2},
         "decode_append": extras["decode_append"],
         "fwd_chunk": extras["fwd_chunk"],
+        "fwd_bwd_rope": extras["fwd_bwd_rope"],
         "kernels": kernels,
         "roofline": roof,
         "timing": ("eager launches between HIP events" if args.eager else

@@ -177,6 +177,51 @@ attn_status attn_bwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, i
                         size_t workspace_bytes, void *stream);
 
 /*
+ * attn_rope -- rotary positions on rows: x, y [B][H][N][d] of dtype dt, row n
+ *   of each head at position pos0 + n.  For pair i in [0, d/2),
+ *   theta_i = base^(-2i/d), a = position * theta_i:
+ *     y_i = x_i cos a - x_{i+d/2} sin a,   y_{i+d/2} = x_i sin a + x_{i+d/2} cos a;
+ *   inverse != 0 applies the transposed rotation (angle -a), which carries a
+ *   gradient with respect to y back to x.  The pages list rotary positions
+ *   beside grouped-query attention ("tang": the "A transformer" panel;
+ *   RustingBrain docs, "What is in the box") without a formula; this is the
+ *   usual rotation on paired halves of the head dimension.  Angles are reduced
+ *   in double precision before f32 sine and cosine.  x and y may be the same
+ *   buffer (device, 16-byte aligned).  base > 0 and finite, |pos0| <= 2^40,
+ *   d in {16, 32, 64, 128}; otherwise ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED.
+ *   One launch on `stream`.
+ */
+attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0, double base,
+                      int inverse, const void *x, void *y, void *stream);
+
+/*
+ * attn_fwd_rope -- attn_fwd_kv over rotated queries and keys: q_rot =
+ *   rope(q) with query row i at position i + (Nk - Nq), k_rot = rope(k) with
+ *   key j at position j (so scores depend on the positions' difference), then
+ *   the forward on (q_rot, k_rot, v).  q_rot [B][Hq][Nq][d] and k_rot
+ *   [B][Hkv][Nk][d] (dtype dt, caller-owned, may alias q and k) receive the
+ *   rotated inputs: attn_bwd_rope takes them, and k_rot is what a key cache
+ *   holds.  Three launches on `stream`.  Other arguments and checks as
+ *   attn_fwd_kv and attn_rope.
+ */
+attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, double base, const void *q, const void *k, const void *v,
+                          void *q_rot, void *k_rot, float *o, float *lse, void *stream);
+
+/*
+ * attn_bwd_rope -- the backward of attn_fwd_rope: attn_bwd_kv at the rotated
+ *   inputs q_rot, k_rot (from attn_fwd_rope), then dq and dk carried back to
+ *   the unrotated q and k by the transposed rotations (in place).  dq, dk, dv
+ *   are the gradients with respect to q, k, v.  dlse may be NULL.  Arguments,
+ *   workspace, streams and checks as attn_bwd_kv and attn_rope.
+ */
+attn_status attn_bwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, double base, const void *q_rot, const void *k_rot,
+                          const void *v, const float *o, const float *lse, const void *dout,
+                          const float *dlse, float *dq, float *dk, float *dv, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * The three stages attn_bwd runs, callable one by one (for example to put the
  * dK/dV stage and the dQ stage on two streams once delta is ready, or to time
  * them).  Arguments mean the same as in attn_bwd; delta [B][Hq][N] f32 is

@@ -39,6 +39,7 @@ def L():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_kv",
+                     "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
                      "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
@@ -209,6 +210,42 @@ def test_bwd_kv_refusals(L):
         if which != 6:                              # dlse may be null
             ptrs[which] = NUL
             assert call(ptrs=ptrs) == INVALID
+
+
+def test_rope_refusals(L):
+    def rope(dt=1, B=1, H=2, N=8, d=64, pos0=0, base=1e4, x=P, y=P):
+        return L.attn_rope(dt, B, H, N, d, pos0, base, 0, x, y, NUL)
+    assert rope(B=0) == INVALID
+    assert rope(N=0) == INVALID
+    assert rope(dt=3) == INVALID
+    assert rope(d=48) == UNSUPPORTED
+    assert rope(base=0.0) == INVALID
+    assert rope(base=-2.0) == INVALID
+    assert rope(base=float("inf")) == INVALID
+    assert rope(pos0=1 << 41) == INVALID
+    assert rope(x=MIS) == INVALID
+    assert rope(y=NUL) == INVALID
+
+    def fwd(Nq=32, Nk=64, base=1e4, ptrs=None):
+        ptrs = ptrs or [P] * 7
+        return L.attn_fwd_rope(1, 1, 4, 2, Nq, Nk, 64, 1, 0.125, base, *ptrs, NUL)
+    assert fwd(Nq=65) == INVALID
+    assert fwd(base=0.0) == INVALID
+    for which in range(7):
+        ptrs = [P] * 7
+        ptrs[which] = MIS
+        assert fwd(ptrs=ptrs) == INVALID
+
+    def bwd(Nq=32, Nk=64, base=1e4, ptrs=None, nb=1 << 20):
+        ptrs = ptrs or [P] * 10
+        return L.attn_bwd_rope(1, 1, 4, 2, Nq, Nk, 64, 1, 0.125, base, *ptrs, P, ctypes.c_size_t(nb), NUL)
+    assert bwd(Nq=65) == INVALID
+    assert bwd(base=float("nan")) == INVALID
+    assert bwd(nb=16) == WORKSPACE
+    for which in range(10):
+        ptrs = [P] * 10
+        ptrs[which] = MIS
+        assert bwd(ptrs=ptrs) == INVALID
 
 
 def test_decode_append_refusals(L):

@@ -342,6 +342,89 @@ def test_bwd_kv_square_equals_bwd(d):
 
 
 # ---------------------------------------------------------------------------
+# rotary positions
+# ---------------------------------------------------------------------------
+
+ROPE = [
+    (2, 3, 37, 64, 0, 10000.0, "bf16"),
+    (1, 4, 130, 128, 4000, 500000.0, "bf16"),
+    (1, 2, 9, 16, 1_000_000, 10000.0, "f32"),     # positions of a million: angle reduction
+    (2, 2, 33, 32, 7, 10.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,pos0,base,dtype", ROPE,
+                         ids=[f"B{c[0]}_H{c[1]}_N{c[2]}_d{c[3]}_p{c[4]}_{c[6]}" for c in ROPE])
+def test_rope(B, H, N, d, pos0, base, dtype):
+    print(f"\n[case] rope B={B} H={H} N={N} d={d} pos0={pos0} {dtype}", flush=True)
+    x = W.random_train(B, H, H, N, d, dtype=dtype, seed=N + d)["q"]
+    gx = _to_dev(x, dtype)
+    for inverse in (False, True):
+        y = attn.attn_rope(gx, pos0, base, inverse=inverse)
+        z = gx.clone()
+        attn.attn_rope(z, pos0, base, inverse=inverse, y=z)            # in place
+        torch.cuda.synchronize()
+        assert torch.equal(y, z)
+        ref = oracle.rope(x, pos0, base, inverse=inverse)
+        got = y.float().cpu().numpy().astype(np.float64)
+        if dtype == "f32":
+            assert float(np.abs(got - ref).max()) <= 1e-6 * max(1.0, float(np.abs(ref).max()))
+        else:   # rounded to bf16: within one bf16 unit in the last place of the exact value
+            assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6 * float(np.abs(x).max()))
+
+
+ATTN_ROPE = [
+    (2, 8, 2, 300, 300, 128, True, "bf16", False),
+    (4, 12, 4, 256, 1024, 64, True, "bf16", True),    # chunk against a cache, with dlse
+    (1, 4, 2, 100, 200, 64, False, "bf16", False),
+    (1, 2, 1, 20, 50, 16, True, "f32", False),        # generic kernels
+    (1, 4, 2, 64, 64, 32, True, "f32", True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype,with_dlse", ATTN_ROPE,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}"
+                              f"_{c[7]}{'_dlse' if c[8] else ''}" for c in ATTN_ROPE])
+def test_attn_rope(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
+    print(f"\n[case] attn_rope B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype} "
+          f"dlse={with_dlse}", flush=True)
+    base = 10000.0
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=7 * Nq + Nk, dout_scale=0.1)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    dl = (np.random.default_rng(Nk).standard_normal((B, Hq, Nq)).astype(np.float32) * 0.3
+          if with_dlse else None)
+    scale = d ** -0.5
+    gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
+    o, lse, q_rot, k_rot = attn.attn_fwd_rope(gq, gk, gv, causal, scale, base)
+    dq, dk, dv = attn.attn_bwd_rope(q_rot, k_rot, gv, o, lse, gdo, causal, scale, base,
+                                    dlse=None if dl is None else torch.from_numpy(dl).cuda())
+    torch.cuda.synchronize()
+    # the rotated inputs are attn_rope's
+    assert torch.equal(q_rot, attn.attn_rope(gq, Nk - Nq, base))
+    assert torch.equal(k_rot, attn.attn_rope(gk, 0, base))
+    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    dl64 = None if dl is None else dl.astype(np.float64)
+    if dtype == "f32":
+        ro, rl = oracle.attn_fwd_rope(q, x["k"], x["v"], causal, scale, base)
+        rdq, rdk, rdv = oracle.attn_bwd_rope(q, x["k"], x["v"], do, causal, scale, base, dl64)
+    else:
+        # the matrix cores take bf16 operands, so the path rounds the rotated q and k to bf16
+        # (test_rope holds that rounding to one unit in the last place); the oracle takes the
+        # same decision on its own exact rotation, then attends and rotates the gradients back
+        qr = W.round_bf16(oracle.rope(q, Nk - Nq, base).astype(np.float32)).astype(np.float64)
+        kr = W.round_bf16(oracle.rope(x["k"], 0, base).astype(np.float32)).astype(np.float64)
+        ro, rl = oracle.attn_fwd(qr, kr, x["v"], causal, scale)
+        if dl64 is None:
+            gq_, gk_, rdv = oracle.attn_bwd(qr, kr, x["v"], do, causal, scale)
+        else:
+            gq_, gk_, rdv = oracle.attn_bwd_dlse(qr, kr, x["v"], do, dl64, causal, scale)
+        rdq = oracle.rope(gq_, Nk - Nq, base, inverse=True)
+        rdk = oracle.rope(gk_, 0, base, inverse=True)
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"attn_rope Nq{Nq} Nk{Nk} d{d}")
+
+
+# ---------------------------------------------------------------------------
 # one decode step with cache append (per-sequence lengths)
 # ---------------------------------------------------------------------------
 
