@@ -272,6 +272,7 @@ attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
                           float scale, double base, const void *q, const void *k, const void *v,
                           void *q_rot, void *k_rot, float *o, float *lse, void *stream)
 {
+    // one launch rotates q and k, then the forward
     if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
     attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
     if (s != ATTN_OK) return s;
@@ -280,8 +281,8 @@ attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
         !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
-    if (attn::rope(dt, (long)B * Hq * Nq, Nq, d, Nk - Nq, base, 0, q, q_rot, st) != hipSuccess ||
-        attn::rope(dt, (long)B * Hkv * Nk, Nk, d, 0, base, 0, k, k_rot, st) != hipSuccess)
+    if (attn::rope2(dt, (long)B * Hq * Nq, Nq, Nk - Nq, q, q_rot, (long)B * Hkv * Nk, Nk, 0, k, k_rot, d,
+                    base, 0, st) != hipSuccess)
         return ATTN_ERR_HIP;
     return hip_status(launch_fwd(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q_rot, k_rot, v, o, lse, st));
 }
@@ -304,8 +305,8 @@ attn_status attn_bwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
                               in_epilogue ? log2(base) : 0.0);
     if (s != ATTN_OK || in_epilogue) return s;
     hipStream_t st = (hipStream_t)stream;
-    if (attn::rope(kF32, (long)B * Hq * Nq, Nq, d, Nk - Nq, base, 1, dq, dq, st) != hipSuccess ||
-        attn::rope(kF32, (long)B * Hkv * Nk, Nk, d, 0, base, 1, dk, dk, st) != hipSuccess)
+    if (attn::rope2(kF32, (long)B * Hq * Nq, Nq, Nk - Nq, dq, dq, (long)B * Hkv * Nk, Nk, 0, dk, dk, d,
+                    base, 1, st) != hipSuccess)
         return ATTN_ERR_HIP;
     return ATTN_OK;
 }

@@ -36,6 +36,9 @@ hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const floa
 // pos0 + r % N (inverse: the transposed rotation); x and y may alias.
 hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
                 void *y, hipStream_t st);
+// The same over two tensors of one dtype and head dim in one launch.
+hipError_t rope2(int dt, long rows0, int N0, long pos00, const void *x0, void *y0, long rows1, int N1,
+                 long pos01, const void *x1, void *y1, int d, double base, int inverse, hipStream_t st);
 // Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
 hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 

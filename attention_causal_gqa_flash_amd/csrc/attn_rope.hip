@@ -47,29 +47,43 @@ __device__ __forceinline__ void store4(float *p, const float (&v)[4])
     *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Row r of `rows` rows of d elements sits at position pos0 + r % N.  A thread
-// owns pairs i0 .. i0+3 of its rows (the grid stride is a multiple of the
-// threads per row, so i0 is fixed and its frequencies are computed once, in
-// double).  The angle is reduced to [-pi, pi] in double before the f32
-// sine and cosine, so positions in the millions keep f32 accuracy.  x and y
-// may be the same buffer.
+// Rows of one tensor: row r of `rows` rows of d elements sits at position
+// pos0 + r % N.
 template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(const T *x, T *y, long rows, int N, int d, long pos0,
-                                                   double log2_base, int inverse)
+struct RopeSeg {
+    const T *x;
+    T *y;
+    long rows;
+    int N;
+    long pos0;
+};
+
+// One launch over one or two tensors (the second may have no rows).  A thread
+// owns pairs i0 .. i0+3 of its rows: the grid stride and the first tensor's
+// thread count are multiples of the threads per row, so i0 is fixed and its
+// frequencies are computed once, in double.  The angle is reduced to [-pi,
+// pi] in double before the f32 sine and cosine, so positions in the millions
+// keep f32 accuracy.  x and y may be the same buffer.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(RopeSeg<T> s0, RopeSeg<T> s1, int d, double log2_base,
+                                                   int inverse)
 {
     const int half = d / 2, tpr = half / kPairs;
     const long t0 = (long)blockIdx.x * 256 + threadIdx.x;
     const long stride = (long)gridDim.x * 256;
+    const long n0 = s0.rows * tpr, n = n0 + s1.rows * tpr;
     const int i0 = (int)(t0 % tpr) * kPairs;
     double th[kPairs];
 #pragma unroll
     for (int e = 0; e < kPairs; ++e) th[e] = rope_theta(i0 + e, d, log2_base);
-    for (long t = t0; t < rows * tpr; t += stride) {
-        const long r = t / tpr;
-        const double p = (double)(pos0 + r % N);
+    for (long t = t0; t < n; t += stride) {
+        const bool first = t < n0;
+        const RopeSeg<T> &sg = first ? s0 : s1;
+        const long r = (first ? t : t - n0) / tpr;
+        const double p = (double)(sg.pos0 + r % sg.N);
         float x0[kPairs], x1[kPairs], y0[kPairs], y1[kPairs];
-        load4(x + r * d + i0, x0);
-        load4(x + r * d + half + i0, x1);
+        load4(sg.x + r * d + i0, x0);
+        load4(sg.x + r * d + half + i0, x1);
 #pragma unroll
         for (int e = 0; e < kPairs; ++e) {
             float s, c;
@@ -78,9 +92,19 @@ __global__ __launch_bounds__(256) void rope_kernel(const T *x, T *y, long rows, 
             y0[e] = x0[e] * c - x1[e] * s;
             y1[e] = x0[e] * s + x1[e] * c;
         }
-        store4(y + r * d + i0, y0);
-        store4(y + r * d + half + i0, y1);
+        store4(sg.y + r * d + i0, y0);
+        store4(sg.y + r * d + half + i0, y1);
     }
+}
+
+template <typename T>
+hipError_t rope_launch(const RopeSeg<T> &s0, const RopeSeg<T> &s1, int d, double base, int inverse,
+                       hipStream_t st)
+{
+    const long threads = (s0.rows + s1.rows) * (d / 2 / kPairs);
+    const unsigned blocks = (unsigned)std::min<long>((threads + 255) / 256, 2048L);
+    hipLaunchKernelGGL(rope_kernel<T>, dim3(blocks), dim3(256), 0, st, s0, s1, d, log2(base), inverse);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -88,16 +112,18 @@ __global__ __launch_bounds__(256) void rope_kernel(const T *x, T *y, long rows, 
 hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
                 void *y, hipStream_t st)
 {
-    const long threads = rows * (d / 2 / kPairs);
-    const unsigned blocks = (unsigned)std::min<long>((threads + 255) / 256, 2048L);
-    const double lb = log2(base);
+    return rope2(dt, rows, N, pos0, x, y, 0, 1, 0, nullptr, nullptr, d, base, inverse, st);
+}
+
+hipError_t rope2(int dt, long rows0, int N0, long pos00, const void *x0, void *y0, long rows1, int N1,
+                 long pos01, const void *x1, void *y1, int d, double base, int inverse, hipStream_t st)
+{
     if (dt == kBF16)
-        hipLaunchKernelGGL(rope_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t *)x,
-                           (bf16_t *)y, rows, N, d, pos0, lb, inverse);
-    else
-        hipLaunchKernelGGL(rope_kernel<float>, dim3(blocks), dim3(256), 0, st, (const float *)x,
-                           (float *)y, rows, N, d, pos0, lb, inverse);
-    return hipGetLastError();
+        return rope_launch<bf16_t>({(const bf16_t *)x0, (bf16_t *)y0, rows0, N0, pos00},
+                                   {(const bf16_t *)x1, (bf16_t *)y1, rows1, N1, pos01}, d, base,
+                                   inverse, st);
+    return rope_launch<float>({(const float *)x0, (float *)y0, rows0, N0, pos00},
+                              {(const float *)x1, (float *)y1, rows1, N1, pos01}, d, base, inverse, st);
 }
 
 }  // namespace attn

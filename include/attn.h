@@ -201,8 +201,8 @@ attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0,
  *   the forward on (q_rot, k_rot, v).  q_rot [B][Hq][Nq][d] and k_rot
  *   [B][Hkv][Nk][d] (dtype dt, caller-owned, may alias q and k) receive the
  *   rotated inputs: attn_bwd_rope takes them, and k_rot is what a key cache
- *   holds.  Three launches on `stream`.  Other arguments and checks as
- *   attn_fwd_kv and attn_rope.
+ *   holds.  Two launches on `stream` (the rotation of q and k, the
+ *   forward).  Other arguments and checks as attn_fwd_kv and attn_rope.
  */
 attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                           float scale, double base, const void *q, const void *k, const void *v,
@@ -210,8 +210,10 @@ attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
 
 /*
  * attn_bwd_rope -- the backward of attn_fwd_rope: attn_bwd_kv at the rotated
- *   inputs q_rot, k_rot (from attn_fwd_rope), then dq and dk carried back to
- *   the unrotated q and k by the transposed rotations (in place).  dq, dk, dv
+ *   inputs q_rot, k_rot (from attn_fwd_rope), with dq and dk carried back to
+ *   the unrotated q and k by the transposed rotations: in the gradient
+ *   kernels' epilogues on the bf16 matrix-core path (hardware sine and cosine
+ *   of the angle reduced in double, about 1e-6), else by one more launch.  dq, dk, dv
  *   are the gradients with respect to q, k, v.  dlse may be NULL.  Arguments,
  *   workspace, streams and checks as attn_bwd_kv and attn_rope.
  */
