@@ -15,6 +15,7 @@ import os
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
            "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
+           "attn_fwd_ex", "attn_bwd_ex",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_kv.argtypes = [i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
     L.attn_bwd_kv.restype = i
     dbl, ll = ctypes.c_double, ctypes.c_longlong
+    L.attn_fwd_ex.argtypes = [i, i, i, i, i, i, i, i, i, f, p, p, p, p, p, p]
+    L.attn_fwd_ex.restype = i
+    L.attn_bwd_ex.argtypes = [i, i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
+    L.attn_bwd_ex.restype = i
     L.attn_rope.argtypes = [i, i, i, i, i, ll, dbl, i, p, p, p]
     L.attn_rope.restype = i
     L.attn_fwd_rope.argtypes = [i, i, i, i, i, i, i, i, f, dbl] + [p] * 7 + [p]
@@ -197,11 +202,11 @@ def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, worksp
         _dev(t, n)
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
-    if fn not in ("attn_bwd_kv", "attn_bwd_rope") and Nk != Nq:
+    if fn not in ("attn_bwd_kv", "attn_bwd_rope", "attn_bwd_ex") and Nk != Nq:
         raise ValueError(f"{fn} needs as many keys as queries (attn_bwd_kv takes Nk > Nq)")
     if dout.shape != q.shape or dout.dtype != q.dtype:
         raise ValueError("dout must match q in shape and dtype")
-    if o.dtype != torch.float32 or lse.dtype != torch.float32:
+    if (o.dtype != torch.float32 and fn != "attn_bwd_ex") or lse.dtype != torch.float32:
         raise ValueError("o and lse must be the float32 outputs of the forward")
     scale = float(d) ** -0.5 if scale is None else float(scale)
     code = _dtype_code(q)
@@ -222,7 +227,8 @@ def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, worksp
         raise ValueError("attn_bwd_dlse needs dlse")
     else:
         dlse_p = None
-    head = (code, B, Hq, Hkv) + ((Nq, Nk) if fn in ("attn_bwd_kv", "attn_bwd_rope") else (Nq,)) + \
+    head = ((code, _dtype_code(o)) if fn == "attn_bwd_ex" else (code,)) + (B, Hq, Hkv) + \
+        ((Nq, Nk) if fn in ("attn_bwd_kv", "attn_bwd_rope", "attn_bwd_ex") else (Nq,)) + \
         (d, int(bool(causal)), scale) + ((float(base),) if fn == "attn_bwd_rope" else ()) + \
         (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout))
     tail = (_ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
@@ -299,6 +305,33 @@ def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None, o=None
                            _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
     _check("attn_fwd_kv", rc)
     return o, lse
+
+
+def attn_fwd_ex(q, k, v, causal: bool = True, scale: float | None = None, o_dtype=None, o=None,
+                lse=None, stream=None):
+    """The general forward: q [B,Hq,Nq,d] against k, v [B,Hkv,Nk,d] (Nk >= Nq), o in o_dtype
+    (torch.float32, the default, or torch.bfloat16).  Returns (o, lse)."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    o_dtype = torch.float32 if o_dtype is None else o_dtype
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=o_dtype)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    rc = lib().attn_fwd_ex(_dtype_code(q), _dtype_code(o), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                           scale, _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
+                           _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    _check("attn_fwd_ex", rc)
+    return o, lse
+
+
+def attn_bwd_ex(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, dq=None,
+                dk=None, dv=None, workspace=None, stream=None, dlse=None):
+    """The general backward: o from attn_fwd_ex in either dtype, dlse optional."""
+    return _bwd_call("attn_bwd_ex", q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv,
+                     workspace, stream)
 
 
 def attn_rope(x, pos0: int, base: float, inverse: bool = False, y=None, stream=None):

@@ -63,23 +63,24 @@ size_t workspace_bytes(int B, int Hq, int N)
 // dk/dv zero-fill piggybacked on the preprocess launch when the dK/dV kernel
 // will accumulate into them (zero_dkdv), else plain preprocess.
 hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                                 const float *o, const void *dout, float *delta, float *dk,
+                                 const void *o, const void *dout, float *delta, float *dk,
                                  float *dv, bool zero_dkdv, hipStream_t st,
-                                 const float *dlse = nullptr)
+                                 const float *dlse = nullptr, bool o_bf16 = false)
 {
     const long n = (long)B * Hkv * Nk * d;
     return attn::bwd_preprocess(dt, (long)B * Hq * Nq, d, dout, o, delta, zero_dkdv ? dk : nullptr,
-                                zero_dkdv ? dv : nullptr, n, dlse, st);
+                                zero_dkdv ? dv : nullptr, n, dlse, st, o_bf16);
 }
 
 // Forward of Nq queries against Nk >= Nq keys (arguments already validated).
 hipError_t launch_fwd(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                      float scale, const void *q, const void *k, const void *v, float *o,
-                      float *lse, hipStream_t st)
+                      float scale, const void *q, const void *k, const void *v, void *o,
+                      float *lse, hipStream_t st, bool o_bf16 = false)
 {
     if (use_mfma(dt, Nk, d, scale))
-        return attn::fwd_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st);
-    return attn::fwd_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st);
+        return attn::fwd_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st, o_bf16);
+    return attn::fwd_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st,
+                             o_bf16);
 }
 
 // Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
@@ -191,9 +192,10 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int
 // (with the upstream lse gradient folded into delta when dlse is given), then
 // the gradient stage.
 attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                      float scale, const void *q, const void *k, const void *v, const float *o,
+                      float scale, const void *q, const void *k, const void *v, const void *o,
                       const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
-                      float *dv, void *workspace, size_t ws_bytes, void *stream, double rope_lb = 0.0)
+                      float *dv, void *workspace, size_t ws_bytes, void *stream, double rope_lb = 0.0,
+                      bool o_bf16 = false)
 {
     if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
     attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
@@ -206,7 +208,7 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
     float *delta = (float *)workspace;
     const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale);
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, Nq, Nk, d, o, dout, delta, dk, dv, hs > 1, st,
-                              dlse) != hipSuccess)
+                              dlse, o_bf16) != hipSuccess)
         return ATTN_ERR_HIP;
     return launch_bwd_grads(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta,
                             dq, dk, dv, hs, st, rope_lb);
@@ -255,6 +257,32 @@ attn_status attn_bwd_dlse(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, i
     if (!aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
     return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
                      dv, workspace, ws_bytes, stream);
+}
+
+attn_status attn_fwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                        int d, int causal, float scale, const void *q, const void *k,
+                        const void *v, void *o, float *lse, void *stream)
+{
+    if (o_dt != ATTN_F32 && o_dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_fwd(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse,
+                                 (hipStream_t)stream, o_dt == ATTN_BF16));
+}
+
+attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                        int d, int causal, float scale, const void *q, const void *k,
+                        const void *v, const void *o, const float *lse, const void *dout,
+                        const float *dlse, float *dq, float *dk, float *dv, void *workspace,
+                        size_t ws_bytes, void *stream)
+{
+    if (o_dt != ATTN_F32 && o_dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (dlse != nullptr && !aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    return bwd_whole(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
+                     dv, workspace, ws_bytes, stream, 0.0, o_dt == ATTN_BF16);
 }
 
 attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0, double base,

@@ -160,10 +160,11 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // (row half, key half) -- the two key halves stream disjoint halves of the
 // key tiles side by side and their softmax states combine through LDS at the
 // end with the associative merge, which halves the longest chain of tiles.
-template <int D, int KSPLIT, int TN>
+// OBF: O is written in bf16 (rounded to nearest even) instead of f32.
+template <int D, int KSPLIT, int TN, bool OBF>
 __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
+    const uint16_t *__restrict__ V, void *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
     int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
 {
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
@@ -309,14 +310,18 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (qi < Nq) {
         const float inv = 1.f / l_tot;
-        float *orow = O + (((size_t)b * Hq + h) * Nq + qi) * D;
+        const size_t orow = (((size_t)b * Hq + h) * Nq + qi) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int d0 = db * 32 + 8 * a + 4 * hf;
-                *(float4 *)(orow + d0) = make_float4(st.oacc[db][4 * a + 0] * inv, st.oacc[db][4 * a + 1] * inv,
-                                                     st.oacc[db][4 * a + 2] * inv, st.oacc[db][4 * a + 3] * inv);
+                const float o0 = st.oacc[db][4 * a + 0] * inv, o1 = st.oacc[db][4 * a + 1] * inv;
+                const float o2 = st.oacc[db][4 * a + 2] * inv, o3 = st.oacc[db][4 * a + 3] * inv;
+                if constexpr (OBF)
+                    *(uint2 *)((uint16_t *)O + orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                else
+                    *(float4 *)((float *)O + orow + d0) = make_float4(o0, o1, o2, o3);
             }
         // lse = ln(sum exp(scale q.k)) = (m + log2 l) * ln 2
         if (hf == 0) LSE[((size_t)b * Hq + h) * Nq + qi] = (st.m_run + __log2f(l_tot)) * kLn2;
@@ -327,9 +332,12 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
 
 bool mfma_supported(int dt, int d) { return dt == kBF16 && (d == 64 || d == 128); }
 
-hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                    const void *q, const void *k, const void *v, float *o, float *lse,
-                    hipStream_t st)
+namespace {
+
+template <bool OBF>
+hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, void *o, float *lse,
+                           hipStream_t st)
 {
     static int cus = 0;
     if (cus == 0) {
@@ -353,21 +361,31 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, f
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     const int nqt64 = (Nq + 63) / 64;
     if (d == 128 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN, OBF>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 128) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2, kBN>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2, kBN, OBF>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
                            lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else if (d == 64 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN, OBF>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
     } else if (d == 64) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32, OBF>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
                            B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
     } else {
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    const void *q, const void *k, const void *v, void *o, float *lse,
+                    hipStream_t st, bool o_bf16)
+{
+    if (o_bf16) return fwd_mfma_launch<true>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st);
+    return fwd_mfma_launch<false>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st);
 }
 
 }  // namespace attn

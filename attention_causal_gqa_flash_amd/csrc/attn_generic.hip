@@ -16,13 +16,20 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------
-// Forward, one thread per query row.
+// Forward, one thread per query row; O of type OT (f32, or bf16 rounded to
+// nearest even).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+__device__ __forceinline__ void put(float *p, float x) { *p = x; }
+__device__ __forceinline__ void put(bf16_t *p, float x)
+{
+    p->bits = __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+template <typename T, int D, typename OT>
 __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q,
                                                          const T *__restrict__ k,
                                                          const T *__restrict__ v,
-                                                         float *__restrict__ o,
+                                                         OT *__restrict__ o,
                                                          float *__restrict__ lse, int Hq, int Hkv,
                                                          int Nq, int Nk, float scale, int causal)
 {
@@ -67,10 +74,10 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
         for (int c = 0; c < D; ++c) acc[c] = fmaf(p, to_f32(vj[c]), acc[c]);
     }
     if (i < Nq) {
-        float *oh = o + (((size_t)b * Hq + h) * Nq + i) * D;
+        OT *oh = o + (((size_t)b * Hq + h) * Nq + i) * D;
         const float inv = 1.f / l;
 #pragma unroll
-        for (int c = 0; c < D; ++c) oh[c] = acc[c] * inv;
+        for (int c = 0; c < D; ++c) put(oh + c, acc[c] * inv);
         lse[((size_t)b * Hq + h) * Nq + i] = m + logf(l);
     }
 }
@@ -95,9 +102,9 @@ __global__ __launch_bounds__(256) void zero_fill2_kernel(float *__restrict__ a, 
     zero2_grid_stride(a, b, n);
 }
 
-template <typename T, int D>
+template <typename T, int D, typename OT>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout,
-                                                      const float *__restrict__ o,
+                                                      const OT *__restrict__ o,
                                                       float *__restrict__ Dws, long rows,
                                                       float *__restrict__ zero,
                                                       float *__restrict__ zero2, long zero_len,
@@ -111,8 +118,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
     float s = 0.f;
     if (row < rows) {
         const size_t base = (size_t)row * D + part * 8;
-        const float4 o0 = *(const float4 *)(o + base);
-        const float4 o1 = *(const float4 *)(o + base + 4);
+        float4 o0, o1;
+        if constexpr (sizeof(OT) == 2) {
+            const uint4 u = *(const uint4 *)((const uint16_t *)o + base);
+            o0 = make_float4(bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y));
+            o1 = make_float4(bf16lo(u.z), bf16hi(u.z), bf16lo(u.w), bf16hi(u.w));
+        } else {
+            o0 = *(const float4 *)((const float *)o + base);
+            o1 = *(const float4 *)((const float *)o + base + 4);
+        }
         float dv[8];
         if constexpr (sizeof(T) == 2) {
             const uint4 u = *(const uint4 *)((const uint16_t *)dout + base);
@@ -441,27 +455,43 @@ __global__ __launch_bounds__(128) void lse_merge_kernel(const float *__restrict_
     else { typedef float T; __VA_ARGS__; }
 
 hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                       float scale, const void *q, const void *k, const void *v, float *o,
-                       float *lse, hipStream_t st)
+                       float scale, const void *q, const void *k, const void *v, void *o,
+                       float *lse, hipStream_t st, bool o_bf16)
 {
     dim3 grid((Nq + 63) / 64, Hq, B);
-    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D>), grid,
-                                                              dim3(64), 0, st, (const T *)q,
-                                                              (const T *)k, (const T *)v, o, lse,
-                                                              Hq, Hkv, Nq, Nk, scale, causal)));
+    if (o_bf16) {
+        ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, bf16_t>), grid,
+                                                                  dim3(64), 0, st, (const T *)q,
+                                                                  (const T *)k, (const T *)v,
+                                                                  (bf16_t *)o, lse, Hq, Hkv, Nq, Nk,
+                                                                  scale, causal)));
+    } else {
+        ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, float>), grid,
+                                                                  dim3(64), 0, st, (const T *)q,
+                                                                  (const T *)k, (const T *)v,
+                                                                  (float *)o, lse, Hq, Hkv, Nq, Nk,
+                                                                  scale, causal)));
+    }
     return hipGetLastError();
 }
 
-hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
+hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const void *o, float *Dws,
                           float *zero, float *zero2, long zero_len, const float *dlse,
-                          hipStream_t st)
+                          hipStream_t st, bool o_bf16)
 {
     const int rpb = 256 / (d / 8);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-    ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D>), grid,
-                                                              dim3(256), 0, st, (const T *)dout,
-                                                              o, Dws, rows, zero, zero2,
-                                                              zero_len, dlse)));
+    if (o_bf16) {
+        ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D, bf16_t>), grid,
+                                                                  dim3(256), 0, st, (const T *)dout,
+                                                                  (const bf16_t *)o, Dws, rows, zero,
+                                                                  zero2, zero_len, dlse)));
+    } else {
+        ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D, float>), grid,
+                                                                  dim3(256), 0, st, (const T *)dout,
+                                                                  (const float *)o, Dws, rows, zero,
+                                                                  zero2, zero_len, dlse)));
+    }
     return hipGetLastError();
 }
 

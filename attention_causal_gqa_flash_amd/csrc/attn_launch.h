@@ -12,10 +12,11 @@ namespace attn {
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
 // Generic kernels: any supported (dtype, d); one thread per query row or key row.
-// Forward of Nq queries against Nk >= Nq keys (query i at key position i + Nk - Nq).
+// Forward of Nq queries against Nk >= Nq keys (query i at key position i + Nk - Nq);
+// o is f32, or bf16 with o_bf16.
 hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                       float scale, const void *q, const void *k, const void *v, float *o,
-                       float *lse, hipStream_t st);
+                       float scale, const void *q, const void *k, const void *v, void *o,
+                       float *lse, hipStream_t st, bool o_bf16 = false);
 // The backward launchers take Nq query rows against Nk >= Nq keys in the same
 // alignment (Nq == Nk: the square case).
 hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
@@ -29,9 +30,9 @@ hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int 
 
 // D_i = dout_i . o_i for every query row (rows = B*Hq*N).  With zero != nullptr
 // the same launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
-hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const float *o, float *Dws,
+hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const void *o, float *Dws,
                           float *zero, float *zero2, long zero_len, const float *dlse,
-                          hipStream_t st);
+                          hipStream_t st, bool o_bf16 = false);
 // Rotary positions on `rows` rows of d elements of dtype dt, row r at position
 // pos0 + r % N (inverse: the transposed rotation); x and y may alias.
 hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
@@ -48,8 +49,8 @@ hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 // transposed rotations in their epilogues.
 bool mfma_supported(int dt, int d);
 hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                    const void *q, const void *k, const void *v, float *o, float *lse,
-                    hipStream_t st);
+                    const void *q, const void *k, const void *v, void *o, float *lse,
+                    hipStream_t st, bool o_bf16 = false);
 // Number of workgroups each group's query heads are split over by the dK/dV
 // kernel; with more than one, dk and dv must be zero-filled before the launch
 // (the kernel adds into them).

@@ -177,6 +177,29 @@ attn_status attn_bwd_kv(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, i
                         size_t workspace_bytes, void *stream);
 
 /*
+ * attn_fwd_ex -- the general forward: attn_fwd_kv (Nq <= Nk, bottom-right
+ *   causal) with the output dtype chosen by o_dt: ATTN_F32 (as attn_fwd_kv),
+ *   or ATTN_BF16 (o rounded to nearest even, half the bytes written and read
+ *   back by the backward; lse stays f32).  o [B][Hq][Nq][d] of dtype o_dt.
+ *   o_dt other than these two: ATTN_ERR_INVALID_ARG; other checks as
+ *   attn_fwd_kv.  One launch on `stream`.
+ */
+attn_status attn_fwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                        int d, int causal, float scale, const void *q, const void *k,
+                        const void *v, void *o, float *lse, void *stream);
+
+/*
+ * attn_bwd_ex -- the general backward: attn_bwd_kv taking o in dtype o_dt
+ *   (the output of attn_fwd_ex with the same o_dt); dlse may be NULL.
+ *   Gradients stay f32.  Other arguments and checks as attn_bwd_kv.
+ */
+attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                        int d, int causal, float scale, const void *q, const void *k,
+                        const void *v, const void *o, const float *lse, const void *dout,
+                        const float *dlse, float *dq, float *dk, float *dv, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
  * attn_rope -- rotary positions on rows: x, y [B][H][N][d] of dtype dt, row n
  *   of each head at position pos0 + n.  For pair i in [0, d/2),
  *   theta_i = base^(-2i/d), a = position * theta_i:

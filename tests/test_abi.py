@@ -39,7 +39,7 @@ def L():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_kv",
-                     "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
+                     "attn_rope", "attn_fwd_rope", "attn_bwd_rope", "attn_fwd_ex", "attn_bwd_ex",
                      "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
@@ -210,6 +210,30 @@ def test_bwd_kv_refusals(L):
         if which != 6:                              # dlse may be null
             ptrs[which] = NUL
             assert call(ptrs=ptrs) == INVALID
+
+
+def test_ex_refusals(L):
+    def fwd(o_dt=1, Nq=32, Nk=64, ptrs=None):
+        ptrs = ptrs or [P] * 5
+        return L.attn_fwd_ex(1, o_dt, 1, 4, 2, Nq, Nk, 64, 1, 0.125, *ptrs, NUL)
+    assert fwd(o_dt=2) == INVALID
+    assert fwd(o_dt=-1) == INVALID
+    assert fwd(Nq=65) == INVALID
+    for which in range(5):
+        ptrs = [P] * 5
+        ptrs[which] = MIS
+        assert fwd(ptrs=ptrs) == INVALID
+
+    def bwd(o_dt=1, Nq=32, Nk=64, ptrs=None, nb=1 << 20):
+        ptrs = ptrs or [P] * 10
+        return L.attn_bwd_ex(1, o_dt, 1, 4, 2, Nq, Nk, 64, 1, 0.125, *ptrs, P, ctypes.c_size_t(nb), NUL)
+    assert bwd(o_dt=7) == INVALID
+    assert bwd(Nq=65) == INVALID
+    assert bwd(nb=16) == WORKSPACE
+    for which in range(10):
+        ptrs = [P] * 10
+        ptrs[which] = MIS
+        assert bwd(ptrs=ptrs) == INVALID
 
 
 def test_rope_refusals(L):

@@ -76,7 +76,7 @@ def _profile_avg_us(kernel_prefix):
 
 
 @pytest.mark.parametrize("kernel,floor", [
-    ("fwd_mfma_kernel<64, 2, 32>", lambda: BD.fwd(4, 12, 4, 1024, 1024, 64, True, 64, 32)),
+    ("fwd_mfma_kernel<64, 2, 32", lambda: BD.fwd(4, 12, 4, 1024, 1024, 64, True, 64, 32)),
     ("bwd_fused_kernel<64", lambda: BD.bwd_grads(4, 12, 4, 1024, 1024, 64, True, 64, 128, 3, 128, 64)),
     ("decode_mfma_kernel<128, false>", lambda: BD.decode(1, 32, 8, 4096, 128, 16, resident=False)),
 ])

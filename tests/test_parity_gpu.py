@@ -342,6 +342,44 @@ def test_bwd_kv_square_equals_bwd(d):
 
 
 # ---------------------------------------------------------------------------
+# bf16 output (attn_fwd_ex / attn_bwd_ex)
+# ---------------------------------------------------------------------------
+
+EX = [
+    (4, 12, 4, 1024, 1024, 64, True, "bf16"),    # key-split forward, one-launch gradients
+    (2, 16, 4, 700, 700, 64, True, "bf16"),      # 128-row forward tiles
+    (1, 8, 2, 300, 800, 128, True, "bf16"),
+    (1, 4, 2, 100, 100, 32, False, "bf16"),      # generic kernels, bf16 inputs
+    (1, 2, 1, 40, 70, 16, True, "f32"),          # generic kernels, f32 inputs
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype", EX,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}_{c[7]}"
+                              for c in EX])
+def test_bf16_output(B, Hq, Hkv, Nq, Nk, d, causal, dtype):
+    print(f"\n[case] bf16 output B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype}",
+          flush=True)
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq + 5 * Nk, dout_scale=0.1)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    scale = d ** -0.5
+    gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
+    o16, l16 = attn.attn_fwd_ex(gq, gk, gv, causal, scale, o_dtype=torch.bfloat16)
+    o32, l32 = attn.attn_fwd_ex(gq, gk, gv, causal, scale)
+    dq, dk, dv = attn.attn_bwd_ex(gq, gk, gv, o16, l16, gdo, causal, scale)
+    torch.cuda.synchronize()
+    # the same kernels: the bf16 output is the f32 output rounded to nearest even
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
+    got = [t.float().cpu().numpy().astype(np.float64) for t in (o16, l16, dq, dk, dv)]
+    ro, rl = oracle.attn_fwd(q, x["k"], x["v"], causal, scale)
+    rdq, rdk, rdv = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
+    # o is now bf16 on both input dtypes: the bf16 bounds apply (o 1e-2, lse 1e-3, grads 2e-2)
+    _check(got, (ro, rl, rdq, rdk, rdv), "bf16", label=f"bf16 out Nq{Nq} Nk{Nk} d{d}")
+
+
+# ---------------------------------------------------------------------------
 # rotary positions
 # ---------------------------------------------------------------------------
 
