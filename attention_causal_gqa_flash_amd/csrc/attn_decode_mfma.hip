@@ -162,8 +162,7 @@ __global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
                 sacc[kb][r] = x;
                 mx = fmaxf(mx, x);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = pair32_max(pair16_max(mx));
         const float m_new = fmaxf(m_run, mx);            // finite: the block's first key is valid
         const float alpha = m_run == -INFINITY ? 0.f : exp2_fast(m_run - m_new);
         float rs = 0.f;
@@ -210,8 +209,7 @@ __global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
     }
 
     // ---- per-wave state -> LDS, then combine the 8 waves ----
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = pair32_sum(pair16_sum(l_run));
     __syncthreads();                                   // V slices are no longer read
     float *wo = reinterpret_cast<float *>(smem);       // [wave][head 16][D]
     float *wm = wo + kWaves * 16 * D;                  // [wave][16]

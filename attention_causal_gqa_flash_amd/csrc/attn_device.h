@@ -247,6 +247,33 @@ __device__ __forceinline__ bf16x8 pack_operand(f32x16 acc)
                                 pack_bf16x2(acc[R0 + 4], acc[R0 + 5]), pack_bf16x2(acc[R0 + 6], acc[R0 + 7])));
 }
 
+// Max / sum of x over the lane pair (l, l ^ 32), or (l, l ^ 16), in every lane
+// of the pair, without the LDS round trip of a shuffle: v_permlane32_swap
+// (v_permlane16_swap) exchanges the two 32-lane (16-lane) halves of two
+// registers, so with both holding x each lane ends with its own value and its
+// partner's, one in each result (which one is which does not matter to a
+// symmetric combine).
+__device__ __forceinline__ float pair32_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

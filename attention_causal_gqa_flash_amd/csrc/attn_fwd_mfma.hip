@@ -109,7 +109,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 #pragma unroll
         for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
     float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+    mx = pair32_max(mx) * c2;
     // Lazy rescale: raise the running max only when some row of the wave grew
     // past it by more than kLazy.  A row that has seen no key yet keeps -inf
     // (its probabilities are then exact zeros, see nm).
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         st.m_run = m;
     }
 
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    const float l_tot = pair32_sum(st.l_run);
     if (qi < Nq) {
         const float inv = 1.f / l_tot;
         const size_t orow = (((size_t)b * Hq + h) * Nq + qi) * D;
