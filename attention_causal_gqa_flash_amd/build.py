@@ -29,14 +29,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def compile_flags() -> list:
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # keep MFMA accumulators in VGPR form: the default AGPR form made the
-            # backward kernels copy every accumulator between AGPRs and VGPRs
-            # around each MFMA
-            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
+# Sources whose MFMA accumulators the compiler may place in AGPRs: in the
+# backward's d = 128 dK/dV kernel (one wave per SIMD, 512 registers) the dK and
+# dV accumulators then sit in AGPRs, which frees enough VGPRs to keep eight LDS
+# operand reads in flight (4096-token dK/dV kernel 321 -> 303 us); its d = 64
+# kernels compile to the same code either way.
+AGPR_FORM = ("attn_bwd_mfma.hip",)
+
+
+def compile_flags(src: str = "") -> list:
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if os.path.basename(src) not in AGPR_FORM:
+        # keep MFMA accumulators in VGPR form: with the AGPR form the score
+        # accumulators, which the softmax reads, are copied from AGPRs to
+        # VGPRs after every block, and the forward's split kernel runs slower
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+    return flags + ["-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def build(verbose: bool = False) -> str:
@@ -47,7 +56,7 @@ def build(verbose: bool = False) -> str:
     procs, objs = [], []
     for src in srcs:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [cc, *compile_flags(), "-c", src, "-o", obj]
+        cmd = [cc, *compile_flags(src), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

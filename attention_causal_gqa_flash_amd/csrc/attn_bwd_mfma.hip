@@ -83,8 +83,6 @@ __device__ __forceinline__ void dkdv_scores(const uint16_t *qt, const uint16_t *
     constexpr int KS = D / 16;
     const int l32 = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
-#pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 aq = tile_row_operand<D>(qt, 32 * qh + l32, 2 * ks + hf);
         const bf16x8 ad = tile_row_operand<D>(dt, 32 * qh + l32, 2 * ks + hf);
@@ -93,37 +91,28 @@ __device__ __forceinline__ void dkdv_scores(const uint16_t *qt, const uint16_t *
     }
 }
 
-// lse and D of the block's rows (register r: local row 32qh + 8(r/4) + 4hf + r%4)
-struct RowStats {
-    float4 l[4], d[4];
-};
-
-__device__ __forceinline__ RowStats dkdv_rows(const float *lt, const float *ddt, int qh, int lane)
+// The row terms of the block's rows as the initial S and dP accumulators
+// (register r: local row 32qh + 8(r/4) + 4hf + r%4): the LDS row arrays hold
+// -lse_i / |scale| and -D_i, so the MFMAs leave q.k - lse_i / |scale| and
+// dP - D_i, and P = 2^(c2 (q.k - lse_i / |scale|)) = e^(scale q.k - lse_i)
+// takes one multiply and one exponential per score.
+__device__ __forceinline__ void dkdv_rows(const float *lt, const float *ddt, int qh, int lane,
+                                          f32x16 &sacc, f32x16 &pacc)
 {
-    RowStats rs;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int rr = 32 * qh + 8 * a + 4 * (lane >> 5);
-        rs.l[a] = *(const float4 *)&lt[rr];
-        rs.d[a] = *(const float4 *)&ddt[rr];
+        const float4 l = *(const float4 *)&lt[rr];
+        const float4 d = *(const float4 *)&ddt[rr];
+        sacc[4 * a + 0] = l.x; sacc[4 * a + 1] = l.y; sacc[4 * a + 2] = l.z; sacc[4 * a + 3] = l.w;
+        pacc[4 * a + 0] = d.x; pacc[4 * a + 1] = d.y; pacc[4 * a + 2] = d.z; pacc[4 * a + 3] = d.w;
     }
-    return rs;
 }
 
-__device__ __forceinline__ void dkdv_probs(const RowStats &rs, f32x16 &sacc, f32x16 &pacc, float c2,
-                                           bool mask, int t)
+__device__ __forceinline__ void dkdv_probs(f32x16 &sacc, f32x16 &pacc, float c2, bool mask, int t)
 {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const float lv[4] = {rs.l[a].x * kLog2e, rs.l[a].y * kLog2e, rs.l[a].z * kLog2e, rs.l[a].w * kLog2e};
-        const float dv[4] = {rs.d[a].x, rs.d[a].y, rs.d[a].z, rs.d[a].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a + e;
-            sacc[r] = exp2_fast(fmaf(sacc[r], c2, -lv[e]));
-            pacc[r] = pacc[r] - dv[e];
-        }
-    }
+    for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(sacc[r] * c2);
     // Register r holds query row q0 + 32qh + 4hf + c, c = 8(r/4) + r%4 (a
     // constant): the causal mask keeps c >= t = kj - off - (q0 + 32qh + 4hf)
     // (key kj is visible to query rows at or after kj - off), one compare and
@@ -160,8 +149,8 @@ __device__ __forceinline__ void dkdv_grads(const uint16_t *qt, const uint16_t *d
     }
 }
 
-// One sub-step, the three phases in sequence (the block's lse and D rows
-// are all read before its probabilities are computed).  kq = kj - off: the
+// One sub-step, the three phases in sequence (the block's row terms are read
+// first: they are the score accumulators' initial values).  kq = kj - off: the
 // first query row that sees this lane's key.
 template <int D>
 __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *dt, const float *lt,
@@ -172,10 +161,10 @@ __device__ __forceinline__ void dkdv_block(const uint16_t *qt, const uint16_t *d
 {
     constexpr int KS = D / 16, DB = D / 32;
     f32x16 sacc, pacc;
+    dkdv_rows(lt, ddt, qh, lane, sacc, pacc);
     dkdv_scores<D>(qt, dt, kf, vf, sacc, pacc, qh, lane);
-    sched_pipeline<2 * KS, 2 * KS, kAhead, 1>();
-    const RowStats rs = dkdv_rows(lt, ddt, qh, lane);
-    dkdv_probs(rs, sacc, pacc, c2, mask, kq - (q0 + 32 * qh + 4 * (lane >> 5)));
+    sched_pipeline<2 * KS + 8, 2 * KS, kAhead + 8, 1>();
+    dkdv_probs(sacc, pacc, c2, mask, kq - (q0 + 32 * qh + 4 * (lane >> 5)));
     dkdv_grads<D>(qt, dt, sacc, pacc, dka, dva, qh, lane);
     sched_pipeline<8 * DB, 4 * DB, kAheadT, 2>();
 }
@@ -266,31 +255,35 @@ __device__ __forceinline__ void dkdv_body(
     const int steps = Gs * nq;               // (query head, query tile) pairs
 
     // Step s covers query head g*G + hsub*Gs + s/nq, query rows (qt0 + s%nq)*SR
-    // .. +SR-1.  Its Q and dO tiles and its lse and D rows move global -> LDS
-    // directly (waves 0/1 copy the two halves of lse, waves 2/3 those of D);
-    // rows past Nq read as zero and are masked in the step's arithmetic.
+    // .. +SR-1.  Its Q and dO tiles move global -> LDS directly; its lse and
+    // D rows go through a register of waves 0/1 (the two halves of lse) and
+    // 2/3 (those of D), which store them as -lse / |scale| and -D at the top
+    // of the step.  Rows past Nq read as zero and are masked in the step's
+    // arithmetic.
     const uint32_t tile_bytes = (uint32_t)Nq * D * 2, row_bytes = (uint32_t)Nq * 4;
     const TileCopy<D, SR, 4> copy(wave, lane);
-    auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd, float *ld, float *ed) {
+    const float row_mul = wave < 2 ? -1.f / fabsf(scale) : -1.f;
+    float row_v = 0.f;                       // this lane's row term of the next step
+    auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd) {
         const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * Nq;
         const int q0_ = (qt0 + s_ % nq) * SR;
         copy(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave);
         copy(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave);
         const int half = wave & 1;
-        if (wave < 2) row_load_lds(ld + 64 * half, make_rsrc(LSE + hrow, row_bytes), q0_ + 64 * half, lane);
-        else row_load_lds(ed + 64 * half, make_rsrc(Dws + hrow, row_bytes), q0_ + 64 * half, lane);
+        row_v = row_load(make_rsrc((wave < 2 ? LSE : Dws) + hrow, row_bytes), q0_ + 64 * half, lane);
     };
-    if (steps > 0) load_step(0, q0s, d0s, l0s, e0s);
+    if (steps > 0) load_step(0, q0s, d0s);
 
     auto run_step = [&](auto bufc, int s) {
         constexpr int BI = decltype(bufc)::value;
         const uint16_t *qc = BI ? q1s : q0s, *dc = BI ? d1s : d0s;
-        const float *lc = BI ? l1s : l0s, *ec = BI ? e1s : e0s;
+        float *lc = BI ? l1s : l0s, *ec = BI ? e1s : e0s;
         wait_vmcnt<0>();                    // this wave's copies of step s have landed
+        (wave < 2 ? lc : ec)[64 * (wave & 1) + lane] = row_v * row_mul;
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
         if (s + 1 < steps) {
-            if (BI) load_step(s + 1, q0s, d0s, l0s, e0s);
-            else load_step(s + 1, q1s, d1s, l1s, e1s);
+            if (BI) load_step(s + 1, q0s, d0s);
+            else load_step(s + 1, q1s, d1s);
         }
         const int qs = (qt0 + s % nq) * SR;  // first query row of the step
 #pragma unroll

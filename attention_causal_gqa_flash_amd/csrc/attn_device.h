@@ -160,6 +160,13 @@ __device__ __forceinline__ void row_load_lds(float *dst, __amdgpu_buffer_rsrc_t 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, (r0 + lane) * 4, 0, 0, 0);
 }
 
+// One f32 per lane, element r0 + lane of the f32 array behind the resource
+// (zero past its end), into a register.
+__device__ __forceinline__ float row_load(__amdgpu_buffer_rsrc_t rs, int r0, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (r0 + lane) * 4, 0, 0));
+}
+
 // 8 bf16 (logical chunk c) of one row: an MFMA operand whose contraction runs
 // along the row.
 template <int D>
