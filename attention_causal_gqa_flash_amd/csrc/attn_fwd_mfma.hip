@@ -60,8 +60,10 @@ struct FwdState {
 // O^T += V^T P^T.  With `mask` (wave-uniform: diagonal and tail tiles) keys
 // after the query row's position qa and past the key count Nk are hidden.  `prefetch`
 // issues the wave's NV direct copies of the next tile; they are interleaved
-// with the S^T MFMAs.
-template <int D, int NV, int NKB, class Prefetch>
+// with the S^T MFMAs.  PRIO raises the wave's issue priority while it issues
+// its MFMAs, so that with two waves per SIMD one wave's matrix work goes
+// first while the other's softmax fills the vector ALU.
+template <int D, int NV, int NKB, bool PRIO, class Prefetch>
 __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, const uint16_t *svb,
                                          float c2, int kv0, int qa, int Nk, int causal, bool mask,
                                          int lane, const Prefetch &prefetch)
@@ -72,6 +74,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 
     // S^T for the tile's NKB 32-key blocks; the K operands are read first and
     // interleaved with the MFMAs (4 reads ahead, then one per MFMA).
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     f32x16 sacc[NKB];
     bf16x8 ka[NKB][KS];
 #pragma unroll
@@ -87,6 +90,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) sacc[kb] = mfma32x32x16(ka[kb][ks], st.qf[ks], sacc[kb]);
     sched_pipeline<NKB * KS, NKB * KS, 4, 1, NV>();
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 
     // Row max on the raw scores (c2 > 0 commutes with max); masked scores are -inf.
     // Register r of block kb holds key kv0 + 4hf + c, c = 32kb + 8(r/4) + r%4
@@ -140,6 +144,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
     // O^T += V^T P^T, 2 NKB 16-key steps.  Step tt consumes accumulator
     // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
     // and 16tt + 8 + 4hf + {0..3}; tr_operand reads V^T in that order.
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     bf16x8 va[2 * NKB][DB];
 #pragma unroll
     for (int tt = 0; tt < 2 * NKB; ++tt)
@@ -152,6 +157,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
         for (int db = 0; db < DB; ++db) st.oacc[db] = mfma32x32x16(va[tt][db], pb, st.oacc[db]);
     }
     sched_pipeline<4 * NKB * DB, 2 * NKB * DB, 4, 2>();
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 }
 
 // KSPLIT = 1: one workgroup = 4 waves = 128 query rows (32 per wave), every
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         const int kv0 = tile_of(kh, s_) * TN;
         if (valid(kh, s_) && qw0 < Nq && (!causal || kv0 <= qw0 + off + 31)) {
             const bool mask = (causal && kv0 + TN - 1 > qw0 + off) || kv0 + TN > Nk;
-            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE, TN / 32>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi + off,
+            fwd_tile<D, 2 * KSPLIT * Copy::PER_WAVE, TN / 32, D == 128 && KSPLIT == 1>(st, skc + kh * TE, svc + kh * TE, c2, kv0, qi + off,
                                                      Nk, causal, mask, lane, prefetch);
         } else {
             prefetch();

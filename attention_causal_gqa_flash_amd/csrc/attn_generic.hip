@@ -438,6 +438,48 @@ __global__ __launch_bounds__(128) void lse_merge_kernel(const float *__restrict_
     if (tid == 0) lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
 }
 
+// The same merge for at most NS <= 64 splits (the usual case): every lane
+// loads its dim of all the partials at once, next to the splits' lse values
+// (the same addresses in every lane), so the kernel waits for memory once;
+// lane s of each wave computes split s's weight and the others read it from
+// that lane, with no block reductions.  Indices past the last split or dim
+// are clamped (the loads stay branch-free) and those splits get weight 0.
+template <int NS>
+__global__ __launch_bounds__(128) void lse_merge_small_kernel(const float *__restrict__ part_o,
+                                                              const float *__restrict__ part_lse,
+                                                              float *__restrict__ o,
+                                                              float *__restrict__ lse, int Hq,
+                                                              int n_splits, int d)
+{
+    static_assert(NS <= 64, "one split per lane");
+    const int tid = threadIdx.x, lane = tid & 63, dc = min(tid, d - 1);
+    const size_t row = (size_t)blockIdx.y * Hq + blockIdx.x;
+    const float *pl = part_lse + row * n_splits;
+    const float *po = part_o + row * (size_t)n_splits * d;
+    float ls[NS], pv[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int sc = min(s, n_splits - 1);
+        ls[s] = pl[sc];
+        pv[s] = po[(size_t)sc * d + dc];
+    }
+    const float own = pl[min(lane, n_splits - 1)];    // split `lane`'s lse
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, ls[s]);
+    // weight of split `lane`; all zero when every chunk is empty (M = -inf)
+    const float w = (lane >= n_splits || M == -INFINITY || own == -INFINITY) ? 0.f : expf(own - M);
+    float W = 0.f, acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+        W += ws;
+        acc = fmaf(ws, pv[s], acc);
+    }
+    if (tid < d) o[row * d + tid] = M == -INFINITY ? 0.f : acc / W;
+    if (tid == 0) lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -557,8 +599,15 @@ hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scal
 hipError_t lse_merge(int B, int Hq, int n_splits, int d, const float *part_o,
                      const float *part_lse, float *o, float *lse, hipStream_t st)
 {
-    hipLaunchKernelGGL(lse_merge_kernel, dim3(Hq, B), dim3(128), 0, st, part_o, part_lse, o, lse,
-                       Hq, n_splits, d);
+    if (n_splits <= 16)
+        hipLaunchKernelGGL(lse_merge_small_kernel<16>, dim3(Hq, B), dim3(128), 0, st, part_o, part_lse,
+                           o, lse, Hq, n_splits, d);
+    else if (n_splits <= 32)
+        hipLaunchKernelGGL(lse_merge_small_kernel<32>, dim3(Hq, B), dim3(128), 0, st, part_o, part_lse,
+                           o, lse, Hq, n_splits, d);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel, dim3(Hq, B), dim3(128), 0, st, part_o, part_lse, o, lse,
+                           Hq, n_splits, d);
     return hipGetLastError();
 }
 

@@ -556,6 +556,33 @@ def test_merge_all_empty():
     assert torch.all(torch.isneginf(lse)).item()
 
 
+MERGE_SPLITS = [1, 5, 16, 32, 33, 100]
+
+
+@pytest.mark.parametrize("S", MERGE_SPLITS)
+def test_merge_split_counts(S):
+    """The merge alone on seeded partials (some chunks empty: lse = -inf, o = 0)
+    against the oracle's merge, on both sides of the 32-split fast path."""
+    print(f"\n[case] lse_merge S={S}", flush=True)
+    rng = np.random.default_rng(4000 + S)
+    B, Hq, d = 2, 5, 128
+    po = rng.standard_normal((B, Hq, S, d)).astype(np.float32)
+    pl = (3.0 * rng.standard_normal((B, Hq, S))).astype(np.float32)
+    empty = rng.random((B, Hq, S)) < 0.3
+    empty[0, 0, :] = S > 1                    # one row with a single live chunk
+    empty[0, 0, -1] = False
+    pl[empty] = -np.inf
+    po[empty] = 0.0
+    o, lse = attn.attn_lse_merge(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_merge(po, pl)
+    assert float(np.abs(o.cpu().numpy() - ro).max()) <= 1e-5
+    gl = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))   # rows whose chunks are all empty
+    live = np.isfinite(rl)
+    assert float(np.abs(gl[live] - rl[live]).max()) <= 1e-5
+
+
 def test_invalid_call_leaves_outputs_untouched():
     q = torch.zeros((1, 3, 8, 64), device="cuda", dtype=torch.bfloat16)
     k = torch.zeros((1, 2, 8, 64), device="cuda", dtype=torch.bfloat16)
