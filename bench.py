@@ -83,7 +83,7 @@ KERNEL_NAMES = (("fwd_mfma_kernel", "fwd"), ("bwd_pre_kernel", "bwd_preprocess")
                 ("bwd_fused_kernel", "bwd_grads"),
                 ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
                 ("decode_mfma_kernel<128, false>", "decode_merged"),
-                ("lse_merge_kernel", "lse_merge"))
+                ("lse_merge", "lse_merge"))
 
 TRAFFIC_TAG = "traffic-json: "
 
