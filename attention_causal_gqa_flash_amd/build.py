@@ -36,10 +36,18 @@ def hipcc() -> str:
 # kernels compile to the same code either way.
 AGPR_FORM = ("attn_bwd_mfma.hip",)
 
+# Sources compiled assuming no NaN operands (infinities are still honoured:
+# masked scores are -inf): fmaxf on matrix-core results then needs no NaN
+# canonicalisation, which in the forward's row maximum was 8 of its 18
+# instructions per tile.  NaN inputs make NaN outputs either way.
+NO_NAN = ("attn_fwd_mfma.hip",)
+
 
 def compile_flags(src: str = "") -> list:
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if os.path.basename(src) in NO_NAN:
+        flags += ["-fno-honor-nans"]
     if os.path.basename(src) not in AGPR_FORM:
         # keep MFMA accumulators in VGPR form: with the AGPR form the score
         # accumulators, which the softmax reads, are copied from AGPRs to

@@ -53,7 +53,10 @@ struct FwdState {
     bf16x8 qf[KS];
     f32x16 oacc[DB];
     float m_run;    // running max of c2 * q.k for this lane's row (log2 units)
-    float l_run;    // this lane's share of the running sum
+    float m_thr;    // m_run + kLazy: a tile max above it raises m_run
+    float nm;       // exponent offset -m_run (0 while m_run = -inf)
+    float lq[4];    // this lane's share of the running sum, in four chains
+    __device__ __forceinline__ float l_sum() const { return (lq[0] + lq[1]) + (lq[2] + lq[3]); }
 };
 
 // One 64-key tile for one wave: S^T = K Q^T, the online-softmax update and
@@ -106,40 +109,42 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
             }
     }
     // Row max and row sum as four independent chains each (short dependency
-    // chains matter: a wave's tile is a latency chain at small head dims).
-    float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // chains matter: a wave's tile is a latency chain at small head dims);
+    // the max chains start from the tile's first scores, the sum chains run
+    // on across tiles (the vector ALU is what bounds small grids).
+    float mq[4] = {sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
+        for (int r = kb == 0 ? 4 : 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], sacc[kb][r]);
     float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = pair32_max(mx) * c2;
     // Lazy rescale: raise the running max only when some row of the wave grew
     // past it by more than kLazy.  A row that has seen no key yet keeps -inf
     // (its probabilities are then exact zeros, see nm).
-    if (__any(mx > st.m_run + kLazy)) {
+    if (__any(mx > st.m_thr)) {
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = st.m_run == -INFINITY ? 0.f : exp2_fast(st.m_run - m_new);
-        st.l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) st.lq[c] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st.oacc[db][r] *= alpha;
         st.m_run = m_new;
+        st.m_thr = m_new + kLazy;
+        st.nm = m_new == -INFINITY ? 0.f : -m_new;
     }
     // p = 2^(c2 s - m): one FMA and one exp per score (exp2(-inf) = 0; a row
     // with no key seen yet has only hidden scores, and m = -inf is taken as 0)
-    float rq[4] = {0.f, 0.f, 0.f, 0.f};
-    const float nm = st.m_run == -INFINITY ? 0.f : -st.m_run;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(fmaf(sacc[kb][r], c2, nm));
+            const float p = exp2_fast(fmaf(sacc[kb][r], c2, st.nm));
             sacc[kb][r] = p;
-            rq[r & 3] += p;
+            st.lq[r & 3] += p;
         }
-    st.l_run += (rq[0] + rq[1]) + (rq[2] + rq[3]);
 
     // O^T += V^T P^T, 2 NKB 16-key steps.  Step tt consumes accumulator
     // registers (tt&1)*8 .. +7 of block tt>>1, i.e. keys 16tt + 4hf + {0..3}
@@ -222,7 +227,10 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         }
     }
     st.m_run = -INFINITY;
-    st.l_run = 0.f;
+    st.m_thr = -INFINITY;
+    st.nm = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st.lq[c] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
 #pragma unroll
                 for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64 + lane] = st.oacc[db][r];
             pm[(rw * 2 + 0) * 64 + lane] = st.m_run;
-            pm[(rw * 2 + 1) * 64 + lane] = st.l_run;
+            pm[(rw * 2 + 1) * 64 + lane] = st.l_sum();
         }
         __syncthreads();
         if (kh == 1) return;
@@ -309,11 +317,12 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 st.oacc[db][r] = st.oacc[db][r] * ea + po[(db * 16 + r) * 64 + lane] * eb;
-        st.l_run = st.l_run * ea + lB * eb;
+        st.lq[0] = st.l_sum() * ea + lB * eb;
+        st.lq[1] = st.lq[2] = st.lq[3] = 0.f;
         st.m_run = m;
     }
 
-    const float l_tot = pair32_sum(st.l_run);
+    const float l_tot = pair32_sum(st.l_sum());
     if (qi < Nq) {
         const float inv = 1.f / l_tot;
         const size_t orow = (((size_t)b * Hq + h) * Nq + qi) * D;
