@@ -305,14 +305,17 @@ __device__ __forceinline__ void dkdv_body(
 
     // Sum the two query halves and write dK = scale (dK^T)^T and dV.
     // Accumulator layout: lane = key column kj, register r of block db = dim
-    // db*32 + 8(r/4) + 4hf + (r&3).  The query-half-1 waves park their partials
-    // in the tile arrays (one array per (key block, dK or dV)) transposed to
-    // [key][dim], the half-0 waves add theirs in place, so that the final
-    // stores (or atomics) run along the dim with consecutive lanes.  Key row
-    // l32 of a key block keeps dim d at [l32][d ^ l32]: the XOR spreads the 32
-    // rows written by one instruction over the banks and keeps each row a
-    // permutation of its dims.
+    // db*32 + 8(r/4) + 4hf + (r&3): registers 4a..4a+3 are four consecutive
+    // dims.  The query-half-1 waves park their partials in the tile arrays
+    // (one array per (key block, dK or dV)) transposed to [key][dim], four
+    // dims per 16-byte write, the half-0 waves add theirs in place, so that
+    // the final stores (or atomics) run along the dim with consecutive lanes.
+    // Key row r keeps its 16-byte chunk c at c ^ (r mod NC): the XOR spreads
+    // the rows written by one instruction over the banks and keeps each row a
+    // permutation of its chunks.
     static_assert(32 * D * sizeof(float) <= SR * D * sizeof(uint16_t), "transposed partial fits");
+    constexpr int NC = D / 4;                                      // 16-byte chunks per row
+    auto pidx = [](int row, int dim) { return row * D + 4 * ((dim >> 2) ^ (row & (NC - 1))) + (dim & 3); };
     float *redk = reinterpret_cast<float *>(kb ? q1s : q0s);
     float *redv = reinterpret_cast<float *>(kb ? d1s : d0s);
     __syncthreads();                         // the last step's reads are done
@@ -320,10 +323,12 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dim = db * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                redk[l32 * D + (dim ^ l32)] = dka[db][r];
-                redv[l32 * D + (dim ^ l32)] = dva[db][r];
+            for (int a = 0; a < 4; ++a) {
+                const int at = pidx(l32, db * 32 + 8 * a + 4 * hf);
+                *(float4 *)&redk[at] = make_float4(dka[db][4 * a], dka[db][4 * a + 1], dka[db][4 * a + 2],
+                                                   dka[db][4 * a + 3]);
+                *(float4 *)&redv[at] = make_float4(dva[db][4 * a], dva[db][4 * a + 1], dva[db][4 * a + 2],
+                                                   dva[db][4 * a + 3]);
             }
     }
     __syncthreads();
@@ -331,11 +336,15 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int dim = db * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                const int at = l32 * D + (dim ^ l32);
-                redk[at] = (redk[at] + dka[db][r]) * scale;
-                redv[at] = redv[at] + dva[db][r];
+            for (int a = 0; a < 4; ++a) {
+                const int at = pidx(l32, db * 32 + 8 * a + 4 * hf);
+                const float4 pk = *(const float4 *)&redk[at];
+                const float4 pv = *(const float4 *)&redv[at];
+                *(float4 *)&redk[at] = make_float4((pk.x + dka[db][4 * a]) * scale, (pk.y + dka[db][4 * a + 1]) * scale,
+                                                   (pk.z + dka[db][4 * a + 2]) * scale,
+                                                   (pk.w + dka[db][4 * a + 3]) * scale);
+                *(float4 *)&redv[at] = make_float4(pv.x + dva[db][4 * a], pv.y + dva[db][4 * a + 1],
+                                                   pv.z + dva[db][4 * a + 2], pv.w + dva[db][4 * a + 3]);
             }
     }
     __syncthreads();
@@ -346,11 +355,11 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int kr = wave + 4 * i;
-        const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s) + (kr & 31) * D;
-        const float *sv = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s) + (kr & 31) * D;
+        const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s);
+        const float *sv = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s);
 #pragma unroll
         for (int c = 0; c < CPR; ++c) {
-            const int src = (64 * c + lane) ^ (kr & 31);
+            const int src = pidx(kr & 31, 64 * c + lane);
             vk[i * CPR + c] = sk[src];
             vv[i * CPR + c] = sv[src];
         }
@@ -363,13 +372,13 @@ __device__ __forceinline__ void dkdv_body(
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             const int kr = wave + 4 * i;
-            const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s) + (kr & 31) * D;
+            const float *sk = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s);
             float sn, cs;
             rope_sincos_hw((double)(k0 + kr) * th, sn, cs);
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
                 const int dim = 64 * c + lane;
-                const float partner = sk[(dim ^ (D / 2)) ^ (kr & 31)];
+                const float partner = sk[pidx(kr & 31, dim ^ (D / 2))];
                 vk[i * CPR + c] = vk[i * CPR + c] * cs + (dim < D / 2 ? sn : -sn) * partner;
             }
         }
