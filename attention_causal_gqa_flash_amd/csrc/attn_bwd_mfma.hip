@@ -611,16 +611,35 @@ __device__ __forceinline__ void dq_body(
                 }
         }
     }
-    if (qi < Nq) {
-        float *row = dQ + (qrow0 + qi) * D;
+    // dQ = scale (dQ^T)^T through LDS: each wave parks its 32 rows as [row][dim]
+    // (four dims per 16-byte write, chunk c of row r at c ^ (r mod NC)) in a
+    // tile array of its own, reads them back along the dim and stores whole
+    // rows (consecutive lanes, consecutive addresses) instead of 32-byte
+    // pieces of 32 rows.
+    constexpr int NC = D / 4, RPI = 64 / NC;    // 16-byte chunks per row, rows per read
+    static_assert(32 * D * sizeof(float) <= kQBN * D * sizeof(uint16_t), "a wave's dQ rows fit");
+    float *pk = reinterpret_cast<float *>(wave == 0 ? sk0 : wave == 1 ? sk1 : wave == 2 ? sv0 : sv1);
+    __syncthreads();                         // the last tile's reads are done
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int d0 = db * 32 + 8 * a + 4 * hf;
-                *(float4 *)(row + d0) = make_float4(dqa[db][4 * a + 0] * scale, dqa[db][4 * a + 1] * scale,
-                                                    dqa[db][4 * a + 2] * scale, dqa[db][4 * a + 3] * scale);
-            }
+        for (int a = 0; a < 4; ++a) {
+            const int c = 8 * db + 2 * a + hf;
+            *(float4 *)&pk[l32 * D + 4 * (c ^ (l32 & (NC - 1)))] =
+                make_float4(dqa[db][4 * a + 0] * scale, dqa[db][4 * a + 1] * scale, dqa[db][4 * a + 2] * scale,
+                            dqa[db][4 * a + 3] * scale);
+        }
+    float4 vq[32 / RPI];
+    const int rl = lane / NC, cl = lane % NC;  // this lane's row within a read, its chunk
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = RPI * i + rl;
+        vq[i] = *(const float4 *)&pk[r * D + 4 * (cl ^ (r & (NC - 1)))];
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int qr = qw0 + RPI * i + rl;
+        if (qr < Nq) *(float4 *)(dQ + (qrow0 + qr) * D + 4 * cl) = vq[i];
     }
 }
 
