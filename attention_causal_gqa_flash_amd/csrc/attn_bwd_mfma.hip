@@ -229,19 +229,27 @@ __device__ __forceinline__ void dkdv_body(
     const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
-    // K^T and V^T operands, resident: lane holds row kj (clamped), dims 16ks + 8hf .. +7.
+    // K^T and V^T operands, resident: lane holds row kj, dims 16ks + 8hf .. +7.
+    // The key tile's K and V rows move global -> LDS directly (whole rows,
+    // rows past Nk read as zero and are never stored), into the second Q and
+    // dO buffers, which step 1's copy fills only after step 0 has read them.
     bf16x8 kf[KS], vf[KS];
     {
-        const int kr = min(kj, Nk - 1);
+        const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+        const TileCopy<D, kKvBN, 4> kvcopy(wave, lane);
+        kvcopy(q1s, make_rsrc(Kg, kv_bytes), k0, wave);
+        kvcopy(d1s, make_rsrc(Vg, kv_bytes), k0, wave);
+    }
+    auto read_kv = [&] {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 uk = *(const uint4 *)(Kg + (size_t)kr * D + 16 * ks + 8 * hf);
-            const uint4 uv = *(const uint4 *)(Vg + (size_t)kr * D + 16 * ks + 8 * hf);
+            uint4 uk = *(const uint4 *)tile_chunk<D>(q1s, 32 * kb + l32, 2 * ks + hf);
+            const uint4 uv = *(const uint4 *)tile_chunk<D>(d1s, 32 * kb + l32, 2 * ks + hf);
             uk.x ^= ksign; uk.y ^= ksign; uk.z ^= ksign; uk.w ^= ksign;
             kf[ks] = as_bf16x8(uk);
             vf[ks] = as_bf16x8(uv);
         }
-    }
+    };
 
     f32x16 dva[DB], dka[DB];
 #pragma unroll
@@ -281,6 +289,12 @@ __device__ __forceinline__ void dkdv_body(
         wait_vmcnt<0>();                    // this wave's copies of step s have landed
         (wave < 2 ? lc : ec)[64 * (wave & 1) + lane] = row_v * row_mul;
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
+        if constexpr (BI == 0) {
+            if (s == 0) {                   // the key tile's K and V rows, then buffer 1 is free
+                read_kv();
+                __syncthreads();
+            }
+        }
         if (s + 1 < steps) {
             if (BI) load_step(s + 1, q0s, d0s);
             else load_step(s + 1, q1s, d1s);
@@ -318,6 +332,7 @@ __device__ __forceinline__ void dkdv_body(
     auto pidx = [](int row, int dim) { return row * D + 4 * ((dim >> 2) ^ (row & (NC - 1))) + (dim & 3); };
     float *redk = reinterpret_cast<float *>(kb ? q1s : q0s);
     float *redv = reinterpret_cast<float *>(kb ? d1s : d0s);
+    wait_vmcnt<0>();                         // (no step: the K/V copies have landed)
     __syncthreads();                         // the last step's reads are done
     if (qh == 1) {
 #pragma unroll
