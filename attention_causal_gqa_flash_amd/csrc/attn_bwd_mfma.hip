@@ -503,8 +503,10 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
 // rows against Nk >= Nq keys (query row i at key position i + Nk - Nq; XL =
 // false compiles the square case).  K and V tiles, row-major with swizzled
 // 16-byte chunks, double-buffered in the first kQBN rows of the Q and dO
-// arrays of `lds`.
-template <int D, bool XL>
+// arrays of `lds`.  STAGE (arrays of kQBM rows or more): the tile's Q and dO
+// rows for the resident operands go global -> LDS directly (whole rows) into
+// the second arrays, which tile 1's copy fills only after tile 0 read them.
+template <int D, bool XL, bool STAGE>
 __device__ __forceinline__ void dq_body(
     int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
@@ -538,7 +540,12 @@ __device__ __forceinline__ void dq_body(
     const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
 
     bf16x8 qf[KS], dof[KS];
-    {
+    if constexpr (STAGE) {
+        const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+        const TileCopy<D, kQBM, 4> qcopy(wave, lane);
+        qcopy(sk1, make_rsrc(Q + qrow0 * D, q_bytes), q0, wave);
+        qcopy(sv1, make_rsrc(dO + qrow0 * D, q_bytes), q0, wave);
+    } else {
         const int qr = min(qi, Nq - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -574,6 +581,19 @@ __device__ __forceinline__ void dq_body(
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of tile t have landed
         __syncthreads();                    // ... and every wave's; buffer t+1 is free
+        if constexpr (STAGE && BI == 0) {
+            if (t == 0) {                   // the resident Q and dO rows, then buffer 1 is free
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    uint4 uq = *(const uint4 *)tile_chunk<D>(sk1, wave * 32 + l32, 2 * ks + hf);
+                    const uint4 ud = *(const uint4 *)tile_chunk<D>(sv1, wave * 32 + l32, 2 * ks + hf);
+                    uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
+                    qf[ks] = as_bf16x8(uq);
+                    dof[ks] = as_bf16x8(ud);
+                }
+                __syncthreads();
+            }
+        }
         // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
         // past the last tile they read nothing (zero-byte resources)
         const uint32_t nb = t + 1 < ntiles ? kv_bytes : 0u;
@@ -672,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int G = Hq / Hkv;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    dq_body<D, XL>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
+    dq_body<D, XL, false>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
                    scale, causal, rope_lb);
 }
 
@@ -690,7 +710,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk,
     float scale, int causal, int hs, BwdPlan plan, double rope_lb)
 {
-    static_assert(kQBN <= BwdLds<D>::SR, "dQ's K/V tiles fit the Q/dO arrays");
+    static_assert(kQBN <= BwdLds<D>::SR && kQBM <= BwdLds<D>::SR, "dQ's K/V tiles and Q/dO rows fit the Q/dO arrays");
     ATTN_BWD_LDS(D, lds);
     const int blk = blockIdx.x;
     int i = 0;
@@ -708,7 +728,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
         dkdv_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale,
                          causal, hsi, rope_lb);
     else
-        dq_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal,
+        dq_body<D, XL, true>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal,
                        rope_lb);
 }
 
