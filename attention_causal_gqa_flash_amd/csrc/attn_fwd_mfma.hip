@@ -216,16 +216,28 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     const float c2 = fabsf(scale) * kLog2e;
 
     FwdState<D> st;
+    // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7].  The tile's
+    // Q rows go global -> LDS directly (whole rows; rows past Nq read as zero
+    // and are never stored) into the second K and V buffers, 64 rows each
+    // (the first 64 rows in sk1, the rest in sv1), which step 1's copy fills
+    // only after step 0 has read them.
+    static_assert(64 * D * sizeof(uint16_t) <= sizeof(sk1), "64 Q rows fit a buffer");
     {
-        // Q^T operand, resident: lane holds q[qi][16ks + 8hf .. +7] (rows past N read row N-1)
-        const int qr = min(qi, Nq - 1);
+        const uint32_t q_bytes = (uint32_t)Nq * D * 2;
+        const TileCopy<D, 64, 4> qcopy(wave, lane);
+        qcopy(sk1, make_rsrc(Qh, q_bytes), q0, wave);
+        if constexpr (BMW > 64) qcopy(sv1, make_rsrc(Qh, q_bytes), q0 + 64, wave);
+    }
+    auto read_q = [&] {
+        const int qr = rw * 32 + l32;        // this lane's row within the tile
+        const uint16_t *qt = qr < 64 ? sk1 : sv1;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 u = *(const uint4 *)(Qh + (size_t)qr * D + 16 * ks + 8 * hf);
+            uint4 u = *(const uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
             u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
             st.qf[ks] = as_bf16x8(u);
         }
-    }
+    };
     st.m_run = -INFINITY;
     st.m_thr = -INFINITY;
     st.nm = 0.f;
@@ -272,6 +284,12 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of step s have landed
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
+        if constexpr (BI == 0) {
+            if (s_ == 0) {                  // the resident Q rows, then buffer 1 is free
+                read_q();
+                __syncthreads();
+            }
+        }
         // copies of step s+1 (branch-free, so they can interleave with MFMAs)
         auto prefetch = [&] { copy_step(skn, svn, s_ + 1); };
         const int kv0 = tile_of(kh, s_) * TN;
