@@ -455,7 +455,7 @@ constexpr int kQBN = 64;    // keys per tile
 template <int D, int NV, class Prefetch>
 __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&dof)[D / 16], f32x16 (&dqa)[D / 32], float c2,
-                                        float lse2, float Di, int kv0, int qk, int Nk, int causal,
+                                        float lse2, const f32x16 &negD, int kv0, int qk, int Nk, int causal,
                                         bool mask, int lane, const Prefetch &prefetch)
 {
     constexpr int KS = D / 16, DB = D / 32;
@@ -463,9 +463,10 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         if (kb == 0) prefetch();
-        f32x16 sacc, pacc;
+        // dP^T starts from -D_i (the lane's row): the MFMAs leave dP^T - D_i
+        f32x16 sacc, pacc = negD;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 ak = tile_row_operand<D>(skb, kb * 32 + l32, 2 * ks + hf);
@@ -486,7 +487,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
             }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * (pacc[r] - Di);
+        for (int r = 0; r < 16; ++r) pacc[r] = sacc[r] * pacc[r];
         // dQ^T += K^T dS^T over this block's 32 keys (two 16-key steps)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -558,6 +559,9 @@ __device__ __forceinline__ void dq_body(
     }
     const float lse2 = qi < Nq ? LSE[qrow0 + qi] * kLog2e : INFINITY;
     const float Di = qi < Nq ? Dws[qrow0 + qi] : 0.f;
+    f32x16 negD;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negD[r] = -Di;
 
     f32x16 dqa[DB];
 #pragma unroll
@@ -608,7 +612,7 @@ __device__ __forceinline__ void dq_body(
         // lse = +inf, so both add exact zeros.
         const int kv0 = t * kQBN;
         const bool mask = (causal && kv0 + kQBN - 1 > qw0 + off) || kv0 + kQBN > Nk;
-        dq_tile<D, 2 * Copy::PER_WAVE>(skc, svc, qf, dof, dqa, c2, lse2, Di, kv0, qi + off, Nk, causal,
+        dq_tile<D, 2 * Copy::PER_WAVE>(skc, svc, qf, dof, dqa, c2, lse2, negD, kv0, qi + off, Nk, causal,
                                        mask, lane, prefetch);
         sched_fence();
     };
