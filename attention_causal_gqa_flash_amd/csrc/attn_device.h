@@ -153,12 +153,6 @@ struct TileCopy {
     }
 };
 
-// 64 consecutive floats (rows r0 .. r0+63 of a per-row vector) -> LDS, one
-// wave instruction; entries past the end of the resource read as zero.
-__device__ __forceinline__ void row_load_lds(float *dst, __amdgpu_buffer_rsrc_t rs, int r0, int lane)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, (r0 + lane) * 4, 0, 0, 0);
-}
 
 // One f32 per lane, element r0 + lane of the f32 array behind the resource
 // (zero past its end), into a register.
