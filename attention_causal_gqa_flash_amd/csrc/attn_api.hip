@@ -190,7 +190,10 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int
 
 // The whole backward of Nq query rows against Nk >= Nq keys: the preprocess
 // (with the upstream lse gradient folded into delta when dlse is given), then
-// the gradient stage.
+// the gradient stage.  At d = 128 on the matrix-core path with f32 o, the dQ
+// kernel computes delta for its own rows instead and the dK/dV kernel follows
+// it on the same stream: no preprocess launch (the two kernels gain nothing
+// from running side by side, both being bound by the same CU resources).
 attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                       float scale, const void *q, const void *k, const void *v, const void *o,
                       const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
@@ -207,6 +210,15 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
     hipStream_t st = (hipStream_t)stream;
     float *delta = (float *)workspace;
     const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale);
+    if (use_mfma(dt, Nk, d, scale) && !fuse_bwd(d) && !o_bf16) {
+        if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * Nk * d, st) != hipSuccess)
+            return ATTN_ERR_HIP;
+        if (attn::bwd_dq_pre_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
+                                  (const float *)o, dlse, delta, dq, st, rope_lb) != hipSuccess)
+            return ATTN_ERR_HIP;
+        return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse,
+                                          dout, delta, dk, dv, hs, st, rope_lb));
+    }
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, Nq, Nk, d, o, dout, delta, dk, dv, hs > 1, st,
                               dlse, o_bf16) != hipSuccess)
         return ATTN_ERR_HIP;

@@ -507,13 +507,19 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
 // arrays of `lds`.  STAGE (arrays of kQBM rows or more): the tile's Q and dO
 // rows for the resident operands go global -> LDS directly (whole rows) into
 // the second arrays, which tile 1's copy fills only after tile 0 read them.
-template <int D, bool XL, bool STAGE>
+// PRE (not with STAGE): the rows' D_i = dO_i . O_i - dlse_i is computed here,
+// from O (f32) and the dO operands the lane holds, and written to Dws for a
+// dK/dV kernel that runs afterwards.
+template <int D, bool XL, bool STAGE, bool PRE = false>
 __device__ __forceinline__ void dq_body(
     int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, double rope_lb)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, double rope_lb,
+    const float *__restrict__ O = nullptr, const float *__restrict__ dlse = nullptr,
+    float *__restrict__ Dout = nullptr)
 {
+    static_assert(!(PRE && STAGE), "the row terms come from the lane's own dO operands");
     constexpr int KS = D / 16, DB = D / 32;
     if constexpr (!XL) Nk = Nq;
     // XL = false: a literal 0, folded before the compiler shapes the loop's branches
@@ -558,7 +564,34 @@ __device__ __forceinline__ void dq_body(
         }
     }
     const float lse2 = qi < Nq ? LSE[qrow0 + qi] * kLog2e : INFINITY;
-    const float Di = qi < Nq ? Dws[qrow0 + qi] : 0.f;
+    float Di;
+    if constexpr (PRE) {
+        // the lane holds dO[qi][16ks + 8hf .. +7]: the matching O elements,
+        // then the two halves of the row summed across the lane pair
+        float s = 0.f;
+        if (qi < Nq) {
+            const float *orow = O + (qrow0 + qi) * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const float4 a = *(const float4 *)(orow + 16 * ks + 8 * hf);
+                const float4 c = *(const float4 *)(orow + 16 * ks + 8 * hf + 4);
+                const uint4 u = __builtin_bit_cast(uint4, dof[ks]);
+                s = fmaf(bf16lo(u.x), a.x, s); s = fmaf(bf16hi(u.x), a.y, s);
+                s = fmaf(bf16lo(u.y), a.z, s); s = fmaf(bf16hi(u.y), a.w, s);
+                s = fmaf(bf16lo(u.z), c.x, s); s = fmaf(bf16hi(u.z), c.y, s);
+                s = fmaf(bf16lo(u.w), c.z, s); s = fmaf(bf16hi(u.w), c.w, s);
+            }
+        }
+        Di = pair32_sum(s);
+        if (qi < Nq) {
+            if (dlse) Di -= dlse[qrow0 + qi];
+            if (hf == 0) Dout[qrow0 + qi] = Di;
+        } else {
+            Di = 0.f;
+        }
+    } else {
+        Di = qi < Nq ? Dws[qrow0 + qi] : 0.f;
+    }
     f32x16 negD;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negD[r] = -Di;
@@ -682,12 +715,13 @@ __device__ __forceinline__ void dq_body(
     }
 }
 
-template <int D, bool XL>
+template <int D, bool XL, bool PRE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
-    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt, double rope_lb)
+    int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt, double rope_lb,
+    const float *__restrict__ O, const float *__restrict__ dlse, float *__restrict__ Dout)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
@@ -696,8 +730,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int G = Hq / Hkv;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    dq_body<D, XL, false>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
-                   scale, causal, rope_lb);
+    dq_body<D, XL, false, PRE>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv,
+                               Nq, Nk, scale, causal, rope_lb, O, dlse, Dout);
 }
 
 // Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
@@ -804,11 +838,30 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
     const int nqt = (Nq + kQBM - 1) / kQBM;
     const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
     return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
-        hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
+        hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value, false>), grid,
                            dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, B, Hq, Hkv,
-                           Nq, Nk, scale, causal, nqt, rope_lb);
+                           Nq, Nk, scale, causal, nqt, rope_lb, nullptr, nullptr, nullptr);
     });
+}
+
+hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, const float *lse,
+                           const void *dout, const float *o, const float *dlse, float *Dws,
+                           float *dq, hipStream_t st, double rope_lb)
+{
+    if (d != 128) return hipErrorInvalidValue;
+    const int nqt = (Nq + kQBM - 1) / kQBM;
+    const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
+    auto launch = [&](auto xc) {
+        hipLaunchKernelGGL((bwd_dq_kernel<128, decltype(xc)::value, true>), grid, dim3(256), 0, st,
+                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, lse,
+                           (const uint16_t *)dout, nullptr, dq, B, Hq, Hkv, Nq, Nk, scale, causal, nqt,
+                           rope_lb, o, dlse, Dws);
+    };
+    if (Nq != Nk) launch(std::true_type{});
+    else launch(std::false_type{});
+    return hipGetLastError();
 }
 
 namespace {

@@ -63,6 +63,12 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st,
                        double rope_lb = 0.0);
+// dQ that also computes D_i = dO_i . O_i - dlse_i (O f32, dlse optional) into
+// Dws for a dK/dV kernel launched after it (bf16, d = 128)
+hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, const float *lse,
+                           const void *dout, const float *o, const float *dlse, float *Dws,
+                           float *dq, hipStream_t st, double rope_lb);
 // dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,

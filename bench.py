@@ -3,9 +3,10 @@
 
 One step = one pass of the whole hot path on seeded synthetic inputs already
 resident in device memory:
-  * the training op: attn_fwd, then attn_bwd (preprocess, then the gradient
-    stage: at d=64 one kernel holding both the dK/dV and the dQ work, at
-    d=128 the dK/dV and dQ kernels side by side) on the training workload
+  * the training op: attn_fwd, then attn_bwd (at d=64 the preprocess, then
+    one kernel holding both the dK/dV and the dQ work; at d=128 the dQ kernel,
+    which also computes the preprocess's row terms, then the dK/dV kernel) on
+    the training workload
     (default: bf16, B=4, 12 query / 4 key-value heads, N=1024, d=64);
   * the decode op: split-KV decode + LSE merge (attn_decode_merged: the decode
     kernel then the merge kernel) on the decode workload (bf16, 32/8 heads, d=128, a 4096-key cache in 16

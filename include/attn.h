@@ -122,15 +122,17 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
  *   then differ from run to run in the last bits.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry do not matter.
- *   Streams: the gradients run as described at attn_bwd_grads; when they are
- *   two kernels, the dq kernel runs on an auxiliary stream of the current
- *   device, forked from and joined back into `stream` with events,
- *   concurrently with the dk/dv kernel; to the caller the call behaves as if
- *   all its work were on `stream` (a graph capture of `stream` captures both
- *   branches).  The auxiliary stream and events are created on the device's
- *   first such call; if that first call is made while `stream` is being
- *   captured, or they cannot be created, the kernels run one after the other
- *   on `stream`.
+ *   Streams: for bf16 inputs at d = 128 (f32 o) the dq kernel computes delta
+ *   itself (into the workspace) and the dk/dv kernel follows it, both on
+ *   `stream`.  Otherwise the preprocess runs, then the gradients as described
+ *   at attn_bwd_grads; when they are two kernels, the dq kernel runs on an
+ *   auxiliary stream of the current device, forked from and joined back into
+ *   `stream` with events, concurrently with the dk/dv kernel; to the caller
+ *   the call behaves as if all its work were on `stream` (a graph capture of
+ *   `stream` captures both branches).  The auxiliary stream and events are
+ *   created on the device's first such call; if that first call is made while
+ *   `stream` is being captured, or they cannot be created, the kernels run
+ *   one after the other on `stream`.
  */
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      const void *q, const void *k, const void *v,
@@ -255,12 +257,14 @@ attn_status attn_bwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
  * attn_bwd_preprocess -- writes delta from o (f32) and dout (dtype dt).
  * attn_bwd_dkdv       -- writes dk and dv; reads q, k, v, lse, dout, delta.
  * attn_bwd_dq         -- writes dq; reads q, k, v, lse, dout, delta.
- * attn_bwd_grads      -- writes dq, dk and dv the way attn_bwd does after its
- *                        preprocess: on the bf16 matrix-core path at d = 64
- *                        ONE kernel launch whose grid holds both the dk/dv and
- *                        the dq work items (after a zero-fill launch of dk and
- *                        dv when they are accumulated with atomics); otherwise
- *                        the dk/dv and dq kernels side by side (see attn_bwd).
+ * attn_bwd_grads      -- writes dq, dk and dv from a given delta: on the bf16
+ *                        matrix-core path at d = 64 ONE kernel launch whose
+ *                        grid holds both the dk/dv and the dq work items (after
+ *                        a zero-fill launch of dk and dv when they are
+ *                        accumulated with atomics), as attn_bwd runs it after
+ *                        its preprocess; otherwise the dk/dv and dq kernels
+ *                        side by side on two streams (see the stream note at
+ *                        attn_bwd).
  * dkdv and dq do not depend on each other; all need the preprocess first.
  */
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d,
