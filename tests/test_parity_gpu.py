@@ -218,7 +218,7 @@ def test_decode_shapes(B, Hq, Hkv, L, d, S, dtype):
 
 DLSE = [
     (4, 12, 4, 1024, 64, True, "bf16"),     # the one-launch gradient kernel, 3-way head split
-    (1, 8, 2, 300, 128, True, "bf16"),      # d = 128, two kernels side by side
+    (1, 8, 2, 300, 128, True, "bf16"),      # d = 128: dQ computing the row terms, then dK/dV (head split)
     (2, 6, 3, 200, 64, False, "bf16"),
     (1, 2, 1, 64, 16, True, "f32"),         # generic kernels
 ]
@@ -287,7 +287,7 @@ def test_fwd_kv_square_equals_fwd():
 
 BWD_KV = [
     (4, 12, 4, 256, 1024, 64, True, "bf16", False),   # one-launch gradients, 3-way head split
-    (1, 8, 2, 300, 700, 128, True, "bf16", True),     # d = 128, two kernels, with dlse
+    (1, 8, 2, 300, 700, 128, True, "bf16", True),     # d = 128, dQ with the row terms then dK/dV, with dlse
     (2, 6, 3, 64, 101, 64, True, "bf16", False),      # ragged tiles on both sides
     (1, 4, 2, 200, 300, 64, False, "bf16", False),
     (2, 6, 2, 1, 333, 64, True, "bf16", True),        # one row against a cache
@@ -652,9 +652,11 @@ def test_bwd_grads_stage(B, Hq, Hkv, N, d, causal):
 def test_graph_replay_matches_eager(mode, d):
     """The whole path captured in a HIP graph: every replay equals the eager run.
     The backward is the preprocess then the dK/dV and dQ stages ("stages"),
-    attn_bwd_grads ("grads") or attn_bwd; at d = 128 the latter two run the dQ
-    kernel on the library's auxiliary stream (a fork/join inside the capture),
-    at d = 64 they are one launch after a zero-fill launch of dk and dv."""
+    attn_bwd_grads ("grads") or attn_bwd; at d = 128 attn_bwd_grads runs the dQ
+    kernel on the library's auxiliary stream (a fork/join inside the capture)
+    and attn_bwd runs the dQ kernel that computes the row terms, then the dK/dV
+    kernel; at d = 64 both are one launch (attn_bwd_grads after a zero-fill
+    launch of dk and dv)."""
     cfg = W.TrainConfig("graph", "bf16", 1, 8, 2, 320, d, seed=11)
     x = W.train_inputs(cfg)
     g = {n: _to_dev(a, "bf16") for n, a in x.items()}
