@@ -13,11 +13,11 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-           "attn_bwd_grads", "attn_bwd_grads_single_launch", "attn_decode_append", "attn_fwd_kv",
+           "attn_bwd_grads", "attn_bwd_grads_plan", "attn_decode_append", "attn_fwd_kv",
            "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
            "attn_fwd_ex", "attn_bwd_ex",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
-           "attn_decode_merged",
+           "attn_decode_merged", "attn_read_probe",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
            "ATTN_F32", "ATTN_BF16"]
 
@@ -80,8 +80,9 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_rope.restype = i
     L.attn_decode_append.argtypes = [i, i, i, i, i, i, f, i] + [p] * 10 + [p]
     L.attn_decode_append.restype = i
-    L.attn_bwd_grads_single_launch.argtypes = [i, i, i, f]
-    L.attn_bwd_grads_single_launch.restype = i
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.attn_bwd_grads_plan.argtypes = [i, i, i, i, i, i, i, i, f, ip, ip]
+    L.attn_bwd_grads_plan.restype = i
     L.attn_bwd_dq.restype = i
     L.attn_decode.argtypes = [i, i, i, i, i, i, f, i, p, p, p, p, p, p]
     L.attn_decode.restype = i
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_merged.restype = i
     L.attn_lse_merge.argtypes = [i, i, i, i, p, p, p, p, p]
     L.attn_lse_merge.restype = i
+    L.attn_read_probe.argtypes = [p, sz, p, p]
+    L.attn_read_probe.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     L.attn_abi_version.argtypes = []
@@ -127,6 +130,32 @@ def _dev(t, name):
     return t
 
 
+def _expect(t, shape, dtype, name, like=None):
+    """t must be a contiguous device tensor of this shape and dtype (on like's device)."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+    return t
+
+
+def _out(t, shape, dtype, name, like, stream):
+    """The caller's output tensor (checked), or a new one.  A new tensor is
+    allocated on the stream the call is enqueued on, so that torch's caching
+    allocator does not hand its memory to other streams while the kernels may
+    still be using it."""
+    if t is not None:
+        return _expect(t, shape, dtype, name, like)
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, device=like.device, dtype=dtype)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, device=like.device, dtype=dtype)
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -142,24 +171,36 @@ def _check(fn: str, rc: int):
         raise AttnError(fn, rc)
 
 
+def _qkv(q, k, v, square: bool):
+    """Shapes of q [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d] (same dtype, device); square: Nk == Nq."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _dtype_code(q)
+    _expect(k, (B, Hkv, Nk, d), q.dtype, "k", q)
+    _expect(v, (B, Hkv, Nk, d), q.dtype, "v", q)
+    if square and Nk != Nq:
+        raise ValueError("k and v must have as many rows as q (the Nq < Nk form is attn_fwd_kv / "
+                         "attn_bwd_kv)")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _scale(scale, d):
+    return float(d) ** -0.5 if scale is None else float(scale)
+
+
 def attn_fwd(q, k, v, causal: bool = True, scale: float | None = None, o=None, lse=None,
              stream=None):
     """Forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] (float32 or bfloat16) -> (o f32, lse f32)."""
     torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k and v must be [B, Hkv, N, d] with q's batch, length, head dim and dtype")
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if o is None:
-        o = torch.empty((B, Hq, N, d), device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
-    rc = lib().attn_fwd(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                        _ptr(q), _ptr(k), _ptr(v), _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")),
-                        _stream(stream))
+    B, Hq, Hkv, N, _, d = _qkv(q, k, v, square=True)
+    o = _out(o, (B, Hq, N, d), torch.float32, "o", q, stream)
+    lse = _out(lse, (B, Hq, N), torch.float32, "lse", q, stream)
+    rc = lib().attn_fwd(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), _scale(scale, d),
+                        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream))
     _check("attn_fwd", rc)
     return o, lse
 
@@ -195,43 +236,42 @@ def attn_bwd_kv(q, k, v, o, lse, dout, causal: bool = True, scale: float | None 
                      workspace, stream)
 
 
+_KV_FORMS = ("attn_bwd_kv", "attn_bwd_rope", "attn_bwd_ex")
+
+
 def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, workspace, stream,
               base=None):
     torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (dout, "dout")):
-        _dev(t, n)
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
-    if fn not in ("attn_bwd_kv", "attn_bwd_rope", "attn_bwd_ex") and Nk != Nq:
-        raise ValueError(f"{fn} needs as many keys as queries (attn_bwd_kv takes Nk > Nq)")
-    if dout.shape != q.shape or dout.dtype != q.dtype:
-        raise ValueError("dout must match q in shape and dtype")
-    if (o.dtype != torch.float32 and fn != "attn_bwd_ex") or lse.dtype != torch.float32:
-        raise ValueError("o and lse must be the float32 outputs of the forward")
-    scale = float(d) ** -0.5 if scale is None else float(scale)
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v, square=fn not in _KV_FORMS)
+    _expect(dout, (B, Hq, Nq, d), q.dtype, "dout", q)
+    if fn == "attn_bwd_ex":
+        _dev(o, "o")
+        _dtype_code(o)
+        _expect(o, (B, Hq, Nq, d), None, "o", q)
+    else:
+        _expect(o, (B, Hq, Nq, d), torch.float32, "o (the float32 output of the forward)", q)
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse", q)
+    scale = _scale(scale, d)
     code = _dtype_code(q)
-    if dq is None:
-        dq = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
-    if dk is None:
-        dk = torch.empty((B, Hkv, Nk, d), device=q.device, dtype=torch.float32)
-    if dv is None:
-        dv = torch.empty((B, Hkv, Nk, d), device=q.device, dtype=torch.float32)
+    dq = _out(dq, (B, Hq, Nq, d), torch.float32, "dq", q, stream)
+    dk = _out(dk, (B, Hkv, Nk, d), torch.float32, "dk", q, stream)
+    dv = _out(dv, (B, Hkv, Nk, d), torch.float32, "dv", q, stream)
     nbytes = attn_bwd_workspace_bytes(code, B, Hq, Hkv, Nq, d)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+        workspace = _out(None, (max(nbytes, 256),), torch.uint8, "workspace", q, stream)
+    else:
+        _dev(workspace, "workspace")
     if dlse is not None:
-        if dlse.dtype != torch.float32 or tuple(dlse.shape) != (B, Hq, Nq):
-            raise ValueError("dlse must be float32 of the shape of lse")
-        dlse_p = _ptr(_dev(dlse, "dlse"))
+        dlse_p = _ptr(_expect(dlse, (B, Hq, Nq), torch.float32, "dlse", q))
     elif fn == "attn_bwd_dlse":
         raise ValueError("attn_bwd_dlse needs dlse")
     else:
         dlse_p = None
     head = ((code, _dtype_code(o)) if fn == "attn_bwd_ex" else (code,)) + (B, Hq, Hkv) + \
-        ((Nq, Nk) if fn in ("attn_bwd_kv", "attn_bwd_rope", "attn_bwd_ex") else (Nq,)) + \
+        ((Nq, Nk) if fn in _KV_FORMS else (Nq,)) + \
         (d, int(bool(causal)), scale) + ((float(base),) if fn == "attn_bwd_rope" else ()) + \
         (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout))
-    tail = (_ptr(_dev(dq, "dq")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _ptr(workspace),
+    tail = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     rc = getattr(lib(), fn)(*head, *((dlse_p,) if fn != "attn_bwd" else ()), *tail)
     _check(fn, rc)
@@ -241,33 +281,37 @@ def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, worksp
 def attn_bwd_preprocess(o, dout, delta=None, stream=None):
     """Stage 1 of the backward: delta [B,Hq,N] f32 = rowwise dout . o."""
     torch = _torch()
-    _dev(o, "o")
     _dev(dout, "dout")
+    if dout.dim() != 4:
+        raise ValueError("dout must be [B, Hq, N, d]")
     B, Hq, N, d = dout.shape
-    if delta is None:
-        delta = torch.empty((B, Hq, N), device=dout.device, dtype=torch.float32)
+    _expect(o, (B, Hq, N, d), torch.float32, "o", dout)
+    delta = _out(delta, (B, Hq, N), torch.float32, "delta", dout, stream)
     rc = lib().attn_bwd_preprocess(_dtype_code(dout), B, Hq, N, d, _ptr(o), _ptr(dout),
-                                   _ptr(_dev(delta, "delta")), _stream(stream))
+                                   _ptr(delta), _stream(stream))
     _check("attn_bwd_preprocess", rc)
     return delta
+
+
+def _stage_inputs(q, k, v, lse, dout, delta):
+    torch = _torch()
+    B, Hq, Hkv, N, _, d = _qkv(q, k, v, square=True)
+    _expect(lse, (B, Hq, N), torch.float32, "lse", q)
+    _expect(dout, (B, Hq, N, d), q.dtype, "dout", q)
+    _expect(delta, (B, Hq, N), torch.float32, "delta", q)
+    return B, Hq, Hkv, N, d
 
 
 def attn_bwd_dkdv(q, k, v, lse, dout, delta, causal=True, scale=None, dk=None, dv=None,
                   stream=None):
     """Stage 2 of the backward: (dk, dv) f32."""
     torch = _torch()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if dk is None:
-        dk = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
-    if dv is None:
-        dv = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
-    rc = lib().attn_bwd_dkdv(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                             _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                             _ptr(_dev(lse, "lse")), _ptr(_dev(dout, "dout")),
-                             _ptr(_dev(delta, "delta")), _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")),
-                             _stream(stream))
+    B, Hq, Hkv, N, d = _stage_inputs(q, k, v, lse, dout, delta)
+    dk = _out(dk, (B, Hkv, N, d), torch.float32, "dk", q, stream)
+    dv = _out(dv, (B, Hkv, N, d), torch.float32, "dv", q, stream)
+    rc = lib().attn_bwd_dkdv(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), _scale(scale, d),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                             _ptr(dk), _ptr(dv), _stream(stream))
     _check("attn_bwd_dkdv", rc)
     return dk, dv
 
@@ -275,17 +319,28 @@ def attn_bwd_dkdv(q, k, v, lse, dout, delta, causal=True, scale=None, dk=None, d
 def attn_bwd_dq(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, stream=None):
     """Stage 3 of the backward: dq f32."""
     torch = _torch()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if dq is None:
-        dq = torch.empty((B, Hq, N, d), device=q.device, dtype=torch.float32)
-    rc = lib().attn_bwd_dq(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                           _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                           _ptr(_dev(lse, "lse")), _ptr(_dev(dout, "dout")),
-                           _ptr(_dev(delta, "delta")), _ptr(_dev(dq, "dq")), _stream(stream))
+    B, Hq, Hkv, N, d = _stage_inputs(q, k, v, lse, dout, delta)
+    dq = _out(dq, (B, Hq, N, d), torch.float32, "dq", q, stream)
+    rc = lib().attn_bwd_dq(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), _scale(scale, d),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                           _ptr(dq), _stream(stream))
     _check("attn_bwd_dq", rc)
     return dq
+
+
+def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, dk=None, dv=None,
+                   stream=None):
+    """Stages 2 and 3 of the backward as attn_bwd runs them: (dq, dk, dv) f32."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _stage_inputs(q, k, v, lse, dout, delta)
+    dq = _out(dq, (B, Hq, N, d), torch.float32, "dq", q, stream)
+    dk = _out(dk, (B, Hkv, N, d), torch.float32, "dk", q, stream)
+    dv = _out(dv, (B, Hkv, N, d), torch.float32, "dv", q, stream)
+    rc = lib().attn_bwd_grads(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), _scale(scale, d),
+                              _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    _check("attn_bwd_grads", rc)
+    return dq, dk, dv
 
 
 def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None, o=None, lse=None,
@@ -293,16 +348,12 @@ def attn_fwd_kv(q, k, v, causal: bool = True, scale: float | None = None, o=None
     """Forward of q [B,Hq,Nq,d] against k, v [B,Hkv,Nk,d] (Nk >= Nq, queries at the last Nq
     positions) -> (o [B,Hq,Nq,d] f32, lse [B,Hq,Nq] f32)."""
     torch = _torch()
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if o is None:
-        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
-    rc = lib().attn_fwd_kv(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
-                           _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                           _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v, square=False)
+    o = _out(o, (B, Hq, Nq, d), torch.float32, "o", q, stream)
+    lse = _out(lse, (B, Hq, Nq), torch.float32, "lse", q, stream)
+    rc = lib().attn_fwd_kv(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                           _scale(scale, d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           _stream(stream))
     _check("attn_fwd_kv", rc)
     return o, lse
 
@@ -312,17 +363,17 @@ def attn_fwd_ex(q, k, v, causal: bool = True, scale: float | None = None, o_dtyp
     """The general forward: q [B,Hq,Nq,d] against k, v [B,Hkv,Nk,d] (Nk >= Nq), o in o_dtype
     (torch.float32, the default, or torch.bfloat16).  Returns (o, lse)."""
     torch = _torch()
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v, square=False)
+    if o is not None and o_dtype is None:
+        o_dtype = o.dtype
     o_dtype = torch.float32 if o_dtype is None else o_dtype
-    if o is None:
-        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=o_dtype)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    if o_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported output dtype {o_dtype}; use float32 or bfloat16")
+    o = _out(o, (B, Hq, Nq, d), o_dtype, "o", q, stream)
+    lse = _out(lse, (B, Hq, Nq), torch.float32, "lse", q, stream)
     rc = lib().attn_fwd_ex(_dtype_code(q), _dtype_code(o), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
-                           scale, _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                           _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+                           _scale(scale, d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           _stream(stream))
     _check("attn_fwd_ex", rc)
     return o, lse
 
@@ -337,14 +388,13 @@ def attn_bwd_ex(q, k, v, o, lse, dout, causal: bool = True, scale: float | None 
 def attn_rope(x, pos0: int, base: float, inverse: bool = False, y=None, stream=None):
     """Rotary positions on x [B,H,N,d] (row n at position pos0 + n) into y (default: a new
     tensor; y may be x).  inverse: the transposed rotation."""
-    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
     B, H, N, d = x.shape
-    if y is None:
-        y = torch.empty_like(x)
-    if y.shape != x.shape or y.dtype != x.dtype:
-        raise ValueError("y must match x in shape and dtype")
+    y = _out(y, tuple(x.shape), x.dtype, "y", x, stream)
     rc = lib().attn_rope(_dtype_code(x), B, H, N, d, int(pos0), float(base), int(bool(inverse)),
-                         _ptr(_dev(x, "x")), _ptr(_dev(y, "y")), _stream(stream))
+                         _ptr(x), _ptr(y), _stream(stream))
     _check("attn_rope", rc)
     return y
 
@@ -354,19 +404,14 @@ def attn_fwd_rope(q, k, v, causal: bool = True, scale: float | None = None, base
     """Forward over rotated q (row i at position Nk - Nq + i) and k (row j at j).
     Returns (o, lse, q_rot, k_rot); attn_bwd_rope takes q_rot and k_rot."""
     torch = _torch()
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    q_rot = torch.empty_like(q) if q_rot is None else q_rot
-    k_rot = torch.empty_like(k) if k_rot is None else k_rot
-    if o is None:
-        o = torch.empty((B, Hq, Nq, d), device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
-    rc = lib().attn_fwd_rope(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
-                             float(base), _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                             _ptr(_dev(q_rot, "q_rot")), _ptr(_dev(k_rot, "k_rot")),
-                             _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v, square=False)
+    q_rot = _out(q_rot, tuple(q.shape), q.dtype, "q_rot", q, stream)
+    k_rot = _out(k_rot, tuple(k.shape), k.dtype, "k_rot", q, stream)
+    o = _out(o, (B, Hq, Nq, d), torch.float32, "o", q, stream)
+    lse = _out(lse, (B, Hq, Nq), torch.float32, "lse", q, stream)
+    rc = lib().attn_fwd_rope(_dtype_code(q), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                             _scale(scale, d), float(base), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(q_rot), _ptr(k_rot), _ptr(o), _ptr(lse), _stream(stream))
     _check("attn_fwd_rope", rc)
     return o, lse, q_rot, k_rot
 
@@ -379,31 +424,28 @@ def attn_bwd_rope(q_rot, k_rot, v, o, lse, dout, causal: bool = True, scale: flo
                      dv, workspace, stream, base=base)
 
 
-def attn_bwd_grads(q, k, v, lse, dout, delta, causal=True, scale=None, dq=None, dk=None, dv=None,
-                   stream=None):
-    """Stages 2 and 3 of the backward as attn_bwd runs them: (dq, dk, dv) f32."""
-    torch = _torch()
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if dq is None:
-        dq = torch.empty((B, Hq, N, d), device=q.device, dtype=torch.float32)
-    if dk is None:
-        dk = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
-    if dv is None:
-        dv = torch.empty((B, Hkv, N, d), device=q.device, dtype=torch.float32)
-    rc = lib().attn_bwd_grads(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)), scale,
-                              _ptr(_dev(q, "q")), _ptr(_dev(k, "k")), _ptr(_dev(v, "v")),
-                              _ptr(_dev(lse, "lse")), _ptr(_dev(dout, "dout")),
-                              _ptr(_dev(delta, "delta")), _ptr(_dev(dq, "dq")),
-                              _ptr(_dev(dk, "dk")), _ptr(_dev(dv, "dv")), _stream(stream))
-    _check("attn_bwd_grads", rc)
-    return dq, dk, dv
+def attn_bwd_grads_plan(dtype_code: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                        causal: bool, scale: float):
+    """(one_kernel, groups, blocks): whether attn_bwd_grads (and the gradient part of attn_bwd /
+    attn_bwd_kv) runs as one kernel for this shape, and its plan's block groups and grid size."""
+    g, b = ctypes.c_int(0), ctypes.c_int(0)
+    one = lib().attn_bwd_grads_plan(int(dtype_code), int(B), int(Hq), int(Hkv), int(Nq), int(Nk),
+                                    int(d), int(bool(causal)), float(scale), ctypes.byref(g),
+                                    ctypes.byref(b))
+    return bool(one), int(g.value), int(b.value)
 
 
-def attn_bwd_grads_single_launch(dtype_code: int, N: int, d: int, scale: float) -> bool:
-    """Whether attn_bwd_grads runs as one kernel for this dtype code, N, d, scale."""
-    return bool(lib().attn_bwd_grads_single_launch(int(dtype_code), int(N), int(d), float(scale)))
+def _decode_inputs(q, k_cache, v_cache, cache_name="caches"):
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, n)
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, Hkv, L, d]")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _dtype_code(q)
+    _expect(k_cache, (B, Hkv, L, d), q.dtype, "k_cache", q)
+    _expect(v_cache, (B, Hkv, L, d), q.dtype, "v_cache", q)
+    return B, Hq, Hkv, L, d
 
 
 def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, n_splits: int,
@@ -413,25 +455,19 @@ def attn_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, n_splits: in
     [B,Hkv,L_cap,d] (row seq_lens[b] is written), seq_lens int32 [B] on the device
     -> (o [B,Hq,d], lse [B,Hq]) f32."""
     torch = _torch()
-    B, Hq, d = q.shape
-    Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
-        raise ValueError(f"seq_lens must be int32 of shape ({B},)")
-    if part_o is None:
-        part_o = torch.empty((B, Hq, n_splits, d), device=q.device, dtype=torch.float32)
-    if part_lse is None:
-        part_lse = torch.empty((B, Hq, n_splits), device=q.device, dtype=torch.float32)
-    if o is None:
-        o = torch.empty((B, Hq, d), device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
-    rc = lib().attn_decode_append(_dtype_code(q), B, Hq, Hkv, L_cap, d, scale, int(n_splits),
-                                  _ptr(_dev(q, "q")), _ptr(_dev(k_new, "k_new")),
-                                  _ptr(_dev(v_new, "v_new")), _ptr(_dev(k_cache, "k_cache")),
-                                  _ptr(_dev(v_cache, "v_cache")), _ptr(_dev(seq_lens, "seq_lens")),
-                                  _ptr(_dev(part_o, "part_o")), _ptr(_dev(part_lse, "part_lse")),
-                                  _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    B, Hq, Hkv, L_cap, d = _decode_inputs(q, k_cache, v_cache)
+    _expect(k_new, (B, Hkv, d), q.dtype, "k_new", q)
+    _expect(v_new, (B, Hkv, d), q.dtype, "v_new", q)
+    _expect(seq_lens, (B,), torch.int32, "seq_lens", q)
+    S = int(n_splits)
+    part_o = _out(part_o, (B, Hq, S, d), torch.float32, "part_o", q, stream)
+    part_lse = _out(part_lse, (B, Hq, S), torch.float32, "part_lse", q, stream)
+    o = _out(o, (B, Hq, d), torch.float32, "o", q, stream)
+    lse = _out(lse, (B, Hq), torch.float32, "lse", q, stream)
+    rc = lib().attn_decode_append(_dtype_code(q), B, Hq, Hkv, L_cap, d, _scale(scale, d), S,
+                                  _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(seq_lens), _ptr(part_o), _ptr(part_lse),
+                                  _ptr(o), _ptr(lse), _stream(stream))
     _check("attn_decode_append", rc)
     return o, lse
 
@@ -440,20 +476,12 @@ def attn_decode(q, k_cache, v_cache, n_splits: int, scale: float | None = None,
                 part_o=None, part_lse=None, stream=None):
     """Split-KV decode.  q [B,Hq,d], caches [B,Hkv,L,d] -> (part_o [B,Hq,S,d], part_lse [B,Hq,S])."""
     torch = _torch()
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _dev(t, n)
-    B, Hq, d = q.shape
-    _, Hkv, L, _ = k_cache.shape
-    if v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("caches must be [B, Hkv, L, d] with q's dtype")
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    if part_o is None:
-        part_o = torch.empty((B, Hq, n_splits, d), device=q.device, dtype=torch.float32)
-    if part_lse is None:
-        part_lse = torch.empty((B, Hq, n_splits), device=q.device, dtype=torch.float32)
-    rc = lib().attn_decode(_dtype_code(q), B, Hq, Hkv, L, d, scale, int(n_splits),
-                           _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                           _ptr(_dev(part_o, "part_o")), _ptr(_dev(part_lse, "part_lse")),
+    B, Hq, Hkv, L, d = _decode_inputs(q, k_cache, v_cache)
+    S = int(n_splits)
+    part_o = _out(part_o, (B, Hq, S, d), torch.float32, "part_o", q, stream)
+    part_lse = _out(part_lse, (B, Hq, S), torch.float32, "part_lse", q, stream)
+    rc = lib().attn_decode(_dtype_code(q), B, Hq, Hkv, L, d, _scale(scale, d), S,
+                           _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(part_o), _ptr(part_lse),
                            _stream(stream))
     _check("attn_decode", rc)
     return part_o, part_lse
@@ -466,22 +494,15 @@ def attn_decode_merged(q, k_cache, v_cache, n_splits: int, scale: float | None =
     Returns (o [B,Hq,d], lse [B,Hq], part_o, part_lse).
     """
     torch = _torch()
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _dev(t, n)
-    B, Hq, d = q.shape
-    _, Hkv, L, _ = k_cache.shape
-    if v_cache.shape != k_cache.shape or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise ValueError("caches must be [B, Hkv, L, d] with q's dtype")
-    scale = float(d) ** -0.5 if scale is None else float(scale)
-    f32 = dict(device=q.device, dtype=torch.float32)
-    part_o = torch.empty((B, Hq, n_splits, d), **f32) if part_o is None else part_o
-    part_lse = torch.empty((B, Hq, n_splits), **f32) if part_lse is None else part_lse
-    o = torch.empty((B, Hq, d), **f32) if o is None else o
-    lse = torch.empty((B, Hq), **f32) if lse is None else lse
-    rc = lib().attn_decode_merged(_dtype_code(q), B, Hq, Hkv, L, d, scale, int(n_splits),
-                                  _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                  _ptr(_dev(part_o, "part_o")), _ptr(_dev(part_lse, "part_lse")),
-                                  _ptr(_dev(o, "o")), _ptr(_dev(lse, "lse")), _stream(stream))
+    B, Hq, Hkv, L, d = _decode_inputs(q, k_cache, v_cache)
+    S = int(n_splits)
+    part_o = _out(part_o, (B, Hq, S, d), torch.float32, "part_o", q, stream)
+    part_lse = _out(part_lse, (B, Hq, S), torch.float32, "part_lse", q, stream)
+    o = _out(o, (B, Hq, d), torch.float32, "o", q, stream)
+    lse = _out(lse, (B, Hq), torch.float32, "lse", q, stream)
+    rc = lib().attn_decode_merged(_dtype_code(q), B, Hq, Hkv, L, d, _scale(scale, d), S,
+                                  _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(part_o),
+                                  _ptr(part_lse), _ptr(o), _ptr(lse), _stream(stream))
     _check("attn_decode_merged", rc)
     return o, lse, part_o, part_lse
 
@@ -490,13 +511,26 @@ def attn_lse_merge(part_o, part_lse, o=None, lse=None, stream=None):
     """Merge split partials: part_o [B,Hq,S,d], part_lse [B,Hq,S] -> (o [B,Hq,d], lse [B,Hq])."""
     torch = _torch()
     _dev(part_o, "part_o")
-    _dev(part_lse, "part_lse")
+    if part_o.dim() != 4:
+        raise ValueError("part_o must be [B, Hq, S, d]")
     B, Hq, S, d = part_o.shape
-    if o is None:
-        o = torch.empty((B, Hq, d), device=part_o.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty((B, Hq), device=part_o.device, dtype=torch.float32)
-    rc = lib().attn_lse_merge(B, Hq, S, d, _ptr(part_o), _ptr(part_lse), _ptr(_dev(o, "o")),
-                              _ptr(_dev(lse, "lse")), _stream(stream))
+    _expect(part_o, (B, Hq, S, d), torch.float32, "part_o")
+    _expect(part_lse, (B, Hq, S), torch.float32, "part_lse", part_o)
+    o = _out(o, (B, Hq, d), torch.float32, "o", part_o, stream)
+    lse = _out(lse, (B, Hq), torch.float32, "lse", part_o, stream)
+    rc = lib().attn_lse_merge(B, Hq, S, d, _ptr(part_o), _ptr(part_lse), _ptr(o), _ptr(lse),
+                              _stream(stream))
     _check("attn_lse_merge", rc)
     return o, lse
+
+
+def attn_read_probe(src, out=None, stream=None):
+    """Read every byte of the contiguous device tensor src once (a bandwidth reference for
+    decode); out: a device int32 tensor of one element (written only on a sentinel match)."""
+    torch = _torch()
+    _dev(src, "src")
+    out = _out(out, (1,), torch.int32, "out", src, stream)
+    nbytes = src.numel() * src.element_size()
+    rc = lib().attn_read_probe(_ptr(src), nbytes, _ptr(out), _stream(stream))
+    _check("attn_read_probe", rc)
+    return out

@@ -13,8 +13,6 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <mutex>
-
 namespace {
 
 using attn::kBF16;
@@ -122,40 +120,17 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, 
 // side by side on two streams, 79.8-80.0 us with the one launch).  Otherwise
 // -- d = 128, where the one launch would hold dQ to the dK/dV kernel's
 // one-wave-per-SIMD occupancy (694 us vs 713 us for the 32/8-head N = 4096
-// step), and the row-wise fallback -- the dK/dV and dQ kernels run
-// concurrently: dQ goes to an auxiliary stream of the device, forked from and
-// joined back into the caller's stream with events (so a graph capture of the
-// caller's stream captures both branches).  One auxiliary stream and two
-// events per device are created on first use (default priority); the
-// fork/join is serialised by a mutex so that concurrent callers do not
-// interleave their event records.
+// step), the row-wise fallback, and shapes whose one-launch plan does not fit
+// its kernel argument -- the dQ kernel and then the dK/dV kernel run on the
+// caller's stream (side by side on two streams they gained nothing at d = 128:
+// both are bound by the same CU resources).
 bool fuse_bwd(int d) { return d == 64; }
 
-struct BwdAux {
-    hipStream_t st = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-
-constexpr int kMaxDevices = 64;
-std::mutex g_aux_mu;
-BwdAux g_aux[kMaxDevices];
-
-// The device's auxiliary stream and events (created on first use), or null
-// when they cannot be used: creation failed, or `st` is capturing and they do
-// not exist yet (nothing may be created during a capture).  Call with
-// g_aux_mu held.
-BwdAux *bwd_aux(hipStream_t st)
+bool one_launch(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                int hs, int *groups = nullptr, int *blocks = nullptr)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    BwdAux &a = g_aux[dev];
-    if (a.st && a.fork && a.join) return &a;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    if (!a.st && hipStreamCreateWithFlags(&a.st, hipStreamNonBlocking) != hipSuccess) a.st = nullptr;
-    if (!a.fork && hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess) a.fork = nullptr;
-    if (!a.join && hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess) a.join = nullptr;
-    return (a.st && a.fork && a.join) ? &a : nullptr;
+    return use_mfma(dt, Nk, d, scale) && fuse_bwd(d) &&
+           attn::bwd_fused_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, groups, blocks);
 }
 
 // dQ, dK, dV from delta (dk/dv already zero when hs > 1).
@@ -164,28 +139,14 @@ attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int
                              const float *lse, const void *dout, const float *delta, float *dq,
                              float *dk, float *dv, int hs, hipStream_t st, double rope_lb = 0.0)
 {
-    if (use_mfma(dt, Nk, d, scale) && fuse_bwd(d))
+    if (one_launch(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, hs))
         return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v,
                                                lse, dout, delta, dq, dk, dv, hs, st, rope_lb));
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    BwdAux *aux = bwd_aux(st);
-    hipStream_t st_dq = st;
-    if (aux) {
-        if (hipEventRecord(aux->fork, st) != hipSuccess ||
-            hipStreamWaitEvent(aux->st, aux->fork, 0) != hipSuccess)
-            return ATTN_ERR_HIP;
-        st_dq = aux->st;
-    }
-    if (launch_bwd_dq(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dq,
-                      st_dq, rope_lb) != hipSuccess)
+    if (launch_bwd_dq(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dq, st,
+                      rope_lb) != hipSuccess)
         return ATTN_ERR_HIP;
-    if (launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dk,
-                        dv, hs, st, rope_lb) != hipSuccess)
-        return ATTN_ERR_HIP;
-    if (aux && (hipEventRecord(aux->join, aux->st) != hipSuccess ||
-                hipStreamWaitEvent(st, aux->join, 0) != hipSuccess))
-        return ATTN_ERR_HIP;
-    return ATTN_OK;
+    return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout,
+                                      delta, dk, dv, hs, st, rope_lb));
 }
 
 // The whole backward of Nq query rows against Nk >= Nq keys: the preprocess
@@ -430,10 +391,14 @@ attn_status attn_bwd_grads(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, 
                             dk, dv, hs, st);
 }
 
-int attn_bwd_grads_single_launch(attn_dtype dt, int N, int d, float scale)
+int attn_bwd_grads_plan(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, int *groups, int *blocks)
 {
-    if (check_common(dt, 1, 1, 1, N, d, scale) != ATTN_OK) return 0;
-    return use_mfma(dt, N, d, scale) && fuse_bwd(d) ? 1 : 0;
+    if (groups) *groups = 0;
+    if (blocks) *blocks = 0;
+    if (Nq <= 0 || Nk < Nq || check_common(dt, B, Hq, Hkv, Nk, d, scale) != ATTN_OK) return 0;
+    const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale);
+    return one_launch(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, hs, groups, blocks) ? 1 : 0;
 }
 
 attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, float scale,
@@ -516,6 +481,14 @@ attn_status attn_lse_merge(int B, int Hq, int n_splits, int d, const float *part
         attn::lse_merge(B, Hq, n_splits, d, part_o, part_lse, o, lse, (hipStream_t)stream));
 }
 
+attn_status attn_read_probe(const void *src, size_t bytes, unsigned *out, void *stream)
+{
+    if (!aligned16(src) || out == nullptr || ((uintptr_t)out & 3u) != 0) return ATTN_ERR_INVALID_ARG;
+    if (bytes == 0 || bytes % 16 != 0) return ATTN_ERR_INVALID_ARG;
+    if (bytes > ((size_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+    return hip_status(attn::read_probe(src, (long)bytes, out, (hipStream_t)stream));
+}
+
 const char *attn_status_str(attn_status s)
 {
     switch (s) {
@@ -528,6 +501,6 @@ const char *attn_status_str(attn_status s)
     return "unknown status";
 }
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 }  // extern "C"

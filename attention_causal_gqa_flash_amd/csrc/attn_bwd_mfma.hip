@@ -787,6 +787,17 @@ hipError_t bwd_variant(int d, bool xl, F &&f)
 
 }  // namespace
 
+int device_cus()
+{
+    // the current device's compute-unit count, queried per call (each device
+    // of a process may differ); 256 (MI355X) when no device answers
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        return n;
+    return 256;
+}
+
 int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
 {
     // Split each group's query heads over workgroups until there are about two
@@ -795,15 +806,7 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
     // x 64 grouped-query workload 46.5 -> 39.6 us with the 3 heads split, while
     // splitting further than two items per CU (32/8 heads at N = 4096) only
     // adds atomic traffic.
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
+    const int cus = device_cus();
     const int G = Hq / Hkv;
     const long base = (long)((Nk + kKvBN - 1) / kKvBN) * B * Hkv;
     int hs = 1;
@@ -896,7 +899,13 @@ void plan_levels(int kind, int nlev, int cap, const double *cost, const int *lev
 
 }  // namespace
 
-BwdPlan bwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *grid)
+// The one-launch plan of a shape, or false when its level groups do not fit
+// BwdPlan (the caller then runs the two gradient kernels instead).  The dK/dV
+// side splits a group wherever the key tiles' head split changes, so it can
+// hold more groups than its cap: the caps shrink (dK/dV first) until both
+// sides fit together.
+bool bwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, BwdPlan &p,
+              int *grid)
 {
     const int off = Nk - Nq;
     const int nkt = (Nk + kKvBN - 1) / kKvBN, nqkv = (Nq + kKvSub * kKvBM - 1) / (kKvSub * kKvBM);
@@ -925,29 +934,50 @@ BwdPlan bwd_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int 
         cq[j] = dq_cost((kv_end + kQBN - 1) / kQBN, d);
     }
     std::vector<PlanLevel> a, q, m;
-    plan_levels(0, nkt, BwdPlan::kMax / 2, ck.data(), lk.data(), hk.data(), a);
-    plan_levels(1, nqt, BwdPlan::kMax / 2, cq.data(), lq.data(), hq.data(), q);
+    int cap_a = BwdPlan::kMax / 2, cap_q = BwdPlan::kMax / 2;
+    for (;;) {
+        a.clear();
+        q.clear();
+        plan_levels(0, nkt, cap_a, ck.data(), lk.data(), hk.data(), a);
+        plan_levels(1, nqt, cap_q, cq.data(), lq.data(), hq.data(), q);
+        if (a.size() + q.size() <= (size_t)BwdPlan::kMax) break;
+        if (cap_a > 1) --cap_a;
+        else if (cap_q > 1) --cap_q;
+        else return false;
+    }
     // merge, heaviest first (ties: dK/dV first)
     size_t ia = 0, iq = 0;
     while (ia < a.size() || iq < q.size()) {
         if (iq == q.size() || (ia < a.size() && a[ia].cost >= q[iq].cost)) m.push_back(a[ia++]);
         else m.push_back(q[iq++]);
     }
-    BwdPlan p{};
+    p = BwdPlan{};
     p.n = (int)m.size();
-    int blk = 0;
+    long blk = 0;
     for (int i = 0; i < p.n; ++i) {
         const int per_level = m[i].kind == 0 ? B * Hkv * m[i].hs : B * Hq;
         const int per_xcd = (per_level + kXcds - 1) / kXcds;
-        p.first[i] = blk;
+        p.first[i] = (int)blk;
         p.lev0[i] = m[i].lev;
         p.kind[i] = m[i].kind;
         p.hs[i] = m[i].hs;
-        blk += m[i].nlev * per_xcd * kXcds;
+        blk += (long)m[i].nlev * per_xcd * kXcds;
+        if (blk > 2147483647L) return false;
     }
-    p.first[p.n] = blk;
-    *grid = blk;
-    return p;
+    p.first[p.n] = (int)blk;
+    *grid = (int)blk;
+    return true;
+}
+
+bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *groups,
+                    int *blocks)
+{
+    BwdPlan p;
+    int nblk = 0;
+    if (!bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, p, &nblk)) return false;
+    if (groups) *groups = p.n;
+    if (blocks) *blocks = nblk;
+    return true;
 }
 
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
@@ -955,8 +985,9 @@ hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
                           int hs, hipStream_t st, double rope_lb)
 {
+    BwdPlan plan;
     int nblk = 0;
-    const BwdPlan plan = bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, &nblk);
+    if (!bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, plan, &nblk)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nblk);
     return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
         hipLaunchKernelGGL((bwd_fused_kernel<decltype(dc)::value, decltype(xc)::value>), grid,

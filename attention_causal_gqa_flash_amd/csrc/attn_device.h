@@ -77,19 +77,38 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t *p)
 }
 
 // Row-major bf16 tiles [rows][D] in LDS with their 16-byte chunks XOR-swizzled
-// by row: logical chunk c of row r lives at chunk c ^ swz(r).  swz is chosen so
-// that the two read patterns of the kernels hit distinct banks:
+// by row: logical chunk c of row r lives at chunk c ^ swz(r).  swz spreads the
+// two read patterns of the kernels over the banks:
 //   * 16 consecutive rows reading the same logical chunk (ds_read_b128 of an
 //     MFMA operand row): swz takes 16 (D = 128) or 8 (D = 64) distinct values
 //     over consecutive rows;
 //   * 4 aligned rows x 2 adjacent chunks (the transposed reads of tr_operand):
 //     swz(r) >> 1 differs between the 4 rows while its low bit is shared.
+// That is conflict-free for 128 bytes a clock.  The gfx950 LDS serves 256
+// bytes a clock (64 banks), and at that width this layout leaves 2-way
+// conflicts (counted on MI355X: 24-33% of the LDS-active cycles of the
+// forward, dQ and dK/dV kernels at d = 128).  ATTN_LDS_SWIZZLE_256 selects a
+// layout that is conflict-free at 256 bytes (a bijection of 16 consecutive
+// rows, and 4 distinct swz >> 2 over 4 aligned rows at D = 128; the same per
+// row parity at D = 64): it removed every conflict, left the forward and
+// dK/dV kernels' times unchanged (their LDS is 30-40% busy) and made the dQ
+// kernel, which uses all 256 of its registers, spill 8 of them (+6%).  It is
+// therefore not the default.
 template <int D>
 __device__ __forceinline__ int swz(int row)
 {
     static_assert(D == 64 || D == 128, "swizzle defined for 8 or 16 chunks per row");
+#ifdef ATTN_LDS_SWIZZLE_256
+    if constexpr (D == 128) {
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else {
+        const int a = (row >> 1) & 7;
+        return ((a & 1) << 2) | (a >> 1);
+    }
+#else
     const int f = ((row & 3) << 1) | ((row >> 2) & 1);
     return D == 128 ? (f | (row & 8)) : f;
+#endif
 }
 
 template <int D>
@@ -133,7 +152,7 @@ struct TileCopy {
     static constexpr int BLOCKS = ROWS * CPR / 64;
     static constexpr int PER_WAVE = BLOCKS / NW;      // copy instructions per wave
     static_assert(ROWS * CPR % 64 == 0 && BLOCKS % NW == 0, "whole 1 KiB blocks per wave");
-    static_assert((64 * NW / CPR) % (D == 128 ? 16 : 8) == 0, "block stride keeps the swizzle");
+    static_assert((64 * NW / CPR) % 16 == 0, "block stride keeps the swizzle");
     int voff;                                         // byte offset of this lane in block `wave`
 
     __device__ __forceinline__ TileCopy(int wave, int lane)

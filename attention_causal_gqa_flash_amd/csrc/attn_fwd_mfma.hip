@@ -372,15 +372,7 @@ hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
                            const void *q, const void *k, const void *v, void *o, float *lse,
                            hipStream_t st)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
+    const int cus = device_cus();
     const int nqt = (Nq + kBM - 1) / kBM;
     // Key split of small grids.  d = 64 (32-key tiles, 32 KB of LDS, up to
     // three workgroups per CU): when the 128-row workgroups would not give

@@ -40,6 +40,11 @@ hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inv
 // The same over two tensors of one dtype and head dim in one launch.
 hipError_t rope2(int dt, long rows0, int N0, long pos00, const void *x0, void *y0, long rows1, int N1,
                  long pos01, const void *x1, void *y1, int d, double base, int inverse, hipStream_t st);
+// The current device's compute-unit count (256 when no device answers).
+int device_cus();
+// Reads `bytes` (a multiple of 16) at src once; writes *out only when the
+// XOR of everything read equals a sentinel (a read-bandwidth reference).
+hipError_t read_probe(const void *src, long bytes, unsigned *out, hipStream_t st);
 // Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
 hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
 
@@ -69,7 +74,12 @@ hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
                            const void *q, const void *k, const void *v, const float *lse,
                            const void *dout, const float *o, const float *dlse, float *Dws,
                            float *dq, hipStream_t st, double rope_lb);
-// dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1).
+// Whether the one-launch plan of a shape fits its kernel argument (at most
+// 48 block groups); writes the group and block counts.  No device work.
+bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *groups,
+                    int *blocks);
+// dQ and dK/dV in one launch (dK/dV zero-filled beforehand when hs > 1);
+// hipErrorInvalidValue, with nothing launched, when bwd_fused_plan is false.
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,

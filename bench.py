@@ -3,42 +3,56 @@
 
 One step = one pass of the whole hot path on seeded synthetic inputs already
 resident in device memory:
-  * the training op: attn_fwd, then attn_bwd (at d=64 the preprocess, then
-    one kernel holding both the dK/dV and the dQ work; at d=128 the dQ kernel,
-    which also computes the preprocess's row terms, then the dK/dV kernel) on
-    the training workload
-    (default: bf16, B=4, 12 query / 4 key-value heads, N=1024, d=64);
+  * the training op: attn_fwd, then attn_bwd on the headline training workload
+    (default: the largest one, bf16, B=1, 32 query / 8 key-value heads,
+    N=4096, d=128; at d=128 attn_bwd runs the dQ kernel, which also computes
+    the preprocess's row terms, then the dK/dV kernel; at d=64 the preprocess
+    then one kernel holding both the dK/dV and the dQ work);
   * the decode op: split-KV decode + LSE merge (attn_decode_merged: the decode
-    kernel then the merge kernel) on the decode workload (bf16, 32/8 heads, d=128, a 4096-key cache in 16
-    splits), rotating over enough distinct caches (default 24 x 16 MiB) that
-    every step reads its keys and values from HBM rather than from cache.
+    kernel then the merge kernel) on the decode workload (bf16, 32/8 heads,
+    d=128, a 4096-key cache in 16 splits), each step on the next of 24
+    distinct caches (24 x 16 MiB, more than L2 and the 256 MB last-level
+    cache), so that every step reads its keys and values from HBM.
 
-The K timed steps are captured into two HIP graphs (K training ops, K decode
-ops) and replayed once each between HIP events; the launches are the same
-C-ABI calls an eager caller makes, without the host-side launch overhead that
-would otherwise dominate the short decode op.  Each kernel's average duration
-is measured the same way (a graph of K launches of that kernel alone; the
-gradient stage `bwd_grads` is timed per attn_bwd_grads call, which includes a
-zero-fill launch of dk/dv when they are accumulated with atomics).
+Timing.  The training op and each cache's decode op are captured once into
+HIP graphs (the launches are the same C-ABI calls an eager caller makes,
+without host launch overhead).  After W untimed warm-up steps, K steps are
+timed between two device synchronisations; inside, every op of every step is
+bracketed by its own pair of HIP events on the stream that runs it.
+`ms_per_step` is the whole timed region divided by K; `value` is the
+headline workload's algorithmic fwd+bwd TFLOP/s at the MEDIAN training-op
+time (4*d flop per unmasked (query, key) pair forward, 10*d backward).
 
-Outside the step, `fwd_chunk` times attn_fwd_kv on a 512-token prefill chunk
-against a 4096-key context (workload chunk_gqa32x8_nq512_nk4096_d128, 4·d flop
-per visible pair), and `decode_append` times one decode step with cache append over
-8 sequences of their own lengths (attn_decode_append, workload
-decode_append_gqa32x8_b8_lc4096_d128_s16), rotating over 4 distinct cache pairs.
+Beside the step (reported, not timed into `ms_per_step`):
+  * `configs`: every training config (C1 f32 tiny; C2 4x1024 d64; C3 N=128
+    and 512 d128; C4 4096 d128) -- fwd alone, attn_bwd alone and fwd+bwd,
+    each the median of >= 100 iterations and >= 200 ms; decode cold (24-cache
+    rotation), warm (one cache, labelled), the decode kernel alone and the
+    read floor (attn_read_probe streaming the same 16 MiB per call over the
+    same rotation);
+  * `kernels`: each kernel of the headline step timed alone (median of
+    iterations of a graph of launches of that kernel), with its algorithmic
+    TFLOP/s, the time floor of its tiling (bounds.py) and, while the kernel
+    sources are those the counters were taken from, its measured HBM bytes;
+  * `roofline`: the kernel with the largest share of the step;
+  * `fwd_chunk` (attn_fwd_kv, a 512-token prefill chunk against 4096 keys),
+    `decode_append` (8 sequences of their own lengths, cache append) and
+    `fwd_bwd_rope` (the headline step over rotated q and k);
+  * `cpu_baseline`: the CPU f64 oracle on the headline workload, one key/value
+    group at a time until the time budget is spent (all 8 groups of the 4096-
+    token workload take about 25 s on 16 threads), with the core count and
+    the CPU model; `configs[*].oracle_s` times the oracle per config (best of 3
+    for C1-C3 and decode, the one run above for C4).
 
-Prints ONE JSON line.  `value` is the training workload's algorithmic fwd+bwd
-TFLOP/s (4*d flop per unmasked (query, key) pair forward, 10*d backward);
-`decode` gives the decode workload's GB/s of algorithmic bytes (K and V caches
-+ q read once, o and lse written once).  `roofline` describes the kernel with
-the largest share of the step's time; `cpu_baseline` times the CPU f64 oracle
-on a bounded sample of the same training workload.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -47,25 +61,32 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0          # 8 TB/s HBM3E
+HEADLINE = "gqa32x8_b1_n4096_d128"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa12x4_b4_n1024_d64",
-                    help="training workload name (see workloads.TRAIN_CONFIGS)")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="headline training workload (see workloads.TRAIN_CONFIGS)")
     ap.add_argument("--decode-caches", type=int, default=24,
                     help="distinct KV caches the decode op rotates over (cold-cache reads)")
     ap.add_argument("--append-caches", type=int, default=4,
                     help="distinct cache pairs the decode-append measurement rotates over")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="time budget of the oracle CPU baseline on the headline workload "
+                         "(0 disables every oracle timing)")
+    ap.add_argument("--min-iters", type=int, default=100,
+                    help="iterations per median (each also spans >= 200 ms)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip fwd_chunk, decode_append and fwd_bwd_rope")
     ap.add_argument("--eager", action="store_true",
-                    help="launch eagerly instead of replaying graphs (for counter collection; "
-                         "short ops are then bound by host launch overhead)")
+                    help="launch eagerly instead of replaying graphs (for counter collection: "
+                         "only the K timed steps run)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain device-to-device copy of known size (the reference "
                          "dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -73,6 +94,9 @@ def parse():
                     metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="summarise four rocprofv3 counter_collection.csv files (the bench's and "
                          "the calibration copy's FETCH_SIZE and WRITE_SIZE runs) as markdown")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="summarise rocprofv3 counter_collection.csv files of SQ/GRBM counter "
+                         "passes (MFMA busy, LDS, VALU, waits per kernel) as markdown")
     return ap.parse_args()
 
 
@@ -163,6 +187,62 @@ def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, worklo
     return "\n".join(lines)
 
 
+# gfx950 (MI355X): 8 XCDs x 32 CUs x 4 SIMDs
+XCDS, CUS, SIMDS = 8, 256, 1024
+
+
+def counter_summary(csvs) -> str:
+    """Markdown summary of SQ/GRBM counter passes per kernel (means over dispatches).
+
+    rocprofv3 reports each counter summed over its hardware instances:
+    GRBM_GUI_ACTIVE over the 8 XCDs (so the cycles of one XCD, the dispatch's
+    active clock count, are that / 8); SQ counters over every SE / SIMD.
+      MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x 1024 SIMDs)
+      bf16 flop  = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+      LDS busy   = SQ_LDS_IDX_ACTIVE / (GUI cycles x 256 CUs)
+      conflicts  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      clock      = GUI cycles / kernel duration
+    """
+    import csv
+    import re
+    agg, dur = {}, {}
+    for path in csvs:
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+                if "attn::" not in k:
+                    continue
+                k = re.sub(r"^void attn::", "", k.split("(")[0]).strip()
+                agg.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                dur.setdefault(k, {})[(path, r["Dispatch_Id"])] = \
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = ["| kernel | dispatches | duration us (median) | clock GHz | MFMA busy % | bf16 GFLOP "
+             "executed | LDS busy % | LDS conflict cycles % | VALU insts / MFMA insts | "
+             "LDS wait % of wave cycles | any-wait % of wave cycles |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(agg):
+        m = {n: sum(v) / len(v) for n, v in agg[k].items()}
+        ds = sorted(dur[k].values())
+        t_us = ds[len(ds) // 2] / 1e3
+        gui = m.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+
+        def pct(num, den):
+            return f"{100.0 * num / den:.1f}" if num is not None and den else "-"
+        mfma = m.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        lds = m.get("SQ_LDS_IDX_ACTIVE")
+        conf = m.get("SQ_LDS_BANK_CONFLICT")
+        valu, nm = m.get("SQ_INSTS_VALU"), m.get("SQ_INSTS_MFMA")
+        wc = m.get("SQ_WAVE_CYCLES")
+        wl, wa = m.get("SQ_WAIT_INST_LDS"), m.get("SQ_WAIT_INST_ANY")
+        lines.append(
+            f"| {k} | {len(ds)} | {t_us:.1f} | {gui / t_us / 1e3:.2f} | "
+            f"{pct(mfma, gui * SIMDS)} | {(mops or 0) * 512 / 1e9:.1f} | {pct(lds, gui * CUS)} | "
+            f"{pct(conf, lds)} | {(valu / nm if valu and nm else float('nan')):.2f} | "
+            f"{pct(wl, wc)} | {pct(wa, wc)} |")
+    return "\n".join(lines)
+
+
 def calibration_copy():
     import torch
     n = CALIB_BYTES // 4
@@ -174,55 +254,111 @@ def calibration_copy():
     print(json.dumps({"calibration_copy_bytes": CALIB_BYTES, "dispatches": 5}), flush=True)
 
 
-def eager_time_us(torch, fns, reps: int) -> float:
-    """Run `fns` eagerly between HIP events; microseconds divided by `reps`."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for fn in fns:
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 WARM_S = 0.05
 
 
-def graph_time_us(torch, fns, reps: int) -> float:
-    """Capture `fns` (a list of zero-argument launch callables) in a graph and
-    return the replay time in microseconds divided by `reps`."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for fn in fns[: min(len(fns), 3)]:
-            fn()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for fn in fns:
-            fn()
-    # untimed replays for at least WARM_S seconds: the GPU's clocks ramp up over
-    # the first tens of milliseconds of work (a single replay of a 40-step graph
-    # of the B=4 workload measured 77.5 us per step, the third one 72.5)
-    t0 = time.perf_counter()
-    while True:
-        g.replay()
+class Timer:
+    """Graph-replay timing with HIP events (torch.cuda.Event records on the
+    current stream, which is the stream every captured launch runs on)."""
+
+    def __init__(self, torch, min_iters: int, min_ms: float = 200.0):
+        self.torch, self.min_iters, self.min_ms = torch, min_iters, min_ms
+
+    def graph(self, fns):
+        """Capture the zero-argument launch callables `fns` into one graph."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for fn in fns[: min(len(fns), 3)]:
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        if time.perf_counter() - t0 >= WARM_S:
-            break
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def warm(self, g):
+        # the GPU's clocks ramp up over the first tens of milliseconds of work
+        t0 = time.perf_counter()
+        while True:
+            g.replay()
+            self.torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_S:
+                break
+
+    def median_us(self, fns, per_replay: int = 1) -> dict:
+        """Median over >= min_iters iterations (and >= min_ms) of one replay of a
+        graph of `fns`, each bracketed by its own events; microseconds per op
+        (`per_replay` ops per replay)."""
+        torch = self.torch
+        g = self.graph(fns)
+        self.warm(g)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        one_ms = max(e0.elapsed_time(e1), 1e-3)
+        iters = max(self.min_iters, math.ceil(self.min_ms / one_ms))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 / per_replay for a, b in ev)
+        return {"median_us": round(statistics.median(ts), 3), "mean_us": round(sum(ts) / len(ts), 3),
+                "min_us": round(ts[0], 3), "iters": iters}
+
+    def ops_for(self, fn, target_us: float = 150.0) -> int:
+        """How many launches of `fn` make a replay of about target_us (so that
+        host launch latency stays outside the events of short ops)."""
+        t = self.median_once(fn)
+        return max(1, min(64, math.ceil(target_us / max(t, 0.5))))
+
+    def median_once(self, fn) -> float:
+        torch = self.torch
+        g = self.graph([fn])
+        self.warm(g)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / 5
+
+    def op(self, fn) -> dict:
+        n = self.ops_for(fn)
+        r = self.median_us([fn] * n, n)
+        r["ops_per_replay"] = n
+        return r
 
 
 def main():
     args = parse()
     if args.traffic_summary:
         print(traffic_summary(*args.traffic_summary, workload=args.workload))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
         return
     if args.gpus != 1:
         print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only; "
@@ -241,232 +377,117 @@ def main():
         return
     attn.lib()
     dev = torch.device("cuda:0")
-
-    cfg = W.TRAIN_CONFIGS[args.workload]
-    dcfg = W.C5
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    T = Timer(torch, args.min_iters)
     f32 = dict(device=dev, dtype=torch.float32)
 
-    x = W.train_inputs(cfg)
-    g = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()}
-    B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
-    o, lse, delta = torch.empty((B, Hq, N, d), **f32), torch.empty((B, Hq, N), **f32), \
-        torch.empty((B, Hq, N), **f32)
-    dq = torch.empty((B, Hq, N, d), **f32)
-    dk, dv = torch.empty((B, Hkv, N, d), **f32), torch.empty((B, Hkv, N, d), **f32)
+    def train_setup(cfg):
+        """Device inputs and outputs of a training workload, and its launch callables."""
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        x = W.train_inputs(cfg)
+        g = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()}
+        B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
+        t = {"o": torch.empty((B, Hq, N, d), **f32), "lse": torch.empty((B, Hq, N), **f32),
+             "delta": torch.empty((B, Hq, N), **f32), "dq": torch.empty((B, Hq, N, d), **f32),
+             "dk": torch.empty((B, Hkv, N, d), **f32), "dv": torch.empty((B, Hkv, N, d), **f32)}
+        code = 1 if cfg.dtype == "bf16" else 0
+        t["ws"] = torch.empty(max(256, attn.attn_bwd_workspace_bytes(code, B, Hq, Hkv, N, d)),
+                              device=dev, dtype=torch.uint8)
+        s = cfg.scale
+        fn = {
+            "fwd": lambda: attn.attn_fwd(g["q"], g["k"], g["v"], True, s, o=t["o"], lse=t["lse"]),
+            "bwd": lambda: attn.attn_bwd(g["q"], g["k"], g["v"], t["o"], t["lse"], g["dout"], True, s,
+                                         dq=t["dq"], dk=t["dk"], dv=t["dv"], workspace=t["ws"]),
+            "bwd_preprocess": lambda: attn.attn_bwd_preprocess(t["o"], g["dout"], delta=t["delta"]),
+            "bwd_dkdv": lambda: attn.attn_bwd_dkdv(g["q"], g["k"], g["v"], t["lse"], g["dout"],
+                                                   t["delta"], True, s, dk=t["dk"], dv=t["dv"]),
+            "bwd_dq": lambda: attn.attn_bwd_dq(g["q"], g["k"], g["v"], t["lse"], g["dout"], t["delta"],
+                                               True, s, dq=t["dq"]),
+            "bwd_grads": lambda: attn.attn_bwd_grads(g["q"], g["k"], g["v"], t["lse"], g["dout"],
+                                                     t["delta"], True, s, dq=t["dq"], dk=t["dk"],
+                                                     dv=t["dv"]),
+        }
+        return x, g, t, fn
 
-    xd = W.decode_inputs(dcfg)
+    cfg = W.TRAIN_CONFIGS[args.workload]
+    B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
+    x, g, tt, fns = train_setup(cfg)
+    fns["fwd"]()
+    fns["bwd_preprocess"]()
+    torch.cuda.synchronize()
+
+    # decode workload: K and V of each cache pair in one allocation (the read
+    # probe streams both in one launch)
+    dcfg = W.C5
     ddt = torch.bfloat16 if dcfg.dtype == "bf16" else torch.float32
+    xd = W.decode_inputs(dcfg)
     qd = torch.from_numpy(xd["q"]).to(dev).to(ddt)
-    kc0 = torch.from_numpy(xd["k_cache"]).to(dev).to(ddt)
-    vc0 = torch.from_numpy(xd["v_cache"]).to(dev).to(ddt)
+    kv0 = torch.stack([torch.from_numpy(xd["k_cache"]), torch.from_numpy(xd["v_cache"])]).to(dev).to(ddt)
     ncache = max(1, args.decode_caches)
-    caches = [(kc0.clone(), vc0.clone()) for _ in range(ncache)]
+    caches = [kv0.clone() for _ in range(ncache)]
+    del kv0
     S = dcfg.n_splits
     part_o, part_lse = torch.empty((dcfg.B, dcfg.Hq, S, dcfg.d), **f32), \
         torch.empty((dcfg.B, dcfg.Hq, S), **f32)
     dec_o, dec_lse = torch.empty((dcfg.B, dcfg.Hq, dcfg.d), **f32), torch.empty((dcfg.B, dcfg.Hq), **f32)
-
-    def fwd():
-        attn.attn_fwd(g["q"], g["k"], g["v"], True, cfg.scale, o=o, lse=lse)
-
-    def pre():
-        attn.attn_bwd_preprocess(o, g["dout"], delta=delta)
-
-    def dkdv():
-        attn.attn_bwd_dkdv(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale,
-                           dk=dk, dv=dv)
-
-    def dqk():
-        attn.attn_bwd_dq(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq)
-
-    def grads():
-        attn.attn_bwd_grads(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, cfg.scale, dq=dq,
-                            dk=dk, dv=dv)
-
-    dt_code = 1 if cfg.dtype == "bf16" else 0
-    grads_one_kernel = attn.attn_bwd_grads_single_launch(dt_code, N, d, cfg.scale)
-
-    bwd_ws = torch.empty(max(256, attn.attn_bwd_workspace_bytes(1 if cfg.dtype == "bf16" else 0,
-                                                                B, Hq, Hkv, N, d)),
-                         device=dev, dtype=torch.uint8)
-
-    def bwd():
-        # the whole backward as a caller runs it (dK/dV and dQ side by side)
-        attn.attn_bwd(g["q"], g["k"], g["v"], o, lse, g["dout"], True, cfg.scale, dq=dq, dk=dk,
-                      dv=dv, workspace=bwd_ws)
+    probe_out = torch.zeros(1, device=dev, dtype=torch.int32)
 
     def decode(i):
-        kc, vc = caches[i % ncache]
-        return lambda: attn.attn_decode_merged(qd, kc, vc, S, dcfg.scale, part_o=part_o,
+        kv = caches[i % ncache]
+        return lambda: attn.attn_decode_merged(qd, kv[0], kv[1], S, dcfg.scale, part_o=part_o,
                                                part_lse=part_lse, o=dec_o, lse=dec_lse)
 
-    # decode step with cache append (per-sequence lengths), outside the step:
-    # rotates over distinct cache pairs so that its reads come from HBM
-    acfg = W.C6
-    xa = W.decode_append_inputs(acfg)
-    ga = {n: torch.from_numpy(xa[n]).to(dev).to(ddt) for n in ("q", "k_new", "v_new")}
-    a_lens = torch.from_numpy(xa["seq_lens"]).to(dev)
-    ka0 = torch.from_numpy(xa["k_cache"]).to(dev).to(ddt)
-    va0 = torch.from_numpy(xa["v_cache"]).to(dev).to(ddt)
-    a_ncache = max(1, args.append_caches)
-    a_caches = [(ka0.clone(), va0.clone()) for _ in range(a_ncache)]
-    del ka0, va0
-    a_po = torch.empty((acfg.B, acfg.Hq, acfg.n_splits, acfg.d), **f32)
-    a_pl = torch.empty((acfg.B, acfg.Hq, acfg.n_splits), **f32)
-    a_o, a_lse = torch.empty((acfg.B, acfg.Hq, acfg.d), **f32), torch.empty((acfg.B, acfg.Hq), **f32)
+    def decode_only(i):
+        kv = caches[i % ncache]
+        return lambda: attn.attn_decode(qd, kv[0], kv[1], S, dcfg.scale, part_o=part_o,
+                                        part_lse=part_lse)
 
-    # forward of a prefill chunk against a cache (attn_fwd_kv), outside the step
-    ccfg = W.C7
-    xc = W.chunk_inputs(ccfg)
-    gc = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in xc.items()}
-    c_o = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d), **f32)
-    c_lse = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq), **f32)
+    def probe(i):
+        kv = caches[i % ncache]
+        return lambda: attn.attn_read_probe(kv, out=probe_out)
 
-    # the training step over rotated q and k (attn_fwd_rope / attn_bwd_rope), outside the step
-    q_rot, k_rot = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+    def train_op():
+        fns["fwd"]()
+        fns["bwd"]()
 
-    def fwd_rope():
-        attn.attn_fwd_rope(g["q"], g["k"], g["v"], True, cfg.scale, 10000.0, q_rot=q_rot, k_rot=k_rot,
-                           o=o, lse=lse)
-
-    def bwd_rope():
-        attn.attn_bwd_rope(q_rot, k_rot, g["v"], o, lse, g["dout"], True, cfg.scale, 10000.0, dq=dq,
-                           dk=dk, dv=dv, workspace=bwd_ws)
-
-    def fwd_chunk():
-        attn.attn_fwd_kv(gc["q"], gc["k"], gc["v"], True, ccfg.scale, o=c_o, lse=c_lse)
-
-    def decode_append(i):
-        kc, vc = a_caches[i % a_ncache]
-        return lambda: attn.attn_decode_append(ga["q"], ga["k_new"], ga["v_new"], kc, vc, a_lens,
-                                               acfg.n_splits, acfg.scale, part_o=a_po,
-                                               part_lse=a_pl, o=a_o, lse=a_lse)
-
-    train_op = [fwd, bwd]
-    for s in range(args.warmup):
-        for fn in train_op:
-            fn()
-        decode(s)()
-        if not args.eager:
-            decode_append(s)()
-            fwd_chunk()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    timer = eager_time_us if args.eager else graph_time_us
-    train_fns = [fn for _ in range(K) for fn in train_op]
-    dec_fns = [decode(s) for s in range(K)]
-    # the timed region: K steps = K training ops and K decode ops
-    train_us = timer(torch, train_fns, K)
-    dec_us = timer(torch, dec_fns, K)
-    step_us = train_us + dec_us
-    # the measurements beside the step (skipped in the eager counter-collection
-    # runs, whose per-kernel counters must describe the step's kernels alone)
-    extras = {"decode_append": None, "fwd_chunk": None, "fwd_bwd_rope": None}
-    if not args.eager:
-        app_us = timer(torch, [decode_append(s) for s in range(K)], K)
-        app_bytes = acfg.algorithmic_bytes()
-        app_gbs = app_bytes / (app_us * 1e-6) / 1e9
-        extras["decode_append"] = {"workload": acfg.name, "GB_per_s": round(app_gbs, 1),
-                                   "frac_hbm_peak": round(app_gbs / PEAK_HBM_GBS, 4),
-                                   "us_per_call": round(app_us, 3), "bytes": app_bytes,
-                                   "distinct_caches": a_ncache, "launches_per_call": 2,
-                                   "seq_lens": list(acfg.seq_lens),
-                                   # the caches rotate through HBM: compulsory bytes at its peak
-                                   "floor_us": round(app_bytes / (BD.PEAK_HBM / 1e6), 3),
-                                   "of_floor": round(app_bytes / (BD.PEAK_HBM / 1e6) / app_us, 4)}
-        rope_us = timer(torch, [f for _ in range(K) for f in (fwd_rope, bwd_rope)], K)
-        extras["fwd_bwd_rope"] = {"us_per_step": round(rope_us, 3),
-                                  "TFLOP_s": round((cfg.fwd_flop + cfg.bwd_flop) / (rope_us * 1e-6) / 1e12, 2),
-                                  "rotary_cost_us": round(rope_us - train_us, 3)}
-        chunk_us = timer(torch, [fwd_chunk] * K, K)
-        chunk_tflops = ccfg.fwd_flop / (chunk_us * 1e-6) / 1e12
-        cf = BD.fwd(ccfg.B, ccfg.Hq, ccfg.Hkv, ccfg.Nq, ccfg.Nk, ccfg.d, True,
-                    **BD.fwd_tile(ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d))
-        extras["fwd_chunk"] = {"workload": ccfg.name, "TFLOP_s": round(chunk_tflops, 2),
-                               "frac_bf16_peak": round(chunk_tflops / PEAK_BF16_TFLOPS, 4),
-                               "us_per_call": round(chunk_us, 3), "flop": ccfg.fwd_flop,
-                               "floor_us": cf["floor_us"], "of_floor": round(cf["floor_us"] / chunk_us, 4)}
-
-    pairs = cfg.pairs
+    # ---------------------------------------------------------------- the timed region
+    K, Wm = args.steps, args.warmup
+    if args.eager:
+        for s in range(Wm):
+            train_op()
+            decode(s)()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for s in range(K):
+            ev[s][0].record()
+            train_op()
+            ev[s][1].record()
+            decode(s)()
+            ev[s][2].record()
+        torch.cuda.synchronize()
+    else:
+        g_train = T.graph([train_op])
+        g_dec = [T.graph([decode(i)]) for i in range(ncache)]
+        for s in range(Wm):
+            g_train.replay()
+            g_dec[s % ncache].replay()
+        T.warm(g_train)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for s in range(K):
+            ev[s][0].record()
+            g_train.replay()
+            ev[s][1].record()
+            g_dec[s % ncache].replay()
+            ev[s][2].record()
+        torch.cuda.synchronize()
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    train_ts = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in ev)
+    dec_ts = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in ev)
+    train_us, dec_us = statistics.median(train_ts), statistics.median(dec_ts)
     train_flop = cfg.fwd_flop + cfg.bwd_flop
     value = train_flop / (train_us * 1e-6) / 1e12
     dec_bytes = dcfg.algorithmic_bytes()
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
-
-    flop = {"fwd": 4 * d * pairs,
-            "bwd_grads": 10 * d * pairs,    # the whole gradient stage
-            "bwd_dkdv": 8 * d * pairs,      # recomputed S, dP, dV, dK
-            "bwd_dq": 2 * d * pairs}        # dQ (its S and dP recompute is not credited)
-    kernels = {}
-    if not args.no_kernel_breakdown:
-        for name, fn in (("fwd", fwd), ("bwd_preprocess", pre), ("bwd_grads", grads),
-                         ("bwd_dkdv", dkdv), ("bwd_dq", dqk)):
-            kernels[name] = {"avg_us": round(timer(torch, [fn] * K, K), 3)}
-        kernels["bwd_grads"]["one_kernel"] = grads_one_kernel
-        kernels["decode_merged"] = {"avg_us": round(dec_us, 3)}
-        for n, f in flop.items():
-            t = kernels[n]["avg_us"] * 1e-6
-            kernels[n]["TFLOP_s"] = round(f / t / 1e12, 2)
-            kernels[n]["frac_bf16_peak"] = round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4)
-        pre_bytes = B * Hq * N * d * (2 if cfg.dtype == "bf16" else 4) + B * Hq * N * d * 4 + B * Hq * N * 4
-        kernels["bwd_preprocess"]["GB_s"] = round(pre_bytes / (kernels["bwd_preprocess"]["avg_us"] * 1e-6) / 1e9, 1)
-        kernels["decode_merged"]["GB_s"] = round(dec_gbs, 1)
-
-    # time floors from the tile sizes (bounds.py), next to each measured time
-    if kernels and cfg.dtype == "bf16":
-        ft = BD.fwd_tile(B, Hq, N, d)
-        hs = BD.head_split(B, Hq, Hkv, N)
-        kv = dict(BKV=64, SR=128, hs=hs)
-        floors = {
-            "fwd": (BD.fwd(B, Hq, Hkv, N, N, d, True, **ft), BD.best_fwd(B, Hq, Hkv, N, N, d)),
-            "bwd_preprocess": (BD.preprocess(B, Hq, Hkv, N, d, hs > 1), None),
-            "bwd_grads": (BD.bwd_grads(B, Hq, Hkv, N, N, d, True, BQ=128, BN=64, **kv),
-                          BD.best_bwd_grads(B, Hq, Hkv, N, N, d)),
-            "bwd_dkdv": (BD.bwd_dkdv(B, Hq, Hkv, N, N, d, True, **kv), BD.best_bwd_dkdv(B, Hq, Hkv, N, N, d)),
-            "bwd_dq": (BD.bwd_dq(B, Hq, Hkv, N, N, d, True, 128, 64), BD.best_bwd_dq(B, Hq, Hkv, N, N, d)),
-            "decode_merged": (BD.decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, dcfg.n_splits, resident=False),
-                              BD.best_decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, resident=False)),
-        }
-        for n, (fl, best) in floors.items():
-            k = kernels[n]
-            k["floor_us"] = fl["floor_us"]
-            k["floor_bound"] = max(fl["terms_us"], key=fl["terms_us"].get)
-            k["of_floor"] = round(fl["floor_us"] / k["avg_us"], 4)
-            k["tile"] = fl["tile"]
-            if best is not None:
-                k["best_tile"], k["best_floor_us"] = best["tile"], best["floor_us"]
-
-    traffic = load_traffic(cfg.name)
-    if traffic:
-        for n, t in traffic.items():
-            if n in kernels:
-                kernels[n]["hbm_bytes_measured"] = t["bytes"]
-
-    roof = None
-    if kernels:
-        # the kernels the training step launches: the gradient stage is one
-        # kernel (bwd_grads) or the dK/dV and dQ kernels
-        in_step = ["fwd", "bwd_preprocess", "decode_merged"] + (
-            ["bwd_grads"] if grads_one_kernel else ["bwd_dkdv", "bwd_dq"])
-        dom = max(in_step, key=lambda n: kernels[n]["avg_us"])
-        t = kernels[dom]["avg_us"]
-        if dom in flop:
-            ach = flop[dom] / (t * 1e-6) / 1e12
-            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
-                    "avg_launch_us": t}
-            for key in ("floor_us", "floor_bound", "of_floor", "tile", "best_tile", "best_floor_us"):
-                if key in kernels[dom]:
-                    roof[key] = kernels[dom][key]
-        else:
-            ach = kernels[dom]["GB_s"]
-            roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
-                    "avg_launch_us": t}
 
     result = {
         "metric": "attn fwd+bwd TFLOP/s & % bf16 MFMA peak; decode GB/s & % HBM peak",
@@ -474,8 +495,8 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_us / 1e3, 5),
+        "warmup": Wm,
+        "ms_per_step": round(total_ms / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -485,49 +506,283 @@ def main():
                    "causal": True, "decode_workload": dcfg.name},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_bwd_us": round(train_us, 3),
-        # the step's kernels run one after another: their floors add (the two
-        # gradient kernels, side by side at d = 128, share the CUs: one floor)
-        "fwd_bwd_floor_us": (round(sum(kernels[n]["floor_us"] for n in ("fwd", "bwd_preprocess", "bwd_grads")), 3)
-                             if "floor_us" in kernels.get("fwd", {}) else None),
+        "fwd_bwd_us_mean": round(sum(train_ts) / K, 3),
         "decode": {"GB_per_s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "us_per_call": round(dec_us, 3), "bytes": dec_bytes, "distinct_caches": ncache,
                    "launches_per_call": 2},
-        "decode_append": extras["decode_append"],
-        "fwd_chunk": extras["fwd_chunk"],
-        "fwd_bwd_rope": extras["fwd_bwd_rope"],
-        "kernels": kernels,
-        "roofline": roof,
-        "timing": ("eager launches between HIP events" if args.eager else
-                   "HIP graph replay of K back-to-back ops between HIP events"),
-        "cpu_baseline": None,
+        "timing": ("eager launches" if args.eager else "HIP graph replays") +
+                  "; per-op HIP events, median over the K steps",
     }
+    if args.eager:
+        print(json.dumps(result), flush=True)
+        return
+
+    # ---------------------------------------------------------------- per kernel
+    pairs = cfg.pairs
+    flop = {"fwd": 4 * d * pairs,
+            "bwd_grads": 10 * d * pairs,    # the whole gradient stage
+            "bwd_dkdv": 8 * d * pairs,      # recomputed S, dP, then dV, dK
+            "bwd_dq": 2 * d * pairs}        # dQ (its S and dP recompute is not credited)
+    dt_code = 1 if cfg.dtype == "bf16" else 0
+    grads_one_kernel = attn.attn_bwd_grads_plan(dt_code, B, Hq, Hkv, N, N, d, True, cfg.scale)[0]
+    kernels = {}
+    if not args.no_kernel_breakdown:
+        for name in ("fwd", "bwd_preprocess", "bwd_grads", "bwd_dkdv", "bwd_dq"):
+            r = T.op(fns[name])
+            kernels[name] = {"avg_us": r["median_us"], "iters": r["iters"],
+                             "launches_per_replay": r["ops_per_replay"]}
+        kernels["bwd_grads"]["one_kernel"] = grads_one_kernel
+        for n, fl in flop.items():
+            t = kernels[n]["avg_us"] * 1e-6
+            kernels[n]["TFLOP_s"] = round(fl / t / 1e12, 2)
+            kernels[n]["frac_bf16_peak"] = round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        esz = 2 if cfg.dtype == "bf16" else 4
+        pre_bytes = B * Hq * N * d * esz + B * Hq * N * d * 4 + B * Hq * N * 4
+        kernels["bwd_preprocess"]["GB_s"] = round(pre_bytes / (kernels["bwd_preprocess"]["avg_us"] * 1e-6) / 1e9, 1)
+        kernels["decode_merged"] = {"avg_us": round(dec_us, 3), "GB_s": round(dec_gbs, 1)}
+        if cfg.dtype == "bf16":
+            ft = BD.fwd_tile(B, Hq, N, d)
+            hs = BD.head_split(B, Hq, Hkv, N)
+            kv = dict(BKV=64, SR=128, hs=hs)
+            floors = {
+                "fwd": (BD.fwd(B, Hq, Hkv, N, N, d, True, **ft), BD.best_fwd(B, Hq, Hkv, N, N, d)),
+                "bwd_preprocess": (BD.preprocess(B, Hq, Hkv, N, d, hs > 1), None),
+                "bwd_grads": (BD.bwd_grads(B, Hq, Hkv, N, N, d, True, BQ=128, BN=64, **kv),
+                              BD.best_bwd_grads(B, Hq, Hkv, N, N, d)),
+                "bwd_dkdv": (BD.bwd_dkdv(B, Hq, Hkv, N, N, d, True, **kv), BD.best_bwd_dkdv(B, Hq, Hkv, N, N, d)),
+                "bwd_dq": (BD.bwd_dq(B, Hq, Hkv, N, N, d, True, 128, 64), BD.best_bwd_dq(B, Hq, Hkv, N, N, d)),
+                "decode_merged": (BD.decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, dcfg.n_splits, resident=False),
+                                  BD.best_decode(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.L, dcfg.d, resident=False)),
+            }
+            for n, (fl, best) in floors.items():
+                k = kernels[n]
+                k["floor_us"] = fl["floor_us"]
+                k["floor_bound"] = max(fl["terms_us"], key=fl["terms_us"].get)
+                k["of_floor"] = round(fl["floor_us"] / k["avg_us"], 4)
+                k["tile"] = fl["tile"]
+                if best is not None:
+                    k["best_tile"], k["best_floor_us"] = best["tile"], best["floor_us"]
+        traffic = load_traffic(cfg.name)
+        if traffic:
+            for n, t in traffic.items():
+                if n in kernels:
+                    kernels[n]["hbm_bytes_measured"] = t["bytes"]
+    else:
+        traffic = None
+    result["kernels"] = kernels
+
+    roof = None
+    if kernels:
+        # the kernels the training step launches: the gradient stage is one
+        # kernel (bwd_grads) or the dQ and dK/dV kernels; the d = 128 step's dQ
+        # kernel also computes the preprocess's row terms (timed as bwd_dq
+        # without them)
+        in_step = ["fwd", "decode_merged"] + (["bwd_preprocess", "bwd_grads"] if grads_one_kernel
+                                              else ["bwd_dkdv", "bwd_dq"])
+        dom = max(in_step, key=lambda n: kernels[n]["avg_us"])
+        t = kernels[dom]["avg_us"]
+        if dom in flop:
+            ach = flop[dom] / (t * 1e-6) / 1e12
+            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
+                    "avg_launch_us": t, "flop_per_launch": flop[dom]}
+            for key in ("floor_us", "floor_bound", "of_floor", "tile", "best_tile", "best_floor_us"):
+                if key in kernels[dom]:
+                    roof[key] = kernels[dom][key]
+        else:
+            ach = kernels[dom]["GB_s"]
+            roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": traffic[dom]["bytes"] if traffic and dom in traffic else None,
+                    "avg_launch_us": t}
+    result["roofline"] = roof
+
+    # ---------------------------------------------------------------- every config
+    configs = {}
+    if not args.no_configs:
+        for c in (W.C1, W.C2, W.C3_128, W.C3_512, W.C4):
+            if c.name == cfg.name:
+                cx, cf = x, fns
+            else:
+                cx, _, _, cf = train_setup(c)
+            row = {"shape": f"B{c.B} Hq{c.Hq} Hkv{c.Hkv} N{c.N} d{c.d} {c.dtype}"}
+            for name, ops, fl in (("fwd", [cf["fwd"]], c.fwd_flop), ("bwd", [cf["bwd"]], c.bwd_flop),
+                                  ("fwd_bwd", [cf["fwd"], cf["bwd"]], c.fwd_flop + c.bwd_flop)):
+                n = T.ops_for(lambda: [f() for f in ops])
+                r = T.median_us(ops * n, n)
+                row[f"{name}_us"] = r["median_us"]
+                if c.dtype == "bf16":
+                    tf = fl / (r["median_us"] * 1e-6) / 1e12
+                    row[f"{name}_TFLOP_s"] = round(tf, 2)
+                    row[f"{name}_frac_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+            row["iters_min"] = args.min_iters
+            configs[c.name] = row
+            if c.name != cfg.name:
+                del cf
+            torch.cuda.synchronize()
+        cold = T.median_us([decode(i) for i in range(ncache)], ncache)
+        warm = T.median_us([decode(0)] * ncache, ncache)
+        kern = T.median_us([decode_only(i) for i in range(ncache)], ncache)
+        floor = T.median_us([probe(i) for i in range(ncache)], ncache)
+        merge_only = T.op(lambda: attn.attn_lse_merge(part_o, part_lse, o=dec_o, lse=dec_lse))
+        rb = 2 * dcfg.B * dcfg.Hkv * dcfg.L * dcfg.d * 2
+        configs[dcfg.name] = {
+            "shape": f"q B{dcfg.B} Hq{dcfg.Hq} d{dcfg.d}; caches Hkv{dcfg.Hkv} L{dcfg.L} bf16; "
+                     f"{S} splits",
+            "decode_merged_us": cold["median_us"],
+            "GB_per_s": round(dec_bytes / (cold["median_us"] * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(dec_bytes / (cold["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "decode_kernel_us": kern["median_us"],
+            "lse_merge_us": merge_only["median_us"],
+            "warm_cache_decode_merged_us (one cache, L2/LLC-resident)": warm["median_us"],
+            "read_floor_us": floor["median_us"],
+            "read_floor_GB_per_s": round(rb / (floor["median_us"] * 1e-6) / 1e9, 1),
+            "of_read_floor": round(floor["median_us"] / cold["median_us"], 4),
+            "distinct_caches": ncache,
+        }
+    result["configs"] = configs
+
+    # ---------------------------------------------------------------- beside the step
+    extras = {"fwd_chunk": None, "decode_append": None, "fwd_bwd_rope": None}
+    if not args.no_extras:
+        acfg = W.C6
+        xa = W.decode_append_inputs(acfg)
+        ga = {n: torch.from_numpy(xa[n]).to(dev).to(ddt) for n in ("q", "k_new", "v_new")}
+        a_lens = torch.from_numpy(xa["seq_lens"]).to(dev)
+        ka0 = torch.from_numpy(xa["k_cache"]).to(dev).to(ddt)
+        va0 = torch.from_numpy(xa["v_cache"]).to(dev).to(ddt)
+        a_n = max(1, args.append_caches)
+        a_caches = [(ka0.clone(), va0.clone()) for _ in range(a_n)]
+        del ka0, va0
+        a_po = torch.empty((acfg.B, acfg.Hq, acfg.n_splits, acfg.d), **f32)
+        a_pl = torch.empty((acfg.B, acfg.Hq, acfg.n_splits), **f32)
+        a_o, a_lse = torch.empty((acfg.B, acfg.Hq, acfg.d), **f32), torch.empty((acfg.B, acfg.Hq), **f32)
+
+        def decode_append(i):
+            kc, vc = a_caches[i % a_n]
+            return lambda: attn.attn_decode_append(ga["q"], ga["k_new"], ga["v_new"], kc, vc, a_lens,
+                                                   acfg.n_splits, acfg.scale, part_o=a_po,
+                                                   part_lse=a_pl, o=a_o, lse=a_lse)
+        app_us = T.median_us([decode_append(i) for i in range(8 * a_n)], 8 * a_n)["median_us"]
+        app_bytes = acfg.algorithmic_bytes()
+        app_gbs = app_bytes / (app_us * 1e-6) / 1e9
+        extras["decode_append"] = {"workload": acfg.name, "GB_per_s": round(app_gbs, 1),
+                                   "frac_hbm_peak": round(app_gbs / PEAK_HBM_GBS, 4),
+                                   "us_per_call": app_us, "bytes": app_bytes,
+                                   "distinct_caches": a_n, "launches_per_call": 2,
+                                   "seq_lens": list(acfg.seq_lens)}
+
+        ccfg = W.C7
+        xc = W.chunk_inputs(ccfg)
+        tdt = torch.bfloat16 if ccfg.dtype == "bf16" else torch.float32
+        gc = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in xc.items()}
+        c_o = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d), **f32)
+        c_lse = torch.empty((ccfg.B, ccfg.Hq, ccfg.Nq), **f32)
+        chunk_us = T.op(lambda: attn.attn_fwd_kv(gc["q"], gc["k"], gc["v"], True, ccfg.scale, o=c_o,
+                                                 lse=c_lse))["median_us"]
+        chunk_tf = ccfg.fwd_flop / (chunk_us * 1e-6) / 1e12
+        cfl = BD.fwd(ccfg.B, ccfg.Hq, ccfg.Hkv, ccfg.Nq, ccfg.Nk, ccfg.d, True,
+                     **BD.fwd_tile(ccfg.B, ccfg.Hq, ccfg.Nq, ccfg.d))
+        extras["fwd_chunk"] = {"workload": ccfg.name, "TFLOP_s": round(chunk_tf, 2),
+                               "frac_bf16_peak": round(chunk_tf / PEAK_BF16_TFLOPS, 4),
+                               "us_per_call": chunk_us, "flop": ccfg.fwd_flop,
+                               "floor_us": cfl["floor_us"], "of_floor": round(cfl["floor_us"] / chunk_us, 4)}
+
+        q_rot, k_rot = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+
+        def rope_step():
+            attn.attn_fwd_rope(g["q"], g["k"], g["v"], True, cfg.scale, 10000.0, q_rot=q_rot,
+                               k_rot=k_rot, o=tt["o"], lse=tt["lse"])
+            attn.attn_bwd_rope(q_rot, k_rot, g["v"], tt["o"], tt["lse"], g["dout"], True, cfg.scale,
+                               10000.0, dq=tt["dq"], dk=tt["dk"], dv=tt["dv"], workspace=tt["ws"])
+        rope_us = T.op(rope_step)["median_us"]
+        extras["fwd_bwd_rope"] = {"us_per_step": rope_us,
+                                  "TFLOP_s": round(train_flop / (rope_us * 1e-6) / 1e12, 2),
+                                  "rotary_cost_us": round(rope_us - train_us, 3)}
+    result.update(extras)
+
+    # ---------------------------------------------------------------- the oracle
+    result["cpu_baseline"] = None
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
+        base, c4_oracle = cpu_baseline(cfg, x, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        if configs:
+            oracle_per_config(configs, c4_oracle, cfg)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cfg, x, budget_s: float) -> dict:
-    """The f64 oracle on (batch, key/value-group) slices of the same workload,
-    fwd + bwd, until the time budget is used; reported in the metric's unit."""
+def cpu_baseline(cfg, x, budget_s: float):
+    """The f64 oracle on the headline workload, fwd then bwd, one (batch,
+    key/value group) slice at a time until the budget is spent (at least one
+    slice); reported in the metric's unit."""
     import oracle
     G = cfg.Hq // cfg.Hkv
     groups = [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
-    done, flop = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < 64 * len(groups):
-        b, g = groups[done % len(groups)]
+    done, t_fwd, t_all = 0, 0.0, 0.0
+    while done < len(groups) and (done == 0 or t_all < budget_s):
+        b, g = groups[done]
         hs = slice(g * G, (g + 1) * G)
         q, k, v, do = (x["q"][b:b + 1, hs], x["k"][b:b + 1, g:g + 1], x["v"][b:b + 1, g:g + 1],
                        x["dout"][b:b + 1, hs])
+        t0 = time.perf_counter()
         oracle.attn_fwd(q, k, v, True, cfg.scale)
+        t1 = time.perf_counter()
         oracle.attn_bwd(q, k, v, do, True, cfg.scale)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_all += t2 - t0
         done += 1
-        flop += G * cfg.N * (cfg.N + 1) // 2 * 14 * cfg.d
-    el = time.perf_counter() - t0
-    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{done} (batch, kv-group) slices of {cfg.name} ({len(groups)} per pass), "
-                      f"fwd+bwd in f64, {el:.1f} s"}
+    frac = done / len(groups)
+    flop = (cfg.fwd_flop + cfg.bwd_flop) * frac
+    base = {"value": round(flop / t_all / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch, kv-group) slices of {cfg.name} (each a kv "
+                      f"head and its {G} query heads), fwd then bwd in f64, {t_all:.1f} s"}
+    full = {"fwd_s": round(t_fwd / frac, 3), "fwd_bwd_s": round(t_all / frac, 3),
+            "measured_fraction": round(frac, 4)}
+    return base, full
+
+
+def oracle_per_config(configs, headline_oracle, hcfg):
+    """Wall time of the oracle per config: best of 3 for the small ones (and the
+    decode), the headline's one run (extrapolated from the slices it ran)."""
+    import oracle
+    from attention_causal_gqa_flash_amd import workloads as W
+    for c in (W.C1, W.C2, W.C3_128, W.C3_512, W.C4):
+        if c.name not in configs:
+            continue
+        if c.name == hcfg.name:
+            configs[c.name]["oracle_s"] = dict(headline_oracle, runs=1)
+            continue
+        if c.name == W.C4.name:
+            continue      # one run of the 4096-token workload only as the headline
+        xx = W.train_inputs(c)
+        bf, bb = float("inf"), float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.attn_fwd(xx["q"], xx["k"], xx["v"], True, c.scale)
+            t1 = time.perf_counter()
+            oracle.attn_bwd(xx["q"], xx["k"], xx["v"], xx["dout"], True, c.scale)
+            t2 = time.perf_counter()
+            bf, bb = min(bf, t1 - t0), min(bb, t2 - t0)
+        configs[c.name]["oracle_s"] = {"fwd_s": round(bf, 4), "fwd_bwd_s": round(bb, 4), "runs": 3}
+        configs[c.name]["gpu_vs_oracle_fwd_bwd"] = round(bb / (configs[c.name]["fwd_bwd_us"] * 1e-6), 1)
+    dc = W.C5
+    if dc.name in configs:
+        xd = W.decode_inputs(dc)
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            po, pl = oracle.attn_decode(xd["q"], xd["k_cache"], xd["v_cache"], dc.scale, dc.n_splits)
+            oracle.lse_merge(po, pl)
+            best = min(best, time.perf_counter() - t0)
+        configs[dc.name]["oracle_s"] = {"decode_s": round(best, 4), "runs": 3}
+    if hcfg.name in configs and "fwd_bwd_us" in configs[hcfg.name]:
+        configs[hcfg.name]["gpu_vs_oracle_fwd_bwd"] = round(
+            headline_oracle["fwd_bwd_s"] / (configs[hcfg.name]["fwd_bwd_us"] * 1e-6), 1)
+    configs["oracle_cores"] = oracle.num_threads()
+    configs["oracle_cpu_model"] = cpu_model()
 
 
 if __name__ == "__main__":

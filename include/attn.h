@@ -19,9 +19,9 @@
  * Conventions common to every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers, owned by the caller.  The library
- *    allocates no device memory and keeps no data between calls.  Its only
- *    state is, per device, one auxiliary stream and two events that attn_bwd
- *    creates on first use (see attn_bwd).
+ *    allocates no device memory, creates no streams or events and keeps no
+ *    state between calls: every call is re-entrant and may be captured into a
+ *    HIP graph (including the first call of a process).
  *  - Layouts are contiguous row-major with the head dimension fastest:
  *        q, dout, o, dq      [B][Hq][N][d]
  *        k, v, dk, dv        [B][Hkv][N][d]
@@ -122,17 +122,10 @@ size_t attn_bwd_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int N, in
  *   then differ from run to run in the last bits.
  *   workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes,
  *   owned by the caller; its contents on entry do not matter.
- *   Streams: for bf16 inputs at d = 128 (f32 o) the dq kernel computes delta
- *   itself (into the workspace) and the dk/dv kernel follows it, both on
- *   `stream`.  Otherwise the preprocess runs, then the gradients as described
- *   at attn_bwd_grads; when they are two kernels, the dq kernel runs on an
- *   auxiliary stream of the current device, forked from and joined back into
- *   `stream` with events, concurrently with the dk/dv kernel; to the caller
- *   the call behaves as if all its work were on `stream` (a graph capture of
- *   `stream` captures both branches).  The auxiliary stream and events are
- *   created on the device's first such call; if that first call is made while
- *   `stream` is being captured, or they cannot be created, the kernels run
- *   one after the other on `stream`.
+ *   Launches, all on `stream`: for bf16 inputs at d = 128 (f32 o) the dq
+ *   kernel computes delta itself (into the workspace) and the dk/dv kernel
+ *   follows it.  Otherwise the preprocess runs, then the gradients as
+ *   described at attn_bwd_grads.
  */
 attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      const void *q, const void *k, const void *v,
@@ -262,9 +255,8 @@ attn_status attn_bwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
  *                        grid holds both the dk/dv and the dq work items (after
  *                        a zero-fill launch of dk and dv when they are
  *                        accumulated with atomics), as attn_bwd runs it after
- *                        its preprocess; otherwise the dk/dv and dq kernels
- *                        side by side on two streams (see the stream note at
- *                        attn_bwd).
+ *                        its preprocess (see attn_bwd_grads_plan); otherwise
+ *                        the dq kernel, then the dk/dv kernel, on `stream`.
  * dkdv and dq do not depend on each other; all need the preprocess first.
  */
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d,
@@ -283,12 +275,17 @@ attn_status attn_bwd_grads(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, 
                            float *dq, float *dk, float *dv, void *stream);
 
 /*
- * attn_bwd_grads_single_launch -- 1 when attn_bwd_grads (and the gradient part
- *   of attn_bwd) runs dq, dk and dv as one kernel for this dtype, sequence
- *   length, head dim and scale, else 0 (also 0 for arguments attn_bwd would
- *   refuse).  No device work.
+ * attn_bwd_grads_plan -- 1 when attn_bwd_grads (and the gradient part of
+ *   attn_bwd / attn_bwd_kv) runs dq, dk and dv as ONE kernel for this shape,
+ *   else 0 (also 0 for arguments attn_bwd_kv would refuse).  The one kernel
+ *   orders its blocks by a host-side plan of at most 48 block groups, passed
+ *   as a kernel argument; a shape whose plan cannot be made to fit (the group
+ *   caps shrink until it does) runs the two gradient kernels instead.  When
+ *   groups / blocks are non-null they receive the plan's group count and grid
+ *   size (0 when the result is 0).  Nq == Nk for attn_bwd.  No device work.
  */
-int attn_bwd_grads_single_launch(attn_dtype dt, int N, int d, float scale);
+int attn_bwd_grads_plan(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                        float scale, int *groups, int *blocks);
 
 /*
  * attn_decode -- split-KV attention of one new query token per (b, query head)
@@ -370,6 +367,17 @@ attn_status attn_decode_append(attn_dtype dt, int B, int Hq, int Hkv, int L_cap,
                                const void *v_new, void *k_cache, void *v_cache,
                                const int *seq_lens, float *part_o, float *part_lse, float *o,
                                float *lse, void *stream);
+
+/*
+ * attn_read_probe -- a reference, not part of attention: reads `bytes` bytes at
+ *   src once (16-byte loads, many in flight on every compute unit) and writes
+ *   nothing but, practically never, a sentinel word to *out.  A decode step is
+ *   bound by reading the cache once (RustingBrain docs, "Generating text"), so
+ *   the time of this call over the same bytes is the decode kernels' measured
+ *   floor.  src: device, 16-byte aligned; bytes: a positive multiple of 16,
+ *   at most 2^40; out: device, 4-byte aligned.  One launch on `stream`.
+ */
+attn_status attn_read_probe(const void *src, size_t bytes, unsigned *out, void *stream);
 
 /* Human-readable name of a status code (a static string). */
 const char *attn_status_str(attn_status s);

@@ -42,7 +42,7 @@ def test_header_declares_the_boundary():
                      "attn_rope", "attn_fwd_rope", "attn_bwd_rope", "attn_fwd_ex", "attn_bwd_ex",
                      "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
-                     "attn_bwd_grads_single_launch", "attn_decode", "attn_decode_append",
+                     "attn_bwd_grads_plan", "attn_decode", "attn_decode_append",
                      "attn_lse_merge",
                      "attn_status_str", "attn_abi_version"):
         assert required in names
@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert attn.attn_abi_version() == 2
+    assert attn.attn_abi_version() == 3
     assert attn.attn_status_str(OK) == "ok"
     assert "invalid" in attn.attn_status_str(INVALID)
     assert "unsupported" in attn.attn_status_str(UNSUPPORTED)
@@ -293,15 +293,44 @@ def test_decode_append_refusals(L):
     assert L.attn_decode_append(1, 2, 8, 2, 64, 128, 0.088, 4, *([P] * 6), P, P, P, MIS, NUL) == INVALID
 
 
-def test_bwd_grads_single_launch_query(L):
-    """One launch exactly for the bf16 matrix-core path at d = 64; no device work."""
-    assert L.attn_bwd_grads_single_launch(1, 1024, 64, 0.125) == 1
-    assert L.attn_bwd_grads_single_launch(1, 4096, 128, 0.088) == 0
-    assert L.attn_bwd_grads_single_launch(0, 1024, 64, 0.125) == 0     # f32: row-wise kernels
-    assert L.attn_bwd_grads_single_launch(1, 1024, 64, 0.0) == 0       # scale 0: row-wise
-    assert L.attn_bwd_grads_single_launch(1, 1024, 40, 0.125) == 0     # unsupported head dim
-    assert L.attn_bwd_grads_single_launch(1, 0, 64, 0.125) == 0
-    assert L.attn_bwd_grads_single_launch(1, 1024, 64, float("nan")) == 0
+def _plan(L, dt, B, Hq, Hkv, Nq, Nk, d, scale, causal=1):
+    g, b = ctypes.c_int(-1), ctypes.c_int(-1)
+    one = L.attn_bwd_grads_plan(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, ctypes.byref(g),
+                                ctypes.byref(b))
+    return one, g.value, b.value
+
+
+def test_bwd_grads_plan_query(L):
+    """Whether the gradient stage is one kernel (host-side answer, no device work)."""
+    assert _plan(L, 1, 4, 12, 4, 1024, 1024, 64, 0.125)[0] == 1
+    assert _plan(L, 1, 1, 32, 8, 4096, 4096, 128, 0.088)[0] == 0     # d = 128: two kernels
+    assert _plan(L, 0, 4, 12, 4, 1024, 1024, 64, 0.125)[0] == 0      # f32: row-wise kernels
+    assert _plan(L, 1, 4, 12, 4, 1024, 1024, 64, 0.0)[0] == 0        # scale 0: row-wise
+    assert _plan(L, 1, 4, 12, 4, 1024, 1024, 40, 0.125) == (0, 0, 0)  # unsupported head dim
+    assert _plan(L, 1, 4, 12, 4, 0, 0, 64, 0.125) == (0, 0, 0)
+    assert _plan(L, 1, 4, 12, 4, 1024, 1000, 64, 0.125) == (0, 0, 0)  # Nk < Nq
+    assert _plan(L, 1, 4, 12, 4, 1024, 1024, 64, float("nan")) == (0, 0, 0)
+
+
+# The one-launch plan is a kernel argument of at most 48 block groups.  The
+# dK/dV side splits a group wherever the key tiles' head split changes, so
+# before the caps shrank, cross-length shapes such as 12/1 heads at Nq = 3008
+# against Nk = 3072 planned 49 groups and wrote past the plan's arrays.
+PLAN_SHAPES = [(1, 12, 1, nq, nk) for nk in (3072, 6016, 9024) for nq in (nk - 64, nk - 1, nk - 500)] + \
+    [(B, Hq, Hkv, nq, nk) for B in (1, 2, 4) for Hq, Hkv in ((12, 1), (12, 4), (24, 2), (60, 1), (8, 8))
+     for nk in (256, 1000, 2048, 4097) for nq in (1, nk // 3, nk - 7, nk)]
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_bwd_grads_plan_fits(L, causal):
+    for B, Hq, Hkv, nq, nk in PLAN_SHAPES:
+        one, groups, blocks = _plan(L, 1, B, Hq, Hkv, nq, nk, 64, 0.125, causal)
+        assert one == 1, (B, Hq, Hkv, nq, nk)
+        assert 1 <= groups <= 48, (B, Hq, Hkv, nq, nk, groups)
+        # every dK/dV key tile and dQ query tile of every head is one block at least
+        nkt, nqt = (nk + 63) // 64, (nq + 127) // 128
+        assert blocks >= nkt * B * Hkv + nqt * B * Hq, (B, Hq, Hkv, nq, nk, blocks)
+        assert blocks % 8 == 0
 
 
 def test_no_unexpected_exports(L):

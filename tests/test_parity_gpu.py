@@ -2,8 +2,8 @@
 
 Tolerances (max abs = max over every element of |gpu - oracle|; relative
 Frobenius = ||gpu - oracle||_F / ||oracle||_F over the whole tensor):
-  f32 inputs : every output (o, lse, dq, dk, dv) max abs <= 1e-5 on the tiny
-               f32 workload; on the other f32 shapes 1e-5 * max(1, max|oracle|);
+  f32 inputs : every output (o, lse, dq, dk, dv) max abs <= 1e-5, on every
+               shape;
   bf16 inputs: o max abs <= 1e-2, lse max abs <= 1e-3, dq/dk/dv relative
                Frobenius <= 2e-2.
 Both sides see the same inputs: float32 draws rounded to bf16 where the
@@ -41,14 +41,14 @@ def _relF(got, ref):
     return d / n if n > 0 else d
 
 
-def _check(got, ref, dtype, tiny_f32=False, label=""):
+def _check(got, ref, dtype, label=""):
     o, lse, dq, dk, dv = got
     ro, rl, rdq, rdk, rdv = ref
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), label
     if dtype == "f32":
         for name, a, b in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rdq), ("dk", dk, rdk),
                            ("dv", dv, rdv)):
-            tol = 1e-5 if tiny_f32 else 1e-5 * max(1.0, float(np.abs(b).max()))
+            tol = 1e-5
             err = float(np.abs(a - b).max())
             assert err <= tol, f"{label} {name}: max abs {err:.3e} > {tol:.1e}"
     else:
@@ -77,33 +77,33 @@ def test_workload_full(cfg):
     x = W.train_inputs(cfg)
     got = _gpu_fwd_bwd(x, cfg.dtype, True, cfg.scale)
     ref = _oracle_fwd_bwd(x, True, cfg.scale)
-    _check(got, ref, cfg.dtype, tiny_f32=(cfg is W.C1), label=cfg.name)
+    _check(got, ref, cfg.dtype, label=cfg.name)
 
 
-def test_long_context_sampled_groups():
-    """N = 4096, d = 128, 32/8 heads: the whole problem on the GPU, the oracle on two
-    grouped-query groups (a key/value head and its 4 query heads), plus
-    properties that hold over the whole output."""
+def test_long_context_all_groups():
+    """N = 4096, d = 128, 32/8 heads: the whole problem on the GPU and in the oracle,
+    compared element by element over every output of every grouped-query group (a
+    key/value head and its 4 query heads; the oracle runs one group at a time)."""
     cfg = W.C4
-    print(f"\n[case] {cfg.name} sampled groups 0 and 7", flush=True)
+    print(f"\n[case] {cfg.name} all {cfg.Hkv} groups", flush=True)
     x = W.train_inputs(cfg)
     o, lse, dq, dk, dv = _gpu_fwd_bwd(x, cfg.dtype, True, cfg.scale)
     G = cfg.Hq // cfg.Hkv
-    for g in (0, cfg.Hkv - 1):
+    parts = {n: [] for n in ("o", "lse", "dq", "dk", "dv")}
+    for g in range(cfg.Hkv):
         hs = slice(g * G, (g + 1) * G)
         xs = {"q": x["q"][:, hs], "k": x["k"][:, g:g + 1], "v": x["v"][:, g:g + 1],
               "dout": x["dout"][:, hs]}
         ref = _oracle_fwd_bwd(xs, True, cfg.scale)
         got = (o[:, hs], lse[:, hs], dq[:, hs], dk[:, g:g + 1], dv[:, g:g + 1])
         _check(got, ref, cfg.dtype, label=f"{cfg.name} group {g}")
-    # Whole-output properties.  Exactly, sum_j dk_j = 0 (key-shift invariance)
-    # and sum_j dv_j = the sum of dout over the group's heads and rows.  An error
-    # E with ||E||_F <= 2e-2 ||dk||_F moves a sum over N rows by at most
-    # sqrt(N) ||E||_F, which bounds both checks.
-    bound = math.sqrt(cfg.N) * 2e-2
-    assert np.linalg.norm(dk.sum(axis=2)) <= bound * np.linalg.norm(dk)
-    dsum = x["dout"].astype(np.float64).reshape(cfg.B, cfg.Hkv, G, cfg.N, cfg.d).sum(axis=(2, 3))
-    assert np.linalg.norm(dv.sum(axis=2) - dsum) <= bound * np.linalg.norm(dv)
+        for n, a in zip(parts, ref):
+            parts[n].append(a)
+        print(f"  group {g} ok", flush=True)
+    # and over the whole tensors at once (the per-group relative Frobenius errors
+    # bound this one, but it is the tolerance's own definition)
+    ref = [np.concatenate(parts[n], axis=1) for n in parts]
+    _check((o, lse, dq, dk, dv), ref, cfg.dtype, label=f"{cfg.name} whole")
 
 
 def test_decode_workload():
@@ -240,8 +240,7 @@ def test_bwd_dlse(B, Hq, Hkv, N, d, causal, dtype):
     ro, rl = oracle.attn_fwd(x["q"], x["k"], x["v"], causal, scale)
     rdq, rdk, rdv = oracle.attn_bwd_dlse(x["q"], x["k"], x["v"], x["dout"], dl.astype(np.float64),
                                          causal, scale)
-    _check(got, (ro, rl, rdq, rdk, rdv), dtype, tiny_f32=(dtype == "f32"),
-           label=f"dlse N{N} d{d}")
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"dlse N{N} d{d}")
 
 
 # ---------------------------------------------------------------------------
@@ -294,6 +293,10 @@ BWD_KV = [
     (1, 4, 1, 512, 4096, 128, True, "bf16", False),   # a 512-token chunk at the end of 4k keys
     (1, 2, 1, 20, 50, 16, True, "f32", True),         # generic kernels
     (1, 4, 2, 37, 130, 32, False, "f32", False),
+    # 12 query heads on one kv head at 3008 queries against 3072 keys: the
+    # one-launch plan's dK/dV side splits its level groups where the head
+    # split changes, which once planned 49 groups for a 48-group argument
+    (1, 12, 1, 3008, 3072, 64, True, "bf16", False),
 ]
 
 
@@ -322,8 +325,7 @@ def test_bwd_kv(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
     else:
         rdq, rdk, rdv = oracle.attn_bwd_dlse(q, x["k"], x["v"], do, dl.astype(np.float64), causal,
                                              scale)
-    _check(got, (ro, rl, rdq, rdk, rdv), dtype, tiny_f32=(dtype == "f32" and Nk <= 64),
-           label=f"bwd_kv Nq{Nq} Nk{Nk} d{d}")
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"bwd_kv Nq{Nq} Nk{Nk} d{d}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -653,10 +655,9 @@ def test_graph_replay_matches_eager(mode, d):
     """The whole path captured in a HIP graph: every replay equals the eager run.
     The backward is the preprocess then the dK/dV and dQ stages ("stages"),
     attn_bwd_grads ("grads") or attn_bwd; at d = 128 attn_bwd_grads runs the dQ
-    kernel on the library's auxiliary stream (a fork/join inside the capture)
-    and attn_bwd runs the dQ kernel that computes the row terms, then the dK/dV
-    kernel; at d = 64 both are one launch (attn_bwd_grads after a zero-fill
-    launch of dk and dv)."""
+    kernel then the dK/dV kernel, and attn_bwd runs the dQ kernel that computes
+    the row terms, then the dK/dV kernel; at d = 64 both are one launch
+    (attn_bwd_grads after a zero-fill launch of dk and dv)."""
     cfg = W.TrainConfig("graph", "bf16", 1, 8, 2, 320, d, seed=11)
     x = W.train_inputs(cfg)
     g = {n: _to_dev(a, "bf16") for n, a in x.items()}
@@ -715,3 +716,58 @@ def test_graph_replay_matches_eager(mode, d):
                     f"replay {rep} differs from the eager run"
             else:
                 assert torch.equal(a, e), f"replay {rep} differs from the eager run"
+
+
+_FRESH_CAPTURE = r"""
+import sys
+import numpy as np
+import torch
+sys.path.insert(0, sys.argv[1])
+import attention_causal_gqa_flash_amd as attn
+from attention_causal_gqa_flash_amd import workloads as W
+x = W.random_train(1, 8, 2, 320, 128, seed=31, dout_scale=0.1)
+g = {n: torch.from_numpy(a).cuda().to(torch.bfloat16) for n, a in x.items()}
+f32 = dict(device="cuda", dtype=torch.float32)
+lse = torch.from_numpy(np.random.default_rng(1).standard_normal((1, 8, 320)).astype(np.float32) + 6).cuda()
+delta = torch.from_numpy(np.random.default_rng(2).standard_normal((1, 8, 320)).astype(np.float32) * 0.1).cuda()
+outs = [torch.empty((1, 8, 320, 128), **f32), torch.empty((1, 2, 320, 128), **f32),
+        torch.empty((1, 2, 320, 128), **f32)]
+def call():
+    attn.attn_bwd_grads(g["q"], g["k"], g["v"], lse, g["dout"], delta, True, 0.088,
+                        dq=outs[0], dk=outs[1], dv=outs[2])
+torch.cuda.synchronize()
+s = torch.cuda.Stream()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.stream(s):
+    with torch.cuda.graph(graph, stream=s):
+        call()                  # the library's first call in this process
+for t in outs:
+    t.fill_(float("nan"))
+torch.cuda.synchronize()
+graph.replay()
+torch.cuda.synchronize()
+replayed = [t.clone() for t in outs]
+call()
+torch.cuda.synchronize()
+# dq is bitwise deterministic; on this small grid dk and dv sum the query heads
+# of a group with f32 atomics (last-bit differences between runs)
+assert all(torch.isfinite(a).all() for a in replayed), "replay left non-finite values"
+assert torch.equal(replayed[0], outs[0]), "dq of the replay differs from the eager call"
+for a, e in zip(replayed[1:], outs[1:]):
+    assert torch.allclose(a, e, rtol=0, atol=1e-5 * float(e.abs().max())), "dk/dv of the replay differ"
+print("fresh-process capture ok", flush=True)
+"""
+
+
+def test_capture_as_first_call_in_fresh_process():
+    """attn_bwd_grads at d = 128 captured into a graph as the library's very first call
+    in a process: the library creates nothing lazily (no streams, events or other
+    state), so the capture holds all of its work and the replay equals an eager call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("\n[case] fresh-process capture of attn_bwd_grads d=128", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FRESH_CAPTURE, root], capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0 and "fresh-process capture ok" in r.stdout, r.stdout + r.stderr
