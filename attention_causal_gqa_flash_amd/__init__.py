@@ -17,7 +17,7 @@ __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preproc
            "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
            "attn_fwd_ex", "attn_bwd_ex",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
-           "attn_decode_merged", "attn_read_probe",
+           "attn_decode_merged", "attn_read_probe", "attn_bwd_noalloc",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
            "ATTN_F32", "ATTN_BF16"]
 
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [i, i, i, i, i, i, i, f] + [p] * 9 + [p, sz, p]
     L.attn_bwd.restype = i
+    L.attn_bwd_noalloc.argtypes = [i, i, i, i, i, i, i, f] + [p] * 9 + [p]
+    L.attn_bwd_noalloc.restype = i
     L.attn_bwd_preprocess.argtypes = [i, i, i, i, i, p, p, p, p]
     L.attn_bwd_preprocess.restype = i
     L.attn_bwd_dkdv.argtypes = [i, i, i, i, i, i, i, f] + [p] * 9
@@ -275,6 +277,26 @@ def _bwd_call(fn, q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv, worksp
             workspace.numel() * workspace.element_size(), _stream(stream))
     rc = getattr(lib(), fn)(*head, *((dlse_p,) if fn != "attn_bwd" else ()), *tail)
     _check(fn, rc)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+                     dq=None, dk=None, dv=None, stream=None):
+    """attn_bwd without a workspace: the row terms live in the library's own device array
+    (B*Hq*N <= 2^20; calls that overlap on one device race).  Pass dq, dk, dv to keep the
+    call free of allocations."""
+    torch = _torch()
+    B, Hq, Hkv, N, _, d = _qkv(q, k, v, square=True)
+    _expect(dout, (B, Hq, N, d), q.dtype, "dout", q)
+    _expect(o, (B, Hq, N, d), torch.float32, "o (the float32 output of the forward)", q)
+    _expect(lse, (B, Hq, N), torch.float32, "lse", q)
+    dq = _out(dq, (B, Hq, N, d), torch.float32, "dq", q, stream)
+    dk = _out(dk, (B, Hkv, N, d), torch.float32, "dk", q, stream)
+    dv = _out(dv, (B, Hkv, N, d), torch.float32, "dv", q, stream)
+    rc = lib().attn_bwd_noalloc(_dtype_code(q), B, Hq, Hkv, N, d, int(bool(causal)),
+                                _scale(scale, d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream))
+    _check("attn_bwd_noalloc", rc)
     return dq, dk, dv
 
 

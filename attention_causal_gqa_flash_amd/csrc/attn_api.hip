@@ -13,6 +13,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 namespace {
 
 using attn::kBF16;
@@ -187,6 +189,31 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
                             dq, dk, dv, hs, st, rope_lb);
 }
 
+// The device array behind attn_bwd_noalloc: scratch for the backward's row
+// terms D_i (one f32 per query row), for callers that cannot allocate.  Each
+// device holds its own copy for the life of the process.  In host code the
+// name is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, resolved once per device (with that device current)
+// and kept in scratch_addr.
+constexpr size_t kScratchBytes = (size_t)4 << 20;   // D for up to 2^20 query rows
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_addr[kMaxDevices];
+
+// The current device's address of `scratch`, or null when it cannot be had.
+// Concurrent first calls may both resolve it; they store the same address.
+void *scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p != nullptr) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +356,20 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
 {
     return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, nullptr, dq,
                      dk, dv, workspace, ws_bytes, stream);
+}
+
+attn_status attn_bwd_noalloc(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                             float scale, const void *q, const void *k, const void *v,
+                             const float *o, const float *lse, const void *dout, float *dq,
+                             float *dk, float *dv, void *stream)
+{
+    attn_status s = check_common(dt, B, Hq, Hkv, N, d, scale);
+    if (s != ATTN_OK) return s;
+    if (workspace_bytes(B, Hq, N) > kScratchBytes) return ATTN_ERR_WORKSPACE;
+    void *ws = scratch_ptr();
+    if (ws == nullptr) return ATTN_ERR_HIP;
+    return bwd_whole(dt, B, Hq, Hkv, N, N, d, causal, scale, q, k, v, o, lse, dout, nullptr, dq,
+                     dk, dv, ws, kScratchBytes, stream);
 }
 
 attn_status attn_bwd_preprocess(attn_dtype dt, int B, int Hq, int N, int d, const float *o,

@@ -20,8 +20,9 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers, owned by the caller.  The library
  *    allocates no device memory, creates no streams or events and keeps no
- *    state between calls: every call is re-entrant and may be captured into a
- *    HIP graph (including the first call of a process).
+ *    state between calls (save the device address of attn_bwd_noalloc's
+ *    array, resolved once per device): every call is re-entrant and may be
+ *    captured into a HIP graph (including the first call of a process).
  *  - Layouts are contiguous row-major with the head dimension fastest:
  *        q, dout, o, dq      [B][Hq][N][d]
  *        k, v, dk, dv        [B][Hkv][N][d]
@@ -132,6 +133,26 @@ attn_status attn_bwd(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int ca
                      const float *o, const float *lse, const void *dout,
                      float *dq, float *dk, float *dv,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ *   or pass a workspace (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid allocation).  The row terms D_i live in a device
+ *   array of the library instead of a caller workspace: 4 MiB per device,
+ *   held for the life of the process, so B * Hq * N may be at most 2^20
+ *   (larger shapes return ATTN_ERR_WORKSPACE and launch nothing).  The
+ *   array's device address is resolved on the first call on each device
+ *   (ATTN_ERR_HIP if it cannot be); no call allocates or frees anything.
+ *   Every call on a device shares that device's array: calls that overlap
+ *   on one device (on different streams, or from several threads) race and
+ *   give wrong results; calls in stream order are safe (the array needs no
+ *   clearing: each call writes every D_i before reading it).  Arguments,
+ *   outputs, launches and every other check as attn_bwd.
+ */
+attn_status attn_bwd_noalloc(attn_dtype dt, int B, int Hq, int Hkv, int N, int d, int causal,
+                             float scale, const void *q, const void *k, const void *v,
+                             const float *o, const float *lse, const void *dout,
+                             float *dq, float *dk, float *dv, void *stream);
 
 /*
  * attn_bwd_dlse -- attn_bwd with an upstream gradient of lse as well:
