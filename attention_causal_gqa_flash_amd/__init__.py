@@ -17,7 +17,8 @@ __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preproc
            "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
            "attn_fwd_ex", "attn_bwd_ex",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
-           "attn_decode_merged", "attn_read_probe", "attn_bwd_noalloc",
+           "attn_decode_merged", "attn_read_probe", "attn_bwd_noalloc", "attn_fwd_strided",
+           "attn_bwd_strided", "AttnLayout",
            "attn_status_str", "attn_abi_version", "AttnError", "lib", "LIB_PATH",
            "ATTN_F32", "ATTN_BF16"]
 
@@ -29,6 +30,11 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
 
 _lib = None
+
+
+class AttnLayout(ctypes.Structure):
+    """Element strides of a [B][H][N][d] tensor whose head dim is contiguous (attn_layout)."""
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
 
 
 class AttnError(RuntimeError):
@@ -92,6 +98,12 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_merged.restype = i
     L.attn_lse_merge.argtypes = [i, i, i, i, p, p, p, p, p]
     L.attn_lse_merge.restype = i
+    lp = ctypes.POINTER(AttnLayout)
+    L.attn_fwd_strided.argtypes = [i] * 8 + [i, f, p, lp, p, lp, p, lp, p, lp, p, p]
+    L.attn_fwd_strided.restype = i
+    L.attn_bwd_strided.argtypes = [i] * 8 + [i, f, p, lp, p, lp, p, lp, p, lp, p, p, lp, p,
+                                             p, lp, p, lp, p, lp, p, sz, p]
+    L.attn_bwd_strided.restype = i
     L.attn_read_probe.argtypes = [p, sz, p, p]
     L.attn_read_probe.restype = i
     L.attn_status_str.argtypes = [i]
@@ -556,3 +568,87 @@ def attn_read_probe(src, out=None, stream=None):
     rc = lib().attn_read_probe(_ptr(src), nbytes, _ptr(out), _stream(stream))
     _check("attn_read_probe", rc)
     return out
+
+
+def _strided(t, shape, dtype, name, like):
+    """A device tensor of this shape and dtype whose last dim is contiguous (any other
+    strides); returns its AttnLayout."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a contiguous last (head) dimension")
+    return AttnLayout(t.stride(0), t.stride(1), t.stride(2))
+
+
+def attn_fwd_strided(q, k, v, causal: bool = True, scale: float | None = None, o_dtype=None, o=None,
+                     lse=None, stream=None):
+    """attn_fwd_ex over views of any strides: q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d] and o may be
+    strided views (e.g. x.view(B, N, H, d).transpose(1, 2) of a [B, N, H, d] tensor) whose
+    head dim is contiguous.  A new o is contiguous.  Returns (o, lse)."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    code = _dtype_code(q)
+    lq = _strided(q, (B, Hq, Nq, d), q.dtype, "q", q)
+    lk = _strided(k, (B, Hkv, Nk, d), q.dtype, "k", q)
+    lv = _strided(v, (B, Hkv, Nk, d), q.dtype, "v", q)
+    if o is None:
+        o = _out(None, (B, Hq, Nq, d), o_dtype or torch.float32, "o", q, stream)
+    lo = _strided(o, (B, Hq, Nq, d), None, "o", q)
+    lse = _out(lse, (B, Hq, Nq), torch.float32, "lse", q, stream)
+    rc = lib().attn_fwd_strided(code, _dtype_code(o), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                                _scale(scale, d), _ptr(q), ctypes.byref(lq), _ptr(k), ctypes.byref(lk),
+                                _ptr(v), ctypes.byref(lv), _ptr(o), ctypes.byref(lo), _ptr(lse),
+                                _stream(stream))
+    _check("attn_fwd_strided", rc)
+    return o, lse
+
+
+def attn_bwd_strided(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+                     dq=None, dk=None, dv=None, workspace=None, stream=None, dlse=None):
+    """attn_bwd_ex over views of any strides (head dim contiguous): q, k, v, o, dout and the
+    outputs dq, dk, dv (new ones are contiguous).  Returns (dq, dk, dv), float32."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    code = _dtype_code(q)
+    lay = [_strided(q, (B, Hq, Nq, d), q.dtype, "q", q),
+           _strided(k, (B, Hkv, Nk, d), q.dtype, "k", q),
+           _strided(v, (B, Hkv, Nk, d), q.dtype, "v", q),
+           _strided(o, (B, Hq, Nq, d), None, "o", q)]
+    _dtype_code(o)
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse", q)
+    ldo = _strided(dout, (B, Hq, Nq, d), q.dtype, "dout", q)
+    dq = dq if dq is not None else _out(None, (B, Hq, Nq, d), torch.float32, "dq", q, stream)
+    dk = dk if dk is not None else _out(None, (B, Hkv, Nk, d), torch.float32, "dk", q, stream)
+    dv = dv if dv is not None else _out(None, (B, Hkv, Nk, d), torch.float32, "dv", q, stream)
+    louts = [_strided(dq, (B, Hq, Nq, d), torch.float32, "dq", q),
+             _strided(dk, (B, Hkv, Nk, d), torch.float32, "dk", q),
+             _strided(dv, (B, Hkv, Nk, d), torch.float32, "dv", q)]
+    if dlse is not None:
+        _expect(dlse, (B, Hq, Nq), torch.float32, "dlse", q)
+    nbytes = attn_bwd_workspace_bytes(code, B, Hq, Hkv, Nq, d)
+    if workspace is None:
+        workspace = _out(None, (max(nbytes, 256),), torch.uint8, "workspace", q, stream)
+    else:
+        _dev(workspace, "workspace")
+    rc = lib().attn_bwd_strided(code, _dtype_code(o), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                                _scale(scale, d), _ptr(q), ctypes.byref(lay[0]), _ptr(k),
+                                ctypes.byref(lay[1]), _ptr(v), ctypes.byref(lay[2]), _ptr(o),
+                                ctypes.byref(lay[3]), _ptr(lse), _ptr(dout), ctypes.byref(ldo),
+                                None if dlse is None else _ptr(dlse), _ptr(dq), ctypes.byref(louts[0]),
+                                _ptr(dk), ctypes.byref(louts[1]), _ptr(dv), ctypes.byref(louts[2]),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check("attn_bwd_strided", rc)
+    return dq, dk, dv

@@ -50,6 +50,18 @@ bool use_mfma(int dt, int N, int d, float scale)
     return attn::mfma_supported(dt, d) && scale != 0.f && (long)N * d * 2 < (1L << 31);
 }
 
+// With strided tensors (L), every bf16 tensor's head must span less than
+// 2^31 bytes: (rows - 1) * row stride + d elements.
+bool use_mfma(int dt, int Nk, int d, float scale, const attn::Layouts *L, int Nq)
+{
+    if (!use_mfma(dt, Nk, d, scale)) return false;
+    if (L == nullptr) return true;
+    auto fits = [&](const attn::TL &t, int rows) {
+        return ((long)(rows - 1) * t.n + d) * 2 < (1L << 31);
+    };
+    return fits(L->q, Nq) && fits(L->dout, Nq) && fits(L->k, Nk) && fits(L->v, Nk);
+}
+
 attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 size_t workspace_bytes(int B, int Hq, int N)
@@ -65,54 +77,63 @@ size_t workspace_bytes(int B, int Hq, int N)
 hipError_t launch_bwd_preprocess(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                                  const void *o, const void *dout, float *delta, float *dk,
                                  float *dv, bool zero_dkdv, hipStream_t st,
-                                 const float *dlse = nullptr, bool o_bf16 = false)
+                                 const float *dlse = nullptr, bool o_bf16 = false,
+                                 const attn::Layouts *L = nullptr)
 {
     const long n = (long)B * Hkv * Nk * d;
-    return attn::bwd_preprocess(dt, (long)B * Hq * Nq, d, dout, o, delta, zero_dkdv ? dk : nullptr,
-                                zero_dkdv ? dv : nullptr, n, dlse, st, o_bf16);
+    return attn::bwd_preprocess(dt, B, Hq, Nq, d, dout, o, delta, zero_dkdv ? dk : nullptr,
+                                zero_dkdv ? dv : nullptr, n, dlse, st, o_bf16, L);
 }
 
 // Forward of Nq queries against Nk >= Nq keys (arguments already validated).
 hipError_t launch_fwd(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                       float scale, const void *q, const void *k, const void *v, void *o,
-                      float *lse, hipStream_t st, bool o_bf16 = false)
+                      float *lse, hipStream_t st, bool o_bf16 = false,
+                      const attn::Layouts *L = nullptr)
 {
-    if (use_mfma(dt, Nk, d, scale))
+    if (use_mfma(dt, Nk, d, scale, L, Nq)) {
+        if (L)
+            return attn::fwd_mfma_strided(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, *L,
+                                          st, o_bf16);
         return attn::fwd_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st, o_bf16);
+    }
     return attn::fwd_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, o, lse, st,
-                             o_bf16);
+                             o_bf16, L);
 }
 
 // Head split of the dK/dV kernel (1 = plain stores; > 1 = atomics into zeroed dk/dv).
 // (use_mfma on Nk covers the Nq <= Nk query rows as well.)
-int dkdv_split(int dt, int B, int Hq, int Hkv, int Nk, int d, float scale)
+int dkdv_split(int dt, int B, int Hq, int Hkv, int Nk, int d, float scale,
+               const attn::Layouts *L = nullptr)
 {
-    return use_mfma(dt, Nk, d, scale) ? attn::dkdv_head_split(B, Hq, Hkv, Nk) : 1;
+    // strided dk / dv take no atomics (a zero-fill would have to follow their strides)
+    return use_mfma(dt, Nk, d, scale) && L == nullptr ? attn::dkdv_head_split(B, Hq, Hkv, Nk) : 1;
 }
 
 // dk and dv must already be zero when hs > 1.
 hipError_t launch_bwd_dkdv(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                            float scale, const void *q, const void *k, const void *v,
                            const float *lse, const void *dout, const float *delta, float *dk,
-                           float *dv, int hs, hipStream_t st, double rope_lb = 0.0)
+                           float *dv, int hs, hipStream_t st, double rope_lb = 0.0,
+                           const attn::Layouts *L = nullptr)
 {
-    if (use_mfma(dt, Nk, d, scale))
+    if (use_mfma(dt, Nk, d, scale, L, Nq))
         return attn::bwd_dkdv_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                   delta, dk, dv, hs, st, rope_lb);
+                                   delta, dk, dv, hs, st, rope_lb, L);
     return attn::bwd_dkdv_colwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse,
-                                  dout, delta, dk, dv, st);
+                                  dout, delta, dk, dv, st, L);
 }
 
 hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                          float scale, const void *q, const void *k, const void *v,
                          const float *lse, const void *dout, const float *delta, float *dq,
-                         hipStream_t st, double rope_lb = 0.0)
+                         hipStream_t st, double rope_lb = 0.0, const attn::Layouts *L = nullptr)
 {
-    if (use_mfma(dt, Nk, d, scale))
+    if (use_mfma(dt, Nk, d, scale, L, Nq))
         return attn::bwd_dq_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                 delta, dq, st, rope_lb);
+                                 delta, dq, st, rope_lb, L);
     return attn::bwd_dq_rowwise(dt, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                delta, dq, st);
+                                delta, dq, st, L);
 }
 
 // The gradient stage after the preprocess.  At d = 64 on the matrix-core path
@@ -129,9 +150,9 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, 
 bool fuse_bwd(int d) { return d == 64; }
 
 bool one_launch(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                int hs, int *groups = nullptr, int *blocks = nullptr)
+                int hs, int *groups = nullptr, int *blocks = nullptr, const attn::Layouts *L = nullptr)
 {
-    return use_mfma(dt, Nk, d, scale) && fuse_bwd(d) &&
+    return use_mfma(dt, Nk, d, scale, L, Nq) && fuse_bwd(d) &&
            attn::bwd_fused_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, groups, blocks);
 }
 
@@ -139,16 +160,17 @@ bool one_launch(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causa
 attn_status launch_bwd_grads(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                              float scale, const void *q, const void *k, const void *v,
                              const float *lse, const void *dout, const float *delta, float *dq,
-                             float *dk, float *dv, int hs, hipStream_t st, double rope_lb = 0.0)
+                             float *dk, float *dv, int hs, hipStream_t st, double rope_lb = 0.0,
+                             const attn::Layouts *L = nullptr)
 {
-    if (one_launch(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, hs))
+    if (one_launch(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, hs, nullptr, nullptr, L))
         return hip_status(attn::bwd_fused_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v,
-                                               lse, dout, delta, dq, dk, dv, hs, st, rope_lb));
+                                               lse, dout, delta, dq, dk, dv, hs, st, rope_lb, L));
     if (launch_bwd_dq(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta, dq, st,
-                      rope_lb) != hipSuccess)
+                      rope_lb, L) != hipSuccess)
         return ATTN_ERR_HIP;
     return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout,
-                                      delta, dk, dv, hs, st, rope_lb));
+                                      delta, dk, dv, hs, st, rope_lb, L));
 }
 
 // The whole backward of Nq query rows against Nk >= Nq keys: the preprocess
@@ -161,7 +183,7 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
                       float scale, const void *q, const void *k, const void *v, const void *o,
                       const float *lse, const void *dout, const float *dlse, float *dq, float *dk,
                       float *dv, void *workspace, size_t ws_bytes, void *stream, double rope_lb = 0.0,
-                      bool o_bf16 = false)
+                      bool o_bf16 = false, const attn::Layouts *L = nullptr)
 {
     if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
     attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
@@ -172,21 +194,21 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
     if (!aligned16(workspace) || ws_bytes < workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     float *delta = (float *)workspace;
-    const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale);
-    if (use_mfma(dt, Nk, d, scale) && !fuse_bwd(d) && !o_bf16) {
+    const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale, L);
+    if (use_mfma(dt, Nk, d, scale, L, Nq) && !fuse_bwd(d) && !o_bf16) {
         if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * Nk * d, st) != hipSuccess)
             return ATTN_ERR_HIP;
         if (attn::bwd_dq_pre_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                  (const float *)o, dlse, delta, dq, st, rope_lb) != hipSuccess)
+                                  (const float *)o, dlse, delta, dq, st, rope_lb, L) != hipSuccess)
             return ATTN_ERR_HIP;
         return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse,
-                                          dout, delta, dk, dv, hs, st, rope_lb));
+                                          dout, delta, dk, dv, hs, st, rope_lb, L));
     }
     if (launch_bwd_preprocess(dt, B, Hq, Hkv, Nq, Nk, d, o, dout, delta, dk, dv, hs > 1, st,
-                              dlse, o_bf16) != hipSuccess)
+                              dlse, o_bf16, L) != hipSuccess)
         return ATTN_ERR_HIP;
     return launch_bwd_grads(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse, dout, delta,
-                            dq, dk, dv, hs, st, rope_lb);
+                            dq, dk, dv, hs, st, rope_lb, L);
 }
 
 // The device array behind attn_bwd_noalloc: scratch for the backward's row
@@ -212,6 +234,22 @@ void *scratch_ptr()
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
     scratch_addr[dev].store(p, std::memory_order_release);
     return p;
+}
+
+// Strides of one tensor from the caller's layout (null: contiguous [B][H][N][d]).
+// Every stride must be positive, a row at least d elements long, and each
+// stride a multiple of 16 bytes so that every row starts 16-byte aligned.
+bool layout_of(const attn_layout *l, int H, int N, int d, int esz, attn::TL &t)
+{
+    if (l == nullptr) {
+        t = attn::TL{(long)H * N * d, (long)N * d, d};
+        return true;
+    }
+    const long long m = 16 / esz;
+    if (l->batch <= 0 || l->head <= 0 || l->row < d || l->row > 0x7fffffffLL) return false;
+    if (l->batch % m || l->head % m || l->row % m) return false;
+    t = attn::TL{(long)l->batch, (long)l->head, (int)l->row};
+    return true;
 }
 
 }  // namespace
@@ -285,6 +323,50 @@ attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, 
                      dv, workspace, ws_bytes, stream, 0.0, o_dt == ATTN_BF16);
 }
 
+attn_status attn_fwd_strided(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, float scale, const void *q, const attn_layout *lq,
+                             const void *k, const attn_layout *lk, const void *v,
+                             const attn_layout *lv, void *o, const attn_layout *lo, float *lse,
+                             void *stream)
+{
+    if (o_dt != ATTN_F32 && o_dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_INVALID_ARG;
+    const int esz = dt == ATTN_BF16 ? 2 : 4, oesz = o_dt == ATTN_BF16 ? 2 : 4;
+    attn::Layouts L = attn::contiguous_layouts(Hq, Hkv, Nq, Nk, d);
+    if (!layout_of(lq, Hq, Nq, d, esz, L.q) || !layout_of(lk, Hkv, Nk, d, esz, L.k) ||
+        !layout_of(lv, Hkv, Nk, d, esz, L.v) || !layout_of(lo, Hq, Nq, d, oesz, L.o))
+        return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_fwd(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse,
+                                 (hipStream_t)stream, o_dt == ATTN_BF16, &L));
+}
+
+attn_status attn_bwd_strided(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, float scale, const void *q, const attn_layout *lq,
+                             const void *k, const attn_layout *lk, const void *v,
+                             const attn_layout *lv, const void *o, const attn_layout *lo,
+                             const float *lse, const void *dout, const attn_layout *ldout,
+                             const float *dlse, float *dq, const attn_layout *ldq, float *dk,
+                             const attn_layout *ldk, float *dv, const attn_layout *ldv,
+                             void *workspace, size_t ws_bytes, void *stream)
+{
+    if (o_dt != ATTN_F32 && o_dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (dlse != nullptr && !aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    const int esz = dt == ATTN_BF16 ? 2 : 4, oesz = o_dt == ATTN_BF16 ? 2 : 4;
+    attn::Layouts L = attn::contiguous_layouts(Hq, Hkv, Nq, Nk, d);
+    if (!layout_of(lq, Hq, Nq, d, esz, L.q) || !layout_of(lk, Hkv, Nk, d, esz, L.k) ||
+        !layout_of(lv, Hkv, Nk, d, esz, L.v) || !layout_of(lo, Hq, Nq, d, oesz, L.o) ||
+        !layout_of(ldout, Hq, Nq, d, esz, L.dout) || !layout_of(ldq, Hq, Nq, d, 4, L.dq) ||
+        !layout_of(ldk, Hkv, Nk, d, 4, L.dk) || !layout_of(ldv, Hkv, Nk, d, 4, L.dv))
+        return ATTN_ERR_INVALID_ARG;
+    return bwd_whole(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, dout, dlse, dq, dk,
+                     dv, workspace, ws_bytes, stream, 0.0, o_dt == ATTN_BF16, &L);
+}
+
 attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0, double base,
                       int inverse, const void *x, void *y, void *stream)
 {
@@ -309,6 +391,15 @@ attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
         !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
+    // matrix-core path: one pass rotates k, the forward rotates each query row
+    // in its prologue and writes q_rot; otherwise one pass rotates both
+    // (log2 base = 0 means "no rotation" to the kernels: a base of 1 takes the pass)
+    if (use_mfma(dt, Nk, d, scale) && log2(base) != 0.0 && q_rot != q) {
+        if (attn::rope(dt, (long)B * Hkv * Nk, Nk, d, 0, base, 0, k, k_rot, st) != hipSuccess)
+            return ATTN_ERR_HIP;
+        return hip_status(attn::fwd_mfma_rope_q(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k_rot, v,
+                                                q_rot, o, lse, log2(base), st));
+    }
     if (attn::rope2(dt, (long)B * Hq * Nq, Nq, Nk - Nq, q, q_rot, (long)B * Hkv * Nk, Nk, 0, k, k_rot, d,
                     base, 0, st) != hipSuccess)
         return ATTN_ERR_HIP;

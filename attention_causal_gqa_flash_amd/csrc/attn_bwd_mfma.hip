@@ -195,13 +195,13 @@ struct BwdLds {
 // outputs.  The copy of step s+1 has the two sub-steps of step s to land; at
 // the end the four tile arrays hold the dK^T / dV^T partials of the two query
 // halves.  XL = false compiles the square case (Nk taken equal to Nq).
-template <int D, bool XL>
+template <int D, bool XL, bool STR = false>
 __device__ __forceinline__ void dkdv_body(
     int kt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
     float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
-    double rope_lb)
+    double rope_lb, const Layouts &L = Layouts{})
 {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int SR = BwdLds<D>::SR;
@@ -226,8 +226,12 @@ __device__ __forceinline__ void dkdv_body(
     const uint32_t ksign = scale < 0.f ? 0x80008000u : 0u;
     const float c2 = fabsf(scale) * kLog2e;
 
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    // strides of the 4-D tensors (STR: the caller's; else contiguous [B][H][N][D])
+    const TL lq = STR ? L.q : contiguous_tl(Hq, Nq, D), ldo = STR ? L.dout : contiguous_tl(Hq, Nq, D);
+    const TL lk = STR ? L.k : contiguous_tl(Hkv, Nk, D), lv = STR ? L.v : contiguous_tl(Hkv, Nk, D);
+    const TL ldk = STR ? L.dk : contiguous_tl(Hkv, Nk, D), ldv = STR ? L.dv : contiguous_tl(Hkv, Nk, D);
+    const uint16_t *Kg = K + b * lk.b + g * lk.h;
+    const uint16_t *Vg = V + b * lv.b + g * lv.h;
 
     // K^T and V^T operands, resident: lane holds row kj, dims 16ks + 8hf .. +7.
     // The key tile's K and V rows move global -> LDS directly (whole rows,
@@ -235,10 +239,9 @@ __device__ __forceinline__ void dkdv_body(
     // dO buffers, which step 1's copy fills only after step 0 has read them.
     bf16x8 kf[KS], vf[KS];
     {
-        const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
-        const TileCopy<D, kKvBN, 4> kvcopy(wave, lane);
-        kvcopy(q1s, make_rsrc(Kg, kv_bytes), k0, wave);
-        kvcopy(d1s, make_rsrc(Vg, kv_bytes), k0, wave);
+        const TileCopy<D, kKvBN, 4> kcopy(wave, lane, lk.n), vcopy(wave, lane, lv.n);
+        kcopy(q1s, make_rsrc(Kg, head_bytes(Nk, lk.n, D, 2)), k0, wave);
+        vcopy(d1s, make_rsrc(Vg, head_bytes(Nk, lv.n, D, 2)), k0, wave);
     }
     auto read_kv = [&] {
 #pragma unroll
@@ -268,15 +271,17 @@ __device__ __forceinline__ void dkdv_body(
     // 2/3 (those of D), which store them as -lse / |scale| and -D at the top
     // of the step.  Rows past Nq read as zero and are masked in the step's
     // arithmetic.
-    const uint32_t tile_bytes = (uint32_t)Nq * D * 2, row_bytes = (uint32_t)Nq * 4;
-    const TileCopy<D, SR, 4> copy(wave, lane);
+    const uint32_t q_bytes = head_bytes(Nq, lq.n, D, 2), do_bytes = head_bytes(Nq, ldo.n, D, 2);
+    const uint32_t row_bytes = (uint32_t)Nq * 4;
+    const TileCopy<D, SR, 4> copy(wave, lane, lq.n), dcopy(wave, lane, ldo.n);
     const float row_mul = wave < 2 ? -1.f / fabsf(scale) : -1.f;
     float row_v = 0.f;                       // this lane's row term of the next step
     auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd) {
-        const size_t hrow = ((size_t)b * Hq + g * G + hsub * Gs + s_ / nq) * Nq;
+        const int hq = g * G + hsub * Gs + s_ / nq;
+        const size_t hrow = ((size_t)b * Hq + hq) * Nq;
         const int q0_ = (qt0 + s_ % nq) * SR;
-        copy(qd, make_rsrc(Q + hrow * D, tile_bytes), q0_, wave);
-        copy(dd, make_rsrc(dO + hrow * D, tile_bytes), q0_, wave);
+        copy(qd, make_rsrc(Q + b * lq.b + hq * lq.h, q_bytes), q0_, wave);
+        dcopy(dd, make_rsrc(dO + b * ldo.b + hq * ldo.h, do_bytes), q0_, wave);
         const int half = wave & 1;
         row_v = row_load(make_rsrc((wave < 2 ? LSE : Dws) + hrow, row_bytes), q0_ + 64 * half, lane);
     };
@@ -398,21 +403,22 @@ __device__ __forceinline__ void dkdv_body(
             }
         }
     }
-    float *dKg = dK + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    float *dVg = dV + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    float *dKg = dK + b * ldk.b + g * ldk.h;
+    float *dVg = dV + b * ldv.b + g * ldv.h;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int key = k0 + wave + 4 * i;
         if (key < Nk) {
 #pragma unroll
             for (int c = 0; c < CPR; ++c) {
-                const size_t at = (size_t)key * D + 64 * c + lane;
+                const size_t atk = (size_t)key * ldk.n + 64 * c + lane;
+                const size_t atv = (size_t)key * ldv.n + 64 * c + lane;
                 if (hs == 1) {
-                    dKg[at] = vk[i * CPR + c];
-                    dVg[at] = vv[i * CPR + c];
+                    dKg[atk] = vk[i * CPR + c];
+                    dVg[atv] = vv[i * CPR + c];
                 } else {
-                    atomicAdd(dKg + at, vk[i * CPR + c]);
-                    atomicAdd(dVg + at, vv[i * CPR + c]);
+                    atomicAdd(dKg + atk, vk[i * CPR + c]);
+                    atomicAdd(dVg + atv, vv[i * CPR + c]);
                 }
             }
         }
@@ -422,13 +428,13 @@ __device__ __forceinline__ void dkdv_body(
 // d = 128 needs more than the 256 registers of two waves per SIMD (K, V
 // operands 64 + dK, dV accumulators 128 + scores 32 + operands in flight):
 // it runs one wave per SIMD with up to 512.
-template <int D, bool XL>
+template <int D, bool XL, bool STR = false>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
     float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
-    double rope_lb)
+    double rope_lb, Layouts L)
 {
     ATTN_BWD_LDS(D, lds);
     if constexpr (!XL) Nk = Nq;
@@ -437,8 +443,328 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(
     const int nkt = (Nk + kKvBN - 1) / kKvBN;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nkt, hs, w)) return;
-    dkdv_body<D, XL>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq,
-                 Hkv, Nq, Nk, scale, causal, hs, rope_lb);
+    dkdv_body<D, XL, STR>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK, dV, B,
+                          Hq, Hkv, Nq, Nk, scale, causal, hs, rope_lb, L);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with paired roles (d = 128): two waves per SIMD
+// ---------------------------------------------------------------------------
+// The kernel above holds, per wave, the K and V operands of its 32 keys and
+// both the dK and the dV accumulators (about 356 registers at d = 128), so it
+// runs one wave per SIMD: while that wave waits on LDS reads or works through
+// the softmax, the matrix core idles.  Here the work of a (32-query, 32-key)
+// block is split between two waves of the same SIMD:
+//   * role P (waves 0-3): K operand resident; S = Q K^T, P = e^(scale S - lse)
+//     (masked), P handed over through LDS, then dV^T += dO^T P;
+//   * role G (waves 4-7): V operand resident; dP = dO V^T, then, with P from
+//     LDS, dS = P (dP - D) and dK^T += Q^T dS.
+// Each wave keeps one operand (32 registers) and one accumulator set (64),
+// about 200 registers in all, so eight waves fit a CU (two per SIMD; a wave
+// and its partner, w and w + 4, share a SIMD) and one wave's MFMAs overlap
+// the other's softmax and LDS waits.  P crosses as bf16 (the precision it has
+// as an MFMA operand anyway) in a per-lane slot of LDS, double-buffered by
+// sub-step; one barrier per sub-step orders the hand-over.  Work items, the
+// step loop over query heads and 128-row query tiles, and the epilogue are
+// those of the kernel above.
+constexpr int kPairWaves = 8;
+
+template <int D>
+struct BwdPairLds {
+    static constexpr int SR = kKvSub * kKvBM;   // query rows per step
+    uint16_t *q0s, *q1s, *d0s, *d1s;
+    float *l0s, *l1s, *e0s, *e1s;
+    uint4 *pbuf;                                // [sub][pair][2][64 lanes]
+};
+
+template <int D, bool XL, bool STR = false>
+__device__ __forceinline__ void dkdv_pair_body(
+    int kt, int item, const BwdPairLds<D> &lds, const uint16_t *__restrict__ Q,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
+    double rope_lb, const Layouts &L = Layouts{})
+{
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int SR = BwdPairLds<D>::SR;
+    if constexpr (!XL) Nk = Nq;
+    const int off = XL ? Nk - Nq : 0;
+    uint16_t *const q0s = lds.q0s, *const q1s = lds.q1s, *const d0s = lds.d0s, *const d1s = lds.d1s;
+    float *const l0s = lds.l0s, *const l1s = lds.l1s, *const e0s = lds.e0s, *const e1s = lds.e1s;
+
+    const int grp = item / hs, hsub = item % hs;
+    const int b = grp / Hkv, g = grp % Hkv;
+    const int G = Hq / Hkv, Gs = G / hs;
+    const int k0 = kt * kKvBN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int l32 = lane & 31, hf = lane >> 5;
+    const bool role_p = wave < 4;            // P and dV; else dP and dK
+    const int pair = wave & 3;
+    const int kb = wave & 1, qh = (wave >> 1) & 1;
+    const int kj = k0 + 32 * kb + l32;       // this lane's key column
+
+    const uint32_t ksign = scale < 0.f ? 0x80008000u : 0u;
+    const float c2 = fabsf(scale) * kLog2e;
+
+    // strides of the 4-D tensors (STR: the caller's; else contiguous [B][H][N][D])
+    const TL lq = STR ? L.q : contiguous_tl(Hq, Nq, D), ldo = STR ? L.dout : contiguous_tl(Hq, Nq, D);
+    const TL lk = STR ? L.k : contiguous_tl(Hkv, Nk, D), lv = STR ? L.v : contiguous_tl(Hkv, Nk, D);
+    const TL ldk = STR ? L.dk : contiguous_tl(Hkv, Nk, D), ldv = STR ? L.dv : contiguous_tl(Hkv, Nk, D);
+    const uint16_t *Kg = K + b * lk.b + g * lk.h;
+    const uint16_t *Vg = V + b * lv.b + g * lv.h;
+
+    // the resident operand: K^T (role P) or V^T (role G), rows of the key
+    // tile copied global -> LDS whole into the second Q / dO buffers first
+    bf16x8 opf[KS];
+    {
+        const TileCopy<D, kKvBN, kPairWaves> kcopy(wave, lane, lk.n), vcopy(wave, lane, lv.n);
+        kcopy(q1s, make_rsrc(Kg, head_bytes(Nk, lk.n, D, 2)), k0, wave);
+        vcopy(d1s, make_rsrc(Vg, head_bytes(Nk, lv.n, D, 2)), k0, wave);
+    }
+    auto read_op = [&] {
+        const uint16_t *src = role_p ? q1s : d1s;
+        const uint32_t sign = role_p ? ksign : 0u;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 u = *(const uint4 *)tile_chunk<D>(src, 32 * kb + l32, 2 * ks + hf);
+            u.x ^= sign; u.y ^= sign; u.z ^= sign; u.w ^= sign;
+            opf[ks] = as_bf16x8(u);
+        }
+    };
+
+    f32x16 acc[DB];                          // dV^T (role P) or dK^T (role G)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    const int nqt = (Nq + SR - 1) / SR;
+    const int qt0 = causal ? (XL ? max(k0 - off, 0) : k0) / SR : 0;
+    const int nq = nqt - qt0;
+    const int steps = Gs * nq;
+
+    const uint32_t q_bytes = head_bytes(Nq, lq.n, D, 2), do_bytes = head_bytes(Nq, ldo.n, D, 2);
+    const uint32_t row_bytes = (uint32_t)Nq * 4;
+    const TileCopy<D, SR, kPairWaves> copy(wave, lane, lq.n), dcopy(wave, lane, ldo.n);
+    // row terms: waves 0/1 load the two halves of lse, 2/3 those of D
+    const float row_mul = wave < 2 ? -1.f / fabsf(scale) : -1.f;
+    float row_v = 0.f;
+    auto load_step = [&](int s_, uint16_t *qd, uint16_t *dd) {
+        const int hq = g * G + hsub * Gs + s_ / nq;
+        const size_t hrow = ((size_t)b * Hq + hq) * Nq;
+        const int q0_ = (qt0 + s_ % nq) * SR;
+        copy(qd, make_rsrc(Q + b * lq.b + hq * lq.h, q_bytes), q0_, wave);
+        dcopy(dd, make_rsrc(dO + b * ldo.b + hq * ldo.h, do_bytes), q0_, wave);
+        if (wave < 4)
+            row_v = row_load(make_rsrc((wave < 2 ? LSE : Dws) + hrow, row_bytes), q0_ + 64 * (wave & 1), lane);
+    };
+    if (steps > 0) load_step(0, q0s, d0s);
+
+    auto run_step = [&](auto bufc, int s) {
+        constexpr int BI = decltype(bufc)::value;
+        const uint16_t *qc = BI ? q1s : q0s, *dc = BI ? d1s : d0s;
+        float *lc = BI ? l1s : l0s, *ec = BI ? e1s : e0s;
+        wait_vmcnt<0>();                    // this wave's copies of step s have landed
+        if (wave < 4) (wave < 2 ? lc : ec)[64 * (wave & 1) + lane] = row_v * row_mul;
+        __syncthreads();                    // ... and every wave's; buffer s+1 is free
+        if constexpr (BI == 0) {
+            if (s == 0) {                   // the resident operand, then buffer 1 is free
+                read_op();
+                __syncthreads();
+            }
+        }
+        if (s + 1 < steps) {
+            if (BI) load_step(s + 1, q0s, d0s);
+            else load_step(s + 1, q1s, d1s);
+        }
+        const int qs = (qt0 + s % nq) * SR;
+#pragma unroll
+        for (int sub = 0; sub < kKvSub; ++sub) {
+            const int q0 = qs + sub * kKvBM;
+            const int qb0 = q0 + 32 * qh;
+            const bool active = qb0 < Nq && k0 + 32 * kb < Nk && (!causal || qb0 + 31 + off >= k0 + 32 * kb);
+            const bool mask = causal && qb0 + off < k0 + 32 * kb + 32;
+            const uint16_t *qt = qc + sub * kKvBM * D, *dt = dc + sub * kKvBM * D;
+            uint4 *pb = lds.pbuf + (sub * 4 + pair) * 128;
+            f32x16 sacc;
+            if (active) {
+                // phase 1: S (role P) or dP (role G) from the row term up
+                const float *rt = role_p ? lc + sub * kKvBM : ec + sub * kKvBM;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float4 t = *(const float4 *)&rt[32 * qh + 8 * a + 4 * hf];
+                    sacc[4 * a + 0] = t.x; sacc[4 * a + 1] = t.y;
+                    sacc[4 * a + 2] = t.z; sacc[4 * a + 3] = t.w;
+                }
+                const uint16_t *src = role_p ? qt : dt;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    sacc = mfma32x32x16(tile_row_operand<D>(src, 32 * qh + l32, 2 * ks + hf), opf[ks], sacc);
+                sched_pipeline<KS + 4, KS, 8, 1>();
+                if (role_p) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[r] = exp2_fast(sacc[r] * c2);
+                    if (mask) {
+                        const int t = kj - off - (q0 + 32 * qh + 4 * hf);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int c = 8 * (r >> 2) + (r & 3);
+                            sacc[r] = c >= t ? sacc[r] : 0.f;
+                        }
+                    }
+                    pb[lane] = __builtin_bit_cast(uint4, pack_operand<0>(sacc));
+                    pb[64 + lane] = __builtin_bit_cast(uint4, pack_operand<8>(sacc));
+                }
+            }
+            __syncthreads();                // P of this sub-step is in LDS
+            if (active) {
+                bf16x8 op0, op1;
+                if (role_p) {
+                    op0 = pack_operand<0>(sacc);
+                    op1 = pack_operand<8>(sacc);
+                } else {
+                    // dS = P (dP - D): P from the partner, in this lane's layout
+                    const uint4 p0 = pb[lane], p1 = pb[64 + lane];
+                    f32x16 ds;
+                    ds[0] = bf16lo(p0.x) * sacc[0]; ds[1] = bf16hi(p0.x) * sacc[1];
+                    ds[2] = bf16lo(p0.y) * sacc[2]; ds[3] = bf16hi(p0.y) * sacc[3];
+                    ds[4] = bf16lo(p0.z) * sacc[4]; ds[5] = bf16hi(p0.z) * sacc[5];
+                    ds[6] = bf16lo(p0.w) * sacc[6]; ds[7] = bf16hi(p0.w) * sacc[7];
+                    ds[8] = bf16lo(p1.x) * sacc[8]; ds[9] = bf16hi(p1.x) * sacc[9];
+                    ds[10] = bf16lo(p1.y) * sacc[10]; ds[11] = bf16hi(p1.y) * sacc[11];
+                    ds[12] = bf16lo(p1.z) * sacc[12]; ds[13] = bf16hi(p1.z) * sacc[13];
+                    ds[14] = bf16lo(p1.w) * sacc[14]; ds[15] = bf16hi(p1.w) * sacc[15];
+                    op0 = pack_operand<0>(ds);
+                    op1 = pack_operand<8>(ds);
+                }
+                // phase 2: dV^T += dO^T P (role P) or dK^T += Q^T dS (role G)
+                const uint16_t *src = role_p ? dt : qt;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = mfma32x32x16(tr_operand<D>(src, 32 * qh + 16 * tt, db * 32, lane),
+                                               tt ? op1 : op0, acc[db]);
+                sched_pipeline<4 * DB, 2 * DB, 8, 2>();
+            }
+        }
+        sched_fence();
+    };
+    for (int s = 0; s < steps; s += 2) {
+        run_step(Buf<0>{}, s);
+        if (s + 1 < steps) run_step(Buf<1>{}, s + 1);
+    }
+
+    // Sum the two query halves: the half-1 waves park their partials in the
+    // tile arrays transposed to [key][dim] (dV of key block kb in the Q
+    // arrays, dK in the dO arrays), the half-0 waves add theirs in place, then
+    // all eight waves store (or add atomically) along the dim.  Key row r
+    // keeps its 16-byte chunk c at c ^ (r mod NC).
+    static_assert(32 * D * sizeof(float) <= SR * D * sizeof(uint16_t), "transposed partial fits");
+    constexpr int NC = D / 4;
+    auto pidx = [](int row, int dim) { return row * D + 4 * ((dim >> 2) ^ (row & (NC - 1))); };
+    float *red = reinterpret_cast<float *>(role_p ? (kb ? q1s : q0s) : (kb ? d1s : d0s));
+    const float amul = role_p ? 1.f : scale;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (qh == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                *(float4 *)&red[pidx(l32, db * 32 + 8 * a + 4 * hf)] =
+                    make_float4(acc[db][4 * a], acc[db][4 * a + 1], acc[db][4 * a + 2], acc[db][4 * a + 3]);
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int at = pidx(l32, db * 32 + 8 * a + 4 * hf);
+                const float4 pv = *(const float4 *)&red[at];
+                *(float4 *)&red[at] = make_float4((pv.x + acc[db][4 * a]) * amul, (pv.y + acc[db][4 * a + 1]) * amul,
+                                                  (pv.z + acc[db][4 * a + 2]) * amul,
+                                                  (pv.w + acc[db][4 * a + 3]) * amul);
+            }
+    }
+    __syncthreads();
+    // wave w takes key rows w, w + 8, ... of the tile, lanes along the dim
+    constexpr int RPW = kKvBN / kPairWaves, CPR = D / 64;
+    float vk[RPW * CPR], vv[RPW * CPR];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int kr = wave + kPairWaves * i;
+        const float *sk = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s);
+        const float *sv = reinterpret_cast<const float *>((kr >> 5) ? q1s : q0s);
+#pragma unroll
+        for (int c = 0; c < CPR; ++c) {
+            const int dim = 64 * c + lane;
+            const int src = pidx(kr & 31, dim) + (dim & 3);
+            vk[i * CPR + c] = sk[src];
+            vv[i * CPR + c] = sv[src];
+        }
+    }
+    if (rope_lb != 0.0) {
+        const double th = rope_theta(lane & (D / 2 - 1), D, rope_lb);
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int kr = wave + kPairWaves * i;
+            const float *sk = reinterpret_cast<const float *>((kr >> 5) ? d1s : d0s);
+            float sn, cs;
+            rope_sincos_hw((double)(k0 + kr) * th, sn, cs);
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) {
+                const int dim = 64 * c + lane;
+                const int pd = dim ^ (D / 2);
+                const float partner = sk[pidx(kr & 31, pd) + (pd & 3)];
+                vk[i * CPR + c] = vk[i * CPR + c] * cs + (dim < D / 2 ? sn : -sn) * partner;
+            }
+        }
+    }
+    float *dKg = dK + b * ldk.b + g * ldk.h;
+    float *dVg = dV + b * ldv.b + g * ldv.h;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int key = k0 + wave + kPairWaves * i;
+        if (key < Nk) {
+#pragma unroll
+            for (int c = 0; c < CPR; ++c) {
+                const size_t atk = (size_t)key * ldk.n + 64 * c + lane;
+                const size_t atv = (size_t)key * ldv.n + 64 * c + lane;
+                if (hs == 1) {
+                    dKg[atk] = vk[i * CPR + c];
+                    dVg[atv] = vv[i * CPR + c];
+                } else {
+                    atomicAdd(dKg + atk, vk[i * CPR + c]);
+                    atomicAdd(dVg + atv, vv[i * CPR + c]);
+                }
+            }
+        }
+    }
+}
+
+template <int D, bool XL, bool STR = false>
+__global__ __launch_bounds__(64 * kPairWaves, 1) void bwd_dkdv_pair_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dK,
+    float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int hs,
+    double rope_lb, Layouts L)
+{
+    constexpr int SR = BwdPairLds<D>::SR;
+    __shared__ __attribute__((aligned(16))) uint16_t q0[SR * D], q1[SR * D], d0[SR * D], d1[SR * D];
+    __shared__ __attribute__((aligned(16))) float l0[SR], l1[SR], e0[SR], e1[SR];
+    __shared__ __attribute__((aligned(16))) uint4 pbuf[kKvSub * 4 * 2 * 64];
+    const BwdPairLds<D> lds{q0, q1, d0, d1, l0, l1, e0, e1, pbuf};
+    if constexpr (!XL) Nk = Nq;
+    const int nkt = (Nk + kKvBN - 1) / kKvBN;
+    WorkItem w;
+    if (!xcd_work_item(blockIdx.x, B * Hkv, nkt, hs, w)) return;
+    dkdv_pair_body<D, XL, STR>(nkt - 1 - w.tile, w.group * hs + w.head, lds, Q, K, V, LSE, dO, Dws, dK,
+                               dV, B, Hq, Hkv, Nq, Nk, scale, causal, hs, rope_lb, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -510,14 +836,14 @@ __device__ __forceinline__ void dq_tile(const uint16_t *skb, const uint16_t *svb
 // PRE (not with STAGE): the rows' D_i = dO_i . O_i - dlse_i is computed here,
 // from O (f32) and the dO operands the lane holds, and written to Dws for a
 // dK/dV kernel that runs afterwards.
-template <int D, bool XL, bool STAGE, bool PRE = false>
+template <int D, bool XL, bool STAGE, bool PRE = false, bool STR = false>
 __device__ __forceinline__ void dq_body(
     int qt, int item, const BwdLds<D> &lds, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
     int Hq, int Hkv, int Nq, int Nk, float scale, int causal, double rope_lb,
     const float *__restrict__ O = nullptr, const float *__restrict__ dlse = nullptr,
-    float *__restrict__ Dout = nullptr)
+    float *__restrict__ Dout = nullptr, const Layouts &L = Layouts{})
 {
     static_assert(!(PRE && STAGE), "the row terms come from the lane's own dO operands");
     constexpr int KS = D / 16, DB = D / 32;
@@ -542,22 +868,26 @@ __device__ __forceinline__ void dq_body(
     const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
     const float c2 = fabsf(scale) * kLog2e;
 
-    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;      // rows of lse, D, dlse
+    // strides of the 4-D tensors (STR: the caller's; else contiguous [B][H][N][D])
+    const TL lq = STR ? L.q : contiguous_tl(Hq, Nq, D), ldo = STR ? L.dout : contiguous_tl(Hq, Nq, D);
+    const TL lo = STR ? L.o : contiguous_tl(Hq, Nq, D), ldq = STR ? L.dq : contiguous_tl(Hq, Nq, D);
+    const TL lk = STR ? L.k : contiguous_tl(Hkv, Nk, D), lv = STR ? L.v : contiguous_tl(Hkv, Nk, D);
+    const uint16_t *Qh = Q + b * lq.b + h * lq.h, *dOh = dO + b * ldo.b + h * ldo.h;
+    const uint16_t *Kg = K + b * lk.b + g * lk.h;
+    const uint16_t *Vg = V + b * lv.b + g * lv.h;
 
     bf16x8 qf[KS], dof[KS];
     if constexpr (STAGE) {
-        const uint32_t q_bytes = (uint32_t)Nq * D * 2;
-        const TileCopy<D, kQBM, 4> qcopy(wave, lane);
-        qcopy(sk1, make_rsrc(Q + qrow0 * D, q_bytes), q0, wave);
-        qcopy(sv1, make_rsrc(dO + qrow0 * D, q_bytes), q0, wave);
+        const TileCopy<D, kQBM, 4> qcopy(wave, lane, lq.n), dcopy(wave, lane, ldo.n);
+        qcopy(sk1, make_rsrc(Qh, head_bytes(Nq, lq.n, D, 2)), q0, wave);
+        dcopy(sv1, make_rsrc(dOh, head_bytes(Nq, ldo.n, D, 2)), q0, wave);
     } else {
         const int qr = min(qi, Nq - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 uq = *(const uint4 *)(Q + (qrow0 + qr) * D + 16 * ks + 8 * hf);
-            const uint4 ud = *(const uint4 *)(dO + (qrow0 + qr) * D + 16 * ks + 8 * hf);
+            uint4 uq = *(const uint4 *)(Qh + (size_t)qr * lq.n + 16 * ks + 8 * hf);
+            const uint4 ud = *(const uint4 *)(dOh + (size_t)qr * ldo.n + 16 * ks + 8 * hf);
             uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
             qf[ks] = as_bf16x8(uq);
             dof[ks] = as_bf16x8(ud);
@@ -570,7 +900,7 @@ __device__ __forceinline__ void dq_body(
         // then the two halves of the row summed across the lane pair
         float s = 0.f;
         if (qi < Nq) {
-            const float *orow = O + (qrow0 + qi) * D;
+            const float *orow = O + b * lo.b + h * lo.h + (size_t)qi * lo.n;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const float4 a = *(const float4 *)(orow + 16 * ks + 8 * hf);
@@ -606,11 +936,11 @@ __device__ __forceinline__ void dq_body(
     const int ntiles = (kv_end + kQBN - 1) / kQBN;
 
     // Tiles move global -> LDS directly; rows past Nk read as zero and are masked.
-    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+    const uint32_t k_bytes = head_bytes(Nk, lk.n, D, 2), v_bytes = head_bytes(Nk, lv.n, D, 2);
     using Copy = TileCopy<D, kQBN, 4>;
-    const Copy copy(wave, lane);
-    copy(sk0, make_rsrc(Kg, kv_bytes), 0, wave);
-    copy(sv0, make_rsrc(Vg, kv_bytes), 0, wave);
+    const Copy copy(wave, lane, lk.n), copyv(wave, lane, lv.n);
+    copy(sk0, make_rsrc(Kg, k_bytes), 0, wave);
+    copyv(sv0, make_rsrc(Vg, v_bytes), 0, wave);
 
     auto run_tile = [&](auto bufc, int t) {
         constexpr int BI = decltype(bufc)::value;
@@ -633,11 +963,12 @@ __device__ __forceinline__ void dq_body(
         }
         // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
         // past the last tile they read nothing (zero-byte resources)
-        const uint32_t nb = t + 1 < ntiles ? kv_bytes : 0u;
-        const __amdgpu_buffer_rsrc_t rkn = make_rsrc(Kg, nb), rvn = make_rsrc(Vg, nb);
+        const bool more = t + 1 < ntiles;
+        const __amdgpu_buffer_rsrc_t rkn = make_rsrc(Kg, more ? k_bytes : 0u),
+                                     rvn = make_rsrc(Vg, more ? v_bytes : 0u);
         auto prefetch = [&] {
             copy(skn, rkn, (t + 1) * kQBN, wave);
-            copy(svn, rvn, (t + 1) * kQBN, wave);
+            copyv(svn, rvn, (t + 1) * kQBN, wave);
         };
         // No branch on whether the wave has work in this tile (a branch would
         // duplicate the interleaved copies and spill registers): a wave whose
@@ -711,17 +1042,17 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
         const int qr = qw0 + RPI * i + rl;
-        if (qr < Nq) *(float4 *)(dQ + (qrow0 + qr) * D + 4 * cl) = vq[i];
+        if (qr < Nq) *(float4 *)(dQ + b * ldq.b + h * ldq.h + (size_t)qr * ldq.n + 4 * cl) = vq[i];
     }
 }
 
-template <int D, bool XL, bool PRE>
+template <int D, bool XL, bool PRE, bool STR = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
     int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt, double rope_lb,
-    const float *__restrict__ O, const float *__restrict__ dlse, float *__restrict__ Dout)
+    const float *__restrict__ O, const float *__restrict__ dlse, float *__restrict__ Dout, Layouts L)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
@@ -730,8 +1061,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int G = Hq / Hkv;
     WorkItem w;
     if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    dq_body<D, XL, false, PRE>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv,
-                               Nq, Nk, scale, causal, rope_lb, O, dlse, Dout);
+    dq_body<D, XL, false, PRE, STR>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq,
+                                    Hkv, Nq, Nk, scale, causal, rope_lb, O, dlse, Dout, L);
 }
 
 // Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
@@ -740,13 +1071,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 // hardware's in-order dispatch of blocks to free CU slots packs the two kinds
 // together.  Within a level, the block's XCD picks a contiguous range of its
 // work items (a group's rows stay in one L2).
-template <int D, bool XL>
+template <int D, bool XL, bool STR = false>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ,
     float *__restrict__ dK, float *__restrict__ dV, int B, int Hq, int Hkv, int Nq, int Nk,
-    float scale, int causal, int hs, BwdPlan plan, double rope_lb)
+    float scale, int causal, int hs, BwdPlan plan, double rope_lb, Layouts L)
 {
     static_assert(kQBN <= BwdLds<D>::SR && kQBM <= BwdLds<D>::SR, "dQ's K/V tiles and Q/dO rows fit the Q/dO arrays");
     ATTN_BWD_LDS(D, lds);
@@ -763,24 +1094,26 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_fused_kernel(
     const int item = (rel % kXcds) * per_xcd + k % per_xcd;
     if (item >= per_level) return;
     if (kind == 0)
-        dkdv_body<D, XL>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale,
-                         causal, hsi, rope_lb);
+        dkdv_body<D, XL, STR>(level, item, lds, Q, K, V, LSE, dO, Dws, dK, dV, B, Hq, Hkv, Nq, Nk, scale,
+                              causal, hsi, rope_lb, L);
     else
-        dq_body<D, XL, true>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk, scale, causal,
-                       rope_lb);
+        dq_body<D, XL, true, false, STR>(level, item, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq, Hkv, Nq, Nk,
+                                         scale, causal, rope_lb, nullptr, nullptr, nullptr, L);
 }
 
-// Runs f(D, XL) (as integral constants) for head dim d and the cross-length
-// flag xl; the square instantiations keep Nk == Nq known to the compiler.
+// Runs f(D, XL, STR) (as integral constants) for head dim d, the
+// cross-length flag xl and the strided-layout flag str; the square
+// instantiations keep Nk == Nq known to the compiler.
 template <class F>
-hipError_t bwd_variant(int d, bool xl, F &&f)
+hipError_t bwd_variant(int d, bool xl, bool str, F &&f)
 {
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;
     using T = std::true_type;
     using Fa = std::false_type;
-    if (d == 128) xl ? f(I128{}, T{}) : f(I128{}, Fa{});
-    else if (d == 64) xl ? f(I64{}, T{}) : f(I64{}, Fa{});
+    auto with_str = [&](auto dc, auto xc) { str ? f(dc, xc, T{}) : f(dc, xc, Fa{}); };
+    if (d == 128) xl ? with_str(I128{}, T{}) : with_str(I128{}, Fa{});
+    else if (d == 64) xl ? with_str(I64{}, T{}) : with_str(I64{}, Fa{});
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -821,50 +1154,61 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
-                         hipStream_t st, double rope_lb)
+                         hipStream_t st, double rope_lb, const Layouts *L)
 {
     const int nkt = (Nk + kKvBN - 1) / kKvBN;
     const dim3 grid((unsigned)(nkt * B * Hkv * hs));
-    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
-                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
-                           (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dk, dv, B, Hq,
-                           Hkv, Nq, Nk, scale, causal, hs, rope_lb);
+    const Layouts lay = L ? *L : Layouts{};
+    return bwd_variant(d, Nq != Nk, L != nullptr, [&](auto dc, auto xc, auto sc) {
+        constexpr int DD = decltype(dc)::value;
+        constexpr bool XX = decltype(xc)::value, SS = decltype(sc)::value;
+#ifndef ATTN_DKDV_ONE_WAVE_PER_SIMD
+        if constexpr (DD == 128) {
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<128, XX, SS>), grid, dim3(64 * kPairWaves), 0, st,
+                               (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, lse,
+                               (const uint16_t *)dout, Dws, dk, dv, B, Hq, Hkv, Nq, Nk, scale, causal,
+                               hs, rope_lb, lay);
+            return;
+        }
+#endif
+        hipLaunchKernelGGL((bwd_dkdv_kernel<DD, XX, SS>), grid, dim3(256), 0, st, (const uint16_t *)q,
+                           (const uint16_t *)k, (const uint16_t *)v, lse, (const uint16_t *)dout, Dws,
+                           dk, dv, B, Hq, Hkv, Nq, Nk, scale, causal, hs, rope_lb, lay);
     });
 }
 
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st,
-                       double rope_lb)
+                       double rope_lb, const Layouts *L)
 {
     const int nqt = (Nq + kQBM - 1) / kQBM;
     const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
-    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
-        hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value, false>), grid,
-                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+    const Layouts lay = L ? *L : Layouts{};
+    return bwd_variant(d, Nq != Nk, L != nullptr, [&](auto dc, auto xc, auto sc) {
+        hipLaunchKernelGGL((bwd_dq_kernel<decltype(dc)::value, decltype(xc)::value, false,
+                                          decltype(sc)::value>),
+                           grid, dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, B, Hq, Hkv,
-                           Nq, Nk, scale, causal, nqt, rope_lb, nullptr, nullptr, nullptr);
+                           Nq, Nk, scale, causal, nqt, rope_lb, nullptr, nullptr, nullptr, lay);
     });
 }
 
 hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, const float *lse,
                            const void *dout, const float *o, const float *dlse, float *Dws,
-                           float *dq, hipStream_t st, double rope_lb)
+                           float *dq, hipStream_t st, double rope_lb, const Layouts *L)
 {
     if (d != 128) return hipErrorInvalidValue;
     const int nqt = (Nq + kQBM - 1) / kQBM;
     const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
-    auto launch = [&](auto xc) {
-        hipLaunchKernelGGL((bwd_dq_kernel<128, decltype(xc)::value, true>), grid, dim3(256), 0, st,
-                           (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, lse,
-                           (const uint16_t *)dout, nullptr, dq, B, Hq, Hkv, Nq, Nk, scale, causal, nqt,
-                           rope_lb, o, dlse, Dws);
-    };
-    if (Nq != Nk) launch(std::true_type{});
-    else launch(std::false_type{});
-    return hipGetLastError();
+    const Layouts lay = L ? *L : Layouts{};
+    return bwd_variant(d, Nq != Nk, L != nullptr, [&](auto, auto xc, auto sc) {
+        hipLaunchKernelGGL((bwd_dq_kernel<128, decltype(xc)::value, true, decltype(sc)::value>), grid,
+                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+                           (const uint16_t *)v, lse, (const uint16_t *)dout, nullptr, dq, B, Hq, Hkv, Nq,
+                           Nk, scale, causal, nqt, rope_lb, o, dlse, Dws, lay);
+    });
 }
 
 namespace {
@@ -983,17 +1327,18 @@ bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, i
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
-                          int hs, hipStream_t st, double rope_lb)
+                          int hs, hipStream_t st, double rope_lb, const Layouts *L)
 {
     BwdPlan plan;
     int nblk = 0;
     if (!bwd_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, plan, &nblk)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nblk);
-    return bwd_variant(d, Nq != Nk, [&](auto dc, auto xc) {
-        hipLaunchKernelGGL((bwd_fused_kernel<decltype(dc)::value, decltype(xc)::value>), grid,
-                           dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
+    const Layouts lay = L ? *L : Layouts{};
+    return bwd_variant(d, Nq != Nk, L != nullptr, [&](auto dc, auto xc, auto sc) {
+        hipLaunchKernelGGL((bwd_fused_kernel<decltype(dc)::value, decltype(xc)::value, decltype(sc)::value>),
+                           grid, dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, Dws, dq, dk, dv, B,
-                           Hq, Hkv, Nq, Nk, scale, causal, hs, plan, rope_lb);
+                           Hq, Hkv, Nq, Nk, scale, causal, hs, plan, rope_lb, lay);
     });
 }
 

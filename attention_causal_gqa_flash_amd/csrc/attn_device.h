@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_launch.h"
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -146,20 +148,25 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // read as zero.  The copy completes asynchronously: wait for vmcnt before the
 // barrier that publishes it.  (The buffer form, unlike global_load_lds, lets
 // the compiler keep partial LDS-read waits while a copy is in flight.)
+// The rows of the tensor in memory lie ld elements apart (ld = D: contiguous
+// rows; a larger ld: a strided layout such as [B][N][H][D]); the LDS tile is
+// always [ROWS][D].
 template <int D, int ROWS, int NW>
 struct TileCopy {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int BLOCKS = ROWS * CPR / 64;
     static constexpr int PER_WAVE = BLOCKS / NW;      // copy instructions per wave
+    static constexpr int RPB = 64 * NW / CPR;         // rows between a wave's blocks
     static_assert(ROWS * CPR % 64 == 0 && BLOCKS % NW == 0, "whole 1 KiB blocks per wave");
-    static_assert((64 * NW / CPR) % 16 == 0, "block stride keeps the swizzle");
+    static_assert(RPB % 16 == 0, "block stride keeps the swizzle");
     int voff;                                         // byte offset of this lane in block `wave`
+    int ld;                                           // elements between rows in memory
 
-    __device__ __forceinline__ TileCopy(int wave, int lane)
+    __device__ __forceinline__ TileCopy(int wave, int lane, int ld_ = D) : ld(ld_)
     {
         const int p = 64 * wave + lane;
         const int row = p / CPR;
-        voff = (row * D + 8 * ((p % CPR) ^ swz<D>(row))) * 2;
+        voff = (row * ld + 8 * ((p % CPR) ^ swz<D>(row))) * 2;
     }
 
     __device__ __forceinline__ void operator()(uint16_t *tile, __amdgpu_buffer_rsrc_t rs, int r0,
@@ -168,9 +175,20 @@ struct TileCopy {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(tile + 512 * (wave + NW * i)), 16, voff,
-                                                     r0 * D * 2 + 1024 * NW * i, 0, 0);
+                                                     (r0 + RPB * i) * ld * 2, 0, 0);
     }
 };
+
+__device__ __host__ __forceinline__ TL contiguous_tl(int H, int N, int D)
+{
+    return TL{(long)H * N * D, (long)N * D, D};
+}
+// Bytes a buffer resource over one head must cover: N rows of D elements, ld apart.
+__device__ __forceinline__ uint32_t head_bytes(int N, int ld, int D, int esz)
+{
+    return (uint32_t)(((long)(N - 1) * ld + D) * esz);
+}
+
 
 
 // One f32 per lane, element r0 + lane of the f32 array behind the resource

@@ -172,12 +172,20 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // key tiles side by side and their softmax states combine through LDS at the
 // end with the associative merge, which halves the longest chain of tiles.
 // OBF: O is written in bf16 (rounded to nearest even) instead of f32.
-template <int D, int KSPLIT, int TN, bool OBF>
+// ROPE: q arrives unrotated; each lane turns its Q row (position i + Nk - Nq)
+// by the rotary angles right after loading it -- the lane already holds both
+// halves (i, i + D/2) of every pair, as chunks ks and ks + KS/2 of its
+// operand -- and writes the rotated row, rounded to bf16, to Qrot (the
+// backward takes it).  rope_lb = log2 of the rotary base.
+// STR: q, k, v and o have the strides of L (else contiguous [B][H][N][D]).
+template <int D, int KSPLIT, int TN, bool OBF, bool ROPE = false, bool STR = false>
 __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, void *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
-    int Hkv, int Nq, int Nk, float scale, int causal, int nqt)
+    int Hkv, int Nq, int Nk, float scale, int causal, int nqt, uint16_t *__restrict__ Qrot,
+    double rope_lb, Layouts L)
 {
+    static_assert(!(ROPE && STR), "the rotated forward takes contiguous tensors");
     constexpr int KS = FwdState<D>::KS, DB = FwdState<D>::DB;
     constexpr int RW = 4 / KSPLIT;           // row waves
     constexpr int BMW = 32 * RW;             // query rows per workgroup
@@ -206,9 +214,11 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // Nq queries against Nk >= Nq keys: query row i sits at key position
     // i + off (the queries are the last Nq positions; off = 0 for self-attention)
     const int off = Nk - Nq;
-    const uint16_t *Qh = Q + ((size_t)b * Hq + h) * (size_t)Nq * D;
-    const uint16_t *Kg = K + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const uint16_t *Vg = V + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const TL lq = STR ? L.q : contiguous_tl(Hq, Nq, D), lo = STR ? L.o : contiguous_tl(Hq, Nq, D);
+    const TL lk = STR ? L.k : contiguous_tl(Hkv, Nk, D), lv = STR ? L.v : contiguous_tl(Hkv, Nk, D);
+    const uint16_t *Qh = Q + b * lq.b + h * lq.h;
+    const uint16_t *Kg = K + b * lk.b + g * lk.h;
+    const uint16_t *Vg = V + b * lv.b + g * lv.h;
 
     // Softmax on c2 q.k with c2 = |scale| log2(e) > 0; a negative scale is
     // carried by negating q, which is exact in bf16.
@@ -223,8 +233,8 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // only after step 0 has read them.
     static_assert(64 * D * sizeof(uint16_t) <= sizeof(sk1), "64 Q rows fit a buffer");
     {
-        const uint32_t q_bytes = (uint32_t)Nq * D * 2;
-        const TileCopy<D, 64, 4> qcopy(wave, lane);
+        const uint32_t q_bytes = head_bytes(Nq, lq.n, D, 2);
+        const TileCopy<D, 64, 4> qcopy(wave, lane, lq.n);
         qcopy(sk1, make_rsrc(Qh, q_bytes), q0, wave);
         if constexpr (BMW > 64) qcopy(sv1, make_rsrc(Qh, q_bytes), q0 + 64, wave);
     }
@@ -236,6 +246,55 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
             uint4 u = *(const uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
             u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
             st.qf[ks] = as_bf16x8(u);
+        }
+    };
+    // ROPE: the tile's Q rows, once in LDS, are turned in place by the lanes
+    // that own them (key half 0 only), one pair of chunks (ks, ks + KS/2) at
+    // a time -- pair i = 16ks + 8hf + e has frequency r^i, r = base^(-2/D):
+    // r^(8hf + 16ks) once per chunk, then steps of r -- and then written out
+    // whole-row by all threads as Qrot.
+    auto rotate_q = [&] {
+        if (kh == 0) {
+            const int qr = rw * 32 + l32;
+            uint16_t *qt = qr < 64 ? sk1 : sv1;
+            const double pos = (double)(qi + off);
+            const double r1 = rope_theta(1, D, rope_lb);
+#pragma unroll 1
+            for (int ks = 0; ks < KS / 2; ++ks) {
+                uint4 *p0 = (uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
+                uint4 *p1 = (uint4 *)tile_chunk<D>(qt, qr & 63, 2 * (ks + KS / 2) + hf);
+                const uint4 a0 = *p0, a1 = *p1;
+                const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
+                uint32_t o0[4], o1[4];
+                double th = rope_theta(16 * ks + 8 * hf, D, rope_lb);
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float y0[2], y1[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh, th *= r1) {
+                        const float x0 = hh ? bf16hi(w0[e2]) : bf16lo(w0[e2]);
+                        const float x1 = hh ? bf16hi(w1[e2]) : bf16lo(w1[e2]);
+                        float sn, cs;
+                        rope_sincos_hw(pos * th, sn, cs);
+                        y0[hh] = x0 * cs - x1 * sn;
+                        y1[hh] = x0 * sn + x1 * cs;
+                    }
+                    o0[e2] = pack_bf16x2(y0[0], y0[1]);
+                    o1[e2] = pack_bf16x2(y1[0], y1[1]);
+                }
+                *p0 = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+                *p1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = D / 8;           // 16-byte chunks per row
+        uint16_t *qrot_h = Qrot + ((size_t)b * Hq + h) * (size_t)Nq * D;
+#pragma unroll 1
+        for (int c = tid; c < BMW * CPR; c += 256) {
+            const int r = c / CPR, ch = c % CPR;
+            if (q0 + r < Nq)
+                *(uint4 *)(qrot_h + (size_t)(q0 + r) * D + 8 * ch) =
+                    *(const uint4 *)tile_chunk<D>(r < 64 ? sk1 : sv1, r & 63, ch);
         }
     };
     st.m_run = -INFINITY;
@@ -263,16 +322,16 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // Tiles move global -> LDS directly (no staging registers); rows past N
     // read as zero, their scores are masked; copies of tiles that do not
     // exist read nothing (zero-byte resources).
-    const uint32_t kv_bytes = (uint32_t)Nk * D * 2;
+    const uint32_t k_bytes = head_bytes(Nk, lk.n, D, 2), v_bytes = head_bytes(Nk, lv.n, D, 2);
     using Copy = TileCopy<D, TN, 4>;
-    const Copy copy(wave, lane);
+    const Copy copy(wave, lane, lk.n), copyv(wave, lane, lv.n);
     auto copy_step = [&](uint16_t *skd, uint16_t *svd, int s_) {
 #pragma unroll
         for (int half = 0; half < KSPLIT; ++half) {
-            const uint32_t nb = valid(half, s_) ? kv_bytes : 0u;
+            const bool ok = valid(half, s_);
             const int t_ = tile_of(half, s_);
-            copy(skd + half * TE, make_rsrc(Kg, nb), t_ * TN, wave);
-            copy(svd + half * TE, make_rsrc(Vg, nb), t_ * TN, wave);
+            copy(skd + half * TE, make_rsrc(Kg, ok ? k_bytes : 0u), t_ * TN, wave);
+            copyv(svd + half * TE, make_rsrc(Vg, ok ? v_bytes : 0u), t_ * TN, wave);
         }
     };
     copy_step(sk0, sv0, 0);
@@ -286,6 +345,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
         if constexpr (BI == 0) {
             if (s_ == 0) {                  // the resident Q rows, then buffer 1 is free
+                if constexpr (ROPE) rotate_q();
                 read_q();
                 __syncthreads();
             }
@@ -343,7 +403,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     const float l_tot = pair32_sum(st.l_sum());
     if (qi < Nq) {
         const float inv = 1.f / l_tot;
-        const size_t orow = (((size_t)b * Hq + h) * Nq + qi) * D;
+        const size_t orow = b * lo.b + h * lo.h + (long)qi * lo.n;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -367,10 +427,10 @@ bool mfma_supported(int dt, int d) { return dt == kBF16 && (d == 64 || d == 128)
 
 namespace {
 
-template <bool OBF>
+template <bool OBF, bool ROPE, bool STR>
 hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, void *o, float *lse,
-                           hipStream_t st)
+                           hipStream_t st, void *q_rot, double rope_lb, const Layouts &L)
 {
     const int cus = device_cus();
     const int nqt = (Nq + kBM - 1) / kBM;
@@ -384,19 +444,20 @@ hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
+    uint16_t *qr = (uint16_t *)q_rot;
     const int nqt64 = (Nq + 63) / 64;
     if (d == 128 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN, OBF>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN, OBF, ROPE, STR>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv,
+                           o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt, qr, rope_lb, L);
     } else if (d == 128) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2, kBN, OBF>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o,
-                           lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 2, kBN, OBF, ROPE, STR>), grid_of(nqt64), dim3(256), 0, st, qq, kk,
+                           vv, o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64, qr, rope_lb, L);
     } else if (d == 64 && !split) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN, OBF>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt);
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN, OBF, ROPE, STR>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv,
+                           o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt, qr, rope_lb, L);
     } else if (d == 64) {
-        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32, OBF>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv, o, lse,
-                           B, Hq, Hkv, Nq, Nk, scale, causal, nqt64);
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32, OBF, ROPE, STR>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv,
+                           o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64, qr, rope_lb, L);
     } else {
         return hipErrorInvalidValue;
     }
@@ -409,8 +470,31 @@ hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, f
                     const void *q, const void *k, const void *v, void *o, float *lse,
                     hipStream_t st, bool o_bf16)
 {
-    if (o_bf16) return fwd_mfma_launch<true>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st);
-    return fwd_mfma_launch<false>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st);
+    const Layouts none{};
+    if (o_bf16)
+        return fwd_mfma_launch<true, false, false>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse,
+                                                   st, nullptr, 0.0, none);
+    return fwd_mfma_launch<false, false, false>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st,
+                                                nullptr, 0.0, none);
+}
+
+hipError_t fwd_mfma_rope_q(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, void *q_rot, float *o,
+                           float *lse, double rope_lb, hipStream_t st)
+{
+    return fwd_mfma_launch<false, true, false>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st,
+                                               q_rot, rope_lb, Layouts{});
+}
+
+hipError_t fwd_mfma_strided(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                            const void *q, const void *k, const void *v, void *o, float *lse,
+                            const Layouts &L, hipStream_t st, bool o_bf16)
+{
+    if (o_bf16)
+        return fwd_mfma_launch<true, false, true>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st,
+                                                  nullptr, 0.0, L);
+    return fwd_mfma_launch<false, false, true>(B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, st,
+                                               nullptr, 0.0, L);
 }
 
 }  // namespace attn

@@ -31,22 +31,23 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
                                                          const T *__restrict__ v,
                                                          OT *__restrict__ o,
                                                          float *__restrict__ lse, int Hq, int Hkv,
-                                                         int Nq, int Nk, float scale, int causal)
+                                                         int Nq, int Nk, float scale, int causal,
+                                                         Layouts L)
 {
     // Nq queries against Nk >= Nq keys; query i sits at key position i + off
     const int i = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = h / (Hq / Hkv);
     const int off = Nk - Nq;
-    const T *qh = q + ((size_t)b * Hq + h) * (size_t)Nq * D;
-    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const T *qh = q + b * L.q.b + h * L.q.h;
+    const T *kg = k + b * L.k.b + g * L.k.h;
+    const T *vg = v + b * L.v.b + g * L.v.h;
     const int row = i < Nq ? i : Nq - 1;
 
     float qr[D], acc[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-        qr[c] = to_f32(qh[(size_t)row * D + c]);
+        qr[c] = to_f32(qh[(size_t)row * L.q.n + c]);
         acc[c] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
@@ -55,7 +56,7 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
     const int wave_end = causal ? min(Nk, (int)(blockIdx.x * 64 + 64) + off) : Nk;
     for (int j = 0; j < wave_end; ++j) {
         if (j >= jend) continue;
-        const T *kj = kg + (size_t)j * D;
+        const T *kj = kg + (size_t)j * L.k.n;
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) s = fmaf(qr[c], to_f32(kj[c]), s);
@@ -69,12 +70,12 @@ __global__ __launch_bounds__(64) void fwd_rowwise_kernel(const T *__restrict__ q
         }
         const float p = expf(s - m);
         l += p;
-        const T *vj = vg + (size_t)j * D;
+        const T *vj = vg + (size_t)j * L.v.n;
 #pragma unroll
         for (int c = 0; c < D; ++c) acc[c] = fmaf(p, to_f32(vj[c]), acc[c]);
     }
     if (i < Nq) {
-        OT *oh = o + (((size_t)b * Hq + h) * Nq + i) * D;
+        OT *oh = o + b * L.o.b + h * L.o.h + (size_t)i * L.o.n;
         const float inv = 1.f / l;
 #pragma unroll
         for (int c = 0; c < D; ++c) put(oh + c, acc[c] * inv);
@@ -102,13 +103,16 @@ __global__ __launch_bounds__(256) void zero_fill2_kernel(float *__restrict__ a, 
     zero2_grid_stride(a, b, n);
 }
 
+// Row r of the B*Hq*N rows is query row r % N of head (r / N) % Hq of batch
+// r / (Hq N); dout and o have the strides of L.dout and L.o.
 template <typename T, int D, typename OT>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout,
                                                       const OT *__restrict__ o,
                                                       float *__restrict__ Dws, long rows,
                                                       float *__restrict__ zero,
                                                       float *__restrict__ zero2, long zero_len,
-                                                      const float *__restrict__ dlse)
+                                                      const float *__restrict__ dlse, int Hq, int N,
+                                                      Layouts L)
 {
     if (zero != nullptr) zero2_grid_stride(zero, zero2, zero_len);
     constexpr int LPR = D / 8;              // lanes per row
@@ -117,7 +121,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
     const int part = threadIdx.x % LPR;
     float s = 0.f;
     if (row < rows) {
-        const size_t base = (size_t)row * D + part * 8;
+        const long bh = row / N, bb = bh / Hq, hh = bh % Hq, ii = row % N;
+        const size_t base = bb * L.o.b + hh * L.o.h + ii * L.o.n + part * 8;
+        const size_t dbase = bb * L.dout.b + hh * L.dout.h + ii * L.dout.n + part * 8;
         float4 o0, o1;
         if constexpr (sizeof(OT) == 2) {
             const uint4 u = *(const uint4 *)((const uint16_t *)o + base);
@@ -129,12 +135,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T *__restrict__ dout
         }
         float dv[8];
         if constexpr (sizeof(T) == 2) {
-            const uint4 u = *(const uint4 *)((const uint16_t *)dout + base);
+            const uint4 u = *(const uint4 *)((const uint16_t *)dout + dbase);
             dv[0] = bf16lo(u.x); dv[1] = bf16hi(u.x); dv[2] = bf16lo(u.y); dv[3] = bf16hi(u.y);
             dv[4] = bf16lo(u.z); dv[5] = bf16hi(u.z); dv[6] = bf16lo(u.w); dv[7] = bf16hi(u.w);
         } else {
-            const float4 a = *(const float4 *)((const float *)dout + base);
-            const float4 c = *(const float4 *)((const float *)dout + base + 4);
+            const float4 a = *(const float4 *)((const float *)dout + dbase);
+            const float4 c = *(const float4 *)((const float *)dout + dbase + 4);
             dv[0] = a.x; dv[1] = a.y; dv[2] = a.z; dv[3] = a.w;
             dv[4] = c.x; dv[5] = c.y; dv[6] = c.z; dv[7] = c.w;
         }
@@ -155,45 +161,47 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void bwd_dq_rowwise_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
-    float *__restrict__ dq, int Hq, int Hkv, int Nq, int Nk, float scale, int causal)
+    float *__restrict__ dq, int Hq, int Hkv, int Nq, int Nk, float scale, int causal, Layouts L)
 {
     const int i = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = h / (Hq / Hkv);
     const int off = Nk - Nq;
-    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
-    const T *kg = k + ((size_t)b * Hkv + g) * (size_t)Nk * D;
-    const T *vg = v + ((size_t)b * Hkv + g) * (size_t)Nk * D;
+    const size_t qrow0 = ((size_t)b * Hq + h) * Nq;     // rows of lse and D
+    const T *kg = k + b * L.k.b + g * L.k.h;
+    const T *vg = v + b * L.v.b + g * L.v.h;
     const int row = i < Nq ? i : Nq - 1;
+    const T *qrw = q + b * L.q.b + h * L.q.h + (size_t)row * L.q.n;
+    const T *drw = dout + b * L.dout.b + h * L.dout.h + (size_t)row * L.dout.n;
 
     float qr[D], dor[D], acc[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-        qr[c] = to_f32(q[(qrow0 + row) * D + c]);
-        dor[c] = to_f32(dout[(qrow0 + row) * D + c]);
+        qr[c] = to_f32(qrw[c]);
+        dor[c] = to_f32(drw[c]);
         acc[c] = 0.f;
     }
-    const float L = lse[qrow0 + row], Di = Dws[qrow0 + row];
+    const float Li = lse[qrow0 + row], Di = Dws[qrow0 + row];
     const int jend = causal ? min(row + 1 + off, Nk) : Nk;
     const int wave_end = causal ? min(Nk, (int)(blockIdx.x * 64 + 64) + off) : Nk;
     for (int j = 0; j < wave_end; ++j) {
         if (j >= jend) continue;
-        const T *kj = kg + (size_t)j * D;
-        const T *vj = vg + (size_t)j * D;
+        const T *kj = kg + (size_t)j * L.k.n;
+        const T *vj = vg + (size_t)j * L.v.n;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
             s = fmaf(qr[c], to_f32(kj[c]), s);
             dp = fmaf(dor[c], to_f32(vj[c]), dp);
         }
-        const float p = expf(s * scale - L);
+        const float p = expf(s * scale - Li);
         const float ds = p * (dp - Di);
 #pragma unroll
         for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, to_f32(kj[c]), acc[c]);
     }
     if (i < Nq) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) dq[(qrow0 + i) * D + c] = acc[c] * scale;
+        for (int c = 0; c < D; ++c) dq[b * L.dq.b + h * L.dq.h + (size_t)i * L.dq.n + c] = acc[c] * scale;
     }
 }
 
@@ -207,20 +215,21 @@ __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ lse, const T *__restrict__ dout, const float *__restrict__ Dws,
     float *__restrict__ dk, float *__restrict__ dv, int Hq, int Hkv, int Nq, int Nk, float scale,
-    int causal)
+    int causal, Layouts L)
 {
     const int j = blockIdx.x * 64 + threadIdx.x;
     const int g = blockIdx.y, b = blockIdx.z;
     const int G = Hq / Hkv;
     const int off = Nk - Nq;
-    const size_t krow0 = ((size_t)b * Hkv + g) * Nk;
     const int row = j < Nk ? j : Nk - 1;
+    const T *krw = k + b * L.k.b + g * L.k.h + (size_t)row * L.k.n;
+    const T *vrw = v + b * L.v.b + g * L.v.h + (size_t)row * L.v.n;
 
     float kr[D], vr[D], dka[D], dva[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
-        kr[c] = to_f32(k[(krow0 + row) * D + c]);
-        vr[c] = to_f32(v[(krow0 + row) * D + c]);
+        kr[c] = to_f32(krw[c]);
+        vr[c] = to_f32(vrw[c]);
         dka[c] = 0.f;
         dva[c] = 0.f;
     }
@@ -228,11 +237,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
     const int wave_start = causal ? max((int)(blockIdx.x * 64) - off, 0) : 0;
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
-        const size_t qrow0 = ((size_t)b * Hq + h) * Nq;
+        const size_t qrow0 = ((size_t)b * Hq + h) * Nq;   // rows of lse and D
         for (int i = wave_start; i < Nq; ++i) {
             if (i < istart) continue;
-            const T *qi = q + (qrow0 + i) * D;
-            const T *di = dout + (qrow0 + i) * D;
+            const T *qi = q + b * L.q.b + h * L.q.h + (size_t)i * L.q.n;
+            const T *di = dout + b * L.dout.b + h * L.dout.h + (size_t)i * L.dout.n;
             float s = 0.f, dp = 0.f;
 #pragma unroll
             for (int c = 0; c < D; ++c) {
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(64) void bwd_dkdv_colwise_kernel(
     if (j < Nk) {
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-            dk[(krow0 + j) * D + c] = dka[c] * scale;
-            dv[(krow0 + j) * D + c] = dva[c];
+            dk[b * L.dk.b + g * L.dk.h + (size_t)j * L.dk.n + c] = dka[c] * scale;
+            dv[b * L.dv.b + g * L.dv.h + (size_t)j * L.dv.n + c] = dva[c];
         }
     }
 }
@@ -498,41 +507,44 @@ __global__ __launch_bounds__(128) void lse_merge_small_kernel(const float *__res
 
 hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                        float scale, const void *q, const void *k, const void *v, void *o,
-                       float *lse, hipStream_t st, bool o_bf16)
+                       float *lse, hipStream_t st, bool o_bf16, const Layouts *L)
 {
+    const Layouts lay = L ? *L : contiguous_layouts(Hq, Hkv, Nq, Nk, d);
     dim3 grid((Nq + 63) / 64, Hq, B);
     if (o_bf16) {
         ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, bf16_t>), grid,
                                                                   dim3(64), 0, st, (const T *)q,
                                                                   (const T *)k, (const T *)v,
                                                                   (bf16_t *)o, lse, Hq, Hkv, Nq, Nk,
-                                                                  scale, causal)));
+                                                                  scale, causal, lay)));
     } else {
         ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((fwd_rowwise_kernel<T, D, float>), grid,
                                                                   dim3(64), 0, st, (const T *)q,
                                                                   (const T *)k, (const T *)v,
                                                                   (float *)o, lse, Hq, Hkv, Nq, Nk,
-                                                                  scale, causal)));
+                                                                  scale, causal, lay)));
     }
     return hipGetLastError();
 }
 
-hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const void *o, float *Dws,
-                          float *zero, float *zero2, long zero_len, const float *dlse,
-                          hipStream_t st, bool o_bf16)
+hipError_t bwd_preprocess(int dt, int B, int Hq, int N, int d, const void *dout, const void *o,
+                          float *Dws, float *zero, float *zero2, long zero_len, const float *dlse,
+                          hipStream_t st, bool o_bf16, const Layouts *L)
 {
+    const Layouts lay = L ? *L : contiguous_layouts(Hq, Hq, N, N, d);
+    const long rows = (long)B * Hq * N;
     const int rpb = 256 / (d / 8);
     dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     if (o_bf16) {
         ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D, bf16_t>), grid,
                                                                   dim3(256), 0, st, (const T *)dout,
                                                                   (const bf16_t *)o, Dws, rows, zero,
-                                                                  zero2, zero_len, dlse)));
+                                                                  zero2, zero_len, dlse, Hq, N, lay)));
     } else {
         ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL((bwd_pre_kernel<T, D, float>), grid,
                                                                   dim3(256), 0, st, (const T *)dout,
                                                                   (const float *)o, Dws, rows, zero,
-                                                                  zero2, zero_len, dlse)));
+                                                                  zero2, zero_len, dlse, Hq, N, lay)));
     }
     return hipGetLastError();
 }
@@ -548,28 +560,30 @@ hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st)
 hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                           float scale, const void *q, const void *k, const void *v,
                           const float *lse, const void *dout, const float *Dws, float *dq,
-                          hipStream_t st)
+                          hipStream_t st, const Layouts *L)
 {
+    const Layouts lay = L ? *L : contiguous_layouts(Hq, Hkv, Nq, Nk, d);
     dim3 grid((Nq + 63) / 64, Hq, B);
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
                                                (bwd_dq_rowwise_kernel<T, D>), grid, dim3(64), 0,
                                                st, (const T *)q, (const T *)k, (const T *)v, lse,
                                                (const T *)dout, Dws, dq, Hq, Hkv, Nq, Nk,
-                                               scale, causal)));
+                                               scale, causal, lay)));
     return hipGetLastError();
 }
 
 hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                             float scale, const void *q, const void *k, const void *v,
                             const float *lse, const void *dout, const float *Dws, float *dk,
-                            float *dv, hipStream_t st)
+                            float *dv, hipStream_t st, const Layouts *L)
 {
+    const Layouts lay = L ? *L : contiguous_layouts(Hq, Hkv, Nq, Nk, d);
     dim3 grid((Nk + 63) / 64, Hkv, B);
     ATTN_DISPATCH_T(dt, ATTN_DISPATCH_D(d, hipLaunchKernelGGL(
                                                (bwd_dkdv_colwise_kernel<T, D>), grid, dim3(64), 0,
                                                st, (const T *)q, (const T *)k, (const T *)v, lse,
                                                (const T *)dout, Dws, dk, dv, Hq, Hkv, Nq, Nk,
-                                               scale, causal)));
+                                               scale, causal, lay)));
     return hipGetLastError();
 }
 

@@ -11,28 +11,51 @@ namespace attn {
 
 enum Dtype { kF32 = 0, kBF16 = 1 };
 
+// Element strides of a [B][H][N][D] tensor whose head dim is contiguous:
+// element (b, h, n, c) sits at b*b + h*h + n*n + c (contiguous: n = D,
+// h = N*D, b = H*N*D).
+struct TL {
+    long b, h;
+    int n;
+};
+
+// The strides of every 4-D tensor of a call (a kernel argument; launchers
+// take a pointer to one, null for contiguous tensors).
+struct Layouts {
+    TL q, k, v, o, dout, dq, dk, dv;
+};
+
+// Contiguous [B][H][N][d] tensors: q, o, dout, dq of Hq heads and Nq rows;
+// k, v, dk, dv of Hkv heads and Nk rows.
+inline Layouts contiguous_layouts(int Hq, int Hkv, int Nq, int Nk, int d)
+{
+    const TL a{(long)Hq * Nq * d, (long)Nq * d, d}, b{(long)Hkv * Nk * d, (long)Nk * d, d};
+    return Layouts{a, b, b, a, a, a, b, b};
+}
+
 // Generic kernels: any supported (dtype, d); one thread per query row or key row.
 // Forward of Nq queries against Nk >= Nq keys (query i at key position i + Nk - Nq);
 // o is f32, or bf16 with o_bf16.
 hipError_t fwd_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                        float scale, const void *q, const void *k, const void *v, void *o,
-                       float *lse, hipStream_t st, bool o_bf16 = false);
+                       float *lse, hipStream_t st, bool o_bf16 = false, const Layouts *L = nullptr);
 // The backward launchers take Nq query rows against Nk >= Nq keys in the same
 // alignment (Nq == Nk: the square case).
 hipError_t bwd_dq_rowwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                           float scale, const void *q, const void *k, const void *v,
                           const float *lse, const void *dout, const float *Dws, float *dq,
-                          hipStream_t st);
+                          hipStream_t st, const Layouts *L = nullptr);
 hipError_t bwd_dkdv_colwise(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                             float scale, const void *q, const void *k, const void *v,
                             const float *lse, const void *dout, const float *Dws, float *dk,
-                            float *dv, hipStream_t st);
+                            float *dv, hipStream_t st, const Layouts *L = nullptr);
 
-// D_i = dout_i . o_i for every query row (rows = B*Hq*N).  With zero != nullptr
-// the same launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
-hipError_t bwd_preprocess(int dt, long rows, int d, const void *dout, const void *o, float *Dws,
-                          float *zero, float *zero2, long zero_len, const float *dlse,
-                          hipStream_t st, bool o_bf16 = false);
+// D_i = dout_i . o_i for every query row (B*Hq*N rows; dout and o contiguous,
+// or of the strides of L->dout and L->o).  With zero != nullptr the same
+// launch also zero-fills `zero_len` floats at `zero` and at `zero2`.
+hipError_t bwd_preprocess(int dt, int B, int Hq, int N, int d, const void *dout, const void *o,
+                          float *Dws, float *zero, float *zero2, long zero_len, const float *dlse,
+                          hipStream_t st, bool o_bf16 = false, const Layouts *L = nullptr);
 // Rotary positions on `rows` rows of d elements of dtype dt, row r at position
 // pos0 + r % N (inverse: the transposed rotation); x and y may alias.
 hipError_t rope(int dt, long rows, int N, int d, long pos0, double base, int inverse, const void *x,
@@ -56,6 +79,16 @@ bool mfma_supported(int dt, int d);
 hipError_t fwd_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                     const void *q, const void *k, const void *v, void *o, float *lse,
                     hipStream_t st, bool o_bf16 = false);
+// The forward over tensors of any strides (L: every 4-D tensor's strides).
+hipError_t fwd_mfma_strided(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                            const void *q, const void *k, const void *v, void *o, float *lse,
+                            const Layouts &L, hipStream_t st, bool o_bf16);
+// The forward over rotated queries: q unrotated, each lane rotating its row
+// in the prologue (hardware sine and cosine of the angle reduced in double)
+// and writing it to q_rot (bf16); k must already be rotated.
+hipError_t fwd_mfma_rope_q(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                           const void *q, const void *k, const void *v, void *q_rot, float *o,
+                           float *lse, double rope_lb, hipStream_t st);
 // Number of workgroups each group's query heads are split over by the dK/dV
 // kernel; with more than one, dk and dv must be zero-filled before the launch
 // (the kernel adds into them).
@@ -63,17 +96,17 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk);
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
-                         hipStream_t st, double rope_lb = 0.0);
+                         hipStream_t st, double rope_lb = 0.0, const Layouts *L = nullptr);
 hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                        const void *q, const void *k, const void *v, const float *lse,
                        const void *dout, const float *Dws, float *dq, hipStream_t st,
-                       double rope_lb = 0.0);
+                       double rope_lb = 0.0, const Layouts *L = nullptr);
 // dQ that also computes D_i = dO_i . O_i - dlse_i (O f32, dlse optional) into
 // Dws for a dK/dV kernel launched after it (bf16, d = 128)
 hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, const float *lse,
                            const void *dout, const float *o, const float *dlse, float *Dws,
-                           float *dq, hipStream_t st, double rope_lb);
+                           float *dq, hipStream_t st, double rope_lb, const Layouts *L = nullptr);
 // Whether the one-launch plan of a shape fits its kernel argument (at most
 // 48 block groups); writes the group and block counts.  No device work.
 bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *groups,
@@ -83,7 +116,7 @@ bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, i
 hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           const void *q, const void *k, const void *v, const float *lse,
                           const void *dout, const float *Dws, float *dq, float *dk, float *dv,
-                          int hs, hipStream_t st, double rope_lb = 0.0);
+                          int hs, hipStream_t st, double rope_lb = 0.0, const Layouts *L = nullptr);
 
 // Split-KV decode and the log-sum-exp merge.
 hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,

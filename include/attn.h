@@ -216,6 +216,55 @@ attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, 
                         size_t workspace_bytes, void *stream);
 
 /*
+ * Strides of a 4-D tensor [B][H][N][d] whose head dim is contiguous, in
+ * elements: element (b, h, n, c) sits at b*batch + h*head + n*row + c.  The
+ * contiguous layout is {H*N*d, N*d, d}; interleaved heads ([B][N][H][d], as
+ * a fused projection writes them) are {N*H*d, d, H*d}.  Every stride must be
+ * positive, row >= d and at most 2^31 - 1, and each a multiple of 16 bytes of
+ * the tensor's element size (so every row starts 16-byte aligned).  Tensors
+ * the call writes must not overlap one another or the inputs.
+ */
+typedef struct {
+    long long batch;
+    long long head;
+    long long row;
+} attn_layout;
+
+/*
+ * attn_fwd_strided -- attn_fwd_ex over tensors of any strides: each of q, k,
+ *   v, o comes with its attn_layout (NULL: contiguous).  lse stays contiguous
+ *   [B][Hq][Nq] f32.  The matrix-core kernels read the strided rows directly
+ *   (one buffer resource per head, its row stride in the tile copies), as
+ *   long as each bf16 head spans less than 2^31 bytes; otherwise the generic
+ *   kernels run.  A layout that breaks the rules above: ATTN_ERR_INVALID_ARG.
+ *   "RustingBrain" docs, "Generating text": caches and activations are read
+ *   where the caller keeps them.  Other arguments, checks and launches as
+ *   attn_fwd_ex.
+ */
+attn_status attn_fwd_strided(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, float scale, const void *q, const attn_layout *lq,
+                             const void *k, const attn_layout *lk, const void *v,
+                             const attn_layout *lv, void *o, const attn_layout *lo, float *lse,
+                             void *stream);
+
+/*
+ * attn_bwd_strided -- attn_bwd_ex over tensors of any strides: q, k, v, o,
+ *   dout, dq, dk, dv each with its attn_layout (NULL: contiguous); lse, dlse
+ *   and the workspace stay contiguous.  dk and dv are written with plain
+ *   stores (the query heads of a group are never split over workgroups, which
+ *   would need a zero-fill that follows their strides).  Other arguments,
+ *   checks and launches as attn_bwd_ex.
+ */
+attn_status attn_bwd_strided(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, float scale, const void *q, const attn_layout *lq,
+                             const void *k, const attn_layout *lk, const void *v,
+                             const attn_layout *lv, const void *o, const attn_layout *lo,
+                             const float *lse, const void *dout, const attn_layout *ldout,
+                             const float *dlse, float *dq, const attn_layout *ldq, float *dk,
+                             const attn_layout *ldk, float *dv, const attn_layout *ldv,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * attn_rope -- rotary positions on rows: x, y [B][H][N][d] of dtype dt, row n
  *   of each head at position pos0 + n.  For pair i in [0, d/2),
  *   theta_i = base^(-2i/d), a = position * theta_i:
@@ -240,8 +289,13 @@ attn_status attn_rope(attn_dtype dt, int B, int H, int N, int d, long long pos0,
  *   the forward on (q_rot, k_rot, v).  q_rot [B][Hq][Nq][d] and k_rot
  *   [B][Hkv][Nk][d] (dtype dt, caller-owned, may alias q and k) receive the
  *   rotated inputs: attn_bwd_rope takes them, and k_rot is what a key cache
- *   holds.  Two launches on `stream` (the rotation of q and k, the
- *   forward).  Other arguments and checks as attn_fwd_kv and attn_rope.
+ *   holds.  Two launches on `stream`.  On the bf16 matrix-core path (q_rot
+ *   not aliasing q): one pass rotates k, and the forward rotates each query
+ *   row as it loads it (hardware sine and cosine of the angle reduced in
+ *   double, about 1e-6, rounded to bf16: q_rot is within one bf16 unit in the
+ *   last place of attn_rope's) and writes q_rot.  Otherwise one pass rotates
+ *   q and k (as attn_rope) before the forward.  Other arguments and checks as
+ *   attn_fwd_kv and attn_rope.
  */
 attn_status attn_fwd_rope(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                           float scale, double base, const void *q, const void *k, const void *v,

@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
                      "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_plan", "attn_decode", "attn_decode_append",
-                     "attn_lse_merge",
+                     "attn_lse_merge", "attn_fwd_strided", "attn_bwd_strided",
+                     "attn_bwd_noalloc", "attn_read_probe",
                      "attn_status_str", "attn_abi_version"):
         assert required in names
 
@@ -350,3 +351,35 @@ def test_decode_merged_refusals(L):
     assert L.attn_decode_merged(1, 1, 34, 8, 4096, 128, 0.088, 16, *([P] * 7), NUL) == INVALID
     assert L.attn_decode_merged(*args, *([P] * 6), MIS, NUL) == INVALID
     assert L.attn_decode_merged(*args, NUL, *([P] * 6), NUL) == INVALID
+
+
+_Layout = attn.AttnLayout
+
+
+@pytest.mark.parametrize("lay", [
+    (0, 64, 64), (4096, 0, 64), (4096, 64, 32),          # non-positive strides, a row shorter than d
+    (4096, 64, 68), (4100, 64, 64), (4096, 68, 64),       # bf16 strides not a multiple of 16 bytes
+    (1 << 40, 64, 1 << 31),                               # a row stride past 2^31 - 1
+])
+def test_strided_refuses_bad_layouts(L, lay):
+    bad = _Layout(*lay)
+    rc = L.attn_fwd_strided(1, 0, 1, 4, 2, 64, 64, 64, 1, 0.125, P, ctypes.byref(bad), P, None, P, None,
+                            P, None, P, NUL)
+    assert rc == INVALID
+    # the same layout on dout (bf16, the rules of the input dtype)
+    rc = L.attn_bwd_strided(1, 0, 1, 4, 2, 64, 64, 64, 1, 0.125, P, None, P, None, P, None, P, None, P,
+                            P, ctypes.byref(bad), None, P, None, P, None, P, None, P, 1 << 20, NUL)
+    assert rc == INVALID
+
+
+def test_strided_refusals_like_the_contiguous_forms(L):
+    ok = _Layout(64 * 8 * 64, 64, 8 * 64)
+    # Nk < Nq, a bad output dtype, a misaligned pointer: refused before the layouts matter
+    assert L.attn_fwd_strided(1, 0, 1, 4, 2, 64, 32, 64, 1, 0.125, P, ctypes.byref(ok), P, None, P, None,
+                              P, None, P, NUL) == INVALID
+    assert L.attn_fwd_strided(1, 5, 1, 4, 2, 64, 64, 64, 1, 0.125, P, None, P, None, P, None, P, None,
+                              P, NUL) == INVALID
+    assert L.attn_fwd_strided(1, 0, 1, 4, 2, 64, 64, 64, 1, 0.125, MIS, None, P, None, P, None, P, None,
+                              P, NUL) == INVALID
+    assert L.attn_bwd_strided(1, 0, 1, 4, 2, 64, 64, 64, 1, 0.125, P, None, P, None, P, None, P, None, P,
+                              P, None, None, P, None, P, None, P, None, P, 8, NUL) == WORKSPACE

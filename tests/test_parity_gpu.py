@@ -415,6 +415,8 @@ def test_rope(B, H, N, d, pos0, base, dtype):
 
 ATTN_ROPE = [
     (2, 8, 2, 300, 300, 128, True, "bf16", False),
+    (2, 32, 8, 512, 512, 128, True, "bf16", False),   # 128-row forward tiles (no key split)
+    (4, 16, 4, 1024, 1024, 64, True, "bf16", False),  # the same at d = 64
     (4, 12, 4, 256, 1024, 64, True, "bf16", True),    # chunk against a cache, with dlse
     (1, 4, 2, 100, 200, 64, False, "bf16", False),
     (1, 2, 1, 20, 50, 16, True, "f32", False),        # generic kernels
@@ -440,9 +442,21 @@ def test_attn_rope(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
     dq, dk, dv = attn.attn_bwd_rope(q_rot, k_rot, gv, o, lse, gdo, causal, scale, base,
                                     dlse=None if dl is None else torch.from_numpy(dl).cuda())
     torch.cuda.synchronize()
-    # the rotated inputs are attn_rope's
-    assert torch.equal(q_rot, attn.attn_rope(gq, Nk - Nq, base))
+    # the rotated inputs are attn_rope's: k bit for bit; q, which the bf16 forward rotates
+    # in its prologue on the hardware sine and cosine (about 1e-6 of the pair's size, where
+    # attn_rope's library sine and cosine are exact to f32), rounds to the same bf16 value
+    # except near rounding midpoints (one unit in the last place) and near zero (the
+    # sine and cosine error, at most 3e-5 for these N(0, 1) pairs)
     assert torch.equal(k_rot, attn.attn_rope(gk, 0, base))
+    ref_q = attn.attn_rope(gq, Nk - Nq, base)
+    if dtype == "f32":
+        assert torch.equal(q_rot, ref_q)
+    else:
+        a, r = q_rot.float(), ref_q.float()
+        _, ex = torch.frexp(r)                                 # |r| in [2^(ex-1), 2^ex)
+        ulp = torch.ldexp(torch.ones_like(r), torch.clamp(ex - 8, min=-133))
+        assert bool(((a - r).abs() <= ulp + 3e-5).all())
+        assert float((a != r).float().mean()) < 0.01
     got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
     dl64 = None if dl is None else dl.astype(np.float64)
     if dtype == "f32":
@@ -771,3 +785,93 @@ def test_capture_as_first_call_in_fresh_process():
     r = subprocess.run([sys.executable, "-c", _FRESH_CAPTURE, root], capture_output=True,
                        text=True, timeout=240)
     assert r.returncode == 0 and "fresh-process capture ok" in r.stdout, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------
+# strided layouts: q, k, v in one fused [B][N][Hq + 2 Hkv][d] projection buffer
+# (interleaved heads), o, dout, dq, dk, dv as views of buffers of their own
+# ---------------------------------------------------------------------------
+
+STRIDED = [
+    # B, Hq, Hkv, Nq, Nk, d, causal, dtype, o_dtype, with_dlse
+    (2, 8, 2, 300, 300, 128, True, "bf16", "f32", False),    # d = 128: dQ with row terms, paired dK/dV
+    (1, 32, 8, 512, 512, 128, True, "bf16", "f32", True),
+    (2, 12, 4, 333, 333, 64, True, "bf16", "f32", False),     # d = 64: one-launch gradients
+    (1, 8, 2, 200, 700, 64, True, "bf16", "bf16", True),      # chunk against a cache, bf16 o
+    (1, 4, 2, 100, 257, 128, False, "bf16", "bf16", False),
+    (1, 4, 2, 65, 65, 32, True, "f32", "f32", True),          # generic kernels
+    (2, 2, 1, 40, 90, 16, True, "f32", "f32", False),
+]
+
+
+def _fused_views(x, B, Hq, Hkv, Nq, Nk, d, dtype):
+    """q, k, v as strided views of one [B][N][Hq + 2 Hkv][d] buffer (q in its last Nq rows)."""
+    H3 = Hq + 2 * Hkv
+    buf = torch.zeros((B, Nk, H3, d), dtype=dtype, device="cuda")
+    buf[:, :, :Hq] = torch.from_numpy(np.ascontiguousarray(x["q"].transpose(0, 2, 1, 3))).to(dtype).cuda()
+    buf[:, :, Hq:Hq + Hkv] = torch.from_numpy(np.ascontiguousarray(x["k"].transpose(0, 2, 1, 3))).to(dtype).cuda()
+    buf[:, :, Hq + Hkv:] = torch.from_numpy(np.ascontiguousarray(x["v"].transpose(0, 2, 1, 3))).to(dtype).cuda()
+    q = buf[:, Nk - Nq:, :Hq].transpose(1, 2)
+    k = buf[:, :, Hq:Hq + Hkv].transpose(1, 2)
+    v = buf[:, :, Hq + Hkv:].transpose(1, 2)
+    return buf, q, k, v
+
+
+def _interleaved(B, H, N, d, dtype, fill):
+    """A [B][H][N][d] view of a [B][N][H + 1][d] buffer filled with `fill` (one spare head per
+    row, so that writes outside the view would show)."""
+    buf = torch.full((B, N, H + 1, d), fill, dtype=dtype, device="cuda")
+    return buf, buf[:, :, :H].transpose(1, 2)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype,o_dtype,with_dlse", STRIDED,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}"
+                              f"_{c[7]}_o{c[8]}{'_dlse' if c[9] else ''}" for c in STRIDED])
+def test_strided_layouts(B, Hq, Hkv, Nq, Nk, d, causal, dtype, o_dtype, with_dlse):
+    print(f"\n[case] strided B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} {dtype} "
+          f"o={o_dtype} dlse={with_dlse}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    odt = torch.bfloat16 if o_dtype == "bf16" else torch.float32
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=11 * Nq + Nk + d, dout_scale=0.1)
+    qn = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    don = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    scale = float(np.float32(d ** -0.5))
+    _, q, k, v = _fused_views(x, B, Hq, Hkv, Nq, Nk, d, tdt)
+    assert not q.is_contiguous() and q.stride(3) == 1
+    obuf, o = _interleaved(B, Hq, Nq, d, odt, 7.0)
+    o, lse = attn.attn_fwd_strided(q, k, v, causal, scale, o=o)
+    dobuf, dout = _interleaved(B, Hq, Nq, d, tdt, 0.0)
+    dout.copy_(torch.from_numpy(don).to(tdt).cuda())
+    dl = (torch.from_numpy(np.random.default_rng(Nq).standard_normal((B, Hq, Nq)).astype(np.float32) * 0.3).cuda()
+          if with_dlse else None)
+    bufs = [_interleaved(B, Hq, Nq, d, torch.float32, 7.0), _interleaved(B, Hkv, Nk, d, torch.float32, 7.0),
+            _interleaved(B, Hkv, Nk, d, torch.float32, 7.0)]
+    dq, dk, dv = attn.attn_bwd_strided(q, k, v, o, lse, dout, causal, scale, dq=bufs[0][1], dk=bufs[1][1],
+                                       dv=bufs[2][1], dlse=dl)
+    torch.cuda.synchronize()
+    # nothing outside the views was written (the spare head of every row keeps its fill)
+    for buf in (obuf, bufs[0][0], bufs[1][0], bufs[2][0]):
+        assert bool((buf[:, :, -1] == 7.0).all())
+    # the same kernels on contiguous copies: o, lse and dq bit for bit (dk, dv may take
+    # atomics there, so to their last bits)
+    gq, gk, gv, gdo = (t.contiguous() for t in (q, k, v, dout))
+    o2, lse2 = attn.attn_fwd_ex(gq, gk, gv, causal, scale, o_dtype=odt)
+    dq2, dk2, dv2 = attn.attn_bwd_ex(gq, gk, gv, o2, lse2, gdo, causal, scale, dlse=dl)
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o2) and torch.equal(lse, lse2)
+    assert torch.equal(dq.contiguous(), dq2)
+    for a, b in ((dk, dk2), (dv, dv2)):
+        assert torch.allclose(a.contiguous(), b, rtol=0, atol=1e-5 * float(b.abs().max()))
+    # and the oracle's tolerances
+    got = [t.contiguous().float().cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    ro, rl = oracle.attn_fwd(qn, x["k"], x["v"], causal, scale)
+    if dl is None:
+        rdq, rdk, rdv = oracle.attn_bwd(qn, x["k"], x["v"], don, causal, scale)
+    else:
+        rdq, rdk, rdv = oracle.attn_bwd_dlse(qn, x["k"], x["v"], don, dl.cpu().numpy().astype(np.float64),
+                                             causal, scale)
+    if o_dtype == "bf16":
+        # o rounded to bf16: half a unit in the last place (2^-9 relative) on top of the bound
+        assert float(np.abs(got[0] - ro).max()) <= 1e-2 + 2.0 ** -9 * float(np.abs(ro).max())
+        got[0] = ro
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"strided Nq{Nq} Nk{Nk} d{d}")
