@@ -107,7 +107,7 @@ int dkdv_split(int dt, int B, int Hq, int Hkv, int Nk, int d, float scale,
                const attn::Layouts *L = nullptr)
 {
     // strided dk / dv take no atomics (a zero-fill would have to follow their strides)
-    return use_mfma(dt, Nk, d, scale) && L == nullptr ? attn::dkdv_head_split(B, Hq, Hkv, Nk) : 1;
+    return use_mfma(dt, Nk, d, scale) && L == nullptr ? attn::dkdv_head_split(B, Hq, Hkv, Nk, d) : 1;
 }
 
 // dk and dv must already be zero when hs > 1.

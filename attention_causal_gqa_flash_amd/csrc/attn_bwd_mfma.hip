@@ -580,17 +580,24 @@ __device__ __forceinline__ void dkdv_pair_body(
             else load_step(s + 1, q1s, d1s);
         }
         const int qs = (qt0 + s % nq) * SR;
+        // Phase 1 of both sub-steps, then one barrier, then phase 2 of both:
+        // while role P works through a sub-step's softmax, role G (on the
+        // same SIMD) issues the score MFMAs of the next one, and role G's dS
+        // arithmetic overlaps role P's dV MFMAs.
+        bool active[kKvSub];
+        f32x16 acc1[kKvSub];                 // role G: dP - D of each sub-step
+        bf16x8 pk[kKvSub][2];                // role P: P of each sub-step as bf16 operands
 #pragma unroll
         for (int sub = 0; sub < kKvSub; ++sub) {
             const int q0 = qs + sub * kKvBM;
             const int qb0 = q0 + 32 * qh;
-            const bool active = qb0 < Nq && k0 + 32 * kb < Nk && (!causal || qb0 + 31 + off >= k0 + 32 * kb);
+            active[sub] = qb0 < Nq && k0 + 32 * kb < Nk && (!causal || qb0 + 31 + off >= k0 + 32 * kb);
             const bool mask = causal && qb0 + off < k0 + 32 * kb + 32;
             const uint16_t *qt = qc + sub * kKvBM * D, *dt = dc + sub * kKvBM * D;
             uint4 *pb = lds.pbuf + (sub * 4 + pair) * 128;
-            f32x16 sacc;
-            if (active) {
+            if (active[sub]) {
                 // phase 1: S (role P) or dP (role G) from the row term up
+                f32x16 sacc;
                 const float *rt = role_p ? lc + sub * kKvBM : ec + sub * kKvBM;
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
@@ -614,41 +621,50 @@ __device__ __forceinline__ void dkdv_pair_body(
                             sacc[r] = c >= t ? sacc[r] : 0.f;
                         }
                     }
-                    pb[lane] = __builtin_bit_cast(uint4, pack_operand<0>(sacc));
-                    pb[64 + lane] = __builtin_bit_cast(uint4, pack_operand<8>(sacc));
-                }
-            }
-            __syncthreads();                // P of this sub-step is in LDS
-            if (active) {
-                bf16x8 op0, op1;
-                if (role_p) {
-                    op0 = pack_operand<0>(sacc);
-                    op1 = pack_operand<8>(sacc);
+                    pk[sub][0] = pack_operand<0>(sacc);
+                    pk[sub][1] = pack_operand<8>(sacc);
+                    pb[lane] = __builtin_bit_cast(uint4, pk[sub][0]);
+                    pb[64 + lane] = __builtin_bit_cast(uint4, pk[sub][1]);
                 } else {
-                    // dS = P (dP - D): P from the partner, in this lane's layout
-                    const uint4 p0 = pb[lane], p1 = pb[64 + lane];
-                    f32x16 ds;
-                    ds[0] = bf16lo(p0.x) * sacc[0]; ds[1] = bf16hi(p0.x) * sacc[1];
-                    ds[2] = bf16lo(p0.y) * sacc[2]; ds[3] = bf16hi(p0.y) * sacc[3];
-                    ds[4] = bf16lo(p0.z) * sacc[4]; ds[5] = bf16hi(p0.z) * sacc[5];
-                    ds[6] = bf16lo(p0.w) * sacc[6]; ds[7] = bf16hi(p0.w) * sacc[7];
-                    ds[8] = bf16lo(p1.x) * sacc[8]; ds[9] = bf16hi(p1.x) * sacc[9];
-                    ds[10] = bf16lo(p1.y) * sacc[10]; ds[11] = bf16hi(p1.y) * sacc[11];
-                    ds[12] = bf16lo(p1.z) * sacc[12]; ds[13] = bf16hi(p1.z) * sacc[13];
-                    ds[14] = bf16lo(p1.w) * sacc[14]; ds[15] = bf16hi(p1.w) * sacc[15];
-                    op0 = pack_operand<0>(ds);
-                    op1 = pack_operand<8>(ds);
+                    acc1[sub] = sacc;
                 }
-                // phase 2: dV^T += dO^T P (role P) or dK^T += Q^T dS (role G)
-                const uint16_t *src = role_p ? dt : qt;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = mfma32x32x16(tr_operand<D>(src, 32 * qh + 16 * tt, db * 32, lane),
-                                               tt ? op1 : op0, acc[db]);
-                sched_pipeline<4 * DB, 2 * DB, 8, 2>();
             }
+        }
+        __syncthreads();                    // every P of the step is in LDS
+#pragma unroll
+        for (int sub = 0; sub < kKvSub; ++sub) {
+            if (!active[sub]) continue;
+            const uint16_t *qt = qc + sub * kKvBM * D, *dt = dc + sub * kKvBM * D;
+            const uint4 *pb = lds.pbuf + (sub * 4 + pair) * 128;
+            bf16x8 op0, op1;
+            if (role_p) {
+                op0 = pk[sub][0];
+                op1 = pk[sub][1];
+            } else {
+                // dS = P (dP - D): P from the partner, in this lane's layout
+                const uint4 p0 = pb[lane], p1 = pb[64 + lane];
+                const f32x16 &dp = acc1[sub];
+                f32x16 ds;
+                ds[0] = bf16lo(p0.x) * dp[0]; ds[1] = bf16hi(p0.x) * dp[1];
+                ds[2] = bf16lo(p0.y) * dp[2]; ds[3] = bf16hi(p0.y) * dp[3];
+                ds[4] = bf16lo(p0.z) * dp[4]; ds[5] = bf16hi(p0.z) * dp[5];
+                ds[6] = bf16lo(p0.w) * dp[6]; ds[7] = bf16hi(p0.w) * dp[7];
+                ds[8] = bf16lo(p1.x) * dp[8]; ds[9] = bf16hi(p1.x) * dp[9];
+                ds[10] = bf16lo(p1.y) * dp[10]; ds[11] = bf16hi(p1.y) * dp[11];
+                ds[12] = bf16lo(p1.z) * dp[12]; ds[13] = bf16hi(p1.z) * dp[13];
+                ds[14] = bf16lo(p1.w) * dp[14]; ds[15] = bf16hi(p1.w) * dp[15];
+                op0 = pack_operand<0>(ds);
+                op1 = pack_operand<8>(ds);
+            }
+            // phase 2: dV^T += dO^T P (role P) or dK^T += Q^T dS (role G)
+            const uint16_t *src = role_p ? dt : qt;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = mfma32x32x16(tr_operand<D>(src, 32 * qh + 16 * tt, db * 32, lane),
+                                           tt ? op1 : op0, acc[db]);
+            sched_pipeline<4 * DB, 2 * DB, 8, 2>();
         }
         sched_fence();
     };
@@ -1131,7 +1147,15 @@ int device_cus()
     return 256;
 }
 
-int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
+// The d = 128 dK/dV work goes to the 128-key kernel (attn_bwd_dkdv128.hip)
+// unless ATTN_DKDV_KV64 selects this file's 64-key kernels.
+#ifdef ATTN_DKDV_KV64
+constexpr bool kDkdv128 = false;
+#else
+constexpr bool kDkdv128 = true;
+#endif
+
+int dkdv_head_split(int B, int Hq, int Hkv, int Nk, int d)
 {
     // Split each group's query heads over workgroups until there are about two
     // work items per CU.  The split workgroups add their partial dK/dV with
@@ -1141,7 +1165,8 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk)
     // adds atomic traffic.
     const int cus = device_cus();
     const int G = Hq / Hkv;
-    const long base = (long)((Nk + kKvBN - 1) / kKvBN) * B * Hkv;
+    const long tiles = kDkdv128 && d == 128 ? dkdv128_tiles(Nk) : (Nk + kKvBN - 1) / kKvBN;
+    const long base = tiles * B * Hkv;
     int hs = 1;
     for (int c = 1; c <= G; ++c)
         if (G % c == 0) {
@@ -1156,6 +1181,9 @@ hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int caus
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
                          hipStream_t st, double rope_lb, const Layouts *L)
 {
+    if (kDkdv128 && d == 128)
+        return bwd_dkdv128_mfma(B, Hq, Hkv, Nq, Nk, causal, scale, q, k, v, lse, dout, Dws, dk, dv, hs, st,
+                                rope_lb, L);
     const int nkt = (Nk + kKvBN - 1) / kKvBN;
     const dim3 grid((unsigned)(nkt * B * Hkv * hs));
     const Layouts lay = L ? *L : Layouts{};

@@ -92,7 +92,13 @@ hipError_t fwd_mfma_rope_q(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
 // Number of workgroups each group's query heads are split over by the dK/dV
 // kernel; with more than one, dk and dv must be zero-filled before the launch
 // (the kernel adds into them).
-int dkdv_head_split(int B, int Hq, int Hkv, int Nk);
+int dkdv_head_split(int B, int Hq, int Hkv, int Nk, int d);
+// The d = 128 dK/dV kernel (128 keys per workgroup) and its key-tile count.
+int dkdv128_tiles(int Nk);
+hipError_t bwd_dkdv128_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int causal, float scale,
+                            const void *q, const void *k, const void *v, const float *lse,
+                            const void *dout, const float *Dws, float *dk, float *dv, int hs,
+                            hipStream_t st, double rope_lb, const Layouts *L);
 hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                          const void *q, const void *k, const void *v, const float *lse,
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
