@@ -277,6 +277,30 @@ __device__ __forceinline__ void sched_pipeline()
     SchedPipeStep<0, NM, NR - AHEAD, RPM, NV, VPM>::emit();
 }
 
+// Scheduling hint for a basic block of NM MFMAs and NR LDS reads: AHEAD reads
+// first, then behind MFMA i as many as bring the reads issued to
+// AHEAD + (i + 1) * NUM / DEN (the rate at which the MFMAs consume them), so
+// that the reads stay a constant distance ahead until they run out.
+// (Masks: 0x008 = MFMA, 0x100 = LDS read.)
+template <int SID, int I, int NM, int NR, int AHEAD, int NUM, int DEN>
+__device__ __forceinline__ void sched_lead_step()
+{
+    constexpr int c0 = AHEAD + I * NUM / DEN, c1 = AHEAD + (I + 1) * NUM / DEN;
+    constexpr int n = (c1 < NR ? c1 : NR) - (c0 < NR ? c0 : NR);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, SID);
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, SID);
+    if constexpr (I + 1 < NM) sched_lead_step<SID, I + 1, NM, NR, AHEAD, NUM, DEN>();
+}
+// SID: a sync id of its own per copy of the code, so that identical hints in
+// different copies are never merged.
+template <int SID, int NR, int NM, int AHEAD, int NUM, int DEN>
+__device__ __forceinline__ void sched_lead()
+{
+    static_assert(AHEAD <= NR, "reads ahead");
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, SID);
+    sched_lead_step<SID, 0, NM, NR, AHEAD, NUM, DEN>();
+}
+
 // Accumulator registers R0..R0+7 of a 32x32 MFMA packed to a bf16 operand.
 template <int R0>
 __device__ __forceinline__ bf16x8 pack_operand(f32x16 acc)
