@@ -109,7 +109,7 @@ CALIB_BYTES = 1 << 30
 # Kernel symbol fragment -> kernel name used in the bench output.
 KERNEL_NAMES = (("fwd_mfma_kernel", "fwd"), ("bwd_pre_kernel", "bwd_preprocess"),
                 ("bwd_fused_kernel", "bwd_grads"),
-                ("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
+                ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"),
                 ("decode_mfma_kernel<128, false>", "decode_merged"),
                 ("lse_merge", "lse_merge"))
 
@@ -564,8 +564,11 @@ def main():
         kernels["decode_merged"] = {"avg_us": round(dec_us, 3), "GB_s": round(dec_gbs, 1)}
         if cfg.dtype == "bf16":
             ft = BD.fwd_tile(B, Hq, N, d)
-            hs = BD.head_split(B, Hq, Hkv, N)
-            kv = dict(BKV=64, SR=128, hs=hs)
+            # the dK/dV kernel's tile: 128 keys x 64 query rows per step at
+            # d = 128, 64 keys x 128 rows at d = 64
+            bkv, sr = (128, 64) if d == 128 else (64, 128)
+            hs = BD.head_split(B, Hq, Hkv, N, BKV=bkv)
+            kv = dict(BKV=bkv, SR=sr, hs=hs)
             floors = {
                 "fwd": (BD.fwd(B, Hq, Hkv, N, N, d, True, **ft), BD.best_fwd(B, Hq, Hkv, N, N, d)),
                 "bwd_preprocess": (BD.preprocess(B, Hq, Hkv, N, d, hs > 1), None),

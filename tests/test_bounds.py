@@ -53,6 +53,7 @@ def test_library_tile_choices():
     assert BD.fwd_tile(1, 32, 512, 128) == {"BM": 64, "BN": 64}
     assert BD.head_split(4, 12, 4, 1024) == 3
     assert BD.head_split(1, 32, 8, 4096) == 1
+    assert BD.head_split(1, 32, 8, 4096, BKV=128) == 2   # the d = 128 kernel's 128-key tiles
 
 
 def test_best_tile_is_feasible_and_no_worse():
