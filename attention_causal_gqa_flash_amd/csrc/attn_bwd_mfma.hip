@@ -1148,12 +1148,22 @@ int device_cus()
 }
 
 // The d = 128 dK/dV work goes to the 128-key kernel (attn_bwd_dkdv128.hip)
-// unless ATTN_DKDV_KV64 selects this file's 64-key kernels.
-#ifdef ATTN_DKDV_KV64
-constexpr bool kDkdv128 = false;
+// unless its key tiles number fewer than a quarter of the CUs: smaller grids
+// take this file's 64-key kernel, which has twice as many items.  Measured
+// on MI355X, attn_bwd at 32/8 heads, causal: N = 256 / 512 27.8 / 39.2 us
+// (64 keys) vs 32.0 / 41.5 us (128 keys); N = 1024 / 4096 80.8 / 482.8 vs
+// 65.4 / 455.3 us.  (ATTN_DKDV_KV64: always the 64-key kernel;
+// ATTN_DKDV_KV128: always the 128-key one.)
+bool dkdv_use128(int B, int Hkv, int Nk, int d)
+{
+#if defined(ATTN_DKDV_KV64)
+    return false;
+#elif defined(ATTN_DKDV_KV128)
+    return d == 128;
 #else
-constexpr bool kDkdv128 = true;
+    return d == 128 && 4L * dkdv128_tiles(Nk) * B * Hkv >= device_cus();
 #endif
+}
 
 int dkdv_head_split(int B, int Hq, int Hkv, int Nk, int d)
 {
@@ -1165,7 +1175,7 @@ int dkdv_head_split(int B, int Hq, int Hkv, int Nk, int d)
     // adds atomic traffic.
     const int cus = device_cus();
     const int G = Hq / Hkv;
-    const long tiles = kDkdv128 && d == 128 ? dkdv128_tiles(Nk) : (Nk + kKvBN - 1) / kKvBN;
+    const long tiles = dkdv_use128(B, Hkv, Nk, d) ? dkdv128_tiles(Nk) : (Nk + kKvBN - 1) / kKvBN;
     const long base = tiles * B * Hkv;
     int hs = 1;
     for (int c = 1; c <= G; ++c)
@@ -1181,7 +1191,7 @@ hipError_t bwd_dkdv_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int caus
                          const void *dout, const float *Dws, float *dk, float *dv, int hs,
                          hipStream_t st, double rope_lb, const Layouts *L)
 {
-    if (kDkdv128 && d == 128)
+    if (dkdv_use128(B, Hkv, Nk, d))
         return bwd_dkdv128_mfma(B, Hq, Hkv, Nq, Nk, causal, scale, q, k, v, lse, dout, Dws, dk, dv, hs, st,
                                 rope_lb, L);
     const int nkt = (Nk + kKvBN - 1) / kKvBN;

@@ -565,8 +565,10 @@ def main():
         if cfg.dtype == "bf16":
             ft = BD.fwd_tile(B, Hq, N, d)
             # the dK/dV kernel's tile: 128 keys x 64 query rows per step at
-            # d = 128, 64 keys x 128 rows at d = 64
-            bkv, sr = (128, 64) if d == 128 else (64, 128)
+            # d = 128 when the 128-key tiles number at least a quarter of the
+            # CUs, else 64 keys x 128 rows
+            use128 = d == 128 and 4 * -(-N // 128) * B * Hkv >= BD.CUS
+            bkv, sr = (128, 64) if use128 else (64, 128)
             hs = BD.head_split(B, Hq, Hkv, N, BKV=bkv)
             kv = dict(BKV=bkv, SR=sr, hs=hs)
             floors = {
