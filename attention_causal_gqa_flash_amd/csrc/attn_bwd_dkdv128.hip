@@ -89,7 +89,10 @@ struct LaneOffsets {
 
 // The second transposed read of tr_operand (8 rows down) differs from the
 // first by a constant: rows 0..7 have swz < 8, so row + 8 flips bit 3 of the
-// chunk, which is bit 1 of db.
+// chunk, which is bit 1 of db.  (That holds for the default swizzle only.)
+#ifdef ATTN_LDS_SWIZZLE_256
+#error "the 128-key dK/dV kernel's operand offsets assume the default LDS swizzle"
+#endif
 constexpr int kTrHi[4] = {2 * (8 * 128 + 64), 2 * (8 * 128 + 64), 2 * (8 * 128 - 64), 2 * (8 * 128 - 64)};
 
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane)
