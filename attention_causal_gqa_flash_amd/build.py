@@ -83,7 +83,9 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(f"--- {s}\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
     tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # -z defs: an unresolved symbol (say a kernel launch stub the host pass did
+    # not emit) fails the build here rather than the first load of the library
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.check_call(link)

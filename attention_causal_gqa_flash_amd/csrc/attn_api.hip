@@ -546,7 +546,7 @@ attn_status attn_decode(attn_dtype dt, int B, int Hq, int Hkv, int L, int d, flo
         !aligned16(part_lse))
         return ATTN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
-    if (attn::decode_mfma_supported(dt, d, Hq / Hkv) && scale != 0.f)
+    if (attn::decode_mfma_supported(dt, d, Hq / Hkv, L) && scale != 0.f)
         return hip_status(attn::decode_split_mfma(B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
                                                   v_cache, part_o, part_lse, st));
     return hip_status(attn::decode_split(dt, B, Hq, Hkv, L, d, scale, n_splits, q, k_cache,
@@ -568,7 +568,7 @@ attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int
         return ATTN_ERR_INVALID_ARG;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
-    if (attn::decode_mfma_supported(dt, d, Hq / Hkv) && scale != 0.f)
+    if (attn::decode_mfma_supported(dt, d, Hq / Hkv, L) && scale != 0.f)
         e = attn::decode_split_mfma(B, Hq, Hkv, L, d, scale, n_splits, q, k_cache, v_cache, part_o,
                                     part_lse, st);
     else
@@ -588,7 +588,7 @@ attn_status attn_decode_append(attn_dtype dt, int B, int Hq, int Hkv, int L_cap,
     if (s != ATTN_OK) return s;
     if (n_splits < 1) return ATTN_ERR_INVALID_ARG;
     if ((long)n_splits > kMaxGridX || (long)Hkv > kMaxGridYZ) return ATTN_ERR_UNSUPPORTED;
-    if (!attn::decode_mfma_supported(dt, d, Hq / Hkv) || scale == 0.f) return ATTN_ERR_UNSUPPORTED;
+    if (!attn::decode_mfma_supported(dt, d, Hq / Hkv, L_cap) || scale == 0.f) return ATTN_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
         !aligned16(v_cache) || !aligned16(part_o) || !aligned16(part_lse) || !aligned16(o) ||
         !aligned16(lse))

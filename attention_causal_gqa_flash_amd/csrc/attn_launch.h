@@ -128,7 +128,7 @@ hipError_t bwd_fused_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
 hipError_t decode_split(int dt, int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
                         const void *q, const void *kc, const void *vc, float *part_o,
                         float *part_lse, hipStream_t st);
-bool decode_mfma_supported(int dt, int d, int G);
+bool decode_mfma_supported(int dt, int d, int G, int L);
 hipError_t decode_split_mfma(int B, int Hq, int Hkv, int L, int d, float scale, int n_splits,
                              const void *q, const void *kc, const void *vc, float *part_o,
                              float *part_lse, hipStream_t st);

@@ -184,6 +184,11 @@ DECODE = [
     (1, 4, 2, 513, 64, 16, "f32"),
     (3, 6, 3, 77, 32, 3, "bf16"),
     (1, 2, 1, 300, 16, 5, "f32"),
+    # group sizes that do not divide 16 (heads repeat unevenly over the 16
+    # score columns) and chunks longer than one pass of the 8 waves (256 keys)
+    (1, 12, 4, 2000, 64, 3, "bf16"),    # G = 3, 667-key chunks
+    (2, 10, 2, 1500, 128, 2, "bf16"),   # G = 5, 750-key chunks
+    (1, 14, 2, 700, 128, 4, "bf16"),    # G = 7
 ]
 
 
@@ -508,6 +513,7 @@ APPEND = [
     (3, 12, 4, 257, 64, 7, [256, 100, 31]),
     (2, 16, 1, 40, 128, 16, [2, 39]),           # more splits than keys, G = 16
     (1, 8, 8, 4096, 64, 16, [4095]),            # full cache, G = 1
+    (2, 12, 4, 3000, 128, 2, [2999, 1500]),     # G = 3, 1500-key chunks (several passes)
 ]
 
 
