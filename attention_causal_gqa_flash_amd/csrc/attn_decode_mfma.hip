@@ -98,8 +98,8 @@ __global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) uint16_t sv[kWaves * kBlk * D];
     __shared__ __attribute__((aligned(16))) float wml[2 * kWaves * 16];
     float *const wo = reinterpret_cast<float *>(APPEND ? sv : sk);            // [wave][16][D]
-    float *const wm = wml;                                                    // [16][wave]
-    float *const wl = wml + kWaves * 16;                                      // [16][wave]
+    float *const wm = wml;                                                    // [head][wave]
+    float *const wl = wml + kWaves * 16;                                      // [head][wave]
     static_assert(kWaves * 16 * D * 4 == kWaves * kBlk * D * 2, "output rows fit one tile set");
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -316,9 +316,13 @@ __global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
 
     // ---- per-wave state -> LDS, then combine the 8 waves ----
     l_run = pair32_sum(pair16_sum(l_run));
-    if (grp == 0) {                                    // [column][wave]
-        wm[l16 * kWaves + wave] = m_run;
-        wl[l16 * kWaves + wave] = l_run;
+    {
+        // [head][wave], from the head's first column
+        const int h = (l16 * G) >> 4;
+        if (grp == 0 && l16 * G < 16 * h + G) {
+            wm[h * kWaves + wave] = m_run;
+            wl[h * kWaves + wave] = l_run;
+        }
     }
     // accumulator row 4grp + r is column n = 4grp + r, i.e. head n G / 16; the
     // first column of each head writes its row: lane l16 holds output column
@@ -338,34 +342,34 @@ __global__ __launch_bounds__(512, APPEND ? 4 : 1) void decode_mfma_kernel(
     __syncthreads();
     for (int t = tid; t < G * D; t += 512) {
         const int hh = t / D, c = t % D;
-        const int n = (16 * hh + G - 1) / G;           // the head's first column
-        static_assert(kWaves == 8, "two 16-byte reads per column");
-        float mw[kWaves], lw[kWaves];
-        *reinterpret_cast<float4 *>(mw) = *reinterpret_cast<const float4 *>(wm + n * kWaves);
-        *reinterpret_cast<float4 *>(mw + 4) = *reinterpret_cast<const float4 *>(wm + n * kWaves + 4);
-        *reinterpret_cast<float4 *>(lw) = *reinterpret_cast<const float4 *>(wl + n * kWaves);
-        *reinterpret_cast<float4 *>(lw + 4) = *reinterpret_cast<const float4 *>(wl + n * kWaves + 4);
+        // every read issued at once: the 8 waves' (max, sum) of head hh and
+        // their output at column c
+        static_assert(kWaves == 8, "two 16-byte reads per head");
+        float mw[kWaves], lw[kWaves], ow[kWaves];
+        *reinterpret_cast<float4 *>(mw) = *reinterpret_cast<const float4 *>(wm + hh * kWaves);
+        *reinterpret_cast<float4 *>(mw + 4) = *reinterpret_cast<const float4 *>(wm + hh * kWaves + 4);
+        *reinterpret_cast<float4 *>(lw) = *reinterpret_cast<const float4 *>(wl + hh * kWaves);
+        *reinterpret_cast<float4 *>(lw + 4) = *reinterpret_cast<const float4 *>(wl + hh * kWaves + 4);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) ow[w] = wo[(w * 16 + hh) * D + (c ^ (16 * (hh & 3)))];
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-        const size_t ob = ((size_t)b * Hq + g * G + hh) * n_splits + s;
-        if (M == -INFINITY) {                          // empty chunk: the identity
-            part_o[ob * D + c] = 0.f;
-            if (c == 0) part_lse[ob] = -INFINITY;
-            continue;
-        }
-        // a wave that saw no key holds (-inf, 0, 0), whose weight 2^-inf is 0
+        // a wave that saw no key holds (-inf, 0, 0), whose weight 2^-inf is 0;
+        // a chunk with no key at all (M = -inf) gives the identity (0, -inf)
         float lt = 0.f, at = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float e = exp2_fast(mw[w] - M);
             lt = fmaf(lw[w], e, lt);
-            at = fmaf(wo[(w * 16 + hh) * D + (c ^ (16 * (hh & 3)))], e, at);
+            at = fmaf(ow[w], e, at);
         }
+        const bool empty = M == -INFINITY;
+        const size_t ob = ((size_t)b * Hq + g * G + hh) * n_splits + s;
         // hardware reciprocal and log2 (about 1 ulp): the partials' bf16-input
         // tolerances are orders of magnitude wider
-        part_o[ob * D + c] = at * __builtin_amdgcn_rcpf(lt);
-        if (c == 0) part_lse[ob] = (M + __builtin_amdgcn_logf(lt)) * kLn2;
+        part_o[ob * D + c] = empty ? 0.f : at * __builtin_amdgcn_rcpf(lt);
+        if (c == 0) part_lse[ob] = empty ? -INFINITY : (M + __builtin_amdgcn_logf(lt)) * kLn2;
     }
 }
 
