@@ -59,12 +59,15 @@ __device__ __forceinline__ void rope_sincos(double a, float &s, float &c)
 // The same on the hardware sine and cosine (v_sin_f32 / v_cos_f32 take the
 // angle in turns), for the matrix-core path's epilogues: a few instructions
 // instead of the library's full-range code, accurate to about 1e-6.
-__device__ __forceinline__ void rope_sincos_hw(double a, float &s, float &c)
+__device__ __forceinline__ void rope_sincos_turns(double t, float &s, float &c)
 {
-    const double t = a * 0.15915494309189535;             // turns
     const float f = (float)(t - rint(t));                  // in [-1/2, 1/2]
     s = __builtin_amdgcn_sinf(f);
     c = __builtin_amdgcn_cosf(f);
+}
+__device__ __forceinline__ void rope_sincos_hw(double a, float &s, float &c)
+{
+    rope_sincos_turns(a * 0.15915494309189535, s, c);      // radians -> turns
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -233,13 +236,27 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int kbase, in
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // No instruction is scheduled across this point (keeps MFMAs issued before a
 // wait instead of after it).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Workgroup barrier for LDS data written before it -- by this wave's LDS
+// stores, or by direct copies whose vmcnt each wave has already waited for --
+// without the wait for every outstanding vector-memory operation that
+// __syncthreads implies (its workgroup fence also covers the direct copies), so
+// that copies of later tiles stay in flight across it.  The empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS accesses are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // LDS tile buffers are separate __shared__ arrays chosen at compile time: the
 // compiler then knows that a read of the current buffer does not alias the

@@ -238,44 +238,59 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         qcopy(sk1, make_rsrc(Qh, q_bytes), q0, wave);
         if constexpr (BMW > 64) qcopy(sv1, make_rsrc(Qh, q_bytes), q0 + 64, wave);
     }
-    auto read_q = [&] {
-        const int qr = rw * 32 + l32;        // this lane's row within the tile
-        const uint16_t *qt = qr < 64 ? sk1 : sv1;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 u = *(const uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
-            u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
-            st.qf[ks] = as_bf16x8(u);
-        }
+    // The Q rows of a wave lie in one of the two arrays (rows 0..63 in sk1,
+    // 64..127 in sv1: a wave-uniform choice).  Each access names its array
+    // directly rather than through a select, so that the compiler can tell it
+    // from the step-0 copies into sk0 / sv0 still in flight and does not wait
+    // for them.
+    const int qr = rw * 32 + l32;            // this lane's row within the tile
+    auto on_q_rows = [&](auto f) {
+        if (BMW <= 64 || qr < 64) f(sk1); else f(sv1);
     };
-    // ROPE: the tile's Q rows, once in LDS, are turned in place by the lanes
-    // that own them (key half 0 only), one pair of chunks (ks, ks + KS/2) at
-    // a time -- pair i = 16ks + 8hf + e has frequency r^i, r = base^(-2/D):
-    // r^(8hf + 16ks) once per chunk, then steps of r -- and then written out
-    // whole-row by all threads as Qrot.
+    auto read_q = [&] {
+        on_q_rows([&](const uint16_t *qt) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 u = *(const uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
+                u.x ^= qsign; u.y ^= qsign; u.z ^= qsign; u.w ^= qsign;
+                st.qf[ks] = as_bf16x8(u);
+            }
+        });
+    };
+    // ROPE: the tile's Q rows, once in LDS, are turned in place, one pair of
+    // chunks (ks, ks + KS/2) at a time; with two key halves both halves' waves
+    // share the chunk pairs of their rows (all four SIMDs busy).  Pair
+    // i = 16ks + 8hf + e turns by pos * r^i / (2 pi) turns, r = base^(-2/D):
+    // one exp2 per lane for r, then products -- r^8 and r^16 by squaring, the
+    // chunk's first frequency, and steps of r -- and then the rows are written
+    // out whole by all threads as Qrot.
     auto rotate_q = [&] {
-        if (kh == 0) {
-            const int qr = rw * 32 + l32;
-            uint16_t *qt = qr < 64 ? sk1 : sv1;
+        on_q_rows([&](uint16_t *qt) {
             const double pos = (double)(qi + off);
             const double r1 = rope_theta(1, D, rope_lb);
+            const double r2 = r1 * r1, r4 = r2 * r2, r8 = r4 * r4, r16 = r8 * r8;
+            // frequency of pair 16 kh + 8 hf, in turns per position
+            double f0 = (hf ? r8 : 1.0) * 0.15915494309189535;
+            for (int j = 0; j < kh; ++j) f0 *= r16;
+            double r16k = 1.0;
+            for (int j = 0; j < KSPLIT; ++j) r16k *= r16;
 #pragma unroll 1
-            for (int ks = 0; ks < KS / 2; ++ks) {
+            for (int ks = kh; ks < KS / 2; ks += KSPLIT, f0 *= r16k) {
                 uint4 *p0 = (uint4 *)tile_chunk<D>(qt, qr & 63, 2 * ks + hf);
                 uint4 *p1 = (uint4 *)tile_chunk<D>(qt, qr & 63, 2 * (ks + KS / 2) + hf);
                 const uint4 a0 = *p0, a1 = *p1;
                 const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w}, w1[4] = {a1.x, a1.y, a1.z, a1.w};
                 uint32_t o0[4], o1[4];
-                double th = rope_theta(16 * ks + 8 * hf, D, rope_lb);
+                double f = f0;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     float y0[2], y1[2];
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh, th *= r1) {
+                    for (int hh = 0; hh < 2; ++hh, f *= r1) {
                         const float x0 = hh ? bf16hi(w0[e2]) : bf16lo(w0[e2]);
                         const float x1 = hh ? bf16hi(w1[e2]) : bf16lo(w1[e2]);
                         float sn, cs;
-                        rope_sincos_hw(pos * th, sn, cs);
+                        rope_sincos_turns(pos * f, sn, cs);
                         y0[hh] = x0 * cs - x1 * sn;
                         y1[hh] = x0 * sn + x1 * cs;
                     }
@@ -285,28 +300,22 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
                 *p0 = make_uint4(o0[0], o0[1], o0[2], o0[3]);
                 *p1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
             }
-        }
-        __syncthreads();
+        });
+        lds_barrier();
         constexpr int CPR = D / 8;           // 16-byte chunks per row
         uint16_t *qrot_h = Qrot + ((size_t)b * Hq + h) * (size_t)Nq * D;
+        auto write_rows = [&](const uint16_t *qt, int r0) {
 #pragma unroll 1
-        for (int c = tid; c < BMW * CPR; c += 256) {
-            const int r = c / CPR, ch = c % CPR;
-            if (q0 + r < Nq)
-                *(uint4 *)(qrot_h + (size_t)(q0 + r) * D + 8 * ch) =
-                    *(const uint4 *)tile_chunk<D>(r < 64 ? sk1 : sv1, r & 63, ch);
-        }
+            for (int c = tid; c < 64 * CPR; c += 256) {
+                const int r = c / CPR, ch = c % CPR;
+                if (q0 + r0 + r < Nq)
+                    *(uint4 *)(qrot_h + (size_t)(q0 + r0 + r) * D + 8 * ch) =
+                        *(const uint4 *)tile_chunk<D>(qt, r, ch);
+            }
+        };
+        write_rows(sk1, 0);
+        if constexpr (BMW > 64) write_rows(sv1, 64);
     };
-    st.m_run = -INFINITY;
-    st.m_thr = -INFINITY;
-    st.nm = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) st.lq[c] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
-
     const int kv_end = causal ? min(Nk, q0 + off + BMW) : Nk;
     const int ntiles = (kv_end + TN - 1) / TN;
     // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles).  A row
@@ -336,6 +345,27 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     };
     copy_step(sk0, sv0, 0);
 
+    // The resident Q rows, while the step-0 copies are in flight: wait for the
+    // Q copies alone (issued first; loads complete in order), rotate them
+    // (ROPE), read the operands, and free buffer 1 for step 1's copies.  The
+    // softmax state is set up only afterwards, so the prologue's registers do
+    // not add to the loop's.
+    wait_vmcnt<2 * KSPLIT * Copy::PER_WAVE>();
+    lds_barrier();
+    if constexpr (ROPE) rotate_q();
+    read_q();
+    __syncthreads();
+
+    st.m_run = -INFINITY;
+    st.m_thr = -INFINITY;
+    st.nm = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st.lq[c] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.oacc[db][r] = 0.f;
+
     // Step s reads buffer s % 2 while step s+1 is copied into the other one.
     auto run_step = [&](auto bufc, int s_) {
         constexpr int BI = decltype(bufc)::value;
@@ -343,13 +373,6 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of step s have landed
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
-        if constexpr (BI == 0) {
-            if (s_ == 0) {                  // the resident Q rows, then buffer 1 is free
-                if constexpr (ROPE) rotate_q();
-                read_q();
-                __syncthreads();
-            }
-        }
         // copies of step s+1 (branch-free, so they can interleave with MFMAs)
         auto prefetch = [&] { copy_step(skn, svn, s_ + 1); };
         const int kv0 = tile_of(kh, s_) * TN;

@@ -26,23 +26,29 @@
 namespace attn {
 namespace {
 
-constexpr int kPairs = 4;   // consecutive pairs per thread
+// Consecutive pairs per thread: 16 bytes of each half row (8 bf16, 4 f32),
+// or the whole half row when it is shorter.
+template <typename T>
+__host__ __device__ constexpr int pairs_per_thread() { return sizeof(T) == 2 ? 8 : 4; }
 
-__device__ __forceinline__ void load4(const bf16_t *p, float (&v)[4])
+__device__ __forceinline__ void load_pairs(const bf16_t *p, float (&v)[8])
 {
-    const uint2 u = *(const uint2 *)p;
-    v[0] = bf16lo(u.x); v[1] = bf16hi(u.x); v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+    const uint4 u = *(const uint4 *)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { v[2 * j] = bf16lo(w[j]); v[2 * j + 1] = bf16hi(w[j]); }
 }
-__device__ __forceinline__ void load4(const float *p, float (&v)[4])
+__device__ __forceinline__ void load_pairs(const float *p, float (&v)[4])
 {
     const float4 u = *(const float4 *)p;
     v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
 }
-__device__ __forceinline__ void store4(bf16_t *p, const float (&v)[4])
+__device__ __forceinline__ void store_pairs(bf16_t *p, const float (&v)[8])
 {
-    *(uint2 *)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    *(uint4 *)p = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7]));
 }
-__device__ __forceinline__ void store4(float *p, const float (&v)[4])
+__device__ __forceinline__ void store_pairs(float *p, const float (&v)[4])
 {
     *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
 }
@@ -59,41 +65,45 @@ struct RopeSeg {
 };
 
 // One launch over one or two tensors (the second may have no rows).  A thread
-// owns pairs i0 .. i0+3 of its rows: the grid stride and the first tensor's
-// thread count are multiples of the threads per row, so i0 is fixed and its
-// frequencies are computed once, in double.  The angle is reduced to [-pi,
-// pi] in double before the f32 sine and cosine, so positions in the millions
-// keep f32 accuracy.  x and y may be the same buffer.
+// owns pairs i0 .. i0+KP-1 of its rows (16-byte accesses): the grid stride and
+// the first tensor's thread count are multiples of the threads per row, so i0
+// is fixed and its frequencies are computed once, in double.  The angle is
+// reduced to whole turns in double before the f32 sine and cosine, so
+// positions in the millions keep f32 accuracy: for bf16 rows on the hardware
+// sine and cosine (about 1e-6, far below bf16's resolution), for f32 rows on
+// the library's.  x and y may be the same buffer.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kernel(RopeSeg<T> s0, RopeSeg<T> s1, int d, double log2_base,
                                                    int inverse)
 {
-    const int half = d / 2, tpr = half / kPairs;
+    constexpr int KP = pairs_per_thread<T>();
+    const int half = d / 2, tpr = half / KP;
     const long t0 = (long)blockIdx.x * 256 + threadIdx.x;
     const long stride = (long)gridDim.x * 256;
     const long n0 = s0.rows * tpr, n = n0 + s1.rows * tpr;
-    const int i0 = (int)(t0 % tpr) * kPairs;
-    double th[kPairs];
+    const int i0 = (int)(t0 % tpr) * KP;
+    double th[KP];
 #pragma unroll
-    for (int e = 0; e < kPairs; ++e) th[e] = rope_theta(i0 + e, d, log2_base);
+    for (int e = 0; e < KP; ++e) th[e] = rope_theta(i0 + e, d, log2_base) * 0.15915494309189535;   // turns
     for (long t = t0; t < n; t += stride) {
         const bool first = t < n0;
         const RopeSeg<T> &sg = first ? s0 : s1;
         const long r = (first ? t : t - n0) / tpr;
         const double p = (double)(sg.pos0 + r % sg.N);
-        float x0[kPairs], x1[kPairs], y0[kPairs], y1[kPairs];
-        load4(sg.x + r * d + i0, x0);
-        load4(sg.x + r * d + half + i0, x1);
+        float x0[KP], x1[KP], y0[KP], y1[KP];
+        load_pairs(sg.x + r * d + i0, x0);
+        load_pairs(sg.x + r * d + half + i0, x1);
 #pragma unroll
-        for (int e = 0; e < kPairs; ++e) {
+        for (int e = 0; e < KP; ++e) {
             float s, c;
-            rope_sincos(p * th[e], s, c);
+            if constexpr (sizeof(T) == 2) rope_sincos_turns(p * th[e], s, c);
+            else rope_sincos(p * th[e] * 6.283185307179586, s, c);
             if (inverse) s = -s;
             y0[e] = x0[e] * c - x1[e] * s;
             y1[e] = x0[e] * s + x1[e] * c;
         }
-        store4(sg.y + r * d + i0, y0);
-        store4(sg.y + r * d + half + i0, y1);
+        store_pairs(sg.y + r * d + i0, y0);
+        store_pairs(sg.y + r * d + half + i0, y1);
     }
 }
 
@@ -101,7 +111,7 @@ template <typename T>
 hipError_t rope_launch(const RopeSeg<T> &s0, const RopeSeg<T> &s1, int d, double base, int inverse,
                        hipStream_t st)
 {
-    const long threads = (s0.rows + s1.rows) * (d / 2 / kPairs);
+    const long threads = (s0.rows + s1.rows) * (d / 2 / pairs_per_thread<T>());
     const unsigned blocks = (unsigned)std::min<long>((threads + 255) / 256, 2048L);
     hipLaunchKernelGGL(rope_kernel<T>, dim3(blocks), dim3(256), 0, st, s0, s1, d, log2(base), inverse);
     return hipGetLastError();

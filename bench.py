@@ -666,6 +666,11 @@ def main():
             "read_floor_us": floor["median_us"],
             "read_floor_GB_per_s": round(rb / (floor["median_us"] * 1e-6) / 1e9, 1),
             "of_read_floor": round(floor["median_us"] / cold["median_us"], 4),
+            # the op is two launches (the partials must be complete before any
+            # merge): its floor is one streaming read of the caches plus one
+            # merge launch
+            "two_launch_floor_us": round(floor["median_us"] + merge_only["median_us"], 3),
+            "of_two_launch_floor": round((floor["median_us"] + merge_only["median_us"]) / cold["median_us"], 4),
             "distinct_caches": ncache,
         }
     result["configs"] = configs
