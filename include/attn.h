@@ -427,7 +427,8 @@ attn_status attn_decode_merged(attn_dtype dt, int B, int Hq, int Hkv, int L, int
  *        chunks of ceil((n + 1) / n_splits) keys, then merged:
  *        o[b][h] = softmax(scale q.K^T) V, lse[b][h] = log-sum-exp.
  *   q [B][Hq][d], k_new / v_new [B][Hkv][d]: dtype dt (bf16 only; d 64 or 128,
- *   Hq/Hkv <= 16, scale != 0; anything else returns ATTN_ERR_UNSUPPORTED).
+ *   Hq/Hkv <= 16, scale != 0, L_cap * d * 2 + 65536 < 2^31; anything else
+ *   returns ATTN_ERR_UNSUPPORTED).
  *   k_cache / v_cache [B][Hkv][L_cap][d] dt: read at rows < n, written at row
  *   n only.  seq_lens [B] int32 device memory, read only (4-byte aligned).
  *   part_o [B][Hq][n_splits][d], part_lse [B][Hq][n_splits] f32 scratch as in

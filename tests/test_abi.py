@@ -285,6 +285,8 @@ def test_decode_append_refusals(L):
     assert call(d=32) == UNSUPPORTED
     assert call(scale=0.0) == UNSUPPORTED
     assert call(Hq=34, Hkv=2) == UNSUPPORTED         # group of 17 heads
+    # a head's cache must stay addressable by 32-bit buffer offsets
+    assert call(Lc=(1 << 31) // 256) == UNSUPPORTED
     assert call(lens=NUL) == INVALID
     assert call(lens=ctypes.c_void_p(0x10002)) == INVALID
     for which in range(5):
