@@ -286,6 +286,14 @@ __device__ __forceinline__ void dkdv_body(
         row_v = row_load(make_rsrc((wave < 2 ? LSE : Dws) + hrow, row_bytes), q0_ + 64 * half, lane);
     };
     if (steps > 0) load_step(0, q0s, d0s);
+    // The resident K and V operands as soon as their copies have landed (they
+    // were issued before step 0's copies and its row load, and loads complete
+    // in order), while step 0's copies are still in flight; step 0's barrier
+    // then also tells every wave that buffer 1 is free for step 1's copies.
+    if (steps > 0) wait_vmcnt<2 * decltype(copy)::PER_WAVE + 1>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    read_kv();
 
     auto run_step = [&](auto bufc, int s) {
         constexpr int BI = decltype(bufc)::value;
@@ -294,12 +302,6 @@ __device__ __forceinline__ void dkdv_body(
         wait_vmcnt<0>();                    // this wave's copies of step s have landed
         (wave < 2 ? lc : ec)[64 * (wave & 1) + lane] = row_v * row_mul;
         __syncthreads();                    // ... and every wave's; buffer s+1 is free
-        if constexpr (BI == 0) {
-            if (s == 0) {                   // the key tile's K and V rows, then buffer 1 is free
-                read_kv();
-                __syncthreads();
-            }
-        }
         if (s + 1 < steps) {
             if (BI) load_step(s + 1, q0s, d0s);
             else load_step(s + 1, q1s, d1s);
@@ -909,34 +911,73 @@ __device__ __forceinline__ void dq_body(
             dof[ks] = as_bf16x8(ud);
         }
     }
-    const float lse2 = qi < Nq ? LSE[qrow0 + qi] * kLog2e : INFINITY;
+    // Every load of the prologue before tile 0's copies, and none behind a
+    // branch (rows clamped, values selected), so that nothing waits for them
+    // before those copies are issued: the row terms, and with PRE the O
+    // elements matching the lane's dO operands (and dlse).
+    const int qcl = min(qi, Nq - 1);
+    const float lse_raw = LSE[qrow0 + qcl];
+    float dr = 0.f, dl = 0.f;
+    float4 oa[KS], oc[KS];
+    if constexpr (PRE) {
+        const float *orow = O + b * lo.b + h * lo.h + (size_t)qcl * lo.n;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            oa[ks] = *(const float4 *)(orow + 16 * ks + 8 * hf);
+            oc[ks] = *(const float4 *)(orow + 16 * ks + 8 * hf + 4);
+        }
+        if (dlse) dl = dlse[qrow0 + qcl];
+    } else {
+        dr = Dws[qrow0 + qcl];
+    }
+
+    const int kv_end = causal ? min(Nk, q0 + kQBM + off) : Nk;
+    const int ntiles = (kv_end + kQBN - 1) / kQBN;
+
+    // Tiles move global -> LDS directly; rows past Nk read as zero and are masked.
+    const uint32_t k_bytes = head_bytes(Nk, lk.n, D, 2), v_bytes = head_bytes(Nk, lv.n, D, 2);
+    using Copy = TileCopy<D, kQBN, 4>;
+    const Copy copy(wave, lane, lk.n), copyv(wave, lane, lv.n);
+    copy(sk0, make_rsrc(Kg, k_bytes), 0, wave);
+    copyv(sv0, make_rsrc(Vg, v_bytes), 0, wave);
+    if constexpr (STAGE) {
+        // the resident Q and dO rows as soon as their copies have landed (issued
+        // before the row-term loads and tile 0's copies; loads complete in
+        // order), while tile 0's copies are still in flight; tile 0's barrier
+        // then also frees buffer 1 for tile 1's copies
+        wait_vmcnt<2 * Copy::PER_WAVE>();
+        lds_barrier();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 uq = *(const uint4 *)tile_chunk<D>(sk1, wave * 32 + l32, 2 * ks + hf);
+            const uint4 ud = *(const uint4 *)tile_chunk<D>(sv1, wave * 32 + l32, 2 * ks + hf);
+            uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
+            qf[ks] = as_bf16x8(uq);
+            dof[ks] = as_bf16x8(ud);
+        }
+    }
+
+    // the row terms, while tile 0's copies are in flight
+    const float lse2 = qi < Nq ? lse_raw * kLog2e : INFINITY;
     float Di;
     if constexpr (PRE) {
-        // the lane holds dO[qi][16ks + 8hf .. +7]: the matching O elements,
-        // then the two halves of the row summed across the lane pair
-        float s = 0.f;
-        if (qi < Nq) {
-            const float *orow = O + b * lo.b + h * lo.h + (size_t)qi * lo.n;
+        // the lane holds dO[qi][16ks + 8hf .. +7] and the matching O elements;
+        // the two halves of the row summed across the lane pair
+        float sm = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const float4 a = *(const float4 *)(orow + 16 * ks + 8 * hf);
-                const float4 c = *(const float4 *)(orow + 16 * ks + 8 * hf + 4);
-                const uint4 u = __builtin_bit_cast(uint4, dof[ks]);
-                s = fmaf(bf16lo(u.x), a.x, s); s = fmaf(bf16hi(u.x), a.y, s);
-                s = fmaf(bf16lo(u.y), a.z, s); s = fmaf(bf16hi(u.y), a.w, s);
-                s = fmaf(bf16lo(u.z), c.x, s); s = fmaf(bf16hi(u.z), c.y, s);
-                s = fmaf(bf16lo(u.w), c.z, s); s = fmaf(bf16hi(u.w), c.w, s);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 a = oa[ks], c = oc[ks];
+            const uint4 u = __builtin_bit_cast(uint4, dof[ks]);
+            sm = fmaf(bf16lo(u.x), a.x, sm); sm = fmaf(bf16hi(u.x), a.y, sm);
+            sm = fmaf(bf16lo(u.y), a.z, sm); sm = fmaf(bf16hi(u.y), a.w, sm);
+            sm = fmaf(bf16lo(u.z), c.x, sm); sm = fmaf(bf16hi(u.z), c.y, sm);
+            sm = fmaf(bf16lo(u.w), c.z, sm); sm = fmaf(bf16hi(u.w), c.w, sm);
         }
-        Di = pair32_sum(s);
-        if (qi < Nq) {
-            if (dlse) Di -= dlse[qrow0 + qi];
-            if (hf == 0) Dout[qrow0 + qi] = Di;
-        } else {
-            Di = 0.f;
-        }
+        Di = pair32_sum(sm) - dl;
+        if (qi < Nq && hf == 0) Dout[qrow0 + qi] = Di;
+        Di = qi < Nq ? Di : 0.f;
     } else {
-        Di = qi < Nq ? Dws[qrow0 + qi] : 0.f;
+        Di = qi < Nq ? dr : 0.f;
     }
     f32x16 negD;
 #pragma unroll
@@ -948,35 +989,12 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
 
-    const int kv_end = causal ? min(Nk, q0 + kQBM + off) : Nk;
-    const int ntiles = (kv_end + kQBN - 1) / kQBN;
-
-    // Tiles move global -> LDS directly; rows past Nk read as zero and are masked.
-    const uint32_t k_bytes = head_bytes(Nk, lk.n, D, 2), v_bytes = head_bytes(Nk, lv.n, D, 2);
-    using Copy = TileCopy<D, kQBN, 4>;
-    const Copy copy(wave, lane, lk.n), copyv(wave, lane, lv.n);
-    copy(sk0, make_rsrc(Kg, k_bytes), 0, wave);
-    copyv(sv0, make_rsrc(Vg, v_bytes), 0, wave);
-
     auto run_tile = [&](auto bufc, int t) {
         constexpr int BI = decltype(bufc)::value;
         const uint16_t *skc = BI ? sk1 : sk0, *svc = BI ? sv1 : sv0;
         uint16_t *skn = BI ? sk0 : sk1, *svn = BI ? sv0 : sv1;
         wait_vmcnt<0>();                    // this wave's copies of tile t have landed
         __syncthreads();                    // ... and every wave's; buffer t+1 is free
-        if constexpr (STAGE && BI == 0) {
-            if (t == 0) {                   // the resident Q and dO rows, then buffer 1 is free
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    uint4 uq = *(const uint4 *)tile_chunk<D>(sk1, wave * 32 + l32, 2 * ks + hf);
-                    const uint4 ud = *(const uint4 *)tile_chunk<D>(sv1, wave * 32 + l32, 2 * ks + hf);
-                    uq.x ^= qsign; uq.y ^= qsign; uq.z ^= qsign; uq.w ^= qsign;
-                    qf[ks] = as_bf16x8(uq);
-                    dof[ks] = as_bf16x8(ud);
-                }
-                __syncthreads();
-            }
-        }
         // copies of tile t+1 (branch-free, so they can interleave with MFMAs);
         // past the last tile they read nothing (zero-byte resources)
         const bool more = t + 1 < ntiles;
