@@ -196,10 +196,10 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
     float *delta = (float *)workspace;
     const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale, L);
     if (use_mfma(dt, Nk, d, scale, L, Nq) && !fuse_bwd(d) && !o_bf16) {
-        if (hs > 1 && attn::zero_fill2(dk, dv, (long)B * Hkv * Nk * d, st) != hipSuccess)
-            return ATTN_ERR_HIP;
+        // the dQ kernel also zeroes dk and dv for the dK/dV kernel's atomic head subsets
         if (attn::bwd_dq_pre_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
-                                  (const float *)o, dlse, delta, dq, st, rope_lb, L) != hipSuccess)
+                                  (const float *)o, dlse, delta, dq, st, rope_lb, L, dk, dv,
+                                  hs > 1 ? (long)B * Hkv * Nk * d : 0L) != hipSuccess)
             return ATTN_ERR_HIP;
         return hip_status(launch_bwd_dkdv(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, lse,
                                           dout, delta, dk, dv, hs, st, rope_lb, L));

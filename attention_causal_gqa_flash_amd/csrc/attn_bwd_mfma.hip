@@ -1086,7 +1086,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ Dws, float *__restrict__ dQ, int B,
     int Hq, int Hkv, int Nq, int Nk, float scale, int causal, int nqt, double rope_lb,
-    const float *__restrict__ O, const float *__restrict__ dlse, float *__restrict__ Dout, Layouts L)
+    const float *__restrict__ O, const float *__restrict__ dlse, float *__restrict__ Dout, Layouts L,
+    float *__restrict__ zf_a = nullptr, float *__restrict__ zf_b = nullptr, long zf_n = 0)
 {
     __shared__ __attribute__((aligned(16))) uint16_t sk0[kQBN * D], sk1[kQBN * D];
     __shared__ __attribute__((aligned(16))) uint16_t sv0[kQBN * D], sv1[kQBN * D];
@@ -1094,9 +1095,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     // work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
     const int G = Hq / Hkv;
     WorkItem w;
-    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
-    dq_body<D, XL, false, PRE, STR>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B, Hq,
-                                    Hkv, Nq, Nk, scale, causal, rope_lb, O, dlse, Dout, L);
+    if (xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w))
+        dq_body<D, XL, false, PRE, STR>(w.tile, w.group * G + w.head, lds, Q, K, V, LSE, dO, Dws, dQ, B,
+                                        Hq, Hkv, Nq, Nk, scale, causal, rope_lb, O, dlse, Dout, L);
+    // zf_n > 0: the dK/dV kernel that follows adds its head subsets into zf_a
+    // and zf_b (zf_n floats each, a multiple of 4) atomically; every block
+    // (padding ones too) zeroes a slice of both after its own work, which
+    // saves a launch of its own
+    if (zf_n > 0) {
+        const long per = ((zf_n + gridDim.x - 1) / gridDim.x + 3) & ~3L;
+        const long end = min(zf_n, (long)(blockIdx.x + 1) * per);
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (long i = (long)blockIdx.x * per + 4 * threadIdx.x; i < end; i += 4 * 256) {
+            *(float4 *)(zf_a + i) = z;
+            *(float4 *)(zf_b + i) = z;
+        }
+    }
 }
 
 // Both gradients in one launch, ordered by a plan (see BwdPlan): groups of
@@ -1253,8 +1267,11 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
 hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, const float *lse,
                            const void *dout, const float *o, const float *dlse, float *Dws,
-                           float *dq, hipStream_t st, double rope_lb, const Layouts *L)
+                           float *dq, hipStream_t st, double rope_lb, const Layouts *L, float *zf_a,
+                           float *zf_b, long zf_n)
 {
+    if (zf_n % 4 != 0 || (zf_n > 0 && (((uintptr_t)zf_a | (uintptr_t)zf_b) & 15) != 0))
+        return hipErrorInvalidValue;
     if (d != 128) return hipErrorInvalidValue;
     const int nqt = (Nq + kQBM - 1) / kQBM;
     const dim3 grid((unsigned)((nqt * B * Hq + kXcds - 1) / kXcds * kXcds));
@@ -1263,7 +1280,7 @@ hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
         hipLaunchKernelGGL((bwd_dq_kernel<128, decltype(xc)::value, true, decltype(sc)::value>), grid,
                            dim3(256), 0, st, (const uint16_t *)q, (const uint16_t *)k,
                            (const uint16_t *)v, lse, (const uint16_t *)dout, nullptr, dq, B, Hq, Hkv, Nq,
-                           Nk, scale, causal, nqt, rope_lb, o, dlse, Dws, lay);
+                           Nk, scale, causal, nqt, rope_lb, o, dlse, Dws, lay, zf_a, zf_b, zf_n);
     });
 }
 

@@ -108,11 +108,14 @@ hipError_t bwd_dq_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
                        const void *dout, const float *Dws, float *dq, hipStream_t st,
                        double rope_lb = 0.0, const Layouts *L = nullptr);
 // dQ that also computes D_i = dO_i . O_i - dlse_i (O f32, dlse optional) into
-// Dws for a dK/dV kernel launched after it (bf16, d = 128)
+// Dws for a dK/dV kernel launched after it (bf16, d = 128), and zeroes zf_n
+// floats (a multiple of 4; 16-byte aligned) at zf_a and at zf_b for that
+// kernel's atomic head subsets
 hipError_t bwd_dq_pre_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                            const void *q, const void *k, const void *v, const float *lse,
                            const void *dout, const float *o, const float *dlse, float *Dws,
-                           float *dq, hipStream_t st, double rope_lb, const Layouts *L = nullptr);
+                           float *dq, hipStream_t st, double rope_lb, const Layouts *L = nullptr,
+                           float *zf_a = nullptr, float *zf_b = nullptr, long zf_n = 0);
 // Whether the one-launch plan of a shape fits its kernel argument (at most
 // 48 block groups); writes the group and block counts.  No device work.
 bool bwd_fused_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int hs, int *groups,
