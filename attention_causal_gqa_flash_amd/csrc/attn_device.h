@@ -374,19 +374,30 @@ __device__ __forceinline__ float wave_sum(float v)
 // its groups start first).  Otherwise blocks take items in plain
 // heaviest-first order.  Returns false for padding blocks (the grid is a
 // multiple of 8).
+// SNAKE, for grids whose workgroups are all resident at once: an XCD places
+// its items on its CUs in dispatch order, one per CU a round, and odd rounds
+// take their items in reverse, so that a CU holding a heavy item of one round
+// holds a light one of the next (the CU's total then decides its end).  With
+// more work than slots, blocks of later rounds start as slots free up and the
+// plain order packs better, so it is the default.
 struct WorkItem {
     int group, tile, head;
 };
 
 constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;   // MI355X: 256 CUs in 8 XCDs
 
+template <bool SNAKE = false>
 __device__ __forceinline__ bool xcd_work_item(int block, int groups, int tiles, int heads, WorkItem &w)
 {
     const int total = groups * tiles * heads;
     if (groups % kXcds == 0) {
         const int per_xcd = total / kXcds, gpx = groups / kXcds;
-        const int x = block % kXcds, k = block / kXcds;
-        if (k >= per_xcd) return false;
+        const int x = block % kXcds, kd = block / kXcds;
+        if (kd >= per_xcd) return false;
+        const int r = kd / kCusPerXcd, p = kd % kCusPerXcd;
+        const int k = (SNAKE && (r & 1) && (r + 1) * kCusPerXcd <= per_xcd)
+                          ? r * kCusPerXcd + kCusPerXcd - 1 - p : kd;
         const int level = k / (gpx * heads), rem = k % (gpx * heads);
         w.tile = tiles - 1 - level;
         w.group = x * gpx + rem / heads;

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
     const int G = Hq / Hkv;
     WorkItem w;
-    if (!xcd_work_item(blockIdx.x, B * Hkv, nqt, G, w)) return;
+    // small grids (two key halves) are resident at once: snake order
+    if (!xcd_work_item<KSPLIT == 2>(blockIdx.x, B * Hkv, nqt, G, w)) return;
     const int qt = w.tile;
     const int b = w.group / Hkv, g = w.group % Hkv;
     const int h = g * G + w.head;
