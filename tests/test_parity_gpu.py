@@ -349,6 +349,68 @@ def test_bwd_kv_square_equals_bwd(d):
 
 
 # ---------------------------------------------------------------------------
+# a seeded sweep of random shapes: the host-side choices (key split of the
+# forward, 64- or 128-key dK/dV kernel, head split, one-launch plan, generic
+# kernels) change with the grid, and these shapes land on both sides of them
+# ---------------------------------------------------------------------------
+
+def _sweep_cases(n=24, seed=20261203, max_work=1.5e9):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([16, 32, 64, 128], p=[0.1, 0.1, 0.4, 0.4]))
+        dtype = "f32" if (d <= 32 and rng.random() < 0.5) or rng.random() < 0.1 else "bf16"
+        Hkv = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        B = int(rng.integers(1, 5))
+        Nk = int(rng.integers(1, 1500))
+        Nq = Nk if rng.random() < 0.6 else int(rng.integers(1, Nk + 1))
+        causal = bool(rng.random() < 0.75)
+        if B * G * Hkv * Nq * Nk * d > max_work:   # keeps the oracle to about a second
+            continue
+        cases.append((B, G * Hkv, Hkv, Nq, Nk, d, dtype, causal))
+    return cases
+
+
+SWEEP = _sweep_cases() + [
+    # either side of the host's thresholds on a 256-CU part (short sequences, many heads):
+    # d = 64 forward: 512 128-row work items run unsplit, 510 split
+    (4, 128, 16, 128, 128, 64, "bf16", True),
+    (2, 255, 85, 128, 128, 64, "bf16", True),
+    # d = 128 forward: 256 items unsplit, 255 split
+    (2, 128, 32, 128, 128, 128, "bf16", True),
+    (1, 255, 85, 128, 128, 128, "bf16", True),
+    # d = 128 dK/dV: 4 x 2 key tiles x 32 kv heads reach 256 (128-key kernel), 31 do not
+    (2, 32, 16, 256, 256, 128, "bf16", True),
+    (1, 62, 31, 256, 256, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", SWEEP,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{c[6]}_{'c' if c[7] else 'nc'}"
+                              for c in SWEEP])
+def test_random_shape_sweep(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    print(f"\n[case] sweep B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal}",
+          flush=True)
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq * 131 + Nk * 7 + d, dout_scale=0.1)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    scale = float(np.float32(d ** -0.5))
+    gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
+    if Nq == Nk:
+        o, lse = attn.attn_fwd(gq, gk, gv, causal, scale)
+        dq, dk, dv = attn.attn_bwd(gq, gk, gv, o, lse, gdo, causal, scale)
+    else:
+        o, lse = attn.attn_fwd_kv(gq, gk, gv, causal, scale)
+        dq, dk, dv = attn.attn_bwd_kv(gq, gk, gv, o, lse, gdo, causal, scale)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    ro, rl = oracle.attn_fwd(q, x["k"], x["v"], causal, scale)
+    rdq, rdk, rdv = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
+    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"sweep Nq{Nq} Nk{Nk} d{d} {dtype}")
+
+
+# ---------------------------------------------------------------------------
 # bf16 output (attn_fwd_ex / attn_bwd_ex)
 # ---------------------------------------------------------------------------
 
