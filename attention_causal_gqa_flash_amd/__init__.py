@@ -15,7 +15,7 @@ import os
 __all__ = ["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
            "attn_bwd_grads", "attn_bwd_grads_plan", "attn_decode_append", "attn_fwd_kv",
            "attn_bwd_dlse", "attn_bwd_kv", "attn_rope", "attn_fwd_rope", "attn_bwd_rope",
-           "attn_fwd_ex", "attn_bwd_ex",
+           "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_bf16grad", "attn_bwd_bf16grad_workspace_bytes",
            "attn_bwd_dkdv", "attn_bwd_dq", "attn_decode", "attn_lse_merge",
            "attn_decode_merged", "attn_read_probe", "attn_bwd_noalloc", "attn_fwd_strided",
            "attn_bwd_strided", "AttnLayout",
@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_ex.restype = i
     L.attn_bwd_ex.argtypes = [i, i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
     L.attn_bwd_ex.restype = i
+    L.attn_bwd_bf16grad_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_bwd_bf16grad_workspace_bytes.restype = sz
+    L.attn_bwd_bf16grad.argtypes = [i, i, i, i, i, i, i, i, i, f] + [p] * 10 + [p, sz, p]
+    L.attn_bwd_bf16grad.restype = i
     L.attn_rope.argtypes = [i, i, i, i, i, ll, dbl, i, p, p, p]
     L.attn_rope.restype = i
     L.attn_fwd_rope.argtypes = [i, i, i, i, i, i, i, i, f, dbl] + [p] * 7 + [p]
@@ -417,6 +421,40 @@ def attn_bwd_ex(q, k, v, o, lse, dout, causal: bool = True, scale: float | None 
     """The general backward: o from attn_fwd_ex in either dtype, dlse optional."""
     return _bwd_call("attn_bwd_ex", q, k, v, o, lse, dout, dlse, causal, scale, dq, dk, dv,
                      workspace, stream)
+
+
+def attn_bwd_bf16grad_workspace_bytes(dtype_code: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                                      d: int) -> int:
+    return int(lib().attn_bwd_bf16grad_workspace_bytes(int(dtype_code), B, Hq, Hkv, Nq, Nk, d))
+
+
+def attn_bwd_bf16grad(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+                      dq=None, dk=None, dv=None, workspace=None, stream=None, dlse=None):
+    """attn_bwd_ex with the gradients in bfloat16 (each the float32 gradient rounded to
+    nearest even).  Returns (dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]), all bfloat16."""
+    torch = _torch()
+    B, Hq, Hkv, Nq, Nk, d = _qkv(q, k, v, square=False)
+    _expect(dout, (B, Hq, Nq, d), q.dtype, "dout", q)
+    _dev(o, "o")
+    _expect(o, (B, Hq, Nq, d), None, "o", q)
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse", q)
+    scale = _scale(scale, d)
+    code = _dtype_code(q)
+    dq = _out(dq, (B, Hq, Nq, d), torch.bfloat16, "dq", q, stream)
+    dk = _out(dk, (B, Hkv, Nk, d), torch.bfloat16, "dk", q, stream)
+    dv = _out(dv, (B, Hkv, Nk, d), torch.bfloat16, "dv", q, stream)
+    dlse_p = None if dlse is None else _ptr(_expect(dlse, (B, Hq, Nq), torch.float32, "dlse", q))
+    nbytes = attn_bwd_bf16grad_workspace_bytes(code, B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None:
+        workspace = _out(None, (max(nbytes, 256),), torch.uint8, "workspace", q, stream)
+    else:
+        _dev(workspace, "workspace")
+    rc = lib().attn_bwd_bf16grad(code, _dtype_code(o), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), dlse_p,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("attn_bwd_bf16grad", rc)
+    return dq, dk, dv
 
 
 def attn_rope(x, pos0: int, base: float, inverse: bool = False, y=None, stream=None):

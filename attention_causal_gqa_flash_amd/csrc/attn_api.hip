@@ -323,6 +323,51 @@ attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, 
                      dv, workspace, ws_bytes, stream, 0.0, o_dt == ATTN_BF16);
 }
 
+// Workspace of attn_bwd_bf16grad: the row terms, then f32 dq, dk and dv, each
+// section 256-byte aligned.
+static size_t bf16grad_sections(int B, int Hq, int Hkv, int Nq, int Nk, int d, size_t *off_dq,
+                                size_t *off_dk, size_t *off_dv)
+{
+    auto r256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t nq = (size_t)B * Hq * Nq * d, nk = (size_t)B * Hkv * Nk * d;
+    *off_dq = workspace_bytes(B, Hq, Nq);
+    *off_dk = *off_dq + r256(nq * sizeof(float));
+    *off_dv = *off_dk + r256(nk * sizeof(float));
+    return *off_dv + r256(nk * sizeof(float));
+}
+
+size_t attn_bwd_bf16grad_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int d)
+{
+    if (Nq <= 0 || Nk < Nq || check_common(dt, B, Hq, Hkv, Nk, d, 1.0f) != ATTN_OK) return 0;
+    size_t a, b, c;
+    return bf16grad_sections(B, Hq, Hkv, Nq, Nk, d, &a, &b, &c);
+}
+
+attn_status attn_bwd_bf16grad(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                              int d, int causal, float scale, const void *q, const void *k,
+                              const void *v, const void *o, const float *lse, const void *dout,
+                              const float *dlse, void *dq, void *dk, void *dv, void *workspace,
+                              size_t ws_bytes, void *stream)
+{
+    if (o_dt != ATTN_F32 && o_dt != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (dlse != nullptr && !aligned16(dlse)) return ATTN_ERR_INVALID_ARG;
+    if (Nq <= 0 || Nk < Nq) return ATTN_ERR_INVALID_ARG;
+    attn_status s = check_common(dt, B, Hq, Hkv, Nk, d, scale);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_INVALID_ARG;
+    size_t off_dq, off_dk, off_dv;
+    const size_t need = bf16grad_sections(B, Hq, Hkv, Nq, Nk, d, &off_dq, &off_dk, &off_dv);
+    if (!aligned16(workspace) || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+    char *w = (char *)workspace;
+    float *dq32 = (float *)(w + off_dq), *dk32 = (float *)(w + off_dk), *dv32 = (float *)(w + off_dv);
+    s = bwd_whole(dt, B, Hq, Hkv, Nq, Nk, d, causal, scale, q, k, v, o, lse, dout, dlse, dq32, dk32,
+                  dv32, workspace, off_dq, stream, 0.0, o_dt == ATTN_BF16);
+    if (s != ATTN_OK) return s;
+    const long nq = (long)B * Hq * Nq * d, nk = (long)B * Hkv * Nk * d;
+    return hip_status(attn::to_bf16_3(dq32, (uint16_t *)dq, nq, dk32, (uint16_t *)dk, nk, dv32,
+                                      (uint16_t *)dv, nk, (hipStream_t)stream));
+}
+
 attn_status attn_fwd_strided(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
                              int d, int causal, float scale, const void *q, const attn_layout *lq,
                              const void *k, const attn_layout *lk, const void *v,

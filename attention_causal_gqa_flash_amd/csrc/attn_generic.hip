@@ -103,6 +103,26 @@ __global__ __launch_bounds__(256) void zero_fill2_kernel(float *__restrict__ a, 
     zero2_grid_stride(a, b, n);
 }
 
+// Three f32 arrays rounded to bf16 (nearest even), eight elements a thread
+// per step over their concatenation: array i holds 8 n8_i elements.
+__global__ __launch_bounds__(256) void to_bf16_3_kernel(const float *__restrict__ s0, uint16_t *__restrict__ d0,
+                                                        long n0, const float *__restrict__ s1,
+                                                        uint16_t *__restrict__ d1, long n1,
+                                                        const float *__restrict__ s2,
+                                                        uint16_t *__restrict__ d2, long n2)
+{
+    const long total = n0 + n1 + n2;
+    for (long i = blockIdx.x * 256L + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+        const bool a = i < n0, b = !a && i < n0 + n1;
+        const float *src = a ? s0 : b ? s1 : s2;
+        uint16_t *dst = a ? d0 : b ? d1 : d2;
+        const long j = a ? i : b ? i - n0 : i - n0 - n1;
+        const float4 x = ((const float4 *)src)[2 * j], y = ((const float4 *)src)[2 * j + 1];
+        ((uint4 *)dst)[j] = make_uint4(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y),
+                                       pack_bf16x2(y.z, y.w));
+    }
+}
+
 // Row r of the B*Hq*N rows is query row r % N of head (r / N) % Hq of batch
 // r / (Hq N); dout and o have the strides of L.dout and L.o.
 template <typename T, int D, typename OT>
@@ -546,6 +566,17 @@ hipError_t bwd_preprocess(int dt, int B, int Hq, int N, int d, const void *dout,
                                                                   (const float *)o, Dws, rows, zero,
                                                                   zero2, zero_len, dlse, Hq, N, lay)));
     }
+    return hipGetLastError();
+}
+
+hipError_t to_bf16_3(const float *s0, uint16_t *d0, long n0, const float *s1, uint16_t *d1, long n1,
+                     const float *s2, uint16_t *d2, long n2, hipStream_t st)
+{
+    if (n0 % 8 || n1 % 8 || n2 % 8) return hipErrorInvalidValue;
+    const long total = (n0 + n1 + n2) / 8;
+    const long blocks = std::min<long>((total + 255) / 256, 8192L);
+    hipLaunchKernelGGL(to_bf16_3_kernel, dim3((unsigned)std::max<long>(blocks, 1)), dim3(256), 0, st, s0, d0,
+                       n0 / 8, s1, d1, n1 / 8, s2, d2, n2 / 8);
     return hipGetLastError();
 }
 

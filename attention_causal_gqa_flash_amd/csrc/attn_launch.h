@@ -70,6 +70,10 @@ int device_cus();
 hipError_t read_probe(const void *src, long bytes, unsigned *out, hipStream_t st);
 // Zero-fill two float buffers of n elements each (a small fill kernel; no memset).
 hipError_t zero_fill2(float *a, float *b, long n, hipStream_t st);
+// s_i (f32, n_i elements, n_i a multiple of 8, 16-byte aligned) rounded to
+// bf16 (nearest even) into d_i, in one launch.
+hipError_t to_bf16_3(const float *s0, uint16_t *d0, long n0, const float *s1, uint16_t *d1, long n1,
+                     const float *s2, uint16_t *d2, long n2, hipStream_t st);
 
 // Matrix-core kernels: bf16 inputs, d in {64, 128}.  The gradient launchers'
 // rope_lb (log2 of the rotary base; 0: none, so a base of 1 is left to the

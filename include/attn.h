@@ -216,6 +216,34 @@ attn_status attn_bwd_ex(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, 
                         size_t workspace_bytes, void *stream);
 
 /*
+ * attn_bwd_bf16grad_workspace_bytes -- device workspace attn_bwd_bf16grad
+ *   needs, in bytes: the row terms of attn_bwd_ex, then f32 copies of dq, dk
+ *   and dv (each section rounded up to 256 bytes).  Returns 0 for invalid
+ *   shapes (as attn_bwd_ex would refuse them).
+ */
+size_t attn_bwd_bf16grad_workspace_bytes(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                                         int d);
+
+/*
+ * attn_bwd_bf16grad -- attn_bwd_ex with the gradients written in bf16: dq
+ *   [B][Hq][Nq][d], dk/dv [B][Hkv][Nk][d], each the f32 gradient of attn_bwd_ex
+ *   (same formulas: "How tang works" part 3) rounded to nearest even.  The
+ *   pages fix no output precision; the gradients are accumulated in f32 and
+ *   rounded once.  The f32 gradients are computed into the workspace (at least
+ *   attn_bwd_bf16grad_workspace_bytes(...) bytes, caller-owned, contents on
+ *   entry irrelevant; dq, dk, dv must not overlap it) and then rounded by one
+ *   more launch on `stream`, so the call moves the f32 gradients through HBM
+ *   twice more than attn_bwd_ex.  dq, dk, dv 16-byte aligned.  Other
+ *   arguments, checks and error codes as attn_bwd_ex; a short workspace gives
+ *   ATTN_ERR_WORKSPACE.
+ */
+attn_status attn_bwd_bf16grad(attn_dtype dt, attn_dtype o_dt, int B, int Hq, int Hkv, int Nq, int Nk,
+                              int d, int causal, float scale, const void *q, const void *k,
+                              const void *v, const void *o, const float *lse, const void *dout,
+                              const float *dlse, void *dq, void *dk, void *dv, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * Strides of a 4-D tensor [B][H][N][d] whose head dim is contiguous, in
  * elements: element (b, h, n, c) sits at b*batch + h*head + n*row + c.  The
  * contiguous layout is {H*N*d, N*d, d}; interleaved heads ([B][N][H][d], as

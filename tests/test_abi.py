@@ -40,6 +40,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("attn_fwd", "attn_fwd_kv", "attn_bwd", "attn_bwd_dlse", "attn_bwd_kv",
                      "attn_rope", "attn_fwd_rope", "attn_bwd_rope", "attn_fwd_ex", "attn_bwd_ex",
+                     "attn_bwd_bf16grad", "attn_bwd_bf16grad_workspace_bytes",
                      "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
                      "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads",
                      "attn_bwd_grads_plan", "attn_decode", "attn_decode_append",
@@ -93,6 +94,44 @@ def test_workspace_size(L):
     assert L.attn_bwd_workspace_bytes(0, 1, 2, 1, 3, 16) == 256
     assert L.attn_bwd_workspace_bytes(1, 1, 6, 4, 64, 64) == 0     # Hq % Hkv != 0
     assert L.attn_bwd_workspace_bytes(1, 1, 4, 4, 64, 48) == 0     # unsupported d
+
+
+def test_bf16grad_workspace_size(L):
+    r256 = lambda x: (x + 255) // 256 * 256
+    # row terms, then f32 dq [B,Hq,Nq,d], dk and dv [B,Hkv,Nk,d]
+    B, Hq, Hkv, Nq, Nk, d = 2, 12, 4, 1000, 1024, 64
+    want = r256(B * Hq * Nq * 4) + r256(B * Hq * Nq * d * 4) + 2 * r256(B * Hkv * Nk * d * 4)
+    assert L.attn_bwd_bf16grad_workspace_bytes(1, B, Hq, Hkv, Nq, Nk, d) == want
+    assert L.attn_bwd_bf16grad_workspace_bytes(0, 1, 2, 1, 3, 3, 16) == 256 + 512 + 2 * 256
+    assert L.attn_bwd_bf16grad_workspace_bytes(1, 1, 4, 2, 65, 64, 64) == 0   # Nq > Nk
+    assert L.attn_bwd_bf16grad_workspace_bytes(1, 1, 6, 4, 64, 64, 64) == 0   # Hq % Hkv != 0
+    assert L.attn_bwd_bf16grad_workspace_bytes(1, 1, 4, 4, 64, 64, 48) == 0   # unsupported d
+
+
+def _bwd_g(L, ws=P, ws_bytes=1 << 30, ptrs=None, **kw):
+    a = dict(dt=1, o_dt=0, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=64, causal=1, scale=0.125)
+    a.update(kw)
+    ptrs = ptrs or [P] * 10
+    return L.attn_bwd_bf16grad(a["dt"], a["o_dt"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                               a["causal"], a["scale"], *ptrs, ws, ws_bytes, NUL)
+
+
+def test_bf16grad_refusals(L):
+    # every refusal is decided on the host, before any launch
+    assert _bwd_g(L, o_dt=7) == INVALID
+    assert _bwd_g(L, Nq=65) == INVALID
+    assert _bwd_g(L, Hq=5) == INVALID
+    assert _bwd_g(L, d=96) == UNSUPPORTED
+    for which in (7, 8, 9):          # dq, dk, dv
+        ptrs = [P] * 10
+        ptrs[which] = MIS
+        assert _bwd_g(L, ptrs=ptrs) == INVALID
+    ptrs = [P] * 10
+    ptrs[6] = MIS                    # dlse misaligned
+    assert _bwd_g(L, ptrs=ptrs) == INVALID
+    need = L.attn_bwd_bf16grad_workspace_bytes(1, 1, 4, 2, 64, 64, 64)
+    assert _bwd_g(L, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd_g(L, ws=MIS) == WORKSPACE
 
 
 def _bwd(L, ws=P, ws_bytes=1 << 20, ptrs=None, **kw):

@@ -27,6 +27,7 @@ def cpu_stand_in(monkeypatch):
     monkeypatch.setattr(attn, "_dev", dev)
     monkeypatch.setattr(attn, "lib", lambda: _NoLib())
     monkeypatch.setattr(attn, "attn_bwd_workspace_bytes", lambda *a: 1024)
+    monkeypatch.setattr(attn, "attn_bwd_bf16grad_workspace_bytes", lambda *a: 1024)
 
 
 def _t(*shape, dtype=torch.bfloat16):
@@ -69,6 +70,20 @@ def test_bwd_refuses_mismatched_inputs(bad):
 def test_bwd_refuses_wrong_outputs(name, shape, dtype):
     with pytest.raises(ValueError):
         attn.attn_bwd(**_bwd_args(), **{name: torch.zeros(shape, dtype=dtype)})
+
+
+@pytest.mark.parametrize("bad", [
+    dict(k=_t(B, Hkv, N, d, dtype=torch.float32)),
+    dict(o=_t(B, Hq, N + 1, d, dtype=torch.float32)),        # o from another call
+    dict(lse=_t(B, Hq, N)),
+    dict(dout=_t(B, Hq, N - 1, d)),
+    dict(dq=torch.zeros((B, Hq, N, d), dtype=torch.float32)),  # the gradients are bf16
+    dict(dk=torch.zeros((B, Hkv + 1, N, d), dtype=torch.bfloat16)),
+    dict(dlse=_t(B, Hq, N + 3, dtype=torch.float32)),
+])
+def test_bf16grad_refuses_mismatched_arguments(bad):
+    with pytest.raises((ValueError, TypeError)):
+        attn.attn_bwd_bf16grad(**_bwd_args(**bad))
 
 
 def test_bwd_kv_forms_check_the_cross_length_shapes():

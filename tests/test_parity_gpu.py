@@ -411,6 +411,57 @@ def test_random_shape_sweep(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
 
 
 # ---------------------------------------------------------------------------
+# bf16 gradients (attn_bwd_bf16grad): the f32 gradients of attn_bwd_ex rounded
+# to nearest even
+# ---------------------------------------------------------------------------
+
+BF16_GRAD = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype, causal, with_dlse, o dtype
+    (2, 12, 4, 300, 300, 64, "bf16", True, False, "f32"),
+    (1, 8, 2, 200, 700, 128, "bf16", True, True, "bf16"),    # cross-length, dlse, bf16 o
+    (4, 12, 4, 256, 1024, 64, "bf16", True, False, "f32"),   # dK/dV head subsets added by atomics
+    (1, 4, 2, 100, 100, 32, "f32", False, False, "f32"),     # generic kernels
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal,with_dlse,o_dtype", BF16_GRAD,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{c[6]}_{'c' if c[7] else 'nc'}"
+                              f"{'_dlse' if c[8] else ''}_o{c[9]}" for c in BF16_GRAD])
+def test_bf16_gradients(B, Hq, Hkv, Nq, Nk, d, dtype, causal, with_dlse, o_dtype):
+    print(f"\n[case] bf16grad B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
+          f"dlse={with_dlse} o={o_dtype}", flush=True)
+    x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq * 5 + Nk + d, dout_scale=0.1)
+    q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
+    do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
+    dl = (np.random.default_rng(Nk).standard_normal((B, Hq, Nq)).astype(np.float32) * 0.3
+          if with_dlse else None)
+    scale = float(np.float32(d ** -0.5))
+    gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
+    gdl = None if dl is None else torch.from_numpy(dl).cuda()
+    o, lse = attn.attn_fwd_ex(gq, gk, gv, causal, scale,
+                              o_dtype=torch.bfloat16 if o_dtype == "bf16" else torch.float32)
+    g16 = attn.attn_bwd_bf16grad(gq, gk, gv, o, lse, gdo, causal, scale, dlse=gdl)
+    g32 = attn.attn_bwd_ex(gq, gk, gv, o, lse, gdo, causal, scale, dlse=gdl)
+    torch.cuda.synchronize()
+    assert all(t.dtype == torch.bfloat16 for t in g16)
+    assert g16[0].shape == (B, Hq, Nq, d) and g16[1].shape == (B, Hkv, Nk, d)
+    # the same f32 values rounded once: dq is deterministic; dk, dv may carry atomics
+    # (order-dependent last bits of the f32 value, so at most one bf16 step apart)
+    assert torch.equal(g16[0], g32[0].to(torch.bfloat16))
+    for a, b in zip(g16[1:], g32[1:]):
+        r = b.to(torch.bfloat16).float()
+        assert float((a.float() - r).abs().max()) <= float(r.abs().max()) * 2.0 ** -7
+    # against the oracle at the bf16 gradient tolerance
+    if dl is None:
+        ref = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
+    else:
+        ref = oracle.attn_bwd_dlse(q, x["k"], x["v"], do, dl.astype(np.float64), causal, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), g16, ref):
+        e = _relF(a.float().cpu().numpy().astype(np.float64), b)
+        assert e <= 2e-2, f"bf16grad {name}: relF {e:.3e}"
+
+
+# ---------------------------------------------------------------------------
 # bf16 output (attn_fwd_ex / attn_bwd_ex)
 # ---------------------------------------------------------------------------
 
