@@ -167,10 +167,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 
 // KSPLIT = 1: one workgroup = 4 waves = 128 query rows (32 per wave), every
 // wave streaming all the key tiles of its query tile.
-// KSPLIT = 2 (small grids, d = 64): one workgroup = 64 query rows; waves
-// (row half, key half) -- the two key halves stream disjoint halves of the
-// key tiles side by side and their softmax states combine through LDS at the
-// end with the associative merge, which halves the longest chain of tiles.
+// KSPLIT = 2 (small grids): one workgroup = 64 query rows; waves (row half,
+// key half) -- the two key halves stream disjoint halves of the key tiles
+// side by side and their softmax states combine through LDS at the end with
+// the associative merge, which halves the longest chain of tiles.  KSPLIT = 4
+// (smaller grids, d = 64): 32 query rows, the four waves each streaming a
+// quarter of the key tiles.
 // OBF: O is written in bf16 (rounded to nearest even) instead of f32.
 // ROPE: q arrives unrotated; each lane turns its Q row (position i + Nk - Nq)
 // by the rotary angles right after loading it -- the lane already holds both
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     const int G = Hq / Hkv;
     WorkItem w;
     // small grids (two key halves) are resident at once: snake order
-    if (!xcd_work_item<KSPLIT == 2>(blockIdx.x, B * Hkv, nqt, G, w)) return;
+    if (!xcd_work_item<(KSPLIT > 1)>(blockIdx.x, B * Hkv, nqt, G, w)) return;
     const int qt = w.tile;
     const int b = w.group / Hkv, g = w.group % Hkv;
     const int h = g * G + w.head;
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         uint16_t *qrot_h = Qrot + ((size_t)b * Hq + h) * (size_t)Nq * D;
         auto write_rows = [&](const uint16_t *qt, int r0) {
 #pragma unroll 1
-            for (int c = tid; c < 64 * CPR; c += 256) {
+            for (int c = tid; c < (BMW < 64 ? BMW : 64) * CPR; c += 256) {
                 const int r = c / CPR, ch = c % CPR;
                 if (q0 + r0 + r < Nq)
                     *(uint4 *)(qrot_h + (size_t)(q0 + r0 + r) * D + 8 * ch) =
@@ -319,15 +321,14 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     };
     const int kv_end = causal ? min(Nk, q0 + off + BMW) : Nk;
     const int ntiles = (kv_end + TN - 1) / TN;
-    // key half 0 takes tiles [0, ntA), key half 1 tiles [ntA, ntiles).  A row
-    // may see no key of one half (its max stays -inf, its weights are zeros);
-    // the half holding tile 0 holds key 0, which every row sees.
-    const int ntA = KSPLIT == 2 ? ntiles / 2 : 0;
-    const int nsteps = ntiles - ntA;
-    auto tile_of = [&](int half, int s_) { return half == 0 && KSPLIT == 2 ? s_ : ntA + s_; };
-    auto valid = [&](int half, int s_) {
-        return (half == 0 && KSPLIT == 2) ? s_ < ntA : s_ < nsteps;
-    };
+    // Key part p (of KSPLIT) takes consecutive tiles from tile_of(p, 0); the
+    // parts' counts differ by at most one, the later parts holding the extra
+    // tiles.  A row may see no key of a part (its max stays -inf, its weights
+    // are zeros); the part holding tile 0 holds key 0, which every row sees.
+    const int kbase = ntiles / KSPLIT, krem = ntiles % KSPLIT;
+    const int nsteps = kbase + (krem > 0 ? 1 : 0);
+    auto tile_of = [&](int part, int s_) { return part * kbase + max(0, part - (KSPLIT - krem)) + s_; };
+    auto valid = [&](int part, int s_) { return s_ < kbase + (part >= KSPLIT - krem ? 1 : 0); };
 
     // Tiles move global -> LDS directly (no staging registers); rows past N
     // read as zero, their scores are masked; copies of tiles that do not
@@ -391,35 +392,56 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
         if (s_ + 1 < nsteps) run_step(Buf<1>{}, s_ + 1);
     }
 
-    if constexpr (KSPLIT == 2) {
-        // Key half 1 parks (O^T, m, l) per lane in LDS; key half 0 merges:
-        // m = max(mA, mB), O = OA 2^(mA-m) + OB 2^(mB-m), l likewise.  One half
-        // saw key 0, so m is finite (a half that saw no key has m = -inf).
-        float *po = reinterpret_cast<float *>(rw == 0 ? sk0 : sk1);   // [DB*16][64] per row wave
-        float *pm = reinterpret_cast<float *>(sv0);                   // [rw][2][64]
-        static_assert(RW == 2 && DB * 16 * 64 * sizeof(float) <= sizeof(sk0), "partial O fits");
-        static_assert(RW * 2 * 64 * sizeof(float) <= sizeof(sv0), "partial m, l fit");
+    if constexpr (KSPLIT > 1) {
+        // Key parts 1 .. KSPLIT-1 park (O^T, m, l) per lane in LDS and part 0
+        // merges them: m = max of the parts' m, O = sum of O_p 2^(m_p - m), l
+        // likewise.  The part that saw key 0 has a finite m; a part that saw no
+        // key has m = -inf and weight 0.
+        constexpr int SLOT = DB * 16 * 64;                               // floats of one parked O^T
+        constexpr int CAP = (int)(sizeof(sk0) / (SLOT * sizeof(float))); // slots per array
+        constexpr int NSLOT = RW * (KSPLIT - 1);
+        static_assert(CAP >= 1 && NSLOT <= 2 * CAP, "parked O^T fits sk0 and sk1");
+        static_assert(NSLOT * 2 * 64 * sizeof(float) <= sizeof(sv0), "parked m, l fit sv0");
+        auto slot_o = [&](int slot) {
+            float *a = reinterpret_cast<float *>(slot < CAP ? sk0 : sk1);
+            return a + (slot % CAP) * SLOT;
+        };
+        float *pm = reinterpret_cast<float *>(sv0);                      // [slot][m, l][64]
         wait_vmcnt<0>();
         __syncthreads();
-        if (kh == 1) {
+        if (kh > 0) {
+            const int slot = rw * (KSPLIT - 1) + kh - 1;
+            float *po = slot_o(slot);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64 + lane] = st.oacc[db][r];
-            pm[(rw * 2 + 0) * 64 + lane] = st.m_run;
-            pm[(rw * 2 + 1) * 64 + lane] = st.l_sum();
+            pm[(slot * 2 + 0) * 64 + lane] = st.m_run;
+            pm[(slot * 2 + 1) * 64 + lane] = st.l_sum();
         }
         __syncthreads();
-        if (kh == 1) return;
-        const float mB = pm[(rw * 2 + 0) * 64 + lane], lB = pm[(rw * 2 + 1) * 64 + lane];
-        const float m = fmaxf(st.m_run, mB);
-        const float ea = exp2_fast(st.m_run - m), eb = exp2_fast(mB - m);
+        if (kh > 0) return;
+        float m = st.m_run;
+#pragma unroll
+        for (int p = 1; p < KSPLIT; ++p) m = fmaxf(m, pm[((rw * (KSPLIT - 1) + p - 1) * 2) * 64 + lane]);
+        const float ea = exp2_fast(st.m_run - m);
+        float l = st.l_sum() * ea;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                st.oacc[db][r] = st.oacc[db][r] * ea + po[(db * 16 + r) * 64 + lane] * eb;
-        st.lq[0] = st.l_sum() * ea + lB * eb;
+            for (int r = 0; r < 16; ++r) st.oacc[db][r] *= ea;
+#pragma unroll
+        for (int p = 1; p < KSPLIT; ++p) {
+            const int slot = rw * (KSPLIT - 1) + p - 1;
+            const float *po = slot_o(slot);
+            const float e = exp2_fast(pm[(slot * 2 + 0) * 64 + lane] - m);
+            l += pm[(slot * 2 + 1) * 64 + lane] * e;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.oacc[db][r] += po[(db * 16 + r) * 64 + lane] * e;
+        }
+        st.lq[0] = l;
         st.lq[1] = st.lq[2] = st.lq[3] = 0.f;
         st.m_run = m;
     }
@@ -464,6 +486,12 @@ hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
     // the 128-row workgroups would leave CUs empty.
     const long items = (long)nqt * B * Hq;
     const bool split = d == 64 ? items < 2L * cus : items < cus;
+    // d = 64, four key parts (32-row workgroups, 64 KB of LDS, two per CU):
+    // when all of them fit on the CUs at once, i.e. at most half a 128-row item
+    // per CU.  Measured on MI355X (forward, causal): 96 items (1 x 12 heads x
+    // 1024) 10.9 -> 8.3 us, 128 items 7.45 -> 6.4 us; at 192 and 256 items,
+    // where the grid takes a second round, 7.9 -> 10.7 and 8.3 -> 11.1 us.
+    const bool split4 = d == 64 && 2 * items <= cus;
     auto grid_of = [&](int n_tiles) {
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
@@ -479,6 +507,10 @@ hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
     } else if (d == 64 && !split) {
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 1, kBN, OBF, ROPE, STR>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv,
                            o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt, qr, rope_lb, L);
+    } else if (d == 64 && split4) {
+        const int nqt32 = (Nq + 31) / 32;
+        hipLaunchKernelGGL((fwd_mfma_kernel<64, 4, 32, OBF, ROPE, STR>), grid_of(nqt32), dim3(256), 0, st, qq, kk, vv,
+                           o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt32, qr, rope_lb, L);
     } else if (d == 64) {
         hipLaunchKernelGGL((fwd_mfma_kernel<64, 2, 32, OBF, ROPE, STR>), grid_of(nqt64), dim3(256), 0, st, qq, kk, vv,
                            o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt64, qr, rope_lb, L);

@@ -374,6 +374,9 @@ def _sweep_cases(n=24, seed=20261203, max_work=1.5e9):
 
 SWEEP = _sweep_cases() + [
     # either side of the host's thresholds on a 256-CU part (short sequences, many heads):
+    # d = 64 forward: 128 128-row work items take four key parts, 132 two
+    (1, 128, 16, 128, 128, 64, "bf16", True),
+    (1, 132, 12, 128, 128, 64, "bf16", True),
     # d = 64 forward: 512 128-row work items run unsplit, 510 split
     (4, 128, 16, 128, 128, 64, "bf16", True),
     (2, 255, 85, 128, 128, 64, "bf16", True),
