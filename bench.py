@@ -7,7 +7,11 @@ resident in device memory:
     (default: the largest one, bf16, B=1, 32 query / 8 key-value heads,
     N=4096, d=128; at d=128 attn_bwd runs the dQ kernel, which also computes
     the preprocess's row terms, then the dK/dV kernel; at d=64 the preprocess
-    then one kernel holding both the dK/dV and the dQ work);
+    then one kernel holding both the dK/dV and the dQ work), each step on the
+    next of several distinct sets of inputs and outputs (more than 512 MB
+    together, twice the last-level cache), so that every step reads its
+    inputs from HBM; `train_input_sets` gives the count and the training
+    op's time on one set, whose inputs stay cached from step to step;
   * the decode op: split-KV decode + LSE merge (attn_decode_merged: the decode
     kernel then the merge kernel) on the decode workload (bf16, 32/8 heads,
     d=128, a 4096-key cache in 16 splits), each step on the next of 24
@@ -102,6 +106,11 @@ def parse():
                          "passes (MFMA busy, LDS, VALU, waits per kernel) as markdown")
     return ap.parse_args()
 
+
+# The training op rotates over input sets of at least this many bytes together
+# (twice the 256 MB last-level cache), at most TRAIN_MAX_SETS of them.
+TRAIN_ROTATE_BYTES = 512 << 20
+TRAIN_MAX_SETS = 32
 
 # Size of the calibration copy: far beyond L2 and the last-level cache.
 CALIB_BYTES = 1 << 30
@@ -385,11 +394,13 @@ def main():
     T = Timer(torch, args.min_iters)
     f32 = dict(device=dev, dtype=torch.float32)
 
-    def train_setup(cfg):
-        """Device inputs and outputs of a training workload, and its launch callables."""
+    def train_setup(cfg, like=None):
+        """Device inputs and outputs of a training workload, and its launch callables
+        (like: the device inputs of another set, copied instead of drawn again)."""
         tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-        x = W.train_inputs(cfg)
-        g = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()}
+        x = W.train_inputs(cfg) if like is None else None
+        g = ({n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()} if like is None
+             else {n: a.clone() for n, a in like.items()})
         B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
         t = {"o": torch.empty((B, Hq, N, d), **f32), "lse": torch.empty((B, Hq, N), **f32),
              "delta": torch.empty((B, Hq, N), **f32), "dq": torch.empty((B, Hq, N, d), **f32),
@@ -416,6 +427,13 @@ def main():
     cfg = W.TRAIN_CONFIGS[args.workload]
     B, Hq, Hkv, N, d = cfg.B, cfg.Hq, cfg.Hkv, cfg.N, cfg.d
     x, g, tt, fns = train_setup(cfg)
+    # The training op runs on distinct sets of inputs and outputs in turn, as
+    # many as make more than TRAIN_ROTATE_BYTES together (twice the 256 MB
+    # last-level cache), so that each step reads its inputs from HBM rather
+    # than finding the previous step's copy cached.
+    set_bytes = sum(a.numel() * a.element_size() for a in list(g.values()) + list(tt.values()))
+    nsets = int(min(TRAIN_MAX_SETS, max(2, math.ceil(TRAIN_ROTATE_BYTES / set_bytes))))
+    train_sets = [(g, tt, fns)] + [train_setup(cfg, like=g)[1:] for _ in range(nsets - 1)]
     fns["fwd"]()
     fns["bwd_preprocess"]()
     torch.cuda.synchronize()
@@ -450,9 +468,9 @@ def main():
         kv = caches[i % ncache]
         return lambda: attn.attn_read_probe(kv, out=probe_out)
 
-    def train_op():
-        fns["fwd"]()
-        fns["bwd"]()
+    def train_op(i):
+        f = train_sets[i % nsets][2]
+        return lambda: (f["fwd"](), f["bwd"]())
 
     # ---------------------------------------------------------------- the timed region
     # K steps = R replays of a graph of M steps (each step: the training op,
@@ -465,7 +483,7 @@ def main():
     K = R * M
     if args.eager:
         for s in range(Wm):
-            train_op()
+            train_op(s)()
             decode(s)()
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(R)]
@@ -473,12 +491,12 @@ def main():
         for r in range(R):
             ev[r][0].record()
             for s in range(M):
-                train_op()
+                train_op(r * M + s)()
                 decode(r * M + s)()
             ev[r][1].record()
         torch.cuda.synchronize()
     else:
-        steps = [f for s in range(M) for f in (train_op, decode(s))]
+        steps = [f for s in range(M) for f in (train_op(s), decode(s))]
         g_step = T.graph(steps)
         for _ in range(max(1, math.ceil(Wm / M))):
             g_step.replay()
@@ -500,9 +518,12 @@ def main():
         value = float("nan")
     else:
         # the two ops of the step, each timed alone: medians over >= 100 replays
-        # of graphs of ~2 ms of that op (the training op; the decode op
-        # rotating over the caches)
-        tr = T.op(train_op)
+        # of graphs of ~2 ms of that op (the training op rotating over its input
+        # sets; the decode op rotating over the caches); and the training op on
+        # one set, whose inputs then stay cached between steps
+        nt = max(nsets, T.ops_for(train_op(0)) // nsets * nsets)
+        tr = T.median_us([train_op(i) for i in range(nt)], nt)
+        tr_one = T.op(train_op(0))
         nd = max(ncache, T.ops_for(decode(0)) // ncache * ncache)
         dr = T.median_us([decode(i) for i in range(nd)], nd)
         train_us, dec_us = tr["median_us"], dr["median_us"]
@@ -527,6 +548,8 @@ def main():
                    "causal": True, "decode_workload": dcfg.name},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_bwd_us": round(train_us, 3),
+        "train_input_sets": {"sets": nsets, "bytes_per_set": set_bytes,
+                             "fwd_bwd_us_one_set": None if args.eager else tr_one["median_us"]},
         "decode": {"GB_per_s": round(dec_gbs, 1), "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "us_per_call": round(dec_us, 3), "bytes": dec_bytes, "distinct_caches": ncache,
                    "launches_per_call": 2},
