@@ -10,6 +10,7 @@ Both sides see the same inputs: float32 draws rounded to bf16 where the
 workload is bf16, widened exactly for the oracle.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -354,7 +355,7 @@ def test_bwd_kv_square_equals_bwd(d):
 # kernels) change with the grid, and these shapes land on both sides of them
 # ---------------------------------------------------------------------------
 
-def _sweep_cases(n=24, seed=20261203, max_work=1.5e9):
+def _sweep_cases(n, seed, max_work=1.5e9):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
@@ -366,51 +367,67 @@ def _sweep_cases(n=24, seed=20261203, max_work=1.5e9):
         Nk = int(rng.integers(1, 1500))
         Nq = Nk if rng.random() < 0.6 else int(rng.integers(1, Nk + 1))
         causal = bool(rng.random() < 0.75)
+        dlse = bool(rng.random() < 0.25)                      # an upstream gradient of lse
+        obf = dtype == "bf16" and bool(rng.random() < 0.25)   # O written in bf16
+        gbf = bool(rng.random() < 0.2)                        # gradients written in bf16
+        neg = bool(rng.random() < 0.1)                        # a negative scale
         if B * G * Hkv * Nq * Nk * d > max_work:   # keeps the oracle to about a second
             continue
-        cases.append((B, G * Hkv, Hkv, Nq, Nk, d, dtype, causal))
+        cases.append((B, G * Hkv, Hkv, Nq, Nk, d, dtype, causal, dlse, obf, gbf, neg))
     return cases
 
 
-SWEEP = _sweep_cases() + [
+# ATTN_SWEEP_N / ATTN_SWEEP_SEED select a longer run (e.g. 1000 shapes)
+SWEEP = _sweep_cases(int(os.environ.get("ATTN_SWEEP_N", "24")),
+                     int(os.environ.get("ATTN_SWEEP_SEED", "20261203"))) + [
     # either side of the host's thresholds on a 256-CU part (short sequences, many heads):
     # d = 64 forward: 128 128-row work items take four key parts, 132 two
-    (1, 128, 16, 128, 128, 64, "bf16", True),
-    (1, 132, 12, 128, 128, 64, "bf16", True),
+    (1, 128, 16, 128, 128, 64, "bf16", True, False, False, False, False),
+    (1, 132, 12, 128, 128, 64, "bf16", True, False, False, False, False),
     # d = 64 forward: 512 128-row work items run unsplit, 510 split
-    (4, 128, 16, 128, 128, 64, "bf16", True),
-    (2, 255, 85, 128, 128, 64, "bf16", True),
+    (4, 128, 16, 128, 128, 64, "bf16", True, False, False, False, False),
+    (2, 255, 85, 128, 128, 64, "bf16", True, False, False, False, False),
     # d = 128 forward: 256 items unsplit, 255 split
-    (2, 128, 32, 128, 128, 128, "bf16", True),
-    (1, 255, 85, 128, 128, 128, "bf16", True),
+    (2, 128, 32, 128, 128, 128, "bf16", True, False, False, False, False),
+    (1, 255, 85, 128, 128, 128, "bf16", True, False, False, False, False),
     # d = 128 dK/dV: 4 x 2 key tiles x 32 kv heads reach 256 (128-key kernel), 31 do not
-    (2, 32, 16, 256, 256, 128, "bf16", True),
-    (1, 62, 31, 256, 256, 128, "bf16", True),
+    (2, 32, 16, 256, 256, 128, "bf16", True, False, False, False, False),
+    (1, 62, 31, 256, 256, 128, "bf16", True, False, False, False, False),
 ]
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", SWEEP,
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal,dlse,obf,gbf,neg", SWEEP,
                          ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{c[6]}_{'c' if c[7] else 'nc'}"
-                              for c in SWEEP])
-def test_random_shape_sweep(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
-    print(f"\n[case] sweep B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal}",
-          flush=True)
+                              f"{'_dlse' if c[8] else ''}{'_obf' if c[9] else ''}{'_gbf' if c[10] else ''}"
+                              f"{'_neg' if c[11] else ''}" for c in SWEEP])
+def test_random_shape_sweep(B, Hq, Hkv, Nq, Nk, d, dtype, causal, dlse, obf, gbf, neg):
+    print(f"\n[case] sweep B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
+          f"dlse={dlse} o_bf16={obf} grads_bf16={gbf} neg_scale={neg}", flush=True)
     x = W.random_train(B, Hq, Hkv, Nk, d, dtype=dtype, seed=Nq * 131 + Nk * 7 + d, dout_scale=0.1)
     q = np.ascontiguousarray(x["q"][:, :, Nk - Nq:])
     do = np.ascontiguousarray(x["dout"][:, :, Nk - Nq:])
-    scale = float(np.float32(d ** -0.5))
+    dl = (np.random.default_rng(Nq + Nk).standard_normal((B, Hq, Nq)).astype(np.float32) * 0.3
+          if dlse else None)
+    scale = float(np.float32(d ** -0.5 * (-0.7 if neg else 1.0)))
     gq, gk, gv, gdo = (_to_dev(a, dtype) for a in (q, x["k"], x["v"], do))
-    if Nq == Nk:
-        o, lse = attn.attn_fwd(gq, gk, gv, causal, scale)
-        dq, dk, dv = attn.attn_bwd(gq, gk, gv, o, lse, gdo, causal, scale)
-    else:
-        o, lse = attn.attn_fwd_kv(gq, gk, gv, causal, scale)
-        dq, dk, dv = attn.attn_bwd_kv(gq, gk, gv, o, lse, gdo, causal, scale)
+    gdl = None if dl is None else torch.from_numpy(dl).cuda()
+    o, lse = attn.attn_fwd_ex(gq, gk, gv, causal, scale, o_dtype=torch.bfloat16 if obf else torch.float32)
+    bwd = attn.attn_bwd_bf16grad if gbf else attn.attn_bwd_ex
+    dq, dk, dv = bwd(gq, gk, gv, o, lse, gdo, causal, scale, dlse=gdl)
     torch.cuda.synchronize()
-    got = [t.cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
+    got = [t.float().cpu().numpy().astype(np.float64) for t in (o, lse, dq, dk, dv)]
     ro, rl = oracle.attn_fwd(q, x["k"], x["v"], causal, scale)
-    rdq, rdk, rdv = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
-    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"sweep Nq{Nq} Nk{Nk} d{d} {dtype}")
+    if dl is None:
+        rdq, rdk, rdv = oracle.attn_bwd(q, x["k"], x["v"], do, causal, scale)
+    else:
+        rdq, rdk, rdv = oracle.attn_bwd_dlse(q, x["k"], x["v"], do, dl.astype(np.float64), causal, scale)
+    label = f"sweep Nq{Nq} Nk{Nk} d{d} {dtype}"
+    if obf:   # o rounded to bf16: half a unit in its last place on top of the bound
+        e16 = float(np.abs(got[0] - ro).max())
+        assert e16 <= 1e-2 + 2.0 ** -9 * float(np.abs(ro).max()), f"{label} bf16 o: max abs {e16:.3e}"
+        got[0] = ro
+    # f32 inputs keep the f32 bound unless something was rounded to bf16 on the way
+    _check(got, (ro, rl, rdq, rdk, rdv), "f32" if dtype == "f32" and not (obf or gbf) else "bf16", label)
 
 
 # ---------------------------------------------------------------------------
