@@ -684,6 +684,55 @@ def test_decode_append(B, Hq, Hkv, Lc, d, S, lens):
         assert float(np.abs(po[b] - rpo[0]).max()) <= 1e-2
 
 
+# seeded random decode shapes (ATTN_SWEEP_N / ATTN_SWEEP_SEED as for the training sweep):
+# split decode then merge, against the oracle's split decode, its merge and the
+# unsplit last row; and the append step with per-sequence lengths
+
+
+def _decode_sweep_cases(n, seed):
+    rng = np.random.default_rng(seed + 1)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([16, 32, 64, 128], p=[0.1, 0.1, 0.4, 0.4]))
+        dtype = "f32" if rng.random() < 0.15 else "bf16"
+        Hkv = int(rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16]))
+        cases.append((int(rng.integers(1, 4)), G * Hkv, Hkv, int(rng.integers(1, 5000)), d,
+                      int(rng.integers(1, 41)), dtype))
+    return cases
+
+
+def _append_sweep_cases(n, seed):
+    rng = np.random.default_rng(seed + 2)
+    cases = []
+    for _ in range(n):
+        B = int(rng.integers(1, 6))
+        Hkv = int(rng.integers(1, 9))
+        Lc = int(rng.integers(1, 5000))
+        lens = [int(v) for v in rng.integers(0, Lc, size=B)]
+        cases.append((B, int(rng.choice([1, 2, 3, 4, 6, 8, 16])) * Hkv, Hkv, Lc,
+                      int(rng.choice([64, 128])), int(rng.integers(1, 33)), lens))
+    return cases
+
+
+_NS = int(os.environ.get("ATTN_SWEEP_N", "24"))
+_SEED = int(os.environ.get("ATTN_SWEEP_SEED", "20261203"))
+DECODE_SWEEP = _decode_sweep_cases(max(8, _NS // 2), _SEED)
+APPEND_SWEEP = _append_sweep_cases(max(6, _NS // 4), _SEED)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,S,dtype", DECODE_SWEEP,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_L{c[3]}_d{c[4]}_S{c[5]}_{c[6]}" for c in DECODE_SWEEP])
+def test_decode_sweep(B, Hq, Hkv, L, d, S, dtype):
+    test_decode_shapes(B, Hq, Hkv, L, d, S, dtype)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lc,d,S,lens", APPEND_SWEEP,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Lc{c[3]}_d{c[4]}_S{c[5]}" for c in APPEND_SWEEP])
+def test_decode_append_sweep(B, Hq, Hkv, Lc, d, S, lens):
+    test_decode_append(B, Hq, Hkv, Lc, d, S, lens)
+
+
 def test_decode_append_invalid_lengths_and_two_steps():
     """Lengths outside [0, L_cap) give NaN outputs and leave that cache alone; a
     second step (lengths + 1, new tokens) continues from the first."""
