@@ -623,7 +623,54 @@ def test_attn_rope(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
             gq_, gk_, rdv = oracle.attn_bwd_dlse(qr, kr, x["v"], do, dl64, causal, scale)
         rdq = oracle.rope(gq_, Nk - Nq, base, inverse=True)
         rdk = oracle.rope(gk_, 0, base, inverse=True)
-    _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"attn_rope Nq{Nq} Nk{Nk} d{d}")
+    label = f"attn_rope Nq{Nq} Nk{Nk} d{d}"
+    if dtype == "f32":
+        _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=label)
+        return
+    # bf16: where the path's rotation lands within its own error of a rounding midpoint it
+    # may round to the other neighbour than the oracle did (one unit in the last place);
+    # each such element moves the scores it enters, and so o and lse, by a bounded amount
+    a = _rope_rounding_allowance(oracle.rope(q, Nk - Nq, base), oracle.rope(x["k"], 0, base),
+                                 scale, causal, Hq // Hkv)
+    el = np.abs(got[1] - rl)
+    assert np.all(el <= 1e-3 + a), f"{label} lse: max excess {float((el - 1e-3 - a).max()):.3e}"
+    eo = np.abs(got[0] - ro).max(axis=-1)
+    vmax = float(np.abs(x["v"]).max())
+    assert np.all(eo <= 1e-2 + np.expm1(2 * a) * vmax), f"{label} o: max abs {float(eo.max()):.3e}"
+    for name, g_, r_ in (("dq", got[2], rdq), ("dk", got[3], rdk), ("dv", got[4], rdv)):
+        e = _relF(g_, r_)
+        assert e <= 2e-2, f"{label} {name}: relF {e:.3e}"
+
+
+def _rope_rounding_allowance(qx, kx, scale, causal, G, eps_abs=6e-5, eps_rel=2.0 ** -20):
+    """Per query row, a bound on how far the scores move where the path rounds a rotated
+    element to the other bf16 neighbour than the oracle: only an element whose exact
+    rotated value (qx [B,Hq,Nq,d], kx [B,Hkv,Nk,d], f64) lies within the path's rotation
+    error (eps_abs + eps_rel |x|: the hardware sine and cosine of the fused forward, the
+    library ones of the rotation pass) of a rounding midpoint can, and by one unit in the
+    last place.  Returns [B,Hq,Nq]: scale * max over the visible keys j of
+    sum_c (u_q[i,c] |k_jc| + |q_ic| u_k[j,c]), u = that unit where the element is such,
+    else 0.  lse moves by at most that much, each probability by a factor within
+    exp(+-2 that)."""
+    def amb_ulp(x):
+        ax = np.abs(x)
+        e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+        ulp = np.exp2(e - 7)                                   # bf16: 8 significant bits
+        mid = (np.floor(ax / ulp) + 0.5) * ulp
+        return np.where(np.abs(ax - mid) <= eps_abs + eps_rel * ax, ulp, 0.0)
+    uq, uk = amb_ulp(qx), amb_ulp(kx)
+    B, Hq, Nq, _ = qx.shape
+    Nk = kx.shape[2]
+    vis = (np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)) if causal else None
+    out = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            m = uq[b, h] @ np.abs(kx[b, g]).T + np.abs(qx[b, h]) @ uk[b, g].T   # [Nq, Nk]
+            if vis is not None:
+                m = np.where(vis, m, 0.0)
+            out[b, h] = scale * m.max(axis=1)
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -1073,3 +1120,44 @@ def test_strided_layouts(B, Hq, Hkv, Nq, Nk, d, causal, dtype, o_dtype, with_dls
         assert float(np.abs(got[0] - ro).max()) <= 1e-2 + 2.0 ** -9 * float(np.abs(ro).max())
         got[0] = ro
     _check(got, (ro, rl, rdq, rdk, rdv), dtype, label=f"strided Nq{Nq} Nk{Nk} d{d}")
+
+
+# seeded random shapes for the strided and the rotary entry points (ATTN_SWEEP_N /
+# ATTN_SWEEP_SEED as for the training sweep), through the tests above
+
+def _layout_sweep_cases(n, seed, salt, max_work=1e9):
+    rng = np.random.default_rng(seed + salt)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([16, 32, 64, 128], p=[0.1, 0.1, 0.4, 0.4]))
+        dtype = "f32" if (d <= 32 and rng.random() < 0.5) or rng.random() < 0.1 else "bf16"
+        Hkv = int(rng.integers(1, 7))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        B = int(rng.integers(1, 4))
+        Nk = int(rng.integers(2, 1200))
+        Nq = Nk if rng.random() < 0.5 else int(rng.integers(2, Nk + 1))
+        causal = bool(rng.random() < 0.75)
+        o_dtype = "bf16" if dtype == "bf16" and rng.random() < 0.3 else "f32"
+        dlse = bool(rng.random() < 0.3)
+        if B * G * Hkv * Nq * Nk * d > max_work:
+            continue
+        cases.append((B, G * Hkv, Hkv, Nq, Nk, d, causal, dtype, o_dtype, dlse))
+    return cases
+
+
+STRIDED_SWEEP = _layout_sweep_cases(max(6, _NS // 4), _SEED, 3)
+ROPE_SWEEP = [c[:8] + c[9:] for c in _layout_sweep_cases(max(6, _NS // 4), _SEED, 4)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype,o_dtype,with_dlse", STRIDED_SWEEP,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}_{c[7]}"
+                              f"_o{c[8]}{'_dlse' if c[9] else ''}" for c in STRIDED_SWEEP])
+def test_strided_sweep(B, Hq, Hkv, Nq, Nk, d, causal, dtype, o_dtype, with_dlse):
+    test_strided_layouts(B, Hq, Hkv, Nq, Nk, d, causal, dtype, o_dtype, with_dlse)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal,dtype,with_dlse", ROPE_SWEEP,
+                         ids=[f"B{c[0]}_H{c[1]}x{c[2]}_Nq{c[3]}_Nk{c[4]}_d{c[5]}_{'c' if c[6] else 'nc'}_{c[7]}"
+                              f"{'_dlse' if c[8] else ''}" for c in ROPE_SWEEP])
+def test_attn_rope_sweep(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse):
+    test_attn_rope(B, Hq, Hkv, Nq, Nk, d, causal, dtype, with_dlse)
