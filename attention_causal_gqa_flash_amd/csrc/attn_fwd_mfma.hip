@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma
     // Work item (query tile, batch, query head), XCD-aware (see xcd_work_item)
     const int G = Hq / Hkv;
     WorkItem w;
-    // small grids (two key halves) are resident at once: snake order
+    // small grids (two or four key parts) are resident at once: snake order
     if (!xcd_work_item<(KSPLIT > 1)>(blockIdx.x, B * Hkv, nqt, G, w)) return;
     const int qt = w.tile;
     const int b = w.group / Hkv, g = w.group % Hkv;
