@@ -140,19 +140,25 @@ hipError_t launch_bwd_dq(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, 
 // it is one launch whose grid holds both the dK/dV and the dQ work items,
 // ordered heaviest first over both kinds (measured on MI355X, 4 x 1024 x 12/4
 // heads, HIP-graph replay of the training step: 83.1 us with the two kernels
-// side by side on two streams, 79.8-80.0 us with the one launch).  Otherwise
-// -- d = 128, where the one launch would hold dQ to the dK/dV kernel's
-// one-wave-per-SIMD occupancy (694 us vs 713 us for the 32/8-head N = 4096
-// step), the row-wise fallback, and shapes whose one-launch plan does not fit
-// its kernel argument -- the dQ kernel and then the dK/dV kernel run on the
-// caller's stream (side by side on two streams they gained nothing at d = 128:
-// both are bound by the same CU resources).
-bool fuse_bwd(int d) { return d == 64; }
+// side by side on two streams, 79.8-80.0 us with the one launch).  At d = 128
+// the same holds for grids whose dK/dV work would take the 64-key kernel
+// anyway: there the two kinds' short chains overlap (attn_bwd, 32/8 heads,
+// causal: N = 128 20.5 -> 14.0 us, N = 512 37.6 -> 28.0 us).  Otherwise -- d =
+// 128 on larger grids, where the one launch would give up the 128-key dK/dV
+// kernel (N = 4096: 452 -> 538 us; N = 1024 about even), the row-wise
+// fallback, and shapes whose one-launch plan does not fit its kernel argument
+// -- the dQ kernel (which computes the row terms itself) and then the dK/dV
+// kernel run on the caller's stream (side by side on two streams they gained
+// nothing at d = 128: both are bound by the same CU resources).
+bool fuse_bwd(int B, int Hkv, int Nk, int d)
+{
+    return d == 64 || (d == 128 && !attn::dkdv_use128(B, Hkv, Nk, d));
+}
 
 bool one_launch(int dt, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                 int hs, int *groups = nullptr, int *blocks = nullptr, const attn::Layouts *L = nullptr)
 {
-    return use_mfma(dt, Nk, d, scale, L, Nq) && fuse_bwd(d) &&
+    return use_mfma(dt, Nk, d, scale, L, Nq) && fuse_bwd(B, Hkv, Nk, d) &&
            attn::bwd_fused_plan(B, Hq, Hkv, Nq, Nk, d, causal, hs, groups, blocks);
 }
 
@@ -195,7 +201,7 @@ attn_status bwd_whole(attn_dtype dt, int B, int Hq, int Hkv, int Nq, int Nk, int
     hipStream_t st = (hipStream_t)stream;
     float *delta = (float *)workspace;
     const int hs = dkdv_split(dt, B, Hq, Hkv, Nk, d, scale, L);
-    if (use_mfma(dt, Nk, d, scale, L, Nq) && !fuse_bwd(d) && !o_bf16) {
+    if (use_mfma(dt, Nk, d, scale, L, Nq) && !fuse_bwd(B, Hkv, Nk, d) && !o_bf16) {
         // the dQ kernel also zeroes dk and dv for the dK/dV kernel's atomic head subsets
         if (attn::bwd_dq_pre_mfma(B, Hq, Hkv, Nq, Nk, d, causal != 0, scale, q, k, v, lse, dout,
                                   (const float *)o, dlse, delta, dq, st, rope_lb, L, dk, dv,

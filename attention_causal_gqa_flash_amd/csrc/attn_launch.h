@@ -97,6 +97,8 @@ hipError_t fwd_mfma_rope_q(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
 // kernel; with more than one, dk and dv must be zero-filled before the launch
 // (the kernel adds into them).
 int dkdv_head_split(int B, int Hq, int Hkv, int Nk, int d);
+// Whether the d = 128 dK/dV work takes the 128-key kernel (larger grids).
+bool dkdv_use128(int B, int Hkv, int Nk, int d);
 // The d = 128 dK/dV kernel (128 keys per workgroup) and its key-tile count.
 int dkdv128_tiles(int Nk);
 hipError_t bwd_dkdv128_mfma(int B, int Hq, int Hkv, int Nq, int Nk, int causal, float scale,

@@ -346,6 +346,8 @@ def test_bwd_grads_plan_query(L):
     """Whether the gradient stage is one kernel (host-side answer, no device work)."""
     assert _plan(L, 1, 4, 12, 4, 1024, 1024, 64, 0.125)[0] == 1
     assert _plan(L, 1, 1, 32, 8, 4096, 4096, 128, 0.088)[0] == 0     # d = 128: two kernels
+    assert _plan(L, 1, 1, 32, 8, 512, 512, 128, 0.088)[0] == 1       # ... except on small grids
+    assert _plan(L, 1, 1, 32, 8, 128, 128, 128, 0.088)[0] == 1
     assert _plan(L, 0, 4, 12, 4, 1024, 1024, 64, 0.125)[0] == 0      # f32: row-wise kernels
     assert _plan(L, 1, 4, 12, 4, 1024, 1024, 64, 0.0)[0] == 0        # scale 0: row-wise
     assert _plan(L, 1, 4, 12, 4, 1024, 1024, 40, 0.125) == (0, 0, 0)  # unsupported head dim
