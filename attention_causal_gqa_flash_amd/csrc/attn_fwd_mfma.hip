@@ -171,8 +171,8 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // key half) -- the two key halves stream disjoint halves of the key tiles
 // side by side and their softmax states combine through LDS at the end with
 // the associative merge, which halves the longest chain of tiles.  KSPLIT = 4
-// (smaller grids, d = 64): 32 query rows, the four waves each streaming a
-// quarter of the key tiles.
+// (smaller grids; 32-key tiles): 32 query rows, the four waves each streaming
+// a quarter of the key tiles.
 // OBF: O is written in bf16 (rounded to nearest even) instead of f32.
 // ROPE: q arrives unrotated; each lane turns its Q row (position i + Nk - Nq)
 // by the rotary angles right after loading it -- the lane already holds both
@@ -181,7 +181,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D> &st, const uint16_t *skb, c
 // backward takes it).  rope_lb = log2 of the rotary base.
 // STR: q, k, v and o have the strides of L (else contiguous [B][H][N][D]).
 template <int D, int KSPLIT, int TN, bool OBF, bool ROPE = false, bool STR = false>
-__global__ __launch_bounds__(256, D == 128 && KSPLIT == 2 ? 1 : 2) void fwd_mfma_kernel(
+__global__ __launch_bounds__(256, D == 128 && KSPLIT > 1 ? 1 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, void *__restrict__ O, float *__restrict__ LSE, int B, int Hq,
     int Hkv, int Nq, int Nk, float scale, int causal, int nqt, uint16_t *__restrict__ Qrot,
@@ -492,13 +492,21 @@ hipError_t fwd_mfma_launch(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
     // 1024) 10.9 -> 8.3 us, 128 items 7.45 -> 6.4 us; at 192 and 256 items,
     // where the grid takes a second round, 7.9 -> 10.7 and 8.3 -> 11.1 us.
     const bool split4 = d == 64 && 2 * items <= cus;
+    // d = 128, four key parts of 32-key tiles (128 KB of LDS, one per CU) when
+    // they all fit at once (at most a quarter of a 128-row item per CU):
+    // 32/8 heads x 128 tokens 6.3 -> 5.9 us, 8/2 heads x 512 10.0 -> 8.3 us.
+    const bool split4_128 = d == 128 && 4 * items <= cus;
     auto grid_of = [&](int n_tiles) {
         return dim3((unsigned)(((long)n_tiles * B * Hq + kXcds - 1) / kXcds * kXcds));
     };
     const uint16_t *qq = (const uint16_t *)q, *kk = (const uint16_t *)k, *vv = (const uint16_t *)v;
     uint16_t *qr = (uint16_t *)q_rot;
     const int nqt64 = (Nq + 63) / 64;
-    if (d == 128 && !split) {
+    if (d == 128 && split4_128) {
+        const int nqt32 = (Nq + 31) / 32;
+        hipLaunchKernelGGL((fwd_mfma_kernel<128, 4, 32, OBF, ROPE, STR>), grid_of(nqt32), dim3(256), 0, st, qq, kk,
+                           vv, o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt32, qr, rope_lb, L);
+    } else if (d == 128 && !split) {
         hipLaunchKernelGGL((fwd_mfma_kernel<128, 1, kBN, OBF, ROPE, STR>), grid_of(nqt), dim3(256), 0, st, qq, kk, vv,
                            o, lse, B, Hq, Hkv, Nq, Nk, scale, causal, nqt, qr, rope_lb, L);
     } else if (d == 128) {
