@@ -51,7 +51,7 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m attention_causal_gqa_flash_amd.build first")
     L = ctypes.CDLL(LIB_PATH)
     i, f, p, sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     L.attn_fwd.argtypes = [i, i, i, i, i, i, i, f, p, p, p, p, p, p]
